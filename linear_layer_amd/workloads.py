@@ -1,0 +1,123 @@
+"""Seeded synthetic inputs for the GEMM / fully-connected workloads.
+
+This module only draws numbers; it holds none of the product's arithmetic.
+Both the GPU path (through the tests and the bench) and the CPU oracle are fed
+the very same host arrays made here.
+
+Recipe: a ``torch.Generator('cpu')`` seeded with ``100*config + tensor``
+(tensor: A 0, B 1, C_in 2, bias 3), uniform values from ``2*rand - 1`` in
+fp32 (so [-1, 1)), the fully-connected operands scaled by 1/64 = 1/sqrt(4096)
+(exact in binary), the bias from ``0.2*rand - 0.1``, and fp16 operands rounded
+from the fp32 draw to nearest-even. Integer-valued variants draw from
+``randint`` and are converted to float exactly.
+
+The five workloads are those of the GEMM pages' measurements: square FP32
+products (page "GPU架构下的矩阵乘法深入优化" measures 4096 cubed, page
+"GEMM 优化详解" 1024 cubed), the fully-connected layer of page
+"GEMM 优化详解" section "Level 6: Kernel Fusion" at a ragged batch, and the
+FP16-input / FP32-accumulate product of the tensor-core section of page
+"GPU架构下的矩阵乘法深入优化" (section 6).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    index: int          # 1-based workload number, also the seed base
+    name: str
+    kind: str           # "gemm_f32", "gemm_f16f32" or "linear"
+    M: int
+    N: int
+    K: int
+    alpha: float = 1.0
+    beta: float = 0.0
+    act: int = 1        # linear only: 0 none, 1 ReLU
+    scale: float = 1.0  # operand scale (linear: 1/64)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+WORKLOADS = {
+    "gemm_f32_256": Workload(1, "gemm_f32_256", "gemm_f32", 256, 256, 256),
+    "gemm_f32_1024_ab": Workload(2, "gemm_f32_1024_ab", "gemm_f32", 1024, 1024, 1024, alpha=1.5, beta=0.5),
+    "gemm_f32_4096": Workload(3, "gemm_f32_4096", "gemm_f32", 4096, 4096, 4096),
+    "linear_relu_2047x4096x11008": Workload(4, "linear_relu_2047x4096x11008", "linear", 2047, 11008, 4096,
+                                            act=1, scale=1.0 / 64.0),
+    "gemm_f16f32_8192": Workload(5, "gemm_f16f32_8192", "gemm_f16f32", 8192, 8192, 8192),
+}
+
+
+def generator(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def uniform(shape, seed: int, scale: float = 1.0) -> torch.Tensor:
+    """fp32 values in [-scale, scale) drawn as scale*(2*rand - 1)."""
+    x = torch.rand(shape, generator=generator(seed), dtype=torch.float32) * 2.0 - 1.0
+    if scale != 1.0:
+        x = x * scale
+    return x
+
+
+def bias_uniform(n: int, seed: int) -> torch.Tensor:
+    """fp32 bias in [-0.1, 0.1) drawn as 0.2*rand - 0.1."""
+    return torch.rand((n,), generator=generator(seed), dtype=torch.float32) * 0.2 - 0.1
+
+
+def integers(shape, seed: int, lo: int, hi: int, dtype=torch.float32) -> torch.Tensor:
+    """Integer values in [lo, hi] (inclusive) as an exact float tensor."""
+    return torch.randint(lo, hi + 1, shape, generator=generator(seed), dtype=torch.int64).to(dtype)
+
+
+def to_half(x: torch.Tensor) -> torch.Tensor:
+    """Round fp32 to binary16, nearest-even."""
+    return x.to(torch.float16)
+
+
+def half_bits(x: torch.Tensor):
+    """The binary16 bit patterns of a float16 tensor as a uint16 numpy array."""
+    return x.contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def make_inputs(w: Workload, integer: bool = False, M: int | None = None,
+                N: int | None = None, K: int | None = None) -> dict:
+    """Host (CPU) input tensors for workload ``w``; sizes may be overridden.
+
+    Returns a dict with A, B (and C for beta != 0, bias for linear). For fp16
+    workloads A and B are float16 tensors. ``integer=True`` gives the
+    integer-valued variant whose exact result every summation order reaches:
+    fp32 entries in [-2, 2], C_in and bias in [-4, 4], fp16 entries in [-8, 8].
+    """
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    K = w.K if K is None else K
+    s = 100 * w.index
+    out = {}
+    if integer:
+        lim = 8 if w.kind == "gemm_f16f32" else 2
+        out["A"] = integers((M, K), s + 0, -lim, lim)
+        out["B"] = integers((K, N), s + 1, -lim, lim)
+        if w.beta != 0.0:
+            out["C"] = integers((M, N), s + 2, -4, 4)
+        if w.kind == "linear":
+            out["bias"] = integers((N,), s + 3, -4, 4)
+    else:
+        out["A"] = uniform((M, K), s + 0, w.scale)
+        out["B"] = uniform((K, N), s + 1, w.scale)
+        if w.beta != 0.0:
+            out["C"] = uniform((M, N), s + 2)
+        if w.kind == "linear":
+            out["bias"] = bias_uniform(N, s + 3)
+    if w.kind == "gemm_f16f32":
+        out["A"] = to_half(out["A"])
+        out["B"] = to_half(out["B"])
+    return out
