@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X GEMM / fully-connected hot path on one GPU.
+
+A step is one call of the hot path on one batch of synthetic input already
+resident in HBM: by default the 4096x4096x4096 FP32 GEMM (C = A*B, alpha 1,
+beta 0), i.e. one gemm_f32 launch. ``--workload`` selects another of the five
+workloads (see linear_layer_amd/workloads.py) for ad-hoc measurement.
+
+Prints ONE JSON line with the metric (TFLOPS = 2*M*N*K / time per step),
+a ``roofline`` object for the GEMM kernel (achieved = algorithmic FLOPs per
+launch / average launch duration from HIP events on the launch stream, peak =
+MI355X's published dense matrix peak for the dtype) and a ``cpu_baseline``
+object: the float64 CPU oracle timed on a bounded sample of the same workload
+(a block of whole output rows) on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Published MI355X dense matrix peaks (TFLOP/s).
+PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "gemm_f16f32": 2516.6}
+KERNEL_SOURCES = {
+    "gemm_f32": ["gemm_f32.hip", "common.hpp"],
+    "linear": ["gemm_f32.hip", "common.hpp"],
+    "gemm_f16f32": ["gemm_f16.hip", "common.hpp"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gemm_f32_4096")
+    ap.add_argument("--tile", type=int, default=-1, help="force a tile shape (-1: automatic)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    return ap.parse_args()
+
+
+def kernel_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "linear_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    s = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    if not m or not s or s.group(1) != kernel_hash(kind):
+        return None
+    return float(m.group(1))
+
+
+def cpu_baseline(w, x, target_s: float):
+    """Time the float64 oracle on whole output rows of the same workload."""
+    import numpy as np
+    import oracle
+    from linear_layer_amd import workloads as wl
+
+    A = x["A"]
+    B = x["B"]
+    if w.kind == "gemm_f16f32":
+        A, B = wl.half_bits(A), wl.half_bits(B)
+    else:
+        A, B = A.numpy(), B.numpy()
+    C = x["C"].numpy() if "C" in x else None
+    bias = x["bias"].numpy() if "bias" in x else None
+
+    def run(rows):
+        t0 = time.perf_counter()
+        if w.kind == "linear":
+            oracle.linear(A[:rows], B, bias, w.act)
+        else:
+            oracle.gemm(A[:rows], B, w.alpha, w.beta, None if C is None else C[:rows])
+        return time.perf_counter() - t0
+
+    rows = min(8, w.M)
+    dt = run(rows)
+    rows = int(max(1, min(w.M, rows * target_s / max(dt, 1e-6))))
+    dt = run(rows)
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOPS",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"first {rows} of {w.M} output rows ({rows}x{w.N}x{w.K}, float64, "
+                  f"{dt:.2f} s)",
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has "
+              f"no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_layer_amd as ll
+    from linear_layer_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ll.load()  # fails loudly if the HIP library is missing
+    w = wl.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = wl.make_inputs(w)
+    A = x["A"].to(dev)
+    B = x["B"].to(dev)
+    C = torch.empty((w.M, w.N), device=dev, dtype=torch.float32)
+    if "C" in x:
+        C.copy_(x["C"].to(dev))
+    bias = x["bias"].to(dev) if "bias" in x else None
+    dtype_id = ll.DTYPE_F16 if w.kind == "gemm_f16f32" else ll.DTYPE_F32
+    if args.tile >= 0:
+        ll.set_tile(dtype_id, args.tile)
+    props = torch.cuda.get_device_properties(dev)
+    tile = ll.chosen_tile(dtype_id, w.M, w.N, props.multi_processor_count)
+
+    def step():
+        if w.kind == "gemm_f32":
+            ll.gemm_f32(A, B, C, w.alpha, w.beta)
+        elif w.kind == "gemm_f16f32":
+            ll.gemm_f16f32(A, B, C, w.alpha, w.beta)
+        else:
+            ll.linear_bias_act(A, B, bias, w.act, C)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)  # the stream the library launches on
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.kind]
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, x, args.cpu_seconds)
+
+    dtype = {"gemm_f32": "f32", "linear": "f32", "gemm_f16f32": "f16 in, f32 accumulate"}[w.kind]
+    out = {
+        "metric": "TFLOPS (2MNK/t) for 4096^3 FP32 GEMM on 1 MI355X; % of matrix peak"
+        if w.name == "gemm_f32_4096" else f"TFLOPS (2MNK/t), {w.name}",
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded uniform inputs, resident in HBM)",
+        "config": {
+            "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
+            **({"act": "relu" if w.act == 1 else "none", "bias": True} if w.kind == "linear" else {}),
+            "tile": ll.tile_name(dtype_id, tile),
+            "device": props.name, "cus": props.multi_processor_count,
+        },
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(w.name, w.kind),
+            "kernel_avg_ms": round(avg_launch_ms, 5),
+            "kernel_min_ms": round(min(launch_ms), 5),
+            "flops_per_launch": flops,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

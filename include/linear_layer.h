@@ -1,0 +1,143 @@
+/*
+ * linear_layer.h — C ABI of the MI355X (gfx950) GEMM / fully-connected library.
+ *
+ * Every entry point enqueues work on the caller's HIP stream and returns at
+ * once; it never synchronises, never allocates device memory and keeps no
+ * state between calls beyond a read-only cache of device properties. All
+ * matrix pointers are DEVICE pointers owned by the caller. Matrices are
+ * row-major: element (r, c) of a matrix with leading dimension ld is at
+ * ptr[r * ld + c]. Dimensions and leading dimensions are int; offsets are
+ * computed in 64 bits inside.
+ *
+ * Errors are never fatal: no abort, no exception crosses this boundary. Each
+ * call returns one of the LL_* status codes below. Argument errors are found
+ * on the host before anything is enqueued; faults during execution surface
+ * on the stream like those of any other kernel.
+ *
+ * `stream` is a hipStream_t passed as void* (NULL = the default stream), so
+ * that this header needs no HIP header.
+ */
+#ifndef LINEAR_LAYER_H
+#define LINEAR_LAYER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define LL_OK 0
+#define LL_ERR_INVALID_VALUE 1   /* negative dimension, leading dimension too small,
+                                    NULL pointer that would be dereferenced, pointer not
+                                    aligned to its element size, unknown activation, or
+                                    an output range overlapping an input range */
+#define LL_ERR_NO_DEVICE 2       /* no HIP device is current / visible */
+#define LL_ERR_UNSUPPORTED_ARCH 3/* the current device is not gfx950 (MI355X class) */
+#define LL_ERR_LAUNCH 4          /* the HIP runtime reported an error at launch */
+
+/* Activations for linear_bias_act. */
+#define LL_ACT_NONE 0
+#define LL_ACT_RELU 1
+
+/*
+ * gemm_f32 — C = alpha * A * B + beta * C in FP32.
+ *
+ * Defined on page "GEMM 优化详解" (GEMM optimisation in detail), section
+ * "GEMM 基础理论 / 数学定义" (mathematical definition): the general form
+ * C = alpha*A*B + beta*C with A M-by-K, B K-by-N, C M-by-N and
+ * C(m,n) = sum_k A(m,k) * B(k,n). The same sum is on page "第5章-基础Kernel",
+ * section 1.1.
+ *
+ *   M, N, K   >= 0. M == 0 or N == 0: returns LL_OK, touches nothing.
+ *   A         M-by-K fp32, lda >= max(1, K). Read only if K > 0 and alpha != 0.
+ *   B         K-by-N fp32, ldb >= max(1, N). Read only if K > 0 and alpha != 0.
+ *   C         M-by-N fp32, ldc >= max(1, N), in/out. Read only if beta != 0, so
+ *             with beta == 0 any bit pattern (NaN included) in C is ignored.
+ *   alpha, beta  fp32 scalars (host values). K == 0 or alpha == 0 gives C = beta*C.
+ *   stream    hipStream_t (void*), NULL for the default stream.
+ *
+ * Products are accumulated in FP32 on the matrix cores (MFMA), in an order of
+ * the kernel's choosing. C must not overlap A or B. Pointers need only be
+ * 4-byte aligned; 16-byte aligned pointers with lda, ldb, ldc, K and N all
+ * multiples of 4 take the 128-bit-load kernels, anything else a scalar-load
+ * variant of the same kernels.
+ */
+int gemm_f32(int M, int N, int K, float alpha,
+             const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream);
+
+/*
+ * gemm_f16f32 — C = alpha * A * B + beta * C with IEEE binary16 A and B,
+ * FP32 accumulation and FP32 C.
+ *
+ * The FP16-input / FP32-accumulate product of page
+ * "GPU架构下的矩阵乘法深入优化" (in-depth matrix-multiply optimisation on
+ * GPU architecture), section 6 (tensor-core implementation), in the general
+ * form of page "GEMM 优化详解", section "GEMM 基础理论 / 数学定义".
+ *
+ *   A  M-by-K binary16 bit patterns (uint16_t), lda >= max(1, K).
+ *   B  K-by-N binary16 bit patterns, ldb >= max(1, N).
+ *   C  M-by-N fp32, ldc >= max(1, N).
+ * Every other argument, rule and error as gemm_f32. Pointers to A and B need
+ * only be 2-byte aligned; the 128-bit kernels need 16-byte aligned pointers
+ * and lda, ldb, K, N multiples of 8 (ldc a multiple of 4).
+ */
+int gemm_f16f32(int M, int N, int K, float alpha,
+                const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                float beta, float *C, int ldc, void *stream);
+
+/*
+ * linear_bias_act — Y = act(X * W + bias), the fused fully-connected layer.
+ *
+ * Page "GEMM 优化详解", table "为什么 GEMM 重要" (an FC layer is
+ * Y = X*W + b) and section "Level 6: Kernel Fusion" (the bias, indexed by
+ * output column, and then the ReLU are applied in the GEMM's write-back, so
+ * the intermediate never goes to memory). The page's four flag combinations
+ * map to (bias != NULL) x (act).
+ *
+ *   X     M-by-K fp32 (a batch of M input rows), ldx >= max(1, K).
+ *   W     K-by-N fp32 weights, row-major K-by-N, ldw >= max(1, N).
+ *   bias  N fp32 values, or NULL for no bias.
+ *   act   LL_ACT_NONE or LL_ACT_RELU; ReLU maps y <= 0 (and NaN) to +0.0.
+ *   Y     M-by-N fp32 output, ldy >= max(1, N); never read.
+ * K == 0 gives Y = act(bias) (or act(0)). Y must not overlap X, W or bias.
+ * Alignment rules as gemm_f32.
+ */
+int linear_bias_act(int M, int N, int K,
+                    const float *X, int ldx, const float *W, int ldw,
+                    const float *bias, int act,
+                    float *Y, int ldy, void *stream);
+
+/* A static, human-readable string for a status code (never NULL). */
+const char *ll_status_string(int status);
+
+/*
+ * Tile selection. Each data type has a small set of block-tile shapes; by
+ * default the library picks one per call from M, N and the CU count so that
+ * large problems get the largest tiles and smaller ones do not leave CUs idle
+ * (the size-dependent strategy of page "GEMM 优化详解", section
+ * "矩阵大小选择策略" (matrix-size strategy), re-derived for 256 CUs).
+ * These calls let a benchmark or a caller pin the choice. They touch only
+ * host memory and never the GPU.
+ */
+#define LL_DTYPE_F32 0 /* gemm_f32 and linear_bias_act */
+#define LL_DTYPE_F16 1 /* gemm_f16f32 */
+
+/* Number of tile shapes for a data type (0 for an unknown dtype). */
+int ll_num_tiles(int dtype);
+/* Name of a tile shape, e.g. "f32_256x256x16" ("" if out of range). Static string. */
+const char *ll_tile_name(int dtype, int tile);
+/* Force tile `tile` for every later call of that dtype in this process;
+ * -1 restores the automatic choice. Process-wide, thread-safe.
+ * Returns LL_OK or LL_ERR_INVALID_VALUE. */
+int ll_set_tile(int dtype, int tile);
+/* The tile the library would use for an M-by-N output on a device with
+ * num_cus compute units (num_cus <= 0: 256), honouring ll_set_tile. */
+int ll_chosen_tile(int dtype, int M, int N, int num_cus);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINEAR_LAYER_H */

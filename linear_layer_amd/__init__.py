@@ -1,0 +1,188 @@
+"""Python binding of the MI355X GEMM / fully-connected C-ABI library.
+
+Argument marshalling only: shape, dtype and layout checks, then the tensors'
+device pointers and the current HIP stream go to ``liblinear_layer.so``,
+whose HIP kernels do all of the arithmetic. There is no fallback: if the
+library is missing, importing the functions raises.
+
+Entry points (same names as the C ABI in ``include/linear_layer.h``):
+
+* ``gemm_f32(A, B, C, alpha=1.0, beta=0.0)`` — C = alpha*A*B + beta*C, fp32.
+* ``gemm_f16f32(A, B, C, alpha=1.0, beta=0.0)`` — fp16 A, B; fp32 C.
+* ``linear_bias_act(X, W, bias, act, Y)`` — Y = act(X*W + bias), fp32.
+
+Tensors are 2-D, row-major with unit column stride (a row stride larger than
+the width is a leading dimension), on the current CUDA/HIP device. The calls
+are asynchronous on ``torch.cuda.current_stream()`` unless ``stream`` is given.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "LinearLayerError", "gemm_f32", "gemm_f16f32", "linear_bias_act", "status_string",
+    "library_path", "load", "set_tile", "num_tiles", "tile_name", "chosen_tile",
+    "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16",
+    "OK", "ERR_INVALID_VALUE", "ERR_NO_DEVICE", "ERR_UNSUPPORTED_ARCH", "ERR_LAUNCH",
+]
+
+OK, ERR_INVALID_VALUE, ERR_NO_DEVICE, ERR_UNSUPPORTED_ARCH, ERR_LAUNCH = 0, 1, 2, 3, 4
+ACT_NONE, ACT_RELU = 0, 1
+DTYPE_F32, DTYPE_F16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liblinear_layer.so")
+_lib = None
+
+# Every symbol the C header declares.
+EXPORTED = ("gemm_f32", "gemm_f16f32", "linear_bias_act", "ll_status_string",
+            "ll_num_tiles", "ll_tile_name", "ll_set_tile", "ll_chosen_tile")
+
+
+class LinearLayerError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load liblinear_layer.so (built in-tree by ``python -m linear_layer_amd._build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m linear_layer_amd._build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, f32, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    lib.gemm_f32.argtypes = [i32, i32, i32, f32, vp, i32, vp, i32, f32, vp, i32, vp]
+    lib.gemm_f16f32.argtypes = lib.gemm_f32.argtypes
+    lib.linear_bias_act.argtypes = [i32, i32, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp]
+    for f in (lib.gemm_f32, lib.gemm_f16f32, lib.linear_bias_act):
+        f.restype = i32
+    lib.ll_status_string.argtypes = [i32]
+    lib.ll_status_string.restype = ctypes.c_char_p
+    lib.ll_num_tiles.argtypes = [i32]
+    lib.ll_num_tiles.restype = i32
+    lib.ll_tile_name.argtypes = [i32, i32]
+    lib.ll_tile_name.restype = ctypes.c_char_p
+    lib.ll_set_tile.argtypes = [i32, i32]
+    lib.ll_set_tile.restype = i32
+    lib.ll_chosen_tile.argtypes = [i32, i32, i32, i32]
+    lib.ll_chosen_tile.restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().ll_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise LinearLayerError(status, where)
+
+
+def set_tile(dtype: int, tile: int) -> None:
+    _check(load().ll_set_tile(int(dtype), int(tile)), "ll_set_tile")
+
+
+def num_tiles(dtype: int) -> int:
+    return load().ll_num_tiles(int(dtype))
+
+
+def tile_name(dtype: int, tile: int) -> str:
+    return load().ll_tile_name(int(dtype), int(tile)).decode()
+
+
+def chosen_tile(dtype: int, M: int, N: int, num_cus: int = 0) -> int:
+    return load().ll_chosen_tile(int(dtype), int(M), int(N), int(num_cus))
+
+
+# ---- tensor marshalling ---------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _mat(t, dtype, name):
+    """(pointer, rows, cols, ld) of a 2-D row-major device tensor."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    if rows > 1 and ld < cols:
+        raise ValueError(f"{name}: row stride {ld} smaller than width {cols}")
+    return t.data_ptr(), rows, cols, max(ld, 1)
+
+
+def _stream(stream, *tensors):
+    torch = _torch()
+    if stream is None:
+        dev = tensors[0].device
+        for t in tensors[1:]:
+            if t is not None and t.device != dev:
+                raise ValueError("all tensors must be on the same device")
+        if torch.cuda.current_device() != dev.index:
+            raise ValueError(f"tensors are on {dev}, but the current device is "
+                             f"cuda:{torch.cuda.current_device()}")
+        stream = torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _gemm(fn_name, in_dtype, A, B, C, alpha, beta, stream):
+    torch = _torch()
+    pa, M, K, lda = _mat(A, in_dtype, "A")
+    pb, K2, N, ldb = _mat(B, in_dtype, "B")
+    pc, M2, N2, ldc = _mat(C, torch.float32, "C")
+    if K2 != K or M2 != M or N2 != N:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    st = getattr(load(), fn_name)(M, N, K, float(alpha), pa, lda, pb, ldb, float(beta), pc, ldc,
+                                  _stream(stream, A, B, C))
+    _check(st, fn_name)
+    return C
+
+
+def gemm_f32(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    """C = alpha*A*B + beta*C (fp32); C is written in place and returned."""
+    return _gemm("gemm_f32", _torch().float32, A, B, C, alpha, beta, stream)
+
+
+def gemm_f16f32(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    """C = alpha*A*B + beta*C with fp16 A, B and fp32 C; C returned."""
+    return _gemm("gemm_f16f32", _torch().float16, A, B, C, alpha, beta, stream)
+
+
+def linear_bias_act(X, W, bias, act: int, Y, stream=None):
+    """Y = act(X*W + bias) (fp32; W is K-by-N row-major; bias may be None)."""
+    torch = _torch()
+    px, M, K, ldx = _mat(X, torch.float32, "X")
+    pw, K2, N, ldw = _mat(W, torch.float32, "W")
+    py, M2, N2, ldy = _mat(Y, torch.float32, "Y")
+    if K2 != K or M2 != M or N2 != N:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}, Y {tuple(Y.shape)}")
+    pbias = None
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.dim() != 1 or bias.shape[0] != N or not bias.is_cuda:
+            raise ValueError("bias must be a 1-D fp32 device tensor of length N")
+        if N > 1 and bias.stride(0) != 1:
+            raise ValueError("bias must be contiguous")
+        pbias = bias.data_ptr()
+    st = load().linear_bias_act(M, N, K, px, ldx, pw, ldw, pbias, int(act), py, ldy,
+                                _stream(stream, X, W, Y, bias))
+    _check(st, "linear_bias_act")
+    return Y

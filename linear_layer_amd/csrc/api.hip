@@ -1,0 +1,290 @@
+// The C ABI: argument checks, quick returns, tile choice and one launch on the
+// caller's stream. Nothing here allocates, synchronises or keeps per-call
+// state; the only global data are a per-device property cache and the
+// optional tile overrides.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+
+#include "linear_layer.h"
+#include "launch.hpp"
+
+using namespace ll;
+
+namespace {
+
+// ---- argument checks (host only, before any HIP call) ----
+
+int64_t span_bytes(int rows, int cols, int64_t ld, int64_t elem)
+{
+    if (rows <= 0 || cols <= 0)
+        return 0;
+    return ((int64_t)(rows - 1) * ld + cols) * elem;
+}
+
+bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes)
+{
+    if (abytes <= 0 || bbytes <= 0)
+        return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+int imax1(int v) { return v > 1 ? v : 1; }
+
+// Returns LL_OK and sets *noop when nothing is to be done.
+int check_gemm(int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
+               const float *C, int ldc, int64_t elem_ab, bool *noop)
+{
+    *noop = false;
+    if (M < 0 || N < 0 || K < 0)
+        return LL_ERR_INVALID_VALUE;
+    if (lda < imax1(K) || ldb < imax1(N) || ldc < imax1(N))
+        return LL_ERR_INVALID_VALUE;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return LL_OK;
+    }
+    if (C == nullptr || !aligned(C, 4))
+        return LL_ERR_INVALID_VALUE;
+    const bool reads_ab = K > 0 && alpha != 0.0f;
+    if (reads_ab) {
+        if (A == nullptr || B == nullptr || !aligned(A, elem_ab) || !aligned(B, elem_ab))
+            return LL_ERR_INVALID_VALUE;
+        const int64_t cb = span_bytes(M, N, ldc, 4);
+        if (overlap(C, cb, A, span_bytes(M, K, lda, elem_ab)) ||
+            overlap(C, cb, B, span_bytes(K, N, ldb, elem_ab)))
+            return LL_ERR_INVALID_VALUE;
+    }
+    return LL_OK;
+}
+
+// ---- device check (cached per device) ----
+
+struct DevInfo {
+    int status;
+    int cus;
+};
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+DevInfo g_dev_info[kMaxDevices];
+
+DevInfo probe_device(int dev)
+{
+    DevInfo d{LL_ERR_NO_DEVICE, 0};
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return d;
+    }
+    d.cus = prop.multiProcessorCount;
+    d.status = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? LL_OK : LL_ERR_UNSUPPORTED_ARCH;
+    return d;
+}
+
+int current_device(DevInfo *out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return LL_ERR_NO_DEVICE;
+    }
+    if (dev >= kMaxDevices) {
+        *out = probe_device(dev);
+    } else {
+        std::call_once(g_dev_once[dev], [dev] { g_dev_info[dev] = probe_device(dev); });
+        *out = g_dev_info[dev];
+    }
+    return out->status;
+}
+
+// ---- tile choice ----
+
+std::atomic<int> g_tile_override[2] = {{-1}, {-1}};  // [0] fp32, [1] fp16
+
+// Relative throughput of each tile shape when every CU is busy (the larger
+// tiles reuse each loaded operand more often and hide more latency).
+const float kF32Eff[kF32NumTiles] = {1.0f, 0.92f, 0.8f, 0.45f};
+const float kF16Eff[kF16NumTiles] = {1.0f, 0.75f, 0.4f};
+
+// Pick the tile minimising (rounds of workgroups over the CUs) x (work per
+// tile) / efficiency: big tiles for big problems, smaller ones when big
+// tiles would leave CUs idle (wave quantisation).
+int pick_tile(const TileInfo *tiles, const float *eff, int n, int M, int N, int cus)
+{
+    int best = 0;
+    double best_cost = 0.0;
+    for (int t = 0; t < n; ++t) {
+        const int64_t tiles_mn = (int64_t)((M + tiles[t].bm - 1) / tiles[t].bm) *
+                                 ((N + tiles[t].bn - 1) / tiles[t].bn);
+        const int64_t rounds = (tiles_mn + cus - 1) / cus;
+        const double cost = (double)rounds * tiles[t].bm * tiles[t].bn / eff[t];
+        if (t == 0 || cost < best_cost) {
+            best = t;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+int choose_tile(int dtype, int M, int N, int cus)
+{
+    const int ov = g_tile_override[dtype].load(std::memory_order_relaxed);
+    if (dtype == 0)
+        return (ov >= 0 && ov < kF32NumTiles) ? ov : pick_tile(kF32Tiles, kF32Eff, kF32NumTiles, M, N, cus);
+    return (ov >= 0 && ov < kF16NumTiles) ? ov : pick_tile(kF16Tiles, kF16Eff, kF16NumTiles, M, N, cus);
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? LL_OK : LL_ERR_LAUNCH; }
+
+GemmParams make_params(int M, int N, int K, float alpha, const void *A, int lda, const void *B,
+                       int ldb, float beta, float *C, int ldc)
+{
+    GemmParams p;
+    memset(&p, 0, sizeof p);
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.bias = nullptr;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.act = 0;
+    p.group_m = 4;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream)
+{
+    bool noop;
+    int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 4, &noop);
+    if (st != LL_OK || noop)
+        return st;
+    DevInfo dev;
+    if ((st = current_device(&dev)) != LL_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0 || alpha == 0.0f)
+        return launch_status(launch_scale(C, ldc, M, N, beta, s));
+    const bool vec = aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && lda % 4 == 0 &&
+                     ldb % 4 == 0 && ldc % 4 == 0 && K % 4 == 0 && N % 4 == 0;
+    GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    const int tile = choose_tile(0, M, N, dev.cus);
+    return launch_status(
+        launch_gemm_f32(p, tile, beta == 0.0f ? EPI_GEMM_BETA0 : EPI_GEMM_BETA, vec, s));
+}
+
+int gemm_f16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+                int ldb, float beta, float *C, int ldc, void *stream)
+{
+    bool noop;
+    int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 2, &noop);
+    if (st != LL_OK || noop)
+        return st;
+    DevInfo dev;
+    if ((st = current_device(&dev)) != LL_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0 || alpha == 0.0f)
+        return launch_status(launch_scale(C, ldc, M, N, beta, s));
+    const bool vec = aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && lda % 8 == 0 &&
+                     ldb % 8 == 0 && ldc % 4 == 0 && K % 8 == 0 && N % 8 == 0;
+    GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    const int tile = choose_tile(1, M, N, dev.cus);
+    return launch_status(
+        launch_gemm_f16(p, tile, beta == 0.0f ? EPI_GEMM_BETA0 : EPI_GEMM_BETA, vec, s));
+}
+
+int linear_bias_act(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
+                    const float *bias, int act, float *Y, int ldy, void *stream)
+{
+    if (act != LL_ACT_NONE && act != LL_ACT_RELU)
+        return LL_ERR_INVALID_VALUE;
+    bool noop;
+    int st = check_gemm(M, N, K, 1.0f, X, ldx, W, ldw, Y, ldy, 4, &noop);
+    if (st != LL_OK || noop)
+        return st;
+    if (bias != nullptr) {
+        if (!aligned(bias, 4) || overlap(Y, span_bytes(M, N, ldy, 4), bias, (int64_t)N * 4))
+            return LL_ERR_INVALID_VALUE;
+    }
+    DevInfo dev;
+    if ((st = current_device(&dev)) != LL_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0)
+        return launch_status(launch_bias_fill(Y, ldy, M, N, bias, act, s));
+    const bool vec = aligned(X, 16) && aligned(W, 16) && aligned(Y, 16) && ldx % 4 == 0 &&
+                     ldw % 4 == 0 && ldy % 4 == 0 && K % 4 == 0 && N % 4 == 0;
+    GemmParams p = make_params(M, N, K, 1.0f, X, ldx, W, ldw, 0.0f, Y, ldy);
+    p.bias = bias;
+    p.act = act;
+    const int tile = choose_tile(0, M, N, dev.cus);
+    return launch_status(launch_gemm_f32(p, tile, EPI_LINEAR, vec, s));
+}
+
+const char *ll_status_string(int status)
+{
+    switch (status) {
+    case LL_OK: return "LL_OK: success";
+    case LL_ERR_INVALID_VALUE: return "LL_ERR_INVALID_VALUE: invalid argument";
+    case LL_ERR_NO_DEVICE: return "LL_ERR_NO_DEVICE: no HIP device available";
+    case LL_ERR_UNSUPPORTED_ARCH: return "LL_ERR_UNSUPPORTED_ARCH: device is not gfx950";
+    case LL_ERR_LAUNCH: return "LL_ERR_LAUNCH: kernel launch failed";
+    default: return "unknown linear_layer status";
+    }
+}
+
+int ll_set_tile(int dtype, int tile)
+{
+    if (dtype != LL_DTYPE_F32 && dtype != LL_DTYPE_F16)
+        return LL_ERR_INVALID_VALUE;
+    const int n = dtype == LL_DTYPE_F32 ? kF32NumTiles : kF16NumTiles;
+    if (tile < -1 || tile >= n)
+        return LL_ERR_INVALID_VALUE;
+    g_tile_override[dtype].store(tile, std::memory_order_relaxed);
+    return LL_OK;
+}
+
+int ll_num_tiles(int dtype)
+{
+    if (dtype == LL_DTYPE_F32)
+        return kF32NumTiles;
+    if (dtype == LL_DTYPE_F16)
+        return kF16NumTiles;
+    return 0;
+}
+
+const char *ll_tile_name(int dtype, int tile)
+{
+    if (dtype == LL_DTYPE_F32 && tile >= 0 && tile < kF32NumTiles)
+        return kF32Tiles[tile].name;
+    if (dtype == LL_DTYPE_F16 && tile >= 0 && tile < kF16NumTiles)
+        return kF16Tiles[tile].name;
+    return "";
+}
+
+int ll_chosen_tile(int dtype, int M, int N, int num_cus)
+{
+    if (dtype != LL_DTYPE_F32 && dtype != LL_DTYPE_F16)
+        return -1;
+    return choose_tile(dtype, M, N, num_cus > 0 ? num_cus : 256);
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device-side building blocks shared by the FP32 and FP16 GEMM kernels:
+// parameter block, workgroup -> output-tile mapping, LDS swizzle and the
+// fused write-back (alpha/beta, bias, ReLU).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ll {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Write-back variants. The write-back is fused into the GEMM kernel, so the
+// product never makes a round trip through memory before bias and activation
+// are applied (page "GEMM 优化详解", section "Level 6: Kernel Fusion").
+enum Epi : int {
+    EPI_GEMM_BETA0 = 0,  // C = alpha*acc            (C not read)
+    EPI_GEMM_BETA = 1,   // C = alpha*acc + beta*C
+    EPI_LINEAR = 2,      // Y = act(acc + bias[n])   (Y not read)
+};
+
+struct GemmParams {
+    const void *A;        // M x K, row-major, leading dimension lda (elements)
+    const void *B;        // K x N, row-major, leading dimension ldb
+    float *C;             // M x N, row-major, leading dimension ldc (in/out)
+    const float *bias;    // N values or nullptr (EPI_LINEAR)
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    float alpha, beta;
+    int act;              // 0 none, 1 ReLU (EPI_LINEAR)
+    int tiles_m, tiles_n; // output tiles along M and N
+    int group_m;          // tile rows per group in the grouped ordering
+};
+
+// Workgroup id -> (tile_m, tile_n).
+//
+// The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn, and
+// each XCD has its own L2. The first step renumbers ids so that the ids one
+// XCD receives are consecutive; the second walks tiles in groups of group_m
+// tile rows, column by column, so that the tiles resident on one XCD at a
+// time form a compact block and share their A rows and B columns in that
+// XCD's L2.
+__device__ __forceinline__ void tile_coords(const GemmParams &p, int &tm, int &tn)
+{
+    const int nwg = gridDim.x, wg = blockIdx.x;
+    const int q = nwg >> 3, r = nwg & 7, x = wg & 7;
+    const int lid = x * q + (x < r ? x : r) + (wg >> 3);
+    const int group = p.group_m * p.tiles_n;
+    const int g = lid / group;
+    const int first_m = g * p.group_m;
+    const int rows = min(p.tiles_m - first_m, p.group_m);
+    const int within = lid - g * group;
+    tm = first_m + within % rows;
+    tn = within / rows;
+}
+
+// XOR swizzle of 16-byte chunks inside an LDS row of ROW_BYTES bytes, so that
+// eight lanes reading the same logical chunk of eight consecutive rows hit
+// all 32 banks. RPL = rows per 128-byte bank line; the chunk index is XORed
+// with the row's line number (mod the chunks per row, at most 8).
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int row)
+{
+    constexpr int CPR = ROW_BYTES / 16;
+    constexpr int RPL = ROW_BYTES >= 128 ? 1 : 128 / ROW_BYTES;
+    constexpr int MASK = (CPR < 8 ? CPR : 8) - 1;
+    return (row / RPL) & MASK;
+}
+
+// The fused write-back of one 32x32 MFMA accumulator block.
+//
+// Accumulator layout of v_mfma_f32_32x32x* (wave64): lane l holds column
+// l % 32; register r holds row 8*(r/4) + 4*(l/32) + r%4.
+template <int EPI>
+__device__ __forceinline__ void write_block(const GemmParams &p, const f32x16 &acc,
+                                            int row0, int col0, int lane)
+{
+    const int col = col0 + (lane & 31);
+    if (col >= p.N)
+        return;
+    const int rbase = row0 + ((lane >> 5) << 2);
+    float bv = 0.0f;
+    if (EPI == EPI_LINEAR && p.bias != nullptr)
+        bv = p.bias[col];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = rbase + ((r >> 2) << 3) + (r & 3);
+        if (row < p.M) {
+            float *dst = p.C + (int64_t)row * p.ldc + col;
+            float v = acc[r];
+            if (EPI == EPI_GEMM_BETA0) {
+                v = p.alpha * v;
+            } else if (EPI == EPI_GEMM_BETA) {
+                v = __builtin_fmaf(p.alpha, v, p.beta * *dst);
+            } else {
+                v = v + bv;
+                if (p.act == 1)
+                    v = v > 0.0f ? v : 0.0f;
+            }
+            *dst = v;
+        }
+    }
+}
+
+}  // namespace ll

@@ -1,0 +1,53 @@
+// Quick-return kernels for the degenerate cases of the GEMM definition
+// (page "GEMM 优化详解", section "GEMM 基础理论 / 数学定义"): when K == 0 or
+// alpha == 0 the product term vanishes and C = beta*C; for the fully-connected
+// layer with K == 0, Y = act(bias). Both are plain HBM-bound row sweeps.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ll {
+
+// One workgroup per row-stripe, threads striding along the row.
+__global__ void __launch_bounds__(256) scale_kernel(float *C, int64_t ldc, int M, int N, float beta)
+{
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+        float *row = C + m * ldc;
+        for (int n = threadIdx.x; n < N; n += blockDim.x)
+            row[n] = (beta == 0.0f) ? 0.0f : beta * row[n];
+    }
+}
+
+__global__ void __launch_bounds__(256) bias_fill_kernel(float *Y, int64_t ldy, int M, int N,
+                                                        const float *bias, int act)
+{
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+        float *row = Y + m * ldy;
+        for (int n = threadIdx.x; n < N; n += blockDim.x) {
+            float v = bias ? bias[n] : 0.0f;
+            if (act == 1)
+                v = v > 0.0f ? v : 0.0f;
+            row[n] = v;
+        }
+    }
+}
+
+static unsigned rows_grid(int M)
+{
+    return (unsigned)(M < 65536 ? M : 65536);
+}
+
+hipError_t launch_scale(float *C, int64_t ldc, int M, int N, float beta, hipStream_t s)
+{
+    hipLaunchKernelGGL(scale_kernel, dim3(rows_grid(M)), dim3(256), 0, s, C, ldc, M, N, beta);
+    return hipGetLastError();
+}
+
+hipError_t launch_bias_fill(float *Y, int64_t ldy, int M, int N, const float *bias, int act,
+                            hipStream_t s)
+{
+    hipLaunchKernelGGL(bias_fill_kernel, dim3(rows_grid(M)), dim3(256), 0, s, Y, ldy, M, N, bias,
+                       act);
+    return hipGetLastError();
+}
+
+}  // namespace ll

@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects bad arguments before touching the device, reports a
+missing device as a status (never an abort), and picks tiles as documented."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_layer_amd as ll
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linear_layer.h")
+
+# Fake, well-aligned, non-overlapping "device" addresses: these calls must
+# fail validation (or find no device) before anything is dereferenced.
+PA, PB, PC = 0x10000000, 0x20000000, 0x30000000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", text))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ll.load()
+    declared = header_functions()
+    assert declared == set(ll.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {ll.library_path()}").read()
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    assert declared <= exported
+
+
+def test_status_strings():
+    for s in range(5):
+        assert ll.status_string(s).startswith(("LL_OK", "LL_ERR"))
+    assert "unknown" in ll.status_string(99)
+
+
+def call_gemm(M, N, K, alpha=1.0, A=PA, lda=None, B=PB, ldb=None, beta=0.0, C=PC, ldc=None, f16=False):
+    lib = ll.load()
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    fn = lib.gemm_f16f32 if f16 else lib.gemm_f32
+    return fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, None)
+
+
+@pytest.mark.parametrize("f16", [False, True])
+def test_invalid_arguments(f16):
+    E = ll.ERR_INVALID_VALUE
+    assert call_gemm(-1, 4, 4, f16=f16) == E
+    assert call_gemm(4, -1, 4, f16=f16) == E
+    assert call_gemm(4, 4, -1, f16=f16) == E
+    assert call_gemm(4, 4, 8, lda=7, f16=f16) == E          # lda < K
+    assert call_gemm(4, 8, 4, ldb=7, f16=f16) == E          # ldb < N
+    assert call_gemm(4, 8, 4, ldc=7, f16=f16) == E          # ldc < N
+    assert call_gemm(4, 4, 4, A=None, f16=f16) == E
+    assert call_gemm(4, 4, 4, B=None, f16=f16) == E
+    assert call_gemm(4, 4, 4, C=None, f16=f16) == E
+    assert call_gemm(4, 4, 4, C=PC + 2, f16=f16) == E       # C not 4-byte aligned
+    assert call_gemm(4, 4, 4, A=PA + 1, f16=f16) == E       # A not element aligned
+    # C overlapping A or B
+    assert call_gemm(4, 4, 4, C=PA + 8, f16=f16) == E
+    assert call_gemm(4, 4, 4, C=PB - 16, f16=f16) == E
+
+
+def test_quick_returns_touch_nothing():
+    # M == 0 or N == 0: OK with no device and even with NULL pointers
+    assert call_gemm(0, 5, 5, A=None, B=None, C=None) == ll.OK
+    assert call_gemm(5, 0, 5, A=None, B=None, C=None, f16=True) == ll.OK
+    lib = ll.load()
+    assert lib.linear_bias_act(0, 3, 3, None, 3, None, 3, None, 1, None, 3, None) == ll.OK
+
+
+def test_linear_invalid_arguments():
+    lib = ll.load()
+    E = ll.ERR_INVALID_VALUE
+    assert lib.linear_bias_act(4, 4, 4, PA, 4, PB, 4, None, 2, PC, 4, None) == E   # unknown act
+    assert lib.linear_bias_act(4, 4, 4, PA, 4, PB, 4, None, -1, PC, 4, None) == E
+    assert lib.linear_bias_act(4, 4, 4, PA, 3, PB, 4, None, 1, PC, 4, None) == E   # ldx < K
+    assert lib.linear_bias_act(4, 4, 4, PA, 4, PB, 4, PC + 4, 1, PC, 4, None) == E  # bias inside Y
+    assert lib.linear_bias_act(4, 4, 4, PA, 4, PB, 4, PB + 2, 1, PC, 4, None) == E  # bias misaligned
+    assert lib.linear_bias_act(4, 4, 4, PA, 4, PB, 4, None, 1, PA, 4, None) == E    # Y overlaps X
+
+
+def test_alpha_zero_does_not_need_a_or_b():
+    # A, B are not read when alpha == 0 or K == 0, so NULL is accepted; with no
+    # device present the call then reports the missing device.
+    st = call_gemm(4, 4, 4, alpha=0.0, A=None, B=None, beta=1.0)
+    assert st in (ll.ERR_NO_DEVICE, ll.OK, ll.ERR_UNSUPPORTED_ARCH)
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-device status on a host without a GPU")
+def test_no_device_is_a_status_not_an_abort():
+    assert call_gemm(64, 64, 64) == ll.ERR_NO_DEVICE
+    assert call_gemm(64, 64, 64, f16=True) == ll.ERR_NO_DEVICE
+    lib = ll.load()
+    assert lib.linear_bias_act(4, 4, 4, PA, 4, PB, 4, None, 1, PC, 4, None) == ll.ERR_NO_DEVICE
+
+
+def test_tile_choice():
+    f32, f16 = ll.DTYPE_F32, ll.DTYPE_F16
+    names32 = [ll.tile_name(f32, t) for t in range(ll.num_tiles(f32))]
+    names16 = [ll.tile_name(f16, t) for t in range(ll.num_tiles(f16))]
+    assert names32[0] == "f32_256x256x16" and names16[0] == "f16_256x256x64"
+    assert ll.tile_name(f32, 99) == "" and ll.num_tiles(7) == 0
+    # 4096^2 on 256 CUs: one 256x256 tile per CU
+    assert names32[ll.chosen_tile(f32, 4096, 4096, 256)] == "f32_256x256x16"
+    # 2047 x 11008: 256x256 tiles leave a partial second round; 256x128 fills better
+    assert names32[ll.chosen_tile(f32, 2047, 11008, 256)] == "f32_256x128x16"
+    # small problems use small tiles so more CUs work
+    assert names32[ll.chosen_tile(f32, 1024, 1024, 256)] == "f32_64x64x16"
+    assert names16[ll.chosen_tile(f16, 8192, 8192, 256)] == "f16_256x256x64"
+    ll.set_tile(f32, 2)
+    try:
+        assert ll.chosen_tile(f32, 4096, 4096, 256) == 2
+    finally:
+        ll.set_tile(f32, -1)
+    assert ll.chosen_tile(f32, 4096, 4096, 256) == 0
+    with pytest.raises(ll.LinearLayerError):
+        ll.set_tile(f32, 17)
+    with pytest.raises(ll.LinearLayerError):
+        ll.set_tile(5, 0)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    A = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        ll.gemm_f32(A, A, A)
+    with pytest.raises(TypeError):
+        ll.gemm_f32(A.double(), A, A)

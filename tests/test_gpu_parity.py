@@ -1,0 +1,403 @@
+"""GPU parity: the HIP path through the C ABI against the float64 CPU oracle.
+
+Tolerance (floating point): |C_gpu - r| <= 1e-4 * t + ulp_fp32(r)/2 element by
+element, where r is the oracle's float64 result and t = sum_k |A[m,k]*B[k,n]|.
+The half-ulp term covers the single fp32 rounding of the stored result when t
+is tiny (e.g. alpha == 0 or a zero row). Integer-valued inputs must give the
+oracle's result bit for bit (every partial sum is an exact fp32 integer).
+
+Sizes: small cases span several tiles of every tile shape with ragged tails
+in M, N and K and are compared in full; the five full-size workloads are run
+in the launch configuration the bench times and compared on sampled elements
+(plus whole edge rows/columns) and on row/column checksums that cover every
+element.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from linear_layer_amd import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU hosts but never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import linear_layer_amd as ll  # noqa: E402
+
+DEV = "cuda:0"
+F32, F16 = ll.DTYPE_F32, ll.DTYPE_F16
+
+
+def np32(t):
+    return t.detach().cpu().numpy()
+
+
+def bits16(t):
+    return wl.half_bits(t.detach().cpu())
+
+
+def assert_close(gpu, R, T, what=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    half_ulp = np.spacing(np.abs(R).astype(np.float32)).astype(np.float64) / 2
+    bound = 1e-4 * T + half_ulp
+    err = np.abs(gpu - R)
+    bad = ~(err <= bound)
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside bound; first at flat {i}: "
+                             f"gpu={gpu.ravel()[i]!r} oracle={R.ravel()[i]!r} t={T.ravel()[i]!r}")
+    return float(np.max(err / np.maximum(T, 1e-300))) if err.size else 0.0
+
+
+def assert_exact(gpu, R, what=""):
+    want = R.astype(np.float32)
+    gpu = np.asarray(gpu, dtype=np.float32)
+    bad = gpu != want
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} differ; first at flat {i}: "
+                             f"gpu={gpu.ravel()[i]!r} want={want.ravel()[i]!r}")
+
+
+@pytest.fixture
+def tile():
+    """Force a tile shape for one test, restore the automatic choice after."""
+    forced = []
+
+    def force(dtype, t):
+        ll.set_tile(dtype, t)
+        forced.append(dtype)
+
+    yield force
+    for d in forced:
+        ll.set_tile(d, -1)
+
+
+def run_gemm_f32(A, B, alpha=1.0, beta=0.0, C=None):
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    Cd = (C.clone() if C is not None else torch.full((A.shape[0], B.shape[1]), float("nan"))).to(DEV)
+    ll.gemm_f32(Ad, Bd, Cd, alpha, beta)
+    torch.cuda.synchronize()
+    return np32(Cd)
+
+
+def run_gemm_f16(A, B, alpha=1.0, beta=0.0, C=None):
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    Cd = (C.clone() if C is not None else torch.full((A.shape[0], B.shape[1]), float("nan"))).to(DEV)
+    ll.gemm_f16f32(Ad, Bd, Cd, alpha, beta)
+    torch.cuda.synchronize()
+    return np32(Cd)
+
+
+def run_linear(X, W, b, act):
+    Xd, Wd = X.to(DEV), W.to(DEV)
+    bd = b.to(DEV) if b is not None else None
+    Yd = torch.full((X.shape[0], W.shape[1]), float("nan"), device=DEV)
+    ll.linear_bias_act(Xd, Wd, bd, act, Yd)
+    torch.cuda.synchronize()
+    return np32(Yd)
+
+
+def rand(shape, seed, scale=1.0):
+    return wl.uniform(shape, seed, scale)
+
+
+# ---- small shapes, every tile, ragged tails ----------------------------------
+
+SMALL = [(600, 520, 200), (257, 300, 64), (33, 70, 36), (1, 1, 4), (130, 1, 12), (1, 260, 20)]
+
+
+@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_f32_small(t, M, N, K, tile):
+    tile(F32, t)
+    A, B = rand((M, K), 1), rand((K, N), 2)
+    R, T = oracle.gemm(np32(A), np32(B))
+    assert_close(run_gemm_f32(A, B), R, T, f"f32 tile {t} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("t", range(4))
+def test_f32_alpha_beta(t, tile):
+    tile(F32, t)
+    M, N, K = 300, 280, 100
+    A, B, C = rand((M, K), 3), rand((K, N), 4), rand((M, N), 5)
+    R, T = oracle.gemm(np32(A), np32(B), 1.5, 0.5, np32(C))
+    assert_close(run_gemm_f32(A, B, 1.5, 0.5, C), R, T, f"f32 alpha/beta tile {t}")
+    R, T = oracle.gemm(np32(A), np32(B), -0.75, 0.0)
+    assert_close(run_gemm_f32(A, B, -0.75, 0.0), R, T, f"f32 alpha only tile {t}")
+
+
+@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("M,N,K", [(301, 517, 203), (70, 33, 5), (5, 9, 1)])
+def test_f32_scalar_path(t, M, N, K, tile):
+    # K or N not a multiple of 4: the scalar-load kernels
+    tile(F32, t)
+    A, B = rand((M, K), 6), rand((K, N), 7)
+    R, T = oracle.gemm(np32(A), np32(B))
+    assert_close(run_gemm_f32(A, B), R, T, f"f32 scalar tile {t}")
+
+
+@pytest.mark.parametrize("t", range(4))
+def test_f32_unaligned_views(t, tile):
+    # operands starting one element into a buffer, with padded leading dims
+    tile(F32, t)
+    M, N, K = 150, 140, 72
+    Abuf, Bbuf = rand((M, K + 5), 8), rand((K, N + 3), 9)
+    A, B = Abuf[:, 1:K + 1], Bbuf[:, 1:N + 1]
+    Cbuf = torch.full((M, N + 6), 7.0, device=DEV)
+    C = Cbuf[:, 2:N + 2]
+    ll.gemm_f32(Abuf.to(DEV)[:, 1:K + 1], Bbuf.to(DEV)[:, 1:N + 1], C, 1.0, 0.0)
+    torch.cuda.synchronize()
+    R, T = oracle.gemm(np32(A), np32(B))
+    assert_close(np32(C), R, T, "unaligned")
+    guard = np32(Cbuf)
+    assert np.all(guard[:, :2] == 7.0) and np.all(guard[:, N + 2:] == 7.0)
+
+
+@pytest.mark.parametrize("t", range(3))
+@pytest.mark.parametrize("M,N,K", [(600, 520, 192), (257, 264, 64), (33, 72, 40), (1, 8, 8)])
+def test_f16_small(t, M, N, K, tile):
+    tile(F16, t)
+    A, B = wl.to_half(rand((M, K), 10)), wl.to_half(rand((K, N), 11))
+    R, T = oracle.gemm(bits16(A), bits16(B))
+    assert_close(run_gemm_f16(A, B), R, T, f"f16 tile {t} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("t", range(3))
+@pytest.mark.parametrize("M,N,K", [(301, 517, 203), (40, 30, 10), (3, 5, 1)])
+def test_f16_scalar_path(t, M, N, K, tile):
+    tile(F16, t)
+    A, B = wl.to_half(rand((M, K), 12)), wl.to_half(rand((K, N), 13))
+    C = rand((M, N), 14)
+    R, T = oracle.gemm(bits16(A), bits16(B), 1.5, 0.5, np32(C))
+    assert_close(run_gemm_f16(A, B, 1.5, 0.5, C), R, T, f"f16 scalar tile {t}")
+
+
+@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_linear_small(t, act, with_bias, tile):
+    tile(F32, t)
+    M, N, K = 513, 260, 96
+    X, W = rand((M, K), 15, 1 / 8), rand((K, N), 16, 1 / 8)
+    b = wl.bias_uniform(N, 17) if with_bias else None
+    R, T = oracle.linear(np32(X), np32(W), None if b is None else np32(b), act)
+    Y = run_linear(X, W, b, act)
+    assert_close(Y, R, T, f"linear tile {t} act {act} bias {with_bias}")
+    if act == 1:
+        assert not np.any(np.signbit(Y))  # +0.0 for y <= 0
+
+
+@pytest.mark.parametrize("t", range(4))
+def test_linear_scalar_path(t, tile):
+    tile(F32, t)
+    M, N, K = 97, 131, 45
+    X, W, b = rand((M, K), 18), rand((K, N), 19), wl.bias_uniform(N, 20)
+    R, T = oracle.linear(np32(X), np32(W), np32(b), 1)
+    assert_close(run_linear(X, W, b, 1), R, T, "linear scalar")
+
+
+# ---- integer-valued inputs: bit-exact --------------------------------------
+
+@pytest.mark.parametrize("t", range(4))
+def test_f32_integer_exact(t, tile):
+    tile(F32, t)
+    M, N, K = 333, 290, 260
+    A = wl.integers((M, K), 21, -2, 2)
+    B = wl.integers((K, N), 22, -2, 2)
+    C = wl.integers((M, N), 23, -4, 4)
+    R, _ = oracle.gemm(np32(A), np32(B), 1.5, 0.5, np32(C))
+    assert_exact(run_gemm_f32(A, B, 1.5, 0.5, C), R, f"f32 int tile {t}")
+
+
+@pytest.mark.parametrize("t", range(3))
+def test_f16_integer_exact(t, tile):
+    tile(F16, t)
+    M, N, K = 300, 280, 256
+    A = wl.to_half(wl.integers((M, K), 24, -8, 8))
+    B = wl.to_half(wl.integers((K, N), 25, -8, 8))
+    R, _ = oracle.gemm(bits16(A), bits16(B))
+    assert_exact(run_gemm_f16(A, B), R, f"f16 int tile {t}")
+
+
+@pytest.mark.parametrize("t", range(4))
+def test_linear_integer_exact(t, tile):
+    tile(F32, t)
+    M, N, K = 300, 264, 128
+    X, W, b = wl.integers((M, K), 26, -2, 2), wl.integers((K, N), 27, -2, 2), wl.integers((N,), 28, -4, 4)
+    R, _ = oracle.linear(np32(X), np32(W), np32(b), 1)
+    assert_exact(run_linear(X, W, b, 1), R, f"linear int tile {t}")
+
+
+# ---- degenerate cases and the write-back contract ---------------------------
+
+def test_k_zero_and_alpha_zero():
+    M, N = 70, 90
+    C = rand((M, N), 30)
+    A0, B0 = torch.zeros((M, 0)), torch.zeros((0, N))
+    got = run_gemm_f32(A0, B0, 2.0, 0.5, C)
+    assert np.array_equal(got, (np32(C) * np.float32(0.5)))
+    A, B = rand((M, 8), 31), rand((8, N), 32)
+    got = run_gemm_f32(A, B, 0.0, -1.0, C)
+    assert np.array_equal(got, -np32(C))
+    got = run_gemm_f32(A, B, 0.0, 0.0, C)
+    assert np.all(got == 0)
+    got = run_gemm_f16(wl.to_half(A0), wl.to_half(B0), 1.0, 0.0, C)
+    assert np.all(got == 0)
+    b = wl.bias_uniform(N, 33)
+    Y = run_linear(torch.zeros((M, 0)), torch.zeros((0, N)), b, 1)
+    assert np.array_equal(Y, np.broadcast_to(np.maximum(np32(b), 0), (M, N)))
+    Y = run_linear(torch.zeros((M, 0)), torch.zeros((0, N)), None, 0)
+    assert np.all(Y == 0)
+
+
+def test_empty_outputs_are_no_ops():
+    C = torch.zeros((0, 5), device=DEV)
+    ll.gemm_f32(torch.zeros((0, 3), device=DEV), torch.zeros((3, 5), device=DEV), C)
+    C = torch.zeros((4, 0), device=DEV)
+    ll.gemm_f16f32(torch.zeros((4, 3), device=DEV, dtype=torch.float16),
+                   torch.zeros((3, 0), device=DEV, dtype=torch.float16), C)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("t", range(4))
+def test_beta_zero_ignores_nan_and_guards_stay(t, tile):
+    tile(F32, t)
+    M, N, K = 131, 100, 48
+    A, B = rand((M, K), 34), rand((K, N), 35)
+    Cbuf = torch.full((M + 3, N + 8), float("nan"), device=DEV)
+    C = Cbuf[:M, :N]
+    ll.gemm_f32(A.to(DEV), B.to(DEV), C, 1.0, 0.0)
+    torch.cuda.synchronize()
+    R, T = oracle.gemm(np32(A), np32(B))
+    assert_close(np32(C), R, T, "nan prefill")
+    g = np32(Cbuf)
+    assert np.all(np.isnan(g[:, N:])) and np.all(np.isnan(g[M:, :]))
+
+
+def test_non_default_stream():
+    M, N, K = 512, 384, 256
+    A, B = rand((M, K), 36), rand((K, N), 37)
+    s = torch.cuda.Stream()
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = torch.empty((M, N), device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        ll.gemm_f32(Ad, Bd, C)
+    s.synchronize()
+    R, T = oracle.gemm(np32(A), np32(B))
+    assert_close(np32(C), R, T, "stream")
+
+
+def test_errors_raise():
+    A = torch.zeros((4, 4), device=DEV)
+    with pytest.raises(ll.LinearLayerError):
+        ll.linear_bias_act(A, A, None, 7, torch.zeros((4, 4), device=DEV))
+    with pytest.raises(ll.LinearLayerError):
+        ll.gemm_f32(A, A, A)  # C overlaps A
+
+
+# ---- full-size workloads, as the bench launches them ------------------------
+
+def sample_positions(M, N, n, seed):
+    g = np.random.default_rng(seed)
+    rows = g.integers(0, M, n)
+    cols = g.integers(0, N, n)
+    # whole first/last row and column (the ragged edges)
+    er = np.concatenate([np.full(N, 0), np.full(N, M - 1), np.arange(M), np.arange(M)])
+    ec = np.concatenate([np.arange(N), np.arange(N), np.full(M, 0), np.full(M, N - 1)])
+    return np.concatenate([rows, er]), np.concatenate([cols, ec])
+
+
+def checksums(gpu, A64, B64, alpha=1.0, beta=0.0, C64=None, bias=None):
+    """Row and column sums of the GPU output against float64 sums of the inputs.
+
+    Row sums of alpha*A*B are alpha*A*(B*1); column sums are alpha*(1'*A)*B.
+    The tolerance is 1e-4 times the matching sums of |A|*|B| (plus the beta*C
+    and bias terms), i.e. the element bound summed over the row or column.
+    """
+    g = gpu.astype(np.float64)
+    absA, absB = np.abs(A64), np.abs(B64)
+    row = alpha * (A64 @ B64.sum(axis=1))
+    col = alpha * (A64.sum(axis=0) @ B64)
+    trow = abs(alpha) * (absA @ absB.sum(axis=1))
+    tcol = abs(alpha) * (absA.sum(axis=0) @ absB)
+    if C64 is not None:
+        row += beta * C64.sum(axis=1)
+        col += beta * C64.sum(axis=0)
+    if bias is not None:
+        row += bias.sum()
+        col += A64.shape[0] * bias
+    slack_r = 1e-4 * trow + 1e-6 * np.abs(row) + 1e-3
+    slack_c = 1e-4 * tcol + 1e-6 * np.abs(col) + 1e-3
+    assert np.all(np.abs(g.sum(axis=1) - row) <= slack_r), "row checksums"
+    assert np.all(np.abs(g.sum(axis=0) - col) <= slack_c), "column checksums"
+
+
+@pytest.mark.parametrize("name", ["gemm_f32_256", "gemm_f32_1024_ab", "gemm_f32_4096"])
+def test_full_gemm_f32(name):
+    w = wl.WORKLOADS[name]
+    x = wl.make_inputs(w)
+    A, B = x["A"], x["B"]
+    C = x.get("C")
+    got = run_gemm_f32(A, B, w.alpha, w.beta, C)
+    rows, cols = sample_positions(w.M, w.N, 20000, w.index)
+    Cn = None if C is None else np32(C)
+    R, T = oracle.gemm_at(np32(A), np32(B), rows, cols, w.alpha, w.beta, Cn)
+    ratio = assert_close(got[rows, cols], R, T, name)
+    print(f"{name}: max err/t on samples = {ratio:.3g}")
+    C64 = None if C is None else Cn.astype(np.float64)
+    checksums(got, np32(A).astype(np.float64), np32(B).astype(np.float64), w.alpha, w.beta, C64)
+
+
+def test_full_linear():
+    w = wl.WORKLOADS["linear_relu_2047x4096x11008"]
+    x = wl.make_inputs(w)
+    X, W, b = x["A"], x["B"], x["bias"]
+    got = run_linear(X, W, b, w.act)
+    rows, cols = sample_positions(w.M, w.N, 20000, w.index)
+    R, T = oracle.linear_at(np32(X), np32(W), rows, cols, np32(b), w.act)
+    ratio = assert_close(got[rows, cols], R, T, w.name)
+    print(f"{w.name}: max err/t on samples = {ratio:.3g}")
+    # the same product without the ReLU, checked by checksums
+    got0 = run_linear(X, W, b, 0)
+    checksums(got0, np32(X).astype(np.float64), np32(W).astype(np.float64),
+              bias=np32(b).astype(np.float64))
+    assert np.array_equal(got, np.where(got0 > 0, got0, np.float32(0)))
+
+
+def test_full_gemm_f16():
+    w = wl.WORKLOADS["gemm_f16f32_8192"]
+    x = wl.make_inputs(w)
+    A, B = x["A"], x["B"]
+    got = run_gemm_f16(A, B)
+    rows, cols = sample_positions(w.M, w.N, 20000, w.index)
+    R, T = oracle.gemm_at(bits16(A), bits16(B), rows, cols)
+    ratio = assert_close(got[rows, cols], R, T, w.name)
+    print(f"{w.name}: max err/t on samples = {ratio:.3g}")
+    checksums(got, A.double().numpy(), B.double().numpy())
+
+
+@pytest.mark.parametrize("name", list(wl.WORKLOADS))
+def test_full_integer_exact(name):
+    w = wl.WORKLOADS[name]
+    x = wl.make_inputs(w, integer=True)
+    A, B = x["A"], x["B"]
+    rows, cols = sample_positions(w.M, w.N, 20000, 1000 + w.index)
+    if w.kind == "gemm_f32":
+        got = run_gemm_f32(A, B, w.alpha, w.beta, x.get("C"))
+        Cn = None if "C" not in x else np32(x["C"])
+        R, _ = oracle.gemm_at(np32(A), np32(B), rows, cols, w.alpha, w.beta, Cn)
+    elif w.kind == "gemm_f16f32":
+        got = run_gemm_f16(A, B)
+        R, _ = oracle.gemm_at(bits16(A), bits16(B), rows, cols)
+    else:
+        got = run_linear(A, B, x["bias"], w.act)
+        R, _ = oracle.linear_at(np32(A), np32(B), rows, cols, np32(x["bias"]), w.act)
+    assert_exact(got[rows, cols], R, name)
+    # every element of an integer-input product is an integer (or half-integer
+    # with alpha = 1.5, beta = 0.5) of bounded size
+    step = 0.5 if w.alpha == 1.5 else 1.0
+    assert np.all(np.mod(got, step) == 0) and np.all(np.isfinite(got))
