@@ -26,6 +26,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+COPY_BYTES = 256 << 20
+
 # Published MI355X dense matrix peaks (TFLOP/s).
 PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "gemm_f16f32": 2516.6}
 KERNEL_SOURCES = {
@@ -44,7 +46,30 @@ def parse():
     ap.add_argument("--tile", type=int, default=-1, help="force a tile shape (-1: automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="instead of the GEMM, run a plain device-to-device copy of 256 MiB "
+                         "--steps times (the reference kernel for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(steps: int):
+    """A plain copy of known size: each launch reads and writes COPY_BYTES."""
+    import torch
+    n = COPY_BYTES // 4
+    src = torch.ones(n, device="cuda:0", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                      "steps": steps, "ms_per_copy": round(ms, 5),
+                      "GB_per_s": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def kernel_hash(kind: str) -> str:
@@ -114,6 +139,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has "
               f"no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
 
     import torch
     import linear_layer_amd as ll
