@@ -108,23 +108,31 @@ int current_device(DevInfo *out)
 
 std::atomic<int> g_tile_override[2] = {{-1}, {-1}};  // [0] fp32, [1] fp16
 
-// Relative throughput of each tile shape when every CU is busy (the larger
-// tiles reuse each loaded operand more often and hide more latency).
-const float kF32Eff[kF32NumTiles] = {1.0f, 0.92f, 0.8f, 0.45f};
-const float kF16Eff[kF16NumTiles] = {1.0f, 0.75f, 0.4f};
+// Estimated time of an M x N output with a tile shape: tiles are dealt
+// round-robin over the CUs, so the busiest CU gets ceil(tiles/CUs) of them.
+// With one workgroup per CU they run one after another at eff_alone; with two
+// they run in pairs at eff_paired (a pair takes twice a tile's work), and an
+// odd last one runs alone. The smallest estimate wins: big tiles for big
+// problems, smaller ones when big tiles would leave CUs idle (wave
+// quantisation) -- the size-dependent choice of page "GEMM 优化详解",
+// section "矩阵大小选择策略", re-derived for 256 CUs.
+double tile_cost(const TileInfo &t, int M, int N, int cus)
+{
+    const int64_t tiles = (int64_t)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
+    const int64_t per_cu = (tiles + cus - 1) / cus;
+    const double work = (double)t.bm * t.bn;
+    if (t.wg_per_cu <= 1 || per_cu == 1)
+        return per_cu * work / t.eff_alone;
+    const int64_t pairs = per_cu / 2, single = per_cu % 2;
+    return pairs * 2.0 * work / t.eff_paired + single * work / t.eff_alone;
+}
 
-// Pick the tile minimising (rounds of workgroups over the CUs) x (work per
-// tile) / efficiency: big tiles for big problems, smaller ones when big
-// tiles would leave CUs idle (wave quantisation).
-int pick_tile(const TileInfo *tiles, const float *eff, int n, int M, int N, int cus)
+int pick_tile(const TileInfo *tiles, int n, int M, int N, int cus)
 {
     int best = 0;
     double best_cost = 0.0;
     for (int t = 0; t < n; ++t) {
-        const int64_t tiles_mn = (int64_t)((M + tiles[t].bm - 1) / tiles[t].bm) *
-                                 ((N + tiles[t].bn - 1) / tiles[t].bn);
-        const int64_t rounds = (tiles_mn + cus - 1) / cus;
-        const double cost = (double)rounds * tiles[t].bm * tiles[t].bn / eff[t];
+        const double cost = tile_cost(tiles[t], M, N, cus);
         if (t == 0 || cost < best_cost) {
             best = t;
             best_cost = cost;
@@ -137,8 +145,8 @@ int choose_tile(int dtype, int M, int N, int cus)
 {
     const int ov = g_tile_override[dtype].load(std::memory_order_relaxed);
     if (dtype == 0)
-        return (ov >= 0 && ov < kF32NumTiles) ? ov : pick_tile(kF32Tiles, kF32Eff, kF32NumTiles, M, N, cus);
-    return (ov >= 0 && ov < kF16NumTiles) ? ov : pick_tile(kF16Tiles, kF16Eff, kF16NumTiles, M, N, cus);
+        return (ov >= 0 && ov < kF32NumTiles) ? ov : pick_tile(kF32Tiles, kF32NumTiles, M, N, cus);
+    return (ov >= 0 && ov < kF16NumTiles) ? ov : pick_tile(kF16Tiles, kF16NumTiles, M, N, cus);
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? LL_OK : LL_ERR_LAUNCH; }

@@ -241,10 +241,12 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     return hipGetLastError();
 }
 
+// {BM, BN, workgroups per CU, relative throughput alone, paired} (see the
+// FP32 table); measured on the 8192^3 product.
 const TileInfo kF16Tiles[kF16NumTiles] = {
-    {F16_L::BM, F16_L::BN, "f16_256x256x64"},
-    {F16_S::BM, F16_S::BN, "f16_128x128x64"},
-    {F16_XS::BM, F16_XS::BN, "f16_64x64x64"},
+    {F16_L::BM, F16_L::BN, 1, 1.00f, 1.00f, "f16_256x256x64"},
+    {F16_S::BM, F16_S::BN, 2, 0.60f, 0.79f, "f16_128x128x64"},
+    {F16_XS::BM, F16_XS::BN, 2, 0.25f, 0.32f, "f16_64x64x64"},
 };
 
 hipError_t launch_gemm_f16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)

@@ -9,6 +9,9 @@ namespace ll {
 
 struct TileInfo {
     int bm, bn;
+    int wg_per_cu;     // workgroups resident per CU (register/LDS limited)
+    float eff_alone;   // relative CU throughput with one workgroup on it
+    float eff_paired;  // relative CU throughput with wg_per_cu workgroups on it
     const char *name;
 };
 

@@ -116,10 +116,13 @@ def test_tile_choice():
     names16 = [ll.tile_name(f16, t) for t in range(ll.num_tiles(f16))]
     assert names32[0] == "f32_256x256x16" and names16[0] == "f16_256x256x64"
     assert ll.tile_name(f32, 99) == "" and ll.num_tiles(7) == 0
-    # 4096^2 on 256 CUs: one 256x256 tile per CU
-    assert names32[ll.chosen_tile(f32, 4096, 4096, 256)] == "f32_256x256x16"
+    # 4096^2 on 256 CUs: two 256x128 tiles per CU, paired (one workgroup covers
+    # the other's waits)
+    assert names32[ll.chosen_tile(f32, 4096, 4096, 256)] == "f32_256x128x16"
     # 2047 x 11008: 256x256 tiles leave a partial second round; 256x128 fills better
     assert names32[ll.chosen_tile(f32, 2047, 11008, 256)] == "f32_256x128x16"
+    # a device with fewer CUs moves the balance
+    assert names32[ll.chosen_tile(f32, 4096, 4096, 64)] in names32
     # small problems use small tiles so more CUs work
     assert names32[ll.chosen_tile(f32, 1024, 1024, 256)] == "f32_64x64x16"
     assert names16[ll.chosen_tile(f16, 8192, 8192, 256)] == "f16_256x256x64"
@@ -128,7 +131,7 @@ def test_tile_choice():
         assert ll.chosen_tile(f32, 4096, 4096, 256) == 2
     finally:
         ll.set_tile(f32, -1)
-    assert ll.chosen_tile(f32, 4096, 4096, 256) == 0
+    assert ll.chosen_tile(f32, 4096, 4096, 256) == 1
     with pytest.raises(ll.LinearLayerError):
         ll.set_tile(f32, 17)
     with pytest.raises(ll.LinearLayerError):

@@ -15,19 +15,24 @@ element.
 import numpy as np
 import pytest
 
+import linear_layer_amd as ll
 import oracle
 from linear_layer_amd import workloads as wl
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-if not torch.cuda.is_available():  # collected on CPU hosts but never run there
-    pytest.skip("needs a GPU", allow_module_level=True)
-
-import linear_layer_amd as ll  # noqa: E402
-
 DEV = "cuda:0"
 F32, F16 = ll.DTYPE_F32, ll.DTYPE_F16
+# every tile shape the library offers, each forced in turn
+T32 = list(range(ll.num_tiles(F32)))
+T16 = list(range(ll.num_tiles(F16)))
+
+
+@pytest.fixture(autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
 
 
 def np32(t):
@@ -109,7 +114,7 @@ def rand(shape, seed, scale=1.0):
 SMALL = [(600, 520, 200), (257, 300, 64), (33, 70, 36), (1, 1, 4), (130, 1, 12), (1, 260, 20)]
 
 
-@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("t", T32)
 @pytest.mark.parametrize("M,N,K", SMALL)
 def test_f32_small(t, M, N, K, tile):
     tile(F32, t)
@@ -118,7 +123,7 @@ def test_f32_small(t, M, N, K, tile):
     assert_close(run_gemm_f32(A, B), R, T, f"f32 tile {t} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("t", T32)
 def test_f32_alpha_beta(t, tile):
     tile(F32, t)
     M, N, K = 300, 280, 100
@@ -129,7 +134,7 @@ def test_f32_alpha_beta(t, tile):
     assert_close(run_gemm_f32(A, B, -0.75, 0.0), R, T, f"f32 alpha only tile {t}")
 
 
-@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("t", T32)
 @pytest.mark.parametrize("M,N,K", [(301, 517, 203), (70, 33, 5), (5, 9, 1)])
 def test_f32_scalar_path(t, M, N, K, tile):
     # K or N not a multiple of 4: the scalar-load kernels
@@ -139,7 +144,7 @@ def test_f32_scalar_path(t, M, N, K, tile):
     assert_close(run_gemm_f32(A, B), R, T, f"f32 scalar tile {t}")
 
 
-@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("t", T32)
 def test_f32_unaligned_views(t, tile):
     # operands starting one element into a buffer, with padded leading dims
     tile(F32, t)
@@ -156,7 +161,7 @@ def test_f32_unaligned_views(t, tile):
     assert np.all(guard[:, :2] == 7.0) and np.all(guard[:, N + 2:] == 7.0)
 
 
-@pytest.mark.parametrize("t", range(3))
+@pytest.mark.parametrize("t", T16)
 @pytest.mark.parametrize("M,N,K", [(600, 520, 192), (257, 264, 64), (33, 72, 40), (1, 8, 8)])
 def test_f16_small(t, M, N, K, tile):
     tile(F16, t)
@@ -165,7 +170,7 @@ def test_f16_small(t, M, N, K, tile):
     assert_close(run_gemm_f16(A, B), R, T, f"f16 tile {t} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("t", range(3))
+@pytest.mark.parametrize("t", T16)
 @pytest.mark.parametrize("M,N,K", [(301, 517, 203), (40, 30, 10), (3, 5, 1)])
 def test_f16_scalar_path(t, M, N, K, tile):
     tile(F16, t)
@@ -175,7 +180,7 @@ def test_f16_scalar_path(t, M, N, K, tile):
     assert_close(run_gemm_f16(A, B, 1.5, 0.5, C), R, T, f"f16 scalar tile {t}")
 
 
-@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("t", T32)
 @pytest.mark.parametrize("act", [0, 1])
 @pytest.mark.parametrize("with_bias", [True, False])
 def test_linear_small(t, act, with_bias, tile):
@@ -190,7 +195,7 @@ def test_linear_small(t, act, with_bias, tile):
         assert not np.any(np.signbit(Y))  # +0.0 for y <= 0
 
 
-@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("t", T32)
 def test_linear_scalar_path(t, tile):
     tile(F32, t)
     M, N, K = 97, 131, 45
@@ -201,7 +206,7 @@ def test_linear_scalar_path(t, tile):
 
 # ---- integer-valued inputs: bit-exact --------------------------------------
 
-@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("t", T32)
 def test_f32_integer_exact(t, tile):
     tile(F32, t)
     M, N, K = 333, 290, 260
@@ -212,7 +217,7 @@ def test_f32_integer_exact(t, tile):
     assert_exact(run_gemm_f32(A, B, 1.5, 0.5, C), R, f"f32 int tile {t}")
 
 
-@pytest.mark.parametrize("t", range(3))
+@pytest.mark.parametrize("t", T16)
 def test_f16_integer_exact(t, tile):
     tile(F16, t)
     M, N, K = 300, 280, 256
@@ -222,7 +227,7 @@ def test_f16_integer_exact(t, tile):
     assert_exact(run_gemm_f16(A, B), R, f"f16 int tile {t}")
 
 
-@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("t", T32)
 def test_linear_integer_exact(t, tile):
     tile(F32, t)
     M, N, K = 300, 264, 128
@@ -262,7 +267,7 @@ def test_empty_outputs_are_no_ops():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("t", range(4))
+@pytest.mark.parametrize("t", T32)
 def test_beta_zero_ignores_nan_and_guards_stay(t, tile):
     tile(F32, t)
     M, N, K = 131, 100, 48
