@@ -70,6 +70,40 @@ __device__ __forceinline__ int swz(int row)
     return (row / RPL) & MASK;
 }
 
+// ---- direct global -> LDS copies ----
+
+// Byte address of an LDS object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// global_load_lds_dwordx4: this lane's 16 bytes at `src` are written to LDS
+// byte address lds_base + 16*lane, without passing through registers (so one
+// wave instruction fills one contiguous KiB). Issued as inline assembly so the
+// compiler does not treat it as an LDS store that every later barrier must
+// wait for; the caller counts these copies itself (s_waitcnt vmcnt) before
+// the barrier that publishes them. Lanes masked off by EXEC copy nothing.
+__device__ __forceinline__ void lds_dma_16(const void *src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "memory", "m0");
+}
+
+// Zero the 16-byte LDS slot at a byte address (for lanes whose source lies
+// outside the matrix; the copy above cannot produce zeros).
+__device__ __forceinline__ void lds_zero_16(uint32_t lds_byte_addr)
+{
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(lds_byte_addr) =
+        u32x4{0u, 0u, 0u, 0u};
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+#define LL_VMCNT(n) ((((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14)))
+
 // The fused write-back of one 32x32 MFMA accumulator block.
 //
 // Accumulator layout of v_mfma_f32_32x32x* (wave64): lane l holds column

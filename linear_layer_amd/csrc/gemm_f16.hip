@@ -214,6 +214,182 @@ gemm_f16_kernel(GemmParams p)
                              n0 + wn * T::WTN + fn * 32, lane);
 }
 
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS FP16 kernel (256x256 block tile, 128-bit-aligned operands).
+//
+// Both operands travel global -> LDS with global_load_lds_dwordx4, so no
+// registers hold prefetched tiles and the 256 accumulators per lane leave room
+// for two register sets of MFMA operands. B keeps its row-major [k][n] layout
+// in LDS; the MFMA's B operand (8 consecutive k of one column per lane) is
+// read with ds_read_b64_tr_b16, gfx950's transposing LDS load: within each
+// group of 16 lanes, lane i receives element i%4 of the 8-byte rows that lanes
+// i/4, 4+i/4, 8+i/4 and 12+i/4 address. If lane j points at
+// B[kb + j/4][nb + 4*(j%4)], lane i therefore receives B[kb .. kb+3][nb + i].
+//
+// LDS, per stage of BK = 32:
+//   A: 256 rows x 64 bytes; 16-byte chunks XOR-swizzled by (row/4)%4, so the
+//      16 lanes one LDS cycle serves (16 consecutive rows, one logical chunk)
+//      hit 16 different 16-byte bank groups (measured conflict-free). One
+//      copy (KiB) = 16 rows; lane l fills row l/4, slot l%4 and fetches the
+//      logical chunk (l%4) ^ ((l/16)%4).
+//   B: 32 rows x 512 bytes; 32-byte units XOR-swizzled by k%4, so the four
+//      k-rows one 16-lane transpose read touches fall in four different
+//      32-byte units of a 128-byte bank line. One copy = 2 rows; lane l fills
+//      row l/32, bytes 16*(l%32) .. +15.
+// Four stages form a ring (128 KiB). The barrier that ends stage kt also
+// publishes stage kt+2, so during stage kt each wave already reads the first
+// operands of stage kt+1 and no LDS latency is exposed after a barrier; the
+// copies of stage kt+3 are issued into the buffer stage kt-1 used.
+template <int EPI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_f16_direct_kernel(GemmParams p)
+{
+    constexpr int BM = 256, BN = 256, BK = 32, NBUF = 4;
+    constexpr int FM = 4, FN = 4, WTM = 128, WTN = 128;
+    constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;      // halves
+    constexpr int COPIES = 4;                                 // per wave per operand per stage
+    constexpr int PER_STAGE = 2 * COPIES;                     // vmcnt entries per stage
+    __shared__ __attribute__((aligned(1024))) uint16_t As[NBUF][A_STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Bs[NBUF][B_STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A);
+    const uint16_t *__restrict__ B = static_cast<const uint16_t *>(p.B);
+    const int M = p.M, N = p.N, K = p.K;
+
+    // Copy sources. A copy j of this wave: rows (wave*4 + j)*16 + lane/4.
+    const int a_c = (lane & 3) ^ ((lane >> 4) & 3);
+    const int a_row0 = wave * COPIES * 16 + (lane >> 2);
+    const uint16_t *a_src = A + (int64_t)(m0 + a_row0) * p.lda + a_c * 8;
+    const int64_t a_jstep = (int64_t)16 * p.lda;
+    // B copy j of this wave: k-row (wave*4 + j)*2 + lane/32; the lane's 16
+    // bytes hold logical unit (((lane%32)/2) ^ (k%4)), half (lane%2).
+    const int b_kr0 = wave * COPIES * 2 + (lane >> 5);
+    const uint32_t as_base = lds_addr(&As[0][0]), bs_base = lds_addr(&Bs[0][0]);
+
+    auto issue = [&](int buf, int k0) {
+        const uint32_t as = as_base + buf * (A_STAGE * 2), bs = bs_base + buf * (B_STAGE * 2);
+#pragma unroll
+        for (int j = 0; j < COPIES; ++j) {
+            const uint32_t dst = as + (wave * COPIES + j) * 1024;
+            if (m0 + a_row0 + j * 16 < M && k0 + a_c * 8 < K)
+                lds_dma_16(a_src + j * a_jstep + k0, dst);
+            else
+                lds_zero_16(dst + lane * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < COPIES; ++j) {
+            const int kr = b_kr0 + j * 2;
+            const uint32_t dst = bs + (wave * COPIES + j) * 1024;
+            const int u = ((lane & 31) >> 1) ^ (kr & 3);
+            const int col = n0 + u * 16 + (lane & 1) * 8;
+            if (k0 + kr < K && col < N)
+                lds_dma_16(B + (int64_t)(k0 + kr) * p.ldb + col, dst);
+            else
+                lds_zero_16(dst + lane * 16);
+        }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.0f;
+
+    const int h = lane >> 5, l32 = lane & 31;
+    const int g_lo = (lane >> 4) & 1, j16 = lane & 15;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+    // Operands of k-step s (k = 16s + 8h + 0..7) of the stage in buffer buf.
+    auto read_step = [&](int buf, int s, f16x8 (&af)[FM], f16x8 (&bf)[FN]) {
+        const uint16_t *as = As[buf];
+        const uint16_t *bs = Bs[buf];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int row = wm * WTM + fm * 32 + l32;
+            const int c = (2 * s + h) ^ ((row >> 2) & 3);
+            af[fm] = *reinterpret_cast<const f16x8 *>(&as[row * BK + c * 8]);
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int n = wn * WTN + fn * 32 + g_lo * 16 + 4 * (j16 & 3);
+            s16x4 v[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int k = 16 * s + 8 * h + 4 * e + (j16 >> 2);
+                const int addr = k * BN + (((n >> 4) ^ (k & 3)) << 4) + (n & 15);
+                v[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(lds_addr(&bs[addr])));
+            }
+            const s16x4 lo = v[0], hi = v[1];
+            bf[fn] = __builtin_bit_cast(f16x8, (short __attribute__((ext_vector_type(8)))){
+                lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+    };
+    auto mfma_step = [&](const f16x8 (&af)[FM], const f16x8 (&bf)[FN]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    for (int st = 0; st < NBUF - 1; ++st)
+        if (st < nk)
+            issue(st, st * BK);
+    // stages 0 and 1 must have landed; stage 2 may still be in flight
+    if (nk > 2)
+        __builtin_amdgcn_s_waitcnt(LL_VMCNT(PER_STAGE));
+    else
+        __builtin_amdgcn_s_waitcnt(LL_VMCNT(0));
+    __syncthreads();
+
+    f16x8 a0[FM], b0[FN];
+    read_step(0, 0, a0, b0);
+    int buf = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool more = kt + 1 < nk;
+        const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+        if (kt + 3 < nk)
+            issue(buf == 0 ? NBUF - 1 : buf - 1, (kt + 3) * BK);   // stage kt-1's buffer
+        f16x8 a1[FM], b1[FN];
+        read_step(buf, 1, a1, b1);
+        mfma_step(a0, b0);
+        // First operands of stage kt+1, published by the last barrier. Read
+        // unconditionally (on the last stage they are stale, in-bounds and
+        // unused) so that no control-flow join makes the compiler's LDS wait
+        // counts conservative for the MFMAs below.
+        read_step(nbuf, 0, a0, b0);
+        mfma_step(a1, b1);
+        if (more) {
+            // publish stage kt+2 (stage kt+3 may still be in flight); after this
+            // barrier every wave is done with stage kt's buffer
+            if (kt + 3 < nk)
+                __builtin_amdgcn_s_waitcnt(LL_VMCNT(PER_STAGE));
+            else
+                __builtin_amdgcn_s_waitcnt(LL_VMCNT(0));
+            __syncthreads();
+        }
+        buf = nbuf;
+    }
+
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            write_block<EPI>(p, acc[fm][fn], m0 + wm * WTM + fm * 32, n0 + wn * WTN + fn * 32, lane);
+}
+
 using F16_L = F16Tile<256, 256, 64>;
 using F16_S = F16Tile<128, 128, 64>;
 using F16_XS = F16Tile<64, 64, 64>;
@@ -244,15 +420,33 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // {BM, BN, workgroups per CU, relative throughput alone, paired} (see the
 // FP32 table); measured on the 8192^3 product.
 const TileInfo kF16Tiles[kF16NumTiles] = {
-    {F16_L::BM, F16_L::BN, 1, 1.00f, 1.00f, "f16_256x256x64"},
-    {F16_S::BM, F16_S::BN, 2, 0.60f, 0.79f, "f16_128x128x64"},
-    {F16_XS::BM, F16_XS::BN, 2, 0.25f, 0.32f, "f16_64x64x64"},
+    {F16_L::BM, F16_L::BN, 1, 1.00f, 1.00f, "f16_256x256x32"},
+    {F16_S::BM, F16_S::BN, 2, 0.52f, 0.68f, "f16_128x128x64"},
+    {F16_XS::BM, F16_XS::BN, 2, 0.22f, 0.28f, "f16_64x64x64"},
 };
+
+static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStream_t s)
+{
+    if (!vec)
+        return launch_t<F16_L, 1>(p0, epi, vec, s);
+    GemmParams p = p0;
+    p.tiles_m = (p.M + 255) / 256;
+    p.tiles_n = (p.N + 255) / 256;
+    const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (ntiles > 0x7fffffff)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)ntiles), block(256);
+    if (epi == EPI_GEMM_BETA0)
+        hipLaunchKernelGGL(gemm_f16_direct_kernel<EPI_GEMM_BETA0>, grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL(gemm_f16_direct_kernel<EPI_GEMM_BETA>, grid, block, 0, s, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm_f16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
 {
     switch (tile) {
-    case 0: return launch_t<F16_L, 1>(p, epi, vec, s);
+    case 0: return launch_direct(p, epi, vec, s);
     case 1: return launch_t<F16_S, 2>(p, epi, vec, s);
     default: return launch_t<F16_XS, 2>(p, epi, vec, s);
     }

@@ -114,7 +114,7 @@ def test_tile_choice():
     f32, f16 = ll.DTYPE_F32, ll.DTYPE_F16
     names32 = [ll.tile_name(f32, t) for t in range(ll.num_tiles(f32))]
     names16 = [ll.tile_name(f16, t) for t in range(ll.num_tiles(f16))]
-    assert names32[0] == "f32_256x256x16" and names16[0] == "f16_256x256x64"
+    assert names32[0] == "f32_256x256x16" and names16[0] == "f16_256x256x32"
     assert ll.tile_name(f32, 99) == "" and ll.num_tiles(7) == 0
     # 4096^2 on 256 CUs: two 256x128 tiles per CU, paired (one workgroup covers
     # the other's waits)
@@ -125,7 +125,7 @@ def test_tile_choice():
     assert names32[ll.chosen_tile(f32, 4096, 4096, 64)] in names32
     # small problems use small tiles so more CUs work
     assert names32[ll.chosen_tile(f32, 1024, 1024, 256)] == "f32_64x64x16"
-    assert names16[ll.chosen_tile(f16, 8192, 8192, 256)] == "f16_256x256x64"
+    assert names16[ll.chosen_tile(f16, 8192, 8192, 256)] == "f16_256x256x32"
     ll.set_tile(f32, 2)
     try:
         assert ll.chosen_tile(f32, 4096, 4096, 256) == 2
