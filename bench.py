@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gemm_f32_4096")
     ap.add_argument("--tile", type=int, default=-1, help="force a tile shape (-1: automatic)")
+    ap.add_argument("--split-k", type=int, default=-1, help="force the K-split count (-1: automatic)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -164,8 +165,11 @@ def main():
     dtype_id = ll.DTYPE_F16 if w.kind == "gemm_f16f32" else ll.DTYPE_F32
     if args.tile >= 0:
         ll.set_tile(dtype_id, args.tile)
+    if args.split_k >= 1:
+        ll.set_split_k(args.split_k)
     props = torch.cuda.get_device_properties(dev)
-    tile = ll.chosen_tile(dtype_id, w.M, w.N, props.multi_processor_count)
+    tile = ll.chosen_tile(dtype_id, w.M, w.N, w.K, props.multi_processor_count)
+    splits = ll.chosen_split_k(dtype_id, w.M, w.N, w.K, props.multi_processor_count)
 
     def step():
         if w.kind == "gemm_f32":
@@ -223,7 +227,7 @@ def main():
         "config": {
             "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
             **({"act": "relu" if w.act == 1 else "none", "bias": True} if w.kind == "linear" else {}),
-            "tile": ll.tile_name(dtype_id, tile),
+            "tile": ll.tile_name(dtype_id, tile), "split_k": splits,
             "device": props.name, "cus": props.multi_processor_count,
         },
         "pct_of_peak": round(100.0 * value / peak, 2),

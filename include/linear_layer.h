@@ -113,11 +113,20 @@ int linear_bias_act(int M, int N, int K,
 const char *ll_status_string(int status);
 
 /*
- * Tile selection. Each data type has a small set of block-tile shapes; by
- * default the library picks one per call from M, N and the CU count so that
- * large problems get the largest tiles and smaller ones do not leave CUs idle
- * (the size-dependent strategy of page "GEMM 优化详解", section
- * "矩阵大小选择策略" (matrix-size strategy), re-derived for 256 CUs).
+ * Tile and K-split selection. Each data type has a small set of block-tile
+ * shapes; by default the library picks, per call, a tile shape and a number
+ * of K-splits from M, N, K and the CU count, minimising an estimate of the
+ * run time: large problems get the largest tiles, and problems too small to
+ * fill the device get smaller tiles or several workgroups along K (the
+ * size-dependent strategy of page "GEMM 优化详解", section "矩阵大小选择策略"
+ * (matrix-size strategy), re-derived for 256 CUs).
+ *
+ * With K-splits (split-K), each split computes alpha * A[:, Ks] * B[Ks, :]
+ * for its range Ks of K and adds it into C with hardware FP32 atomics, after
+ * a pass that scales C by beta (for linear_bias_act: fills Y with the bias,
+ * then applies the ReLU in a pass afterwards). The result is the same sum in
+ * a different, run-dependent order; it still allocates nothing.
+ *
  * These calls let a benchmark or a caller pin the choice. They touch only
  * host memory and never the GPU.
  */
@@ -132,9 +141,15 @@ const char *ll_tile_name(int dtype, int tile);
  * -1 restores the automatic choice. Process-wide, thread-safe.
  * Returns LL_OK or LL_ERR_INVALID_VALUE. */
 int ll_set_tile(int dtype, int tile);
-/* The tile the library would use for an M-by-N output on a device with
- * num_cus compute units (num_cus <= 0: 256), honouring ll_set_tile. */
-int ll_chosen_tile(int dtype, int M, int N, int num_cus);
+/* Force `splits` K-splits (1 .. 16; the split length is rounded up to a
+ * multiple of 64, so small K may use fewer) for every later call of any dtype;
+ * -1 restores the automatic choice. Returns LL_OK or LL_ERR_INVALID_VALUE. */
+int ll_set_split_k(int splits);
+/* The tile / the number of K-splits the library would use for an M-by-N
+ * output with inner dimension K on a device with num_cus compute units
+ * (num_cus <= 0: 256), honouring the overrides. -1 for an unknown dtype. */
+int ll_chosen_tile(int dtype, int M, int N, int K, int num_cus);
+int ll_chosen_split_k(int dtype, int M, int N, int K, int num_cus);
 
 #ifdef __cplusplus
 }

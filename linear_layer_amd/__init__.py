@@ -23,6 +23,7 @@ import os
 __all__ = [
     "LinearLayerError", "gemm_f32", "gemm_f16f32", "linear_bias_act", "status_string",
     "library_path", "load", "set_tile", "num_tiles", "tile_name", "chosen_tile",
+    "set_split_k", "chosen_split_k",
     "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16",
     "OK", "ERR_INVALID_VALUE", "ERR_NO_DEVICE", "ERR_UNSUPPORTED_ARCH", "ERR_LAUNCH",
 ]
@@ -37,7 +38,8 @@ _lib = None
 
 # Every symbol the C header declares.
 EXPORTED = ("gemm_f32", "gemm_f16f32", "linear_bias_act", "ll_status_string",
-            "ll_num_tiles", "ll_tile_name", "ll_set_tile", "ll_chosen_tile")
+            "ll_num_tiles", "ll_tile_name", "ll_set_tile", "ll_chosen_tile",
+            "ll_set_split_k", "ll_chosen_split_k")
 
 
 class LinearLayerError(RuntimeError):
@@ -72,8 +74,12 @@ def load():
     lib.ll_tile_name.restype = ctypes.c_char_p
     lib.ll_set_tile.argtypes = [i32, i32]
     lib.ll_set_tile.restype = i32
-    lib.ll_chosen_tile.argtypes = [i32, i32, i32, i32]
+    lib.ll_chosen_tile.argtypes = [i32, i32, i32, i32, i32]
     lib.ll_chosen_tile.restype = i32
+    lib.ll_chosen_split_k.argtypes = [i32, i32, i32, i32, i32]
+    lib.ll_chosen_split_k.restype = i32
+    lib.ll_set_split_k.argtypes = [i32]
+    lib.ll_set_split_k.restype = i32
     _lib = lib
     return lib
 
@@ -99,8 +105,17 @@ def tile_name(dtype: int, tile: int) -> str:
     return load().ll_tile_name(int(dtype), int(tile)).decode()
 
 
-def chosen_tile(dtype: int, M: int, N: int, num_cus: int = 0) -> int:
-    return load().ll_chosen_tile(int(dtype), int(M), int(N), int(num_cus))
+def chosen_tile(dtype: int, M: int, N: int, K: int, num_cus: int = 0) -> int:
+    return load().ll_chosen_tile(int(dtype), int(M), int(N), int(K), int(num_cus))
+
+
+def set_split_k(splits: int) -> None:
+    """Force the number of K-splits (1..16) for later calls; -1 = automatic."""
+    _check(load().ll_set_split_k(int(splits)), "ll_set_split_k")
+
+
+def chosen_split_k(dtype: int, M: int, N: int, K: int, num_cus: int = 0) -> int:
+    return load().ll_chosen_split_k(int(dtype), int(M), int(N), int(K), int(num_cus))
 
 
 # ---- tensor marshalling ---------------------------------------------------

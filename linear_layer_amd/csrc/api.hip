@@ -104,49 +104,87 @@ int current_device(DevInfo *out)
     return out->status;
 }
 
-// ---- tile choice ----
+// ---- tile and K-split choice ----
 
 std::atomic<int> g_tile_override[2] = {{-1}, {-1}};  // [0] fp32, [1] fp16
+std::atomic<int> g_split_override{-1};
 
-// Estimated time of an M x N output with a tile shape: tiles are dealt
-// round-robin over the CUs, so the busiest CU gets ceil(tiles/CUs) of them.
-// With one workgroup per CU they run one after another at eff_alone; with two
-// they run in pairs at eff_paired (a pair takes twice a tile's work), and an
-// odd last one runs alone. The smallest estimate wins: big tiles for big
-// problems, smaller ones when big tiles would leave CUs idle (wave
-// quantisation) -- the size-dependent choice of page "GEMM 优化详解",
-// section "矩阵大小选择策略", re-derived for 256 CUs.
-double tile_cost(const TileInfo &t, int M, int N, int cus)
+constexpr int kSplitAlign = 64;     // K per split is a multiple of every kernel's stage depth
+constexpr int kMaxSplits = 16;
+
+// Work units are multiply-adds on one CU at the 256x256 tile's throughput;
+// at the FP32 matrix peak one CU does 157.3e12 / 2 / 256 = 307e3 of them per
+// microsecond.
+constexpr double kUnitsPerUs = 307e3;
+
+// Estimated time of a launch with `wgs` workgroups of `work` units each: the
+// dispatcher deals workgroups round-robin, so the busiest CU gets
+// ceil(wgs/CUs). With one workgroup per CU they run one after another at
+// eff_alone; with two they run in pairs at eff_paired (a pair takes twice a
+// workgroup's work), and an odd last one runs alone.
+double wg_cost(const TileInfo &t, int64_t wgs, double work, int cus)
 {
-    const int64_t tiles = (int64_t)((M + t.bm - 1) / t.bm) * ((N + t.bn - 1) / t.bn);
-    const int64_t per_cu = (tiles + cus - 1) / cus;
-    const double work = (double)t.bm * t.bn;
+    const int64_t per_cu = (wgs + cus - 1) / cus;
     if (t.wg_per_cu <= 1 || per_cu == 1)
         return per_cu * work / t.eff_alone;
     const int64_t pairs = per_cu / 2, single = per_cu % 2;
     return pairs * 2.0 * work / t.eff_paired + single * work / t.eff_alone;
 }
 
-int pick_tile(const TileInfo *tiles, int n, int M, int N, int cus)
+struct Plan {
+    int tile;
+    int splits;
+    int k_split;
+};
+
+// Choose the tile shape and the number of K-splits minimising the estimate:
+// big tiles for big problems; smaller ones, or several workgroups along K
+// whose partial sums are added atomically into C, when big tiles would leave
+// CUs idle (wave quantisation). This is the size-dependent choice of page
+// "GEMM 优化详解", section "矩阵大小选择策略", re-derived for 256 CUs.
+// A split costs a pre-pass over C (beta*C, or the bias), the atomic traffic of
+// every split's partial tile and, for ReLU, a pass afterwards.
+Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int cus, bool relu)
 {
-    int best = 0;
+    const int t_ov = g_tile_override[dtype].load(std::memory_order_relaxed);
+    const int s_ov = g_split_override.load(std::memory_order_relaxed);
+    Plan best{0, 1, K};
     double best_cost = 0.0;
-    for (int t = 0; t < n; ++t) {
-        const double cost = tile_cost(tiles[t], M, N, cus);
-        if (t == 0 || cost < best_cost) {
-            best = t;
-            best_cost = cost;
+    bool have = false;
+    for (int t = 0; t < ntiles; ++t) {
+        if (t_ov >= 0 && t != t_ov)
+            continue;
+        const TileInfo &ti = tiles[t];
+        const int64_t tiles_mn = (int64_t)((M + ti.bm - 1) / ti.bm) * ((N + ti.bn - 1) / ti.bn);
+        for (int s = 1; s <= kMaxSplits; ++s) {
+            if (s_ov >= 1 && s != s_ov)
+                continue;
+            if (s_ov < 1 && s > 1 && (int64_t)K < (int64_t)s * kSplitAlign)
+                break;
+            int k_split = K;
+            int splits = 1;
+            if (s > 1) {
+                k_split = (int)((((int64_t)K + s - 1) / s + kSplitAlign - 1) / kSplitAlign * kSplitAlign);
+                splits = (int)(((int64_t)K + k_split - 1) / k_split);
+                if (splits != s && s_ov < 1)
+                    continue;   // the same partition is reached with fewer splits
+            }
+            double cost = wg_cost(ti, tiles_mn * splits, (double)ti.bm * ti.bn * k_split, cus);
+            if (splits > 1) {
+                const double mn = (double)M * N;
+                const double bytes = 8.0 * mn * (relu ? 2 : 1) + 4.0 * mn * splits;
+                cost += ((relu ? 6.0 : 3.0) + bytes / 3.0e6) * kUnitsPerUs;
+            }
+            if (!have || cost < best_cost) {
+                best = Plan{t, splits, k_split};
+                best_cost = cost;
+                have = true;
+            }
         }
     }
+    if (best.k_split <= 0)
+        best.k_split = 1;
     return best;
-}
-
-int choose_tile(int dtype, int M, int N, int cus)
-{
-    const int ov = g_tile_override[dtype].load(std::memory_order_relaxed);
-    if (dtype == 0)
-        return (ov >= 0 && ov < kF32NumTiles) ? ov : pick_tile(kF32Tiles, kF32NumTiles, M, N, cus);
-    return (ov >= 0 && ov < kF16NumTiles) ? ov : pick_tile(kF16Tiles, kF16NumTiles, M, N, cus);
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? LL_OK : LL_ERR_LAUNCH; }
@@ -170,7 +208,25 @@ GemmParams make_params(int M, int N, int K, float alpha, const void *A, int lda,
     p.beta = beta;
     p.act = 0;
     p.group_m = 4;
+    p.k_split = K > 0 ? K : 1;
     return p;
+}
+
+typedef hipError_t (*launch_fn)(const GemmParams &, int, int, bool, hipStream_t);
+
+// One GEMM per plan: a single launch with the alpha/beta write-back, or, when
+// K is split, C = beta*C followed by the split launch adding alpha*partials.
+hipError_t run_gemm(GemmParams p, const Plan &pl, bool vec, hipStream_t s, launch_fn launch)
+{
+    if (pl.splits == 1)
+        return launch(p, pl.tile, p.beta == 0.0f ? EPI_GEMM_BETA0 : EPI_GEMM_BETA, vec, s);
+    if (p.beta != 1.0f) {
+        const hipError_t e = launch_scale(p.C, p.ldc, p.M, p.N, p.beta, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    p.k_split = pl.k_split;
+    return launch(p, pl.tile, EPI_ATOMIC, vec, s);
 }
 
 }  // namespace
@@ -193,9 +249,8 @@ int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const fl
     const bool vec = aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && lda % 4 == 0 &&
                      ldb % 4 == 0 && ldc % 4 == 0 && K % 4 == 0 && N % 4 == 0;
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    const int tile = choose_tile(0, M, N, dev.cus);
-    return launch_status(
-        launch_gemm_f32(p, tile, beta == 0.0f ? EPI_GEMM_BETA0 : EPI_GEMM_BETA, vec, s));
+    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false);
+    return launch_status(run_gemm(p, pl, vec, s, launch_gemm_f32));
 }
 
 int gemm_f16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
@@ -214,9 +269,8 @@ int gemm_f16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, co
     const bool vec = aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && lda % 8 == 0 &&
                      ldb % 8 == 0 && ldc % 4 == 0 && K % 8 == 0 && N % 8 == 0;
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    const int tile = choose_tile(1, M, N, dev.cus);
-    return launch_status(
-        launch_gemm_f16(p, tile, beta == 0.0f ? EPI_GEMM_BETA0 : EPI_GEMM_BETA, vec, s));
+    const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false);
+    return launch_status(run_gemm(p, pl, vec, s, launch_gemm_f16));
 }
 
 int linear_bias_act(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
@@ -243,8 +297,18 @@ int linear_bias_act(int M, int N, int K, const float *X, int ldx, const float *W
     GemmParams p = make_params(M, N, K, 1.0f, X, ldx, W, ldw, 0.0f, Y, ldy);
     p.bias = bias;
     p.act = act;
-    const int tile = choose_tile(0, M, N, dev.cus);
-    return launch_status(launch_gemm_f32(p, tile, EPI_LINEAR, vec, s));
+    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU);
+    if (pl.splits == 1)
+        return launch_status(launch_gemm_f32(p, pl.tile, EPI_LINEAR, vec, s));
+    // split-K: Y = bias, then every split adds its partial product, then ReLU
+    hipError_t e = launch_bias_fill(Y, ldy, M, N, bias, LL_ACT_NONE, s);
+    if (e == hipSuccess) {
+        p.k_split = pl.k_split;
+        e = launch_gemm_f32(p, pl.tile, EPI_ATOMIC, vec, s);
+    }
+    if (e == hipSuccess && act == LL_ACT_RELU)
+        e = launch_relu(Y, ldy, M, N, s);
+    return launch_status(e);
 }
 
 const char *ll_status_string(int status)
@@ -288,11 +352,30 @@ const char *ll_tile_name(int dtype, int tile)
     return "";
 }
 
-int ll_chosen_tile(int dtype, int M, int N, int num_cus)
+int ll_chosen_tile(int dtype, int M, int N, int K, int num_cus)
 {
-    if (dtype != LL_DTYPE_F32 && dtype != LL_DTYPE_F16)
-        return -1;
-    return choose_tile(dtype, M, N, num_cus > 0 ? num_cus : 256);
+    if (dtype == LL_DTYPE_F32)
+        return plan(0, kF32Tiles, kF32NumTiles, M, N, K, num_cus > 0 ? num_cus : 256, false).tile;
+    if (dtype == LL_DTYPE_F16)
+        return plan(1, kF16Tiles, kF16NumTiles, M, N, K, num_cus > 0 ? num_cus : 256, false).tile;
+    return -1;
+}
+
+int ll_chosen_split_k(int dtype, int M, int N, int K, int num_cus)
+{
+    if (dtype == LL_DTYPE_F32)
+        return plan(0, kF32Tiles, kF32NumTiles, M, N, K, num_cus > 0 ? num_cus : 256, false).splits;
+    if (dtype == LL_DTYPE_F16)
+        return plan(1, kF16Tiles, kF16NumTiles, M, N, K, num_cus > 0 ? num_cus : 256, false).splits;
+    return -1;
+}
+
+int ll_set_split_k(int splits)
+{
+    if (splits != -1 && (splits < 1 || splits > kMaxSplits))
+        return LL_ERR_INVALID_VALUE;
+    g_split_override.store(splits, std::memory_order_relaxed);
+    return LL_OK;
 }
 
 }  // extern "C"

@@ -20,6 +20,7 @@ enum Epi : int {
     EPI_GEMM_BETA0 = 0,  // C = alpha*acc            (C not read)
     EPI_GEMM_BETA = 1,   // C = alpha*acc + beta*C
     EPI_LINEAR = 2,      // Y = act(acc + bias[n])   (Y not read)
+    EPI_ATOMIC = 3,      // C += alpha*acc atomically (one K-split's share)
 };
 
 struct GemmParams {
@@ -33,7 +34,18 @@ struct GemmParams {
     int act;              // 0 none, 1 ReLU (EPI_LINEAR)
     int tiles_m, tiles_n; // output tiles along M and N
     int group_m;          // tile rows per group in the grouped ordering
+    int k_split;          // K per split (a multiple of 64); K itself when not split
 };
+
+// The K range of this workgroup: split blockIdx.y covers
+// [blockIdx.y*k_split, min(K, (blockIdx.y+1)*k_split)). Returns the offset;
+// `k_len` receives the length.
+__device__ __forceinline__ int split_range(const GemmParams &p, int &k_len)
+{
+    const int kb = blockIdx.y * p.k_split;
+    k_len = min(p.K - kb, p.k_split);
+    return kb;
+}
 
 // Workgroup id -> (tile_m, tile_n).
 //
@@ -125,6 +137,11 @@ __device__ __forceinline__ void write_block(const GemmParams &p, const f32x16 &a
         if (row < p.M) {
             float *dst = p.C + (int64_t)row * p.ldc + col;
             float v = acc[r];
+            if (EPI == EPI_ATOMIC) {
+                // split-K: every split adds its share; C was pre-scaled by beta
+                __hip_atomic_fetch_add(dst, p.alpha * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                continue;
+            }
             if (EPI == EPI_GEMM_BETA0) {
                 v = p.alpha * v;
             } else if (EPI == EPI_GEMM_BETA) {

@@ -1,7 +1,9 @@
-// Quick-return kernels for the degenerate cases of the GEMM definition
-// (page "GEMM 优化详解", section "GEMM 基础理论 / 数学定义"): when K == 0 or
-// alpha == 0 the product term vanishes and C = beta*C; for the fully-connected
-// layer with K == 0, Y = act(bias). Both are plain HBM-bound row sweeps.
+// Elementwise row sweeps (HBM-bound). They serve the degenerate cases of the
+// GEMM definition (page "GEMM 优化详解", section "GEMM 基础理论 / 数学定义"):
+// when K == 0 or alpha == 0 the product term vanishes and C = beta*C; for the
+// fully-connected layer with K == 0, Y = act(bias). They also frame a split-K
+// product: C = beta*C (or Y = bias) before the atomically added partial sums,
+// and the ReLU after them.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -31,6 +33,19 @@ __global__ void __launch_bounds__(256) bias_fill_kernel(float *Y, int64_t ldy, i
     }
 }
 
+// In-place ReLU (y <= 0 and NaN -> +0), the last step of a split-K
+// fully-connected layer whose partial sums were accumulated atomically.
+__global__ void __launch_bounds__(256) relu_kernel(float *Y, int64_t ldy, int M, int N)
+{
+    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
+        float *row = Y + m * ldy;
+        for (int n = threadIdx.x; n < N; n += blockDim.x) {
+            const float v = row[n];
+            row[n] = v > 0.0f ? v : 0.0f;
+        }
+    }
+}
+
 static unsigned rows_grid(int M)
 {
     return (unsigned)(M < 65536 ? M : 65536);
@@ -39,6 +54,12 @@ static unsigned rows_grid(int M)
 hipError_t launch_scale(float *C, int64_t ldc, int M, int N, float beta, hipStream_t s)
 {
     hipLaunchKernelGGL(scale_kernel, dim3(rows_grid(M)), dim3(256), 0, s, C, ldc, M, N, beta);
+    return hipGetLastError();
+}
+
+hipError_t launch_relu(float *Y, int64_t ldy, int M, int N, hipStream_t s)
+{
+    hipLaunchKernelGGL(relu_kernel, dim3(rows_grid(M)), dim3(256), 0, s, Y, ldy, M, N);
     return hipGetLastError();
 }
 

@@ -59,9 +59,11 @@ gemm_f16_kernel(GemmParams p)
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A);
-    const uint16_t *__restrict__ B = static_cast<const uint16_t *>(p.B);
-    const int M = p.M, N = p.N, K = p.K;
+    int K;
+    const int kb = split_range(p, K);
+    const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A) + kb;
+    const uint16_t *__restrict__ B = static_cast<const uint16_t *>(p.B) + (int64_t)kb * p.ldb;
+    const int M = p.M, N = p.N;
 
     // A chunk i of this thread: row a_r0 + i*A_RSTEP, 16-byte chunk a_c.
     const int a_c = tid % CPR;
@@ -259,9 +261,11 @@ gemm_f16_direct_kernel(GemmParams p)
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A);
-    const uint16_t *__restrict__ B = static_cast<const uint16_t *>(p.B);
-    const int M = p.M, N = p.N, K = p.K;
+    int K;
+    const int kb = split_range(p, K);
+    const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A) + kb;
+    const uint16_t *__restrict__ B = static_cast<const uint16_t *>(p.B) + (int64_t)kb * p.ldb;
+    const int M = p.M, N = p.N;
 
     // Copy sources. A copy j of this wave: rows (wave*4 + j)*16 + lane/4.
     const int a_c = (lane & 3) ^ ((lane >> 4) & 3);
@@ -403,15 +407,17 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > 0x7fffffff)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)ntiles), block(T::NT);
+    const dim3 grid((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split)), block(T::NT);
 #define LL_F16_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f16_kernel<T, E, V, WPE>), grid, block, 0, s, p)
     if (vec) {
         if (epi == EPI_GEMM_BETA0) LL_F16_LAUNCH(EPI_GEMM_BETA0, true);
-        else LL_F16_LAUNCH(EPI_GEMM_BETA, true);
+        else if (epi == EPI_GEMM_BETA) LL_F16_LAUNCH(EPI_GEMM_BETA, true);
+        else LL_F16_LAUNCH(EPI_ATOMIC, true);
     } else {
         if (epi == EPI_GEMM_BETA0) LL_F16_LAUNCH(EPI_GEMM_BETA0, false);
-        else LL_F16_LAUNCH(EPI_GEMM_BETA, false);
+        else if (epi == EPI_GEMM_BETA) LL_F16_LAUNCH(EPI_GEMM_BETA, false);
+        else LL_F16_LAUNCH(EPI_ATOMIC, false);
     }
 #undef LL_F16_LAUNCH
     return hipGetLastError();
@@ -435,11 +441,13 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > 0x7fffffff)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)ntiles), block(256);
+    const dim3 grid((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split)), block(256);
     if (epi == EPI_GEMM_BETA0)
         hipLaunchKernelGGL(gemm_f16_direct_kernel<EPI_GEMM_BETA0>, grid, block, 0, s, p);
-    else
+    else if (epi == EPI_GEMM_BETA)
         hipLaunchKernelGGL(gemm_f16_direct_kernel<EPI_GEMM_BETA>, grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL(gemm_f16_direct_kernel<EPI_ATOMIC>, grid, block, 0, s, p);
     return hipGetLastError();
 }
 

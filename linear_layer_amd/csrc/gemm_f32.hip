@@ -69,9 +69,11 @@ gemm_f32_kernel(GemmParams p)
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const float *__restrict__ A = static_cast<const float *>(p.A);
-    const float *__restrict__ B = static_cast<const float *>(p.B);
-    const int M = p.M, N = p.N, K = p.K;
+    int K;
+    const int kb = split_range(p, K);
+    const float *__restrict__ A = static_cast<const float *>(p.A) + kb;
+    const float *__restrict__ B = static_cast<const float *>(p.B) + (int64_t)kb * p.ldb;
+    const int M = p.M, N = p.N;
 
     // Fixed per-thread load assignment: A chunk i is row a_row(i), chunk a_c;
     // B chunk i is k-row b_k(i), column chunk b_c.
@@ -218,17 +220,19 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > 0x7fffffff)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)ntiles), block(T::NT);
+    const dim3 grid((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split)), block(T::NT);
 #define LL_F32_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE>), grid, block, 0, s, p)
     if (vec) {
         if (epi == EPI_GEMM_BETA0) LL_F32_LAUNCH(EPI_GEMM_BETA0, true);
         else if (epi == EPI_GEMM_BETA) LL_F32_LAUNCH(EPI_GEMM_BETA, true);
-        else LL_F32_LAUNCH(EPI_LINEAR, true);
+        else if (epi == EPI_LINEAR) LL_F32_LAUNCH(EPI_LINEAR, true);
+        else LL_F32_LAUNCH(EPI_ATOMIC, true);
     } else {
         if (epi == EPI_GEMM_BETA0) LL_F32_LAUNCH(EPI_GEMM_BETA0, false);
         else if (epi == EPI_GEMM_BETA) LL_F32_LAUNCH(EPI_GEMM_BETA, false);
-        else LL_F32_LAUNCH(EPI_LINEAR, false);
+        else if (epi == EPI_LINEAR) LL_F32_LAUNCH(EPI_LINEAR, false);
+        else LL_F32_LAUNCH(EPI_ATOMIC, false);
     }
 #undef LL_F32_LAUNCH
     return hipGetLastError();

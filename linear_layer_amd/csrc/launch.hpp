@@ -22,12 +22,15 @@ extern const TileInfo kF16Tiles[kF16NumTiles];
 
 // One GEMM launch. `tile` indexes kF32Tiles / kF16Tiles, `epi` is an Epi
 // value, `vec` selects the 128-bit-load kernels (the caller has checked
-// alignment and divisibility). Fills p.tiles_m / p.tiles_n itself.
+// alignment and divisibility). Fills p.tiles_m / p.tiles_n itself; the grid
+// has ceil(K / p.k_split) K-splits along y (EPI_ATOMIC when more than one).
 hipError_t launch_gemm_f32(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
 hipError_t launch_gemm_f16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
 
 // C = beta*C over an M x N matrix (beta == 0 writes zeros without reading C).
 hipError_t launch_scale(float *C, int64_t ldc, int M, int N, float beta, hipStream_t s);
+// In-place ReLU over an M x N matrix.
+hipError_t launch_relu(float *Y, int64_t ldy, int M, int N, hipStream_t s);
 // Y = act(bias) broadcast over M rows (bias may be nullptr: act(0)).
 hipError_t launch_bias_fill(float *Y, int64_t ldy, int M, int N, const float *bias, int act,
                             hipStream_t s);

@@ -116,26 +116,45 @@ def test_tile_choice():
     names16 = [ll.tile_name(f16, t) for t in range(ll.num_tiles(f16))]
     assert names32[0] == "f32_256x256x16" and names16[0] == "f16_256x256x32"
     assert ll.tile_name(f32, 99) == "" and ll.num_tiles(7) == 0
+
+    def choice(dt, M, N, K, cus=256):
+        names = names32 if dt == f32 else names16
+        return names[ll.chosen_tile(dt, M, N, K, cus)], ll.chosen_split_k(dt, M, N, K, cus)
+
     # 4096^2 on 256 CUs: two 256x128 tiles per CU, paired (one workgroup covers
-    # the other's waits)
-    assert names32[ll.chosen_tile(f32, 4096, 4096, 256)] == "f32_256x128x16"
+    # the other's waits); no K-split
+    assert choice(f32, 4096, 4096, 4096) == ("f32_256x128x16", 1)
     # 2047 x 11008: 256x256 tiles leave a partial second round; 256x128 fills better
-    assert names32[ll.chosen_tile(f32, 2047, 11008, 256)] == "f32_256x128x16"
-    # a device with fewer CUs moves the balance
-    assert names32[ll.chosen_tile(f32, 4096, 4096, 64)] in names32
-    # small problems use small tiles so more CUs work
-    assert names32[ll.chosen_tile(f32, 1024, 1024, 256)] == "f32_64x64x16"
-    assert names16[ll.chosen_tile(f16, 8192, 8192, 256)] == "f16_256x256x32"
+    assert choice(f32, 2047, 11008, 4096) == ("f32_256x128x16", 1)
+    assert choice(f16, 8192, 8192, 8192) == ("f16_256x256x32", 1)
+    # problems too small to fill 256 CUs use small tiles and split K
+    assert choice(f32, 1024, 1024, 1024)[1] > 1
+    assert choice(f32, 256, 256, 256) == ("f32_64x64x16", 4)
+    # short K is never split below 64 per split
+    assert choice(f32, 512, 512, 64)[1] == 1
+    assert choice(f32, 64, 64, 100)[1] <= 2
+    # a device with fewer CUs moves the balance towards bigger tiles
+    assert choice(f32, 4096, 4096, 4096, 64)[0] in names32
     ll.set_tile(f32, 2)
     try:
-        assert ll.chosen_tile(f32, 4096, 4096, 256) == 2
+        assert ll.chosen_tile(f32, 4096, 4096, 4096, 256) == 2
     finally:
         ll.set_tile(f32, -1)
-    assert ll.chosen_tile(f32, 4096, 4096, 256) == 1
+    ll.set_split_k(5)
+    try:
+        assert ll.chosen_split_k(f32, 4096, 4096, 4096, 256) == 5
+        assert ll.chosen_split_k(f32, 64, 64, 100, 256) == 2   # 100 = 64 + 36
+    finally:
+        ll.set_split_k(-1)
+    assert ll.chosen_tile(f32, 4096, 4096, 4096, 256) == 1
     with pytest.raises(ll.LinearLayerError):
         ll.set_tile(f32, 17)
     with pytest.raises(ll.LinearLayerError):
         ll.set_tile(5, 0)
+    with pytest.raises(ll.LinearLayerError):
+        ll.set_split_k(0)
+    with pytest.raises(ll.LinearLayerError):
+        ll.set_split_k(17)
 
 
 def test_binding_rejects_host_tensors():

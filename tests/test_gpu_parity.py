@@ -80,6 +80,13 @@ def tile():
         ll.set_tile(d, -1)
 
 
+@pytest.fixture
+def split():
+    """Force the K-split count for one test, restore the automatic choice after."""
+    yield ll.set_split_k
+    ll.set_split_k(-1)
+
+
 def run_gemm_f32(A, B, alpha=1.0, beta=0.0, C=None):
     Ad, Bd = A.to(DEV), B.to(DEV)
     Cd = (C.clone() if C is not None else torch.full((A.shape[0], B.shape[1]), float("nan"))).to(DEV)
@@ -234,6 +241,83 @@ def test_linear_integer_exact(t, tile):
     X, W, b = wl.integers((M, K), 26, -2, 2), wl.integers((K, N), 27, -2, 2), wl.integers((N,), 28, -4, 4)
     R, _ = oracle.linear(np32(X), np32(W), np32(b), 1)
     assert_exact(run_linear(X, W, b, 1), R, f"linear int tile {t}")
+
+
+# ---- split-K: partial products added atomically -----------------------------
+
+@pytest.mark.parametrize("t", T32)
+@pytest.mark.parametrize("S", [2, 3, 5])
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (1.5, 0.5), (-0.5, 1.0)])
+def test_f32_split_k(t, S, alpha, beta, tile, split):
+    tile(F32, t)
+    split(S)
+    M, N, K = 300, 260, 1000          # ragged in every dimension, K not a multiple of the split
+    A, B, C = rand((M, K), 40), rand((K, N), 41), rand((M, N), 42)
+    R, T = oracle.gemm(np32(A), np32(B), alpha, beta, np32(C))
+    got = run_gemm_f32(A, B, alpha, beta, C if beta != 0.0 else None)
+    assert_close(got, R, T, f"f32 split {S} tile {t}")
+
+
+@pytest.mark.parametrize("t", T32)
+@pytest.mark.parametrize("S", [2, 4])
+def test_f32_split_k_scalar_path(t, S, tile, split):
+    tile(F32, t)
+    split(S)
+    M, N, K = 97, 131, 517
+    A, B = rand((M, K), 43), rand((K, N), 44)
+    R, T = oracle.gemm(np32(A), np32(B))
+    assert_close(run_gemm_f32(A, B), R, T, f"f32 split scalar {S} tile {t}")
+
+
+@pytest.mark.parametrize("t", T16)
+@pytest.mark.parametrize("S", [2, 3])
+def test_f16_split_k(t, S, tile, split):
+    tile(F16, t)
+    split(S)
+    for (M, N, K), seed in (((257, 264, 520), 45), ((130, 70, 301), 46)):
+        A, B, C = wl.to_half(rand((M, K), seed)), wl.to_half(rand((K, N), seed + 1)), rand((M, N), seed + 2)
+        R, T = oracle.gemm(bits16(A), bits16(B), 1.5, 0.5, np32(C))
+        assert_close(run_gemm_f16(A, B, 1.5, 0.5, C), R, T, f"f16 split {S} tile {t} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("t", T32)
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_linear_split_k(t, act, with_bias, tile, split):
+    tile(F32, t)
+    split(3)
+    M, N, K = 200, 300, 700
+    X, W = rand((M, K), 47, 1 / 16), rand((K, N), 48, 1 / 16)
+    b = wl.bias_uniform(N, 49) if with_bias else None
+    R, T = oracle.linear(np32(X), np32(W), None if b is None else np32(b), act)
+    Y = run_linear(X, W, b, act)
+    assert_close(Y, R, T, f"linear split tile {t} act {act} bias {with_bias}")
+    if act == 1:
+        assert not np.any(np.signbit(Y))
+
+
+@pytest.mark.parametrize("S", [2, 7, 16])
+def test_split_k_integer_exact(S, split):
+    split(S)
+    M, N, K = 190, 210, 1500
+    A, B, C = wl.integers((M, K), 50, -2, 2), wl.integers((K, N), 51, -2, 2), wl.integers((M, N), 52, -4, 4)
+    R, _ = oracle.gemm(np32(A), np32(B), 1.5, 0.5, np32(C))
+    assert_exact(run_gemm_f32(A, B, 1.5, 0.5, C), R, f"f32 int split {S}")
+    Ah, Bh = wl.to_half(wl.integers((M, K), 53, -8, 8)), wl.to_half(wl.integers((K, N), 54, -8, 8))
+    R, _ = oracle.gemm(bits16(Ah), bits16(Bh))
+    assert_exact(run_gemm_f16(Ah, Bh), R, f"f16 int split {S}")
+    X, W, b = wl.integers((M, K), 55, -2, 2), wl.integers((K, N), 56, -2, 2), wl.integers((N,), 57, -4, 4)
+    R, _ = oracle.linear(np32(X), np32(W), np32(b), 1)
+    assert_exact(run_linear(X, W, b, 1), R, f"linear int split {S}")
+
+
+def test_split_k_beta_zero_ignores_nan(split):
+    split(4)
+    M, N, K = 100, 120, 640
+    A, B = rand((M, K), 58), rand((K, N), 59)
+    R, T = oracle.gemm(np32(A), np32(B), 2.0, 0.0)
+    got = run_gemm_f32(A, B, 2.0, 0.0)   # C prefilled with NaN
+    assert_close(got, R, T, "split NaN prefill")
 
 
 # ---- degenerate cases and the write-back contract ---------------------------
