@@ -29,11 +29,12 @@ sys.path.insert(0, ROOT)
 COPY_BYTES = 256 << 20
 
 # Published MI355X dense matrix peaks (TFLOP/s).
-PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "gemm_f16f32": 2516.6}
+PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "gemm_f16f32": 2516.6, "gemm_bf16f32": 2516.6}
 KERNEL_SOURCES = {
     "gemm_f32": ["gemm_f32.hip", "common.hpp"],
     "linear": ["gemm_f32.hip", "common.hpp"],
     "gemm_f16f32": ["gemm_f16.hip", "common.hpp"],
+    "gemm_bf16f32": ["gemm_f16.hip", "common.hpp"],
 }
 
 
@@ -103,7 +104,7 @@ def cpu_baseline(w, x, target_s: float):
 
     A = x["A"]
     B = x["B"]
-    if w.kind == "gemm_f16f32":
+    if w.kind in ("gemm_f16f32", "gemm_bf16f32"):
         A, B = wl.half_bits(A), wl.half_bits(B)
     else:
         A, B = A.numpy(), B.numpy()
@@ -115,7 +116,8 @@ def cpu_baseline(w, x, target_s: float):
         if w.kind == "linear":
             oracle.linear(A[:rows], B, bias, w.act)
         else:
-            oracle.gemm(A[:rows], B, w.alpha, w.beta, None if C is None else C[:rows])
+            oracle.gemm(A[:rows], B, w.alpha, w.beta, None if C is None else C[:rows],
+                        bf16=w.kind == "gemm_bf16f32")
         return time.perf_counter() - t0
 
     rows = min(8, w.M)
@@ -162,7 +164,7 @@ def main():
     if "C" in x:
         C.copy_(x["C"].to(dev))
     bias = x["bias"].to(dev) if "bias" in x else None
-    dtype_id = ll.DTYPE_F16 if w.kind == "gemm_f16f32" else ll.DTYPE_F32
+    dtype_id = ll.DTYPE_F16 if w.kind in ("gemm_f16f32", "gemm_bf16f32") else ll.DTYPE_F32
     if args.tile >= 0:
         ll.set_tile(dtype_id, args.tile)
     if args.split_k >= 1:
@@ -176,6 +178,8 @@ def main():
             ll.gemm_f32(A, B, C, w.alpha, w.beta)
         elif w.kind == "gemm_f16f32":
             ll.gemm_f16f32(A, B, C, w.alpha, w.beta)
+        elif w.kind == "gemm_bf16f32":
+            ll.gemm_bf16f32(A, B, C, w.alpha, w.beta)
         else:
             ll.linear_bias_act(A, B, bias, w.act, C)
 
@@ -209,7 +213,8 @@ def main():
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, x, args.cpu_seconds)
 
-    dtype = {"gemm_f32": "f32", "linear": "f32", "gemm_f16f32": "f16 in, f32 accumulate"}[w.kind]
+    dtype = {"gemm_f32": "f32", "linear": "f32", "gemm_f16f32": "f16 in, f32 accumulate",
+             "gemm_bf16f32": "bf16 in, f32 accumulate"}[w.kind]
     out = {
         "metric": "TFLOPS (2MNK/t) for 4096^3 FP32 GEMM on 1 MI355X; % of matrix peak"
         if w.name == "gemm_f32_4096" else f"TFLOPS (2MNK/t), {w.name}",

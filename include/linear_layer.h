@@ -88,6 +88,24 @@ int gemm_f16f32(int M, int N, int K, float alpha,
                 float beta, float *C, int ldc, void *stream);
 
 /*
+ * gemm_bf16f32 — C = alpha * A * B + beta * C with bfloat16 A and B, FP32
+ * accumulation and FP32 C.
+ *
+ * Page "GEMM 优化详解", section "进一步优化方向" (further directions),
+ * item "Tensor Core (WMMA)": the matrix units take FP16 or BF16 inputs. Same
+ * product as gemm_f16f32 with the inputs in bfloat16 (1 sign, 8 exponent,
+ * 7 fraction bits) instead of binary16.
+ *
+ *   A  M-by-K bfloat16 bit patterns (uint16_t), lda >= max(1, K).
+ *   B  K-by-N bfloat16 bit patterns, ldb >= max(1, N).
+ * Every other argument, rule and error as gemm_f16f32 (same kernels and tile
+ * shapes, selected by LL_DTYPE_F16 below).
+ */
+int gemm_bf16f32(int M, int N, int K, float alpha,
+                 const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                 float beta, float *C, int ldc, void *stream);
+
+/*
  * linear_bias_act — Y = act(X * W + bias), the fused fully-connected layer.
  *
  * Page "GEMM 优化详解", table "为什么 GEMM 重要" (an FC layer is
@@ -131,7 +149,7 @@ const char *ll_status_string(int status);
  * host memory and never the GPU.
  */
 #define LL_DTYPE_F32 0 /* gemm_f32 and linear_bias_act */
-#define LL_DTYPE_F16 1 /* gemm_f16f32 */
+#define LL_DTYPE_F16 1 /* gemm_f16f32 and gemm_bf16f32 */
 
 /* Number of tile shapes for a data type (0 for an unknown dtype). */
 int ll_num_tiles(int dtype);

@@ -9,6 +9,7 @@ Entry points (same names as the C ABI in ``include/linear_layer.h``):
 
 * ``gemm_f32(A, B, C, alpha=1.0, beta=0.0)`` — C = alpha*A*B + beta*C, fp32.
 * ``gemm_f16f32(A, B, C, alpha=1.0, beta=0.0)`` — fp16 A, B; fp32 C.
+* ``gemm_bf16f32(A, B, C, alpha=1.0, beta=0.0)`` — bf16 A, B; fp32 C.
 * ``linear_bias_act(X, W, bias, act, Y)`` — Y = act(X*W + bias), fp32.
 
 Tensors are 2-D, row-major with unit column stride (a row stride larger than
@@ -21,7 +22,7 @@ import ctypes
 import os
 
 __all__ = [
-    "LinearLayerError", "gemm_f32", "gemm_f16f32", "linear_bias_act", "status_string",
+    "LinearLayerError", "gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "status_string",
     "library_path", "load", "set_tile", "num_tiles", "tile_name", "chosen_tile",
     "set_split_k", "chosen_split_k",
     "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16",
@@ -37,7 +38,7 @@ _LIB_PATH = os.path.join(_HERE, "liblinear_layer.so")
 _lib = None
 
 # Every symbol the C header declares.
-EXPORTED = ("gemm_f32", "gemm_f16f32", "linear_bias_act", "ll_status_string",
+EXPORTED = ("gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "ll_status_string",
             "ll_num_tiles", "ll_tile_name", "ll_set_tile", "ll_chosen_tile",
             "ll_set_split_k", "ll_chosen_split_k")
 
@@ -63,8 +64,9 @@ def load():
     i32, f32, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     lib.gemm_f32.argtypes = [i32, i32, i32, f32, vp, i32, vp, i32, f32, vp, i32, vp]
     lib.gemm_f16f32.argtypes = lib.gemm_f32.argtypes
+    lib.gemm_bf16f32.argtypes = lib.gemm_f32.argtypes
     lib.linear_bias_act.argtypes = [i32, i32, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp]
-    for f in (lib.gemm_f32, lib.gemm_f16f32, lib.linear_bias_act):
+    for f in (lib.gemm_f32, lib.gemm_f16f32, lib.gemm_bf16f32, lib.linear_bias_act):
         f.restype = i32
     lib.ll_status_string.argtypes = [i32]
     lib.ll_status_string.restype = ctypes.c_char_p
@@ -180,6 +182,11 @@ def gemm_f32(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
 def gemm_f16f32(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
     """C = alpha*A*B + beta*C with fp16 A, B and fp32 C; C returned."""
     return _gemm("gemm_f16f32", _torch().float16, A, B, C, alpha, beta, stream)
+
+
+def gemm_bf16f32(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    """C = alpha*A*B + beta*C with bf16 A, B and fp32 C; C returned."""
+    return _gemm("gemm_bf16f32", _torch().bfloat16, A, B, C, alpha, beta, stream)
 
 
 def linear_bias_act(X, W, bias, act: int, Y, stream=None):

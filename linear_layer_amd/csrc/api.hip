@@ -253,8 +253,9 @@ int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const fl
     return launch_status(run_gemm(p, pl, vec, s, launch_gemm_f32));
 }
 
-int gemm_f16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
-                int ldb, float beta, float *C, int ldc, void *stream)
+// Both 16-bit formats share the kernels, tiles and checks.
+static int gemm_16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+                   int ldb, float beta, float *C, int ldc, void *stream, launch_fn launch)
 {
     bool noop;
     int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 2, &noop);
@@ -270,7 +271,19 @@ int gemm_f16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, co
                      ldb % 8 == 0 && ldc % 4 == 0 && K % 8 == 0 && N % 8 == 0;
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false);
-    return launch_status(run_gemm(p, pl, vec, s, launch_gemm_f16));
+    return launch_status(run_gemm(p, pl, vec, s, launch));
+}
+
+int gemm_f16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+                int ldb, float beta, float *C, int ldc, void *stream)
+{
+    return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, launch_gemm_f16);
+}
+
+int gemm_bf16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+                 int ldb, float beta, float *C, int ldc, void *stream)
+{
+    return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, launch_gemm_bf16);
 }
 
 int linear_bias_act(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,

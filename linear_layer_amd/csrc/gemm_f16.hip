@@ -1,5 +1,5 @@
-// FP16-input GEMM with FP32 accumulation and FP32 output on the CDNA4 matrix
-// cores: C = alpha*A*B + beta*C with binary16 A and B.
+// 16-bit-input GEMM with FP32 accumulation and FP32 output on the CDNA4 matrix
+// cores: C = alpha*A*B + beta*C with binary16 or bfloat16 A and B.
 //
 // The FP16-in / FP32-accumulate product is the tensor-core step of page
 // "GPU架构下的矩阵乘法深入优化", section 6, in the general form of page
@@ -45,7 +45,21 @@ struct F16Tile {
 
 __device__ __forceinline__ uint16_t ld_u16(const uint16_t *p) { return *p; }
 
-template <class T, int EPI, bool VEC, int WPE>
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// The MFMA for the 16-bit input format: binary16 or bfloat16 operands,
+// 8 k-values per lane, FP32 accumulation. The operands are handled as raw
+// 16-bit patterns everywhere else.
+template <bool BF16>
+__device__ __forceinline__ f32x16 mma16(const f16x8 &a, const f16x8 &b, const f32x16 &c)
+{
+    if (BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+template <class T, int EPI, bool VEC, int WPE, bool BF16>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f16_kernel(GemmParams p)
 {
@@ -200,8 +214,7 @@ gemm_f16_kernel(GemmParams p)
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[fm], bf[fn],
-                                                                         acc[fm][fn], 0, 0, 0);
+                    acc[fm][fn] = mma16<BF16>(af[fm], bf[fn], acc[fm][fn]);
         }
         if (kt + 1 < nk)
             lstore(cur ^ 1);
@@ -243,7 +256,7 @@ gemm_f16_kernel(GemmParams p)
 // publishes stage kt+2, so during stage kt each wave already reads the first
 // operands of stage kt+1 and no LDS latency is exposed after a barrier; the
 // copies of stage kt+3 are issued into the buffer stage kt-1 used.
-template <int EPI>
+template <int EPI, bool BF16>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_f16_direct_kernel(GemmParams p)
 {
@@ -344,7 +357,7 @@ gemm_f16_direct_kernel(GemmParams p)
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[fm], bf[fn], acc[fm][fn], 0, 0, 0);
+                acc[fm][fn] = mma16<BF16>(af[fm], bf[fn], acc[fm][fn]);
     };
 
     const int nk = (K + BK - 1) / BK;
@@ -398,7 +411,7 @@ using F16_L = F16Tile<256, 256, 64>;
 using F16_S = F16Tile<128, 128, 64>;
 using F16_XS = F16Tile<64, 64, 64>;
 
-template <class T, int WPE>
+template <class T, int WPE, bool BF16>
 static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
     GemmParams p = p0;
@@ -409,7 +422,7 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split)), block(T::NT);
 #define LL_F16_LAUNCH(E, V) \
-    hipLaunchKernelGGL((gemm_f16_kernel<T, E, V, WPE>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((gemm_f16_kernel<T, E, V, WPE, BF16>), grid, block, 0, s, p)
     if (vec) {
         if (epi == EPI_GEMM_BETA0) LL_F16_LAUNCH(EPI_GEMM_BETA0, true);
         else if (epi == EPI_GEMM_BETA) LL_F16_LAUNCH(EPI_GEMM_BETA, true);
@@ -431,10 +444,11 @@ const TileInfo kF16Tiles[kF16NumTiles] = {
     {F16_XS::BM, F16_XS::BN, 2, 0.22f, 0.28f, "f16_64x64x64"},
 };
 
+template <bool BF16>
 static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
     if (!vec)
-        return launch_t<F16_L, 1>(p0, epi, vec, s);
+        return launch_t<F16_L, 1, BF16>(p0, epi, vec, s);
     GemmParams p = p0;
     p.tiles_m = (p.M + 255) / 256;
     p.tiles_n = (p.N + 255) / 256;
@@ -443,21 +457,32 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split)), block(256);
     if (epi == EPI_GEMM_BETA0)
-        hipLaunchKernelGGL(gemm_f16_direct_kernel<EPI_GEMM_BETA0>, grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_GEMM_BETA0, BF16>), grid, block, 0, s, p);
     else if (epi == EPI_GEMM_BETA)
-        hipLaunchKernelGGL(gemm_f16_direct_kernel<EPI_GEMM_BETA>, grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_GEMM_BETA, BF16>), grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL(gemm_f16_direct_kernel<EPI_ATOMIC>, grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_ATOMIC, BF16>), grid, block, 0, s, p);
     return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t launch_16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
+{
+    switch (tile) {
+    case 0: return launch_direct<BF16>(p, epi, vec, s);
+    case 1: return launch_t<F16_S, 2, BF16>(p, epi, vec, s);
+    default: return launch_t<F16_XS, 2, BF16>(p, epi, vec, s);
+    }
 }
 
 hipError_t launch_gemm_f16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
 {
-    switch (tile) {
-    case 0: return launch_direct(p, epi, vec, s);
-    case 1: return launch_t<F16_S, 2>(p, epi, vec, s);
-    default: return launch_t<F16_XS, 2>(p, epi, vec, s);
-    }
+    return launch_16<false>(p, tile, epi, vec, s);
+}
+
+hipError_t launch_gemm_bf16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
+{
+    return launch_16<true>(p, tile, epi, vec, s);
 }
 
 }  // namespace ll

@@ -7,16 +7,18 @@ the very same host arrays made here.
 Recipe: a ``torch.Generator('cpu')`` seeded with ``100*config + tensor``
 (tensor: A 0, B 1, C_in 2, bias 3), uniform values from ``2*rand - 1`` in
 fp32 (so [-1, 1)), the fully-connected operands scaled by 1/64 = 1/sqrt(4096)
-(exact in binary), the bias from ``0.2*rand - 0.1``, and fp16 operands rounded
-from the fp32 draw to nearest-even. Integer-valued variants draw from
+(exact in binary), the bias from ``0.2*rand - 0.1``, and fp16 / bf16 operands
+rounded from the fp32 draw to nearest-even. Integer-valued variants draw from
 ``randint`` and are converted to float exactly.
 
-The five workloads are those of the GEMM pages' measurements: square FP32
+The first five workloads are those of the GEMM pages' measurements: square FP32
 products (page "GPU架构下的矩阵乘法深入优化" measures 4096 cubed, page
 "GEMM 优化详解" 1024 cubed), the fully-connected layer of page
 "GEMM 优化详解" section "Level 6: Kernel Fusion" at a ragged batch, and the
 FP16-input / FP32-accumulate product of the tensor-core section of page
-"GPU架构下的矩阵乘法深入优化" (section 6).
+"GPU架构下的矩阵乘法深入优化" (section 6). The sixth is the same 16-bit
+product with bfloat16 inputs (page "GEMM 优化详解", "进一步优化方向": the
+matrix units take FP16 or BF16).
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ import torch
 class Workload:
     index: int          # 1-based workload number, also the seed base
     name: str
-    kind: str           # "gemm_f32", "gemm_f16f32" or "linear"
+    kind: str           # "gemm_f32", "gemm_f16f32", "gemm_bf16f32" or "linear"
     M: int
     N: int
     K: int
@@ -51,6 +53,8 @@ WORKLOADS = {
     "linear_relu_2047x4096x11008": Workload(4, "linear_relu_2047x4096x11008", "linear", 2047, 11008, 4096,
                                             act=1, scale=1.0 / 64.0),
     "gemm_f16f32_8192": Workload(5, "gemm_f16f32_8192", "gemm_f16f32", 8192, 8192, 8192),
+    # the bfloat16 variant of the 16-bit product (same shape, inputs rounded to bf16)
+    "gemm_bf16f32_8192": Workload(6, "gemm_bf16f32_8192", "gemm_bf16f32", 8192, 8192, 8192),
 }
 
 
@@ -83,8 +87,13 @@ def to_half(x: torch.Tensor) -> torch.Tensor:
     return x.to(torch.float16)
 
 
+def to_bf16(x: torch.Tensor) -> torch.Tensor:
+    """Round fp32 to bfloat16, nearest-even."""
+    return x.to(torch.bfloat16)
+
+
 def half_bits(x: torch.Tensor):
-    """The binary16 bit patterns of a float16 tensor as a uint16 numpy array."""
+    """The 16-bit patterns of a float16 or bfloat16 tensor as a uint16 numpy array."""
     return x.contiguous().view(torch.int16).numpy().view("uint16")
 
 
@@ -93,7 +102,7 @@ def make_inputs(w: Workload, integer: bool = False, M: int | None = None,
     """Host (CPU) input tensors for workload ``w``; sizes may be overridden.
 
     Returns a dict with A, B (and C for beta != 0, bias for linear). For fp16
-    workloads A and B are float16 tensors. ``integer=True`` gives the
+    and bf16 workloads A and B are float16 / bfloat16 tensors. ``integer=True`` gives the
     integer-valued variant whose exact result every summation order reaches:
     fp32 entries in [-2, 2], C_in and bias in [-4, 4], fp16 entries in [-8, 8].
     """
@@ -103,7 +112,7 @@ def make_inputs(w: Workload, integer: bool = False, M: int | None = None,
     s = 100 * w.index
     out = {}
     if integer:
-        lim = 8 if w.kind == "gemm_f16f32" else 2
+        lim = 8 if w.kind in ("gemm_f16f32", "gemm_bf16f32") else 2
         out["A"] = integers((M, K), s + 0, -lim, lim)
         out["B"] = integers((K, N), s + 1, -lim, lim)
         if w.beta != 0.0:
@@ -120,4 +129,7 @@ def make_inputs(w: Workload, integer: bool = False, M: int | None = None,
     if w.kind == "gemm_f16f32":
         out["A"] = to_half(out["A"])
         out["B"] = to_half(out["B"])
+    if w.kind == "gemm_bf16f32":
+        out["A"] = to_bf16(out["A"])
+        out["B"] = to_bf16(out["B"])
     return out

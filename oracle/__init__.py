@@ -53,15 +53,20 @@ def _load():
     vp = ctypes.c_void_p
     lib.oracle_gemm_f32.argtypes = [i64, i64, i64, f64, vp, i64, vp, i64, f64, vp, i64, vp, vp, i32]
     lib.oracle_gemm_f16.argtypes = lib.oracle_gemm_f32.argtypes
+    lib.oracle_gemm_bf16.argtypes = lib.oracle_gemm_f32.argtypes
     lib.oracle_linear.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i32, vp, vp, i32]
     lib.oracle_gemm_f32_at.argtypes = [i64, f64, vp, i64, vp, i64, f64, vp, i64, i64, vp, vp, vp, vp, i32]
     lib.oracle_gemm_f16_at.argtypes = lib.oracle_gemm_f32_at.argtypes
+    lib.oracle_gemm_bf16_at.argtypes = lib.oracle_gemm_f32_at.argtypes
     lib.oracle_linear_at.argtypes = [i64, vp, i64, vp, i64, vp, i32, i64, vp, vp, vp, vp, i32]
-    for f in (lib.oracle_gemm_f32, lib.oracle_gemm_f16, lib.oracle_linear,
-              lib.oracle_gemm_f32_at, lib.oracle_gemm_f16_at, lib.oracle_linear_at):
+    for f in (lib.oracle_gemm_f32, lib.oracle_gemm_f16, lib.oracle_gemm_bf16, lib.oracle_linear,
+              lib.oracle_gemm_f32_at, lib.oracle_gemm_f16_at, lib.oracle_gemm_bf16_at,
+              lib.oracle_linear_at):
         f.restype = None
     lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     lib.oracle_half_to_double.restype = f64
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_double.restype = f64
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = i32
     _lib = lib
@@ -98,11 +103,16 @@ def half_to_double(bits: int) -> float:
     return _load().oracle_half_to_double(int(bits) & 0xFFFF)
 
 
-def gemm(A, B, alpha=1.0, beta=0.0, C=None, nthreads=None):
+def bf16_to_double(bits: int) -> float:
+    """Decode one bfloat16 bit pattern (the oracle's own decoder)."""
+    return _load().oracle_bf16_to_double(int(bits) & 0xFFFF)
+
+
+def gemm(A, B, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=False):
     """R = alpha*A*B + beta*C for fp32 A (MxK), B (KxN); C read only if beta != 0.
 
-    A and B may instead be uint16 arrays of binary16 bit patterns (both of them),
-    which selects the fp16-input routine.
+    A and B may instead be uint16 arrays of 16-bit bit patterns (both of them):
+    binary16 by default, bfloat16 with ``bf16=True``.
     """
     lib = _load()
     half = np.asarray(A).dtype == np.uint16
@@ -121,7 +131,9 @@ def gemm(A, B, alpha=1.0, beta=0.0, C=None, nthreads=None):
         C, ldc = None, max(N, 1)
     R = np.empty((M, N), np.float64)
     T = np.empty((M, N), np.float64)
-    fn = lib.oracle_gemm_f16 if half else lib.oracle_gemm_f32
+    if bf16 and not half:
+        raise TypeError("bf16=True needs uint16 bit patterns")
+    fn = (lib.oracle_gemm_bf16 if bf16 else lib.oracle_gemm_f16) if half else lib.oracle_gemm_f32
     fn(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
        _ptr(R), _ptr(T), _threads(nthreads))
     return R, T
@@ -155,7 +167,7 @@ def _idx(rows, cols):
     return rows, cols
 
 
-def gemm_at(A, B, rows, cols, alpha=1.0, beta=0.0, C=None, nthreads=None):
+def gemm_at(A, B, rows, cols, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=False):
     """gemm() evaluated only at the positions (rows[p], cols[p])."""
     lib = _load()
     half = np.asarray(A).dtype == np.uint16
@@ -177,7 +189,9 @@ def gemm_at(A, B, rows, cols, alpha=1.0, beta=0.0, C=None, nthreads=None):
         C, ldc = None, max(N, 1)
     R = np.empty(rows.size, np.float64)
     T = np.empty(rows.size, np.float64)
-    fn = lib.oracle_gemm_f16_at if half else lib.oracle_gemm_f32_at
+    if bf16 and not half:
+        raise TypeError("bf16=True needs uint16 bit patterns")
+    fn = (lib.oracle_gemm_bf16_at if bf16 else lib.oracle_gemm_f16_at) if half else lib.oracle_gemm_f32_at
     fn(K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
        rows.size, _ptr(rows), _ptr(cols), _ptr(R), _ptr(T), _threads(nthreads))
     return R, T

@@ -8,8 +8,9 @@
  *
  * What it computes (float64 throughout, k summed in increasing order):
  *
- *   GEMM, page "GEMM 优化详解" (GEMM optimisation in detail), section
- *   "GEMM 基础理论 / 数学定义" (mathematical definition): the full form is
+ *   GEMM (fp32, binary16 or bfloat16 inputs), page "GEMM 优化详解" (GEMM
+ *   optimisation in detail), section "GEMM 基础理论 / 数学定义"
+ *   (mathematical definition): the full form is
  *   C = alpha*A*B + beta*C, with A M-by-K, B K-by-N, C M-by-N and
  *   C(m,n) = sum over k of A(m,k)*B(k,n). Page "第5章-基础Kernel" section 1.1
  *   gives the same sum with k running from 0 to K-1, and its section 7.1
@@ -25,9 +26,10 @@
  *   - beta == 0 means C is not read (so NaN in C does not propagate);
  *     alpha == 0 (or K == 0) means the result is beta*C and A, B are not read.
  *   - ReLU returns +0.0 for y <= 0.
- *   - Every product of two fp32 (24-bit) or two fp16 (11-bit) significands is
- *     exact in a double, so only the additions round; no fast-math may be
- *     used to build this file, because reassociating k changes the result.
+ *   - Every product of two fp32 (24-bit), binary16 (11-bit) or bfloat16
+ *     (8-bit) significands is exact in a double, so only the additions round;
+ *     no fast-math may be used to build this file, because reassociating k
+ *     changes the result.
  *
  * Besides the value r, every routine returns t = sum over k of |A(m,k)*B(k,n)|,
  * which is the basis of the parity tolerance |C_gpu - r| <= 1e-4 * t.
@@ -63,7 +65,26 @@ double oracle_half_to_double(uint16_t h)
     return sign ? -v : v;
 }
 
+/* bfloat16 to double, from the format's definition: 1 sign bit, 8 exponent
+ * bits (bias 127), 7 fraction bits; exponent 0 is subnormal (f * 2^-133),
+ * exponent 255 is infinity (f == 0) or NaN. */
+double oracle_bf16_to_double(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int e = (h >> 7) & 0xff;
+    const int f = h & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);
+    else if (e == 255)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f + 128), e - 134);
+    return sign ? -v : v;
+}
+
 static inline double ld_f32(const void *p, int64_t i) { return (double)((const float *)p)[i]; }
+static inline double ld_bf16(const void *p, int64_t i) { return oracle_bf16_to_double(((const uint16_t *)p)[i]); }
 static inline double ld_f16(const void *p, int64_t i) { return oracle_half_to_double(((const uint16_t *)p)[i]); }
 
 typedef double (*loader_fn)(const void *, int64_t);
@@ -233,6 +254,16 @@ void oracle_gemm_f16(int64_t M, int64_t N, int64_t K, double alpha,
     full_product(M, N, K, A, lda, ld_f16, B, ldb, ld_f16, &e, R, T, nthreads);
 }
 
+/* As oracle_gemm_f32 but A and B hold bfloat16 bit patterns. */
+void oracle_gemm_bf16(int64_t M, int64_t N, int64_t K, double alpha,
+                      const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                      double beta, const float *Cin, int64_t ldc,
+                      double *R, double *T, int nthreads)
+{
+    epilogue_t e = gemm_epi(alpha, beta, Cin, ldc);
+    full_product(M, N, K, A, lda, ld_bf16, B, ldb, ld_bf16, &e, R, T, nthreads);
+}
+
 /* Y = act(X*W + bias); bias may be NULL; act 0 = none, 1 = ReLU. */
 void oracle_linear(int64_t M, int64_t N, int64_t K,
                    const float *X, int64_t ldx, const float *W, int64_t ldw,
@@ -258,6 +289,15 @@ void oracle_gemm_f16_at(int64_t K, double alpha, const uint16_t *A, int64_t lda,
 {
     epilogue_t e = gemm_epi(alpha, beta, Cin, ldc);
     sampled_product(K, A, lda, ld_f16, B, ldb, ld_f16, &e, P, rows, cols, R, T, nthreads);
+}
+
+void oracle_gemm_bf16_at(int64_t K, double alpha, const uint16_t *A, int64_t lda,
+                         const uint16_t *B, int64_t ldb, double beta, const float *Cin,
+                         int64_t ldc, int64_t P, const int64_t *rows, const int64_t *cols,
+                         double *R, double *T, int nthreads)
+{
+    epilogue_t e = gemm_epi(alpha, beta, Cin, ldc);
+    sampled_product(K, A, lda, ld_bf16, B, ldb, ld_bf16, &e, P, rows, cols, R, T, nthreads);
 }
 
 void oracle_linear_at(int64_t K, const float *X, int64_t ldx, const float *W, int64_t ldw,

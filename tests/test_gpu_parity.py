@@ -103,6 +103,14 @@ def run_gemm_f16(A, B, alpha=1.0, beta=0.0, C=None):
     return np32(Cd)
 
 
+def run_gemm_bf16(A, B, alpha=1.0, beta=0.0, C=None):
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    Cd = (C.clone() if C is not None else torch.full((A.shape[0], B.shape[1]), float("nan"))).to(DEV)
+    ll.gemm_bf16f32(Ad, Bd, Cd, alpha, beta)
+    torch.cuda.synchronize()
+    return np32(Cd)
+
+
 def run_linear(X, W, b, act):
     Xd, Wd = X.to(DEV), W.to(DEV)
     bd = b.to(DEV) if b is not None else None
@@ -185,6 +193,36 @@ def test_f16_scalar_path(t, M, N, K, tile):
     C = rand((M, N), 14)
     R, T = oracle.gemm(bits16(A), bits16(B), 1.5, 0.5, np32(C))
     assert_close(run_gemm_f16(A, B, 1.5, 0.5, C), R, T, f"f16 scalar tile {t}")
+
+
+@pytest.mark.parametrize("t", T16)
+@pytest.mark.parametrize("M,N,K", [(600, 520, 192), (257, 264, 64), (33, 72, 40), (301, 517, 203)])
+def test_bf16_small(t, M, N, K, tile):
+    tile(F16, t)
+    A, B, C = wl.to_bf16(rand((M, K), 60)), wl.to_bf16(rand((K, N), 61)), rand((M, N), 62)
+    R, T = oracle.gemm(bits16(A), bits16(B), 1.5, 0.5, np32(C), bf16=True)
+    assert_close(run_gemm_bf16(A, B, 1.5, 0.5, C), R, T, f"bf16 tile {t} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("t", T16)
+def test_bf16_integer_exact(t, tile):
+    tile(F16, t)
+    M, N, K = 300, 280, 256
+    A = wl.to_bf16(wl.integers((M, K), 63, -8, 8))
+    B = wl.to_bf16(wl.integers((K, N), 64, -8, 8))
+    R, _ = oracle.gemm(bits16(A), bits16(B), bf16=True)
+    assert_exact(run_gemm_bf16(A, B), R, f"bf16 int tile {t}")
+
+
+def test_bf16_is_not_read_as_fp16():
+    # the same bits through both entry points give different products
+    M, N, K = 64, 64, 64
+    A, B = wl.to_bf16(rand((M, K), 65)), wl.to_bf16(rand((K, N), 66))
+    got = run_gemm_bf16(A, B)
+    R, T = oracle.gemm(bits16(A), bits16(B), bf16=True)
+    assert_close(got, R, T, "bf16")
+    R16, _ = oracle.gemm(bits16(A), bits16(B))
+    assert not np.allclose(got, R16)
 
 
 @pytest.mark.parametrize("t", T32)
@@ -278,6 +316,9 @@ def test_f16_split_k(t, S, tile, split):
         A, B, C = wl.to_half(rand((M, K), seed)), wl.to_half(rand((K, N), seed + 1)), rand((M, N), seed + 2)
         R, T = oracle.gemm(bits16(A), bits16(B), 1.5, 0.5, np32(C))
         assert_close(run_gemm_f16(A, B, 1.5, 0.5, C), R, T, f"f16 split {S} tile {t} {M}x{N}x{K}")
+        Ab, Bb = wl.to_bf16(rand((M, K), seed)), wl.to_bf16(rand((K, N), seed + 1))
+        R, T = oracle.gemm(bits16(Ab), bits16(Bb), 1.5, 0.5, np32(C), bf16=True)
+        assert_close(run_gemm_bf16(Ab, Bb, 1.5, 0.5, C), R, T, f"bf16 split {S} tile {t} {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("t", T32)
@@ -457,13 +498,15 @@ def test_full_linear():
     assert np.array_equal(got, np.where(got0 > 0, got0, np.float32(0)))
 
 
-def test_full_gemm_f16():
-    w = wl.WORKLOADS["gemm_f16f32_8192"]
+@pytest.mark.parametrize("name", ["gemm_f16f32_8192", "gemm_bf16f32_8192"])
+def test_full_gemm_16bit(name):
+    w = wl.WORKLOADS[name]
     x = wl.make_inputs(w)
     A, B = x["A"], x["B"]
-    got = run_gemm_f16(A, B)
+    bf = w.kind == "gemm_bf16f32"
+    got = (run_gemm_bf16 if bf else run_gemm_f16)(A, B)
     rows, cols = sample_positions(w.M, w.N, 20000, w.index)
-    R, T = oracle.gemm_at(bits16(A), bits16(B), rows, cols)
+    R, T = oracle.gemm_at(bits16(A), bits16(B), rows, cols, bf16=bf)
     ratio = assert_close(got[rows, cols], R, T, w.name)
     print(f"{w.name}: max err/t on samples = {ratio:.3g}")
     checksums(got, A.double().numpy(), B.double().numpy())
@@ -479,9 +522,10 @@ def test_full_integer_exact(name):
         got = run_gemm_f32(A, B, w.alpha, w.beta, x.get("C"))
         Cn = None if "C" not in x else np32(x["C"])
         R, _ = oracle.gemm_at(np32(A), np32(B), rows, cols, w.alpha, w.beta, Cn)
-    elif w.kind == "gemm_f16f32":
-        got = run_gemm_f16(A, B)
-        R, _ = oracle.gemm_at(bits16(A), bits16(B), rows, cols)
+    elif w.kind in ("gemm_f16f32", "gemm_bf16f32"):
+        bf = w.kind == "gemm_bf16f32"
+        got = (run_gemm_bf16 if bf else run_gemm_f16)(A, B)
+        R, _ = oracle.gemm_at(bits16(A), bits16(B), rows, cols, bf16=bf)
     else:
         got = run_linear(A, B, x["bias"], w.act)
         R, _ = oracle.linear_at(np32(A), np32(B), rows, cols, np32(x["bias"]), w.act)

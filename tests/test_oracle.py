@@ -181,6 +181,38 @@ def test_f16_against_numpy_float64():
     assert np.all(np.abs(R - ref) <= 2 * K * 2.0 ** -52 * T)
 
 
+def test_bf16_decoder_all_patterns():
+    # pinned to torch's bfloat16 -> float64 conversion on all 65536 patterns
+    import torch
+    bits = np.arange(65536, dtype=np.int64)
+    ref = torch.from_numpy(bits.astype(np.int16)).view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_integer_exact_and_numpy():
+    import torch
+    M, N, K = 36, 28, 300
+    Ai = rand_int(M, K, lo=-8, hi=8)
+    Bi = rand_int(K, N, lo=-8, hi=8)
+    A = torch.from_numpy(Ai).to(torch.bfloat16)
+    B = torch.from_numpy(Bi).to(torch.bfloat16)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    R, _ = oracle.gemm(bits(A), bits(B), bf16=True)
+    assert np.array_equal(R, (Ai.astype(np.int64) @ Bi.astype(np.int64)).astype(np.float64))
+    Af = torch.from_numpy(rand_f32(M, K)).to(torch.bfloat16)
+    Bf = torch.from_numpy(rand_f32(K, N)).to(torch.bfloat16)
+    R, T = oracle.gemm(bits(Af), bits(Bf), bf16=True)
+    ref = Af.double().numpy() @ Bf.double().numpy()
+    assert np.all(np.abs(R - ref) <= 2 * K * 2.0 ** -52 * T)
+    # the same bits read as binary16 give a different product: the flag matters
+    R16, _ = oracle.gemm(bits(Af), bits(Bf))
+    assert not np.allclose(R16, R)
+
+
 def test_half_decoder_all_patterns():
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     ref = bits.view(np.float16).astype(np.float64)
@@ -247,7 +279,7 @@ def test_ragged_rows_are_a_prefix():
     assert np.array_equal(L127, L128[:127])
 
 
-@pytest.mark.parametrize("kind", ["f32", "f16", "linear"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "bf16", "linear"])
 def test_blocked_equals_per_element_loop(kind):
     M, N, K = 40, 150, 77  # several row and column blocks, ragged both ways
     rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
@@ -260,8 +292,11 @@ def test_blocked_equals_per_element_loop(kind):
         A, B, C = rand_f32(M, K), rand_f32(K, N), rand_f32(M, N)
         if kind == "f16":
             A, B = A.astype(np.float16).view(np.uint16), B.astype(np.float16).view(np.uint16)
-        R, T = oracle.gemm(A, B, alpha=1.5, beta=0.5, C=C)
-        r, t = oracle.gemm_at(A, B, rows, cols, alpha=1.5, beta=0.5, C=C)
+        if kind == "bf16":   # upper halves of fp32 patterns are valid bfloat16 patterns
+            A, B = (A.view(np.uint32) >> 16).astype(np.uint16), (B.view(np.uint32) >> 16).astype(np.uint16)
+        bf = kind == "bf16"
+        R, T = oracle.gemm(A, B, alpha=1.5, beta=0.5, C=C, bf16=bf)
+        r, t = oracle.gemm_at(A, B, rows, cols, alpha=1.5, beta=0.5, C=C, bf16=bf)
     assert np.array_equal(R.ravel(), r) and np.array_equal(T.ravel(), t)
 
 
