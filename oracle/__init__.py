@@ -51,14 +51,14 @@ def _load():
     lib = ctypes.CDLL(_LIB)
     i64, f64, i32 = ctypes.c_int64, ctypes.c_double, ctypes.c_int
     vp = ctypes.c_void_p
-    lib.oracle_gemm_f32.argtypes = [i64, i64, i64, f64, vp, i64, vp, i64, f64, vp, i64, vp, vp, i32]
+    lib.oracle_gemm_f32.argtypes = [i64, i64, i64, f64, vp, i64, vp, i64, i32, f64, vp, i64, vp, vp, i32]
     lib.oracle_gemm_f16.argtypes = lib.oracle_gemm_f32.argtypes
     lib.oracle_gemm_bf16.argtypes = lib.oracle_gemm_f32.argtypes
-    lib.oracle_linear.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i32, vp, vp, i32]
-    lib.oracle_gemm_f32_at.argtypes = [i64, f64, vp, i64, vp, i64, f64, vp, i64, i64, vp, vp, vp, vp, i32]
+    lib.oracle_linear.argtypes = [i64, i64, i64, vp, i64, vp, i64, i32, vp, i32, vp, vp, i32]
+    lib.oracle_gemm_f32_at.argtypes = [i64, f64, vp, i64, vp, i64, i32, f64, vp, i64, i64, vp, vp, vp, vp, i32]
     lib.oracle_gemm_f16_at.argtypes = lib.oracle_gemm_f32_at.argtypes
     lib.oracle_gemm_bf16_at.argtypes = lib.oracle_gemm_f32_at.argtypes
-    lib.oracle_linear_at.argtypes = [i64, vp, i64, vp, i64, vp, i32, i64, vp, vp, vp, vp, i32]
+    lib.oracle_linear_at.argtypes = [i64, vp, i64, vp, i64, i32, vp, i32, i64, vp, vp, vp, vp, i32]
     for f in (lib.oracle_gemm_f32, lib.oracle_gemm_f16, lib.oracle_gemm_bf16, lib.oracle_linear,
               lib.oracle_gemm_f32_at, lib.oracle_gemm_f16_at, lib.oracle_gemm_bf16_at,
               lib.oracle_linear_at):
@@ -108,11 +108,12 @@ def bf16_to_double(bits: int) -> float:
     return _load().oracle_bf16_to_double(int(bits) & 0xFFFF)
 
 
-def gemm(A, B, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=False):
+def gemm(A, B, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=False, b_trans=False):
     """R = alpha*A*B + beta*C for fp32 A (MxK), B (KxN); C read only if beta != 0.
 
     A and B may instead be uint16 arrays of 16-bit bit patterns (both of them):
-    binary16 by default, bfloat16 with ``bf16=True``.
+    binary16 by default, bfloat16 with ``bf16=True``. With ``b_trans=True``, B
+    is given N-by-K and the product is alpha*A*B^T + beta*C.
     """
     lib = _load()
     half = np.asarray(A).dtype == np.uint16
@@ -120,7 +121,7 @@ def gemm(A, B, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=False):
     A, lda = _mat(A, dt, "A")
     B, ldb = _mat(B, dt, "B")
     M, K = A.shape
-    K2, N = B.shape
+    N, K2 = B.shape if b_trans else B.shape[::-1]
     if K2 != K:
         raise ValueError("inner dimensions differ")
     if beta != 0.0:
@@ -134,18 +135,22 @@ def gemm(A, B, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=False):
     if bf16 and not half:
         raise TypeError("bf16=True needs uint16 bit patterns")
     fn = (lib.oracle_gemm_bf16 if bf16 else lib.oracle_gemm_f16) if half else lib.oracle_gemm_f32
-    fn(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
+    fn(M, N, K, float(alpha), _ptr(A), lda, _ptr(B), ldb, int(b_trans), float(beta), _ptr(C), ldc,
        _ptr(R), _ptr(T), _threads(nthreads))
     return R, T
 
 
-def linear(X, W, bias=None, act=1, nthreads=None):
-    """R = act(X*W + bias) for fp32 X (MxK), W (KxN), bias (N) or None."""
+def linear(X, W, bias=None, act=1, nthreads=None, w_trans=False):
+    """R = act(X*W + bias) for fp32 X (MxK), W (KxN), bias (N) or None.
+
+    With ``w_trans=True``, W is given N-by-K (the layout of a PyTorch Linear
+    weight) and the layer is act(X*W^T + bias).
+    """
     lib = _load()
     X, ldx = _mat(X, np.float32, "X")
     W, ldw = _mat(W, np.float32, "W")
     M, K = X.shape
-    K2, N = W.shape
+    N, K2 = W.shape if w_trans else W.shape[::-1]
     if K2 != K:
         raise ValueError("inner dimensions differ")
     if bias is not None:
@@ -154,7 +159,7 @@ def linear(X, W, bias=None, act=1, nthreads=None):
             raise ValueError("bias shape")
     R = np.empty((M, N), np.float64)
     T = np.empty((M, N), np.float64)
-    lib.oracle_linear(M, N, K, _ptr(X), ldx, _ptr(W), ldw, _ptr(bias), int(act),
+    lib.oracle_linear(M, N, K, _ptr(X), ldx, _ptr(W), ldw, int(w_trans), _ptr(bias), int(act),
                       _ptr(R), _ptr(T), _threads(nthreads))
     return R, T
 
@@ -167,7 +172,8 @@ def _idx(rows, cols):
     return rows, cols
 
 
-def gemm_at(A, B, rows, cols, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=False):
+def gemm_at(A, B, rows, cols, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=False,
+            b_trans=False):
     """gemm() evaluated only at the positions (rows[p], cols[p])."""
     lib = _load()
     half = np.asarray(A).dtype == np.uint16
@@ -175,8 +181,8 @@ def gemm_at(A, B, rows, cols, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=F
     A, lda = _mat(A, dt, "A")
     B, ldb = _mat(B, dt, "B")
     M, K = A.shape
-    N = B.shape[1]
-    if B.shape[0] != K:
+    N, K2 = B.shape if b_trans else B.shape[::-1]
+    if K2 != K:
         raise ValueError("inner dimensions differ")
     rows, cols = _idx(rows, cols)
     if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
@@ -192,19 +198,19 @@ def gemm_at(A, B, rows, cols, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=F
     if bf16 and not half:
         raise TypeError("bf16=True needs uint16 bit patterns")
     fn = (lib.oracle_gemm_bf16_at if bf16 else lib.oracle_gemm_f16_at) if half else lib.oracle_gemm_f32_at
-    fn(K, float(alpha), _ptr(A), lda, _ptr(B), ldb, float(beta), _ptr(C), ldc,
+    fn(K, float(alpha), _ptr(A), lda, _ptr(B), ldb, int(b_trans), float(beta), _ptr(C), ldc,
        rows.size, _ptr(rows), _ptr(cols), _ptr(R), _ptr(T), _threads(nthreads))
     return R, T
 
 
-def linear_at(X, W, rows, cols, bias=None, act=1, nthreads=None):
+def linear_at(X, W, rows, cols, bias=None, act=1, nthreads=None, w_trans=False):
     """linear() evaluated only at the positions (rows[p], cols[p])."""
     lib = _load()
     X, ldx = _mat(X, np.float32, "X")
     W, ldw = _mat(W, np.float32, "W")
     M, K = X.shape
-    N = W.shape[1]
-    if W.shape[0] != K:
+    N, K2 = W.shape if w_trans else W.shape[::-1]
+    if K2 != K:
         raise ValueError("inner dimensions differ")
     rows, cols = _idx(rows, cols)
     if rows.size and (rows.min() < 0 or rows.max() >= M or cols.min() < 0 or cols.max() >= N):
@@ -215,6 +221,6 @@ def linear_at(X, W, rows, cols, bias=None, act=1, nthreads=None):
             raise ValueError("bias shape")
     R = np.empty(rows.size, np.float64)
     T = np.empty(rows.size, np.float64)
-    lib.oracle_linear_at(K, _ptr(X), ldx, _ptr(W), ldw, _ptr(bias), int(act),
+    lib.oracle_linear_at(K, _ptr(X), ldx, _ptr(W), ldw, int(w_trans), _ptr(bias), int(act),
                          rows.size, _ptr(rows), _ptr(cols), _ptr(R), _ptr(T), _threads(nthreads))
     return R, T

@@ -31,6 +31,9 @@
  *     no fast-math may be used to build this file, because reassociating k
  *     changes the result.
  *
+ * B (or W) is K-by-N, or, with b_trans (w_trans) set, stored N-by-K so that
+ * element (k, n) is at B[n*ldb + k] (the product is then A*B^T, X*W^T).
+ *
  * Besides the value r, every routine returns t = sum over k of |A(m,k)*B(k,n)|,
  * which is the basis of the parity tolerance |C_gpu - r| <= 1e-4 * t.
  *
@@ -148,7 +151,7 @@ static inline int needs_sum(const epilogue_t *e)
 /* Full M-by-N result into R (row-major, ld N) and T (same layout). */
 static void full_product(int64_t M, int64_t N, int64_t K,
                          const void *A, int64_t lda, loader_fn la,
-                         const void *B, int64_t ldb, loader_fn lb,
+                         const void *B, int64_t ldb, loader_fn lb, int b_trans,
                          const epilogue_t *e, double *R, double *T, int nthreads)
 {
     if (M <= 0 || N <= 0)
@@ -170,9 +173,9 @@ static void full_product(int64_t M, int64_t N, int64_t K,
             if (sum) {
                 for (int64_t k = 0; k < K; ++k) {
                     const double a = la(A, m * lda + k);
-                    const int64_t brow = k * ldb + n0;
                     for (int64_t j = 0; j < nb; ++j) {
-                        const double p = a * lb(B, brow + j);
+                        const int64_t bi = b_trans ? (n0 + j) * ldb + k : k * ldb + n0 + j;
+                        const double p = a * lb(B, bi);
                         s[j] += p;
                         t[j] += fabs(p);
                     }
@@ -188,7 +191,7 @@ static void full_product(int64_t M, int64_t N, int64_t K,
 
 /* Selected elements (rows[p], cols[p]): each is one plain dot product over k. */
 static void sampled_product(int64_t K, const void *A, int64_t lda, loader_fn la,
-                            const void *B, int64_t ldb, loader_fn lb,
+                            const void *B, int64_t ldb, loader_fn lb, int b_trans,
                             const epilogue_t *e, int64_t P, const int64_t *rows,
                             const int64_t *cols, double *R, double *T, int nthreads)
 {
@@ -200,7 +203,7 @@ static void sampled_product(int64_t K, const void *A, int64_t lda, loader_fn la,
         double s = 0.0, t = 0.0;
         if (sum) {
             for (int64_t k = 0; k < K; ++k) {
-                const double prod = la(A, m * lda + k) * lb(B, k * ldb + n);
+                const double prod = la(A, m * lda + k) * lb(B, b_trans ? n * ldb + k : k * ldb + n);
                 s += prod;
                 t += fabs(prod);
             }
@@ -236,74 +239,74 @@ static epilogue_t linear_epi(const float *bias, int act)
 
 /* C = alpha*A*B + beta*Cin with fp32 A, B, Cin; results in float64. */
 void oracle_gemm_f32(int64_t M, int64_t N, int64_t K, double alpha,
-                     const float *A, int64_t lda, const float *B, int64_t ldb,
+                     const float *A, int64_t lda, const float *B, int64_t ldb, int b_trans,
                      double beta, const float *Cin, int64_t ldc,
                      double *R, double *T, int nthreads)
 {
     epilogue_t e = gemm_epi(alpha, beta, Cin, ldc);
-    full_product(M, N, K, A, lda, ld_f32, B, ldb, ld_f32, &e, R, T, nthreads);
+    full_product(M, N, K, A, lda, ld_f32, B, ldb, ld_f32, b_trans, &e, R, T, nthreads);
 }
 
 /* As oracle_gemm_f32 but A and B hold IEEE binary16 bit patterns. */
 void oracle_gemm_f16(int64_t M, int64_t N, int64_t K, double alpha,
-                     const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                     const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int b_trans,
                      double beta, const float *Cin, int64_t ldc,
                      double *R, double *T, int nthreads)
 {
     epilogue_t e = gemm_epi(alpha, beta, Cin, ldc);
-    full_product(M, N, K, A, lda, ld_f16, B, ldb, ld_f16, &e, R, T, nthreads);
+    full_product(M, N, K, A, lda, ld_f16, B, ldb, ld_f16, b_trans, &e, R, T, nthreads);
 }
 
 /* As oracle_gemm_f32 but A and B hold bfloat16 bit patterns. */
 void oracle_gemm_bf16(int64_t M, int64_t N, int64_t K, double alpha,
-                      const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                      const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb, int b_trans,
                       double beta, const float *Cin, int64_t ldc,
                       double *R, double *T, int nthreads)
 {
     epilogue_t e = gemm_epi(alpha, beta, Cin, ldc);
-    full_product(M, N, K, A, lda, ld_bf16, B, ldb, ld_bf16, &e, R, T, nthreads);
+    full_product(M, N, K, A, lda, ld_bf16, B, ldb, ld_bf16, b_trans, &e, R, T, nthreads);
 }
 
 /* Y = act(X*W + bias); bias may be NULL; act 0 = none, 1 = ReLU. */
 void oracle_linear(int64_t M, int64_t N, int64_t K,
-                   const float *X, int64_t ldx, const float *W, int64_t ldw,
+                   const float *X, int64_t ldx, const float *W, int64_t ldw, int w_trans,
                    const float *bias, int act, double *R, double *T, int nthreads)
 {
     epilogue_t e = linear_epi(bias, act);
-    full_product(M, N, K, X, ldx, ld_f32, W, ldw, ld_f32, &e, R, T, nthreads);
+    full_product(M, N, K, X, ldx, ld_f32, W, ldw, ld_f32, w_trans, &e, R, T, nthreads);
 }
 
 void oracle_gemm_f32_at(int64_t K, double alpha, const float *A, int64_t lda,
-                        const float *B, int64_t ldb, double beta, const float *Cin,
+                        const float *B, int64_t ldb, int b_trans, double beta, const float *Cin,
                         int64_t ldc, int64_t P, const int64_t *rows, const int64_t *cols,
                         double *R, double *T, int nthreads)
 {
     epilogue_t e = gemm_epi(alpha, beta, Cin, ldc);
-    sampled_product(K, A, lda, ld_f32, B, ldb, ld_f32, &e, P, rows, cols, R, T, nthreads);
+    sampled_product(K, A, lda, ld_f32, B, ldb, ld_f32, b_trans, &e, P, rows, cols, R, T, nthreads);
 }
 
 void oracle_gemm_f16_at(int64_t K, double alpha, const uint16_t *A, int64_t lda,
-                        const uint16_t *B, int64_t ldb, double beta, const float *Cin,
+                        const uint16_t *B, int64_t ldb, int b_trans, double beta, const float *Cin,
                         int64_t ldc, int64_t P, const int64_t *rows, const int64_t *cols,
                         double *R, double *T, int nthreads)
 {
     epilogue_t e = gemm_epi(alpha, beta, Cin, ldc);
-    sampled_product(K, A, lda, ld_f16, B, ldb, ld_f16, &e, P, rows, cols, R, T, nthreads);
+    sampled_product(K, A, lda, ld_f16, B, ldb, ld_f16, b_trans, &e, P, rows, cols, R, T, nthreads);
 }
 
 void oracle_gemm_bf16_at(int64_t K, double alpha, const uint16_t *A, int64_t lda,
-                         const uint16_t *B, int64_t ldb, double beta, const float *Cin,
+                         const uint16_t *B, int64_t ldb, int b_trans, double beta, const float *Cin,
                          int64_t ldc, int64_t P, const int64_t *rows, const int64_t *cols,
                          double *R, double *T, int nthreads)
 {
     epilogue_t e = gemm_epi(alpha, beta, Cin, ldc);
-    sampled_product(K, A, lda, ld_bf16, B, ldb, ld_bf16, &e, P, rows, cols, R, T, nthreads);
+    sampled_product(K, A, lda, ld_bf16, B, ldb, ld_bf16, b_trans, &e, P, rows, cols, R, T, nthreads);
 }
 
 void oracle_linear_at(int64_t K, const float *X, int64_t ldx, const float *W, int64_t ldw,
-                      const float *bias, int act, int64_t P, const int64_t *rows,
+                      int w_trans, const float *bias, int act, int64_t P, const int64_t *rows,
                       const int64_t *cols, double *R, double *T, int nthreads)
 {
     epilogue_t e = linear_epi(bias, act);
-    sampled_product(K, X, ldx, ld_f32, W, ldw, ld_f32, &e, P, rows, cols, R, T, nthreads);
+    sampled_product(K, X, ldx, ld_f32, W, ldw, ld_f32, w_trans, &e, P, rows, cols, R, T, nthreads);
 }

@@ -316,6 +316,48 @@ def test_leading_dimensions():
     assert np.array_equal(R, Rc) and np.array_equal(T, Tc)
 
 
+# ---- transposed B (B given N-by-K) ------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["f32", "f16", "bf16"])
+def test_b_transposed_equals_explicit_transpose(fmt):
+    # A*B^T with B stored N-by-K equals A*(B^T stored K-by-N), bit for bit
+    M, N, K = 37, 45, 150
+    A, Bt, C = rand_f32(M, K), rand_f32(N, K), rand_f32(M, N)
+    kw = {}
+    if fmt == "f16":
+        A, Bt = A.astype(np.float16).view(np.uint16), Bt.astype(np.float16).view(np.uint16)
+    elif fmt == "bf16":
+        A, Bt = (A.view(np.uint32) >> 16).astype(np.uint16), (Bt.view(np.uint32) >> 16).astype(np.uint16)
+        kw["bf16"] = True
+    R, T = oracle.gemm(A, Bt, 1.5, 0.5, C, b_trans=True, **kw)
+    R2, T2 = oracle.gemm(A, np.ascontiguousarray(Bt.T), 1.5, 0.5, C, **kw)
+    assert np.array_equal(R, R2) and np.array_equal(T, T2)
+    rows, cols = np.arange(M).repeat(N), np.tile(np.arange(N), M)
+    r, t = oracle.gemm_at(A, Bt, rows, cols, 1.5, 0.5, C, b_trans=True, **kw)
+    assert np.array_equal(r, R.ravel()) and np.array_equal(t, T.ravel())
+
+
+def test_b_transposed_integer_exact():
+    M, N, K = 31, 23, 90
+    A, Bt = rand_int(M, K), rand_int(N, K)
+    R, _ = oracle.gemm(A, Bt, b_trans=True)
+    assert np.array_equal(R, (A.astype(np.int64) @ Bt.astype(np.int64).T).astype(np.float64))
+    # a non-square transposed operand read the wrong way round is caught
+    with pytest.raises(ValueError):
+        oracle.gemm(A, Bt)
+
+
+def test_linear_w_transposed():
+    M, N, K = 19, 41, 66
+    X, Wt, b = rand_int(M, K), rand_int(N, K), rand_int(N, lo=-4, hi=4)
+    R, _ = oracle.linear(X, Wt, b, act=1, w_trans=True)
+    y = X.astype(np.int64) @ Wt.astype(np.int64).T + b.astype(np.int64)
+    assert np.array_equal(R, np.maximum(y, 0).astype(np.float64))
+    rows, cols = np.arange(M).repeat(N), np.tile(np.arange(N), M)
+    r, _ = oracle.linear_at(X, Wt, rows, cols, b, act=1, w_trans=True)
+    assert np.array_equal(r, R.ravel())
+
+
 def test_sampled_rejects_out_of_range():
     with pytest.raises(IndexError):
         oracle.gemm_at(rand_f32(3, 4), rand_f32(4, 5), [3], [0])
