@@ -29,12 +29,15 @@ sys.path.insert(0, ROOT)
 COPY_BYTES = 256 << 20
 
 # Published MI355X dense matrix peaks (TFLOP/s).
-PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "gemm_f16f32": 2516.6, "gemm_bf16f32": 2516.6}
+PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "linear_nt": 157.3,
+               "gemm_f16f32": 2516.6, "gemm_bf16f32": 2516.6, "gemm_f16f32_nt": 2516.6}
 KERNEL_SOURCES = {
     "gemm_f32": ["gemm_f32.hip", "common.hpp"],
     "linear": ["gemm_f32.hip", "common.hpp"],
     "gemm_f16f32": ["gemm_f16.hip", "common.hpp"],
     "gemm_bf16f32": ["gemm_f16.hip", "common.hpp"],
+    "linear_nt": ["gemm_f32.hip", "common.hpp"],
+    "gemm_f16f32_nt": ["gemm_f16.hip", "common.hpp"],
 }
 
 
@@ -104,20 +107,21 @@ def cpu_baseline(w, x, target_s: float):
 
     A = x["A"]
     B = x["B"]
-    if w.kind in ("gemm_f16f32", "gemm_bf16f32"):
+    if w.kind in wl.HALF_KINDS:
         A, B = wl.half_bits(A), wl.half_bits(B)
     else:
         A, B = A.numpy(), B.numpy()
+    bt = w.kind in wl.B_TRANSPOSED_KINDS
     C = x["C"].numpy() if "C" in x else None
     bias = x["bias"].numpy() if "bias" in x else None
 
     def run(rows):
         t0 = time.perf_counter()
-        if w.kind == "linear":
-            oracle.linear(A[:rows], B, bias, w.act)
+        if w.kind in ("linear", "linear_nt"):
+            oracle.linear(A[:rows], B, bias, w.act, w_trans=bt)
         else:
             oracle.gemm(A[:rows], B, w.alpha, w.beta, None if C is None else C[:rows],
-                        bf16=w.kind == "gemm_bf16f32")
+                        bf16=w.kind == "gemm_bf16f32", b_trans=bt)
         return time.perf_counter() - t0
 
     rows = min(8, w.M)
@@ -164,7 +168,7 @@ def main():
     if "C" in x:
         C.copy_(x["C"].to(dev))
     bias = x["bias"].to(dev) if "bias" in x else None
-    dtype_id = ll.DTYPE_F16 if w.kind in ("gemm_f16f32", "gemm_bf16f32") else ll.DTYPE_F32
+    dtype_id = ll.DTYPE_F16 if w.kind in wl.HALF_KINDS else ll.DTYPE_F32
     if args.tile >= 0:
         ll.set_tile(dtype_id, args.tile)
     if args.split_k >= 1:
@@ -180,6 +184,10 @@ def main():
             ll.gemm_f16f32(A, B, C, w.alpha, w.beta)
         elif w.kind == "gemm_bf16f32":
             ll.gemm_bf16f32(A, B, C, w.alpha, w.beta)
+        elif w.kind == "gemm_f16f32_nt":
+            ll.gemm_f16f32_nt(A, B, C, w.alpha, w.beta)
+        elif w.kind == "linear_nt":
+            ll.linear_bias_act_nt(A, B, bias, w.act, C)
         else:
             ll.linear_bias_act(A, B, bias, w.act, C)
 
@@ -213,7 +221,8 @@ def main():
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, x, args.cpu_seconds)
 
-    dtype = {"gemm_f32": "f32", "linear": "f32", "gemm_f16f32": "f16 in, f32 accumulate",
+    dtype = {"gemm_f32": "f32", "linear": "f32", "linear_nt": "f32",
+             "gemm_f16f32": "f16 in, f32 accumulate", "gemm_f16f32_nt": "f16 in, f32 accumulate",
              "gemm_bf16f32": "bf16 in, f32 accumulate"}[w.kind]
     out = {
         "metric": "TFLOPS (2MNK/t) for 4096^3 FP32 GEMM on 1 MI355X; % of matrix peak"
@@ -231,7 +240,9 @@ def main():
         "data": "synthetic (seeded uniform inputs, resident in HBM)",
         "config": {
             "workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta,
-            **({"act": "relu" if w.act == 1 else "none", "bias": True} if w.kind == "linear" else {}),
+            **({"act": "relu" if w.act == 1 else "none", "bias": True}
+               if w.kind in ("linear", "linear_nt") else {}),
+            **({"b_layout": "N-by-K"} if w.kind in wl.B_TRANSPOSED_KINDS else {}),
             "tile": ll.tile_name(dtype_id, tile), "split_k": splits,
             "device": props.name, "cus": props.multi_processor_count,
         },

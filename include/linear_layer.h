@@ -127,6 +127,34 @@ int linear_bias_act(int M, int N, int K,
                     const float *bias, int act,
                     float *Y, int ldy, void *stream);
 
+/*
+ * Transposed-B forms: B (or W) is given N-by-K, row-major, leading dimension
+ * ldb >= max(1, K) (ldw for W), so that its element (k, n) is at B[n*ldb + k]:
+ *
+ *   gemm_f32_nt, gemm_f16f32_nt, gemm_bf16f32_nt:  C = alpha * A * B^T + beta * C
+ *   linear_bias_act_nt:                            Y = act(X * W^T + bias)
+ *
+ * This is how a fully-connected weight is usually stored ([out][in]) and the
+ * shape of products such as Q * K^T (page "GEMM 优化详解", table
+ * "为什么 GEMM 重要"). B is then k-contiguous like A and the kernels stage and
+ * read it exactly like A. Every other argument, rule and error is that of the
+ * corresponding function above; the 128-bit kernels need ldb (ldw) to be a
+ * multiple of 4 (fp32) or 8 (16-bit) instead of N.
+ */
+int gemm_f32_nt(int M, int N, int K, float alpha,
+                const float *A, int lda, const float *B, int ldb,
+                float beta, float *C, int ldc, void *stream);
+int gemm_f16f32_nt(int M, int N, int K, float alpha,
+                   const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                   float beta, float *C, int ldc, void *stream);
+int gemm_bf16f32_nt(int M, int N, int K, float alpha,
+                    const uint16_t *A, int lda, const uint16_t *B, int ldb,
+                    float beta, float *C, int ldc, void *stream);
+int linear_bias_act_nt(int M, int N, int K,
+                       const float *X, int ldx, const float *W, int ldw,
+                       const float *bias, int act,
+                       float *Y, int ldy, void *stream);
+
 /* A static, human-readable string for a status code (never NULL). */
 const char *ll_status_string(int status);
 
@@ -148,8 +176,8 @@ const char *ll_status_string(int status);
  * These calls let a benchmark or a caller pin the choice. They touch only
  * host memory and never the GPU.
  */
-#define LL_DTYPE_F32 0 /* gemm_f32 and linear_bias_act */
-#define LL_DTYPE_F16 1 /* gemm_f16f32 and gemm_bf16f32 */
+#define LL_DTYPE_F32 0 /* gemm_f32, linear_bias_act and their _nt forms */
+#define LL_DTYPE_F16 1 /* gemm_f16f32, gemm_bf16f32 and their _nt forms */
 
 /* Number of tile shapes for a data type (0 for an unknown dtype). */
 int ll_num_tiles(int dtype);

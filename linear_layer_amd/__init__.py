@@ -11,6 +11,9 @@ Entry points (same names as the C ABI in ``include/linear_layer.h``):
 * ``gemm_f16f32(A, B, C, alpha=1.0, beta=0.0)`` — fp16 A, B; fp32 C.
 * ``gemm_bf16f32(A, B, C, alpha=1.0, beta=0.0)`` — bf16 A, B; fp32 C.
 * ``linear_bias_act(X, W, bias, act, Y)`` — Y = act(X*W + bias), fp32.
+* ``gemm_f32_nt``, ``gemm_f16f32_nt``, ``gemm_bf16f32_nt``, ``linear_bias_act_nt``
+  — the same with B (W) given N-by-K: C = alpha*A*B^T + beta*C, Y = act(X*W^T + b)
+  (W in the [out_features, in_features] layout of ``torch.nn.Linear.weight``).
 
 Tensors are 2-D, row-major with unit column stride (a row stride larger than
 the width is a leading dimension), on the current CUDA/HIP device. The calls
@@ -23,6 +26,7 @@ import os
 
 __all__ = [
     "LinearLayerError", "gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "status_string",
+    "gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt", "linear_bias_act_nt",
     "library_path", "load", "set_tile", "num_tiles", "tile_name", "chosen_tile",
     "set_split_k", "chosen_split_k",
     "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16",
@@ -39,6 +43,7 @@ _lib = None
 
 # Every symbol the C header declares.
 EXPORTED = ("gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "ll_status_string",
+            "gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt", "linear_bias_act_nt",
             "ll_num_tiles", "ll_tile_name", "ll_set_tile", "ll_chosen_tile",
             "ll_set_split_k", "ll_chosen_split_k")
 
@@ -66,7 +71,11 @@ def load():
     lib.gemm_f16f32.argtypes = lib.gemm_f32.argtypes
     lib.gemm_bf16f32.argtypes = lib.gemm_f32.argtypes
     lib.linear_bias_act.argtypes = [i32, i32, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp]
-    for f in (lib.gemm_f32, lib.gemm_f16f32, lib.gemm_bf16f32, lib.linear_bias_act):
+    for nt in ("gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt"):
+        getattr(lib, nt).argtypes = lib.gemm_f32.argtypes
+    lib.linear_bias_act_nt.argtypes = lib.linear_bias_act.argtypes
+    for f in (lib.gemm_f32, lib.gemm_f16f32, lib.gemm_bf16f32, lib.linear_bias_act,
+              lib.gemm_f32_nt, lib.gemm_f16f32_nt, lib.gemm_bf16f32_nt, lib.linear_bias_act_nt):
         f.restype = i32
     lib.ll_status_string.argtypes = [i32]
     lib.ll_status_string.restype = ctypes.c_char_p
@@ -161,10 +170,13 @@ def _stream(stream, *tensors):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _gemm(fn_name, in_dtype, A, B, C, alpha, beta, stream):
+def _gemm(fn_name, in_dtype, A, B, C, alpha, beta, stream, bt=False):
     torch = _torch()
     pa, M, K, lda = _mat(A, in_dtype, "A")
-    pb, K2, N, ldb = _mat(B, in_dtype, "B")
+    if bt:
+        pb, N, K2, ldb = _mat(B, in_dtype, "B")
+    else:
+        pb, K2, N, ldb = _mat(B, in_dtype, "B")
     pc, M2, N2, ldc = _mat(C, torch.float32, "C")
     if K2 != K or M2 != M or N2 != N:
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
@@ -189,11 +201,38 @@ def gemm_bf16f32(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
     return _gemm("gemm_bf16f32", _torch().bfloat16, A, B, C, alpha, beta, stream)
 
 
+def gemm_f32_nt(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    """C = alpha*A*B^T + beta*C (fp32) with B given N-by-K; C returned."""
+    return _gemm("gemm_f32_nt", _torch().float32, A, B, C, alpha, beta, stream, bt=True)
+
+
+def gemm_f16f32_nt(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    """C = alpha*A*B^T + beta*C with fp16 A, B (B N-by-K) and fp32 C."""
+    return _gemm("gemm_f16f32_nt", _torch().float16, A, B, C, alpha, beta, stream, bt=True)
+
+
+def gemm_bf16f32_nt(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    """C = alpha*A*B^T + beta*C with bf16 A, B (B N-by-K) and fp32 C."""
+    return _gemm("gemm_bf16f32_nt", _torch().bfloat16, A, B, C, alpha, beta, stream, bt=True)
+
+
+def linear_bias_act_nt(X, W, bias, act: int, Y, stream=None):
+    """Y = act(X*W^T + bias) (fp32; W is N-by-K, e.g. a torch Linear weight)."""
+    return _linear("linear_bias_act_nt", X, W, bias, act, Y, stream, wt=True)
+
+
 def linear_bias_act(X, W, bias, act: int, Y, stream=None):
     """Y = act(X*W + bias) (fp32; W is K-by-N row-major; bias may be None)."""
+    return _linear("linear_bias_act", X, W, bias, act, Y, stream)
+
+
+def _linear(fn_name, X, W, bias, act, Y, stream, wt=False):
     torch = _torch()
     px, M, K, ldx = _mat(X, torch.float32, "X")
-    pw, K2, N, ldw = _mat(W, torch.float32, "W")
+    if wt:
+        pw, N, K2, ldw = _mat(W, torch.float32, "W")
+    else:
+        pw, K2, N, ldw = _mat(W, torch.float32, "W")
     py, M2, N2, ldy = _mat(Y, torch.float32, "Y")
     if K2 != K or M2 != M or N2 != N:
         raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W {tuple(W.shape)}, Y {tuple(Y.shape)}")
@@ -204,7 +243,7 @@ def linear_bias_act(X, W, bias, act: int, Y, stream=None):
         if N > 1 and bias.stride(0) != 1:
             raise ValueError("bias must be contiguous")
         pbias = bias.data_ptr()
-    st = load().linear_bias_act(M, N, K, px, ldx, pw, ldw, pbias, int(act), py, ldy,
-                                _stream(stream, X, W, Y, bias))
-    _check(st, "linear_bias_act")
+    st = getattr(load(), fn_name)(M, N, K, px, ldx, pw, ldw, pbias, int(act), py, ldy,
+                                  _stream(stream, X, W, Y, bias))
+    _check(st, fn_name)
     return Y

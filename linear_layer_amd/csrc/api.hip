@@ -37,14 +37,15 @@ bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
 int imax1(int v) { return v > 1 ? v : 1; }
 
-// Returns LL_OK and sets *noop when nothing is to be done.
+// Returns LL_OK and sets *noop when nothing is to be done. b_trans: B is
+// given N-by-K (ldb >= K) instead of K-by-N (ldb >= N).
 int check_gemm(int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
-               const float *C, int ldc, int64_t elem_ab, bool *noop)
+               const float *C, int ldc, int64_t elem_ab, bool *noop, bool b_trans = false)
 {
     *noop = false;
     if (M < 0 || N < 0 || K < 0)
         return LL_ERR_INVALID_VALUE;
-    if (lda < imax1(K) || ldb < imax1(N) || ldc < imax1(N))
+    if (lda < imax1(K) || ldb < imax1(b_trans ? K : N) || ldc < imax1(N))
         return LL_ERR_INVALID_VALUE;
     if (M == 0 || N == 0) {
         *noop = true;
@@ -58,7 +59,7 @@ int check_gemm(int M, int N, int K, float alpha, const void *A, int lda, const v
             return LL_ERR_INVALID_VALUE;
         const int64_t cb = span_bytes(M, N, ldc, 4);
         if (overlap(C, cb, A, span_bytes(M, K, lda, elem_ab)) ||
-            overlap(C, cb, B, span_bytes(K, N, ldb, elem_ab)))
+            overlap(C, cb, B, b_trans ? span_bytes(N, K, ldb, elem_ab) : span_bytes(K, N, ldb, elem_ab)))
             return LL_ERR_INVALID_VALUE;
     }
     return LL_OK;
@@ -233,11 +234,11 @@ hipError_t run_gemm(GemmParams p, const Plan &pl, bool vec, hipStream_t s, launc
 
 extern "C" {
 
-int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
-             float beta, float *C, int ldc, void *stream)
+static int gemm_f32_impl(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                         int ldb, float beta, float *C, int ldc, void *stream, bool bt)
 {
     bool noop;
-    int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 4, &noop);
+    int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 4, &noop, bt);
     if (st != LL_OK || noop)
         return st;
     DevInfo dev;
@@ -247,18 +248,30 @@ int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const fl
     if (K == 0 || alpha == 0.0f)
         return launch_status(launch_scale(C, ldc, M, N, beta, s));
     const bool vec = aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && lda % 4 == 0 &&
-                     ldb % 4 == 0 && ldc % 4 == 0 && K % 4 == 0 && N % 4 == 0;
+                     ldb % 4 == 0 && ldc % 4 == 0 && K % 4 == 0 && (bt || N % 4 == 0);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false);
-    return launch_status(run_gemm(p, pl, vec, s, launch_gemm_f32));
+    return launch_status(run_gemm(p, pl, vec, s, bt ? launch_gemm_f32_bt : launch_gemm_f32));
 }
 
-// Both 16-bit formats share the kernels, tiles and checks.
+int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+             float beta, float *C, int ldc, void *stream)
+{
+    return gemm_f32_impl(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, false);
+}
+
+int gemm_f32_nt(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+                float beta, float *C, int ldc, void *stream)
+{
+    return gemm_f32_impl(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, true);
+}
+
+// Both 16-bit formats and both B layouts share the kernels, tiles and checks.
 static int gemm_16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
-                   int ldb, float beta, float *C, int ldc, void *stream, launch_fn launch)
+                   int ldb, float beta, float *C, int ldc, void *stream, launch_fn launch, bool bt)
 {
     bool noop;
-    int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 2, &noop);
+    int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 2, &noop, bt);
     if (st != LL_OK || noop)
         return st;
     DevInfo dev;
@@ -268,7 +281,7 @@ static int gemm_16(int M, int N, int K, float alpha, const uint16_t *A, int lda,
     if (K == 0 || alpha == 0.0f)
         return launch_status(launch_scale(C, ldc, M, N, beta, s));
     const bool vec = aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && lda % 8 == 0 &&
-                     ldb % 8 == 0 && ldc % 4 == 0 && K % 8 == 0 && N % 8 == 0;
+                     ldb % 8 == 0 && ldc % 4 == 0 && K % 8 == 0 && (bt || N % 8 == 0);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false);
     return launch_status(run_gemm(p, pl, vec, s, launch));
@@ -277,22 +290,34 @@ static int gemm_16(int M, int N, int K, float alpha, const uint16_t *A, int lda,
 int gemm_f16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
                 int ldb, float beta, float *C, int ldc, void *stream)
 {
-    return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, launch_gemm_f16);
+    return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, launch_gemm_f16, false);
 }
 
 int gemm_bf16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
                  int ldb, float beta, float *C, int ldc, void *stream)
 {
-    return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, launch_gemm_bf16);
+    return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, launch_gemm_bf16, false);
 }
 
-int linear_bias_act(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
-                    const float *bias, int act, float *Y, int ldy, void *stream)
+int gemm_f16f32_nt(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+                   int ldb, float beta, float *C, int ldc, void *stream)
+{
+    return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, launch_gemm_f16_bt, true);
+}
+
+int gemm_bf16f32_nt(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
+                    int ldb, float beta, float *C, int ldc, void *stream)
+{
+    return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, launch_gemm_bf16_bt, true);
+}
+
+static int linear_impl(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
+                       const float *bias, int act, float *Y, int ldy, void *stream, bool wt)
 {
     if (act != LL_ACT_NONE && act != LL_ACT_RELU)
         return LL_ERR_INVALID_VALUE;
     bool noop;
-    int st = check_gemm(M, N, K, 1.0f, X, ldx, W, ldw, Y, ldy, 4, &noop);
+    int st = check_gemm(M, N, K, 1.0f, X, ldx, W, ldw, Y, ldy, 4, &noop, wt);
     if (st != LL_OK || noop)
         return st;
     if (bias != nullptr) {
@@ -306,22 +331,35 @@ int linear_bias_act(int M, int N, int K, const float *X, int ldx, const float *W
     if (K == 0)
         return launch_status(launch_bias_fill(Y, ldy, M, N, bias, act, s));
     const bool vec = aligned(X, 16) && aligned(W, 16) && aligned(Y, 16) && ldx % 4 == 0 &&
-                     ldw % 4 == 0 && ldy % 4 == 0 && K % 4 == 0 && N % 4 == 0;
+                     ldw % 4 == 0 && ldy % 4 == 0 && K % 4 == 0 && (wt || N % 4 == 0);
     GemmParams p = make_params(M, N, K, 1.0f, X, ldx, W, ldw, 0.0f, Y, ldy);
     p.bias = bias;
     p.act = act;
+    const launch_fn launch = wt ? launch_gemm_f32_bt : launch_gemm_f32;
     const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU);
     if (pl.splits == 1)
-        return launch_status(launch_gemm_f32(p, pl.tile, EPI_LINEAR, vec, s));
+        return launch_status(launch(p, pl.tile, EPI_LINEAR, vec, s));
     // split-K: Y = bias, then every split adds its partial product, then ReLU
     hipError_t e = launch_bias_fill(Y, ldy, M, N, bias, LL_ACT_NONE, s);
     if (e == hipSuccess) {
         p.k_split = pl.k_split;
-        e = launch_gemm_f32(p, pl.tile, EPI_ATOMIC, vec, s);
+        e = launch(p, pl.tile, EPI_ATOMIC, vec, s);
     }
     if (e == hipSuccess && act == LL_ACT_RELU)
         e = launch_relu(Y, ldy, M, N, s);
     return launch_status(e);
+}
+
+int linear_bias_act(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
+                    const float *bias, int act, float *Y, int ldy, void *stream)
+{
+    return linear_impl(M, N, K, X, ldx, W, ldw, bias, act, Y, ldy, stream, false);
+}
+
+int linear_bias_act_nt(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
+                       const float *bias, int act, float *Y, int ldy, void *stream)
+{
+    return linear_impl(M, N, K, X, ldx, W, ldw, bias, act, Y, ldy, stream, true);
 }
 
 const char *ll_status_string(int status)

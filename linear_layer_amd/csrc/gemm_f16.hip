@@ -38,7 +38,9 @@ struct F16Tile {
     static constexpr int A_PT = A_CH / NT;
     static constexpr int B_BLK = (BK / 8) * (BN / 8);  // 8x8 B blocks per stage
     static constexpr int B_PT = (B_BLK + NT - 1) / NT;
+    static constexpr int BT_PT = BN * CPR / NT;          // B given N-by-K: chunks per thread
     static_assert(BK == 64, "LDS rows are 128 bytes");
+    static_assert(BT_PT >= 1 && BT_PT * NT == BN * CPR, "B^T chunks must split evenly");
     static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
     static_assert(A_PT >= 1 && A_PT * NT == A_CH, "A chunks must split evenly");
 };
@@ -59,7 +61,9 @@ __device__ __forceinline__ f32x16 mma16(const f16x8 &a, const f16x8 &b, const f3
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-template <class T, int EPI, bool VEC, int WPE, bool BF16>
+// BT: B is given N-by-K (k contiguous); it is then loaded and stored exactly
+// like A and needs no transposition.
+template <class T, int EPI, bool VEC, int WPE, bool BF16, bool BT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f16_kernel(GemmParams p)
 {
@@ -76,15 +80,43 @@ gemm_f16_kernel(GemmParams p)
     int K;
     const int kb = split_range(p, K);
     const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A) + kb;
-    const uint16_t *__restrict__ B = static_cast<const uint16_t *>(p.B) + (int64_t)kb * p.ldb;
+    const uint16_t *__restrict__ B =
+        static_cast<const uint16_t *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
     const int M = p.M, N = p.N;
 
-    // A chunk i of this thread: row a_r0 + i*A_RSTEP, 16-byte chunk a_c.
+    // A chunk i of this thread: row a_r0 + i*A_RSTEP, 16-byte chunk a_c; with
+    // BT the same mapping over B's rows (n).
     const int a_c = tid % CPR;
     const int a_r0 = tid / CPR;
     constexpr int A_RSTEP = T::NT / CPR;
     const uint16_t *a_ptr = A + (int64_t)(m0 + a_r0) * p.lda + a_c * 8;
     const int64_t a_istep = (int64_t)A_RSTEP * p.lda;
+    const uint16_t *bt_ptr = B + (int64_t)(n0 + a_r0) * p.ldb + a_c * 8;
+    const int64_t bt_istep = (int64_t)A_RSTEP * p.ldb;
+    u32x4 rbt[BT ? T::BT_PT : 1];
+
+    // k-contiguous rows (A, or B given N-by-K): chunk i of this thread.
+    auto load_rows = [&](const uint16_t *ptr, int64_t istep, int first, int nrows, int npt,
+                         u32x4 *dst, int k0) {
+        for (int i = 0; i < npt; ++i) {
+            const bool rok = first + a_r0 + i * A_RSTEP < nrows;
+            const int kk = k0 + a_c * 8;
+            const uint16_t *src = ptr + i * istep + k0;
+            if (VEC) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (rok && kk < K)
+                    v = *reinterpret_cast<const u32x4 *>(src);
+                dst[i] = v;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = (rok && kk + 2 * j < K) ? ld_u16(src + 2 * j) : 0u;
+                    const uint32_t hi = (rok && kk + 2 * j + 1 < K) ? ld_u16(src + 2 * j + 1) : 0u;
+                    dst[i][j] = lo | (hi << 16);
+                }
+            }
+        }
+    };
 
     // B block i of this thread: id = i*NT + tid; k-block id % (BK/8) (so the
     // eight lanes of a group write eight different k-chunks of one LDS row),
@@ -93,24 +125,10 @@ gemm_f16_kernel(GemmParams p)
     u32x4 rb[T::B_PT][8];
 
     auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < T::A_PT; ++i) {
-            const bool rok = m0 + a_r0 + i * A_RSTEP < M;
-            const int kk = k0 + a_c * 8;
-            const uint16_t *src = a_ptr + i * a_istep + k0;
-            if (VEC) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (rok && kk < K)
-                    v = *reinterpret_cast<const u32x4 *>(src);
-                ra[i] = v;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t lo = (rok && kk + 2 * j < K) ? ld_u16(src + 2 * j) : 0u;
-                    const uint32_t hi = (rok && kk + 2 * j + 1 < K) ? ld_u16(src + 2 * j + 1) : 0u;
-                    ra[i][j] = lo | (hi << 16);
-                }
-            }
+        load_rows(a_ptr, a_istep, m0, M, T::A_PT, ra, k0);
+        if (BT) {
+            load_rows(bt_ptr, bt_istep, n0, N, T::BT_PT, rbt, k0);
+            return;
         }
 #pragma unroll
         for (int i = 0; i < T::B_PT; ++i) {
@@ -146,6 +164,15 @@ gemm_f16_kernel(GemmParams p)
             const int row = a_r0 + i * A_RSTEP;
             const int c = a_c ^ swz<BK * 2>(row);
             *reinterpret_cast<u32x4 *>(&As[buf][row * BK + c * 8]) = ra[i];
+        }
+        if (BT) {
+#pragma unroll
+            for (int i = 0; i < (BT ? T::BT_PT : 1); ++i) {
+                const int row = a_r0 + i * A_RSTEP;
+                const int c = a_c ^ swz<BK * 2>(row);
+                *reinterpret_cast<u32x4 *>(&Bs[buf][row * BK + c * 8]) = rbt[i];
+            }
+            return;
         }
 #pragma unroll
         for (int i = 0; i < T::B_PT; ++i) {
@@ -256,7 +283,11 @@ gemm_f16_kernel(GemmParams p)
 // publishes stage kt+2, so during stage kt each wave already reads the first
 // operands of stage kt+1 and no LDS latency is exposed after a barrier; the
 // copies of stage kt+3 are issued into the buffer stage kt-1 used.
-template <int EPI, bool BF16>
+//
+// With BT (B given N-by-K, k contiguous) B is copied and read exactly like A:
+// 256 rows x 64 bytes, the same swizzle, 128-bit operand reads, no transposing
+// loads.
+template <int EPI, bool BF16, bool BT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_f16_direct_kernel(GemmParams p)
 {
@@ -277,7 +308,8 @@ gemm_f16_direct_kernel(GemmParams p)
     int K;
     const int kb = split_range(p, K);
     const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A) + kb;
-    const uint16_t *__restrict__ B = static_cast<const uint16_t *>(p.B) + (int64_t)kb * p.ldb;
+    const uint16_t *__restrict__ B =
+        static_cast<const uint16_t *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
     const int M = p.M, N = p.N;
 
     // Copy sources. A copy j of this wave: rows (wave*4 + j)*16 + lane/4.
@@ -285,6 +317,8 @@ gemm_f16_direct_kernel(GemmParams p)
     const int a_row0 = wave * COPIES * 16 + (lane >> 2);
     const uint16_t *a_src = A + (int64_t)(m0 + a_row0) * p.lda + a_c * 8;
     const int64_t a_jstep = (int64_t)16 * p.lda;
+    const uint16_t *bt_src = B + (int64_t)(n0 + a_row0) * p.ldb + a_c * 8;   // BT
+    const int64_t bt_jstep = (int64_t)16 * p.ldb;
     // B copy j of this wave: k-row (wave*4 + j)*2 + lane/32; the lane's 16
     // bytes hold logical unit (((lane%32)/2) ^ (k%4)), half (lane%2).
     const int b_kr0 = wave * COPIES * 2 + (lane >> 5);
@@ -299,6 +333,17 @@ gemm_f16_direct_kernel(GemmParams p)
                 lds_dma_16(a_src + j * a_jstep + k0, dst);
             else
                 lds_zero_16(dst + lane * 16);
+        }
+        if (BT) {
+#pragma unroll
+            for (int j = 0; j < COPIES; ++j) {
+                const uint32_t dst = bs + (wave * COPIES + j) * 1024;
+                if (n0 + a_row0 + j * 16 < N && k0 + a_c * 8 < K)
+                    lds_dma_16(bt_src + j * bt_jstep + k0, dst);
+                else
+                    lds_zero_16(dst + lane * 16);
+            }
+            return;
         }
 #pragma unroll
         for (int j = 0; j < COPIES; ++j) {
@@ -335,6 +380,15 @@ gemm_f16_direct_kernel(GemmParams p)
             const int row = wm * WTM + fm * 32 + l32;
             const int c = (2 * s + h) ^ ((row >> 2) & 3);
             af[fm] = *reinterpret_cast<const f16x8 *>(&as[row * BK + c * 8]);
+        }
+        if (BT) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int row = wn * WTN + fn * 32 + l32;
+                const int c = (2 * s + h) ^ ((row >> 2) & 3);
+                bf[fn] = *reinterpret_cast<const f16x8 *>(&bs[row * BK + c * 8]);
+            }
+            return;
         }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
@@ -411,7 +465,7 @@ using F16_L = F16Tile<256, 256, 64>;
 using F16_S = F16Tile<128, 128, 64>;
 using F16_XS = F16Tile<64, 64, 64>;
 
-template <class T, int WPE, bool BF16>
+template <class T, int WPE, bool BF16, bool BT>
 static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
     GemmParams p = p0;
@@ -422,7 +476,7 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split)), block(T::NT);
 #define LL_F16_LAUNCH(E, V) \
-    hipLaunchKernelGGL((gemm_f16_kernel<T, E, V, WPE, BF16>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((gemm_f16_kernel<T, E, V, WPE, BF16, BT>), grid, block, 0, s, p)
     if (vec) {
         if (epi == EPI_GEMM_BETA0) LL_F16_LAUNCH(EPI_GEMM_BETA0, true);
         else if (epi == EPI_GEMM_BETA) LL_F16_LAUNCH(EPI_GEMM_BETA, true);
@@ -444,11 +498,11 @@ const TileInfo kF16Tiles[kF16NumTiles] = {
     {F16_XS::BM, F16_XS::BN, 2, 0.22f, 0.28f, "f16_64x64x64"},
 };
 
-template <bool BF16>
+template <bool BF16, bool BT>
 static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
     if (!vec)
-        return launch_t<F16_L, 1, BF16>(p0, epi, vec, s);
+        return launch_t<F16_L, 1, BF16, BT>(p0, epi, vec, s);
     GemmParams p = p0;
     p.tiles_m = (p.M + 255) / 256;
     p.tiles_n = (p.N + 255) / 256;
@@ -457,32 +511,42 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split)), block(256);
     if (epi == EPI_GEMM_BETA0)
-        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_GEMM_BETA0, BF16>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_GEMM_BETA0, BF16, BT>), grid, block, 0, s, p);
     else if (epi == EPI_GEMM_BETA)
-        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_GEMM_BETA, BF16>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_GEMM_BETA, BF16, BT>), grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_ATOMIC, BF16>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_ATOMIC, BF16, BT>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 
-template <bool BF16>
+template <bool BF16, bool BT>
 static hipError_t launch_16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
 {
     switch (tile) {
-    case 0: return launch_direct<BF16>(p, epi, vec, s);
-    case 1: return launch_t<F16_S, 2, BF16>(p, epi, vec, s);
-    default: return launch_t<F16_XS, 2, BF16>(p, epi, vec, s);
+    case 0: return launch_direct<BF16, BT>(p, epi, vec, s);
+    case 1: return launch_t<F16_S, 2, BF16, BT>(p, epi, vec, s);
+    default: return launch_t<F16_XS, 2, BF16, BT>(p, epi, vec, s);
     }
 }
 
 hipError_t launch_gemm_f16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
 {
-    return launch_16<false>(p, tile, epi, vec, s);
+    return launch_16<false, false>(p, tile, epi, vec, s);
 }
 
 hipError_t launch_gemm_bf16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
 {
-    return launch_16<true>(p, tile, epi, vec, s);
+    return launch_16<true, false>(p, tile, epi, vec, s);
+}
+
+hipError_t launch_gemm_f16_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
+{
+    return launch_16<false, true>(p, tile, epi, vec, s);
+}
+
+hipError_t launch_gemm_bf16_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
+{
+    return launch_16<true, true>(p, tile, epi, vec, s);
 }
 
 }  // namespace ll

@@ -42,20 +42,91 @@ struct F32Tile {
     static constexpr int WTM = BM / 2, WTN = BN / 2;
     static constexpr int FM = WTM / 32, FN = WTN / 32;
     static constexpr int KH = BK / 2;              // k values per lane half per stage
-    static constexpr int ACPR = BK / 4;            // 16-byte chunks per A row
-    static constexpr int A_PT = BM * ACPR / NT;    // A chunks per thread
-    static constexpr int BCPR = BN / 4;            // 16-byte chunks per B row
-    static constexpr int B_PT = BK * BCPR / NT;    // B chunks per thread
-    static constexpr int BNP = BN + 4;             // padded B row (floats)
+    static constexpr int CPR = BK / 4;             // 16-byte chunks per k-contiguous row
+    static constexpr int A_PT = BM * CPR / NT;     // A chunks per thread
+    static constexpr int BCPR = BN / 4;            // 16-byte chunks per B k-row (B K-by-N)
+    static constexpr int B_PT = BK * BCPR / NT;    // B chunks per thread (B K-by-N)
+    static constexpr int BT_PT = BN * CPR / NT;    // B chunks per thread (B N-by-K)
+    static constexpr int BNP = BN + 4;             // padded B k-row (floats)
     static constexpr int A_STAGE = BM * BK;        // floats
-    static constexpr int B_STAGE = BK * BNP;
+    static constexpr int B_STAGE = BK * BNP;       // >= BN * BK, fits either B layout
     static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
-    static_assert(A_PT >= 1 && A_PT * NT == BM * ACPR, "A chunks must split evenly");
+    static_assert(A_PT >= 1 && A_PT * NT == BM * CPR, "A chunks must split evenly");
     static_assert(B_PT >= 1 && B_PT * NT == BK * BCPR, "B chunks must split evenly");
+    static_assert(BT_PT >= 1 && BT_PT * NT == BN * CPR, "B^T chunks must split evenly");
     static_assert(KH % 4 == 0, "BK must be a multiple of 8");
 };
 
-template <class T, int EPI, bool VEC, int WPE>
+// A panel of ROWS rows, each BK consecutive k of one row of a k-contiguous
+// matrix (A, or B given N-by-K), staged through registers into a swizzled
+// [row][k] LDS tile. Thread t owns chunks (t + i*NT): row (t + i*NT)/CPR,
+// 16-byte chunk t%CPR.
+template <class T, int ROWS, bool VEC>
+struct RowPanel {
+    static constexpr int CPR = T::CPR, BK = T::BK;
+    static constexpr int PT = ROWS * CPR / T::NT;
+    static constexpr int RSTEP = T::NT / CPR;
+    const float *ptr;   // chunk 0 of this thread at k = 0
+    int64_t istep;      // RSTEP rows
+    int r0, c, row_base, rows;
+    f32x4 reg[PT];
+
+    __device__ void init(const float *base, int64_t ld, int first_row, int nrows, int tid)
+    {
+        c = tid % CPR;
+        r0 = tid / CPR;
+        row_base = first_row;
+        rows = nrows;
+        ptr = base + (int64_t)(first_row + r0) * ld + c * 4;
+        istep = (int64_t)RSTEP * ld;
+    }
+    __device__ void load(int k0, int K)
+    {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const bool rok = row_base + r0 + i * RSTEP < rows;
+            const float *src = ptr + i * istep + k0;
+            const int kk = k0 + c * 4;
+            if (VEC) {
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                if (rok && kk < K)
+                    v = *reinterpret_cast<const f32x4 *>(src);
+                reg[i] = v;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    reg[i][j] = (rok && kk + j < K) ? src[j] : 0.0f;
+            }
+        }
+    }
+    __device__ void store(float *lds) const
+    {
+#pragma unroll
+        for (int i = 0; i < PT; ++i) {
+            const int row = r0 + i * RSTEP;
+            *reinterpret_cast<f32x4 *>(&lds[row * BK + (c ^ swz<BK * 4>(row)) * 4]) = reg[i];
+        }
+    }
+};
+
+// The MFMA operand of one 32-row block: the lane's row, k = h*KH .. h*KH+KH-1,
+// as KH/4 vectors read from a swizzled [row][k] tile.
+template <class T>
+__device__ __forceinline__ void read_rows(const float *lds, int row, int h, f32x4 (&dst)[T::KH / 4])
+{
+#pragma unroll
+    for (int q = 0; q < T::KH / 4; ++q) {
+        const int c = (h * (T::KH / 4) + q) ^ swz<T::BK * 4>(row);
+        dst[q] = *reinterpret_cast<const f32x4 *>(&lds[row * T::BK + c * 4]);
+    }
+}
+
+// BT = false: B is K-by-N (row-major, n contiguous); its k-rows go to LDS as
+// [k][n] (rows padded by 4 floats) and each lane reads one float per MFMA step.
+// BT = true: B is given N-by-K (k contiguous, e.g. a fully-connected weight
+// stored [out][in]); it is staged exactly like A, as swizzled [n][k] rows, and
+// read with 128-bit LDS loads like A.
+template <class T, int EPI, bool VEC, int WPE, bool BT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f32_kernel(GemmParams p)
 {
@@ -72,41 +143,28 @@ gemm_f32_kernel(GemmParams p)
     int K;
     const int kb = split_range(p, K);
     const float *__restrict__ A = static_cast<const float *>(p.A) + kb;
-    const float *__restrict__ B = static_cast<const float *>(p.B) + (int64_t)kb * p.ldb;
+    const float *__restrict__ B =
+        static_cast<const float *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
     const int M = p.M, N = p.N;
 
-    // Fixed per-thread load assignment: A chunk i is row a_row(i), chunk a_c;
-    // B chunk i is k-row b_k(i), column chunk b_c.
-    const int a_c = tid % T::ACPR;
-    const int a_r0 = tid / T::ACPR;
-    constexpr int A_RSTEP = T::NT / T::ACPR;
+    RowPanel<T, BM, VEC> pa;
+    pa.init(A, p.lda, m0, M, tid);
+    RowPanel<T, BN, VEC> pbt;   // B given N-by-K
+    // B given K-by-N: chunk i is k-row b_k0 + i*B_KSTEP, columns n0 + 4*b_c ..
     const int b_c = tid % T::BCPR;
     const int b_k0 = tid / T::BCPR;
     constexpr int B_KSTEP = T::NT / T::BCPR;
-
-    const float *a_ptr = A + (int64_t)(m0 + a_r0) * p.lda + a_c * 4;
     const float *b_ptr = B + (int64_t)b_k0 * p.ldb + n0 + b_c * 4;
-    const int64_t a_istep = (int64_t)A_RSTEP * p.lda;
     const int64_t b_istep = (int64_t)B_KSTEP * p.ldb;
-
-    f32x4 ra[T::A_PT], rb[T::B_PT];
+    f32x4 rb[BT ? 1 : T::B_PT];
+    if (BT)
+        pbt.init(B, p.ldb, n0, N, tid);
 
     auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < T::A_PT; ++i) {
-            const bool rok = m0 + a_r0 + i * A_RSTEP < M;
-            const float *src = a_ptr + i * a_istep + k0;
-            const int kk = k0 + a_c * 4;
-            if (VEC) {
-                f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (rok && kk < K)
-                    v = *reinterpret_cast<const f32x4 *>(src);
-                ra[i] = v;
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    ra[i][j] = (rok && kk + j < K) ? src[j] : 0.0f;
-            }
+        pa.load(k0, K);
+        if (BT) {
+            pbt.load(k0, K);
+            return;
         }
 #pragma unroll
         for (int i = 0; i < T::B_PT; ++i) {
@@ -127,11 +185,10 @@ gemm_f32_kernel(GemmParams p)
     };
 
     auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < T::A_PT; ++i) {
-            const int row = a_r0 + i * A_RSTEP;
-            const int c = a_c ^ swz<BK * 4>(row);
-            *reinterpret_cast<f32x4 *>(&As[buf][row * BK + c * 4]) = ra[i];
+        pa.store(As[buf]);
+        if (BT) {
+            pbt.store(Bs[buf]);
+            return;
         }
 #pragma unroll
         for (int i = 0; i < T::B_PT; ++i) {
@@ -161,30 +218,39 @@ gemm_f32_kernel(GemmParams p)
         if (kt + 1 < nk)
             gload((kt + 1) * BK);
 
-        // A fragments for the whole stage: row = lane's row, k = h*KH .. h*KH+KH-1.
+        // A fragments for the whole stage.
         f32x4 af[FM][KH / 4];
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int row = wm * T::WTM + fm * 32 + l32;
-#pragma unroll
-            for (int q = 0; q < KH / 4; ++q) {
-                const int c = (h * (KH / 4) + q) ^ swz<BK * 4>(row);
-                af[fm][q] = *reinterpret_cast<const f32x4 *>(&As[cur][row * BK + c * 4]);
-            }
-        }
-        const float *bsrc = &Bs[cur][(h * KH) * BNP + wn * T::WTN + l32];
-#pragma unroll
-        for (int s = 0; s < KH; ++s) {
-            float bf[FN];
+        for (int fm = 0; fm < FM; ++fm)
+            read_rows<T>(As[cur], wm * T::WTM + fm * 32 + l32, h, af[fm]);
+        if (BT) {
+            f32x4 bt[FN][KH / 4];
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                bf[fn] = bsrc[s * BNP + fn * 32];
+                read_rows<T>(Bs[cur], wn * T::WTN + fn * 32 + l32, h, bt[fn]);
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
+            for (int s = 0; s < KH; ++s)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            af[fm][s >> 2][s & 3], bt[fn][s >> 2][s & 3], acc[fm][fn], 0, 0, 0);
+        } else {
+            const float *bsrc = &Bs[cur][(h * KH) * BNP + wn * T::WTN + l32];
+#pragma unroll
+            for (int s = 0; s < KH; ++s) {
+                float bf[FN];
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                        af[fm][s >> 2][s & 3], bf[fn], acc[fm][fn], 0, 0, 0);
+                    bf[fn] = bsrc[s * BNP + fn * 32];
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            af[fm][s >> 2][s & 3], bf[fn], acc[fm][fn], 0, 0, 0);
+            }
         }
 
         if (kt + 1 < nk)
@@ -211,7 +277,7 @@ using F32_M = F32Tile<256, 128, 16>;   // 128x64 per wave
 using F32_S = F32Tile<128, 128, 16>;   // 64x64 per wave
 using F32_XS = F32Tile<64, 64, 16>;    // 32x32 per wave
 
-template <class T, int WPE>
+template <class T, int WPE, bool BT>
 static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
     GemmParams p = p0;
@@ -222,7 +288,7 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split)), block(T::NT);
 #define LL_F32_LAUNCH(E, V) \
-    hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE, BT>), grid, block, 0, s, p)
     if (vec) {
         if (epi == EPI_GEMM_BETA0) LL_F32_LAUNCH(EPI_GEMM_BETA0, true);
         else if (epi == EPI_GEMM_BETA) LL_F32_LAUNCH(EPI_GEMM_BETA, true);
@@ -248,14 +314,25 @@ const TileInfo kF32Tiles[kF32NumTiles] = {
     {F32_XS::BM, F32_XS::BN, 2, 0.40f, 0.72f, "f32_64x64x16"},
 };
 
-hipError_t launch_gemm_f32(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
+template <bool BT>
+static hipError_t launch_f32(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
 {
     switch (tile) {
-    case 0: return launch_t<F32_L, 1>(p, epi, vec, s);
-    case 1: return launch_t<F32_M, 2>(p, epi, vec, s);
-    case 2: return launch_t<F32_S, 2>(p, epi, vec, s);
-    default: return launch_t<F32_XS, 2>(p, epi, vec, s);
+    case 0: return launch_t<F32_L, 1, BT>(p, epi, vec, s);
+    case 1: return launch_t<F32_M, 2, BT>(p, epi, vec, s);
+    case 2: return launch_t<F32_S, 2, BT>(p, epi, vec, s);
+    default: return launch_t<F32_XS, 2, BT>(p, epi, vec, s);
     }
+}
+
+hipError_t launch_gemm_f32(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
+{
+    return launch_f32<false>(p, tile, epi, vec, s);
+}
+
+hipError_t launch_gemm_f32_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
+{
+    return launch_f32<true>(p, tile, epi, vec, s);
 }
 
 }  // namespace ll

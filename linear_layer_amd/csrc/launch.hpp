@@ -25,8 +25,12 @@ extern const TileInfo kF16Tiles[kF16NumTiles];
 // alignment and divisibility). Fills p.tiles_m / p.tiles_n itself; the grid
 // has ceil(K / p.k_split) K-splits along y (EPI_ATOMIC when more than one).
 hipError_t launch_gemm_f32(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
+// As above with B given N-by-K (C = alpha*A*B^T + beta*C).
+hipError_t launch_gemm_f32_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
 hipError_t launch_gemm_f16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
 hipError_t launch_gemm_bf16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
+hipError_t launch_gemm_f16_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
+hipError_t launch_gemm_bf16_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
 
 // C = beta*C over an M x N matrix (beta == 0 writes zeros without reading C).
 hipError_t launch_scale(float *C, int64_t ldc, int M, int N, float beta, hipStream_t s);

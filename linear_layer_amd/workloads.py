@@ -18,7 +18,9 @@ products (page "GPU架构下的矩阵乘法深入优化" measures 4096 cubed, pa
 FP16-input / FP32-accumulate product of the tensor-core section of page
 "GPU架构下的矩阵乘法深入优化" (section 6). The sixth is the same 16-bit
 product with bfloat16 inputs (page "GEMM 优化详解", "进一步优化方向": the
-matrix units take FP16 or BF16).
+matrix units take FP16 or BF16); the seventh and eighth give B (W) N-by-K, the
+[out][in] weight layout and the B^T of Q*K^T (page "GEMM 优化详解", table
+"为什么 GEMM 重要"). B (W) of the transposed forms is drawn in its N-by-K shape.
 """
 from __future__ import annotations
 
@@ -31,7 +33,8 @@ import torch
 class Workload:
     index: int          # 1-based workload number, also the seed base
     name: str
-    kind: str           # "gemm_f32", "gemm_f16f32", "gemm_bf16f32" or "linear"
+    kind: str           # "gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear" (and _nt forms:
+                        # B given N-by-K)
     M: int
     N: int
     K: int
@@ -55,7 +58,15 @@ WORKLOADS = {
     "gemm_f16f32_8192": Workload(5, "gemm_f16f32_8192", "gemm_f16f32", 8192, 8192, 8192),
     # the bfloat16 variant of the 16-bit product (same shape, inputs rounded to bf16)
     "gemm_bf16f32_8192": Workload(6, "gemm_bf16f32_8192", "gemm_bf16f32", 8192, 8192, 8192),
+    # transposed-B forms: the same fully-connected layer with its weight stored
+    # [out][in] (N-by-K), and the 16-bit product with B given N-by-K
+    "linear_relu_nt_2047x4096x11008": Workload(7, "linear_relu_nt_2047x4096x11008", "linear_nt",
+                                               2047, 11008, 4096, act=1, scale=1.0 / 64.0),
+    "gemm_f16f32_nt_8192": Workload(8, "gemm_f16f32_nt_8192", "gemm_f16f32_nt", 8192, 8192, 8192),
 }
+
+HALF_KINDS = ("gemm_f16f32", "gemm_bf16f32", "gemm_f16f32_nt")
+B_TRANSPOSED_KINDS = ("linear_nt", "gemm_f16f32_nt")
 
 
 def generator(seed: int) -> torch.Generator:
@@ -111,22 +122,24 @@ def make_inputs(w: Workload, integer: bool = False, M: int | None = None,
     K = w.K if K is None else K
     s = 100 * w.index
     out = {}
+    bshape = (N, K) if w.kind in B_TRANSPOSED_KINDS else (K, N)
+    linear = w.kind in ("linear", "linear_nt")
     if integer:
-        lim = 8 if w.kind in ("gemm_f16f32", "gemm_bf16f32") else 2
+        lim = 8 if w.kind in HALF_KINDS else 2
         out["A"] = integers((M, K), s + 0, -lim, lim)
-        out["B"] = integers((K, N), s + 1, -lim, lim)
+        out["B"] = integers(bshape, s + 1, -lim, lim)
         if w.beta != 0.0:
             out["C"] = integers((M, N), s + 2, -4, 4)
-        if w.kind == "linear":
+        if linear:
             out["bias"] = integers((N,), s + 3, -4, 4)
     else:
         out["A"] = uniform((M, K), s + 0, w.scale)
-        out["B"] = uniform((K, N), s + 1, w.scale)
+        out["B"] = uniform(bshape, s + 1, w.scale)
         if w.beta != 0.0:
             out["C"] = uniform((M, N), s + 2)
-        if w.kind == "linear":
+        if linear:
             out["bias"] = bias_uniform(N, s + 3)
-    if w.kind == "gemm_f16f32":
+    if w.kind in ("gemm_f16f32", "gemm_f16f32_nt"):
         out["A"] = to_half(out["A"])
         out["B"] = to_half(out["B"])
     if w.kind == "gemm_bf16f32":

@@ -68,6 +68,29 @@ def test_invalid_arguments(f16):
     assert call_gemm(4, 4, 4, C=PB - 16, f16=f16) == E
 
 
+@pytest.mark.parametrize("name", ["gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt"])
+def test_nt_leading_dimension_rule(name):
+    """With B given N-by-K, ldb is bounded by K, not N."""
+    fn = getattr(ll.load(), name)
+    E = ll.ERR_INVALID_VALUE
+    # M=4, N=16, K=8: ldb = 8 is fine for B^T (would be too small for a K-by-N B)
+    ok = fn(4, 16, 8, 1.0, PA, 8, PB, 8, 0.0, PC, 16, None)
+    assert ok in (ll.ERR_NO_DEVICE, ll.OK, ll.ERR_UNSUPPORTED_ARCH)
+    assert fn(4, 16, 8, 1.0, PA, 8, PB, 7, 0.0, PC, 16, None) == E          # ldb < K
+    assert fn(4, 16, 8, 1.0, PA, 8, PB, 8, 0.0, PC, 15, None) == E          # ldc < N
+    assert fn(4, 16, 8, 1.0, PA, 8, PB, 8, 0.0, PB + 64, 16, None) == E   # C inside B
+    assert fn(0, 16, 8, 1.0, None, 8, None, 8, 0.0, None, 16, None) == ll.OK
+
+
+def test_linear_nt_leading_dimension_rule():
+    lib = ll.load()
+    E = ll.ERR_INVALID_VALUE
+    ok = lib.linear_bias_act_nt(4, 16, 8, PA, 8, PB, 8, None, 1, PC, 16, None)
+    assert ok in (ll.ERR_NO_DEVICE, ll.OK, ll.ERR_UNSUPPORTED_ARCH)
+    assert lib.linear_bias_act_nt(4, 16, 8, PA, 8, PB, 7, None, 1, PC, 16, None) == E   # ldw < K
+    assert lib.linear_bias_act_nt(4, 16, 8, PA, 8, PB, 8, None, 3, PC, 16, None) == E   # unknown act
+
+
 def test_quick_returns_touch_nothing():
     # M == 0 or N == 0: OK with no device and even with NULL pointers
     assert call_gemm(0, 5, 5, A=None, B=None, C=None) == ll.OK

@@ -7,7 +7,7 @@ is tiny (e.g. alpha == 0 or a zero row). Integer-valued inputs must give the
 oracle's result bit for bit (every partial sum is an exact fp32 integer).
 
 Sizes: small cases span several tiles of every tile shape with ragged tails
-in M, N and K and are compared in full; the five full-size workloads are run
+in M, N and K and are compared in full; the full-size workloads are run
 in the launch configuration the bench times and compared on sampled elements
 (plus whole edge rows/columns) and on row/column checksums that cover every
 element.
@@ -116,6 +116,24 @@ def run_linear(X, W, b, act):
     bd = b.to(DEV) if b is not None else None
     Yd = torch.full((X.shape[0], W.shape[1]), float("nan"), device=DEV)
     ll.linear_bias_act(Xd, Wd, bd, act, Yd)
+    torch.cuda.synchronize()
+    return np32(Yd)
+
+
+def run_nt(fn, A, B, alpha=1.0, beta=0.0, C=None):
+    """C = alpha*A*B^T + beta*C through one of the _nt entry points (B is N-by-K)."""
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    Cd = (C.clone() if C is not None else torch.full((A.shape[0], B.shape[0]), float("nan"))).to(DEV)
+    fn(Ad, Bd, Cd, alpha, beta)
+    torch.cuda.synchronize()
+    return np32(Cd)
+
+
+def run_linear_nt(X, W, b, act):
+    Xd, Wd = X.to(DEV), W.to(DEV)
+    bd = b.to(DEV) if b is not None else None
+    Yd = torch.full((X.shape[0], W.shape[0]), float("nan"), device=DEV)
+    ll.linear_bias_act_nt(Xd, Wd, bd, act, Yd)
     torch.cuda.synchronize()
     return np32(Yd)
 
@@ -429,6 +447,143 @@ def test_errors_raise():
         ll.gemm_f32(A, A, A)  # C overlaps A
 
 
+# ---- transposed B (B given N-by-K): every tile, ragged tails -----------------
+
+NT16 = {"f16": (ll.gemm_f16f32_nt, torch.float16, False),
+        "bf16": (ll.gemm_bf16f32_nt, torch.bfloat16, True)}
+
+
+@pytest.mark.parametrize("t", T32)
+@pytest.mark.parametrize("M,N,K", SMALL + [(301, 517, 203), (70, 33, 5)])
+def test_f32_nt_small(t, M, N, K, tile):
+    tile(F32, t)
+    A, B = rand((M, K), 71), rand((N, K), 72)
+    C = rand((M, N), 73)
+    for alpha, beta in ((1.0, 0.0), (1.5, 0.5)):
+        got = run_nt(ll.gemm_f32_nt, A, B, alpha, beta, C if beta else None)
+        R, T = oracle.gemm(np32(A), np32(B), alpha, beta, np32(C), b_trans=True)
+        assert_close(got, R, T, f"f32_nt tile {t} {M}x{N}x{K} a={alpha} b={beta}")
+
+
+@pytest.mark.parametrize("t", T32)
+def test_f32_nt_strided_b(t, tile):
+    """B as a column slice of a wider matrix: ldb = K + 12 (vector path), K + 3 (scalar)."""
+    tile(F32, t)
+    M, N, K = 300, 270, 132
+    A = rand((M, K), 74)
+    for pad in (12, 3):
+        Bw = rand((N, K + pad), 75)
+        B = Bw[:, :K]
+        Bd = Bw.to(DEV)[:, :K]
+        Cd = torch.full((M, N), float("nan"), device=DEV)
+        ll.gemm_f32_nt(A.to(DEV), Bd, Cd)
+        torch.cuda.synchronize()
+        R, T = oracle.gemm(np32(A), np32(B).copy(), b_trans=True)
+        assert_close(np32(Cd), R, T, f"f32_nt tile {t} ldb={K + pad}")
+
+
+@pytest.mark.parametrize("t", T32)
+def test_f32_nt_matches_explicit_transpose(t, tile, split):
+    """A*B^T through the _nt entry point equals gemm_f32 on B^T made contiguous, bit for bit:
+    both feed the matrix units the same operands in the same k order. (One K-split:
+    split-K adds its partial sums atomically, in no fixed order.)"""
+    tile(F32, t)
+    split(1)
+    M, N, K = 520, 392, 200
+    A, B = rand((M, K), 76), rand((N, K), 77)
+    got = run_nt(ll.gemm_f32_nt, A, B)
+    ref = run_gemm_f32(A, B.t().contiguous())
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("t", T16)
+@pytest.mark.parametrize("which", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K", [(600, 520, 192), (257, 264, 64), (33, 70, 40), (301, 517, 203), (1, 8, 8)])
+def test_16bit_nt_small(t, which, M, N, K, tile):
+    tile(F16, t)
+    fn, dt, bf = NT16[which]
+    A, B = rand((M, K), 81).to(dt), rand((N, K), 82).to(dt)
+    C = rand((M, N), 83)
+    for alpha, beta in ((1.0, 0.0), (-0.75, 0.5)):
+        got = run_nt(fn, A, B, alpha, beta, C if beta else None)
+        R, T = oracle.gemm(bits16(A), bits16(B), alpha, beta, np32(C), bf16=bf, b_trans=True)
+        assert_close(got, R, T, f"{which}_nt tile {t} {M}x{N}x{K} a={alpha} b={beta}")
+
+
+@pytest.mark.parametrize("t", T16)
+@pytest.mark.parametrize("which", ["f16", "bf16"])
+def test_16bit_nt_matches_explicit_transpose(t, which, tile, split):
+    tile(F16, t)
+    split(1)
+    fn, dt, _ = NT16[which]
+    nn = ll.gemm_bf16f32 if which == "bf16" else ll.gemm_f16f32
+    M, N, K = 520, 392, 192
+    A, B = rand((M, K), 84).to(dt), rand((N, K), 85).to(dt)
+    got = run_nt(fn, A, B)
+    ref = run_nt(lambda a, b, c, al, be: nn(a, b.t().contiguous(), c, al, be), A, B)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("t", T32)
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_linear_nt_small(t, act, with_bias, tile):
+    tile(F32, t)
+    for M, N, K in ((300, 520, 136), (257, 70, 33)):
+        X, W = rand((M, K), 91, 0.125), rand((N, K), 92, 0.125)
+        b = wl.bias_uniform(N, 93) if with_bias else None
+        got = run_linear_nt(X, W, b, act)
+        R, T = oracle.linear(np32(X), np32(W), None if b is None else np32(b), act, w_trans=True)
+        assert_close(got, R, T, f"linear_nt tile {t} {M}x{N}x{K} act={act} bias={with_bias}")
+
+
+@pytest.mark.parametrize("t", T32)
+def test_nt_integer_exact(t, tile):
+    tile(F32, t)
+    tile(F16, min(t, len(T16) - 1))
+    M, N, K = 333, 301, 260
+    A, B = wl.integers((M, K), 94, -2, 2), wl.integers((N, K), 95, -2, 2)
+    R, _ = oracle.gemm(np32(A), np32(B), b_trans=True)
+    assert_exact(run_nt(ll.gemm_f32_nt, A, B), R, f"f32_nt tile {t}")
+    A8, B8 = wl.integers((M, K), 96, -8, 8), wl.integers((N, K), 97, -8, 8)
+    for fn, dt, bf in NT16.values():
+        R, _ = oracle.gemm(bits16(A8.to(dt)), bits16(B8.to(dt)), bf16=bf, b_trans=True)
+        assert_exact(run_nt(fn, A8.to(dt), B8.to(dt)), R, f"16-bit nt bf16={bf}")
+    b = wl.integers((N,), 98, -4, 4)
+    R, _ = oracle.linear(np32(A), np32(B), np32(b), 1, w_trans=True)
+    assert_exact(run_linear_nt(A, B, b, 1), R, f"linear_nt tile {t}")
+
+
+@pytest.mark.parametrize("S", [2, 5])
+def test_nt_split_k(S, split):
+    split(S)
+    M, N, K = 200, 264, 1000
+    A, B, C = rand((M, K), 101), rand((N, K), 102), rand((M, N), 103)
+    got = run_nt(ll.gemm_f32_nt, A, B, 1.5, 0.5, C)
+    R, T = oracle.gemm(np32(A), np32(B), 1.5, 0.5, np32(C), b_trans=True)
+    assert_close(got, R, T, f"f32_nt split {S}")
+    for which, (fn, dt, bf) in NT16.items():
+        A16, B16 = A.to(dt), B.to(dt)
+        got = run_nt(fn, A16, B16)
+        R, T = oracle.gemm(bits16(A16), bits16(B16), bf16=bf, b_trans=True)
+        assert_close(got, R, T, f"{which}_nt split {S}")
+    b = wl.bias_uniform(N, 104)
+    got = run_linear_nt(A, B, b, 1)
+    R, T = oracle.linear(np32(A), np32(B), np32(b), 1, w_trans=True)
+    assert_close(got, R, T, f"linear_nt split {S}")
+
+
+def test_nt_shape_errors():
+    A = torch.zeros((8, 16), device=DEV)
+    B = torch.zeros((12, 16), device=DEV)
+    C = torch.zeros((8, 12), device=DEV)
+    ll.gemm_f32_nt(A, B, C)
+    with pytest.raises((ValueError, ll.LinearLayerError)):
+        ll.gemm_f32_nt(A, B.t(), C)          # B given K-by-N
+    with pytest.raises((ValueError, ll.LinearLayerError)):
+        ll.linear_bias_act_nt(A, B, torch.zeros(16, device=DEV), 1, C)   # bias of length K
+
+
 # ---- full-size workloads, as the bench launches them ------------------------
 
 def sample_positions(M, N, n, seed):
@@ -512,6 +667,33 @@ def test_full_gemm_16bit(name):
     checksums(got, A.double().numpy(), B.double().numpy())
 
 
+def test_full_linear_nt():
+    w = wl.WORKLOADS["linear_relu_nt_2047x4096x11008"]
+    x = wl.make_inputs(w)
+    X, W, b = x["A"], x["B"], x["bias"]
+    got = run_linear_nt(X, W, b, w.act)
+    rows, cols = sample_positions(w.M, w.N, 20000, w.index)
+    R, T = oracle.linear_at(np32(X), np32(W), rows, cols, np32(b), w.act, w_trans=True)
+    ratio = assert_close(got[rows, cols], R, T, w.name)
+    print(f"{w.name}: max err/t on samples = {ratio:.3g}")
+    got0 = run_linear_nt(X, W, b, 0)
+    checksums(got0, np32(X).astype(np.float64), np32(W).T.astype(np.float64),
+              bias=np32(b).astype(np.float64))
+    assert np.array_equal(got, np.where(got0 > 0, got0, np.float32(0)))
+
+
+def test_full_gemm_f16_nt():
+    w = wl.WORKLOADS["gemm_f16f32_nt_8192"]
+    x = wl.make_inputs(w)
+    A, B = x["A"], x["B"]
+    got = run_nt(ll.gemm_f16f32_nt, A, B)
+    rows, cols = sample_positions(w.M, w.N, 20000, w.index)
+    R, T = oracle.gemm_at(bits16(A), bits16(B), rows, cols, b_trans=True)
+    ratio = assert_close(got[rows, cols], R, T, w.name)
+    print(f"{w.name}: max err/t on samples = {ratio:.3g}")
+    checksums(got, A.double().numpy(), B.double().numpy().T)
+
+
 @pytest.mark.parametrize("name", list(wl.WORKLOADS))
 def test_full_integer_exact(name):
     w = wl.WORKLOADS[name]
@@ -526,6 +708,12 @@ def test_full_integer_exact(name):
         bf = w.kind == "gemm_bf16f32"
         got = (run_gemm_bf16 if bf else run_gemm_f16)(A, B)
         R, _ = oracle.gemm_at(bits16(A), bits16(B), rows, cols, bf16=bf)
+    elif w.kind == "gemm_f16f32_nt":
+        got = run_nt(ll.gemm_f16f32_nt, A, B)
+        R, _ = oracle.gemm_at(bits16(A), bits16(B), rows, cols, b_trans=True)
+    elif w.kind == "linear_nt":
+        got = run_linear_nt(A, B, x["bias"], w.act)
+        R, _ = oracle.linear_at(np32(A), np32(B), rows, cols, np32(x["bias"]), w.act, w_trans=True)
     else:
         got = run_linear(A, B, x["bias"], w.act)
         R, _ = oracle.linear_at(np32(A), np32(B), rows, cols, np32(x["bias"]), w.act)
