@@ -12,7 +12,9 @@ of ``|A[m,k]*B[k,n]|`` that the parity tolerance is scaled by.
 Definitions followed (cited in full in ``oracle.c``): page "GEMM 优化详解",
 section "GEMM 基础理论 / 数学定义" (C = alpha*A*B + beta*C) and section
 "Level 6: Kernel Fusion" (ReLU(X*W + bias)); page "第5章-基础Kernel",
-sections 1.1 and 7.1 (the sum over k and the CPU triple loop).
+sections 1.1 and 7.1 (the sum over k and the CPU triple loop). The batched form
+(page "GEMM 优化详解", section "矩阵大小选择策略": many small products as one
+batched GEMM) is that definition applied to each batch item independently.
 """
 from __future__ import annotations
 
@@ -161,6 +163,30 @@ def linear(X, W, bias=None, act=1, nthreads=None, w_trans=False):
     T = np.empty((M, N), np.float64)
     lib.oracle_linear(M, N, K, _ptr(X), ldx, _ptr(W), ldw, int(w_trans), _ptr(bias), int(act),
                       _ptr(R), _ptr(T), _threads(nthreads))
+    return R, T
+
+
+def gemm_batched(A, B, alpha=1.0, beta=0.0, C=None, nthreads=None, bf16=False, b_trans=False):
+    """gemm() of every batch item: R[i] = alpha*A[i]*B[i] + beta*C[i].
+
+    A, B (and C when beta != 0) are 3-D arrays whose first axis is the batch;
+    an operand shared by every item may be given with batch stride 0
+    (``numpy.broadcast_to``). Returns (R, T) of shape (batch, M, N).
+    """
+    A, B = np.asarray(A), np.asarray(B)
+    if A.ndim != 3 or B.ndim != 3 or A.shape[0] != B.shape[0]:
+        raise ValueError("A and B must be 3-D with the same batch size")
+    nb, M = A.shape[0], A.shape[1]
+    N = B.shape[1] if b_trans else B.shape[2]
+    if beta != 0.0:
+        C = np.asarray(C)
+        if C.shape != (nb, M, N):
+            raise ValueError("C shape")
+    R = np.empty((nb, M, N), np.float64)
+    T = np.empty((nb, M, N), np.float64)
+    for i in range(nb):
+        R[i], T[i] = gemm(A[i], B[i], alpha, beta, None if beta == 0.0 else C[i], nthreads,
+                          bf16=bf16, b_trans=b_trans)
     return R, T
 
 

@@ -358,6 +358,50 @@ def test_linear_w_transposed():
     assert np.array_equal(r, R.ravel())
 
 
+# ---- batched (strided) products -------------------------------------------
+
+def test_batched_integer_exact_against_int64_matmul():
+    # distinct, non-square items: a batch index taken from the wrong operand or
+    # item, or one item's result written to another, changes the exact result
+    nb, M, N, K = 5, 7, 11, 13
+    A, B, C = rand_int(nb, M, K), rand_int(nb, K, N), rand_int(nb, M, N, lo=-4, hi=4)
+    R, _ = oracle.gemm_batched(A, B, 1.5, 0.5, C)
+    want = 1.5 * np.matmul(A.astype(np.int64), B.astype(np.int64)) + 0.5 * C.astype(np.float64)
+    assert np.array_equal(R, want)
+    Rt, _ = oracle.gemm_batched(A, np.ascontiguousarray(B.transpose(0, 2, 1)), b_trans=True)
+    assert np.array_equal(Rt, np.matmul(A.astype(np.int64), B.astype(np.int64)).astype(np.float64))
+
+
+def test_batched_16bit_integer_exact():
+    nb, M, N, K = 3, 9, 6, 40
+    A, B = rand_int(nb, M, K, lo=-8, hi=8), rand_int(nb, K, N, lo=-8, hi=8)
+    want = np.matmul(A.astype(np.int64), B.astype(np.int64)).astype(np.float64)
+    Rh, _ = oracle.gemm_batched(A.astype(np.float16).view(np.uint16), B.astype(np.float16).view(np.uint16))
+    bf = lambda x: (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    Rb, _ = oracle.gemm_batched(bf(A), bf(B), bf16=True)
+    assert np.array_equal(Rh, want) and np.array_equal(Rb, want)
+
+
+def test_batched_shared_operand_stride_zero():
+    # one B for every item (batch stride 0) equals the per-item products
+    nb, M, N, K = 4, 6, 8, 10
+    A, B = rand_f32(nb, M, K), rand_f32(K, N)
+    R, T = oracle.gemm_batched(A, np.broadcast_to(B, (nb, K, N)))
+    for i in range(nb):
+        Ri, Ti = oracle.gemm(A[i], B)
+        assert np.array_equal(R[i], Ri) and np.array_equal(T[i], Ti)
+    np.testing.assert_allclose(R, np.matmul(A.astype(np.float64), B.astype(np.float64)), rtol=0,
+                               atol=1e-12)
+
+
+def test_batched_empty_and_single():
+    R, T = oracle.gemm_batched(np.zeros((0, 3, 4), np.float32), np.zeros((0, 4, 5), np.float32))
+    assert R.shape == (0, 3, 5) and T.shape == (0, 3, 5)
+    A, B = rand_f32(1, 5, 6), rand_f32(1, 6, 7)
+    R, _ = oracle.gemm_batched(A, B)
+    assert np.array_equal(R[0], oracle.gemm(A[0], B[0])[0])
+
+
 def test_sampled_rejects_out_of_range():
     with pytest.raises(IndexError):
         oracle.gemm_at(rand_f32(3, 4), rand_f32(4, 5), [3], [0])
