@@ -3,15 +3,15 @@
 
 A step is one call of the hot path on one batch of synthetic input already
 resident in HBM: by default the 4096x4096x4096 FP32 GEMM (C = A*B, alpha 1,
-beta 0), i.e. one gemm_f32 launch. ``--workload`` selects another of the five
-workloads (see linear_layer_amd/workloads.py) for ad-hoc measurement.
+beta 0), i.e. one gemm_f32 launch. ``--workload`` selects another of the
+workloads in linear_layer_amd/workloads.py for ad-hoc measurement.
 
-Prints ONE JSON line with the metric (TFLOPS = 2*M*N*K / time per step),
+Prints ONE JSON line with the metric (TFLOPS = 2*M*N*K*batch / time per step),
 a ``roofline`` object for the GEMM kernel (achieved = algorithmic FLOPs per
 launch / average launch duration from HIP events on the launch stream, peak =
 MI355X's published dense matrix peak for the dtype) and a ``cpu_baseline``
 object: the float64 CPU oracle timed on a bounded sample of the same workload
-(a block of whole output rows) on this host's cores.
+(a block of whole output rows, or of whole batch items) on this host's cores.
 """
 from __future__ import annotations
 
@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 COPY_BYTES = 256 << 20
 
 # Published MI355X dense matrix peaks (TFLOP/s).
-PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "linear_nt": 157.3,
+PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "linear_nt": 157.3, "gemm_f32_batched": 157.3,
                "gemm_f16f32": 2516.6, "gemm_bf16f32": 2516.6, "gemm_f16f32_nt": 2516.6}
 KERNEL_SOURCES = {
     "gemm_f32": ["gemm_f32.hip", "common.hpp"],
@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "gemm_f16f32": ["gemm_f16.hip", "common.hpp"],
     "gemm_bf16f32": ["gemm_f16.hip", "common.hpp"],
     "linear_nt": ["gemm_f32.hip", "common.hpp"],
+    "gemm_f32_batched": ["gemm_f32.hip", "common.hpp"],
     "gemm_f16f32_nt": ["gemm_f16.hip", "common.hpp"],
 }
 
@@ -99,6 +100,31 @@ def measured_traffic(workload: str, kind: str):
     return float(m.group(1))
 
 
+def cpu_baseline_batched(w, A, B, C, target_s: float):
+    """Time the oracle on the first items of a batched workload."""
+    import oracle
+
+    def run(items):
+        t0 = time.perf_counter()
+        oracle.gemm_batched(A[:items], B[:items], w.alpha, w.beta, None if C is None else C[:items])
+        return time.perf_counter() - t0
+
+    items = 1
+    dt = run(items)
+    items = int(max(1, min(w.batch, items * target_s / max(dt, 1e-6))))
+    dt = run(items)
+    flops = 2.0 * items * w.M * w.N * w.K
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOPS",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"first {items} of {w.batch} batch items ({w.M}x{w.N}x{w.K} each, float64, "
+                  f"{dt:.2f} s)",
+        "seconds": dt,
+    }
+
+
 def cpu_baseline(w, x, target_s: float):
     """Time the float64 oracle on whole output rows of the same workload."""
     import numpy as np
@@ -114,6 +140,9 @@ def cpu_baseline(w, x, target_s: float):
     bt = w.kind in wl.B_TRANSPOSED_KINDS
     C = x["C"].numpy() if "C" in x else None
     bias = x["bias"].numpy() if "bias" in x else None
+
+    if w.kind in wl.BATCHED_KINDS:
+        return cpu_baseline_batched(w, A, B, C, target_s)
 
     def run(rows):
         t0 = time.perf_counter()
@@ -164,7 +193,8 @@ def main():
     x = wl.make_inputs(w)
     A = x["A"].to(dev)
     B = x["B"].to(dev)
-    C = torch.empty((w.M, w.N), device=dev, dtype=torch.float32)
+    batched = w.kind in wl.BATCHED_KINDS
+    C = torch.empty(((w.batch,) if batched else ()) + (w.M, w.N), device=dev, dtype=torch.float32)
     if "C" in x:
         C.copy_(x["C"].to(dev))
     bias = x["bias"].to(dev) if "bias" in x else None
@@ -174,8 +204,8 @@ def main():
     if args.split_k >= 1:
         ll.set_split_k(args.split_k)
     props = torch.cuda.get_device_properties(dev)
-    tile = ll.chosen_tile(dtype_id, w.M, w.N, w.K, props.multi_processor_count)
-    splits = ll.chosen_split_k(dtype_id, w.M, w.N, w.K, props.multi_processor_count)
+    tile = ll.chosen_tile(dtype_id, w.M, w.N, w.K, props.multi_processor_count, w.batch)
+    splits = ll.chosen_split_k(dtype_id, w.M, w.N, w.K, props.multi_processor_count, w.batch)
 
     def step():
         if w.kind == "gemm_f32":
@@ -188,6 +218,8 @@ def main():
             ll.gemm_f16f32_nt(A, B, C, w.alpha, w.beta)
         elif w.kind == "linear_nt":
             ll.linear_bias_act_nt(A, B, bias, w.act, C)
+        elif w.kind == "gemm_f32_batched":
+            ll.gemm_f32_batched(A, B, C, w.alpha, w.beta)
         else:
             ll.linear_bias_act(A, B, bias, w.act, C)
 
@@ -221,7 +253,7 @@ def main():
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, x, args.cpu_seconds)
 
-    dtype = {"gemm_f32": "f32", "linear": "f32", "linear_nt": "f32",
+    dtype = {"gemm_f32": "f32", "linear": "f32", "linear_nt": "f32", "gemm_f32_batched": "f32",
              "gemm_f16f32": "f16 in, f32 accumulate", "gemm_f16f32_nt": "f16 in, f32 accumulate",
              "gemm_bf16f32": "bf16 in, f32 accumulate"}[w.kind]
     out = {
@@ -243,6 +275,7 @@ def main():
             **({"act": "relu" if w.act == 1 else "none", "bias": True}
                if w.kind in ("linear", "linear_nt") else {}),
             **({"b_layout": "N-by-K"} if w.kind in wl.B_TRANSPOSED_KINDS else {}),
+            **({"batch": w.batch} if batched else {}),
             "tile": ll.tile_name(dtype_id, tile), "split_k": splits,
             "device": props.name, "cus": props.multi_processor_count,
         },

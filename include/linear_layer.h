@@ -155,6 +155,40 @@ int linear_bias_act_nt(int M, int N, int K,
                        const float *bias, int act,
                        float *Y, int ldy, void *stream);
 
+/*
+ * Strided-batched products (page "GEMM 优化详解", section "矩阵大小选择策略":
+ * small matrices are best run as one batched GEMM). For i in [0, batch):
+ *
+ *   C_i = alpha * A_i * op(B_i) + beta * C_i,   op(B) = B (trans_b 0) or B^T (trans_b 1)
+ *
+ * with A_i = A + i*stride_a, B_i = B + i*stride_b, C_i = C + i*stride_c
+ * (strides in ELEMENTS of the operand's type). Each item follows the rules of
+ * gemm_f32 / gemm_f16f32 / gemm_bf16f32 (trans_b 0: B_i K-by-N, ldb >= N;
+ * trans_b 1: B_i N-by-K, ldb >= K). A stride of 0 shares one A or B among all
+ * items; C items must not overlap (stride_c >= (M-1)*ldc + N when batch > 1),
+ * and the address range spanned by all C items must not meet that of A's or
+ * B's items. batch == 0 returns LL_OK with no launch; negative strides or
+ * batch, or trans_b outside {0, 1}, give LL_ERR_INVALID_VALUE. All items run
+ * in one launch (several when batch exceeds 65535), their tiles sharing the
+ * CUs. The 128-bit kernels also need stride_a, stride_b (in bytes) and
+ * stride_c*4 to be multiples of 16.
+ */
+int gemm_f32_batched(int trans_b, int M, int N, int K, float alpha,
+                     const float *A, int lda, int64_t stride_a,
+                     const float *B, int ldb, int64_t stride_b,
+                     float beta, float *C, int ldc, int64_t stride_c,
+                     int batch, void *stream);
+int gemm_f16f32_batched(int trans_b, int M, int N, int K, float alpha,
+                        const uint16_t *A, int lda, int64_t stride_a,
+                        const uint16_t *B, int ldb, int64_t stride_b,
+                        float beta, float *C, int ldc, int64_t stride_c,
+                        int batch, void *stream);
+int gemm_bf16f32_batched(int trans_b, int M, int N, int K, float alpha,
+                         const uint16_t *A, int lda, int64_t stride_a,
+                         const uint16_t *B, int ldb, int64_t stride_b,
+                         float beta, float *C, int ldc, int64_t stride_c,
+                         int batch, void *stream);
+
 /* A static, human-readable string for a status code (never NULL). */
 const char *ll_status_string(int status);
 
@@ -191,11 +225,12 @@ int ll_set_tile(int dtype, int tile);
  * multiple of 64, so small K may use fewer) for every later call of any dtype;
  * -1 restores the automatic choice. Returns LL_OK or LL_ERR_INVALID_VALUE. */
 int ll_set_split_k(int splits);
-/* The tile / the number of K-splits the library would use for an M-by-N
- * output with inner dimension K on a device with num_cus compute units
- * (num_cus <= 0: 256), honouring the overrides. -1 for an unknown dtype. */
-int ll_chosen_tile(int dtype, int M, int N, int K, int num_cus);
-int ll_chosen_split_k(int dtype, int M, int N, int K, int num_cus);
+/* The tile / the number of K-splits the library would use for `batch`
+ * M-by-N outputs (batch 1: a single product) with inner dimension K on a
+ * device with num_cus compute units (num_cus <= 0: 256), honouring the
+ * overrides. -1 for an unknown dtype or batch < 1. */
+int ll_chosen_tile(int dtype, int M, int N, int K, int batch, int num_cus);
+int ll_chosen_split_k(int dtype, int M, int N, int K, int batch, int num_cus);
 
 #ifdef __cplusplus
 }

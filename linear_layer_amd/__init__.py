@@ -14,8 +14,12 @@ Entry points (same names as the C ABI in ``include/linear_layer.h``):
 * ``gemm_f32_nt``, ``gemm_f16f32_nt``, ``gemm_bf16f32_nt``, ``linear_bias_act_nt``
   — the same with B (W) given N-by-K: C = alpha*A*B^T + beta*C, Y = act(X*W^T + b)
   (W in the [out_features, in_features] layout of ``torch.nn.Linear.weight``).
+* ``gemm_f32_batched``, ``gemm_f16f32_batched``, ``gemm_bf16f32_batched``
+  ``(A, B, C, alpha=1.0, beta=0.0, trans_b=False)`` — C[i] = alpha*A[i]*op(B[i])
+  + beta*C[i] over 3-D tensors whose first axis is the batch; its stride is the
+  batch stride (0, e.g. from ``expand``, shares one matrix among all items).
 
-Tensors are 2-D, row-major with unit column stride (a row stride larger than
+Matrices are 2-D, row-major with unit column stride (a row stride larger than
 the width is a leading dimension), on the current CUDA/HIP device. The calls
 are asynchronous on ``torch.cuda.current_stream()`` unless ``stream`` is given.
 """
@@ -27,6 +31,7 @@ import os
 __all__ = [
     "LinearLayerError", "gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "status_string",
     "gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt", "linear_bias_act_nt",
+    "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
     "library_path", "load", "set_tile", "num_tiles", "tile_name", "chosen_tile",
     "set_split_k", "chosen_split_k",
     "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16",
@@ -44,6 +49,7 @@ _lib = None
 # Every symbol the C header declares.
 EXPORTED = ("gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "ll_status_string",
             "gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt", "linear_bias_act_nt",
+            "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
             "ll_num_tiles", "ll_tile_name", "ll_set_tile", "ll_chosen_tile",
             "ll_set_split_k", "ll_chosen_split_k")
 
@@ -74,8 +80,13 @@ def load():
     for nt in ("gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt"):
         getattr(lib, nt).argtypes = lib.gemm_f32.argtypes
     lib.linear_bias_act_nt.argtypes = lib.linear_bias_act.argtypes
+    i64 = ctypes.c_int64
+    for b in ("gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched"):
+        getattr(lib, b).argtypes = [i32, i32, i32, i32, f32, vp, i32, i64, vp, i32, i64,
+                                    f32, vp, i32, i64, i32, vp]
     for f in (lib.gemm_f32, lib.gemm_f16f32, lib.gemm_bf16f32, lib.linear_bias_act,
-              lib.gemm_f32_nt, lib.gemm_f16f32_nt, lib.gemm_bf16f32_nt, lib.linear_bias_act_nt):
+              lib.gemm_f32_nt, lib.gemm_f16f32_nt, lib.gemm_bf16f32_nt, lib.linear_bias_act_nt,
+              lib.gemm_f32_batched, lib.gemm_f16f32_batched, lib.gemm_bf16f32_batched):
         f.restype = i32
     lib.ll_status_string.argtypes = [i32]
     lib.ll_status_string.restype = ctypes.c_char_p
@@ -85,9 +96,9 @@ def load():
     lib.ll_tile_name.restype = ctypes.c_char_p
     lib.ll_set_tile.argtypes = [i32, i32]
     lib.ll_set_tile.restype = i32
-    lib.ll_chosen_tile.argtypes = [i32, i32, i32, i32, i32]
+    lib.ll_chosen_tile.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.ll_chosen_tile.restype = i32
-    lib.ll_chosen_split_k.argtypes = [i32, i32, i32, i32, i32]
+    lib.ll_chosen_split_k.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.ll_chosen_split_k.restype = i32
     lib.ll_set_split_k.argtypes = [i32]
     lib.ll_set_split_k.restype = i32
@@ -116,8 +127,8 @@ def tile_name(dtype: int, tile: int) -> str:
     return load().ll_tile_name(int(dtype), int(tile)).decode()
 
 
-def chosen_tile(dtype: int, M: int, N: int, K: int, num_cus: int = 0) -> int:
-    return load().ll_chosen_tile(int(dtype), int(M), int(N), int(K), int(num_cus))
+def chosen_tile(dtype: int, M: int, N: int, K: int, num_cus: int = 0, batch: int = 1) -> int:
+    return load().ll_chosen_tile(int(dtype), int(M), int(N), int(K), int(batch), int(num_cus))
 
 
 def set_split_k(splits: int) -> None:
@@ -125,8 +136,8 @@ def set_split_k(splits: int) -> None:
     _check(load().ll_set_split_k(int(splits)), "ll_set_split_k")
 
 
-def chosen_split_k(dtype: int, M: int, N: int, K: int, num_cus: int = 0) -> int:
-    return load().ll_chosen_split_k(int(dtype), int(M), int(N), int(K), int(num_cus))
+def chosen_split_k(dtype: int, M: int, N: int, K: int, num_cus: int = 0, batch: int = 1) -> int:
+    return load().ll_chosen_split_k(int(dtype), int(M), int(N), int(K), int(batch), int(num_cus))
 
 
 # ---- tensor marshalling ---------------------------------------------------
@@ -154,6 +165,64 @@ def _mat(t, dtype, name):
     if rows > 1 and ld < cols:
         raise ValueError(f"{name}: row stride {ld} smaller than width {cols}")
     return t.data_ptr(), rows, cols, max(ld, 1)
+
+
+def _bmat(t, dtype, name):
+    """(pointer, batch, rows, cols, ld, batch stride) of a 3-D tensor of row-major matrices."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be 3-D (batch, rows, cols), got shape {tuple(t.shape)}")
+    nb = t.shape[0]
+    if nb == 0:
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        return 0, 0, t.shape[1], t.shape[2], max(t.shape[2], 1), 0
+    ptr, rows, cols, ld = _mat(t[0], dtype, name)
+    bstride = t.stride(0) if nb > 1 else 0
+    if bstride < 0:
+        raise ValueError(f"{name}: negative batch stride")
+    return t.data_ptr(), nb, rows, cols, ld, bstride
+
+
+def _gemm_batched(fn_name, in_dtype, A, B, C, alpha, beta, trans_b, stream):
+    torch = _torch()
+    pa, nb, M, K, lda, sa = _bmat(A, in_dtype, "A")
+    if trans_b:
+        pb, nb2, N, K2, ldb, sb = _bmat(B, in_dtype, "B")
+    else:
+        pb, nb2, K2, N, ldb, sb = _bmat(B, in_dtype, "B")
+    pc, nb3, M2, N2, ldc, sc = _bmat(C, torch.float32, "C")
+    if nb2 != nb or nb3 != nb or K2 != K or M2 != M or N2 != N:
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    if nb == 0:
+        return C
+    st = getattr(load(), fn_name)(int(bool(trans_b)), M, N, K, float(alpha), pa, lda, sa, pb, ldb, sb,
+                                  float(beta), pc, ldc, sc, nb, _stream(stream, A, B, C))
+    _check(st, fn_name)
+    return C
+
+
+def gemm_f32_batched(A, B, C, alpha: float = 1.0, beta: float = 0.0, trans_b: bool = False,
+                     stream=None):
+    """C[i] = alpha*A[i]*op(B[i]) + beta*C[i], fp32; op(B) = B^T when trans_b."""
+    return _gemm_batched("gemm_f32_batched", _torch().float32, A, B, C, alpha, beta, trans_b, stream)
+
+
+def gemm_f16f32_batched(A, B, C, alpha: float = 1.0, beta: float = 0.0, trans_b: bool = False,
+                        stream=None):
+    """Batched product with fp16 A, B and fp32 C."""
+    return _gemm_batched("gemm_f16f32_batched", _torch().float16, A, B, C, alpha, beta, trans_b, stream)
+
+
+def gemm_bf16f32_batched(A, B, C, alpha: float = 1.0, beta: float = 0.0, trans_b: bool = False,
+                         stream=None):
+    """Batched product with bf16 A, B and fp32 C."""
+    return _gemm_batched("gemm_bf16f32_batched", _torch().bfloat16, A, B, C, alpha, beta, trans_b,
+                         stream)
 
 
 def _stream(stream, *tensors):

@@ -37,29 +37,60 @@ bool aligned(const void *p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
 int imax1(int v) { return v > 1 ? v : 1; }
 
+// A strided batch: `count` products whose operands lie stride_{a,b,c}
+// elements apart (a single product is {1, 0, 0, 0}).
+struct Batch {
+    int count;
+    int64_t sa, sb, sc;
+};
+constexpr Batch kSingle{1, 0, 0, 0};
+
+// Bytes from the first item's first element to the last item's last one;
+// -1 on overflow.
+int64_t batch_span(int count, int64_t stride, int64_t one, int64_t elem)
+{
+    int64_t step, reach, total;
+    if (__builtin_mul_overflow(stride, elem, &step) ||
+        __builtin_mul_overflow((int64_t)(count - 1), step, &reach) ||
+        __builtin_add_overflow(reach, one, &total))
+        return -1;
+    return total;
+}
+
 // Returns LL_OK and sets *noop when nothing is to be done. b_trans: B is
-// given N-by-K (ldb >= K) instead of K-by-N (ldb >= N).
+// given N-by-K (ldb >= K) instead of K-by-N (ldb >= N). For a batch, the
+// items of C must not overlap one another (stride_c covers one item), and the
+// whole address range of C must not meet that of A or of B.
 int check_gemm(int M, int N, int K, float alpha, const void *A, int lda, const void *B, int ldb,
-               const float *C, int ldc, int64_t elem_ab, bool *noop, bool b_trans = false)
+               const float *C, int ldc, int64_t elem_ab, bool *noop, bool b_trans = false,
+               const Batch &bt = kSingle)
 {
     *noop = false;
-    if (M < 0 || N < 0 || K < 0)
+    if (M < 0 || N < 0 || K < 0 || bt.count < 0 || bt.sa < 0 || bt.sb < 0 || bt.sc < 0)
         return LL_ERR_INVALID_VALUE;
     if (lda < imax1(K) || ldb < imax1(b_trans ? K : N) || ldc < imax1(N))
         return LL_ERR_INVALID_VALUE;
-    if (M == 0 || N == 0) {
+    if (M == 0 || N == 0 || bt.count == 0) {
         *noop = true;
         return LL_OK;
     }
     if (C == nullptr || !aligned(C, 4))
         return LL_ERR_INVALID_VALUE;
+    const int64_t c_one = span_bytes(M, N, ldc, 4);
+    if (bt.count > 1 && bt.sc * 4 < c_one)
+        return LL_ERR_INVALID_VALUE;
+    const int64_t cb = batch_span(bt.count, bt.sc, c_one, 4);
+    if (cb < 0)
+        return LL_ERR_INVALID_VALUE;
     const bool reads_ab = K > 0 && alpha != 0.0f;
     if (reads_ab) {
         if (A == nullptr || B == nullptr || !aligned(A, elem_ab) || !aligned(B, elem_ab))
             return LL_ERR_INVALID_VALUE;
-        const int64_t cb = span_bytes(M, N, ldc, 4);
-        if (overlap(C, cb, A, span_bytes(M, K, lda, elem_ab)) ||
-            overlap(C, cb, B, b_trans ? span_bytes(N, K, ldb, elem_ab) : span_bytes(K, N, ldb, elem_ab)))
+        const int64_t ab = batch_span(bt.count, bt.sa, span_bytes(M, K, lda, elem_ab), elem_ab);
+        const int64_t bb = batch_span(bt.count, bt.sb,
+                                      b_trans ? span_bytes(N, K, ldb, elem_ab)
+                                              : span_bytes(K, N, ldb, elem_ab), elem_ab);
+        if (ab < 0 || bb < 0 || overlap(C, cb, A, ab) || overlap(C, cb, B, bb))
             return LL_ERR_INVALID_VALUE;
     }
     return LL_OK;
@@ -145,8 +176,10 @@ struct Plan {
 // "GEMM 优化详解", section "矩阵大小选择策略", re-derived for 256 CUs.
 // A split costs a pre-pass over C (beta*C, or the bias), the atomic traffic of
 // every split's partial tile and, for ReLU, a pass afterwards.
-Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int cus, bool relu)
+Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int cus, bool relu,
+          int batch = 1)
 {
+    const int items = batch < kMaxGridZ ? batch : kMaxGridZ;   // items per launch
     const int t_ov = g_tile_override[dtype].load(std::memory_order_relaxed);
     const int s_ov = g_split_override.load(std::memory_order_relaxed);
     Plan best{0, 1, K};
@@ -170,9 +203,9 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
                 if (splits != s && s_ov < 1)
                     continue;   // the same partition is reached with fewer splits
             }
-            double cost = wg_cost(ti, tiles_mn * splits, (double)ti.bm * ti.bn * k_split, cus);
+            double cost = wg_cost(ti, tiles_mn * splits * items, (double)ti.bm * ti.bn * k_split, cus);
             if (splits > 1) {
-                const double mn = (double)M * N;
+                const double mn = (double)M * N * items;
                 const double bytes = 8.0 * mn * (relu ? 2 : 1) + 4.0 * mn * splits;
                 cost += ((relu ? 6.0 : 3.0) + bytes / 3.0e6) * kUnitsPerUs;
             }
@@ -210,6 +243,7 @@ GemmParams make_params(int M, int N, int K, float alpha, const void *A, int lda,
     p.act = 0;
     p.group_m = 4;
     p.k_split = K > 0 ? K : 1;
+    p.batch = 1;
     return p;
 }
 
@@ -217,12 +251,12 @@ typedef hipError_t (*launch_fn)(const GemmParams &, int, int, bool, hipStream_t)
 
 // One GEMM per plan: a single launch with the alpha/beta write-back, or, when
 // K is split, C = beta*C followed by the split launch adding alpha*partials.
-hipError_t run_gemm(GemmParams p, const Plan &pl, bool vec, hipStream_t s, launch_fn launch)
+hipError_t run_one(GemmParams p, const Plan &pl, bool vec, hipStream_t s, launch_fn launch)
 {
     if (pl.splits == 1)
         return launch(p, pl.tile, p.beta == 0.0f ? EPI_GEMM_BETA0 : EPI_GEMM_BETA, vec, s);
     if (p.beta != 1.0f) {
-        const hipError_t e = launch_scale(p.C, p.ldc, p.M, p.N, p.beta, s);
+        const hipError_t e = launch_scale(p.C, p.ldc, p.M, p.N, p.beta, s, p.batch, p.stride_c);
         if (e != hipSuccess)
             return e;
     }
@@ -230,15 +264,55 @@ hipError_t run_gemm(GemmParams p, const Plan &pl, bool vec, hipStream_t s, launc
     return launch(p, pl.tile, EPI_ATOMIC, vec, s);
 }
 
+// A strided batch in launches of at most kMaxGridZ items (grid z).
+hipError_t run_gemm(GemmParams p, const Plan &pl, bool vec, hipStream_t s, launch_fn launch,
+                    int64_t elem_ab, const Batch &bt = kSingle)
+{
+    p.stride_a = bt.sa * elem_ab;
+    p.stride_b = bt.sb * elem_ab;
+    p.stride_c = bt.sc * 4;
+    for (int64_t done = 0; done < bt.count; done += kMaxGridZ) {
+        GemmParams q = p;
+        q.batch = (int)(bt.count - done < kMaxGridZ ? bt.count - done : kMaxGridZ);
+        q.A = static_cast<const char *>(p.A) + done * p.stride_a;
+        q.B = static_cast<const char *>(p.B) + done * p.stride_b;
+        q.C = reinterpret_cast<float *>(reinterpret_cast<char *>(p.C) + done * p.stride_c);
+        const hipError_t e = run_one(q, pl, vec, s, launch);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+// C = beta*C for every item of a batch (K == 0 or alpha == 0).
+hipError_t scale_batch(float *C, int ldc, int M, int N, float beta, hipStream_t s, const Batch &bt)
+{
+    for (int64_t done = 0; done < bt.count; done += kMaxGridZ) {
+        const int n = (int)(bt.count - done < kMaxGridZ ? bt.count - done : kMaxGridZ);
+        const hipError_t e = launch_scale(C + done * bt.sc, ldc, M, N, beta, s, n, bt.sc * 4);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+// 16-byte operand loads need every item's base 16-byte aligned.
+bool batch_aligned(const Batch &bt, int64_t elem_ab)
+{
+    return bt.count <= 1 || ((bt.sa * elem_ab) % 16 == 0 && (bt.sb * elem_ab) % 16 == 0 &&
+                             (bt.sc * 4) % 16 == 0);
+}
+
 }  // namespace
 
 extern "C" {
 
 static int gemm_f32_impl(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
-                         int ldb, float beta, float *C, int ldc, void *stream, bool bt)
+                         int ldb, float beta, float *C, int ldc, void *stream, bool bt,
+                         const Batch &bat = kSingle)
 {
     bool noop;
-    int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 4, &noop, bt);
+    int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 4, &noop, bt, bat);
     if (st != LL_OK || noop)
         return st;
     DevInfo dev;
@@ -246,12 +320,13 @@ static int gemm_f32_impl(int M, int N, int K, float alpha, const float *A, int l
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (K == 0 || alpha == 0.0f)
-        return launch_status(launch_scale(C, ldc, M, N, beta, s));
+        return launch_status(scale_batch(C, ldc, M, N, beta, s, bat));
     const bool vec = aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && lda % 4 == 0 &&
-                     ldb % 4 == 0 && ldc % 4 == 0 && K % 4 == 0 && (bt || N % 4 == 0);
+                     ldb % 4 == 0 && ldc % 4 == 0 && K % 4 == 0 && (bt || N % 4 == 0) &&
+                     batch_aligned(bat, 4);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false);
-    return launch_status(run_gemm(p, pl, vec, s, bt ? launch_gemm_f32_bt : launch_gemm_f32));
+    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false, bat.count);
+    return launch_status(run_gemm(p, pl, vec, s, bt ? launch_gemm_f32_bt : launch_gemm_f32, 4, bat));
 }
 
 int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
@@ -268,10 +343,11 @@ int gemm_f32_nt(int M, int N, int K, float alpha, const float *A, int lda, const
 
 // Both 16-bit formats and both B layouts share the kernels, tiles and checks.
 static int gemm_16(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
-                   int ldb, float beta, float *C, int ldc, void *stream, launch_fn launch, bool bt)
+                   int ldb, float beta, float *C, int ldc, void *stream, launch_fn launch, bool bt,
+                   const Batch &bat = kSingle)
 {
     bool noop;
-    int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 2, &noop, bt);
+    int st = check_gemm(M, N, K, alpha, A, lda, B, ldb, C, ldc, 2, &noop, bt, bat);
     if (st != LL_OK || noop)
         return st;
     DevInfo dev;
@@ -279,12 +355,13 @@ static int gemm_16(int M, int N, int K, float alpha, const uint16_t *A, int lda,
         return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (K == 0 || alpha == 0.0f)
-        return launch_status(launch_scale(C, ldc, M, N, beta, s));
+        return launch_status(scale_batch(C, ldc, M, N, beta, s, bat));
     const bool vec = aligned(A, 16) && aligned(B, 16) && aligned(C, 16) && lda % 8 == 0 &&
-                     ldb % 8 == 0 && ldc % 4 == 0 && K % 8 == 0 && (bt || N % 8 == 0);
+                     ldb % 8 == 0 && ldc % 4 == 0 && K % 8 == 0 && (bt || N % 8 == 0) &&
+                     batch_aligned(bat, 2);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false);
-    return launch_status(run_gemm(p, pl, vec, s, launch));
+    const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false, bat.count);
+    return launch_status(run_gemm(p, pl, vec, s, launch, 2, bat));
 }
 
 int gemm_f16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
@@ -309,6 +386,38 @@ int gemm_bf16f32_nt(int M, int N, int K, float alpha, const uint16_t *A, int lda
                     int ldb, float beta, float *C, int ldc, void *stream)
 {
     return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, launch_gemm_bf16_bt, true);
+}
+
+int gemm_f32_batched(int trans_b, int M, int N, int K, float alpha, const float *A, int lda,
+                     int64_t stride_a, const float *B, int ldb, int64_t stride_b, float beta, float *C,
+                     int ldc, int64_t stride_c, int batch, void *stream)
+{
+    if (trans_b != 0 && trans_b != 1)
+        return LL_ERR_INVALID_VALUE;
+    return gemm_f32_impl(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, trans_b == 1,
+                         Batch{batch, stride_a, stride_b, stride_c});
+}
+
+int gemm_f16f32_batched(int trans_b, int M, int N, int K, float alpha, const uint16_t *A, int lda,
+                        int64_t stride_a, const uint16_t *B, int ldb, int64_t stride_b, float beta,
+                        float *C, int ldc, int64_t stride_c, int batch, void *stream)
+{
+    if (trans_b != 0 && trans_b != 1)
+        return LL_ERR_INVALID_VALUE;
+    return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                   trans_b ? launch_gemm_f16_bt : launch_gemm_f16, trans_b == 1,
+                   Batch{batch, stride_a, stride_b, stride_c});
+}
+
+int gemm_bf16f32_batched(int trans_b, int M, int N, int K, float alpha, const uint16_t *A, int lda,
+                         int64_t stride_a, const uint16_t *B, int ldb, int64_t stride_b, float beta,
+                         float *C, int ldc, int64_t stride_c, int batch, void *stream)
+{
+    if (trans_b != 0 && trans_b != 1)
+        return LL_ERR_INVALID_VALUE;
+    return gemm_16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                   trans_b ? launch_gemm_bf16_bt : launch_gemm_bf16, trans_b == 1,
+                   Batch{batch, stride_a, stride_b, stride_c});
 }
 
 static int linear_impl(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
@@ -403,22 +512,29 @@ const char *ll_tile_name(int dtype, int tile)
     return "";
 }
 
-int ll_chosen_tile(int dtype, int M, int N, int K, int num_cus)
+static Plan chosen_plan(int dtype, int M, int N, int K, int batch, int num_cus, bool *ok)
 {
+    *ok = (dtype == LL_DTYPE_F32 || dtype == LL_DTYPE_F16) && batch >= 1;
+    if (!*ok)
+        return Plan{-1, -1, 0};
+    const int cus = num_cus > 0 ? num_cus : 256;
     if (dtype == LL_DTYPE_F32)
-        return plan(0, kF32Tiles, kF32NumTiles, M, N, K, num_cus > 0 ? num_cus : 256, false).tile;
-    if (dtype == LL_DTYPE_F16)
-        return plan(1, kF16Tiles, kF16NumTiles, M, N, K, num_cus > 0 ? num_cus : 256, false).tile;
-    return -1;
+        return plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, false, batch);
+    return plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch);
 }
 
-int ll_chosen_split_k(int dtype, int M, int N, int K, int num_cus)
+int ll_chosen_tile(int dtype, int M, int N, int K, int batch, int num_cus)
 {
-    if (dtype == LL_DTYPE_F32)
-        return plan(0, kF32Tiles, kF32NumTiles, M, N, K, num_cus > 0 ? num_cus : 256, false).splits;
-    if (dtype == LL_DTYPE_F16)
-        return plan(1, kF16Tiles, kF16NumTiles, M, N, K, num_cus > 0 ? num_cus : 256, false).splits;
-    return -1;
+    bool ok;
+    const Plan p = chosen_plan(dtype, M, N, K, batch, num_cus, &ok);
+    return ok ? p.tile : -1;
+}
+
+int ll_chosen_split_k(int dtype, int M, int N, int K, int batch, int num_cus)
+{
+    bool ok;
+    const Plan p = chosen_plan(dtype, M, N, K, batch, num_cus, &ok);
+    return ok ? p.splits : -1;
 }
 
 int ll_set_split_k(int splits)

@@ -35,7 +35,26 @@ struct GemmParams {
     int tiles_m, tiles_n; // output tiles along M and N
     int group_m;          // tile rows per group in the grouped ordering
     int k_split;          // K per split (a multiple of 64); K itself when not split
+    int batch;            // batch items in this launch (grid z); 1 for a single product
+    int64_t stride_a, stride_b, stride_c;  // byte distance between batch items (0: shared)
 };
+
+// Strided batch: workgroups with blockIdx.z = i compute item i, whose A, B and
+// C start stride_{a,b,c}*i bytes after the first item's (page "GEMM 优化详解",
+// section "矩阵大小选择策略": small products are run as one batched GEMM).
+__device__ __forceinline__ void select_batch(GemmParams &p)
+{
+    const int64_t z = blockIdx.z;
+    p.A = static_cast<const char *>(p.A) + z * p.stride_a;
+    p.B = static_cast<const char *>(p.B) + z * p.stride_b;
+    p.C = reinterpret_cast<float *>(reinterpret_cast<char *>(p.C) + z * p.stride_c);
+}
+
+// Launch grid of a product: x = output tiles, y = K-splits, z = batch items.
+inline dim3 gemm_grid(const GemmParams &p, int64_t ntiles)
+{
+    return dim3((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split), (unsigned)p.batch);
+}
 
 // The K range of this workgroup: split blockIdx.y covers
 // [blockIdx.y*k_split, min(K, (blockIdx.y+1)*k_split)). Returns the offset;

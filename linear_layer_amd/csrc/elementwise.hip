@@ -9,9 +9,12 @@
 
 namespace ll {
 
-// One workgroup per row-stripe, threads striding along the row.
-__global__ void __launch_bounds__(256) scale_kernel(float *C, int64_t ldc, int M, int N, float beta)
+// One workgroup per row-stripe, threads striding along the row; grid z walks
+// the items of a strided batch (stride_c bytes apart).
+__global__ void __launch_bounds__(256) scale_kernel(float *C, int64_t ldc, int M, int N, float beta,
+                                                    int64_t stride_c)
 {
+    C = reinterpret_cast<float *>(reinterpret_cast<char *>(C) + (int64_t)blockIdx.z * stride_c);
     for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
         float *row = C + m * ldc;
         for (int n = threadIdx.x; n < N; n += blockDim.x)
@@ -51,9 +54,11 @@ static unsigned rows_grid(int M)
     return (unsigned)(M < 65536 ? M : 65536);
 }
 
-hipError_t launch_scale(float *C, int64_t ldc, int M, int N, float beta, hipStream_t s)
+hipError_t launch_scale(float *C, int64_t ldc, int M, int N, float beta, hipStream_t s, int batch,
+                        int64_t stride_c)
 {
-    hipLaunchKernelGGL(scale_kernel, dim3(rows_grid(M)), dim3(256), 0, s, C, ldc, M, N, beta);
+    hipLaunchKernelGGL(scale_kernel, dim3(rows_grid(M), 1, (unsigned)batch), dim3(256), 0, s, C, ldc,
+                       M, N, beta, stride_c);
     return hipGetLastError();
 }
 

@@ -74,6 +74,7 @@ gemm_f16_kernel(GemmParams p)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
+    select_batch(p);
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -302,6 +303,7 @@ gemm_f16_direct_kernel(GemmParams p)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
+    select_batch(p);
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -472,9 +474,9 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     p.tiles_m = (p.M + T::BM - 1) / T::BM;
     p.tiles_n = (p.N + T::BN - 1) / T::BN;
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
-    if (ntiles > 0x7fffffff)
+    if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split)), block(T::NT);
+    const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F16_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f16_kernel<T, E, V, WPE, BF16, BT>), grid, block, 0, s, p)
     if (vec) {
@@ -507,9 +509,9 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
     p.tiles_m = (p.M + 255) / 256;
     p.tiles_n = (p.N + 255) / 256;
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
-    if (ntiles > 0x7fffffff)
+    if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split)), block(256);
+    const dim3 grid = gemm_grid(p, ntiles), block(256);
     if (epi == EPI_GEMM_BETA0)
         hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_GEMM_BETA0, BF16, BT>), grid, block, 0, s, p);
     else if (epi == EPI_GEMM_BETA)

@@ -23,7 +23,8 @@ extern const TileInfo kF16Tiles[kF16NumTiles];
 // One GEMM launch. `tile` indexes kF32Tiles / kF16Tiles, `epi` is an Epi
 // value, `vec` selects the 128-bit-load kernels (the caller has checked
 // alignment and divisibility). Fills p.tiles_m / p.tiles_n itself; the grid
-// has ceil(K / p.k_split) K-splits along y (EPI_ATOMIC when more than one).
+// has ceil(K / p.k_split) K-splits along y (EPI_ATOMIC when more than one)
+// and p.batch items along z (at most kMaxGridZ).
 hipError_t launch_gemm_f32(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
 // As above with B given N-by-K (C = alpha*A*B^T + beta*C).
 hipError_t launch_gemm_f32_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
@@ -32,8 +33,15 @@ hipError_t launch_gemm_bf16(const GemmParams &p, int tile, int epi, bool vec, hi
 hipError_t launch_gemm_f16_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
 hipError_t launch_gemm_bf16_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
 
-// C = beta*C over an M x N matrix (beta == 0 writes zeros without reading C).
-hipError_t launch_scale(float *C, int64_t ldc, int M, int N, float beta, hipStream_t s);
+// Largest grid y / z extent a launch may use, and the most output tiles
+// (grid x) a 256-thread launch may have (its work-item count must fit 32 bits).
+constexpr int kMaxGridZ = 65535;
+constexpr int64_t kMaxTiles = (int64_t)(0xffffffffu / 256u);
+
+// C = beta*C over an M x N matrix (beta == 0 writes zeros without reading C),
+// for each of `batch` matrices stride_c bytes apart.
+hipError_t launch_scale(float *C, int64_t ldc, int M, int N, float beta, hipStream_t s,
+                        int batch = 1, int64_t stride_c = 0);
 // In-place ReLU over an M x N matrix.
 hipError_t launch_relu(float *Y, int64_t ldy, int M, int N, hipStream_t s);
 // Y = act(bias) broadcast over M rows (bias may be nullptr: act(0)).

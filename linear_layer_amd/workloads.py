@@ -21,6 +21,9 @@ product with bfloat16 inputs (page "GEMM 优化详解", "进一步优化方向":
 matrix units take FP16 or BF16); the seventh and eighth give B (W) N-by-K, the
 [out][in] weight layout and the B^T of Q*K^T (page "GEMM 优化详解", table
 "为什么 GEMM 重要"). B (W) of the transposed forms is drawn in its N-by-K shape.
+The ninth runs C1's 256-cubed product 256 times as one strided batch (page
+"GEMM 优化详解", section "矩阵大小选择策略": small matrices are batched); its
+operands are drawn as (batch, rows, cols) tensors.
 """
 from __future__ import annotations
 
@@ -42,11 +45,12 @@ class Workload:
     beta: float = 0.0
     act: int = 1        # linear only: 0 none, 1 ReLU
     scale: float = 1.0  # operand scale (linear: 1/64)
+    batch: int = 1      # strided batch of independent products (batched kinds)
     extra: dict = field(default_factory=dict)
 
     @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        return 2 * self.M * self.N * self.K * self.batch
 
 
 WORKLOADS = {
@@ -63,9 +67,13 @@ WORKLOADS = {
     "linear_relu_nt_2047x4096x11008": Workload(7, "linear_relu_nt_2047x4096x11008", "linear_nt",
                                                2047, 11008, 4096, act=1, scale=1.0 / 64.0),
     "gemm_f16f32_nt_8192": Workload(8, "gemm_f16f32_nt_8192", "gemm_f16f32_nt", 8192, 8192, 8192),
+    # many small products in one batched call: 256 independent 256^3 FP32 GEMMs
+    "gemm_f32_batched_256x256x256_b256": Workload(9, "gemm_f32_batched_256x256x256_b256",
+                                                  "gemm_f32_batched", 256, 256, 256, batch=256),
 }
 
 HALF_KINDS = ("gemm_f16f32", "gemm_bf16f32", "gemm_f16f32_nt")
+BATCHED_KINDS = ("gemm_f32_batched",)
 B_TRANSPOSED_KINDS = ("linear_nt", "gemm_f16f32_nt")
 
 
@@ -109,34 +117,39 @@ def half_bits(x: torch.Tensor):
 
 
 def make_inputs(w: Workload, integer: bool = False, M: int | None = None,
-                N: int | None = None, K: int | None = None) -> dict:
+                N: int | None = None, K: int | None = None, batch: int | None = None) -> dict:
     """Host (CPU) input tensors for workload ``w``; sizes may be overridden.
 
     Returns a dict with A, B (and C for beta != 0, bias for linear). For fp16
-    and bf16 workloads A and B are float16 / bfloat16 tensors. ``integer=True`` gives the
-    integer-valued variant whose exact result every summation order reaches:
-    fp32 entries in [-2, 2], C_in and bias in [-4, 4], fp16 entries in [-8, 8].
+    and bf16 workloads A and B are float16 / bfloat16 tensors; for batched
+    workloads every tensor gains a leading batch axis. ``integer=True`` gives
+    the integer-valued variant whose exact result every summation order
+    reaches: fp32 entries in [-2, 2], C_in and bias in [-4, 4], fp16 entries in
+    [-8, 8].
     """
     M = w.M if M is None else M
     N = w.N if N is None else N
     K = w.K if K is None else K
+    lead = ((w.batch if batch is None else batch),) if w.kind in BATCHED_KINDS else ()
     s = 100 * w.index
     out = {}
-    bshape = (N, K) if w.kind in B_TRANSPOSED_KINDS else (K, N)
+    ashape = lead + (M, K)
+    bshape = lead + ((N, K) if w.kind in B_TRANSPOSED_KINDS else (K, N))
+    cshape = lead + (M, N)
     linear = w.kind in ("linear", "linear_nt")
     if integer:
         lim = 8 if w.kind in HALF_KINDS else 2
-        out["A"] = integers((M, K), s + 0, -lim, lim)
+        out["A"] = integers(ashape, s + 0, -lim, lim)
         out["B"] = integers(bshape, s + 1, -lim, lim)
         if w.beta != 0.0:
-            out["C"] = integers((M, N), s + 2, -4, 4)
+            out["C"] = integers(cshape, s + 2, -4, 4)
         if linear:
             out["bias"] = integers((N,), s + 3, -4, 4)
     else:
-        out["A"] = uniform((M, K), s + 0, w.scale)
+        out["A"] = uniform(ashape, s + 0, w.scale)
         out["B"] = uniform(bshape, s + 1, w.scale)
         if w.beta != 0.0:
-            out["C"] = uniform((M, N), s + 2)
+            out["C"] = uniform(cshape, s + 2)
         if linear:
             out["bias"] = bias_uniform(N, s + 3)
     if w.kind in ("gemm_f16f32", "gemm_f16f32_nt"):

@@ -91,6 +91,38 @@ def test_linear_nt_leading_dimension_rule():
     assert lib.linear_bias_act_nt(4, 16, 8, PA, 8, PB, 8, None, 3, PC, 16, None) == E   # unknown act
 
 
+def call_batched(M, N, K, sa, sb, sc, batch, trans_b=0, A=PA, B=PB, C=PC, lda=None, ldb=None,
+                 ldc=None, name="gemm_f32_batched", alpha=1.0):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(K if trans_b else N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    fn = getattr(ll.load(), name)
+    return fn(trans_b, M, N, K, alpha, A, lda, sa, B, ldb, sb, 0.0, C, ldc, sc, batch, None)
+
+
+@pytest.mark.parametrize("name", ["gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched"])
+def test_batched_invalid_arguments(name):
+    E = ll.ERR_INVALID_VALUE
+    fine = (ll.ERR_NO_DEVICE, ll.OK, ll.ERR_UNSUPPORTED_ARCH)
+    one = 8 * 8
+    assert call_batched(8, 8, 8, one, one, one, 3, name=name) in fine
+    assert call_batched(8, 8, 8, 0, 0, one, 3, name=name) in fine             # shared A and B
+    assert call_batched(8, 8, 8, one, one, one, 3, trans_b=1, name=name) in fine
+    assert call_batched(8, 8, 8, one, one, one, -1, name=name) == E           # negative batch
+    assert call_batched(8, 8, 8, -one, one, one, 3, name=name) == E           # negative stride
+    assert call_batched(8, 8, 8, one, one, one - 1, 3, name=name) == E        # C items overlap
+    assert call_batched(8, 8, 8, one, one, 0, 2, name=name) == E              # one C for two items
+    assert call_batched(8, 8, 8, one, one, one, 3, trans_b=2, name=name) == E
+    # the last C item reaches B: C + 2*stride_c*4 bytes spans into [B, ...)
+    assert call_batched(8, 8, 8, one, one, one, 3, C=PB - 2 * one * 4, name=name) == E
+    # ... while the same C with one item stays clear of B
+    assert call_batched(8, 8, 8, one, one, one, 1, C=PB - one * 4, name=name) in fine
+    # strides whose span overflows 64 bits are rejected, not wrapped
+    assert call_batched(8, 8, 8, 1 << 62, one, one, 3, name=name) == E
+    # batch 0, like M = 0, is a no-op that touches nothing
+    assert call_batched(8, 8, 8, one, one, one, 0, A=None, B=None, C=None, name=name) == ll.OK
+
+
 def test_quick_returns_touch_nothing():
     # M == 0 or N == 0: OK with no device and even with NULL pointers
     assert call_gemm(0, 5, 5, A=None, B=None, C=None) == ll.OK
@@ -170,6 +202,11 @@ def test_tile_choice():
     finally:
         ll.set_split_k(-1)
     assert ll.chosen_tile(f32, 4096, 4096, 4096, 256) == 1
+    # a batch counts all its items' tiles: 256 items of 256^3 fill the CUs
+    # without splitting K, one item alone splits it
+    assert ll.chosen_split_k(f32, 256, 256, 256, 256, batch=256) == 1
+    assert ll.chosen_split_k(f32, 256, 256, 256, 256, batch=1) > 1
+    assert ll.chosen_tile(f32, 256, 256, 256, 256, batch=0) == -1
     with pytest.raises(ll.LinearLayerError):
         ll.set_tile(f32, 17)
     with pytest.raises(ll.LinearLayerError):

@@ -584,6 +584,167 @@ def test_nt_shape_errors():
         ll.linear_bias_act_nt(A, B, torch.zeros(16, device=DEV), 1, C)   # bias of length K
 
 
+
+# ---- strided batches ------------------------------------------------------------
+
+BATCHED = {"f32": (ll.gemm_f32_batched, torch.float32, False),
+           "f16": (ll.gemm_f16f32_batched, torch.float16, False),
+           "bf16": (ll.gemm_bf16f32_batched, torch.bfloat16, True)}
+
+
+def host_bits(t, which):
+    return np32(t) if which == "f32" else bits16(t)
+
+
+def run_batched(fn, A, B, alpha=1.0, beta=0.0, C=None, trans_b=False, N=None):
+    """Device copies of 3-D host tensors (expanded ones keep batch stride 0)."""
+    def dev(t):
+        if t.shape[0] > 1 and t.stride(0) == 0:
+            return t[:1].to(DEV).expand(t.shape)
+        return t.to(DEV)
+    Ad, Bd = dev(A), dev(B)
+    nb, M = A.shape[0], A.shape[1]
+    N = (B.shape[1] if trans_b else B.shape[2]) if N is None else N
+    Cd = (C.clone() if C is not None else torch.full((nb, M, N), float("nan"))).to(DEV)
+    fn(Ad, Bd, Cd, alpha, beta, trans_b=trans_b)
+    torch.cuda.synchronize()
+    return np32(Cd)
+
+
+def oracle_batched(A, B, which, alpha=1.0, beta=0.0, C=None, trans_b=False):
+    Ah = host_bits(A.contiguous(), which)
+    Bh = host_bits(B.contiguous(), which)
+    return oracle.gemm_batched(Ah, Bh, alpha, beta, None if C is None else np32(C),
+                               bf16=which == "bf16", b_trans=trans_b)
+
+
+@pytest.mark.parametrize("which", list(BATCHED))
+@pytest.mark.parametrize("trans_b", [False, True])
+@pytest.mark.parametrize("nb,M,N,K", [(7, 130, 70, 72), (3, 257, 300, 64), (16, 33, 40, 24)])
+def test_batched_small(which, trans_b, nb, M, N, K):
+    fn, dt, _ = BATCHED[which]
+    A = rand((nb, M, K), 111).to(dt)
+    B = rand((nb, N, K) if trans_b else (nb, K, N), 112).to(dt)
+    C = rand((nb, M, N), 113)
+    for alpha, beta in ((1.0, 0.0), (1.5, -0.5)):
+        got = run_batched(fn, A, B, alpha, beta, C if beta else None, trans_b)
+        R, T = oracle_batched(A, B, which, alpha, beta, C if beta else None, trans_b)
+        assert_close(got, R, T, f"{which} batched tb={trans_b} {nb}x{M}x{N}x{K} a={alpha} b={beta}")
+
+
+@pytest.mark.parametrize("t", T32)
+def test_batched_f32_every_tile(t, tile):
+    tile(F32, t)
+    nb, M, N, K = 5, 300, 264, 136
+    A, B = rand((nb, M, K), 114), rand((nb, K, N), 115)
+    got = run_batched(ll.gemm_f32_batched, A, B)
+    R, T = oracle_batched(A, B, "f32")
+    assert_close(got, R, T, f"f32 batched tile {t}")
+
+
+@pytest.mark.parametrize("t", T16)
+def test_batched_16bit_every_tile(t, tile):
+    tile(F16, t)
+    nb, M, N, K = 5, 300, 264, 136
+    for which in ("f16", "bf16"):
+        fn, dt, _ = BATCHED[which]
+        A, B = rand((nb, M, K), 116).to(dt), rand((nb, N, K), 117).to(dt)
+        got = run_batched(fn, A, B, trans_b=True)
+        R, T = oracle_batched(A, B, which, trans_b=True)
+        assert_close(got, R, T, f"{which} batched tile {t}")
+
+
+@pytest.mark.parametrize("which", ["f32", "f16"])
+def test_batched_shared_operands(which):
+    """Batch stride 0: one A (or B) for every item."""
+    fn, dt, _ = BATCHED[which]
+    nb, M, N, K = 6, 140, 96, 80
+    A1, B = rand((1, M, K), 118).to(dt), rand((nb, K, N), 119).to(dt)
+    A = A1.expand(nb, M, K)
+    got = run_batched(fn, A, B)
+    R, T = oracle_batched(A, B, which)
+    assert_close(got, R, T, f"{which} shared A")
+    B1 = rand((1, K, N), 120).to(dt)
+    got = run_batched(fn, rand((nb, M, K), 121).to(dt), B1.expand(nb, K, N))
+    R, T = oracle_batched(rand((nb, M, K), 121).to(dt), B1.expand(nb, K, N), which)
+    assert_close(got, R, T, f"{which} shared B")
+
+
+def test_batched_padded_strides_and_guards():
+    """Items further apart than one matrix (stride > span) and C row padding:
+    the gaps between items and the padding columns keep their contents."""
+    nb, M, N, K = 4, 70, 50, 44
+    Aw, Bw = rand((nb, M + 3, K + 4), 122), rand((nb, K + 2, N + 8), 123)
+    A, B = Aw[:, :M, :K], Bw[:, :K, :N]
+    Cw = torch.full((nb, M + 2, N + 4), 7.0, device=DEV)
+    Cd = Cw[:, :M, :N]
+    ll.gemm_f32_batched(Aw.to(DEV)[:, :M, :K], Bw.to(DEV)[:, :K, :N], Cd)
+    torch.cuda.synchronize()
+    R, T = oracle_batched(A, B, "f32")
+    assert_close(np32(Cd), R, T, "padded strides")
+    guard = np32(Cw).copy()
+    guard[:, :M, :N] = 7.0
+    assert np.all(guard == 7.0)
+
+
+@pytest.mark.parametrize("S", [2, 3])
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
+def test_batched_split_k(S, beta, split):
+    """Split-K on a batch: C_i = beta*C_i for every item first, then atomics."""
+    split(S)
+    nb, M, N, K = 3, 100, 72, 400
+    A, B, C = rand((nb, M, K), 124), rand((nb, K, N), 125), rand((nb, M, N), 126)
+    got = run_batched(ll.gemm_f32_batched, A, B, 1.25, beta, C if beta else None)
+    R, T = oracle_batched(A, B, "f32", 1.25, beta, C if beta else None)
+    assert_close(got, R, T, f"batched split {S} beta {beta}")
+    for which in ("f16", "bf16"):
+        fn, dt, _ = BATCHED[which]
+        A16, B16 = A.to(dt), B.to(dt)
+        got = run_batched(fn, A16, B16, 1.0, beta, C if beta else None)
+        R, T = oracle_batched(A16, B16, which, 1.0, beta, C if beta else None)
+        assert_close(got, R, T, f"{which} batched split {S} beta {beta}")
+
+
+def test_batched_degenerate():
+    nb, M, N = 5, 20, 12
+    C = rand((nb, M, N), 127)
+    # K == 0 and alpha == 0: C_i = beta*C_i for every item
+    for K, alpha in ((0, 1.0), (8, 0.0)):
+        A, B = rand((nb, M, K), 128), rand((nb, K, N), 129)
+        got = run_batched(ll.gemm_f32_batched, A, B, alpha, 0.5, C)
+        R, T = oracle_batched(A, B, "f32", alpha, 0.5, C)
+        assert_close(got, R, T, f"K={K} alpha={alpha}")
+    # an empty batch is a no-op
+    Ce = torch.zeros((0, M, N), device=DEV)
+    ll.gemm_f32_batched(torch.zeros((0, M, 8), device=DEV), torch.zeros((0, 8, N), device=DEV), Ce)
+    # one item equals the single-product entry point bit for bit
+    A, B = rand((1, M, 8), 130), rand((1, 8, N), 131)
+    assert np.array_equal(run_batched(ll.gemm_f32_batched, A, B), run_gemm_f32(A[0], B[0])[None])
+
+
+def test_batched_more_items_than_one_launch():
+    """70000 items exceed the 65535 items of one launch's grid z."""
+    nb, M, N, K = 70000, 8, 8, 8
+    A, B = wl.integers((nb, M, K), 132, -2, 2), wl.integers((nb, K, N), 133, -2, 2)
+    got = run_batched(ll.gemm_f32_batched, A, B)
+    R, _ = oracle_batched(A, B, "f32")
+    assert_exact(got, R, "70000 items")
+
+
+def test_batched_integer_exact():
+    nb, M, N, K = 9, 150, 130, 260
+    A, B = wl.integers((nb, M, K), 134, -2, 2), wl.integers((nb, N, K), 135, -2, 2)
+    for trans_b in (False, True):
+        Bx = B if trans_b else B.transpose(1, 2).contiguous()
+        R, _ = oracle_batched(A, Bx, "f32", trans_b=trans_b)
+        assert_exact(run_batched(ll.gemm_f32_batched, A, Bx, trans_b=trans_b), R, f"f32 tb={trans_b}")
+    A8, B8 = wl.integers((nb, M, K), 136, -8, 8), wl.integers((nb, N, K), 137, -8, 8)
+    for which in ("f16", "bf16"):
+        fn, dt, _ = BATCHED[which]
+        R, _ = oracle_batched(A8.to(dt), B8.to(dt), which, trans_b=True)
+        assert_exact(run_batched(fn, A8.to(dt), B8.to(dt), trans_b=True), R, which)
+
+
 # ---- full-size workloads, as the bench launches them ------------------------
 
 def sample_positions(M, N, n, seed):
@@ -694,11 +855,33 @@ def test_full_gemm_f16_nt():
     checksums(got, A.double().numpy(), B.double().numpy().T)
 
 
+def test_full_gemm_f32_batched():
+    """256 items of 256^3: eight whole items against the oracle (first, last and
+    six drawn at random) and row/column checksums of every item."""
+    w = wl.WORKLOADS["gemm_f32_batched_256x256x256_b256"]
+    x = wl.make_inputs(w)
+    A, B = x["A"], x["B"]
+    got = run_batched(ll.gemm_f32_batched, A, B, w.alpha, w.beta)
+    items = np.unique(np.concatenate([[0, w.batch - 1],
+                                      np.random.default_rng(w.index).integers(0, w.batch, 6)]))
+    R, T = oracle.gemm_batched(np32(A[items]), np32(B[items]), w.alpha, w.beta)
+    ratio = assert_close(got[items], R, T, w.name)
+    print(f"{w.name}: max err/t on {len(items)} items = {ratio:.3g}")
+    A64, B64 = np32(A).astype(np.float64), np32(B).astype(np.float64)
+    for i in range(w.batch):
+        checksums(got[i], A64[i], B64[i], w.alpha)
+
+
 @pytest.mark.parametrize("name", list(wl.WORKLOADS))
 def test_full_integer_exact(name):
     w = wl.WORKLOADS[name]
     x = wl.make_inputs(w, integer=True)
     A, B = x["A"], x["B"]
+    if w.kind in wl.BATCHED_KINDS:
+        got = run_batched(ll.gemm_f32_batched, A, B, w.alpha, w.beta)
+        R, _ = oracle.gemm_batched(np32(A), np32(B), w.alpha, w.beta)
+        assert_exact(got, R, name)
+        return
     rows, cols = sample_positions(w.M, w.N, 20000, 1000 + w.index)
     if w.kind == "gemm_f32":
         got = run_gemm_f32(A, B, w.alpha, w.beta, x.get("C"))
