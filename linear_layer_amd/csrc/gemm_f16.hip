@@ -258,6 +258,11 @@ gemm_f16_kernel(GemmParams p)
 }
 
 
+// Sixteen zero bytes in device memory: the source of every direct copy whose
+// elements lie outside A or B, so that each copy is still issued (and counted
+// by the wave's vmcnt) and fills its LDS slot with zeros.
+__device__ __attribute__((aligned(16))) const uint16_t kZeroChunk[8] = {};
+
 // ---------------------------------------------------------------------------
 // Direct-to-LDS FP16 kernel (256x256 block tile, 128-bit-aligned operands).
 //
@@ -280,10 +285,14 @@ gemm_f16_kernel(GemmParams p)
 //      k-rows one 16-lane transpose read touches fall in four different
 //      32-byte units of a 128-byte bank line. One copy = 2 rows; lane l fills
 //      row l/32, bytes 16*(l%32) .. +15.
-// Four stages form a ring (128 KiB). The barrier that ends stage kt also
-// publishes stage kt+2, so during stage kt each wave already reads the first
-// operands of stage kt+1 and no LDS latency is exposed after a barrier; the
-// copies of stage kt+3 are issued into the buffer stage kt-1 used.
+// Four stages form a ring (128 KiB). Each stage holds two k-steps, and its
+// barrier sits between them: by then every wave holds the second k-step's
+// operands in registers, so the barrier publishes stage kt+1 and frees stage
+// kt's buffer, which is refilled at once with stage kt+4. The first operands
+// of stage kt+1 are read while the second k-step's MFMAs run, so no LDS
+// latency is exposed, and each stage has three stages' time to arrive. The
+// refill's copies are spread among those MFMAs, one after every second MFMA,
+// instead of being issued in one burst the matrix cores would wait through.
 //
 // With BT (B given N-by-K, k contiguous) B is copied and read exactly like A:
 // 256 rows x 64 bytes, the same swizzle, 128-bit operand reads, no transposing
@@ -326,38 +335,38 @@ gemm_f16_direct_kernel(GemmParams p)
     const int b_kr0 = wave * COPIES * 2 + (lane >> 5);
     const uint32_t as_base = lds_addr(&As[0][0]), bs_base = lds_addr(&Bs[0][0]);
 
-    auto issue = [&](int buf, int k0) {
-        const uint32_t as = as_base + buf * (A_STAGE * 2), bs = bs_base + buf * (B_STAGE * 2);
+    // Copy c (0..3: A, 4..7: B) of the stage at k0 into buffer buf. Every
+    // copy is one global_load_lds on every lane: lanes whose 16 bytes lie
+    // outside A or B read kZeroChunk instead, so each stage is exactly
+    // PER_STAGE copies per wave and the vmcnt waits below count exactly.
+    const uint16_t *b_src[COPIES];
 #pragma unroll
-        for (int j = 0; j < COPIES; ++j) {
-            const uint32_t dst = as + (wave * COPIES + j) * 1024;
-            if (m0 + a_row0 + j * 16 < M && k0 + a_c * 8 < K)
-                lds_dma_16(a_src + j * a_jstep + k0, dst);
-            else
-                lds_zero_16(dst + lane * 16);
-        }
-        if (BT) {
-#pragma unroll
-            for (int j = 0; j < COPIES; ++j) {
-                const uint32_t dst = bs + (wave * COPIES + j) * 1024;
-                if (n0 + a_row0 + j * 16 < N && k0 + a_c * 8 < K)
-                    lds_dma_16(bt_src + j * bt_jstep + k0, dst);
-                else
-                    lds_zero_16(dst + lane * 16);
+    for (int j = 0; j < COPIES; ++j) {
+        const int kr = b_kr0 + j * 2;
+        const int u = ((lane & 31) >> 1) ^ (kr & 3);
+        b_src[j] = B + (int64_t)kr * p.ldb + n0 + u * 16 + (lane & 1) * 8;
+    }
+    auto copy = [&](int buf, int k0, int c) {
+        const uint16_t *src;
+        uint32_t dst;
+        if (c < COPIES) {
+            dst = as_base + buf * (A_STAGE * 2) + (wave * COPIES + c) * 1024;
+            const bool ok = m0 + a_row0 + c * 16 < M && k0 + a_c * 8 < K;
+            src = ok ? a_src + c * a_jstep + k0 : kZeroChunk;
+        } else {
+            const int j = c - COPIES;
+            dst = bs_base + buf * (B_STAGE * 2) + (wave * COPIES + j) * 1024;
+            if (BT) {
+                const bool ok = n0 + a_row0 + j * 16 < N && k0 + a_c * 8 < K;
+                src = ok ? bt_src + j * bt_jstep + k0 : kZeroChunk;
+            } else {
+                const int kr = b_kr0 + j * 2;
+                const int col = n0 + ((((lane & 31) >> 1) ^ (kr & 3)) * 16) + (lane & 1) * 8;
+                const bool ok = k0 + kr < K && col < N;
+                src = ok ? b_src[j] + (int64_t)k0 * p.ldb : kZeroChunk;
             }
-            return;
         }
-#pragma unroll
-        for (int j = 0; j < COPIES; ++j) {
-            const int kr = b_kr0 + j * 2;
-            const uint32_t dst = bs + (wave * COPIES + j) * 1024;
-            const int u = ((lane & 31) >> 1) ^ (kr & 3);
-            const int col = n0 + u * 16 + (lane & 1) * 8;
-            if (k0 + kr < K && col < N)
-                lds_dma_16(B + (int64_t)(k0 + kr) * p.ldb + col, dst);
-            else
-                lds_zero_16(dst + lane * 16);
-        }
+        lds_dma_16(src, dst);
     };
 
     f32x16 acc[FM][FN];
@@ -416,42 +425,58 @@ gemm_f16_direct_kernel(GemmParams p)
                 acc[fm][fn] = mma16<BF16>(af[fm], bf[fn], acc[fm][fn]);
     };
 
+    // Wait until at most n stages of copies are still in flight.
+    auto wait_stages = [&](int n) {
+        if (n >= 3)
+            __builtin_amdgcn_s_waitcnt(LL_VMCNT(3 * PER_STAGE));
+        else if (n == 2)
+            __builtin_amdgcn_s_waitcnt(LL_VMCNT(2 * PER_STAGE));
+        else if (n == 1)
+            __builtin_amdgcn_s_waitcnt(LL_VMCNT(PER_STAGE));
+        else
+            __builtin_amdgcn_s_waitcnt(LL_VMCNT(0));
+    };
+    static_assert(NBUF - 1 <= 3, "wait_stages covers at most three stages in flight");
+
     const int nk = (K + BK - 1) / BK;
-    for (int st = 0; st < NBUF - 1; ++st)
-        if (st < nk)
-            issue(st, st * BK);
-    // stages 0 and 1 must have landed; stage 2 may still be in flight
-    if (nk > 2)
-        __builtin_amdgcn_s_waitcnt(LL_VMCNT(PER_STAGE));
-    else
-        __builtin_amdgcn_s_waitcnt(LL_VMCNT(0));
+    for (int st = 0; st < NBUF; ++st)
+        if (st < nk) {
+#pragma unroll
+            for (int c = 0; c < PER_STAGE; ++c)
+                copy(st, st * BK, c);
+        }
+    wait_stages((nk < NBUF ? nk : NBUF) - 1);   // stage 0 has landed
     __syncthreads();
 
     f16x8 a0[FM], b0[FN];
     read_step(0, 0, a0, b0);
     int buf = 0;
     for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
         const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
-        if (kt + 3 < nk)
-            issue(buf == 0 ? NBUF - 1 : buf - 1, (kt + 3) * BK);   // stage kt-1's buffer
         f16x8 a1[FM], b1[FN];
         read_step(buf, 1, a1, b1);
         mfma_step(a0, b0);
-        // First operands of stage kt+1, published by the last barrier. Read
-        // unconditionally (on the last stage they are stale, in-bounds and
-        // unused) so that no control-flow join makes the compiler's LDS wait
-        // counts conservative for the MFMAs below.
-        read_step(nbuf, 0, a0, b0);
-        mfma_step(a1, b1);
-        if (more) {
-            // publish stage kt+2 (stage kt+3 may still be in flight); after this
-            // barrier every wave is done with stage kt's buffer
-            if (kt + 3 < nk)
-                __builtin_amdgcn_s_waitcnt(LL_VMCNT(PER_STAGE));
-            else
-                __builtin_amdgcn_s_waitcnt(LL_VMCNT(0));
+        if (kt + 1 < nk) {
+            // stage kt+1 has landed (stages up to kt+NBUF-1 were issued); after
+            // the barrier every wave is done with this stage's buffer
+            wait_stages((kt + NBUF - 1 < nk ? kt + NBUF - 1 : nk - 1) - (kt + 1));
             __syncthreads();
+        }
+        const int k_next = (kt + NBUF) * BK;   // refill this buffer with stage kt+NBUF
+        const bool refill = kt + NBUF < nk;
+        // First operands of stage kt+1. Read unconditionally (after the last
+        // stage they are stale, in-bounds and unused) so that no control-flow
+        // join makes the compiler's LDS wait counts conservative.
+        read_step(nbuf, 0, a0, b0);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = mma16<BF16>(a1[fm], b1[fn], acc[fm][fn]);
+            if (refill) {
+                copy(buf, k_next, 2 * fm);
+                copy(buf, k_next, 2 * fm + 1);
+            }
         }
         buf = nbuf;
     }
