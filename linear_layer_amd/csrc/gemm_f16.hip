@@ -275,37 +275,43 @@ __device__ __attribute__((aligned(16))) const uint16_t kZeroChunk[8] = {};
 // i/4, 4+i/4, 8+i/4 and 12+i/4 address. If lane j points at
 // B[kb + j/4][nb + 4*(j%4)], lane i therefore receives B[kb .. kb+3][nb + i].
 //
-// LDS, per stage of BK = 32:
-//   A: 256 rows x 64 bytes; 16-byte chunks XOR-swizzled by (row/4)%4, so the
-//      16 lanes one LDS cycle serves (16 consecutive rows, one logical chunk)
-//      hit 16 different 16-byte bank groups (measured conflict-free). One
-//      copy (KiB) = 16 rows; lane l fills row l/4, slot l%4 and fetches the
-//      logical chunk (l%4) ^ ((l/16)%4).
-//   B: 32 rows x 512 bytes; 32-byte units XOR-swizzled by k%4, so the four
+// LDS, per stage of BK k-values (CPR = BK/8 16-byte chunks per A row):
+//   A: 256 rows x 2*BK bytes; chunks XOR-swizzled by (row / (16/CPR)) % CPR,
+//      so the 16 lanes one LDS cycle serves (16 consecutive rows, one logical
+//      chunk) hit 16 different 16-byte bank groups (measured conflict-free).
+//      One copy (KiB) = 64/CPR rows; lane l fills row l/CPR, slot l%CPR, and
+//      fetches the logical chunk that the swizzle puts in that slot.
+//   B: BK rows x 512 bytes; 32-byte units XOR-swizzled by k%4, so the four
 //      k-rows one 16-lane transpose read touches fall in four different
 //      32-byte units of a 128-byte bank line. One copy = 2 rows; lane l fills
 //      row l/32, bytes 16*(l%32) .. +15.
-// Four stages form a ring (128 KiB). Each stage holds two k-steps, and its
-// barrier sits between them: by then every wave holds the second k-step's
-// operands in registers, so the barrier publishes stage kt+1 and frees stage
-// kt's buffer, which is refilled at once with stage kt+4. The first operands
-// of stage kt+1 are read while the second k-step's MFMAs run, so no LDS
-// latency is exposed, and each stage has three stages' time to arrive. The
-// refill's copies are spread among those MFMAs, one after every second MFMA,
-// instead of being issued in one burst the matrix cores would wait through.
+// NBUF stages form a ring. A stage holds BK/16 k-steps; each step's operands
+// are read while the previous step's MFMAs run. The stage's barrier sits
+// before its last step, whose operands are then in registers: it publishes
+// stage kt+1 and frees stage kt's buffer, which is refilled at once with stage
+// kt+NBUF while the last step's MFMAs run (a few copies after each row of
+// four MFMAs, not one burst the matrix cores would wait through). The first
+// operands of stage kt+1 are read during those MFMAs too, so no LDS latency
+// is exposed after a barrier.
 //
 // With BT (B given N-by-K, k contiguous) B is copied and read exactly like A:
-// 256 rows x 64 bytes, the same swizzle, 128-bit operand reads, no transposing
-// loads.
-template <int EPI, bool BF16, bool BT>
+// 256 rows x 2*BK bytes, the same swizzle, 128-bit operand reads, no
+// transposing loads.
+template <int EPI, bool BF16, bool BT, int BK, int NBUF>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_f16_direct_kernel(GemmParams p)
 {
-    constexpr int BM = 256, BN = 256, BK = 32, NBUF = 4;
+    constexpr int BM = 256, BN = 256;
     constexpr int FM = 4, FN = 4, WTM = 128, WTN = 128;
-    constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;      // halves
-    constexpr int COPIES = 4;                                 // per wave per operand per stage
-    constexpr int PER_STAGE = 2 * COPIES;                     // vmcnt entries per stage
+    constexpr int STEPS = BK / 16;                        // MFMA k-steps per stage
+    constexpr int CPR = BK / 8;                           // 16-byte chunks per A row
+    constexpr int RPC = 64 / CPR;                         // A rows per copy
+    constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;   // halves
+    constexpr int COPIES_A = BM / RPC / 4;                // per wave per stage
+    constexpr int COPIES_B = BT ? COPIES_A : BK / 2 / 4;
+    constexpr int PER_STAGE = COPIES_A + COPIES_B;        // vmcnt entries per stage
+    static_assert(STEPS % 2 == 0 && PER_STAGE % FM == 0, "stage layout");
+    static_assert((NBUF - 1) * PER_STAGE <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) uint16_t As[NBUF][A_STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t Bs[NBUF][B_STAGE];
 
@@ -322,49 +328,57 @@ gemm_f16_direct_kernel(GemmParams p)
     const uint16_t *__restrict__ B =
         static_cast<const uint16_t *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
     const int M = p.M, N = p.N;
+    auto swz = [](int row) { return (row / (16 / CPR)) & (CPR - 1); };
 
-    // Copy sources. A copy j of this wave: rows (wave*4 + j)*16 + lane/4.
-    const int a_c = (lane & 3) ^ ((lane >> 4) & 3);
-    const int a_row0 = wave * COPIES * 16 + (lane >> 2);
-    const uint16_t *a_src = A + (int64_t)(m0 + a_row0) * p.lda + a_c * 8;
-    const int64_t a_jstep = (int64_t)16 * p.lda;
-    const uint16_t *bt_src = B + (int64_t)(n0 + a_row0) * p.ldb + a_c * 8;   // BT
-    const int64_t bt_jstep = (int64_t)16 * p.ldb;
-    // B copy j of this wave: k-row (wave*4 + j)*2 + lane/32; the lane's 16
-    // bytes hold logical unit (((lane%32)/2) ^ (k%4)), half (lane%2).
-    const int b_kr0 = wave * COPIES * 2 + (lane >> 5);
+    // Copy sources. Row-panel copy j of this wave (A, or B given N-by-K)
+    // covers rows (wave*COPIES_A + j)*RPC + lane/CPR. Each wave's first row is
+    // a multiple of 16, so the swizzled chunk a lane fetches depends only on
+    // (j*RPC) % 16: one variant when RPC = 16, two (j even, j odd) when RPC = 8.
+    const int r_lane = wave * COPIES_A * RPC + lane / CPR;   // row of copy 0
+    const int slot = lane % CPR;
+    int ch[2];
+    const uint16_t *a_src[2], *bt_src[2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        ch[v] = slot ^ swz(((v * RPC) & 15) + lane / CPR);
+        a_src[v] = A + (int64_t)(m0 + r_lane) * p.lda + ch[v] * 8;
+        bt_src[v] = B + (int64_t)(n0 + r_lane) * p.ldb + ch[v] * 8;
+    }
+    // B copy j (given K-by-N): k-row (wave*COPIES_B + j)*2 + lane/32; the
+    // lane's 16 bytes hold logical unit (((lane%32)/2) ^ (k%4)), half lane%2.
+    constexpr int NB_SRC = BT ? 1 : COPIES_B;
+    const uint16_t *b_src[NB_SRC];
+    bool b_col_ok[NB_SRC];
+#pragma unroll
+    for (int j = 0; j < NB_SRC; ++j) {
+        const int kr = (wave * COPIES_B + j) * 2 + (lane >> 5);
+        const int col = n0 + ((((lane & 31) >> 1) ^ (kr & 3)) * 16) + (lane & 1) * 8;
+        b_src[j] = B + (int64_t)kr * p.ldb + col;
+        b_col_ok[j] = col < N;
+    }
     const uint32_t as_base = lds_addr(&As[0][0]), bs_base = lds_addr(&Bs[0][0]);
 
-    // Copy c (0..3: A, 4..7: B) of the stage at k0 into buffer buf. Every
-    // copy is one global_load_lds on every lane: lanes whose 16 bytes lie
-    // outside A or B read kZeroChunk instead, so each stage is exactly
+    // Copy c (A: 0 .. COPIES_A-1, then B) of the stage at k0 into buffer buf.
+    // Every copy is one global_load_lds on every lane: lanes whose 16 bytes
+    // lie outside A or B read kZeroChunk instead, so each stage is exactly
     // PER_STAGE copies per wave and the vmcnt waits below count exactly.
-    const uint16_t *b_src[COPIES];
-#pragma unroll
-    for (int j = 0; j < COPIES; ++j) {
-        const int kr = b_kr0 + j * 2;
-        const int u = ((lane & 31) >> 1) ^ (kr & 3);
-        b_src[j] = B + (int64_t)kr * p.ldb + n0 + u * 16 + (lane & 1) * 8;
-    }
     auto copy = [&](int buf, int k0, int c) {
         const uint16_t *src;
         uint32_t dst;
-        if (c < COPIES) {
-            dst = as_base + buf * (A_STAGE * 2) + (wave * COPIES + c) * 1024;
-            const bool ok = m0 + a_row0 + c * 16 < M && k0 + a_c * 8 < K;
-            src = ok ? a_src + c * a_jstep + k0 : kZeroChunk;
+        if (c < COPIES_A || BT) {
+            const bool is_a = c < COPIES_A;
+            const int j = is_a ? c : c - COPIES_A;
+            const int v = ((j * RPC) & 15) != 0;
+            dst = (is_a ? as_base + buf * (A_STAGE * 2) : bs_base + buf * (B_STAGE * 2)) +
+                  (wave * COPIES_A + j) * 1024;
+            const bool ok = r_lane + j * RPC < (is_a ? M - m0 : N - n0) && k0 + ch[v] * 8 < K;
+            const int64_t step = (int64_t)(j * RPC) * (is_a ? p.lda : p.ldb) + k0;
+            src = ok ? (is_a ? a_src[v] : bt_src[v]) + step : kZeroChunk;
         } else {
-            const int j = c - COPIES;
-            dst = bs_base + buf * (B_STAGE * 2) + (wave * COPIES + j) * 1024;
-            if (BT) {
-                const bool ok = n0 + a_row0 + j * 16 < N && k0 + a_c * 8 < K;
-                src = ok ? bt_src + j * bt_jstep + k0 : kZeroChunk;
-            } else {
-                const int kr = b_kr0 + j * 2;
-                const int col = n0 + ((((lane & 31) >> 1) ^ (kr & 3)) * 16) + (lane & 1) * 8;
-                const bool ok = k0 + kr < K && col < N;
-                src = ok ? b_src[j] + (int64_t)k0 * p.ldb : kZeroChunk;
-            }
+            const int j = c - COPIES_A;
+            dst = bs_base + buf * (B_STAGE * 2) + (wave * COPIES_B + j) * 1024;
+            const bool ok = k0 + (wave * COPIES_B + j) * 2 + (lane >> 5) < K && b_col_ok[j];
+            src = ok ? b_src[j] + (int64_t)k0 * p.ldb : kZeroChunk;
         }
         lds_dma_16(src, dst);
     };
@@ -389,14 +403,14 @@ gemm_f16_direct_kernel(GemmParams p)
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
             const int row = wm * WTM + fm * 32 + l32;
-            const int c = (2 * s + h) ^ ((row >> 2) & 3);
+            const int c = (2 * s + h) ^ swz(row);
             af[fm] = *reinterpret_cast<const f16x8 *>(&as[row * BK + c * 8]);
         }
         if (BT) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
                 const int row = wn * WTN + fn * 32 + l32;
-                const int c = (2 * s + h) ^ ((row >> 2) & 3);
+                const int c = (2 * s + h) ^ swz(row);
                 bf[fn] = *reinterpret_cast<const f16x8 *>(&bs[row * BK + c * 8]);
             }
             return;
@@ -428,9 +442,9 @@ gemm_f16_direct_kernel(GemmParams p)
     // Wait until at most n stages of copies are still in flight.
     auto wait_stages = [&](int n) {
         if (n >= 3)
-            __builtin_amdgcn_s_waitcnt(LL_VMCNT(3 * PER_STAGE));
+            __builtin_amdgcn_s_waitcnt(LL_VMCNT(3 * PER_STAGE > 63 ? 63 : 3 * PER_STAGE));
         else if (n == 2)
-            __builtin_amdgcn_s_waitcnt(LL_VMCNT(2 * PER_STAGE));
+            __builtin_amdgcn_s_waitcnt(LL_VMCNT(2 * PER_STAGE > 63 ? 63 : 2 * PER_STAGE));
         else if (n == 1)
             __builtin_amdgcn_s_waitcnt(LL_VMCNT(PER_STAGE));
         else
@@ -448,14 +462,16 @@ gemm_f16_direct_kernel(GemmParams p)
     wait_stages((nk < NBUF ? nk : NBUF) - 1);   // stage 0 has landed
     __syncthreads();
 
-    f16x8 a0[FM], b0[FN];
-    read_step(0, 0, a0, b0);
+    f16x8 fa[2][FM], fb[2][FN];   // operands of two consecutive k-steps
+    read_step(0, 0, fa[0], fb[0]);
     int buf = 0;
     for (int kt = 0; kt < nk; ++kt) {
         const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
-        f16x8 a1[FM], b1[FN];
-        read_step(buf, 1, a1, b1);
-        mfma_step(a0, b0);
+#pragma unroll
+        for (int s = 0; s + 1 < STEPS; ++s) {
+            read_step(buf, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            mfma_step(fa[s & 1], fb[s & 1]);
+        }
         if (kt + 1 < nk) {
             // stage kt+1 has landed (stages up to kt+NBUF-1 were issued); after
             // the barrier every wave is done with this stage's buffer
@@ -467,15 +483,17 @@ gemm_f16_direct_kernel(GemmParams p)
         // First operands of stage kt+1. Read unconditionally (after the last
         // stage they are stale, in-bounds and unused) so that no control-flow
         // join makes the compiler's LDS wait counts conservative.
-        read_step(nbuf, 0, a0, b0);
+        read_step(nbuf, 0, fa[0], fb[0]);
+        constexpr int G = PER_STAGE / FM;   // refill copies after each row of MFMAs
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                acc[fm][fn] = mma16<BF16>(a1[fm], b1[fn], acc[fm][fn]);
+                acc[fm][fn] = mma16<BF16>(fa[1][fm], fb[1][fn], acc[fm][fn]);
             if (refill) {
-                copy(buf, k_next, 2 * fm);
-                copy(buf, k_next, 2 * fm + 1);
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    copy(buf, k_next, fm * G + g);
             }
         }
         buf = nbuf;
@@ -487,6 +505,14 @@ gemm_f16_direct_kernel(GemmParams p)
         for (int fn = 0; fn < FN; ++fn)
             write_block<EPI>(p, acc[fm][fn], m0 + wm * WTM + fm * 32, n0 + wn * WTN + fn * 32, lane);
 }
+
+// Stage depth and ring length of the direct kernel, per B layout (measured
+// on 4096- and 8192-cubed products): with B given N-by-K both operands are
+// copied as row panels, which read whole 128-byte lines at BK = 64 (+5 %);
+// with B given K-by-N, BK = 32 in a four-stage ring is as fast or faster.
+template <bool BT> struct DirectCfg {
+    static constexpr int BK = BT ? 64 : 32, NBUF = BT ? 2 : 4;
+};
 
 using F16_L = F16Tile<256, 256, 64>;
 using F16_S = F16Tile<128, 128, 64>;
@@ -520,7 +546,7 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // {BM, BN, workgroups per CU, relative throughput alone, paired} (see the
 // FP32 table); measured on the 8192^3 product.
 const TileInfo kF16Tiles[kF16NumTiles] = {
-    {F16_L::BM, F16_L::BN, 1, 1.00f, 1.00f, "f16_256x256x32"},
+    {F16_L::BM, F16_L::BN, 1, 1.00f, 1.00f, "f16_256x256_direct"},
     {F16_S::BM, F16_S::BN, 2, 0.52f, 0.68f, "f16_128x128x64"},
     {F16_XS::BM, F16_XS::BN, 2, 0.22f, 0.28f, "f16_64x64x64"},
 };
@@ -537,12 +563,16 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
         return hipErrorInvalidValue;
     const dim3 grid = gemm_grid(p, ntiles), block(256);
+    using Cfg = DirectCfg<BT>;
+#define LL_DIRECT(E) \
+    hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF>), grid, block, 0, s, p)
     if (epi == EPI_GEMM_BETA0)
-        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_GEMM_BETA0, BF16, BT>), grid, block, 0, s, p);
+        LL_DIRECT(EPI_GEMM_BETA0);
     else if (epi == EPI_GEMM_BETA)
-        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_GEMM_BETA, BF16, BT>), grid, block, 0, s, p);
+        LL_DIRECT(EPI_GEMM_BETA);
     else
-        hipLaunchKernelGGL((gemm_f16_direct_kernel<EPI_ATOMIC, BF16, BT>), grid, block, 0, s, p);
+        LL_DIRECT(EPI_ATOMIC);
+#undef LL_DIRECT
     return hipGetLastError();
 }
 

@@ -169,7 +169,7 @@ def test_tile_choice():
     f32, f16 = ll.DTYPE_F32, ll.DTYPE_F16
     names32 = [ll.tile_name(f32, t) for t in range(ll.num_tiles(f32))]
     names16 = [ll.tile_name(f16, t) for t in range(ll.num_tiles(f16))]
-    assert names32[0] == "f32_256x256x16" and names16[0] == "f16_256x256x32"
+    assert names32[0] == "f32_256x256x16" and names16[0] == "f16_256x256_direct"
     assert ll.tile_name(f32, 99) == "" and ll.num_tiles(7) == 0
 
     def choice(dt, M, N, K, cus=256):
@@ -181,7 +181,7 @@ def test_tile_choice():
     assert choice(f32, 4096, 4096, 4096) == ("f32_256x128x16", 1)
     # 2047 x 11008: 256x256 tiles leave a partial second round; 256x128 fills better
     assert choice(f32, 2047, 11008, 4096) == ("f32_256x128x16", 1)
-    assert choice(f16, 8192, 8192, 8192) == ("f16_256x256x32", 1)
+    assert choice(f16, 8192, 8192, 8192) == ("f16_256x256_direct", 1)
     # problems too small to fill 256 CUs use small tiles and split K
     assert choice(f32, 1024, 1024, 1024)[1] > 1
     assert choice(f32, 256, 256, 256) == ("f32_64x64x16", 4)
