@@ -281,10 +281,14 @@ __device__ __attribute__((aligned(16))) const uint16_t kZeroChunk[8] = {};
 //      chunk) hit 16 different 16-byte bank groups (measured conflict-free).
 //      One copy (KiB) = 64/CPR rows; lane l fills row l/CPR, slot l%CPR, and
 //      fetches the logical chunk that the swizzle puts in that slot.
-//   B: BK rows x 512 bytes; 32-byte units XOR-swizzled by k%4, so the four
-//      k-rows one 16-lane transpose read touches fall in four different
-//      32-byte units of a 128-byte bank line. One copy = 2 rows; lane l fills
-//      row l/32, bytes 16*(l%32) .. +15.
+//   B: BK rows x 512 bytes; 32-byte units XOR-swizzled by 2*(k%4). A
+//      transposing read is served 32 lanes (256 bytes) per LDS cycle: two
+//      16-lane groups, each reading one 32-byte unit (units u and u+1, u
+//      even) of the same four k-rows. The XOR sends the even group to units
+//      u^{0,2,4,6} and the odd one to the odd units between, eight different
+//      32-byte slots of the 256-byte bank line (XOR by k%4 would put both
+//      groups on units u..u+3: a two-way conflict, measured). One copy = 2
+//      rows; lane l fills row l/32, bytes 16*(l%32) .. +15.
 // NBUF stages form a ring. A stage holds BK/16 k-steps; each step's operands
 // are read while the previous step's MFMAs run. The stage's barrier sits
 // before its last step, whose operands are then in registers: it publishes
@@ -352,7 +356,7 @@ gemm_f16_direct_kernel(GemmParams p)
 #pragma unroll
     for (int j = 0; j < NB_SRC; ++j) {
         const int kr = (wave * COPIES_B + j) * 2 + (lane >> 5);
-        const int col = n0 + ((((lane & 31) >> 1) ^ (kr & 3)) * 16) + (lane & 1) * 8;
+        const int col = n0 + ((((lane & 31) >> 1) ^ (2 * (kr & 3))) * 16) + (lane & 1) * 8;
         b_src[j] = B + (int64_t)kr * p.ldb + col;
         b_col_ok[j] = col < N;
     }
@@ -422,7 +426,7 @@ gemm_f16_direct_kernel(GemmParams p)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int k = 16 * s + 8 * h + 4 * e + (j16 >> 2);
-                const int addr = k * BN + (((n >> 4) ^ (k & 3)) << 4) + (n & 15);
+                const int addr = k * BN + (((n >> 4) ^ (2 * (k & 3))) << 4) + (n & 15);
                 v[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) s16x4 *)(lds_addr(&bs[addr])));
             }
@@ -506,12 +510,12 @@ gemm_f16_direct_kernel(GemmParams p)
             write_block<EPI>(p, acc[fm][fn], m0 + wm * WTM + fm * 32, n0 + wn * WTN + fn * 32, lane);
 }
 
-// Stage depth and ring length of the direct kernel, per B layout (measured
-// on 4096- and 8192-cubed products): with B given N-by-K both operands are
-// copied as row panels, which read whole 128-byte lines at BK = 64 (+5 %);
-// with B given K-by-N, BK = 32 in a four-stage ring is as fast or faster.
+// Stage depth and ring length of the direct kernel. At BK = 64 a row panel's
+// copies read whole 128-byte lines and a stage holds four k-steps under one
+// barrier; two 64 KiB stages measured 6-10 % faster than four 32 KiB ones
+// (BK = 32) for both B layouts on 4096- and 8192-cubed products.
 template <bool BT> struct DirectCfg {
-    static constexpr int BK = BT ? 64 : 32, NBUF = BT ? 2 : 4;
+    static constexpr int BK = 64, NBUF = 2;
 };
 
 using F16_L = F16Tile<256, 256, 64>;
