@@ -123,12 +123,16 @@ __device__ __forceinline__ void lds_dma_16(const void *src, uint32_t lds_base)
                  : "memory", "m0");
 }
 
-// Zero the 16-byte LDS slot at a byte address (for lanes whose source lies
-// outside the matrix; the copy above cannot produce zeros).
-__device__ __forceinline__ void lds_zero_16(uint32_t lds_byte_addr)
+// Sixteen zero bytes in device memory: the source of every direct copy whose
+// elements lie outside the matrix. Such a copy is still issued on every lane
+// (so each wave's vmcnt counts a fixed number of copies per stage) and fills
+// its LDS slot with zeros.
+static __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+
+template <class T>
+__device__ __forceinline__ const T *zero_chunk()
 {
-    *reinterpret_cast<__attribute__((address_space(3))) u32x4 *>(lds_byte_addr) =
-        u32x4{0u, 0u, 0u, 0u};
+    return reinterpret_cast<const T *>(kZeroChunk);
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of

@@ -258,11 +258,6 @@ gemm_f16_kernel(GemmParams p)
 }
 
 
-// Sixteen zero bytes in device memory: the source of every direct copy whose
-// elements lie outside A or B, so that each copy is still issued (and counted
-// by the wave's vmcnt) and fills its LDS slot with zeros.
-__device__ __attribute__((aligned(16))) const uint16_t kZeroChunk[8] = {};
-
 // ---------------------------------------------------------------------------
 // Direct-to-LDS FP16 kernel (256x256 block tile, 128-bit-aligned operands).
 //
@@ -364,7 +359,7 @@ gemm_f16_direct_kernel(GemmParams p)
 
     // Copy c (A: 0 .. COPIES_A-1, then B) of the stage at k0 into buffer buf.
     // Every copy is one global_load_lds on every lane: lanes whose 16 bytes
-    // lie outside A or B read kZeroChunk instead, so each stage is exactly
+    // lie outside A or B read the zero chunk instead, so each stage is exactly
     // PER_STAGE copies per wave and the vmcnt waits below count exactly.
     auto copy = [&](int buf, int k0, int c) {
         const uint16_t *src;
@@ -377,12 +372,12 @@ gemm_f16_direct_kernel(GemmParams p)
                   (wave * COPIES_A + j) * 1024;
             const bool ok = r_lane + j * RPC < (is_a ? M - m0 : N - n0) && k0 + ch[v] * 8 < K;
             const int64_t step = (int64_t)(j * RPC) * (is_a ? p.lda : p.ldb) + k0;
-            src = ok ? (is_a ? a_src[v] : bt_src[v]) + step : kZeroChunk;
+            src = ok ? (is_a ? a_src[v] : bt_src[v]) + step : zero_chunk<uint16_t>();
         } else {
             const int j = c - COPIES_A;
             dst = bs_base + buf * (B_STAGE * 2) + (wave * COPIES_B + j) * 1024;
             const bool ok = k0 + (wave * COPIES_B + j) * 2 + (lane >> 5) < K && b_col_ok[j];
-            src = ok ? b_src[j] + (int64_t)k0 * p.ldb : kZeroChunk;
+            src = ok ? b_src[j] + (int64_t)k0 * p.ldb : zero_chunk<uint16_t>();
         }
         lds_dma_16(src, dst);
     };

@@ -267,16 +267,235 @@ gemm_f32_kernel(GemmParams p)
                              n0 + wn * T::WTN + fn * 32, lane);
 }
 
+// Direct-to-LDS FP32 kernel for B given K-by-N and 128-bit-aligned operands.
+//
+// The same arithmetic as gemm_f32_kernel (k = 8h + s at MFMA step s, A read
+// as eight k-values per lane per stage), but both operands travel global ->
+// LDS with global_load_lds_dwordx4: no staging registers, no LDS stores, and a
+// ring of NBUF stages instead of two.
+//   A: BM rows x 64 bytes per stage; 16-byte chunks XOR-swizzled by
+//      (row/4)%4, so the 16 lanes one LDS cycle serves (16 consecutive rows,
+//      one logical chunk) hit 16 different 16-byte bank groups. One copy
+//      (KiB) = 16 rows; lane l fills row l/4, slot l%4 and fetches the logical
+//      chunk that the swizzle puts there.
+//   B: 16 k-rows x BN floats, unpadded; 16-byte chunks of rows 8..15 XOR 8,
+//      so the two half-waves (rows s and 8+s of a step, 128 bytes each) fall
+//      in different halves of the 256-byte bank line. One copy = 1024/(4*BN)
+//      rows.
+// A stage holds eight k-steps. Its barrier sits before the last step, when
+// the wave holds that step's operands in registers: the barrier publishes
+// stage kt+1 and frees stage kt's buffer, which is refilled with stage
+// kt+NBUF while the last step's MFMAs run (a few copies after each row of
+// MFMAs), and the next stage's A operands and first B operands are read then
+// too. Every copy is one global_load_lds on every lane (lanes outside A or B
+// read the zero chunk), so the vmcnt waits count exactly.
+template <int EPI, int BM, int BN, int NBUF, int WPE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+gemm_f32_direct_kernel(GemmParams p)
+{
+    constexpr int BK = 16, KH = 8;
+    constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
+    constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;       // floats
+    constexpr int COPIES_A = BM / 16 / 4;                     // per wave per stage
+    constexpr int CPB = BN / 4;                               // 16-byte chunks per B row
+    constexpr int RB = 64 / CPB;                              // B rows per copy
+    constexpr int COPIES_B = BK / RB / 4;
+    constexpr int PER_STAGE = COPIES_A + COPIES_B;
+    static_assert(COPIES_A >= 1 && COPIES_B >= 1 && RB >= 1 && CPB >= 16, "tile shape");
+    static_assert((NBUF - 1) * PER_STAGE <= 63 && NBUF >= 2 && NBUF <= 4, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) float As[NBUF][A_STAGE];
+    __shared__ __attribute__((aligned(1024))) float Bs[NBUF][B_STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    select_batch(p);
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    int K;
+    const int kb = split_range(p, K);
+    const float *__restrict__ A = static_cast<const float *>(p.A) + kb;
+    const float *__restrict__ B = static_cast<const float *>(p.B) + (int64_t)kb * p.ldb;
+    const int M = p.M, N = p.N;
+
+    // A copy j of this wave: rows (wave*COPIES_A + j)*16 + lane/4; every
+    // wave's rows start at a multiple of 16, so the chunk is j-independent.
+    const int a_row = wave * COPIES_A * 16 + (lane >> 2);
+    const int a_ch = (lane & 3) ^ ((lane >> 4) & 3);
+    const float *a_src = A + (int64_t)(m0 + a_row) * p.lda + a_ch * 4;
+    // B copy j of this wave: k-rows (wave*COPIES_B + j)*RB + lane/CPB; the
+    // lane fills physical chunk lane%CPB of its row, which holds logical chunk
+    // (lane%CPB) ^ (8 if k%16 >= 8).
+    const int b_r = lane / CPB, b_pc = lane % CPB;
+    const float *b_src[COPIES_B];
+    bool b_ok[COPIES_B];
+#pragma unroll
+    for (int j = 0; j < COPIES_B; ++j) {
+        const int kr = (wave * COPIES_B + j) * RB + b_r;
+        const int col = n0 + (b_pc ^ (kr & 8)) * 4;
+        b_src[j] = B + (int64_t)kr * p.ldb + col;
+        b_ok[j] = col < N;
+    }
+    const uint32_t as_base = lds_addr(&As[0][0]), bs_base = lds_addr(&Bs[0][0]);
+
+    auto copy = [&](int buf, int k0, int c) {
+        const float *src;
+        uint32_t dst;
+        if (c < COPIES_A) {
+            dst = as_base + buf * (A_STAGE * 4) + (wave * COPIES_A + c) * 1024;
+            const bool ok = m0 + a_row + c * 16 < M && k0 + a_ch * 4 < K;
+            src = ok ? a_src + (int64_t)(c * 16) * p.lda + k0 : zero_chunk<float>();
+        } else {
+            const int j = c - COPIES_A;
+            dst = bs_base + buf * (B_STAGE * 4) + (wave * COPIES_B + j) * 1024;
+            const bool ok = k0 + (wave * COPIES_B + j) * RB + b_r < K && b_ok[j];
+            src = ok ? b_src[j] + (int64_t)k0 * p.ldb : zero_chunk<float>();
+        }
+        lds_dma_16(src, dst);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[i][j][r] = 0.0f;
+
+    const int h = lane >> 5, l32 = lane & 31;
+    // A operands of a stage: the lane's row, k = 8h .. 8h+7 (chunks 2h, 2h+1).
+    auto read_a = [&](int buf, f32x4 (&af)[FM][2]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int row = wm * WTM + fm * 32 + l32;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int c = (2 * h + q) ^ ((row >> 2) & 3);
+                af[fm][q] = *reinterpret_cast<const f32x4 *>(&As[buf][row * BK + c * 4]);
+            }
+        }
+    };
+    // B operands of step s: k = 8h + s, the lane's column of each block.
+    auto read_b = [&](int buf, int s, float (&bf)[FN]) {
+        const int k = 8 * h + s;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int n = wn * WTN + fn * 32 + l32;
+            bf[fn] = Bs[buf][k * BN + (((n >> 2) ^ (8 * h)) << 2) + (n & 3)];
+        }
+    };
+    auto mfma_step = [&](const f32x4 (&af)[FM][2], int s, const float (&bf)[FN]) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[fm][s >> 2][s & 3], bf[fn],
+                                                                   acc[fm][fn], 0, 0, 0);
+    };
+    auto wait_stages = [&](int n) {
+        if (n >= 3)
+            __builtin_amdgcn_s_waitcnt(LL_VMCNT(3 * PER_STAGE > 63 ? 63 : 3 * PER_STAGE));
+        else if (n == 2)
+            __builtin_amdgcn_s_waitcnt(LL_VMCNT(2 * PER_STAGE > 63 ? 63 : 2 * PER_STAGE));
+        else if (n == 1)
+            __builtin_amdgcn_s_waitcnt(LL_VMCNT(PER_STAGE));
+        else
+            __builtin_amdgcn_s_waitcnt(LL_VMCNT(0));
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    for (int st = 0; st < NBUF; ++st)
+        if (st < nk) {
+#pragma unroll
+            for (int c = 0; c < PER_STAGE; ++c)
+                copy(st, st * BK, c);
+        }
+    wait_stages((nk < NBUF ? nk : NBUF) - 1);   // stage 0 has landed
+    __syncthreads();
+
+    f32x4 af[FM][2], an[FM][2];   // this stage's and the next stage's A operands
+    float bf[2][FN];
+    read_a(0, af);
+    read_b(0, 0, bf[0]);
+    int buf = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
+#pragma unroll
+        for (int s = 0; s + 1 < KH; ++s) {
+            read_b(buf, s + 1, bf[(s + 1) & 1]);
+            mfma_step(af, s, bf[s & 1]);
+        }
+        if (kt + 1 < nk) {
+            // stage kt+1 has landed (stages up to kt+NBUF-1 were issued); after
+            // the barrier every wave is done with this stage's buffer
+            wait_stages((kt + NBUF - 1 < nk ? kt + NBUF - 1 : nk - 1) - (kt + 1));
+            __syncthreads();
+        }
+        const int k_next = (kt + NBUF) * BK;   // refill this buffer with stage kt+NBUF
+        const bool refill = kt + NBUF < nk;
+        // Operands of stage kt+1 (after the last stage: stale, in-bounds, unused).
+        read_a(nbuf, an);
+        read_b(nbuf, 0, bf[0]);
+        constexpr int G = (PER_STAGE + FM - 1) / FM;   // refill copies per MFMA row
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[fm][1][3], bf[1][fn],
+                                                                   acc[fm][fn], 0, 0, 0);
+            if (refill && fm * G < PER_STAGE) {
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    if (fm * G + g < PER_STAGE)
+                        copy(buf, k_next, fm * G + g);
+            }
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            af[fm][0] = an[fm][0];
+            af[fm][1] = an[fm][1];
+        }
+        buf = nbuf;
+    }
+
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            write_block<EPI>(p, acc[fm][fn], m0 + wm * WTM + fm * 32, n0 + wn * WTN + fn * 32, lane);
+}
+
 // Tile configurations. The 256x256 tile runs one wave per SIMD (256
 // accumulators per lane); the others are compiled for two waves per SIMD, so
 // two workgroups share a CU and each covers the other's barrier and memory
-// waits. Measured on the 4096^3 product, 256x128 at two workgroups per CU is
-// the fastest (about 83 % of the FP32 matrix peak), and it also quantises
-// best on the 2047 x 11008 fully-connected layer.
+// waits. With the direct-to-LDS kernel, 256x256 (one tile per CU) is the
+// fastest on the 4096^3 product (about 87 % of the FP32 matrix peak) and
+// 256x128 at two workgroups per CU quantises best on the 2047 x 11008
+// fully-connected layer.
 using F32_L = F32Tile<256, 256, 16>;   // 128x128 per wave
 using F32_M = F32Tile<256, 128, 16>;   // 128x64 per wave
 using F32_S = F32Tile<128, 128, 16>;   // 64x64 per wave
 using F32_XS = F32Tile<64, 64, 16>;    // 32x32 per wave
+// Ring lengths of the direct kernel: 256x256 (one workgroup per CU) and
+// 256x128 (two per CU, at most 80 KiB of LDS each). Longer rings measured no
+// faster (within 1 %).
+constexpr int kDirectNbufL = 3, kDirectNbufM = 2;
+
+template <int BM, int BN, int NBUF, int WPE>
+static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hipStream_t s)
+{
+    const dim3 grid = gemm_grid(p, ntiles), block(256);
+#define LL_F32_DIRECT(E) \
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, NBUF, WPE>), grid, block, 0, s, p)
+    if (epi == EPI_GEMM_BETA0) LL_F32_DIRECT(EPI_GEMM_BETA0);
+    else if (epi == EPI_GEMM_BETA) LL_F32_DIRECT(EPI_GEMM_BETA);
+    else if (epi == EPI_LINEAR) LL_F32_DIRECT(EPI_LINEAR);
+    else LL_F32_DIRECT(EPI_ATOMIC);
+#undef LL_F32_DIRECT
+    return hipGetLastError();
+}
 
 template <class T, int WPE, bool BT>
 static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t s)
@@ -287,6 +506,12 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
         return hipErrorInvalidValue;
+    // 128-bit-aligned operands with B given K-by-N take the direct-to-LDS
+    // kernel on the two large tiles.
+    if (vec && !BT && T::BM == 256 && T::BN == 256)
+        return launch_direct<256, 256, kDirectNbufL, 1>(p, ntiles, epi, s);
+    if (vec && !BT && T::BM == 256 && T::BN == 128)
+        return launch_direct<256, 128, kDirectNbufM, 2>(p, ntiles, epi, s);
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F32_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE, BT>), grid, block, 0, s, p)
@@ -310,7 +535,7 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // the 256x256 tile.
 const TileInfo kF32Tiles[kF32NumTiles] = {
     {F32_L::BM, F32_L::BN, 1, 1.00f, 1.00f, "f32_256x256x16"},
-    {F32_M::BM, F32_M::BN, 2, 0.89f, 1.01f, "f32_256x128x16"},
+    {F32_M::BM, F32_M::BN, 2, 0.89f, 0.985f, "f32_256x128x16"},
     {F32_S::BM, F32_S::BN, 2, 0.80f, 0.94f, "f32_128x128x16"},
     {F32_XS::BM, F32_XS::BN, 2, 0.40f, 0.72f, "f32_64x64x16"},
 };

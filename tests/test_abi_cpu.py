@@ -176,9 +176,8 @@ def test_tile_choice():
         names = names32 if dt == f32 else names16
         return names[ll.chosen_tile(dt, M, N, K, cus)], ll.chosen_split_k(dt, M, N, K, cus)
 
-    # 4096^2 on 256 CUs: two 256x128 tiles per CU, paired (one workgroup covers
-    # the other's waits); no K-split
-    assert choice(f32, 4096, 4096, 4096) == ("f32_256x128x16", 1)
+    # 4096^2 on 256 CUs: exactly one 256x256 tile per CU; no K-split
+    assert choice(f32, 4096, 4096, 4096) == ("f32_256x256x16", 1)
     # 2047 x 11008: 256x256 tiles leave a partial second round; 256x128 fills better
     assert choice(f32, 2047, 11008, 4096) == ("f32_256x128x16", 1)
     assert choice(f16, 8192, 8192, 8192) == ("f16_256x256_direct", 1)
@@ -201,7 +200,7 @@ def test_tile_choice():
         assert ll.chosen_split_k(f32, 64, 64, 100, 256) == 2   # 100 = 64 + 36
     finally:
         ll.set_split_k(-1)
-    assert ll.chosen_tile(f32, 4096, 4096, 4096, 256) == 1
+    assert ll.chosen_tile(f32, 4096, 4096, 4096, 256) == 0
     # a batch counts all its items' tiles: 256 items of 256^3 fill the CUs
     # without splitting K, one item alone splits it
     assert ll.chosen_split_k(f32, 256, 256, 256, 256, batch=256) == 1
