@@ -267,7 +267,7 @@ gemm_f32_kernel(GemmParams p)
                              n0 + wn * T::WTN + fn * 32, lane);
 }
 
-// Direct-to-LDS FP32 kernel for B given K-by-N and 128-bit-aligned operands.
+// Direct-to-LDS FP32 kernel for 128-bit-aligned operands.
 //
 // The same arithmetic as gemm_f32_kernel (k = 8h + s at MFMA step s, A read
 // as eight k-values per lane per stage), but both operands travel global ->
@@ -278,18 +278,19 @@ gemm_f32_kernel(GemmParams p)
 //      one logical chunk) hit 16 different 16-byte bank groups. One copy
 //      (KiB) = 16 rows; lane l fills row l/4, slot l%4 and fetches the logical
 //      chunk that the swizzle puts there.
-//   B: 16 k-rows x BN floats, unpadded; 16-byte chunks of rows 8..15 XOR 8,
-//      so the two half-waves (rows s and 8+s of a step, 128 bytes each) fall
-//      in different halves of the 256-byte bank line. One copy = 1024/(4*BN)
-//      rows.
+//   B given K-by-N: 16 k-rows x BN floats, unpadded; 16-byte chunks of rows
+//      8..15 XOR 8, so the two half-waves (rows s and 8+s of a step, 128
+//      bytes each) fall in different halves of the 256-byte bank line. One
+//      copy = 1024/(4*BN) rows; each lane reads one float per MFMA step.
+//   B given N-by-K (BT): BN rows x 64 bytes, copied and read exactly like A.
 // A stage holds eight k-steps. Its barrier sits before the last step, when
 // the wave holds that step's operands in registers: the barrier publishes
 // stage kt+1 and frees stage kt's buffer, which is refilled with stage
 // kt+NBUF while the last step's MFMAs run (a few copies after each row of
-// MFMAs), and the next stage's A operands and first B operands are read then
-// too. Every copy is one global_load_lds on every lane (lanes outside A or B
+// MFMAs), and the next stage's row-panel operands and first per-step B
+// operands are read then too. Every copy is one global_load_lds on every lane (lanes outside A or B
 // read the zero chunk), so the vmcnt waits count exactly.
-template <int EPI, int BM, int BN, int NBUF, int WPE>
+template <int EPI, int BM, int BN, int NBUF, int WPE, bool BT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f32_direct_kernel(GemmParams p)
 {
@@ -299,9 +300,9 @@ gemm_f32_direct_kernel(GemmParams p)
     constexpr int COPIES_A = BM / 16 / 4;                     // per wave per stage
     constexpr int CPB = BN / 4;                               // 16-byte chunks per B row
     constexpr int RB = 64 / CPB;                              // B rows per copy
-    constexpr int COPIES_B = BK / RB / 4;
+    constexpr int COPIES_B = BT ? BN / 16 / 4 : BK / RB / 4;
     constexpr int PER_STAGE = COPIES_A + COPIES_B;
-    static_assert(COPIES_A >= 1 && COPIES_B >= 1 && RB >= 1 && CPB >= 16, "tile shape");
+    static_assert(COPIES_A >= 1 && COPIES_B >= 1 && RB >= 1 && (BT || CPB >= 16), "tile shape");
     static_assert((NBUF - 1) * PER_STAGE <= 63 && NBUF >= 2 && NBUF <= 4, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) float As[NBUF][A_STAGE];
     __shared__ __attribute__((aligned(1024))) float Bs[NBUF][B_STAGE];
@@ -316,7 +317,8 @@ gemm_f32_direct_kernel(GemmParams p)
     int K;
     const int kb = split_range(p, K);
     const float *__restrict__ A = static_cast<const float *>(p.A) + kb;
-    const float *__restrict__ B = static_cast<const float *>(p.B) + (int64_t)kb * p.ldb;
+    const float *__restrict__ B =
+        static_cast<const float *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
     const int M = p.M, N = p.N;
 
     // A copy j of this wave: rows (wave*COPIES_A + j)*16 + lane/4; every
@@ -324,14 +326,17 @@ gemm_f32_direct_kernel(GemmParams p)
     const int a_row = wave * COPIES_A * 16 + (lane >> 2);
     const int a_ch = (lane & 3) ^ ((lane >> 4) & 3);
     const float *a_src = A + (int64_t)(m0 + a_row) * p.lda + a_ch * 4;
+    const int bt_row = wave * COPIES_B * 16 + (lane >> 2);   // BT: B's rows, like A's
+    const float *bt_src = B + (int64_t)(n0 + bt_row) * p.ldb + a_ch * 4;
     // B copy j of this wave: k-rows (wave*COPIES_B + j)*RB + lane/CPB; the
     // lane fills physical chunk lane%CPB of its row, which holds logical chunk
     // (lane%CPB) ^ (8 if k%16 >= 8).
     const int b_r = lane / CPB, b_pc = lane % CPB;
-    const float *b_src[COPIES_B];
-    bool b_ok[COPIES_B];
+    constexpr int NB_SRC = BT ? 1 : COPIES_B;
+    const float *b_src[NB_SRC];
+    bool b_ok[NB_SRC];
 #pragma unroll
-    for (int j = 0; j < COPIES_B; ++j) {
+    for (int j = 0; j < NB_SRC; ++j) {
         const int kr = (wave * COPIES_B + j) * RB + b_r;
         const int col = n0 + (b_pc ^ (kr & 8)) * 4;
         b_src[j] = B + (int64_t)kr * p.ldb + col;
@@ -346,6 +351,11 @@ gemm_f32_direct_kernel(GemmParams p)
             dst = as_base + buf * (A_STAGE * 4) + (wave * COPIES_A + c) * 1024;
             const bool ok = m0 + a_row + c * 16 < M && k0 + a_ch * 4 < K;
             src = ok ? a_src + (int64_t)(c * 16) * p.lda + k0 : zero_chunk<float>();
+        } else if (BT) {
+            const int j = c - COPIES_A;
+            dst = bs_base + buf * (B_STAGE * 4) + (wave * COPIES_B + j) * 1024;
+            const bool ok = n0 + bt_row + j * 16 < N && k0 + a_ch * 4 < K;
+            src = ok ? bt_src + (int64_t)(j * 16) * p.ldb + k0 : zero_chunk<float>();
         } else {
             const int j = c - COPIES_A;
             dst = bs_base + buf * (B_STAGE * 4) + (wave * COPIES_B + j) * 1024;
@@ -365,18 +375,22 @@ gemm_f32_direct_kernel(GemmParams p)
                 acc[i][j][r] = 0.0f;
 
     const int h = lane >> 5, l32 = lane & 31;
-    // A operands of a stage: the lane's row, k = 8h .. 8h+7 (chunks 2h, 2h+1).
-    auto read_a = [&](int buf, f32x4 (&af)[FM][2]) {
+    // Row-panel operands of a stage (A, and B given N-by-K): the lane's row,
+    // k = 8h .. 8h+7 (chunks 2h, 2h+1).
+    auto read_rows = [&](const float *lds, int row0, auto &frag) {
+        constexpr int F = sizeof(frag) / sizeof(frag[0]);
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-            const int row = wm * WTM + fm * 32 + l32;
+        for (int f = 0; f < F; ++f) {
+            const int row = row0 + f * 32 + l32;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int c = (2 * h + q) ^ ((row >> 2) & 3);
-                af[fm][q] = *reinterpret_cast<const f32x4 *>(&As[buf][row * BK + c * 4]);
+                frag[f][q] = *reinterpret_cast<const f32x4 *>(&lds[row * BK + c * 4]);
             }
         }
     };
+    auto read_a = [&](int buf, f32x4 (&af)[FM][2]) { read_rows(As[buf], wm * WTM, af); };
+    auto read_bt = [&](int buf, auto &bt) { read_rows(Bs[buf], wn * WTN, bt); };
     // B operands of step s: k = 8h + s, the lane's column of each block.
     auto read_b = [&](int buf, int s, float (&bf)[FN]) {
         const int k = 8 * h + s;
@@ -386,13 +400,18 @@ gemm_f32_direct_kernel(GemmParams p)
             bf[fn] = Bs[buf][k * BN + (((n >> 2) ^ (8 * h)) << 2) + (n & 3)];
         }
     };
-    auto mfma_step = [&](const f32x4 (&af)[FM][2], int s, const float (&bf)[FN]) {
+    // B operand of block column fn at step s: from the per-step reads (B
+    // given K-by-N) or from the stage's row-panel operands (BT).
+    constexpr int FT = BT ? FN : 1;   // row-panel B operands kept per stage
+    auto mfma_step = [&](const f32x4 (&af)[FM][2], int s, const float (&bf)[FN],
+                         const f32x4 (&bt)[FT][2]) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[fm][s >> 2][s & 3], bf[fn],
-                                                                   acc[fm][fn], 0, 0, 0);
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                    af[fm][s >> 2][s & 3], BT ? bt[BT ? fn : 0][s >> 2][s & 3] : bf[fn], acc[fm][fn],
+                    0, 0, 0);
     };
     auto wait_stages = [&](int n) {
         if (n >= 3)
@@ -416,16 +435,21 @@ gemm_f32_direct_kernel(GemmParams p)
     __syncthreads();
 
     f32x4 af[FM][2], an[FM][2];   // this stage's and the next stage's A operands
-    float bf[2][FN];
+    f32x4 bt[FT][2], btn[FT][2];  // the same for B given N-by-K
+    float bf[2][FN];              // B given K-by-N: two steps' operands
     read_a(0, af);
-    read_b(0, 0, bf[0]);
+    if constexpr (BT)
+        read_bt(0, bt);
+    else
+        read_b(0, 0, bf[0]);
     int buf = 0;
     for (int kt = 0; kt < nk; ++kt) {
         const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
 #pragma unroll
         for (int s = 0; s + 1 < KH; ++s) {
-            read_b(buf, s + 1, bf[(s + 1) & 1]);
-            mfma_step(af, s, bf[s & 1]);
+            if constexpr (!BT)
+                read_b(buf, s + 1, bf[(s + 1) & 1]);
+            mfma_step(af, s, bf[s & 1], bt);
         }
         if (kt + 1 < nk) {
             // stage kt+1 has landed (stages up to kt+NBUF-1 were issued); after
@@ -437,14 +461,17 @@ gemm_f32_direct_kernel(GemmParams p)
         const bool refill = kt + NBUF < nk;
         // Operands of stage kt+1 (after the last stage: stale, in-bounds, unused).
         read_a(nbuf, an);
-        read_b(nbuf, 0, bf[0]);
+        if constexpr (BT)
+            read_bt(nbuf, btn);
+        else
+            read_b(nbuf, 0, bf[0]);
         constexpr int G = (PER_STAGE + FM - 1) / FM;   // refill copies per MFMA row
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[fm][1][3], bf[1][fn],
-                                                                   acc[fm][fn], 0, 0, 0);
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                    af[fm][1][3], BT ? bt[BT ? fn : 0][1][3] : bf[1][fn], acc[fm][fn], 0, 0, 0);
             if (refill && fm * G < PER_STAGE) {
 #pragma unroll
                 for (int g = 0; g < G; ++g)
@@ -456,6 +483,13 @@ gemm_f32_direct_kernel(GemmParams p)
         for (int fm = 0; fm < FM; ++fm) {
             af[fm][0] = an[fm][0];
             af[fm][1] = an[fm][1];
+        }
+        if constexpr (BT) {
+#pragma unroll
+            for (int fn = 0; fn < FT; ++fn) {
+                bt[fn][0] = btn[fn][0];
+                bt[fn][1] = btn[fn][1];
+            }
         }
         buf = nbuf;
     }
@@ -483,12 +517,12 @@ using F32_XS = F32Tile<64, 64, 16>;    // 32x32 per wave
 // faster (within 1 %).
 constexpr int kDirectNbufL = 3, kDirectNbufM = 2;
 
-template <int BM, int BN, int NBUF, int WPE>
+template <int BM, int BN, int NBUF, int WPE, bool BT>
 static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hipStream_t s)
 {
     const dim3 grid = gemm_grid(p, ntiles), block(256);
 #define LL_F32_DIRECT(E) \
-    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, NBUF, WPE>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, NBUF, WPE, BT>), grid, block, 0, s, p)
     if (epi == EPI_GEMM_BETA0) LL_F32_DIRECT(EPI_GEMM_BETA0);
     else if (epi == EPI_GEMM_BETA) LL_F32_DIRECT(EPI_GEMM_BETA);
     else if (epi == EPI_LINEAR) LL_F32_DIRECT(EPI_LINEAR);
@@ -506,12 +540,12 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
         return hipErrorInvalidValue;
-    // 128-bit-aligned operands with B given K-by-N take the direct-to-LDS
-    // kernel on the two large tiles.
-    if (vec && !BT && T::BM == 256 && T::BN == 256)
-        return launch_direct<256, 256, kDirectNbufL, 1>(p, ntiles, epi, s);
-    if (vec && !BT && T::BM == 256 && T::BN == 128)
-        return launch_direct<256, 128, kDirectNbufM, 2>(p, ntiles, epi, s);
+    // 128-bit-aligned operands take the direct-to-LDS kernel on the two large
+    // tiles.
+    if (vec && T::BM == 256 && T::BN == 256)
+        return launch_direct<256, 256, kDirectNbufL, 1, BT>(p, ntiles, epi, s);
+    if (vec && T::BM == 256 && T::BN == 128)
+        return launch_direct<256, 128, kDirectNbufM, 2, BT>(p, ntiles, epi, s);
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F32_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE, BT>), grid, block, 0, s, p)
