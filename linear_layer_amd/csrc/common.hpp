@@ -88,16 +88,19 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int &tm, int &t
     tn = within / rows;
 }
 
-// XOR swizzle of 16-byte chunks inside an LDS row of ROW_BYTES bytes, so that
-// eight lanes reading the same logical chunk of eight consecutive rows hit
-// all 32 banks. RPL = rows per 128-byte bank line; the chunk index is XORed
-// with the row's line number (mod the chunks per row, at most 8).
+// XOR swizzle of 16-byte chunks inside an LDS row of ROW_BYTES bytes. The
+// LDS has 64 banks of 4 bytes and serves a 128-bit read 16 lanes per cycle,
+// so 16 lanes reading the same logical chunk of 16 consecutive rows must hit
+// 16 different 16-byte bank groups of the 256-byte bank line: RPL rows share
+// a line, and the chunk index is XORed with the row's line number (mod the
+// chunks per row, at most 16). (Measured with the bank-conflict counter: for
+// 64-byte rows, XOR by (row/4)%4 is conflict-free, by (row/2)%4 two-way.)
 template <int ROW_BYTES>
 __device__ __forceinline__ int swz(int row)
 {
     constexpr int CPR = ROW_BYTES / 16;
-    constexpr int RPL = ROW_BYTES >= 128 ? 1 : 128 / ROW_BYTES;
-    constexpr int MASK = (CPR < 8 ? CPR : 8) - 1;
+    constexpr int RPL = ROW_BYTES >= 256 ? 1 : 256 / ROW_BYTES;
+    constexpr int MASK = (CPR < 16 ? CPR : 16) - 1;
     return (row / RPL) & MASK;
 }
 

@@ -16,8 +16,8 @@
 //     thread loads an 8x8 block of B (eight 128-bit row loads), transposes it
 //     in registers with 16-bit packs, and stores eight 128-bit [n][k] rows.
 //   * Rows of both LDS tiles are 128 bytes; 16-byte chunks are XOR-swizzled
-//     with the row index, so eight lanes reading the same logical chunk of
-//     eight rows (or writing eight k-chunks of one row) cover all 32 banks.
+//     by (row/2)%8, so 16 lanes reading the same logical chunk of 16 rows hit
+//     16 different 16-byte groups of the 64 banks.
 //   * Two LDS stages, register-staged prefetch of the next stage during the
 //     MFMAs of the current one, one barrier per stage. Zero-filled loads
 //     outside M, N, K; masked, fused write-back.

@@ -17,8 +17,8 @@
 //     stage (the ping-pong of page "GPU架构下的矩阵乘法深入优化", section 5).
 //   * A stays row-major in LDS ([m][k]) with an XOR swizzle of its 16-byte
 //     chunks, so a lane fetches its BK/2 k-values of one row with 128-bit LDS
-//     reads and eight lanes of consecutive rows cover all banks (the pages pad
-//     or transpose instead). B stays [k][n]; its rows are padded by 4 floats
+//     reads and 16 lanes of consecutive rows hit 16 different 16-byte groups
+//     of the 64 banks (the pages pad or transpose instead). B stays [k][n]; its rows are padded by 4 floats
 //     so that the two half-waves, which read rows BK/2 apart, land on
 //     different banks.
 //   * Inside a stage, lane half h (lanes 32h..32h+31) handles k = h*BK/2 + s
