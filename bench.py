@@ -8,8 +8,9 @@ workloads in linear_layer_amd/workloads.py for ad-hoc measurement.
 
 Prints ONE JSON line with the metric (TFLOPS = 2*M*N*K*batch / time per step),
 a ``roofline`` object for the GEMM kernel (achieved = algorithmic FLOPs per
-launch / average launch duration from HIP events on the launch stream, peak =
-MI355X's published dense matrix peak for the dtype) and a ``cpu_baseline``
+launch / average launch duration, from a second pass of K steps each between
+its own pair of HIP events on the launch stream; peak = MI355X's published
+dense matrix peak for the dtype) and a ``cpu_baseline``
 object: the float64 CPU oracle timed on a bounded sample of the same workload
 (a block of whole output rows, or of whole batch items) on this host's cores.
 """
@@ -228,20 +229,27 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)  # the stream the library launches on
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # Timed region: K steps back to back, bracketed by events on the launch
+    # stream and a device synchronisation on both sides.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for e0, e1 in ev:
-        e0.record(stream)
+    for _ in range(args.steps):
         step()
-        e1.record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    # Per-launch durations for the roofline: a second pass of K steps, each
+    # bracketed by its own pair of events on the same stream.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
     flops = float(w.flops)
