@@ -513,9 +513,12 @@ using F32_M = F32Tile<256, 128, 16>;   // 128x64 per wave
 using F32_S = F32Tile<128, 128, 16>;   // 64x64 per wave
 using F32_XS = F32Tile<64, 64, 16>;    // 32x32 per wave
 // Ring lengths of the direct kernel: 256x256 (one workgroup per CU) and
-// 256x128 (two per CU, at most 80 KiB of LDS each). Longer rings measured no
-// faster (within 1 %).
-constexpr int kDirectNbufL = 3, kDirectNbufM = 2;
+// 256x128 (two per CU, at most 80 KiB of LDS each) measured no faster with
+// longer rings (within 1 %). The 128x128 and 64x64 tiles serve problems too
+// small to fill the CUs, whose stages are latency-bound: four stages in
+// flight (64 and 32 KiB), the 64x64 tile at four waves per SIMD (2048^3:
+// 108-110 vs 94-103 TFLOP/s with the staged kernel).
+constexpr int kDirectNbufL = 3, kDirectNbufM = 2, kDirectNbufS = 4;
 
 template <int BM, int BN, int NBUF, int WPE, bool BT>
 static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hipStream_t s)
@@ -540,12 +543,15 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
         return hipErrorInvalidValue;
-    // 128-bit-aligned operands take the direct-to-LDS kernel on the two large
-    // tiles.
+    // 128-bit-aligned operands take the direct-to-LDS kernel.
     if (vec && T::BM == 256 && T::BN == 256)
         return launch_direct<256, 256, kDirectNbufL, 1, BT>(p, ntiles, epi, s);
     if (vec && T::BM == 256 && T::BN == 128)
         return launch_direct<256, 128, kDirectNbufM, 2, BT>(p, ntiles, epi, s);
+    if (vec && T::BM == 128 && T::BN == 128)
+        return launch_direct<128, 128, kDirectNbufS, 2, BT>(p, ntiles, epi, s);
+    if (vec && T::BM == 64 && T::BN == 64)
+        return launch_direct<64, 64, kDirectNbufS, 4, BT>(p, ntiles, epi, s);
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F32_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE, BT>), grid, block, 0, s, p)
