@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--workload", default="gemm_f32_4096")
     ap.add_argument("--tile", type=int, default=-1, help="force a tile shape (-1: automatic)")
     ap.add_argument("--split-k", type=int, default=-1, help="force the K-split count (-1: automatic)")
+    ap.add_argument("--stream-k", type=int, default=-1,
+                    help="stream-K for leftover tiles: -1 automatic, 0 never, 1 whenever possible")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -204,9 +206,19 @@ def main():
         ll.set_tile(dtype_id, args.tile)
     if args.split_k >= 1:
         ll.set_split_k(args.split_k)
+    if args.stream_k != -1:
+        ll.set_stream_k(args.stream_k)
     props = torch.cuda.get_device_properties(dev)
-    tile = ll.chosen_tile(dtype_id, w.M, w.N, w.K, props.multi_processor_count, w.batch)
-    splits = ll.chosen_split_k(dtype_id, w.M, w.N, w.K, props.multi_processor_count, w.batch)
+    # the plan the step runs: the fused layer with ReLU pays for its extra
+    # pass; B given N-by-K is planned on its own
+    plan_id = dtype_id
+    if w.kind.startswith("linear") and w.act == 1:
+        plan_id |= ll.PLAN_RELU
+    if w.kind in wl.B_TRANSPOSED_KINDS:
+        plan_id |= ll.PLAN_B_NK
+    tile = ll.chosen_tile(plan_id, w.M, w.N, w.K, props.multi_processor_count, w.batch)
+    splits = ll.chosen_split_k(plan_id, w.M, w.N, w.K, props.multi_processor_count, w.batch)
+    sk_tiles = ll.chosen_stream_k(plan_id, w.M, w.N, w.K, props.multi_processor_count, w.batch)
 
     def step():
         if w.kind == "gemm_f32":
@@ -284,7 +296,7 @@ def main():
                if w.kind in ("linear", "linear_nt") else {}),
             **({"b_layout": "N-by-K"} if w.kind in wl.B_TRANSPOSED_KINDS else {}),
             **({"batch": w.batch} if batched else {}),
-            "tile": ll.tile_name(dtype_id, tile), "split_k": splits,
+            "tile": ll.tile_name(dtype_id, tile), "split_k": splits, "stream_k_tiles": sk_tiles,
             "device": props.name, "cus": props.multi_processor_count,
         },
         "pct_of_peak": round(100.0 * value / peak, 2),

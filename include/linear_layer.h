@@ -212,10 +212,16 @@ const char *ll_status_string(int status);
  */
 #define LL_DTYPE_F32 0 /* gemm_f32, linear_bias_act and their _nt forms */
 #define LL_DTYPE_F16 1 /* gemm_f16f32, gemm_bf16f32 and their _nt forms */
+/* Flags the ll_chosen_* queries accept OR-ed into `dtype`:
+ * LL_PLAN_RELU: linear_bias_act with the ReLU, whose K-split and stream-K
+ * plans pay for one more pass over Y (LL_DTYPE_F32 only);
+ * LL_PLAN_B_NK: the _nt form (B given N-by-K). */
+#define LL_PLAN_RELU 0x100
+#define LL_PLAN_B_NK 0x200
 
 /* Number of tile shapes for a data type (0 for an unknown dtype). */
 int ll_num_tiles(int dtype);
-/* Name of a tile shape, e.g. "f32_256x256x16" ("" if out of range). Static string. */
+/* Name of a tile shape, e.g. "f32_256x256" ("" if out of range). Static string. */
 const char *ll_tile_name(int dtype, int tile);
 /* Force tile `tile` for every later call of that dtype in this process;
  * -1 restores the automatic choice. Process-wide, thread-safe.
@@ -228,9 +234,29 @@ int ll_set_split_k(int splits);
 /* The tile / the number of K-splits the library would use for `batch`
  * M-by-N outputs (batch 1: a single product) with inner dimension K on a
  * device with num_cus compute units (num_cus <= 0: 256), honouring the
- * overrides. -1 for an unknown dtype or batch < 1. */
+ * overrides and the LL_PLAN_* flags in dtype. -1 for an unknown dtype or
+ * flag, or batch < 1. */
 int ll_chosen_tile(int dtype, int M, int N, int K, int batch, int num_cus);
 int ll_chosen_split_k(int dtype, int M, int N, int K, int batch, int num_cus);
+
+/*
+ * Stream-K (FP32 products with 128-bit-aligned operands, single products):
+ * when the output tiles do not fill a whole number of rounds of the CUs, the
+ * planner may run the full rounds tile by tile and share the leftover tiles'
+ * K range out evenly over one round of workgroups, whose partial sums are
+ * added atomically into C (prepared with beta*C, or the bias, beforehand;
+ * the ReLU applied afterwards). Like a K-split, this makes the summation
+ * order of those tiles run-dependent (still within the error bound; integer
+ * inputs stay exact); it allocates nothing.
+ *   ll_set_stream_k: -1 automatic (default; never for the _nt forms, where
+ *   it measured slower), 0 never, 1 whenever the shape allows it (a forced
+ *   K-split takes precedence). Returns LL_OK or LL_ERR_INVALID_VALUE.
+ *   ll_chosen_stream_k: the number of tiles the plan shares out (0: none),
+ *   assuming 128-bit-aligned operands; dtype and flags as for
+ *   ll_chosen_tile; -1 for an unknown dtype or flag, or batch < 1.
+ */
+int ll_set_stream_k(int mode);
+int ll_chosen_stream_k(int dtype, int M, int N, int K, int batch, int num_cus);
 
 #ifdef __cplusplus
 }

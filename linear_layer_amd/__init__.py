@@ -33,14 +33,15 @@ __all__ = [
     "gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt", "linear_bias_act_nt",
     "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
     "library_path", "load", "set_tile", "num_tiles", "tile_name", "chosen_tile",
-    "set_split_k", "chosen_split_k",
-    "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16",
+    "set_split_k", "chosen_split_k", "set_stream_k", "chosen_stream_k",
+    "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16", "PLAN_RELU", "PLAN_B_NK",
     "OK", "ERR_INVALID_VALUE", "ERR_NO_DEVICE", "ERR_UNSUPPORTED_ARCH", "ERR_LAUNCH",
 ]
 
 OK, ERR_INVALID_VALUE, ERR_NO_DEVICE, ERR_UNSUPPORTED_ARCH, ERR_LAUNCH = 0, 1, 2, 3, 4
 ACT_NONE, ACT_RELU = 0, 1
 DTYPE_F32, DTYPE_F16 = 0, 1
+PLAN_RELU, PLAN_B_NK = 0x100, 0x200   # flags OR-ed into dtype for the chosen_* queries
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblinear_layer.so")
@@ -51,7 +52,7 @@ EXPORTED = ("gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "ll_st
             "gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt", "linear_bias_act_nt",
             "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
             "ll_num_tiles", "ll_tile_name", "ll_set_tile", "ll_chosen_tile",
-            "ll_set_split_k", "ll_chosen_split_k")
+            "ll_set_split_k", "ll_chosen_split_k", "ll_set_stream_k", "ll_chosen_stream_k")
 
 
 class LinearLayerError(RuntimeError):
@@ -102,6 +103,10 @@ def load():
     lib.ll_chosen_split_k.restype = i32
     lib.ll_set_split_k.argtypes = [i32]
     lib.ll_set_split_k.restype = i32
+    lib.ll_set_stream_k.argtypes = [i32]
+    lib.ll_set_stream_k.restype = i32
+    lib.ll_chosen_stream_k.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.ll_chosen_stream_k.restype = i32
     _lib = lib
     return lib
 
@@ -138,6 +143,16 @@ def set_split_k(splits: int) -> None:
 
 def chosen_split_k(dtype: int, M: int, N: int, K: int, num_cus: int = 0, batch: int = 1) -> int:
     return load().ll_chosen_split_k(int(dtype), int(M), int(N), int(K), int(batch), int(num_cus))
+
+
+def set_stream_k(mode: int) -> None:
+    """Stream-K for leftover tiles: -1 automatic, 0 never, 1 whenever possible."""
+    _check(load().ll_set_stream_k(int(mode)), "ll_set_stream_k")
+
+
+def chosen_stream_k(dtype: int, M: int, N: int, K: int, num_cus: int = 0, batch: int = 1) -> int:
+    """Number of tiles the plan shares out with stream-K (0: none)."""
+    return load().ll_chosen_stream_k(int(dtype), int(M), int(N), int(K), int(batch), int(num_cus))
 
 
 # ---- tensor marshalling ---------------------------------------------------

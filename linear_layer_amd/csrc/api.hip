@@ -167,7 +167,21 @@ struct Plan {
     int tile;
     int splits;
     int k_split;
+    int dp_tiles;   // stream-K hybrid: tiles run whole (data-parallel); the rest are shared out
+    int sk_grid;    // workgroups of the stream-K share; 0 when the plan has none
 };
+
+std::atomic<int> g_sk_override{-1};   // -1 automatic, 0 never, 1 whenever possible
+
+// Stream-K needs the direct kernels (128-bit-aligned operands). With B given
+// N-by-K the automatic choice leaves it out: measured on the 2047x11008x4096
+// layer, the shared-out phase runs at about three quarters of the whole-tile
+// rate there (the K-by-N form runs it at the full rate), so 256x128 tiles
+// without sharing are faster. Forcing it (mode 1) still applies it.
+bool sk_allowed(bool vec, bool b_trans)
+{
+    return vec && (!b_trans || g_sk_override.load(std::memory_order_relaxed) == 1);
+}
 
 // Choose the tile shape and the number of K-splits minimising the estimate:
 // big tiles for big problems; smaller ones, or several workgroups along K
@@ -177,14 +191,16 @@ struct Plan {
 // A split costs a pre-pass over C (beta*C, or the bias), the atomic traffic of
 // every split's partial tile and, for ReLU, a pass afterwards.
 Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int cus, bool relu,
-          int batch = 1)
+          int batch = 1, bool allow_sk = false)
 {
     const int items = batch < kMaxGridZ ? batch : kMaxGridZ;   // items per launch
     const int t_ov = g_tile_override[dtype].load(std::memory_order_relaxed);
     const int s_ov = g_split_override.load(std::memory_order_relaxed);
-    Plan best{0, 1, K};
-    double best_cost = 0.0;
-    bool have = false;
+    const int sk_ov = g_sk_override.load(std::memory_order_relaxed);
+    allow_sk = allow_sk && batch == 1 && s_ov < 1 && sk_ov != 0 && K > 0;
+    Plan best{0, 1, K, 0, 0}, best_sk{0, 1, K, 0, 0};
+    double best_cost = 0.0, best_sk_cost = 0.0;
+    bool have = false, have_sk = false;
     for (int t = 0; t < ntiles; ++t) {
         if (t_ov >= 0 && t != t_ov)
             continue;
@@ -210,12 +226,41 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
                 cost += ((relu ? 6.0 : 3.0) + bytes / 3.0e6) * kUnitsPerUs;
             }
             if (!have || cost < best_cost) {
-                best = Plan{t, splits, k_split};
+                best = Plan{t, splits, k_split, 0, 0};
                 best_cost = cost;
                 have = true;
             }
         }
+        // Stream-K hybrid: the full rounds of tiles run whole; the leftover
+        // tiles' k-units are shared out evenly over one round of workgroups,
+        // which add their partial sums atomically (framed by a pass that
+        // prepares those tiles and, for ReLU, one that finishes them).
+        if (allow_sk) {
+            const int64_t slots = (int64_t)cus * ti.wg_per_cu;
+            const int64_t rounds = tiles_mn / slots, rest = tiles_mn - rounds * slots;
+            const int64_t units = ((int64_t)K + kSkUnit - 1) / kSkUnit;
+            if (rest > 0 && units >= 2 && tiles_mn <= kMaxTiles) {
+                const int64_t grid = rest * units < slots ? rest * units : slots;
+                const int64_t per_wg = (rest * units + grid - 1) / grid;
+                const double work = (double)ti.bm * ti.bn * K;
+                double cost = rounds > 0 ? wg_cost(ti, rounds * slots, work, cus) : 0.0;
+                cost += wg_cost(ti, grid, work * (double)per_wg / (double)units, cus);
+                // atomics: one partial tile per segment (at most grid + rest of
+                // them); passes: the prepare write and, for ReLU, a read and write
+                const double area = 4.0 * ti.bm * ti.bn;
+                const double bytes = area * (double)(grid + rest) + area * rest * (relu ? 3 : 1);
+                cost += ((relu ? 6.0 : 3.0) + bytes / 3.0e6) * kUnitsPerUs;
+                if (!have_sk || cost < best_sk_cost) {
+                    best_sk = Plan{t, 1, K, (int)(rounds * slots), (int)grid};
+                    best_sk_cost = cost;
+                    have_sk = true;
+                }
+            }
+        }
     }
+    // stream-K forced: its best plan whenever the shape allows one
+    if (have_sk && (sk_ov == 1 || !have || best_sk_cost < best_cost))
+        best = best_sk;
     if (best.k_split <= 0)
         best.k_split = 1;
     return best;
@@ -264,10 +309,46 @@ hipError_t run_one(GemmParams p, const Plan &pl, bool vec, hipStream_t s, launch
     return launch(p, pl.tile, EPI_ATOMIC, vec, s);
 }
 
+// Tile grid of a plan's tile shape, for the per-tile passes.
+GemmParams with_tile_grid(GemmParams p, const TileInfo &ti)
+{
+    p.tiles_m = (p.M + ti.bm - 1) / ti.bm;
+    p.tiles_n = (p.N + ti.bn - 1) / ti.bn;
+    return p;
+}
+
+// A stream-K hybrid plan: prepare the shared-out tiles (pre_pass), then one
+// launch whose first dp_tiles workgroups run whole tiles with `epi` and whose
+// sk_grid others share out the rest (they start as whole tiles finish), then
+// (ReLU) finish the shared-out tiles.
+hipError_t run_stream_k(GemmParams p, const Plan &pl, const TileInfo &ti, int epi, int pre_pass,
+                        bool relu_after, bool vec, hipStream_t s, launch_fn launch)
+{
+    const GemmParams g = with_tile_grid(p, ti);
+    const int64_t tiles_mn = (int64_t)g.tiles_m * g.tiles_n;
+    const int rest = (int)(tiles_mn - pl.dp_tiles);
+    hipError_t e = hipSuccess;
+    if (pre_pass >= 0)
+        e = launch_tile_pass(g, ti.bm, ti.bn, pl.dp_tiles, rest, pre_pass, s);
+    if (e == hipSuccess) {
+        GemmParams q = p;
+        q.grid_x = pl.dp_tiles + pl.sk_grid;
+        q.sk_block = pl.dp_tiles;
+        q.sk_tiles = rest;
+        e = launch(q, pl.tile, epi, vec, s);
+    }
+    if (e == hipSuccess && relu_after)
+        e = launch_tile_pass(g, ti.bm, ti.bn, pl.dp_tiles, rest, TILE_RELU, s);
+    return e;
+}
+
 // A strided batch in launches of at most kMaxGridZ items (grid z).
 hipError_t run_gemm(GemmParams p, const Plan &pl, bool vec, hipStream_t s, launch_fn launch,
-                    int64_t elem_ab, const Batch &bt = kSingle)
+                    int64_t elem_ab, const Batch &bt = kSingle, const TileInfo *ti = nullptr)
 {
+    if (pl.sk_grid > 0)   // single products only (the planner offers it for batch 1)
+        return run_stream_k(p, pl, *ti, p.beta == 0.0f ? EPI_GEMM_BETA0 : EPI_GEMM_BETA,
+                            p.beta == 1.0f ? -1 : TILE_SCALE, false, vec, s, launch);
     p.stride_a = bt.sa * elem_ab;
     p.stride_b = bt.sb * elem_ab;
     p.stride_c = bt.sc * 4;
@@ -325,8 +406,10 @@ static int gemm_f32_impl(int M, int N, int K, float alpha, const float *A, int l
                      ldb % 4 == 0 && ldc % 4 == 0 && K % 4 == 0 && (bt || N % 4 == 0) &&
                      batch_aligned(bat, 4);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false, bat.count);
-    return launch_status(run_gemm(p, pl, vec, s, bt ? launch_gemm_f32_bt : launch_gemm_f32, 4, bat));
+    const Plan pl =
+        plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false, bat.count, sk_allowed(vec, bt));
+    return launch_status(run_gemm(p, pl, vec, s, bt ? launch_gemm_f32_bt : launch_gemm_f32, 4, bat,
+                                  &kF32Tiles[pl.tile]));
 }
 
 int gemm_f32(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
@@ -445,7 +528,11 @@ static int linear_impl(int M, int N, int K, const float *X, int ldx, const float
     p.bias = bias;
     p.act = act;
     const launch_fn launch = wt ? launch_gemm_f32_bt : launch_gemm_f32;
-    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU);
+    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU, 1,
+                         sk_allowed(vec, wt));
+    if (pl.sk_grid > 0)
+        return launch_status(run_stream_k(p, pl, kF32Tiles[pl.tile], EPI_LINEAR, TILE_BIAS,
+                                          act == LL_ACT_RELU, vec, s, launch));
     if (pl.splits == 1)
         return launch_status(launch(p, pl.tile, EPI_LINEAR, vec, s));
     // split-K: Y = bias, then every split adds its partial product, then ReLU
@@ -514,12 +601,15 @@ const char *ll_tile_name(int dtype, int tile)
 
 static Plan chosen_plan(int dtype, int M, int N, int K, int batch, int num_cus, bool *ok)
 {
-    *ok = (dtype == LL_DTYPE_F32 || dtype == LL_DTYPE_F16) && batch >= 1;
+    const int base = dtype & 0xff, flags = dtype & ~0xff;
+    const bool relu = flags & LL_PLAN_RELU, b_nk = flags & LL_PLAN_B_NK;
+    *ok = (base == LL_DTYPE_F32 || (base == LL_DTYPE_F16 && !relu)) &&
+          (flags & ~(LL_PLAN_RELU | LL_PLAN_B_NK)) == 0 && batch >= 1;
     if (!*ok)
         return Plan{-1, -1, 0};
     const int cus = num_cus > 0 ? num_cus : 256;
-    if (dtype == LL_DTYPE_F32)
-        return plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, false, batch);
+    if (base == LL_DTYPE_F32)
+        return plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, relu, batch, sk_allowed(true, b_nk));
     return plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch);
 }
 
@@ -535,6 +625,26 @@ int ll_chosen_split_k(int dtype, int M, int N, int K, int batch, int num_cus)
     bool ok;
     const Plan p = chosen_plan(dtype, M, N, K, batch, num_cus, &ok);
     return ok ? p.splits : -1;
+}
+
+int ll_chosen_stream_k(int dtype, int M, int N, int K, int batch, int num_cus)
+{
+    bool ok;
+    const Plan p = chosen_plan(dtype, M, N, K, batch, num_cus, &ok);
+    if (!ok)
+        return -1;
+    if (p.sk_grid == 0)
+        return 0;
+    const TileInfo &ti = kF32Tiles[p.tile];
+    return (int)((int64_t)((M + ti.bm - 1) / ti.bm) * ((N + ti.bn - 1) / ti.bn) - p.dp_tiles);
+}
+
+int ll_set_stream_k(int mode)
+{
+    if (mode < -1 || mode > 1)
+        return LL_ERR_INVALID_VALUE;
+    g_sk_override.store(mode, std::memory_order_relaxed);
+    return LL_OK;
 }
 
 int ll_set_split_k(int splits)

@@ -37,7 +37,14 @@ struct GemmParams {
     int k_split;          // K per split (a multiple of 64); K itself when not split
     int batch;            // batch items in this launch (grid z); 1 for a single product
     int64_t stride_a, stride_b, stride_c;  // byte distance between batch items (0: shared)
+    int tile_base;        // index (in the grouped order) of this launch's first tile
+    int grid_x;           // workgroups along x; 0: one per tile of the whole grid
+    int sk_tiles;         // stream-K: the number of tiles shared out; 0: none
+    int sk_block;         // stream-K: workgroups below this run whole tiles, the rest share
 };
+
+// K granularity of a stream-K share: a multiple of every kernel's stage depth.
+constexpr int kSkUnit = 64;
 
 // Strided batch: workgroups with blockIdx.z = i compute item i, whose A, B and
 // C start stride_{a,b,c}*i bytes after the first item's (page "GEMM 优化详解",
@@ -66,19 +73,23 @@ __device__ __forceinline__ int split_range(const GemmParams &p, int &k_len)
     return kb;
 }
 
-// Workgroup id -> (tile_m, tile_n).
+// Workgroup -> output tile.
 //
 // The dispatcher hands consecutive workgroup ids to the 8 XCDs in turn, and
-// each XCD has its own L2. The first step renumbers ids so that the ids one
-// XCD receives are consecutive; the second walks tiles in groups of group_m
+// each XCD has its own L2. block_index() renumbers the nwg ids so that the ids one
+// XCD receives are consecutive; tile_of() walks tiles in groups of group_m
 // tile rows, column by column, so that the tiles resident on one XCD at a
 // time form a compact block and share their A rows and B columns in that
 // XCD's L2.
-__device__ __forceinline__ void tile_coords(const GemmParams &p, int &tm, int &tn)
+__device__ __forceinline__ int block_index(int wg, int nwg)
 {
-    const int nwg = gridDim.x, wg = blockIdx.x;
     const int q = nwg >> 3, r = nwg & 7, x = wg & 7;
-    const int lid = x * q + (x < r ? x : r) + (wg >> 3);
+    return x * q + (x < r ? x : r) + (wg >> 3);
+}
+
+// Tile `lid` of the grouped order -> (tile_m, tile_n).
+__device__ __forceinline__ void tile_of(const GemmParams &p, int lid, int &tm, int &tn)
+{
     const int group = p.group_m * p.tiles_n;
     const int g = lid / group;
     const int first_m = g * p.group_m;
@@ -86,6 +97,41 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int &tm, int &t
     const int within = lid - g * group;
     tm = first_m + within % rows;
     tn = within / rows;
+}
+
+// The tile of this workgroup in a data-parallel launch (tiles tile_base ..),
+// or of a whole-tile workgroup (blockIdx.x < sk_block) of a stream-K launch.
+__device__ __forceinline__ void tile_coords(const GemmParams &p, int &tm, int &tn)
+{
+    const int nwg = p.sk_tiles > 0 ? p.sk_block : (int)gridDim.x;
+    tile_of(p, p.tile_base + block_index(blockIdx.x, nwg), tm, tn);
+}
+
+// Stream-K: the sk_tiles tiles after the whole ones (from tile_base + sk_block
+// on) are cut into units of kSkUnit k-values, and sharing workgroup w (of the
+// gridDim.x - sk_block from sk_block on) takes the w-th of equal contiguous
+// runs of those (tile, unit) pairs -- less than one tile's worth, so at most
+// two segments. Segment `seg` of this workgroup: returns false if there is
+// none, else its tile and k-range [kb, kb + k_len).
+__device__ __forceinline__ bool sk_segment(const GemmParams &p, int seg, int &tm, int &tn, int &kb,
+                                           int &k_len)
+{
+    const int units = (p.K + kSkUnit - 1) / kSkUnit;
+    const int64_t total = (int64_t)p.sk_tiles * units;
+    const int64_t w = (int64_t)blockIdx.x - p.sk_block, nw = (int64_t)gridDim.x - p.sk_block;
+    int64_t u0 = total * w / nw;
+    const int64_t u1 = total * (w + 1) / nw;
+    for (int s = 0; s < seg && u0 < u1; ++s)
+        u0 = (u0 / units + 1) * units;   // skip to the next tile's first unit
+    if (u0 >= u1)
+        return false;
+    const int t = (int)(u0 / units), lo = (int)(u0 % units);
+    const int64_t tile_end = (int64_t)(t + 1) * units;
+    const int hi = (int)((u1 < tile_end ? u1 : tile_end) - (int64_t)t * units);
+    tile_of(p, p.tile_base + p.sk_block + t, tm, tn);
+    kb = lo * kSkUnit;
+    k_len = min(p.K, hi * kSkUnit) - kb;
+    return true;
 }
 
 // XOR swizzle of 16-byte chunks inside an LDS row of ROW_BYTES bytes. The

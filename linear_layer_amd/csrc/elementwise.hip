@@ -49,6 +49,45 @@ __global__ void __launch_bounds__(256) relu_kernel(float *Y, int64_t ldy, int M,
     }
 }
 
+// The same three operations on whole output tiles: tiles tile_base ..
+// tile_base + count - 1 of p's grouped tile order (tiles of bm x bn). They
+// frame the stream-K share of a product, whose tiles receive atomic partial
+// sums: C = beta*C or Y = bias before, ReLU after. Each tile is swept by
+// kParts workgroups, rows interleaved.
+constexpr int kParts = 4;
+
+__global__ void __launch_bounds__(256) tile_pass_kernel(GemmParams p, int bm, int bn, int mode)
+{
+    const int t = blockIdx.x / kParts, part = blockIdx.x % kParts;
+    int tm, tn;
+    tile_of(p, p.tile_base + t, tm, tn);
+    const int m0 = tm * bm, n0 = tn * bn;
+    const int m1 = min(p.M, m0 + bm), n1 = min(p.N, n0 + bn);
+    for (int m = m0 + part; m < m1; m += kParts) {
+        float *row = p.C + (int64_t)m * p.ldc;
+        for (int n = n0 + (int)threadIdx.x; n < n1; n += blockDim.x) {
+            if (mode == TILE_SCALE)
+                row[n] = p.beta == 0.0f ? 0.0f : p.beta * row[n];
+            else if (mode == TILE_BIAS)
+                row[n] = p.bias ? p.bias[n] : 0.0f;
+            else
+                row[n] = row[n] > 0.0f ? row[n] : 0.0f;
+        }
+    }
+}
+
+hipError_t launch_tile_pass(const GemmParams &p0, int bm, int bn, int first_tile, int count, int mode,
+                            hipStream_t s)
+{
+    if (count <= 0)
+        return hipSuccess;
+    GemmParams p = p0;
+    p.tile_base = first_tile;
+    hipLaunchKernelGGL(tile_pass_kernel, dim3((unsigned)count * kParts), dim3(256), 0, s, p, bm, bn,
+                       mode);
+    return hipGetLastError();
+}
+
 static unsigned rows_grid(int M)
 {
     return (unsigned)(M < 65536 ? M : 65536);

@@ -524,8 +524,8 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     p.tiles_m = (p.M + T::BM - 1) / T::BM;
     p.tiles_n = (p.N + T::BN - 1) / T::BN;
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
-    if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
-        return hipErrorInvalidValue;
+    if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ || p.grid_x != 0 || p.sk_tiles != 0)
+        return hipErrorInvalidValue;   // the 16-bit kernels run whole grids only
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F16_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f16_kernel<T, E, V, WPE, BF16, BT>), grid, block, 0, s, p)
@@ -559,8 +559,8 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
     p.tiles_m = (p.M + 255) / 256;
     p.tiles_n = (p.N + 255) / 256;
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
-    if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
-        return hipErrorInvalidValue;
+    if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ || p.grid_x != 0 || p.sk_tiles != 0)
+        return hipErrorInvalidValue;   // the 16-bit kernels run whole grids only
     const dim3 grid = gemm_grid(p, ntiles), block(256);
     using Cfg = DirectCfg<BT>;
 #define LL_DIRECT(E) \

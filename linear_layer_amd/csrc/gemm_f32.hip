@@ -269,40 +269,47 @@ gemm_f32_kernel(GemmParams p)
 
 // Direct-to-LDS FP32 kernel for 128-bit-aligned operands.
 //
-// The same arithmetic as gemm_f32_kernel (k = 8h + s at MFMA step s, A read
-// as eight k-values per lane per stage), but both operands travel global ->
-// LDS with global_load_lds_dwordx4: no staging registers, no LDS stores, and a
-// ring of NBUF stages instead of two.
-//   A: BM rows x 64 bytes per stage; 16-byte chunks XOR-swizzled by
-//      (row/4)%4, so the 16 lanes one LDS cycle serves (16 consecutive rows,
-//      one logical chunk) hit 16 different 16-byte bank groups. One copy
-//      (KiB) = 16 rows; lane l fills row l/4, slot l%4 and fetches the logical
-//      chunk that the swizzle puts there.
-//   B given K-by-N: 16 k-rows x BN floats, unpadded; 16-byte chunks of rows
-//      8..15 XOR 8, so the two half-waves (rows s and 8+s of a step, 128
-//      bytes each) fall in different halves of the 256-byte bank line. One
-//      copy = 1024/(4*BN) rows; each lane reads one float per MFMA step.
-//   B given N-by-K (BT): BN rows x 64 bytes, copied and read exactly like A.
-// A stage holds eight k-steps. Its barrier sits before the last step, when
-// the wave holds that step's operands in registers: the barrier publishes
-// stage kt+1 and frees stage kt's buffer, which is refilled with stage
-// kt+NBUF while the last step's MFMAs run (a few copies after each row of
-// MFMAs), and the next stage's row-panel operands and first per-step B
-// operands are read then too. Every copy is one global_load_lds on every lane (lanes outside A or B
-// read the zero chunk), so the vmcnt waits count exactly.
-template <int EPI, int BM, int BN, int NBUF, int WPE, bool BT>
+// The same arithmetic as gemm_f32_kernel (k = 16q + 8h + s at MFMA step s of
+// half-stage q, A read as eight k-values per lane per half-stage), but both
+// operands travel global -> LDS with global_load_dwordx4-to-LDS copies: no
+// staging registers, no LDS stores, and a ring of NBUF stages of BK = 16 or 32
+// k-values (one or two half-stages).
+//   A: BM rows x 4*BK bytes per stage; 16-byte chunks XOR-swizzled by
+//      (row / (16/CPR)) % CPR (CPR = BK/4 chunks per row), so the 16 lanes one
+//      LDS cycle serves (16 consecutive rows, one logical chunk) hit 16
+//      different 16-byte bank groups. One copy (KiB) = 64/CPR rows; at
+//      BK = 32 a row's stage is a whole 128-byte line.
+//   B given K-by-N: BK k-rows x BN floats, unpadded; the 16-byte chunks of
+//      rows with k % 16 >= 8 XOR 8, so the two half-waves (rows 16q + s and
+//      16q + 8 + s of a step, 128 bytes each) fall in different halves of the
+//      256-byte bank line. One copy = 1024/(4*BN) rows; each lane reads one
+//      float per MFMA step.
+//   B given N-by-K (BT): BN rows, copied and read exactly like A.
+// A stage's barrier sits before its last k-step, when the wave holds that
+// step's operands in registers: the barrier publishes stage kt+1 and frees
+// stage kt's buffer, which is refilled with stage kt+NBUF while the last
+// step's MFMAs run (a few copies after each row of MFMAs), and the next
+// stage's first operands are read then too; a half-stage's row-panel
+// operands are read at the start of the half before. Every copy is one
+// global_load_lds on every lane (lanes outside A or B read the zero chunk),
+// so the vmcnt waits count exactly.
+template <int EPI, int BM, int BN, int BK, int NBUF, int WPE, bool BT, bool SK>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f32_direct_kernel(GemmParams p)
 {
-    constexpr int BK = 16, KH = 8;
+    constexpr int HALVES = BK / 16, STEPS = BK / 2;           // half-stages, MFMA k-steps
     constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
     constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;       // floats
-    constexpr int COPIES_A = BM / 16 / 4;                     // per wave per stage
-    constexpr int CPB = BN / 4;                               // 16-byte chunks per B row
-    constexpr int RB = 64 / CPB;                              // B rows per copy
-    constexpr int COPIES_B = BT ? BN / 16 / 4 : BK / RB / 4;
+    constexpr int CPR = BK / 4;                               // 16-byte chunks per panel row
+    constexpr int RPC = 64 / CPR;                             // panel rows per copy
+    constexpr int COPIES_A = BM / RPC / 4;                    // per wave per stage
+    constexpr int CPB = BN / 4;                               // 16-byte chunks per B k-row
+    constexpr int RB = 64 / CPB;                              // B k-rows per copy
+    constexpr int COPIES_B = BT ? BN / RPC / 4 : BK / RB / 4;
     constexpr int PER_STAGE = COPIES_A + COPIES_B;
-    static_assert(COPIES_A >= 1 && COPIES_B >= 1 && RB >= 1 && (BT || CPB >= 16), "tile shape");
+    static_assert(BK == 16 || BK == 32, "stage depth");
+    static_assert(COPIES_A >= 1 && COPIES_B >= 1 && RB >= 1 && RB <= 8 && (BT || CPB >= 16),
+                  "tile shape");
     static_assert((NBUF - 1) * PER_STAGE <= 63 && NBUF >= 2 && NBUF <= 4, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) float As[NBUF][A_STAGE];
     __shared__ __attribute__((aligned(1024))) float Bs[NBUF][B_STAGE];
@@ -310,57 +317,82 @@ gemm_f32_direct_kernel(GemmParams p)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
+    auto swz = [](int row) { return (row / (16 / CPR)) & (CPR - 1); };
     select_batch(p);
-    int tm, tn;
-    tile_coords(p, tm, tn);
+    // One tile per workgroup, or (a stream-K launch's sharing workgroups, from
+    // sk_block on) up to two (tile, k-range) segments, each a complete pass of
+    // the pipeline below whose partial sums are added atomically.
+    const bool sharing = SK && (int)blockIdx.x >= p.sk_block;
+    for (int seg = 0;; ++seg) {
+    int tm, tn, K, kb;
+    if (sharing) {
+        if (!sk_segment(p, seg, tm, tn, kb, K))
+            break;
+        if (seg > 0)
+            __syncthreads();   // every wave is done with the previous segment's LDS
+    } else {
+        if (seg > 0)
+            break;
+        tile_coords(p, tm, tn);
+        kb = split_range(p, K);
+    }
     const int m0 = tm * BM, n0 = tn * BN;
-    int K;
-    const int kb = split_range(p, K);
     const float *__restrict__ A = static_cast<const float *>(p.A) + kb;
     const float *__restrict__ B =
         static_cast<const float *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
     const int M = p.M, N = p.N;
 
-    // A copy j of this wave: rows (wave*COPIES_A + j)*16 + lane/4; every
-    // wave's rows start at a multiple of 16, so the chunk is j-independent.
-    const int a_row = wave * COPIES_A * 16 + (lane >> 2);
-    const int a_ch = (lane & 3) ^ ((lane >> 4) & 3);
-    const float *a_src = A + (int64_t)(m0 + a_row) * p.lda + a_ch * 4;
-    const int bt_row = wave * COPIES_B * 16 + (lane >> 2);   // BT: B's rows, like A's
-    const float *bt_src = B + (int64_t)(n0 + bt_row) * p.ldb + a_ch * 4;
-    // B copy j of this wave: k-rows (wave*COPIES_B + j)*RB + lane/CPB; the
-    // lane fills physical chunk lane%CPB of its row, which holds logical chunk
-    // (lane%CPB) ^ (8 if k%16 >= 8).
-    const int b_r = lane / CPB, b_pc = lane % CPB;
-    constexpr int NB_SRC = BT ? 1 : COPIES_B;
-    const float *b_src[NB_SRC];
-    bool b_ok[NB_SRC];
+    // Copy sources. Row-panel copy j (A, or B given N-by-K) covers rows
+    // (wave*COPIES + j)*RPC + lane/CPR. Each wave's rows start at a multiple
+    // of 16, so the swizzled chunk a lane fetches depends only on
+    // (j*RPC) % 16: one variant at BK = 16, two (j even, j odd) at BK = 32.
+    const int r_lane = lane / CPR, slot = lane % CPR;
+    const int a_row = wave * COPIES_A * RPC + r_lane;    // row of copy 0 (A)
+    const int bt_row = wave * COPIES_B * RPC + r_lane;   // row of copy 0 (B given N-by-K)
+    int ch[2];
+    const float *a_src[2], *bt_src[2];
 #pragma unroll
-    for (int j = 0; j < NB_SRC; ++j) {
-        const int kr = (wave * COPIES_B + j) * RB + b_r;
-        const int col = n0 + (b_pc ^ (kr & 8)) * 4;
-        b_src[j] = B + (int64_t)kr * p.ldb + col;
-        b_ok[j] = col < N;
+    for (int v = 0; v < 2; ++v) {
+        ch[v] = slot ^ swz(((v * RPC) & 15) + r_lane);
+        a_src[v] = A + (int64_t)(m0 + a_row) * p.lda + ch[v] * 4;
+        bt_src[v] = B + (int64_t)(n0 + bt_row) * p.ldb + ch[v] * 4;
+    }
+    // B copy j (given K-by-N): k-rows kr0 + lane/CPB with kr0 =
+    // (wave*COPIES_B + j)*RB; the lane fills physical chunk lane%CPB, holding
+    // logical chunk (lane%CPB) ^ (kr & 8), and kr & 8 = kr0 & 8 (kr0 is a
+    // multiple of RB <= 8), so two sources cover every copy.
+    const int b_r = lane / CPB, b_pc = lane % CPB;
+    const float *b_src[2];
+    bool b_ok[2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        const int col = n0 + (b_pc ^ (8 * v)) * 4;
+        b_src[v] = B + (int64_t)b_r * p.ldb + col;
+        b_ok[v] = col < N;
     }
     const uint32_t as_base = lds_addr(&As[0][0]), bs_base = lds_addr(&Bs[0][0]);
 
+    // Copy c (A: 0 .. COPIES_A-1, then B) of the stage at k0 into buffer buf.
     auto copy = [&](int buf, int k0, int c) {
         const float *src;
         uint32_t dst;
-        if (c < COPIES_A) {
-            dst = as_base + buf * (A_STAGE * 4) + (wave * COPIES_A + c) * 1024;
-            const bool ok = m0 + a_row + c * 16 < M && k0 + a_ch * 4 < K;
-            src = ok ? a_src + (int64_t)(c * 16) * p.lda + k0 : zero_chunk<float>();
-        } else if (BT) {
-            const int j = c - COPIES_A;
-            dst = bs_base + buf * (B_STAGE * 4) + (wave * COPIES_B + j) * 1024;
-            const bool ok = n0 + bt_row + j * 16 < N && k0 + a_ch * 4 < K;
-            src = ok ? bt_src + (int64_t)(j * 16) * p.ldb + k0 : zero_chunk<float>();
+        if (c < COPIES_A || BT) {
+            const bool is_a = c < COPIES_A;
+            const int j = is_a ? c : c - COPIES_A;
+            const int v = ((j * RPC) & 15) != 0;
+            dst = (is_a ? as_base + buf * (A_STAGE * 4) : bs_base + buf * (B_STAGE * 4)) +
+                  (wave * (is_a ? COPIES_A : COPIES_B) + j) * 1024;
+            const bool ok = (is_a ? a_row < M - m0 - j * RPC : bt_row < N - n0 - j * RPC) &&
+                            k0 + ch[v] * 4 < K;
+            const int64_t step = (int64_t)(j * RPC) * (is_a ? p.lda : p.ldb) + k0;
+            src = ok ? (is_a ? a_src[v] : bt_src[v]) + step : zero_chunk<float>();
         } else {
             const int j = c - COPIES_A;
+            const int kr0 = (wave * COPIES_B + j) * RB;
+            const int v = (kr0 & 8) != 0;
             dst = bs_base + buf * (B_STAGE * 4) + (wave * COPIES_B + j) * 1024;
-            const bool ok = k0 + (wave * COPIES_B + j) * RB + b_r < K && b_ok[j];
-            src = ok ? b_src[j] + (int64_t)k0 * p.ldb : zero_chunk<float>();
+            const bool ok = k0 + kr0 + b_r < K && b_ok[v];
+            src = ok ? b_src[v] + (int64_t)(k0 + kr0) * p.ldb : zero_chunk<float>();
         }
         lds_dma_16(src, dst);
     };
@@ -375,34 +407,32 @@ gemm_f32_direct_kernel(GemmParams p)
                 acc[i][j][r] = 0.0f;
 
     const int h = lane >> 5, l32 = lane & 31;
-    // Row-panel operands of a stage (A, and B given N-by-K): the lane's row,
-    // k = 8h .. 8h+7 (chunks 2h, 2h+1).
-    auto read_rows = [&](const float *lds, int row0, auto &frag) {
+    // Row-panel operands of half-stage q (A, and B given N-by-K): the lane's
+    // row, k = 16q + 8h .. 16q + 8h + 7 (logical chunks 4q + 2h, 4q + 2h + 1).
+    auto read_rows = [&](const float *lds, int row0, int q, auto &frag) {
         constexpr int F = sizeof(frag) / sizeof(frag[0]);
 #pragma unroll
         for (int f = 0; f < F; ++f) {
             const int row = row0 + f * 32 + l32;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int c = (2 * h + q) ^ ((row >> 2) & 3);
-                frag[f][q] = *reinterpret_cast<const f32x4 *>(&lds[row * BK + c * 4]);
+            for (int e = 0; e < 2; ++e) {
+                const int c = (4 * q + 2 * h + e) ^ swz(row);
+                frag[f][e] = *reinterpret_cast<const f32x4 *>(&lds[row * BK + c * 4]);
             }
         }
     };
-    auto read_a = [&](int buf, f32x4 (&af)[FM][2]) { read_rows(As[buf], wm * WTM, af); };
-    auto read_bt = [&](int buf, auto &bt) { read_rows(Bs[buf], wn * WTN, bt); };
-    // B operands of step s: k = 8h + s, the lane's column of each block.
-    auto read_b = [&](int buf, int s, float (&bf)[FN]) {
-        const int k = 8 * h + s;
+    auto read_a = [&](int buf, int q, f32x4 (&af)[FM][2]) { read_rows(As[buf], wm * WTM, q, af); };
+    auto read_bt = [&](int buf, int q, auto &bt) { read_rows(Bs[buf], wn * WTN, q, bt); };
+    // B operands of k-step t of a stage (B given K-by-N): k = 16(t/8) + 8h + t%8.
+    auto read_b = [&](int buf, int t, float (&bf)[FN]) {
+        const int k = 16 * (t / 8) + 8 * h + (t % 8);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int n = wn * WTN + fn * 32 + l32;
             bf[fn] = Bs[buf][k * BN + (((n >> 2) ^ (8 * h)) << 2) + (n & 3)];
         }
     };
-    // B operand of block column fn at step s: from the per-step reads (B
-    // given K-by-N) or from the stage's row-panel operands (BT).
-    constexpr int FT = BT ? FN : 1;   // row-panel B operands kept per stage
+    constexpr int FT = BT ? FN : 1;   // row-panel B operands kept per half-stage
     auto mfma_step = [&](const f32x4 (&af)[FM][2], int s, const float (&bf)[FN],
                          const f32x4 (&bt)[FT][2]) {
 #pragma unroll
@@ -434,22 +464,42 @@ gemm_f32_direct_kernel(GemmParams p)
     wait_stages((nk < NBUF ? nk : NBUF) - 1);   // stage 0 has landed
     __syncthreads();
 
-    f32x4 af[FM][2], an[FM][2];   // this stage's and the next stage's A operands
+    f32x4 af[FM][2], an[FM][2];   // the current and the next half-stage's A operands
     f32x4 bt[FT][2], btn[FT][2];  // the same for B given N-by-K
     float bf[2][FN];              // B given K-by-N: two steps' operands
-    read_a(0, af);
+    read_a(0, 0, af);
     if constexpr (BT)
-        read_bt(0, bt);
+        read_bt(0, 0, bt);
     else
         read_b(0, 0, bf[0]);
     int buf = 0;
     for (int kt = 0; kt < nk; ++kt) {
         const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;
 #pragma unroll
-        for (int s = 0; s + 1 < KH; ++s) {
+        for (int t = 0; t + 1 < STEPS; ++t) {
+            const int q = t / 8, s = t % 8;
             if constexpr (!BT)
-                read_b(buf, s + 1, bf[(s + 1) & 1]);
-            mfma_step(af, s, bf[s & 1], bt);
+                read_b(buf, t + 1, bf[(t + 1) & 1]);
+            if (HALVES > 1 && s == 0 && q + 1 < HALVES) {   // the next half-stage's panels
+                read_a(buf, q + 1, an);
+                if constexpr (BT)
+                    read_bt(buf, q + 1, btn);
+            }
+            mfma_step(af, s, bf[t & 1], bt);
+            if (HALVES > 1 && s == 7) {
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    af[fm][0] = an[fm][0];
+                    af[fm][1] = an[fm][1];
+                }
+                if constexpr (BT) {
+#pragma unroll
+                    for (int fn = 0; fn < FT; ++fn) {
+                        bt[fn][0] = btn[fn][0];
+                        bt[fn][1] = btn[fn][1];
+                    }
+                }
+            }
         }
         if (kt + 1 < nk) {
             // stage kt+1 has landed (stages up to kt+NBUF-1 were issued); after
@@ -460,9 +510,9 @@ gemm_f32_direct_kernel(GemmParams p)
         const int k_next = (kt + NBUF) * BK;   // refill this buffer with stage kt+NBUF
         const bool refill = kt + NBUF < nk;
         // Operands of stage kt+1 (after the last stage: stale, in-bounds, unused).
-        read_a(nbuf, an);
+        read_a(nbuf, 0, an);
         if constexpr (BT)
-            read_bt(nbuf, btn);
+            read_bt(nbuf, 0, btn);
         else
             read_b(nbuf, 0, bf[0]);
         constexpr int G = (PER_STAGE + FM - 1) / FM;   // refill copies per MFMA row
@@ -498,7 +548,13 @@ gemm_f32_direct_kernel(GemmParams p)
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-            write_block<EPI>(p, acc[fm][fn], m0 + wm * WTM + fm * 32, n0 + wn * WTN + fn * 32, lane);
+            if (sharing)
+                write_block<EPI_ATOMIC>(p, acc[fm][fn], m0 + wm * WTM + fm * 32,
+                                        n0 + wn * WTN + fn * 32, lane);
+            else
+                write_block<EPI>(p, acc[fm][fn], m0 + wm * WTM + fm * 32, n0 + wn * WTN + fn * 32,
+                                 lane);
+    }
 }
 
 // Tile configurations. The 256x256 tile runs one wave per SIMD (256
@@ -518,18 +574,29 @@ using F32_XS = F32Tile<64, 64, 16>;    // 32x32 per wave
 // small to fill the CUs, whose stages are latency-bound: four stages in
 // flight (64 and 32 KiB), the 64x64 tile at four waves per SIMD (2048^3:
 // 108-110 vs 94-103 TFLOP/s with the staged kernel).
-constexpr int kDirectNbufL = 3, kDirectNbufM = 2, kDirectNbufS = 4;
+constexpr int kDirectNbufL = 2, kDirectNbufM = 2, kDirectNbufS = 4;
+// Stage depth of the 256x256 tile: 32 (two 64 KiB stages), so each row-panel
+// copy reads whole 128-byte lines; the other tiles keep 16.
+constexpr int kDirectBkL = 32;
 
-template <int BM, int BN, int NBUF, int WPE, bool BT>
+template <int BM, int BN, int BK, int NBUF, int WPE, bool BT>
 static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hipStream_t s)
 {
     const dim3 grid = gemm_grid(p, ntiles), block(256);
-#define LL_F32_DIRECT(E) \
-    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, NBUF, WPE, BT>), grid, block, 0, s, p)
-    if (epi == EPI_GEMM_BETA0) LL_F32_DIRECT(EPI_GEMM_BETA0);
-    else if (epi == EPI_GEMM_BETA) LL_F32_DIRECT(EPI_GEMM_BETA);
-    else if (epi == EPI_LINEAR) LL_F32_DIRECT(EPI_LINEAR);
-    else LL_F32_DIRECT(EPI_ATOMIC);
+#define LL_F32_DIRECT(E, SK) \
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, BT, SK>), grid, block, 0, s, p)
+    if (p.sk_tiles > 0) {
+        // whole tiles with `epi`, shared ones added atomically
+        if (epi == EPI_GEMM_BETA0) LL_F32_DIRECT(EPI_GEMM_BETA0, true);
+        else if (epi == EPI_GEMM_BETA) LL_F32_DIRECT(EPI_GEMM_BETA, true);
+        else if (epi == EPI_LINEAR) LL_F32_DIRECT(EPI_LINEAR, true);
+        else return hipErrorInvalidValue;
+    } else {
+        if (epi == EPI_GEMM_BETA0) LL_F32_DIRECT(EPI_GEMM_BETA0, false);
+        else if (epi == EPI_GEMM_BETA) LL_F32_DIRECT(EPI_GEMM_BETA, false);
+        else if (epi == EPI_LINEAR) LL_F32_DIRECT(EPI_LINEAR, false);
+        else LL_F32_DIRECT(EPI_ATOMIC, false);
+    }
 #undef LL_F32_DIRECT
     return hipGetLastError();
 }
@@ -540,18 +607,22 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     GemmParams p = p0;
     p.tiles_m = (p.M + T::BM - 1) / T::BM;
     p.tiles_n = (p.N + T::BN - 1) / T::BN;
-    const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
+    int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
         return hipErrorInvalidValue;
+    if (p.grid_x > 0)
+        ntiles = p.grid_x;   // part of the tiles, or a stream-K launch
+    if (p.sk_tiles > 0 && !vec)
+        return hipErrorInvalidValue;   // stream-K runs on the direct kernel only
     // 128-bit-aligned operands take the direct-to-LDS kernel.
     if (vec && T::BM == 256 && T::BN == 256)
-        return launch_direct<256, 256, kDirectNbufL, 1, BT>(p, ntiles, epi, s);
+        return launch_direct<256, 256, kDirectBkL, kDirectNbufL, 1, BT>(p, ntiles, epi, s);
     if (vec && T::BM == 256 && T::BN == 128)
-        return launch_direct<256, 128, kDirectNbufM, 2, BT>(p, ntiles, epi, s);
+        return launch_direct<256, 128, 16, kDirectNbufM, 2, BT>(p, ntiles, epi, s);
     if (vec && T::BM == 128 && T::BN == 128)
-        return launch_direct<128, 128, kDirectNbufS, 2, BT>(p, ntiles, epi, s);
+        return launch_direct<128, 128, 16, kDirectNbufS, 2, BT>(p, ntiles, epi, s);
     if (vec && T::BM == 64 && T::BN == 64)
-        return launch_direct<64, 64, kDirectNbufS, 4, BT>(p, ntiles, epi, s);
+        return launch_direct<64, 64, 16, kDirectNbufS, 4, BT>(p, ntiles, epi, s);
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F32_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE, BT>), grid, block, 0, s, p)
@@ -574,10 +645,10 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // second workgroup beside it} -- throughputs measured on MI355X relative to
 // the 256x256 tile.
 const TileInfo kF32Tiles[kF32NumTiles] = {
-    {F32_L::BM, F32_L::BN, 1, 1.00f, 1.00f, "f32_256x256x16"},
-    {F32_M::BM, F32_M::BN, 2, 0.89f, 0.985f, "f32_256x128x16"},
-    {F32_S::BM, F32_S::BN, 2, 0.80f, 0.94f, "f32_128x128x16"},
-    {F32_XS::BM, F32_XS::BN, 2, 0.40f, 0.72f, "f32_64x64x16"},
+    {F32_L::BM, F32_L::BN, 1, 1.00f, 1.00f, "f32_256x256"},
+    {F32_M::BM, F32_M::BN, 2, 0.89f, 0.985f, "f32_256x128"},
+    {F32_S::BM, F32_S::BN, 2, 0.80f, 0.94f, "f32_128x128"},
+    {F32_XS::BM, F32_XS::BN, 2, 0.40f, 0.72f, "f32_64x64"},
 };
 
 template <bool BT>

@@ -42,6 +42,12 @@ constexpr int64_t kMaxTiles = (int64_t)(0xffffffffu / 256u);
 // for each of `batch` matrices stride_c bytes apart.
 hipError_t launch_scale(float *C, int64_t ldc, int M, int N, float beta, hipStream_t s,
                         int batch = 1, int64_t stride_c = 0);
+// Passes over whole output tiles first_tile .. first_tile+count-1 of p's
+// grouped tile order (p.tiles_m, p.tiles_n, p.group_m set for bm x bn tiles):
+// C = beta*C, Y = bias (or 0), or in-place ReLU.
+enum TilePass { TILE_SCALE = 0, TILE_BIAS = 1, TILE_RELU = 2 };
+hipError_t launch_tile_pass(const GemmParams &p, int bm, int bn, int first_tile, int count, int mode,
+                            hipStream_t s);
 // In-place ReLU over an M x N matrix.
 hipError_t launch_relu(float *Y, int64_t ldy, int M, int N, hipStream_t s);
 // Y = act(bias) broadcast over M rows (bias may be nullptr: act(0)).

@@ -169,7 +169,7 @@ def test_tile_choice():
     f32, f16 = ll.DTYPE_F32, ll.DTYPE_F16
     names32 = [ll.tile_name(f32, t) for t in range(ll.num_tiles(f32))]
     names16 = [ll.tile_name(f16, t) for t in range(ll.num_tiles(f16))]
-    assert names32[0] == "f32_256x256x16" and names16[0] == "f16_256x256_direct"
+    assert names32[0] == "f32_256x256" and names16[0] == "f16_256x256_direct"
     assert ll.tile_name(f32, 99) == "" and ll.num_tiles(7) == 0
 
     def choice(dt, M, N, K, cus=256):
@@ -177,13 +177,25 @@ def test_tile_choice():
         return names[ll.chosen_tile(dt, M, N, K, cus)], ll.chosen_split_k(dt, M, N, K, cus)
 
     # 4096^2 on 256 CUs: exactly one 256x256 tile per CU; no K-split
-    assert choice(f32, 4096, 4096, 4096) == ("f32_256x256x16", 1)
-    # 2047 x 11008: 256x256 tiles leave a partial second round; 256x128 fills better
-    assert choice(f32, 2047, 11008, 4096) == ("f32_256x128x16", 1)
+    assert choice(f32, 4096, 4096, 4096) == ("f32_256x256", 1)
+    # 2047 x 11008: 344 tiles of 256x256 are 1.34 rounds; the full round runs
+    # tile by tile and the 88 leftover tiles are shared out with stream-K
+    assert choice(f32, 2047, 11008, 4096) == ("f32_256x256", 1)
+    assert ll.chosen_stream_k(f32, 2047, 11008, 4096, 256) == 88
+    assert ll.chosen_stream_k(f32, 4096, 4096, 4096, 256) == 0     # one whole round
+    assert ll.chosen_stream_k(f16, 8192, 8192, 8192, 256) == 0     # 16-bit: never
+    ll.set_stream_k(0)
+    try:
+        assert choice(f32, 2047, 11008, 4096) == ("f32_256x128", 1)
+        assert ll.chosen_stream_k(f32, 2047, 11008, 4096, 256) == 0
+    finally:
+        ll.set_stream_k(-1)
+    with pytest.raises(ll.LinearLayerError):
+        ll.set_stream_k(2)
     assert choice(f16, 8192, 8192, 8192) == ("f16_256x256_direct", 1)
     # problems too small to fill 256 CUs use small tiles and split K
     assert choice(f32, 1024, 1024, 1024)[1] > 1
-    assert choice(f32, 256, 256, 256) == ("f32_64x64x16", 4)
+    assert choice(f32, 256, 256, 256) == ("f32_64x64", 4)
     # short K is never split below 64 per split
     assert choice(f32, 512, 512, 64)[1] == 1
     assert choice(f32, 64, 64, 100)[1] <= 2
@@ -214,6 +226,28 @@ def test_tile_choice():
         ll.set_split_k(0)
     with pytest.raises(ll.LinearLayerError):
         ll.set_split_k(17)
+
+
+def test_plan_query_flags():
+    f32, f16 = ll.DTYPE_F32, ll.DTYPE_F16
+    relu, nk = ll.PLAN_RELU, ll.PLAN_B_NK
+    shape = (2047, 11008, 4096, 256)
+    # the fused layer with ReLU still shares out the 88 leftover tiles
+    assert ll.chosen_stream_k(f32 | relu, *shape) == 88
+    # B given N-by-K: no stream-K unless forced; 256x128 tiles instead
+    assert ll.chosen_stream_k(f32 | nk, *shape) == 0
+    assert ll.chosen_stream_k(f32 | relu | nk, *shape) == 0
+    assert ll.tile_name(f32, ll.chosen_tile(f32 | relu | nk, *shape)) == "f32_256x128"
+    ll.set_stream_k(1)
+    try:
+        assert ll.chosen_stream_k(f32 | nk, *shape) == 88
+    finally:
+        ll.set_stream_k(-1)
+    # 16-bit: the layout flag is accepted, the ReLU flag (no 16-bit layer) is not
+    assert ll.chosen_tile(f16 | nk, 8192, 8192, 8192, 256) == 0
+    assert ll.chosen_tile(f16 | relu, 8192, 8192, 8192, 256) == -1
+    assert ll.chosen_tile(f32 | 0x400, 8192, 8192, 8192, 256) == -1
+    assert ll.chosen_split_k(f32 | 0x400, 64, 64, 64, 256) == -1
 
 
 def test_binding_rejects_host_tensors():

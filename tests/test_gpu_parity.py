@@ -87,6 +87,13 @@ def split():
     ll.set_split_k(-1)
 
 
+@pytest.fixture
+def stream_k():
+    """Force stream-K on or off for one test, restore the automatic choice after."""
+    yield ll.set_stream_k
+    ll.set_stream_k(-1)
+
+
 def run_gemm_f32(A, B, alpha=1.0, beta=0.0, C=None):
     Ad, Bd = A.to(DEV), B.to(DEV)
     Cd = (C.clone() if C is not None else torch.full((A.shape[0], B.shape[1]), float("nan"))).to(DEV)
@@ -745,7 +752,88 @@ def test_batched_integer_exact():
         assert_exact(run_batched(fn, A8.to(dt), B8.to(dt), trans_b=True), R, which)
 
 
+# ---- stream-K: leftover tiles shared out over one round of workgroups -------
+
+@pytest.mark.parametrize("t", T32)
+@pytest.mark.parametrize("M,N,K", [(300, 264, 200), (257, 70, 1000), (600, 520, 72)])
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (1.5, 0.5), (-0.5, 1.0)])
+def test_f32_stream_k(t, M, N, K, alpha, beta, tile, stream_k):
+    """Every tile shared out (fewer tiles than CUs): several atomic segments per tile."""
+    tile(F32, t)
+    stream_k(1)
+    A, B, C = rand((M, K), 141), rand((K, N), 142), rand((M, N), 143)
+    got = run_gemm_f32(A, B, alpha, beta, C if beta else None)
+    R, T = oracle.gemm(np32(A), np32(B), alpha, beta, np32(C))
+    assert_close(got, R, T, f"stream-K tile {t} {M}x{N}x{K} a={alpha} b={beta}")
+    got = run_nt(ll.gemm_f32_nt, A, B.t().contiguous(), alpha, beta, C if beta else None)
+    assert_close(got, R, T, f"stream-K A*B^T tile {t} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("t", T32)
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_linear_stream_k(t, act, with_bias, tile, stream_k):
+    tile(F32, t)
+    stream_k(1)
+    M, N, K = 330, 270, 520
+    X, W = rand((M, K), 144, 0.125), rand((K, N), 145, 0.125)
+    b = wl.bias_uniform(N, 146) if with_bias else None
+    got = run_linear(X, W, b, act)
+    R, T = oracle.linear(np32(X), np32(W), None if b is None else np32(b), act)
+    assert_close(got, R, T, f"stream-K linear tile {t} act={act} bias={with_bias}")
+    got = run_linear_nt(X, W.t().contiguous(), b, act)
+    assert_close(got, R, T, f"stream-K linear_nt tile {t}")
+
+
+def test_stream_k_hybrid_rounds(tile, stream_k):
+    """576 tiles of 64x64 on 512 slots: one data-parallel round, 64 tiles shared out."""
+    tile(F32, 3)
+    stream_k(1)
+    M = N = 1536
+    K = 256
+    props = torch.cuda.get_device_properties(0)
+    assert ll.chosen_stream_k(F32, M, N, K, props.multi_processor_count) > 0
+    A, B, C = wl.integers((M, K), 147, -2, 2), wl.integers((K, N), 148, -2, 2), wl.integers((M, N), 149, -4, 4)
+    R, _ = oracle.gemm(np32(A), np32(B), 1.5, 0.5, np32(C))
+    assert_exact(run_gemm_f32(A, B, 1.5, 0.5, C), R, "hybrid integer")
+    Af, Bf = rand((M, K), 150), rand((K, N), 151)
+    R, T = oracle.gemm(np32(Af), np32(Bf))
+    assert_close(run_gemm_f32(Af, Bf), R, T, "hybrid")
+    b = wl.integers((N,), 152, -4, 4)
+    R, _ = oracle.linear(np32(A), np32(B), np32(b), 1)
+    assert_exact(run_linear(A, B, b, 1), R, "hybrid linear integer")
+
+
+def test_stream_k_guards_untouched(tile, stream_k):
+    """Shared-out tiles' passes stay inside the output: the padding columns of C keep their values."""
+    tile(F32, 1)
+    stream_k(1)
+    M, N, K = 300, 264, 192
+    A, B = rand((M, K), 153), rand((K, N), 154)
+    Cw = torch.full((M, N + 8), 7.0, device=DEV)
+    Cd = Cw[:, :N]
+    ll.gemm_f32(A.to(DEV), B.to(DEV), Cd, 1.0, 0.0)
+    b = wl.bias_uniform(N, 155).to(DEV)
+    Yw = torch.full((M, N + 8), 7.0, device=DEV)
+    ll.linear_bias_act(A.to(DEV), B.to(DEV), b, 1, Yw[:, :N])
+    torch.cuda.synchronize()
+    assert torch.all(Cw[:, N:] == 7.0) and torch.all(Yw[:, N:] == 7.0)
+    R, T = oracle.gemm(np32(A), np32(B))
+    assert_close(np32(Cd), R, T, "stream-K strided C")
+
+
 # ---- full-size workloads, as the bench launches them ------------------------
+
+def relu_matches(got, got0, tol=1e-5):
+    """The ReLU run equals ReLU of the run without it: +0 where the pre-activation
+    is clearly negative, equal within tol where it is clearly positive. (Not bit
+    for bit: split-K and stream-K add partial sums atomically, in no fixed order.)"""
+    assert np.all(got[got0 < -tol] == 0) and not np.any(np.signbit(got))
+    pos = got0 > tol
+    assert np.all(np.abs(got[pos] - got0[pos]) <= tol)
+    near = ~(got0 < -tol) & ~pos
+    assert np.all(got[near] <= 2 * tol)
+
 
 def sample_positions(M, N, n, seed):
     g = np.random.default_rng(seed)
@@ -811,7 +899,7 @@ def test_full_linear():
     got0 = run_linear(X, W, b, 0)
     checksums(got0, np32(X).astype(np.float64), np32(W).astype(np.float64),
               bias=np32(b).astype(np.float64))
-    assert np.array_equal(got, np.where(got0 > 0, got0, np.float32(0)))
+    relu_matches(got, got0)
 
 
 @pytest.mark.parametrize("name", ["gemm_f16f32_8192", "gemm_bf16f32_8192"])
@@ -840,7 +928,7 @@ def test_full_linear_nt():
     got0 = run_linear_nt(X, W, b, 0)
     checksums(got0, np32(X).astype(np.float64), np32(W).T.astype(np.float64),
               bias=np32(b).astype(np.float64))
-    assert np.array_equal(got, np.where(got0 > 0, got0, np.float32(0)))
+    relu_matches(got, got0)
 
 
 def test_full_gemm_f16_nt():
