@@ -52,26 +52,48 @@ __global__ void __launch_bounds__(256) relu_kernel(float *Y, int64_t ldy, int M,
 // The same three operations on whole output tiles: tiles tile_base ..
 // tile_base + count - 1 of p's grouped tile order (tiles of bm x bn). They
 // frame the stream-K share of a product, whose tiles receive atomic partial
-// sums: C = beta*C or Y = bias before, ReLU after. Each tile is swept by
-// kParts workgroups, rows interleaved.
-constexpr int kParts = 4;
+// sums: C = beta*C or Y = bias before, ReLU after. A workgroup sweeps
+// kPassRows rows of a tile with 128-bit accesses (stream-K runs only with C
+// 16-byte aligned and ldc a multiple of 4; a column tail short of 4 values,
+// possible when B is given N-by-K, is done value by value).
+constexpr int kPassRows = 16;
+
+__device__ __forceinline__ float pass_one(float v, float b, const GemmParams &p, int mode)
+{
+    if (mode == TILE_SCALE)
+        return p.beta == 0.0f ? 0.0f : p.beta * v;
+    if (mode == TILE_BIAS)
+        return b;
+    return v > 0.0f ? v : 0.0f;
+}
 
 __global__ void __launch_bounds__(256) tile_pass_kernel(GemmParams p, int bm, int bn, int mode)
 {
-    const int t = blockIdx.x / kParts, part = blockIdx.x % kParts;
+    const int parts = bm / kPassRows;
+    const int t = blockIdx.x / parts, part = blockIdx.x % parts;
     int tm, tn;
     tile_of(p, p.tile_base + t, tm, tn);
-    const int m0 = tm * bm, n0 = tn * bn;
-    const int m1 = min(p.M, m0 + bm), n1 = min(p.N, n0 + bn);
-    for (int m = m0 + part; m < m1; m += kParts) {
-        float *row = p.C + (int64_t)m * p.ldc;
-        for (int n = n0 + (int)threadIdx.x; n < n1; n += blockDim.x) {
-            if (mode == TILE_SCALE)
-                row[n] = p.beta == 0.0f ? 0.0f : p.beta * row[n];
-            else if (mode == TILE_BIAS)
-                row[n] = p.bias ? p.bias[n] : 0.0f;
-            else
-                row[n] = row[n] > 0.0f ? row[n] : 0.0f;
+    const int lanes_per_row = bn / 4, rows_per_iter = 256 / lanes_per_row;
+    const int m0 = tm * bm + part * kPassRows, m1 = min(p.M, m0 + kPassRows);
+    const int n = tn * bn + 4 * ((int)threadIdx.x % lanes_per_row), n1 = min(p.N, tn * bn + bn);
+    if (n >= n1)
+        return;
+    const int width = n1 - n < 4 ? n1 - n : 4;
+    float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (mode == TILE_BIAS && p.bias != nullptr)
+        for (int e = 0; e < width; ++e)
+            b[e] = p.bias[n + e];
+    for (int m = m0 + (int)threadIdx.x / lanes_per_row; m < m1; m += rows_per_iter) {
+        float *dst = p.C + (int64_t)m * p.ldc + n;
+        if (width == 4) {
+            f32x4 v = mode == TILE_BIAS ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<f32x4 *>(dst);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = pass_one(v[e], b[e], p, mode);
+            *reinterpret_cast<f32x4 *>(dst) = v;
+        } else {
+            for (int e = 0; e < width; ++e)
+                dst[e] = pass_one(mode == TILE_BIAS ? 0.0f : dst[e], b[e], p, mode);
         }
     }
 }
@@ -83,8 +105,10 @@ hipError_t launch_tile_pass(const GemmParams &p0, int bm, int bn, int first_tile
         return hipSuccess;
     GemmParams p = p0;
     p.tile_base = first_tile;
-    hipLaunchKernelGGL(tile_pass_kernel, dim3((unsigned)count * kParts), dim3(256), 0, s, p, bm, bn,
-                       mode);
+    if (bm % kPassRows != 0 || bn % 4 != 0 || bn > 1024 || 1024 % bn != 0)
+        return hipErrorInvalidValue;   // every tile shape here passes
+    hipLaunchKernelGGL(tile_pass_kernel, dim3((unsigned)count * (bm / kPassRows)), dim3(256), 0, s,
+                       p, bm, bn, mode);
     return hipGetLastError();
 }
 
