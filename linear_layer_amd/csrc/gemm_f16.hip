@@ -296,27 +296,35 @@ gemm_f16_kernel(GemmParams p)
 // With BT (B given N-by-K, k contiguous) B is copied and read exactly like A:
 // 256 rows x 2*BK bytes, the same swizzle, 128-bit operand reads, no
 // transposing loads.
-template <int EPI, bool BF16, bool BT, int BK, int NBUF>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+//
+// The workgroup is a WGM x WGN grid of waves, each owning a (256/WGM) x
+// (256/WGN) block: 2 x 2 runs one wave per SIMD; with 8 waves, two per SIMD,
+// one wave's MFMAs can run while the other waits to issue its copies.
+template <int EPI, bool BF16, bool BT, int BK, int NBUF, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN)
+__attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 gemm_f16_direct_kernel(GemmParams p)
 {
-    constexpr int BM = 256, BN = 256;
-    constexpr int FM = 4, FN = 4, WTM = 128, WTN = 128;
+    constexpr int BM = 256, BN = 256, NW = WGM * WGN;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
     constexpr int STEPS = BK / 16;                        // MFMA k-steps per stage
     constexpr int CPR = BK / 8;                           // 16-byte chunks per A row
     constexpr int RPC = 64 / CPR;                         // A rows per copy
     constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;   // halves
-    constexpr int COPIES_A = BM / RPC / 4;                // per wave per stage
-    constexpr int COPIES_B = BT ? COPIES_A : BK / 2 / 4;
+    constexpr int COPIES_A = BM / RPC / NW;               // per wave per stage
+    constexpr int COPIES_B = BT ? COPIES_A : BK / 2 / NW;
     constexpr int PER_STAGE = COPIES_A + COPIES_B;        // vmcnt entries per stage
     static_assert(STEPS % 2 == 0 && PER_STAGE % FM == 0, "stage layout");
+    static_assert(COPIES_A * RPC * NW == BM && (COPIES_A * RPC) % 16 == 0 &&
+                      (BT || COPIES_B * 2 * NW == BK) && WTM % 32 == 0 && WTN % 32 == 0,
+                  "copies cover the stage; each wave's rows start at a multiple of 16");
     static_assert((NBUF - 1) * PER_STAGE <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) uint16_t As[NBUF][A_STAGE];
     __shared__ __attribute__((aligned(1024))) uint16_t Bs[NBUF][B_STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     select_batch(p);
     int tm, tn;
     tile_coords(p, tm, tn);
@@ -509,8 +517,23 @@ gemm_f16_direct_kernel(GemmParams p)
 // copies read whole 128-byte lines and a stage holds four k-steps under one
 // barrier; two 64 KiB stages measured 6-10 % faster than four 32 KiB ones
 // (BK = 32) for both B layouts on 4096- and 8192-cubed products.
+// Wave grid, per B layout: 2 x 4 (eight waves, two per SIMD, 128x64 each)
+// measured faster than 2 x 2 (one wave per SIMD) and 4 x 2, in one process:
+// 8192^3 fp16 1079 -> 1168 TFLOP/s, bf16 1114 -> 1234, B given N-by-K
+// 1171 -> 1191. A wave that waits to issue a copy no longer idles its SIMD's
+// matrix core, and the 4-wave kernel's 8 spilled registers are gone.
+#ifndef LL_F16_NN_WGM
+#define LL_F16_NN_WGM 2
+#define LL_F16_NN_WGN 4
+#endif
+#ifndef LL_F16_BT_WGM
+#define LL_F16_BT_WGM 2
+#define LL_F16_BT_WGN 4
+#endif
 template <bool BT> struct DirectCfg {
     static constexpr int BK = 64, NBUF = 2;
+    static constexpr int WGM = BT ? LL_F16_BT_WGM : LL_F16_NN_WGM;
+    static constexpr int WGN = BT ? LL_F16_BT_WGN : LL_F16_NN_WGN;
 };
 
 using F16_L = F16Tile<256, 256, 64>;
@@ -561,10 +584,11 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ || p.grid_x != 0 || p.sk_tiles != 0)
         return hipErrorInvalidValue;   // the 16-bit kernels run whole grids only
-    const dim3 grid = gemm_grid(p, ntiles), block(256);
     using Cfg = DirectCfg<BT>;
+    const dim3 grid = gemm_grid(p, ntiles), block(64 * Cfg::WGM * Cfg::WGN);
 #define LL_DIRECT(E) \
-    hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF, Cfg::WGM, Cfg::WGN>), \
+                       grid, block, 0, s, p)
     if (epi == EPI_GEMM_BETA0)
         LL_DIRECT(EPI_GEMM_BETA0);
     else if (epi == EPI_GEMM_BETA)

@@ -293,30 +293,39 @@ gemm_f32_kernel(GemmParams p)
 // operands are read at the start of the half before. Every copy is one
 // global_load_lds on every lane (lanes outside A or B read the zero chunk),
 // so the vmcnt waits count exactly.
-template <int EPI, int BM, int BN, int BK, int NBUF, int WPE, bool BT, bool SK>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+// The workgroup is a WGM x WGN grid of waves, each owning a (BM/WGM) x
+// (BN/WGN) block of the tile; at 2 x 4 and two waves per SIMD, one wave's
+// MFMAs keep the SIMD busy while the other waits at a barrier, on an LDS read
+// or on issuing a copy.
+template <int EPI, int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, bool BT, bool SK>
+__global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f32_direct_kernel(GemmParams p)
 {
+    constexpr int NW = WGM * WGN;                             // waves
     constexpr int HALVES = BK / 16, STEPS = BK / 2;           // half-stages, MFMA k-steps
-    constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
     constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;       // floats
     constexpr int CPR = BK / 4;                               // 16-byte chunks per panel row
     constexpr int RPC = 64 / CPR;                             // panel rows per copy
-    constexpr int COPIES_A = BM / RPC / 4;                    // per wave per stage
+    constexpr int COPIES_A = BM / RPC / NW;                   // per wave per stage
     constexpr int CPB = BN / 4;                               // 16-byte chunks per B k-row
     constexpr int RB = 64 / CPB;                              // B k-rows per copy
-    constexpr int COPIES_B = BT ? BN / RPC / 4 : BK / RB / 4;
+    constexpr int COPIES_B = BT ? BN / RPC / NW : BK / RB / NW;
     constexpr int PER_STAGE = COPIES_A + COPIES_B;
     static_assert(BK == 16 || BK == 32, "stage depth");
     static_assert(COPIES_A >= 1 && COPIES_B >= 1 && RB >= 1 && RB <= 8 && (BT || CPB >= 16),
                   "tile shape");
+    static_assert(COPIES_A * RPC * NW == BM && COPIES_B * (BT ? RPC : RB) * NW == (BT ? BN : BK) &&
+                      (COPIES_A * RPC) % 16 == 0 && (!BT || (COPIES_B * RPC) % 16 == 0) &&
+                      FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0,
+                  "copies cover the stage; each wave's panel rows start at a multiple of 16");
     static_assert((NBUF - 1) * PER_STAGE <= 63 && NBUF >= 2 && NBUF <= 4, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) float As[NBUF][A_STAGE];
     __shared__ __attribute__((aligned(1024))) float Bs[NBUF][B_STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WGN, wn = wave % WGN;
     auto swz = [](int row) { return (row / (16 / CPR)) & (CPR - 1); };
     select_batch(p);
     // One tile per workgroup, or (a stream-K launch's sharing workgroups, from
@@ -557,13 +566,14 @@ gemm_f32_direct_kernel(GemmParams p)
     }
 }
 
-// Tile configurations. The 256x256 tile runs one wave per SIMD (256
-// accumulators per lane); the others are compiled for two waves per SIMD, so
-// two workgroups share a CU and each covers the other's barrier and memory
-// waits. With the direct-to-LDS kernel, 256x256 (one tile per CU) is the
-// fastest on the 4096^3 product (about 87 % of the FP32 matrix peak) and
-// 256x128 at two workgroups per CU quantises best on the 2047 x 11008
-// fully-connected layer.
+// Tile configurations. The staged 256x256 kernel runs one wave per SIMD (256
+// accumulators per lane; the direct one's wave grid is chosen below); the
+// other tiles are compiled for two waves per SIMD, so two workgroups share a
+// CU and each covers the other's barrier and memory waits. With the
+// direct-to-LDS kernel, 256x256 (one tile per CU) is the fastest on the
+// 4096^3 product (about 89 % of the FP32 matrix peak); 256x128 at two
+// workgroups per CU is the plain choice for the 2047 x 11008 fully-connected
+// layer, whose leftover tiles stream-K otherwise shares out.
 using F32_L = F32Tile<256, 256, 16>;   // 128x128 per wave
 using F32_M = F32Tile<256, 128, 16>;   // 128x64 per wave
 using F32_S = F32Tile<128, 128, 16>;   // 64x64 per wave
@@ -578,13 +588,32 @@ constexpr int kDirectNbufL = 2, kDirectNbufM = 2, kDirectNbufS = 4;
 // Stage depth of the 256x256 tile: 32 (two 64 KiB stages), so each row-panel
 // copy reads whole 128-byte lines; the other tiles keep 16.
 constexpr int kDirectBkL = 32;
+// Wave grid of the 256x256 tile, per B layout: 2 x 2 (one wave per SIMD,
+// 128x128 each) or 8 waves (two per SIMD). Measured in one process: B given
+// K-by-N 2 x 4 (4096^3 138 -> 140 TFLOP/s, 8192^3 139 -> 141); B given
+// N-by-K 2 x 2 (8 waves: 141 -> 129, the next stage's 128-bit operand reads
+// of all eight waves burst into the LDS right after each barrier).
+#ifndef LL_F32_NN_WGM
+#define LL_F32_NN_WGM 2
+#define LL_F32_NN_WGN 4
+#endif
+#ifndef LL_F32_BT_WGM
+#define LL_F32_BT_WGM 2
+#define LL_F32_BT_WGN 2
+#endif
+template <bool BT> struct WaveGridL {
+    static constexpr int M = BT ? LL_F32_BT_WGM : LL_F32_NN_WGM;
+    static constexpr int N = BT ? LL_F32_BT_WGN : LL_F32_NN_WGN;
+    static constexpr int WPE = M * N / 4;
+};
 
-template <int BM, int BN, int BK, int NBUF, int WPE, bool BT>
+template <int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, bool BT>
 static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hipStream_t s)
 {
-    const dim3 grid = gemm_grid(p, ntiles), block(256);
+    const dim3 grid = gemm_grid(p, ntiles), block(64 * WGM * WGN);
 #define LL_F32_DIRECT(E, SK) \
-    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, BT, SK>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, BT, SK>), grid, \
+                       block, 0, s, p)
     if (p.sk_tiles > 0) {
         // whole tiles with `epi`, shared ones added atomically
         if (epi == EPI_GEMM_BETA0) LL_F32_DIRECT(EPI_GEMM_BETA0, true);
@@ -616,13 +645,14 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
         return hipErrorInvalidValue;   // stream-K runs on the direct kernel only
     // 128-bit-aligned operands take the direct-to-LDS kernel.
     if (vec && T::BM == 256 && T::BN == 256)
-        return launch_direct<256, 256, kDirectBkL, kDirectNbufL, 1, BT>(p, ntiles, epi, s);
+        return launch_direct<256, 256, kDirectBkL, kDirectNbufL, WaveGridL<BT>::WPE, WaveGridL<BT>::M,
+                             WaveGridL<BT>::N, BT>(p, ntiles, epi, s);
     if (vec && T::BM == 256 && T::BN == 128)
-        return launch_direct<256, 128, 16, kDirectNbufM, 2, BT>(p, ntiles, epi, s);
+        return launch_direct<256, 128, 16, kDirectNbufM, 2, 2, 2, BT>(p, ntiles, epi, s);
     if (vec && T::BM == 128 && T::BN == 128)
-        return launch_direct<128, 128, 16, kDirectNbufS, 2, BT>(p, ntiles, epi, s);
+        return launch_direct<128, 128, 16, kDirectNbufS, 2, 2, 2, BT>(p, ntiles, epi, s);
     if (vec && T::BM == 64 && T::BN == 64)
-        return launch_direct<64, 64, 16, kDirectNbufS, 4, BT>(p, ntiles, epi, s);
+        return launch_direct<64, 64, 16, kDirectNbufS, 4, 2, 2, BT>(p, ntiles, epi, s);
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F32_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE, BT>), grid, block, 0, s, p)
