@@ -235,7 +235,7 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
         // tiles' k-units are shared out evenly over one round of workgroups,
         // which add their partial sums atomically (framed by a pass that
         // prepares those tiles and, for ReLU, one that finishes them).
-        if (allow_sk) {
+        if (allow_sk && ti.k_slices == 1) {
             const int64_t slots = (int64_t)cus * ti.wg_per_cu;
             const int64_t rounds = tiles_mn / slots, rest = tiles_mn - rounds * slots;
             const int64_t units = ((int64_t)K + kSkUnit - 1) / kSkUnit;

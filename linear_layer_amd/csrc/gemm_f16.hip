@@ -438,12 +438,17 @@ gemm_f16_direct_kernel(GemmParams p)
                 lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         }
     };
+    // The MFMA groups raise the wave's issue priority (s_setprio), so a wave
+    // with MFMAs ready wins the arbitration over its SIMD's other wave while
+    // that one issues reads and copies (measured about +1 %).
     auto mfma_step = [&](const f16x8 (&af)[FM], const f16x8 (&bf)[FN]) {
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
                 acc[fm][fn] = mma16<BF16>(af[fm], bf[fn], acc[fm][fn]);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // Wait until at most n stages of copies are still in flight.
@@ -492,6 +497,7 @@ gemm_f16_direct_kernel(GemmParams p)
         // join makes the compiler's LDS wait counts conservative.
         read_step(nbuf, 0, fa[0], fb[0]);
         constexpr int G = PER_STAGE / FM;   // refill copies after each row of MFMAs
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -503,6 +509,7 @@ gemm_f16_direct_kernel(GemmParams p)
                     copy(buf, k_next, fm * G + g);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         buf = nbuf;
     }
 

@@ -297,11 +297,21 @@ gemm_f32_kernel(GemmParams p)
 // (BN/WGN) block of the tile; at 2 x 4 and two waves per SIMD, one wave's
 // MFMAs keep the SIMD busy while the other waits at a barrier, on an LDS read
 // or on issuing a copy.
-template <int EPI, int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, bool BT, bool SK>
-__global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+//
+// K-slices (KS > 1, for problems too small to fill the CUs with tiles): the
+// workgroup holds KS such grids, slice s running the pipeline above on its own
+// ring over the s-th of KS equal, stage-aligned parts of the tile's K range
+// (all slices run the same number of stages, past the end on zeros, so they
+// share every barrier). The partial tiles are then summed through the LDS in
+// slice order and slice 0 writes the result: K split without atomics, extra
+// passes or a second launch, and with KS times the waves to hide each
+// stage's load latency.
+template <int EPI, int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, int KS, bool BT,
+          bool SK>
+__global__ void __launch_bounds__(64 * WGM * WGN * KS) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f32_direct_kernel(GemmParams p)
 {
-    constexpr int NW = WGM * WGN;                             // waves
+    constexpr int NW = WGM * WGN;                             // waves per slice
     constexpr int HALVES = BK / 16, STEPS = BK / 2;           // half-stages, MFMA k-steps
     constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
     constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;       // floats
@@ -320,11 +330,14 @@ gemm_f32_direct_kernel(GemmParams p)
                       FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0,
                   "copies cover the stage; each wave's panel rows start at a multiple of 16");
     static_assert((NBUF - 1) * PER_STAGE <= 63 && NBUF >= 2 && NBUF <= 4, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) float As[NBUF][A_STAGE];
-    __shared__ __attribute__((aligned(1024))) float Bs[NBUF][B_STAGE];
+    static_assert(KS >= 1 && NW * KS <= 16 && (KS == 1 || !SK), "K-slices");
+    static_assert((KS - 1) * NW * FM * FN * 16 * 64 <= KS * NBUF * A_STAGE, "slice partials fit");
+    __shared__ __attribute__((aligned(1024))) float As[KS][NBUF][A_STAGE];
+    __shared__ __attribute__((aligned(1024))) float Bs[KS][NBUF][B_STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slice = wave_wg / NW, wave = wave_wg % NW;   // wave within the slice
     const int wm = wave / WGN, wn = wave % WGN;
     auto swz = [](int row) { return (row / (16 / CPR)) & (CPR - 1); };
     select_batch(p);
@@ -344,6 +357,14 @@ gemm_f32_direct_kernel(GemmParams p)
             break;
         tile_coords(p, tm, tn);
         kb = split_range(p, K);
+    }
+    // This slice's part of the K range; every slice runs k_steps k-values.
+    int k_steps = K;
+    if (KS > 1) {
+        k_steps = ((K + KS - 1) / KS + BK - 1) / BK * BK;
+        const int lo = slice * k_steps;
+        kb += lo < K ? lo : K;
+        K = K - lo < k_steps ? (K - lo > 0 ? K - lo : 0) : k_steps;
     }
     const int m0 = tm * BM, n0 = tn * BN;
     const float *__restrict__ A = static_cast<const float *>(p.A) + kb;
@@ -379,7 +400,7 @@ gemm_f32_direct_kernel(GemmParams p)
         b_src[v] = B + (int64_t)b_r * p.ldb + col;
         b_ok[v] = col < N;
     }
-    const uint32_t as_base = lds_addr(&As[0][0]), bs_base = lds_addr(&Bs[0][0]);
+    const uint32_t as_base = lds_addr(&As[slice][0][0]), bs_base = lds_addr(&Bs[slice][0][0]);
 
     // Copy c (A: 0 .. COPIES_A-1, then B) of the stage at k0 into buffer buf.
     auto copy = [&](int buf, int k0, int c) {
@@ -430,15 +451,17 @@ gemm_f32_direct_kernel(GemmParams p)
             }
         }
     };
-    auto read_a = [&](int buf, int q, f32x4 (&af)[FM][2]) { read_rows(As[buf], wm * WTM, q, af); };
-    auto read_bt = [&](int buf, int q, auto &bt) { read_rows(Bs[buf], wn * WTN, q, bt); };
+    auto read_a = [&](int buf, int q, f32x4 (&af)[FM][2]) {
+        read_rows(As[slice][buf], wm * WTM, q, af);
+    };
+    auto read_bt = [&](int buf, int q, auto &bt) { read_rows(Bs[slice][buf], wn * WTN, q, bt); };
     // B operands of k-step t of a stage (B given K-by-N): k = 16(t/8) + 8h + t%8.
     auto read_b = [&](int buf, int t, float (&bf)[FN]) {
         const int k = 16 * (t / 8) + 8 * h + (t % 8);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int n = wn * WTN + fn * 32 + l32;
-            bf[fn] = Bs[buf][k * BN + (((n >> 2) ^ (8 * h)) << 2) + (n & 3)];
+            bf[fn] = Bs[slice][buf][k * BN + (((n >> 2) ^ (8 * h)) << 2) + (n & 3)];
         }
     };
     constexpr int FT = BT ? FN : 1;   // row-panel B operands kept per half-stage
@@ -463,7 +486,7 @@ gemm_f32_direct_kernel(GemmParams p)
             __builtin_amdgcn_s_waitcnt(LL_VMCNT(0));
     };
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (k_steps + BK - 1) / BK;   // the same in every slice
     for (int st = 0; st < NBUF; ++st)
         if (st < nk) {
 #pragma unroll
@@ -553,6 +576,36 @@ gemm_f32_direct_kernel(GemmParams p)
         buf = nbuf;
     }
 
+    if constexpr (KS > 1) {
+        // Slices 1.. park their partial tiles in the (now idle) A rings, one
+        // float per lane per slot, then slice 0 adds them in slice order.
+        float *part = &As[0][0][0];
+        constexpr int SLOTS = FM * FN * 16;
+        __syncthreads();   // every slice is done reading its ring
+        if (slice > 0) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        part[((((slice - 1) * NW + wave) * SLOTS) + (fm * FN + fn) * 16 + r) * 64 + lane] =
+                            acc[fm][fn][r];
+        }
+        __syncthreads();
+        if (slice > 0)
+            return;   // no barrier follows
+        for (int sl = 1; sl < KS; ++sl)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[fm][fn][r] +=
+                            part[((((sl - 1) * NW + wave) * SLOTS) + (fm * FN + fn) * 16 + r) * 64 + lane];
+    }
+
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -580,11 +633,12 @@ using F32_S = F32Tile<128, 128, 16>;   // 64x64 per wave
 using F32_XS = F32Tile<64, 64, 16>;    // 32x32 per wave
 // Ring lengths of the direct kernel: 256x256 (one workgroup per CU) and
 // 256x128 (two per CU, at most 80 KiB of LDS each) measured no faster with
-// longer rings (within 1 %). The 128x128 and 64x64 tiles serve problems too
-// small to fill the CUs, whose stages are latency-bound: four stages in
-// flight (64 and 32 KiB), the 64x64 tile at four waves per SIMD (2048^3:
-// 108-110 vs 94-103 TFLOP/s with the staged kernel).
-constexpr int kDirectNbufL = 2, kDirectNbufM = 2, kDirectNbufS = 4;
+// longer rings (within 1 %). The 128x128 and 64x64 tiles (plain or K-sliced)
+// serve problems too small to fill the CUs; they run two stages of BK = 32,
+// which measured faster than four of BK = 16 in the same LDS (whole-line
+// copies, half the barriers): 1024^3 as 64x64 in four K-slices 29.5 -> 27.4
+// us, 2048^3 as 128x128 in two 144 -> 139 us.
+constexpr int kDirectNbufL = 2, kDirectNbufM = 2;
 // Stage depth of the 256x256 tile: 32 (two 64 KiB stages), so each row-panel
 // copy reads whole 128-byte lines; the other tiles keep 16.
 constexpr int kDirectBkL = 32;
@@ -607,14 +661,21 @@ template <bool BT> struct WaveGridL {
     static constexpr int WPE = M * N / 4;
 };
 
-template <int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, bool BT>
+template <int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, bool BT, int KS = 1>
 static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hipStream_t s)
 {
-    const dim3 grid = gemm_grid(p, ntiles), block(64 * WGM * WGN);
+    const dim3 grid = gemm_grid(p, ntiles), block(64 * WGM * WGN * KS);
 #define LL_F32_DIRECT(E, SK) \
-    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, BT, SK>), grid, \
-                       block, 0, s, p)
-    if (p.sk_tiles > 0) {
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, KS, BT, SK>), \
+                       grid, block, 0, s, p)
+    if (KS > 1 && p.sk_tiles > 0)
+        return hipErrorInvalidValue;
+    if constexpr (KS > 1) {
+        if (epi == EPI_GEMM_BETA0) LL_F32_DIRECT(EPI_GEMM_BETA0, false);
+        else if (epi == EPI_GEMM_BETA) LL_F32_DIRECT(EPI_GEMM_BETA, false);
+        else if (epi == EPI_LINEAR) LL_F32_DIRECT(EPI_LINEAR, false);
+        else LL_F32_DIRECT(EPI_ATOMIC, false);
+    } else if (p.sk_tiles > 0) {
         // whole tiles with `epi`, shared ones added atomically
         if (epi == EPI_GEMM_BETA0) LL_F32_DIRECT(EPI_GEMM_BETA0, true);
         else if (epi == EPI_GEMM_BETA) LL_F32_DIRECT(EPI_GEMM_BETA, true);
@@ -630,7 +691,7 @@ static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hi
     return hipGetLastError();
 }
 
-template <class T, int WPE, bool BT>
+template <class T, int WPE, bool BT, int KS = 1>
 static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
     GemmParams p = p0;
@@ -644,15 +705,18 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     if (p.sk_tiles > 0 && !vec)
         return hipErrorInvalidValue;   // stream-K runs on the direct kernel only
     // 128-bit-aligned operands take the direct-to-LDS kernel.
-    if (vec && T::BM == 256 && T::BN == 256)
-        return launch_direct<256, 256, kDirectBkL, kDirectNbufL, WaveGridL<BT>::WPE, WaveGridL<BT>::M,
-                             WaveGridL<BT>::N, BT>(p, ntiles, epi, s);
-    if (vec && T::BM == 256 && T::BN == 128)
-        return launch_direct<256, 128, 16, kDirectNbufM, 2, 2, 2, BT>(p, ntiles, epi, s);
-    if (vec && T::BM == 128 && T::BN == 128)
-        return launch_direct<128, 128, 16, kDirectNbufS, 2, 2, 2, BT>(p, ntiles, epi, s);
-    if (vec && T::BM == 64 && T::BN == 64)
-        return launch_direct<64, 64, 16, kDirectNbufS, 4, 2, 2, BT>(p, ntiles, epi, s);
+    static_assert(KS == 1 || (T::BM == T::BN && T::BM <= 128), "K-slices: the small tiles only");
+    if (vec) {
+        if constexpr (T::BM == 256 && T::BN == 256)
+            return launch_direct<256, 256, kDirectBkL, kDirectNbufL, WaveGridL<BT>::WPE,
+                                 WaveGridL<BT>::M, WaveGridL<BT>::N, BT>(p, ntiles, epi, s);
+        else if constexpr (T::BM == 256 && T::BN == 128)
+            return launch_direct<256, 128, 16, kDirectNbufM, 2, 2, 2, BT>(p, ntiles, epi, s);
+        else if constexpr (T::BM == 128 && T::BN == 128)
+            return launch_direct<128, 128, 32, 2, 2 * KS, 2, 2, BT, KS>(p, ntiles, epi, s);
+        else if constexpr (T::BM == 64 && T::BN == 64)
+            return launch_direct<64, 64, 32, 2, (KS > 1 ? KS : 4), 2, 2, BT, KS>(p, ntiles, epi, s);
+    }
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F32_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE, BT>), grid, block, 0, s, p)
@@ -678,7 +742,11 @@ const TileInfo kF32Tiles[kF32NumTiles] = {
     {F32_L::BM, F32_L::BN, 1, 1.00f, 1.00f, "f32_256x256"},
     {F32_M::BM, F32_M::BN, 2, 0.89f, 0.985f, "f32_256x128"},
     {F32_S::BM, F32_S::BN, 2, 0.80f, 0.94f, "f32_128x128"},
-    {F32_XS::BM, F32_XS::BN, 2, 0.40f, 0.72f, "f32_64x64"},
+    {F32_XS::BM, F32_XS::BN, 2, 0.52f, 0.72f, "f32_64x64"},
+    // K-sliced tiles (direct kernel only; the staged fallback runs the plain
+    // tile): four slices of 64x64 (1024^3: 0.57), two of 128x128 (2048^3: 0.90).
+    {F32_XS::BM, F32_XS::BN, 1, 0.57f, 0.57f, "f32_64x64_k4", 4},
+    {F32_S::BM, F32_S::BN, 1, 0.90f, 0.90f, "f32_128x128_k2", 2},
 };
 
 template <bool BT>
@@ -688,7 +756,9 @@ static hipError_t launch_f32(const GemmParams &p, int tile, int epi, bool vec, h
     case 0: return launch_t<F32_L, 1, BT>(p, epi, vec, s);
     case 1: return launch_t<F32_M, 2, BT>(p, epi, vec, s);
     case 2: return launch_t<F32_S, 2, BT>(p, epi, vec, s);
-    default: return launch_t<F32_XS, 2, BT>(p, epi, vec, s);
+    case 3: return launch_t<F32_XS, 2, BT>(p, epi, vec, s);
+    case 4: return launch_t<F32_XS, 2, BT, 4>(p, epi, vec, s);
+    default: return launch_t<F32_S, 2, BT, 2>(p, epi, vec, s);
     }
 }
 

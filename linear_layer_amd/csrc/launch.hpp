@@ -13,9 +13,10 @@ struct TileInfo {
     float eff_alone;   // relative CU throughput with one workgroup on it
     float eff_paired;  // relative CU throughput with wg_per_cu workgroups on it
     const char *name;
+    int k_slices = 1;  // K-slices inside the workgroup (such tiles take no stream-K share)
 };
 
-constexpr int kF32NumTiles = 4;
+constexpr int kF32NumTiles = 6;
 constexpr int kF16NumTiles = 3;
 extern const TileInfo kF32Tiles[kF32NumTiles];
 extern const TileInfo kF16Tiles[kF16NumTiles];

@@ -193,9 +193,19 @@ def test_tile_choice():
     with pytest.raises(ll.LinearLayerError):
         ll.set_stream_k(2)
     assert choice(f16, 8192, 8192, 8192) == ("f16_256x256_direct", 1)
-    # problems too small to fill 256 CUs use small tiles and split K
-    assert choice(f32, 1024, 1024, 1024)[1] > 1
-    assert choice(f32, 256, 256, 256) == ("f32_64x64", 4)
+    # problems too small to fill 256 CUs use small tiles split along K: in
+    # the workgroup (K-slices), across workgroups, or both
+    assert choice(f32, 1024, 1024, 1024) == ("f32_64x64_k4", 1)
+    assert choice(f32, 2048, 2048, 2048) == ("f32_128x128_k2", 1)
+    assert choice(f32, 256, 256, 256) == ("f32_64x64_k4", 4)
+    # K-sliced tiles take no stream-K share
+    ll.set_tile(f32, 4)
+    ll.set_stream_k(1)
+    try:
+        assert ll.chosen_stream_k(f32, 2047, 11008, 4096, 256) == 0
+    finally:
+        ll.set_stream_k(-1)
+        ll.set_tile(f32, -1)
     # short K is never split below 64 per split
     assert choice(f32, 512, 512, 64)[1] == 1
     assert choice(f32, 64, 64, 100)[1] <= 2

@@ -377,6 +377,25 @@ def test_split_k_integer_exact(S, split):
     assert_exact(run_linear(X, W, b, 1), R, f"linear int split {S}")
 
 
+@pytest.mark.parametrize("t", [4, 5])
+@pytest.mark.parametrize("K", [1, 40, 96, 97, 1000])
+@pytest.mark.parametrize("S", [1, 3])
+def test_k_slices_integer_exact(t, K, S, tile, split):
+    """K-sliced tiles: slices past the end of K (K = 1, 40), ragged last stages, a
+    workgroup-level K-split on top; integer inputs, so every order is exact."""
+    tile(F32, t)
+    split(S)
+    M, N = 150, 136   # N % 4 == 0: K-by-N B takes the direct kernel when K % 4 == 0
+    A, B, C = wl.integers((M, K), 160, -2, 2), wl.integers((K, N), 161, -2, 2), wl.integers((M, N), 162, -4, 4)
+    R, _ = oracle.gemm(np32(A), np32(B), 1.5, 0.5, np32(C))
+    assert_exact(run_gemm_f32(A, B, 1.5, 0.5, C), R, f"k-sliced tile {t} K={K} split {S}")
+    got = run_nt(ll.gemm_f32_nt, A, B.t().contiguous(), 1.5, 0.5, C)
+    assert_exact(got, R, f"k-sliced tile {t} K={K} split {S}, B given N-by-K")
+    b = wl.integers((N,), 163, -4, 4)
+    R, _ = oracle.linear(np32(A), np32(B), np32(b), 1)
+    assert_exact(run_linear(A, B, b, 1), R, f"k-sliced linear tile {t} K={K} split {S}")
+
+
 def test_split_k_beta_zero_ignores_nan(split):
     split(4)
     M, N, K = 100, 120, 640
