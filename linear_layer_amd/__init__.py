@@ -240,17 +240,34 @@ def gemm_bf16f32_batched(A, B, C, alpha: float = 1.0, beta: float = 0.0, trans_b
                          stream)
 
 
+_RAW = None
+
+
+def _raw_getters():
+    """(current device index, raw current stream of a device): torch's direct
+    getters when it has them (no Stream object per call), else the public API."""
+    global _RAW
+    if _RAW is None:
+        torch = _torch()
+        get_dev = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
+        get_raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if get_raw is None:
+            def get_raw(index):
+                return torch.cuda.current_stream(index).cuda_stream
+        _RAW = (get_dev, get_raw)
+    return _RAW
+
+
 def _stream(stream, *tensors):
-    torch = _torch()
     if stream is None:
         dev = tensors[0].device
         for t in tensors[1:]:
             if t is not None and t.device != dev:
                 raise ValueError("all tensors must be on the same device")
-        if torch.cuda.current_device() != dev.index:
-            raise ValueError(f"tensors are on {dev}, but the current device is "
-                             f"cuda:{torch.cuda.current_device()}")
-        stream = torch.cuda.current_stream(dev)
+        get_dev, get_raw = _raw_getters()
+        if get_dev() != dev.index:
+            raise ValueError(f"tensors are on {dev}, but the current device is cuda:{get_dev()}")
+        return ctypes.c_void_p(get_raw(dev.index))
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
