@@ -297,7 +297,7 @@ def main():
             **({"b_layout": "N-by-K"} if w.kind in wl.B_TRANSPOSED_KINDS else {}),
             **({"batch": w.batch} if batched else {}),
             "tile": ll.tile_name(dtype_id, tile), "split_k": splits, "stream_k_tiles": sk_tiles,
-            "device": props.name, "cus": props.multi_processor_count,
+            "device": props.name, "cus": props.multi_processor_count, "hip": torch.version.hip,
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {

@@ -465,8 +465,14 @@ gemm_f32_direct_kernel(GemmParams p)
         }
     };
     constexpr int FT = BT ? FN : 1;   // row-panel B operands kept per half-stage
+    // With several waves per SIMD, each group of MFMAs runs at raised issue
+    // priority (s_setprio), so the wave with MFMAs ready wins the arbitration
+    // over the others while they read, copy or wait (4096^3: +1.4 %, 2048^3
+    // as two K-slices: +3.5 %).
     auto mfma_step = [&](const f32x4 (&af)[FM][2], int s, const float (&bf)[FN],
                          const f32x4 (&bt)[FT][2]) {
+        if (NW * KS > 4)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -474,6 +480,8 @@ gemm_f32_direct_kernel(GemmParams p)
                 acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                     af[fm][s >> 2][s & 3], BT ? bt[BT ? fn : 0][s >> 2][s & 3] : bf[fn], acc[fm][fn],
                     0, 0, 0);
+        if (NW * KS > 4)
+            __builtin_amdgcn_s_setprio(0);
     };
     auto wait_stages = [&](int n) {
         if (n >= 3)
@@ -548,6 +556,8 @@ gemm_f32_direct_kernel(GemmParams p)
         else
             read_b(nbuf, 0, bf[0]);
         constexpr int G = (PER_STAGE + FM - 1) / FM;   // refill copies per MFMA row
+        if (NW * KS > 4)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
@@ -561,6 +571,8 @@ gemm_f32_direct_kernel(GemmParams p)
                         copy(buf, k_next, fm * G + g);
             }
         }
+        if (NW * KS > 4)
+            __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
             af[fm][0] = an[fm][0];
