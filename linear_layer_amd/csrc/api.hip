@@ -148,6 +148,11 @@ constexpr int kMaxSplits = 16;
 // at the FP32 matrix peak one CU does 157.3e12 / 2 / 256 = 307e3 of them per
 // microsecond.
 constexpr double kUnitsPerUs = 307e3;
+// Fixed cost (us) of the extra launches a K-split or stream-K plan makes: the
+// pass that prepares C (or Y) and, for ReLU, the pass after. Through the
+// Python binding a 256^3 product measured 8.6 us per call as one launch and
+// 10.3 us split four ways, so a pass is charged more than its GPU time.
+constexpr double kPassUs = 5.0, kReluPassUs = 3.0;
 
 // Estimated time of a launch with `wgs` workgroups of `work` units each: the
 // dispatcher deals workgroups round-robin, so the busiest CU gets
@@ -223,7 +228,7 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
             if (splits > 1) {
                 const double mn = (double)M * N * items;
                 const double bytes = 8.0 * mn * (relu ? 2 : 1) + 4.0 * mn * splits;
-                cost += ((relu ? 6.0 : 3.0) + bytes / 3.0e6) * kUnitsPerUs;
+                cost += ((relu ? kPassUs + kReluPassUs : kPassUs) + bytes / 3.0e6) * kUnitsPerUs;
             }
             if (!have || cost < best_cost) {
                 best = Plan{t, splits, k_split, 0, 0};
@@ -249,7 +254,7 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
                 // them); passes: the prepare write and, for ReLU, a read and write
                 const double area = 4.0 * ti.bm * ti.bn;
                 const double bytes = area * (double)(grid + rest) + area * rest * (relu ? 3 : 1);
-                cost += ((relu ? 6.0 : 3.0) + bytes / 3.0e6) * kUnitsPerUs;
+                cost += ((relu ? kPassUs + kReluPassUs : kPassUs) + bytes / 3.0e6) * kUnitsPerUs;
                 if (!have_sk || cost < best_sk_cost) {
                     best_sk = Plan{t, 1, K, (int)(rounds * slots), (int)grid};
                     best_sk_cost = cost;

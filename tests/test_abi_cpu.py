@@ -197,7 +197,8 @@ def test_tile_choice():
     # the workgroup (K-slices), across workgroups, or both
     assert choice(f32, 1024, 1024, 1024) == ("f32_64x64_k4", 1)
     assert choice(f32, 2048, 2048, 2048) == ("f32_128x128_k2", 1)
-    assert choice(f32, 256, 256, 256) == ("f32_64x64_k4", 4)
+    assert choice(f32, 256, 256, 256) == ("f32_64x64_k4", 1)   # one launch: launch-bound size
+    assert choice(f32, 512, 512, 512) == ("f32_64x64_k4", 4)
     # K-sliced tiles take no stream-K share
     ll.set_tile(f32, 4)
     ll.set_stream_k(1)
