@@ -225,9 +225,10 @@ def test_tile_choice():
         ll.set_split_k(-1)
     assert ll.chosen_tile(f32, 4096, 4096, 4096, 256) == 0
     # a batch counts all its items' tiles: 256 items of 256^3 fill the CUs
-    # without splitting K, one item alone splits it
+    # with 256x256 tiles, one item alone takes small K-sliced tiles
+    assert ll.chosen_tile(f32, 256, 256, 256, 256, batch=256) == 0
     assert ll.chosen_split_k(f32, 256, 256, 256, 256, batch=256) == 1
-    assert ll.chosen_split_k(f32, 256, 256, 256, 256, batch=1) > 1
+    assert ll.tile_name(f32, ll.chosen_tile(f32, 256, 256, 256, 256, batch=1)) == "f32_64x64_k4"
     assert ll.chosen_tile(f32, 256, 256, 256, 256, batch=0) == -1
     with pytest.raises(ll.LinearLayerError):
         ll.set_tile(f32, 17)
