@@ -248,9 +248,10 @@ int ll_chosen_split_k(int dtype, int M, int N, int K, int batch, int num_cus);
  * the ReLU applied afterwards). Like a K-split, this makes the summation
  * order of those tiles run-dependent (still within the error bound; integer
  * inputs stay exact); it allocates nothing.
- *   ll_set_stream_k: -1 automatic (default; never for the _nt forms, where
- *   it measured slower), 0 never, 1 whenever the shape allows it (a forced
- *   K-split takes precedence). Returns LL_OK or LL_ERR_INVALID_VALUE.
+ *   ll_set_stream_k: -1 automatic (default; for the _nt forms not on the
+ *   256x256 tile, where it measured slower), 0 never, 1 whenever the shape
+ *   allows it (a forced K-split takes precedence; K-sliced tiles never
+ *   share out). Returns LL_OK or LL_ERR_INVALID_VALUE.
  *   ll_chosen_stream_k: the number of tiles the plan shares out (0: none),
  *   assuming 128-bit-aligned operands; dtype and flags as for
  *   ll_chosen_tile; -1 for an unknown dtype or flag, or batch < 1.
