@@ -32,14 +32,14 @@ COPY_BYTES = 256 << 20
 # Published MI355X dense matrix peaks (TFLOP/s).
 PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "linear_nt": 157.3, "gemm_f32_batched": 157.3,
                "gemm_f16f32": 2516.6, "gemm_bf16f32": 2516.6, "gemm_f16f32_nt": 2516.6}
-KERNEL_SOURCES = {
-    "gemm_f32": ["gemm_f32.hip", "common.hpp"],
-    "linear": ["gemm_f32.hip", "common.hpp"],
-    "gemm_f16f32": ["gemm_f16.hip", "common.hpp"],
-    "gemm_bf16f32": ["gemm_f16.hip", "common.hpp"],
-    "linear_nt": ["gemm_f32.hip", "common.hpp"],
-    "gemm_f32_batched": ["gemm_f32.hip", "common.hpp"],
-    "gemm_f16f32_nt": ["gemm_f16.hip", "common.hpp"],
+KERNEL_SOURCES = {   # the kernels, and the planner that picks which one runs
+    "gemm_f32": ["gemm_f32.hip", "common.hpp", "api.hip"],
+    "linear": ["gemm_f32.hip", "common.hpp", "api.hip"],
+    "gemm_f16f32": ["gemm_f16.hip", "common.hpp", "api.hip"],
+    "gemm_bf16f32": ["gemm_f16.hip", "common.hpp", "api.hip"],
+    "linear_nt": ["gemm_f32.hip", "common.hpp", "api.hip"],
+    "gemm_f32_batched": ["gemm_f32.hip", "common.hpp", "api.hip"],
+    "gemm_f16f32_nt": ["gemm_f16.hip", "common.hpp", "api.hip"],
 }
 
 
