@@ -529,18 +529,9 @@ gemm_f16_direct_kernel(GemmParams p)
 // 8192^3 fp16 1079 -> 1168 TFLOP/s, bf16 1114 -> 1234, B given N-by-K
 // 1171 -> 1191. A wave that waits to issue a copy no longer idles its SIMD's
 // matrix core, and the 4-wave kernel's 8 spilled registers are gone.
-#ifndef LL_F16_NN_WGM
-#define LL_F16_NN_WGM 2
-#define LL_F16_NN_WGN 4
-#endif
-#ifndef LL_F16_BT_WGM
-#define LL_F16_BT_WGM 2
-#define LL_F16_BT_WGN 4
-#endif
 template <bool BT> struct DirectCfg {
     static constexpr int BK = 64, NBUF = 2;
-    static constexpr int WGM = BT ? LL_F16_BT_WGM : LL_F16_NN_WGM;
-    static constexpr int WGN = BT ? LL_F16_BT_WGN : LL_F16_NN_WGN;
+    static constexpr int WGM = 2, WGN = 4;
 };
 
 using F16_L = F16Tile<256, 256, 64>;

@@ -659,18 +659,10 @@ constexpr int kDirectBkL = 32;
 // K-by-N 2 x 4 (4096^3 138 -> 140 TFLOP/s, 8192^3 139 -> 141); B given
 // N-by-K 2 x 2 (8 waves: 141 -> 129, the next stage's 128-bit operand reads
 // of all eight waves burst into the LDS right after each barrier).
-#ifndef LL_F32_NN_WGM
-#define LL_F32_NN_WGM 2
-#define LL_F32_NN_WGN 4
-#endif
-#ifndef LL_F32_BT_WGM
-#define LL_F32_BT_WGM 2
-#define LL_F32_BT_WGN 2
-#endif
 template <bool BT> struct WaveGridL {
-    static constexpr int M = BT ? LL_F32_BT_WGM : LL_F32_NN_WGM;
-    static constexpr int N = BT ? LL_F32_BT_WGN : LL_F32_NN_WGN;
-    static constexpr int WPE = M * N / 4;
+    static constexpr int M = 2;
+    static constexpr int N = BT ? 2 : 4;
+    static constexpr int WPE = M * N / 4;   // waves per SIMD
 };
 
 template <int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, bool BT, int KS = 1>
