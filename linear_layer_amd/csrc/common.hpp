@@ -163,10 +163,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
 // wave instruction fills one contiguous KiB). Issued as inline assembly so the
 // compiler does not treat it as an LDS store that every later barrier must
 // wait for; the caller counts these copies itself (s_waitcnt vmcnt) before
-// the barrier that publishes them. Lanes masked off by EXEC copy nothing.
+// the barrier that publishes them. Lanes masked off by EXEC copy nothing. One
+// wait state separates the scalar write of M0 from the load that reads it
+// (the compiler's hazard checks do not look inside inline assembly).
 __device__ __forceinline__ void lds_dma_16(const void *src, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(lds_base), "v"(src)
                  : "memory", "m0");
