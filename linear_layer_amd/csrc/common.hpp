@@ -43,6 +43,12 @@ struct GemmParams {
     int sk_block;         // stream-K: workgroups below this run whole tiles, the rest share
 };
 
+// A compile-time flag passed to generic lambdas.
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 // K granularity of a stream-K share: a multiple of every kernel's stage depth.
 constexpr int kSkUnit = 64;
 

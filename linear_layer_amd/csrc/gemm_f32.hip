@@ -403,7 +403,10 @@ gemm_f32_direct_kernel(GemmParams p)
     const uint32_t as_base = lds_addr(&As[slice][0][0]), bs_base = lds_addr(&Bs[slice][0][0]);
 
     // Copy c (A: 0 .. COPIES_A-1, then B) of the stage at k0 into buffer buf.
-    auto copy = [&](int buf, int k0, int c) {
+    // With `interior` (the tile lies inside M and N and K fills whole stages)
+    // every lane's chunk is inside the matrix and no bounds select is needed.
+    auto copy = [&](int buf, int k0, int c, auto interior) {
+        constexpr bool IN = decltype(interior)::value;
         const float *src;
         uint32_t dst;
         if (c < COPIES_A || BT) {
@@ -412,17 +415,25 @@ gemm_f32_direct_kernel(GemmParams p)
             const int v = ((j * RPC) & 15) != 0;
             dst = (is_a ? as_base + buf * (A_STAGE * 4) : bs_base + buf * (B_STAGE * 4)) +
                   (wave * (is_a ? COPIES_A : COPIES_B) + j) * 1024;
-            const bool ok = (is_a ? a_row < M - m0 - j * RPC : bt_row < N - n0 - j * RPC) &&
-                            k0 + ch[v] * 4 < K;
             const int64_t step = (int64_t)(j * RPC) * (is_a ? p.lda : p.ldb) + k0;
-            src = ok ? (is_a ? a_src[v] : bt_src[v]) + step : zero_chunk<float>();
+            const float *in = (is_a ? a_src[v] : bt_src[v]) + step;
+            if constexpr (IN) {
+                src = in;
+            } else {
+                const bool ok = (is_a ? a_row < M - m0 - j * RPC : bt_row < N - n0 - j * RPC) &&
+                                k0 + ch[v] * 4 < K;
+                src = ok ? in : zero_chunk<float>();
+            }
         } else {
             const int j = c - COPIES_A;
             const int kr0 = (wave * COPIES_B + j) * RB;
             const int v = (kr0 & 8) != 0;
             dst = bs_base + buf * (B_STAGE * 4) + (wave * COPIES_B + j) * 1024;
-            const bool ok = k0 + kr0 + b_r < K && b_ok[v];
-            src = ok ? b_src[v] + (int64_t)(k0 + kr0) * p.ldb : zero_chunk<float>();
+            const float *in = b_src[v] + (int64_t)(k0 + kr0) * p.ldb;
+            if constexpr (IN)
+                src = in;
+            else
+                src = k0 + kr0 + b_r < K && b_ok[v] ? in : zero_chunk<float>();
         }
         lds_dma_16(src, dst);
     };
@@ -495,11 +506,14 @@ gemm_f32_direct_kernel(GemmParams p)
     };
 
     const int nk = (k_steps + BK - 1) / BK;   // the same in every slice
+    // The pipeline, instantiated for interior tiles and for edge tiles (both
+    // run the same barriers, so slices taking different ones stay in step).
+    auto pipeline = [&](auto interior) {
     for (int st = 0; st < NBUF; ++st)
         if (st < nk) {
 #pragma unroll
             for (int c = 0; c < PER_STAGE; ++c)
-                copy(st, st * BK, c);
+                copy(st, st * BK, c, interior);
         }
     wait_stages((nk < NBUF ? nk : NBUF) - 1);   // stage 0 has landed
     __syncthreads();
@@ -568,7 +582,7 @@ gemm_f32_direct_kernel(GemmParams p)
 #pragma unroll
                 for (int g = 0; g < G; ++g)
                     if (fm * G + g < PER_STAGE)
-                        copy(buf, k_next, fm * G + g);
+                        copy(buf, k_next, fm * G + g, interior);
             }
         }
         if (NW * KS > 4)
@@ -586,6 +600,21 @@ gemm_f32_direct_kernel(GemmParams p)
             }
         }
         buf = nbuf;
+    }
+    };
+    // The interior instance measured faster for every tile but 256x128 (two
+    // workgroups per CU), whose interior loop scheduled its LDS reads worse:
+    // 4096^3 141 -> 146 TFLOP/s, 2048^3 as two K-slices 123 -> 130, 1024^3 85
+    // -> 90, but the 2047x11008 layer on 256x128 tiles 131 -> 122.
+    constexpr bool FAST = !(BM == 256 && BN == 128);
+    const bool interior = m0 + BM <= M && n0 + BN <= N && K == nk * BK;
+    if constexpr (FAST) {
+        if (interior)
+            pipeline(BoolTag<true>{});
+        else
+            pipeline(BoolTag<false>{});
+    } else {
+        pipeline(BoolTag<false>{});
     }
 
     if constexpr (KS > 1) {

@@ -377,6 +377,22 @@ def test_split_k_integer_exact(S, split):
     assert_exact(run_linear(X, W, b, 1), R, f"linear int split {S}")
 
 
+@pytest.mark.parametrize("t", T32)
+@pytest.mark.parametrize("N", [512, 516])
+def test_interior_and_edge_tiles_exact(t, N, tile):
+    """Whole tiles (the copy path without bounds selects) beside ragged ones in
+    one launch (N = 516: a last tile column 4 wide); integer inputs, exact."""
+    tile(F32, t)
+    M, K = 512, 256
+    A, B, C = wl.integers((M, K), 170, -2, 2), wl.integers((K, N), 171, -2, 2), wl.integers((M, N), 172, -4, 4)
+    R, _ = oracle.gemm(np32(A), np32(B), 1.5, 0.5, np32(C))
+    assert_exact(run_gemm_f32(A, B, 1.5, 0.5, C), R, f"tile {t} N={N}")
+    assert_exact(run_nt(ll.gemm_f32_nt, A, B.t().contiguous(), 1.5, 0.5, C), R, f"tile {t} N={N} nt")
+    b = wl.integers((N,), 173, -4, 4)
+    R, _ = oracle.linear(np32(A), np32(B), np32(b), 1)
+    assert_exact(run_linear(A, B, b, 1), R, f"linear tile {t} N={N}")
+
+
 @pytest.mark.parametrize("t", [4, 5])
 @pytest.mark.parametrize("K", [1, 40, 96, 97, 1000])
 @pytest.mark.parametrize("S", [1, 3])
