@@ -300,7 +300,11 @@ gemm_f16_kernel(GemmParams p)
 // The workgroup is a WGM x WGN grid of waves, each owning a (256/WGM) x
 // (256/WGN) block: 2 x 2 runs one wave per SIMD; with 8 waves, two per SIMD,
 // one wave's MFMAs can run while the other waits to issue its copies.
-template <int EPI, bool BF16, bool BT, int BK, int NBUF, int WGM, int WGN>
+//
+// IN (interior): launched only when every tile lies inside M and N and every
+// workgroup's K range is a whole number of stages; the copies then need no
+// bounds selects.
+template <int EPI, bool BF16, bool BT, int BK, int NBUF, int WGM, int WGN, bool IN>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 gemm_f16_direct_kernel(GemmParams p)
@@ -378,14 +382,24 @@ gemm_f16_direct_kernel(GemmParams p)
             const int v = ((j * RPC) & 15) != 0;
             dst = (is_a ? as_base + buf * (A_STAGE * 2) : bs_base + buf * (B_STAGE * 2)) +
                   (wave * COPIES_A + j) * 1024;
-            const bool ok = r_lane + j * RPC < (is_a ? M - m0 : N - n0) && k0 + ch[v] * 8 < K;
             const int64_t step = (int64_t)(j * RPC) * (is_a ? p.lda : p.ldb) + k0;
-            src = ok ? (is_a ? a_src[v] : bt_src[v]) + step : zero_chunk<uint16_t>();
+            const uint16_t *in = (is_a ? a_src[v] : bt_src[v]) + step;
+            if constexpr (IN) {
+                src = in;
+            } else {
+                const bool ok = r_lane + j * RPC < (is_a ? M - m0 : N - n0) && k0 + ch[v] * 8 < K;
+                src = ok ? in : zero_chunk<uint16_t>();
+            }
         } else {
             const int j = c - COPIES_A;
             dst = bs_base + buf * (B_STAGE * 2) + (wave * COPIES_B + j) * 1024;
-            const bool ok = k0 + (wave * COPIES_B + j) * 2 + (lane >> 5) < K && b_col_ok[j];
-            src = ok ? b_src[j] + (int64_t)k0 * p.ldb : zero_chunk<uint16_t>();
+            const uint16_t *in = b_src[j] + (int64_t)k0 * p.ldb;
+            if constexpr (IN)
+                src = in;
+            else
+                src = k0 + (wave * COPIES_B + j) * 2 + (lane >> 5) < K && b_col_ok[j]
+                          ? in
+                          : zero_chunk<uint16_t>();
         }
         lds_dma_16(src, dst);
     };
@@ -584,9 +598,17 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
         return hipErrorInvalidValue;   // the 16-bit kernels run whole grids only
     using Cfg = DirectCfg<BT>;
     const dim3 grid = gemm_grid(p, ntiles), block(64 * Cfg::WGM * Cfg::WGN);
+    // every copy inside the matrices: whole tiles, whole stages in every K range
+    const bool in = p.M % 256 == 0 && p.N % 256 == 0 && p.K % Cfg::BK == 0 && p.k_split % Cfg::BK == 0;
 #define LL_DIRECT(E) \
-    hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF, Cfg::WGM, Cfg::WGN>), \
-                       grid, block, 0, s, p)
+    do { \
+        if (in) \
+            hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF, Cfg::WGM, \
+                                                       Cfg::WGN, true>), grid, block, 0, s, p); \
+        else \
+            hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF, Cfg::WGM, \
+                                                       Cfg::WGN, false>), grid, block, 0, s, p); \
+    } while (0)
     if (epi == EPI_GEMM_BETA0)
         LL_DIRECT(EPI_GEMM_BETA0);
     else if (epi == EPI_GEMM_BETA)

@@ -306,8 +306,13 @@ gemm_f32_kernel(GemmParams p)
 // slice order and slice 0 writes the result: K split without atomics, extra
 // passes or a second launch, and with KS times the waves to hide each
 // stage's load latency.
+//
+// IN (interior): launched only when every tile lies inside M and N and every
+// workgroup's (and slice's) K range is a whole number of stages, so every
+// lane's chunk is inside the matrix and the copies need no bounds selects
+// (about a quarter of the per-stage VALU work).
 template <int EPI, int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, int KS, bool BT,
-          bool SK>
+          bool SK, bool IN>
 __global__ void __launch_bounds__(64 * WGM * WGN * KS) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f32_direct_kernel(GemmParams p)
 {
@@ -403,10 +408,7 @@ gemm_f32_direct_kernel(GemmParams p)
     const uint32_t as_base = lds_addr(&As[slice][0][0]), bs_base = lds_addr(&Bs[slice][0][0]);
 
     // Copy c (A: 0 .. COPIES_A-1, then B) of the stage at k0 into buffer buf.
-    // With `interior` (the tile lies inside M and N and K fills whole stages)
-    // every lane's chunk is inside the matrix and no bounds select is needed.
-    auto copy = [&](int buf, int k0, int c, auto interior) {
-        constexpr bool IN = decltype(interior)::value;
+    auto copy = [&](int buf, int k0, int c) {
         const float *src;
         uint32_t dst;
         if (c < COPIES_A || BT) {
@@ -506,14 +508,11 @@ gemm_f32_direct_kernel(GemmParams p)
     };
 
     const int nk = (k_steps + BK - 1) / BK;   // the same in every slice
-    // The pipeline, instantiated for interior tiles and for edge tiles (both
-    // run the same barriers, so slices taking different ones stay in step).
-    auto pipeline = [&](auto interior) {
     for (int st = 0; st < NBUF; ++st)
         if (st < nk) {
 #pragma unroll
             for (int c = 0; c < PER_STAGE; ++c)
-                copy(st, st * BK, c, interior);
+                copy(st, st * BK, c);
         }
     wait_stages((nk < NBUF ? nk : NBUF) - 1);   // stage 0 has landed
     __syncthreads();
@@ -582,7 +581,7 @@ gemm_f32_direct_kernel(GemmParams p)
 #pragma unroll
                 for (int g = 0; g < G; ++g)
                     if (fm * G + g < PER_STAGE)
-                        copy(buf, k_next, fm * G + g, interior);
+                        copy(buf, k_next, fm * G + g);
             }
         }
         if (NW * KS > 4)
@@ -600,21 +599,6 @@ gemm_f32_direct_kernel(GemmParams p)
             }
         }
         buf = nbuf;
-    }
-    };
-    // The interior instance measured faster for every tile but 256x128 (two
-    // workgroups per CU), whose interior loop scheduled its LDS reads worse:
-    // 4096^3 141 -> 146 TFLOP/s, 2048^3 as two K-slices 123 -> 130, 1024^3 85
-    // -> 90, but the 2047x11008 layer on 256x128 tiles 131 -> 122.
-    constexpr bool FAST = !(BM == 256 && BN == 128);
-    const bool interior = m0 + BM <= M && n0 + BN <= N && K == nk * BK;
-    if constexpr (FAST) {
-        if (interior)
-            pipeline(BoolTag<true>{});
-        else
-            pipeline(BoolTag<false>{});
-    } else {
-        pipeline(BoolTag<false>{});
     }
 
     if constexpr (KS > 1) {
@@ -694,13 +678,31 @@ template <bool BT> struct WaveGridL {
     static constexpr int WPE = M * N / 4;   // waves per SIMD
 };
 
+// Whether every copy of a launch of tile BMxBN (KS K-slices of stages of BK)
+// lies inside the matrices: tiles inside M and N, and every workgroup's and
+// slice's K range a whole number of stages (stream-K shares in units of
+// kSkUnit, a multiple of BK).
+static bool interior_launch(const GemmParams &p, int BM, int BN, int BK, int KS)
+{
+    const int kq = KS * BK;
+    return p.M % BM == 0 && p.N % BN == 0 && p.K % kq == 0 && p.k_split % kq == 0 &&
+           (p.sk_tiles == 0 || (KS == 1 && p.K % kSkUnit == 0 && kSkUnit % BK == 0));
+}
+
 template <int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, bool BT, int KS = 1>
 static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hipStream_t s)
 {
     const dim3 grid = gemm_grid(p, ntiles), block(64 * WGM * WGN * KS);
+    const bool in = interior_launch(p, BM, BN, BK, KS);
 #define LL_F32_DIRECT(E, SK) \
-    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, KS, BT, SK>), \
-                       grid, block, 0, s, p)
+    do { \
+        if (in) \
+            hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, KS, BT, SK, \
+                                                       true>), grid, block, 0, s, p); \
+        else \
+            hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, KS, BT, SK, \
+                                                       false>), grid, block, 0, s, p); \
+    } while (0)
     if (KS > 1 && p.sk_tiles > 0)
         return hipErrorInvalidValue;
     if constexpr (KS > 1) {

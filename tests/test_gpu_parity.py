@@ -379,18 +379,38 @@ def test_split_k_integer_exact(S, split):
 
 @pytest.mark.parametrize("t", T32)
 @pytest.mark.parametrize("N", [512, 516])
-def test_interior_and_edge_tiles_exact(t, N, tile):
-    """Whole tiles (the copy path without bounds selects) beside ragged ones in
-    one launch (N = 516: a last tile column 4 wide); integer inputs, exact."""
+@pytest.mark.parametrize("S", [1, 2])
+def test_interior_and_edge_tiles_exact(t, N, S, tile, split):
+    """N = 512: every tile whole, so the launch takes the kernel whose copies
+    need no bounds selects (also with K split in two); N = 516: a ragged last
+    tile column, the checked kernel. Integer inputs, exact."""
     tile(F32, t)
-    M, K = 512, 256
+    split(S)
+    M, K = 512, 512
     A, B, C = wl.integers((M, K), 170, -2, 2), wl.integers((K, N), 171, -2, 2), wl.integers((M, N), 172, -4, 4)
     R, _ = oracle.gemm(np32(A), np32(B), 1.5, 0.5, np32(C))
-    assert_exact(run_gemm_f32(A, B, 1.5, 0.5, C), R, f"tile {t} N={N}")
+    assert_exact(run_gemm_f32(A, B, 1.5, 0.5, C), R, f"tile {t} N={N} split {S}")
     assert_exact(run_nt(ll.gemm_f32_nt, A, B.t().contiguous(), 1.5, 0.5, C), R, f"tile {t} N={N} nt")
     b = wl.integers((N,), 173, -4, 4)
     R, _ = oracle.linear(np32(A), np32(B), np32(b), 1)
-    assert_exact(run_linear(A, B, b, 1), R, f"linear tile {t} N={N}")
+    assert_exact(run_linear(A, B, b, 1), R, f"linear tile {t} N={N} split {S}")
+
+
+@pytest.mark.parametrize("N", [512, 520])
+def test_16bit_interior_and_edge_tiles_exact(N):
+    """16-bit direct kernel: whole 256x256 tiles (no bounds selects) or a ragged
+    last column; both B layouts; integer inputs, exact."""
+    M, K = 512, 256
+    for bf in (False, True):
+        dt = torch.bfloat16 if bf else torch.float16
+        A8, B8 = wl.integers((M, K), 174, -8, 8), wl.integers((K, N), 175, -8, 8)
+        R, _ = oracle.gemm(np32(A8), np32(B8))
+        fn, fn_nt = (ll.gemm_bf16f32, ll.gemm_bf16f32_nt) if bf else (ll.gemm_f16f32, ll.gemm_f16f32_nt)
+        Cd = torch.full((M, N), float("nan"), device=DEV)
+        fn(A8.to(dt).to(DEV), B8.to(dt).to(DEV), Cd)
+        torch.cuda.synchronize()
+        assert_exact(np32(Cd), R, f"16-bit bf16={bf} N={N}")
+        assert_exact(run_nt(fn_nt, A8.to(dt), B8.t().contiguous().to(dt)), R, f"16-bit nt bf16={bf} N={N}")
 
 
 @pytest.mark.parametrize("t", [4, 5])
