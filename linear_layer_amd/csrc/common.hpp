@@ -43,11 +43,8 @@ struct GemmParams {
     int sk_block;         // stream-K: workgroups below this run whole tiles, the rest share
 };
 
-// A compile-time flag passed to generic lambdas.
-template <bool B>
-struct BoolTag {
-    static constexpr bool value = B;
-};
+// Bounds a direct kernel's copies check (a template mask; see the launchers).
+enum : int { CHK_M = 1, CHK_N = 2, CHK_K = 4 };
 
 // K granularity of a stream-K share: a multiple of every kernel's stage depth.
 constexpr int kSkUnit = 64;

@@ -307,12 +307,14 @@ gemm_f32_kernel(GemmParams p)
 // passes or a second launch, and with KS times the waves to hide each
 // stage's load latency.
 //
-// IN (interior): launched only when every tile lies inside M and N and every
-// workgroup's (and slice's) K range is a whole number of stages, so every
-// lane's chunk is inside the matrix and the copies need no bounds selects
-// (about a quarter of the per-stage VALU work).
+// CHK: which bounds the copies check (CHK_M: rows of A, CHK_N: columns of B,
+// or rows given N-by-K, CHK_K: the K range). The launcher leaves out a check
+// when every copy of the launch passes it: tiles inside M, or N, and every
+// workgroup's (and slice's) K range a whole number of stages. An unchecked
+// copy needs no select: interior launches save about a quarter of the
+// per-stage VALU work.
 template <int EPI, int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, int KS, bool BT,
-          bool SK, bool IN>
+          bool SK, int CHK>
 __global__ void __launch_bounds__(64 * WGM * WGN * KS) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f32_direct_kernel(GemmParams p)
 {
@@ -419,11 +421,13 @@ gemm_f32_direct_kernel(GemmParams p)
                   (wave * (is_a ? COPIES_A : COPIES_B) + j) * 1024;
             const int64_t step = (int64_t)(j * RPC) * (is_a ? p.lda : p.ldb) + k0;
             const float *in = (is_a ? a_src[v] : bt_src[v]) + step;
-            if constexpr (IN) {
+            const bool row_chk = is_a ? (CHK & CHK_M) != 0 : (CHK & CHK_N) != 0;
+            if (!row_chk && !(CHK & CHK_K)) {
                 src = in;
             } else {
-                const bool ok = (is_a ? a_row < M - m0 - j * RPC : bt_row < N - n0 - j * RPC) &&
-                                k0 + ch[v] * 4 < K;
+                const bool ok =
+                    (!row_chk || (is_a ? a_row < M - m0 - j * RPC : bt_row < N - n0 - j * RPC)) &&
+                    (!(CHK & CHK_K) || k0 + ch[v] * 4 < K);
                 src = ok ? in : zero_chunk<float>();
             }
         } else {
@@ -432,10 +436,12 @@ gemm_f32_direct_kernel(GemmParams p)
             const int v = (kr0 & 8) != 0;
             dst = bs_base + buf * (B_STAGE * 4) + (wave * COPIES_B + j) * 1024;
             const float *in = b_src[v] + (int64_t)(k0 + kr0) * p.ldb;
-            if constexpr (IN)
+            if constexpr (!(CHK & (CHK_N | CHK_K)))
                 src = in;
             else
-                src = k0 + kr0 + b_r < K && b_ok[v] ? in : zero_chunk<float>();
+                src = (!(CHK & CHK_K) || k0 + kr0 + b_r < K) && (!(CHK & CHK_N) || b_ok[v])
+                          ? in
+                          : zero_chunk<float>();
         }
         lds_dma_16(src, dst);
     };
@@ -678,30 +684,41 @@ template <bool BT> struct WaveGridL {
     static constexpr int WPE = M * N / 4;   // waves per SIMD
 };
 
-// Whether every copy of a launch of tile BMxBN (KS K-slices of stages of BK)
-// lies inside the matrices: tiles inside M and N, and every workgroup's and
-// slice's K range a whole number of stages (stream-K shares in units of
-// kSkUnit, a multiple of BK).
-static bool interior_launch(const GemmParams &p, int BM, int BN, int BK, int KS)
+// The bounds checks a launch of tile BMxBN (KS K-slices of stages of BK)
+// needs: rows of A unless the tiles lie inside M; the N bound unless inside
+// N; the K bound unless every workgroup's and slice's K range is a whole
+// number of stages (stream-K shares are whole kSkUnit units, a multiple of
+// BK). Instances exist for none, M only (B given K-by-N: the 2047x11008 layer
+// 134.3 -> 137.9 TFLOP/s; given N-by-K it measured 1.4 % slower than all
+// three), and all three.
+static int launch_checks(const GemmParams &p, int BM, int BN, int BK, int KS, bool b_trans)
 {
     const int kq = KS * BK;
-    return p.M % BM == 0 && p.N % BN == 0 && p.K % kq == 0 && p.k_split % kq == 0 &&
-           (p.sk_tiles == 0 || (KS == 1 && p.K % kSkUnit == 0 && kSkUnit % BK == 0));
+    const bool k_whole = p.K % kq == 0 && p.k_split % kq == 0 &&
+                         (p.sk_tiles == 0 || (KS == 1 && p.K % kSkUnit == 0 && kSkUnit % BK == 0));
+    if (p.N % BN != 0 || !k_whole)
+        return CHK_M | CHK_N | CHK_K;
+    if (p.M % BM == 0)
+        return 0;
+    return b_trans ? CHK_M | CHK_N | CHK_K : CHK_M;
 }
 
 template <int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, bool BT, int KS = 1>
 static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hipStream_t s)
 {
     const dim3 grid = gemm_grid(p, ntiles), block(64 * WGM * WGN * KS);
-    const bool in = interior_launch(p, BM, BN, BK, KS);
+    const int chk = launch_checks(p, BM, BN, BK, KS, BT);
+#define LL_F32_DIRECT_C(E, SK, C) \
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, KS, BT, SK, C>), \
+                       grid, block, 0, s, p)
 #define LL_F32_DIRECT(E, SK) \
     do { \
-        if (in) \
-            hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, KS, BT, SK, \
-                                                       true>), grid, block, 0, s, p); \
+        if (chk == 0) \
+            LL_F32_DIRECT_C(E, SK, 0); \
+        else if (chk == CHK_M) \
+            LL_F32_DIRECT_C(E, SK, CHK_M); \
         else \
-            hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, KS, BT, SK, \
-                                                       false>), grid, block, 0, s, p); \
+            LL_F32_DIRECT_C(E, SK, CHK_M | CHK_N | CHK_K); \
     } while (0)
     if (KS > 1 && p.sk_tiles > 0)
         return hipErrorInvalidValue;
@@ -723,6 +740,7 @@ static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hi
         else LL_F32_DIRECT(EPI_ATOMIC, false);
     }
 #undef LL_F32_DIRECT
+#undef LL_F32_DIRECT_C
     return hipGetLastError();
 }
 

@@ -378,22 +378,23 @@ def test_split_k_integer_exact(S, split):
 
 
 @pytest.mark.parametrize("t", T32)
-@pytest.mark.parametrize("N", [512, 516])
+@pytest.mark.parametrize("M,N", [(512, 512), (500, 512), (512, 516)])
 @pytest.mark.parametrize("S", [1, 2])
-def test_interior_and_edge_tiles_exact(t, N, S, tile, split):
-    """N = 512: every tile whole, so the launch takes the kernel whose copies
-    need no bounds selects (also with K split in two); N = 516: a ragged last
-    tile column, the checked kernel. Integer inputs, exact."""
+def test_interior_and_edge_tiles_exact(t, M, N, S, tile, split):
+    """512 x 512: every tile whole, so the launch takes the kernel whose copies
+    need no bounds selects (also with K split in two); M = 500: only A's rows
+    checked (B given K-by-N); N = 516: a ragged last tile column, every bound
+    checked. Integer inputs, exact."""
     tile(F32, t)
     split(S)
-    M, K = 512, 512
+    K = 512
     A, B, C = wl.integers((M, K), 170, -2, 2), wl.integers((K, N), 171, -2, 2), wl.integers((M, N), 172, -4, 4)
     R, _ = oracle.gemm(np32(A), np32(B), 1.5, 0.5, np32(C))
-    assert_exact(run_gemm_f32(A, B, 1.5, 0.5, C), R, f"tile {t} N={N} split {S}")
-    assert_exact(run_nt(ll.gemm_f32_nt, A, B.t().contiguous(), 1.5, 0.5, C), R, f"tile {t} N={N} nt")
+    assert_exact(run_gemm_f32(A, B, 1.5, 0.5, C), R, f"tile {t} {M}x{N} split {S}")
+    assert_exact(run_nt(ll.gemm_f32_nt, A, B.t().contiguous(), 1.5, 0.5, C), R, f"tile {t} {M}x{N} nt")
     b = wl.integers((N,), 173, -4, 4)
     R, _ = oracle.linear(np32(A), np32(B), np32(b), 1)
-    assert_exact(run_linear(A, B, b, 1), R, f"linear tile {t} N={N} split {S}")
+    assert_exact(run_linear(A, B, b, 1), R, f"linear tile {t} {M}x{N} split {S}")
 
 
 @pytest.mark.parametrize("N", [512, 520])
