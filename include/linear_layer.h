@@ -207,6 +207,12 @@ const char *ll_status_string(int status);
  * then applies the ReLU in a pass afterwards). The result is the same sum in
  * a different, run-dependent order; it still allocates nothing.
  *
+ * Two FP32 shapes split K inside the workgroup instead ("K-sliced" tiles,
+ * named *_k4 and *_k2): the workgroup's slices sum disjoint stage-aligned
+ * K ranges and add their partial tiles through on-chip memory in a fixed
+ * order, so the result does not depend on the run; no atomics, no extra
+ * pass. They serve problems too small to fill the device (e.g. 1024^3).
+ *
  * These calls let a benchmark or a caller pin the choice. They touch only
  * host memory and never the GPU.
  */
