@@ -221,7 +221,8 @@ const char *ll_status_string(int status);
 /* Flags the ll_chosen_* queries accept OR-ed into `dtype`:
  * LL_PLAN_RELU: linear_bias_act with the ReLU, whose K-split and stream-K
  * plans pay for one more pass over Y (LL_DTYPE_F32 only);
- * LL_PLAN_B_NK: the _nt form (B given N-by-K). */
+ * LL_PLAN_B_NK: the _nt form (B given N-by-K; accepted for callers that
+ * describe the call fully, the plans do not currently depend on it). */
 #define LL_PLAN_RELU 0x100
 #define LL_PLAN_B_NK 0x200
 
@@ -254,8 +255,7 @@ int ll_chosen_split_k(int dtype, int M, int N, int K, int batch, int num_cus);
  * the ReLU applied afterwards). Like a K-split, this makes the summation
  * order of those tiles run-dependent (still within the error bound; integer
  * inputs stay exact); it allocates nothing.
- *   ll_set_stream_k: -1 automatic (default; for the _nt forms not on the
- *   256x256 tile, where it measured slower), 0 never, 1 whenever the shape
+ *   ll_set_stream_k: -1 automatic (default), 0 never, 1 whenever the shape
  *   allows it (a forced K-split takes precedence; K-sliced tiles never
  *   share out). Returns LL_OK or LL_ERR_INVALID_VALUE.
  *   ll_chosen_stream_k: the number of tiles the plan shares out (0: none),

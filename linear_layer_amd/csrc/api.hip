@@ -178,19 +178,11 @@ struct Plan {
 
 std::atomic<int> g_sk_override{-1};   // -1 automatic, 0 never, 1 whenever possible
 
-// Whether a plan may share tiles out with stream-K on tile shape `ti`. It
-// needs the direct kernels (128-bit-aligned operands) and no K-slices. With B
-// given N-by-K the automatic choice leaves the 256x256 tile out: on the
-// 2047x11008x4096 layer its shared-out phase ran at about three quarters of
-// its whole-tile rate (122.5 TFLOP/s in all), while 256x128 tiles with
-// stream-K reached 132.4 (and 120.0 without). Forcing stream-K (mode 1)
-// still allows every tile.
-bool sk_tile_ok(const TileInfo &ti, bool b_trans)
+// Whether a plan may share tiles out with stream-K on tile shape `ti`: it
+// needs the direct kernels (128-bit-aligned operands) and no K-slices.
+bool sk_tile_ok(const TileInfo &ti)
 {
-    if (ti.k_slices != 1)
-        return false;
-    return !(b_trans && ti.bm == 256 && ti.bn == 256) ||
-           g_sk_override.load(std::memory_order_relaxed) == 1;
+    return ti.k_slices == 1;
 }
 
 // Choose the tile shape and the number of K-splits minimising the estimate:
@@ -201,7 +193,7 @@ bool sk_tile_ok(const TileInfo &ti, bool b_trans)
 // A split costs a pre-pass over C (beta*C, or the bias), the atomic traffic of
 // every split's partial tile and, for ReLU, a pass afterwards.
 Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int cus, bool relu,
-          int batch = 1, bool allow_sk = false, bool b_trans = false)
+          int batch = 1, bool allow_sk = false)
 {
     const int items = batch < kMaxGridZ ? batch : kMaxGridZ;   // items per launch
     const int t_ov = g_tile_override[dtype].load(std::memory_order_relaxed);
@@ -245,7 +237,7 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
         // tiles' k-units are shared out evenly over one round of workgroups,
         // which add their partial sums atomically (framed by a pass that
         // prepares those tiles and, for ReLU, one that finishes them).
-        if (allow_sk && sk_tile_ok(ti, b_trans)) {
+        if (allow_sk && sk_tile_ok(ti)) {
             const int64_t slots = (int64_t)cus * ti.wg_per_cu;
             const int64_t rounds = tiles_mn / slots, rest = tiles_mn - rounds * slots;
             const int64_t units = ((int64_t)K + kSkUnit - 1) / kSkUnit;
@@ -417,7 +409,7 @@ static int gemm_f32_impl(int M, int N, int K, float alpha, const float *A, int l
                      batch_aligned(bat, 4);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     const Plan pl =
-        plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false, bat.count, vec, bt);
+        plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false, bat.count, vec);
     return launch_status(run_gemm(p, pl, vec, s, bt ? launch_gemm_f32_bt : launch_gemm_f32, 4, bat,
                                   &kF32Tiles[pl.tile]));
 }
@@ -539,7 +531,7 @@ static int linear_impl(int M, int N, int K, const float *X, int ldx, const float
     p.act = act;
     const launch_fn launch = wt ? launch_gemm_f32_bt : launch_gemm_f32;
     const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU, 1,
-                         vec, wt);
+                         vec);
     if (pl.sk_grid > 0)
         return launch_status(run_stream_k(p, pl, kF32Tiles[pl.tile], EPI_LINEAR, TILE_BIAS,
                                           act == LL_ACT_RELU, vec, s, launch));
@@ -612,14 +604,14 @@ const char *ll_tile_name(int dtype, int tile)
 static Plan chosen_plan(int dtype, int M, int N, int K, int batch, int num_cus, bool *ok)
 {
     const int base = dtype & 0xff, flags = dtype & ~0xff;
-    const bool relu = flags & LL_PLAN_RELU, b_nk = flags & LL_PLAN_B_NK;
+    const bool relu = flags & LL_PLAN_RELU;   // LL_PLAN_B_NK: accepted, plans alike
     *ok = (base == LL_DTYPE_F32 || (base == LL_DTYPE_F16 && !relu)) &&
           (flags & ~(LL_PLAN_RELU | LL_PLAN_B_NK)) == 0 && batch >= 1;
     if (!*ok)
         return Plan{-1, -1, 0};
     const int cus = num_cus > 0 ? num_cus : 256;
     if (base == LL_DTYPE_F32)
-        return plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, relu, batch, true, b_nk);
+        return plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, relu, batch, true);
     return plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch);
 }
 

@@ -673,14 +673,13 @@ constexpr int kDirectNbufL = 2, kDirectNbufM = 2;
 // Stage depth of the 256x256 tile: 32 (two 64 KiB stages), so each row-panel
 // copy reads whole 128-byte lines; the other tiles keep 16.
 constexpr int kDirectBkL = 32;
-// Wave grid of the 256x256 tile, per B layout: 2 x 2 (one wave per SIMD,
-// 128x128 each) or 8 waves (two per SIMD). Measured in one process: B given
-// K-by-N 2 x 4 (4096^3 138 -> 140 TFLOP/s, 8192^3 139 -> 141); B given
-// N-by-K 2 x 2 (8 waves: 141 -> 129, the next stage's 128-bit operand reads
-// of all eight waves burst into the LDS right after each barrier).
+// Wave grid of the 256x256 tile: 2 x 4, eight waves (two per SIMD, 128x64
+// each), for both B layouts. Against 2 x 2 (one wave per SIMD), measured in
+// one process: B given K-by-N 4096^3 138 -> 140 TFLOP/s, 8192^3 139 -> 141;
+// B given N-by-K 4096^3 144 either way (with bounds-checked copies eight
+// waves lost, 141 -> 129), the 2047x11008 layer with stream-K 132.4 -> 133.7.
 template <bool BT> struct WaveGridL {
-    static constexpr int M = 2;
-    static constexpr int N = BT ? 2 : 4;
+    static constexpr int M = 2, N = 4;
     static constexpr int WPE = M * N / 4;   // waves per SIMD
 };
 

@@ -246,24 +246,21 @@ def test_plan_query_flags():
     shape = (2047, 11008, 4096, 256)
     # the fused layer with ReLU still shares out the 88 leftover tiles
     assert ll.chosen_stream_k(f32 | relu, *shape) == 88
-    # B given N-by-K: stream-K on 256x128 tiles (688 tiles, 512 slots: 176
-    # shared out); 256x256 tiles share out only when forced
-    assert ll.tile_name(f32, ll.chosen_tile(f32 | relu | nk, *shape)) == "f32_256x128"
-    assert ll.chosen_stream_k(f32 | nk, *shape) == 176
-    assert ll.chosen_stream_k(f32 | relu | nk, *shape) == 176
+    # B given N-by-K plans alike
+    assert ll.tile_name(f32, ll.chosen_tile(f32 | relu | nk, *shape)) == "f32_256x256"
+    assert ll.chosen_stream_k(f32 | nk, *shape) == 88
+    assert ll.chosen_stream_k(f32 | relu | nk, *shape) == 88
     ll.set_stream_k(0)
     try:
         assert ll.chosen_stream_k(f32 | nk, *shape) == 0
         assert ll.tile_name(f32, ll.chosen_tile(f32 | nk, *shape)) == "f32_256x128"
     finally:
         ll.set_stream_k(-1)
-    ll.set_tile(f32, 0)
+    # 256x128 tiles: 688 tiles on 512 slots, 176 shared out
+    ll.set_tile(f32, 1)
     try:
-        assert ll.chosen_stream_k(f32 | nk, *shape) == 0
-        ll.set_stream_k(1)
-        assert ll.chosen_stream_k(f32 | nk, *shape) == 88
+        assert ll.chosen_stream_k(f32 | relu | nk, *shape) == 176
     finally:
-        ll.set_stream_k(-1)
         ll.set_tile(f32, -1)
     # 16-bit: the layout flag is accepted, the ReLU flag (no 16-bit layer) is not
     assert ll.chosen_tile(f16 | nk, 8192, 8192, 8192, 256) == 0
