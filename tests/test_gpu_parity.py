@@ -696,9 +696,17 @@ def test_batched_small(which, trans_b, nb, M, N, K):
 
 
 @pytest.mark.parametrize("t", T32)
-def test_batched_f32_every_tile(t, tile):
+@pytest.mark.parametrize("M,N,K", [(300, 264, 136), (256, 256, 256)])
+def test_batched_f32_every_tile(t, M, N, K, tile):
+    """(256, 256, 256): whole tiles, the kernels without bounds selects, on
+    every item of the batch (integer inputs, exact)."""
     tile(F32, t)
-    nb, M, N, K = 5, 300, 264, 136
+    nb = 5
+    if M % 256 == 0:
+        A, B = wl.integers((nb, M, K), 116, -2, 2), wl.integers((nb, K, N), 117, -2, 2)
+        R, _ = oracle_batched(A, B, "f32")
+        assert_exact(run_batched(ll.gemm_f32_batched, A, B), R, f"f32 batched tile {t} whole tiles")
+        return
     A, B = rand((nb, M, K), 114), rand((nb, K, N), 115)
     got = run_batched(ll.gemm_f32_batched, A, B)
     R, T = oracle_batched(A, B, "f32")
