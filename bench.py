@@ -33,12 +33,12 @@ COPY_BYTES = 256 << 20
 PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "linear_nt": 157.3, "gemm_f32_batched": 157.3,
                "gemm_f16f32": 2516.6, "gemm_bf16f32": 2516.6, "gemm_f16f32_nt": 2516.6}
 KERNEL_SOURCES = {   # the kernels, and the planner that picks which one runs
-    "gemm_f32": ["gemm_f32.hip", "common.hpp", "api.hip"],
-    "linear": ["gemm_f32.hip", "common.hpp", "api.hip"],
+    "gemm_f32": ["gemm_f32.hip", "gemm_f32_nt.hip", "common.hpp", "api.hip"],
+    "linear": ["gemm_f32.hip", "gemm_f32_nt.hip", "common.hpp", "api.hip"],
     "gemm_f16f32": ["gemm_f16.hip", "common.hpp", "api.hip"],
     "gemm_bf16f32": ["gemm_f16.hip", "common.hpp", "api.hip"],
-    "linear_nt": ["gemm_f32.hip", "common.hpp", "api.hip"],
-    "gemm_f32_batched": ["gemm_f32.hip", "common.hpp", "api.hip"],
+    "linear_nt": ["gemm_f32.hip", "gemm_f32_nt.hip", "common.hpp", "api.hip"],
+    "gemm_f32_batched": ["gemm_f32.hip", "gemm_f32_nt.hip", "common.hpp", "api.hip"],
     "gemm_f16f32_nt": ["gemm_f16.hip", "common.hpp", "api.hip"],
 }
 

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblinear_layer.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.hip", "gemm_f32.hip", "gemm_f16.hip", "elementwise.hip"]
+SOURCES = ["api.hip", "gemm_f32.hip", "gemm_f32_nt.hip", "gemm_f16.hip", "elementwise.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

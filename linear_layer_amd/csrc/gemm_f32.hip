@@ -787,6 +787,10 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     return hipGetLastError();
 }
 
+// This file builds the instances for B given K-by-N and the tile table; the
+// translation unit gemm_f32_nt.hip includes it with LL_F32_NT_UNIT defined to
+// build the instances for B given N-by-K, so the two compile in parallel.
+#ifndef LL_F32_NT_UNIT
 // {BM, BN, workgroups per CU, relative throughput alone on a CU, with a
 // second workgroup beside it} -- throughputs measured on MI355X relative to
 // the 256x256 tile.
@@ -800,6 +804,7 @@ const TileInfo kF32Tiles[kF32NumTiles] = {
     {F32_XS::BM, F32_XS::BN, 1, 0.57f, 0.57f, "f32_64x64_k4", 4},
     {F32_S::BM, F32_S::BN, 1, 0.90f, 0.90f, "f32_128x128_k2", 2},
 };
+#endif
 
 template <bool BT>
 static hipError_t launch_f32(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
@@ -814,14 +819,16 @@ static hipError_t launch_f32(const GemmParams &p, int tile, int epi, bool vec, h
     }
 }
 
+#ifndef LL_F32_NT_UNIT
 hipError_t launch_gemm_f32(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
 {
     return launch_f32<false>(p, tile, epi, vec, s);
 }
-
+#else
 hipError_t launch_gemm_f32_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
 {
     return launch_f32<true>(p, tile, epi, vec, s);
 }
+#endif
 
 }  // namespace ll
