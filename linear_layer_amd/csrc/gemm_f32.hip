@@ -687,26 +687,23 @@ template <bool BT> struct WaveGridL {
 // needs: rows of A unless the tiles lie inside M; the N bound unless inside
 // N; the K bound unless every workgroup's and slice's K range is a whole
 // number of stages (stream-K shares are whole kSkUnit units, a multiple of
-// BK). Instances exist for none, M only (B given K-by-N: the 2047x11008 layer
-// 134.3 -> 137.9 TFLOP/s; given N-by-K it measured 1.4 % slower than all
-// three), and all three.
-static int launch_checks(const GemmParams &p, int BM, int BN, int BK, int KS, bool b_trans)
+// BK). Instances exist for none, M only (the 2047x11008 layer: 134.3 -> 137.9
+// TFLOP/s with W given K-by-N, 133.4 -> 136.6 given N-by-K), and all three.
+static int launch_checks(const GemmParams &p, int BM, int BN, int BK, int KS)
 {
     const int kq = KS * BK;
     const bool k_whole = p.K % kq == 0 && p.k_split % kq == 0 &&
                          (p.sk_tiles == 0 || (KS == 1 && p.K % kSkUnit == 0 && kSkUnit % BK == 0));
     if (p.N % BN != 0 || !k_whole)
         return CHK_M | CHK_N | CHK_K;
-    if (p.M % BM == 0)
-        return 0;
-    return b_trans ? CHK_M | CHK_N | CHK_K : CHK_M;
+    return p.M % BM == 0 ? 0 : CHK_M;
 }
 
 template <int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, bool BT, int KS = 1>
 static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hipStream_t s)
 {
     const dim3 grid = gemm_grid(p, ntiles), block(64 * WGM * WGN * KS);
-    const int chk = launch_checks(p, BM, BN, BK, KS, BT);
+    const int chk = launch_checks(p, BM, BN, BK, KS);
 #define LL_F32_DIRECT_C(E, SK, C) \
     hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, KS, BT, SK, C>), \
                        grid, block, 0, s, p)
