@@ -193,6 +193,28 @@ __device__ __forceinline__ const T *zero_chunk()
 // this wave are outstanding (expcnt and lgkmcnt left at their maxima).
 #define LL_VMCNT(n) ((((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14)))
 
+// The fused epilogue of one output element: acc is the accumulated product,
+// bv the bias of its column (EPI_LINEAR).
+template <int EPI>
+__device__ __forceinline__ void store_one(const GemmParams &p, float *dst, float v, float bv)
+{
+    if (EPI == EPI_ATOMIC) {
+        // split-K: every split adds its share; C was pre-scaled by beta
+        __hip_atomic_fetch_add(dst, p.alpha * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+    if (EPI == EPI_GEMM_BETA0) {
+        v = p.alpha * v;
+    } else if (EPI == EPI_GEMM_BETA) {
+        v = __builtin_fmaf(p.alpha, v, p.beta * *dst);
+    } else {
+        v = v + bv;
+        if (p.act == 1)
+            v = v > 0.0f ? v : 0.0f;
+    }
+    *dst = v;
+}
+
 // The fused write-back of one 32x32 MFMA accumulator block.
 //
 // Accumulator layout of v_mfma_f32_32x32x* (wave64): lane l holds column
@@ -211,25 +233,29 @@ __device__ __forceinline__ void write_block(const GemmParams &p, const f32x16 &a
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = rbase + ((r >> 2) << 3) + (r & 3);
-        if (row < p.M) {
-            float *dst = p.C + (int64_t)row * p.ldc + col;
-            float v = acc[r];
-            if (EPI == EPI_ATOMIC) {
-                // split-K: every split adds its share; C was pre-scaled by beta
-                __hip_atomic_fetch_add(dst, p.alpha * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                continue;
-            }
-            if (EPI == EPI_GEMM_BETA0) {
-                v = p.alpha * v;
-            } else if (EPI == EPI_GEMM_BETA) {
-                v = __builtin_fmaf(p.alpha, v, p.beta * *dst);
-            } else {
-                v = v + bv;
-                if (p.act == 1)
-                    v = v > 0.0f ? v : 0.0f;
-            }
-            *dst = v;
-        }
+        if (row < p.M)
+            store_one<EPI>(p, p.C + (int64_t)row * p.ldc + col, acc[r], bv);
+    }
+}
+
+// The same for one 16x16 block of v_mfma_f32_16x16x*: lane l holds column
+// l % 16; register r holds row 4*(l/16) + r.
+template <int EPI>
+__device__ __forceinline__ void write_block16(const GemmParams &p, const f32x4 &acc,
+                                              int row0, int col0, int lane)
+{
+    const int col = col0 + (lane & 15);
+    if (col >= p.N)
+        return;
+    const int rbase = row0 + ((lane >> 4) << 2);
+    float bv = 0.0f;
+    if (EPI == EPI_LINEAR && p.bias != nullptr)
+        bv = p.bias[col];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = rbase + r;
+        if (row < p.M)
+            store_one<EPI>(p, p.C + (int64_t)row * p.ldc + col, acc[r], bv);
     }
 }
 

@@ -61,6 +61,20 @@ __device__ __forceinline__ f32x16 mma16(const f16x8 &a, const f16x8 &b, const f3
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// The 16x16x32 form: the same 8 k-values per lane (lane l: row or column
+// l%16, k = 8*(l/16) .. +7), a 16x16 block in four accumulators per lane.
+template <bool BF16>
+__device__ __forceinline__ f32x4 mma16(const f16x8 &a, const f16x8 &b, const f32x4 &c)
+{
+    if (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int MF> struct AccBlock { using type = f32x16; static constexpr int R = 16; };
+template <> struct AccBlock<16> { using type = f32x4; static constexpr int R = 4; };
+
 // BT: B is given N-by-K (k contiguous); it is then loaded and stored exactly
 // like A and needs no transposition.
 template <class T, int EPI, bool VEC, int WPE, bool BF16, bool BT>
@@ -262,8 +276,14 @@ gemm_f16_kernel(GemmParams p)
 // Direct-to-LDS FP16 kernel (256x256 block tile, 128-bit-aligned operands).
 //
 // Both operands travel global -> LDS with global_load_lds_dwordx4, so no
-// registers hold prefetched tiles and the 256 accumulators per lane leave room
-// for two register sets of MFMA operands. B keeps its row-major [k][n] layout
+// registers hold prefetched tiles and the 128 accumulators per lane leave room
+// for two register sets of MFMA operands.
+//
+// The inner product runs on v_mfma_f32_16x16x32 (MF = 16; MF = 32 selects
+// v_mfma_f32_32x32x16, the same 8 k-values per lane over half the k-step).
+// Both reach the same peak rate, but in a register-only loop over changing
+// operands on all CUs the 16x16 form sustained about 1.5x the 32x32 one (the
+// chip holds a higher clock), and in this kernel it measured 3-10 % faster. B keeps its row-major [k][n] layout
 // in LDS; the MFMA's B operand (8 consecutive k of one column per lane) is
 // read with ds_read_b64_tr_b16, gfx950's transposing LDS load: within each
 // group of 16 lanes, lane i receives element i%4 of the 8-byte rows that lanes
@@ -276,22 +296,25 @@ gemm_f16_kernel(GemmParams p)
 //      chunk) hit 16 different 16-byte bank groups (measured conflict-free).
 //      One copy (KiB) = 64/CPR rows; lane l fills row l/CPR, slot l%CPR, and
 //      fetches the logical chunk that the swizzle puts in that slot.
-//   B: BK rows x 512 bytes; 32-byte units XOR-swizzled by 2*(k%4). A
+//   B: BK rows x 512 bytes; 32-byte units XOR-swizzled per k-row. A
 //      transposing read is served 32 lanes (256 bytes) per LDS cycle: two
-//      16-lane groups, each reading one 32-byte unit (units u and u+1, u
-//      even) of the same four k-rows. The XOR sends the even group to units
-//      u^{0,2,4,6} and the odd one to the odd units between, eight different
-//      32-byte slots of the 256-byte bank line (XOR by k%4 would put both
-//      groups on units u..u+3: a two-way conflict, measured). One copy = 2
-//      rows; lane l fills row l/32, bytes 16*(l%32) .. +15.
-// NBUF stages form a ring. A stage holds BK/16 k-steps; each step's operands
-// are read while the previous step's MFMAs run. The stage's barrier sits
-// before its last step, whose operands are then in registers: it publishes
-// stage kt+1 and frees stage kt's buffer, which is refilled at once with stage
-// kt+NBUF while the last step's MFMAs run (a few copies after each row of
-// four MFMAs, not one burst the matrix cores would wait through). The first
-// operands of stage kt+1 are read during those MFMAs too, so no LDS latency
-// is exposed after a barrier.
+//      16-lane groups, each reading one 32-byte unit of four k-rows.
+//      MF = 32: the groups read units u and u+1 (u even) of the same rows;
+//      XOR by 2*(k%4) sends the even group to units u^{0,2,4,6} and the odd
+//      one to the odd units between, eight different 32-byte slots of the
+//      256-byte bank line (XOR by k%4 would put both groups on units u..u+3:
+//      a two-way conflict, measured).
+//      MF = 16: the groups read the same unit u of rows k..k+3 and k+8..k+11;
+//      XOR by 2*(k%4) + (k/8)%2 sends them to u^{0,2,4,6} and u^{1,3,5,7}.
+//      One copy = 2 rows; lane l fills row l/32, bytes 16*(l%32) .. +15.
+// NBUF stages form a ring. A stage holds BK/32 k-steps (BK/16 with MF = 32);
+// each step's operands are read while the previous step's MFMAs run. The
+// stage's barrier sits before its last step, whose operands are then in
+// registers: it publishes stage kt+1 and frees stage kt's buffer, which is
+// refilled at once with stage kt+NBUF while the last step's MFMAs run (a few
+// copies after each of the first rows of MFMAs, not one burst the matrix
+// cores would wait through). The first operands of stage kt+1 are read
+// during those MFMAs too, so no LDS latency is exposed after a barrier.
 //
 // With BT (B given N-by-K, k contiguous) B is copied and read exactly like A:
 // 256 rows x 2*BK bytes, the same swizzle, 128-bit operand reads, no
@@ -304,14 +327,15 @@ gemm_f16_kernel(GemmParams p)
 // IN (interior): launched only when every tile lies inside M and N and every
 // workgroup's K range is a whole number of stages; the copies then need no
 // bounds selects.
-template <int EPI, bool BF16, bool BT, int BK, int NBUF, int WGM, int WGN, bool IN>
+template <int EPI, bool BF16, bool BT, int BK, int NBUF, int WGM, int WGN, bool IN, int MF>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 gemm_f16_direct_kernel(GemmParams p)
 {
     constexpr int BM = 256, BN = 256, NW = WGM * WGN;
-    constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
-    constexpr int STEPS = BK / 16;                        // MFMA k-steps per stage
+    constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / MF, FN = WTN / MF;
+    constexpr int KSTEP = MF == 32 ? 16 : 32;             // k per MFMA
+    constexpr int STEPS = BK / KSTEP;                     // MFMA k-steps per stage
     constexpr int CPR = BK / 8;                           // 16-byte chunks per A row
     constexpr int RPC = 64 / CPR;                         // A rows per copy
     constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;   // halves
@@ -320,7 +344,8 @@ gemm_f16_direct_kernel(GemmParams p)
     constexpr int PER_STAGE = COPIES_A + COPIES_B;        // vmcnt entries per stage
     static_assert(STEPS % 2 == 0 && PER_STAGE % FM == 0, "stage layout");
     static_assert(COPIES_A * RPC * NW == BM && (COPIES_A * RPC) % 16 == 0 &&
-                      (BT || COPIES_B * 2 * NW == BK) && WTM % 32 == 0 && WTN % 32 == 0,
+                      (BT || COPIES_B * 2 * NW == BK) && WTM % MF == 0 && WTN % MF == 0 &&
+                      (MF == 16 || MF == 32),
                   "copies cover the stage; each wave's rows start at a multiple of 16");
     static_assert((NBUF - 1) * PER_STAGE <= 63, "vmcnt range");
     __shared__ __attribute__((aligned(1024))) uint16_t As[NBUF][A_STAGE];
@@ -340,6 +365,8 @@ gemm_f16_direct_kernel(GemmParams p)
         static_cast<const uint16_t *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
     const int M = p.M, N = p.N;
     auto swz = [](int row) { return (row / (16 / CPR)) & (CPR - 1); };
+    // B (K-by-N) unit swizzle of k-row k (see the layout notes above).
+    auto bsw = [](int k) { return MF == 32 ? 2 * (k & 3) : 2 * (k & 3) + ((k >> 3) & 1); };
 
     // Copy sources. Row-panel copy j of this wave (A, or B given N-by-K)
     // covers rows (wave*COPIES_A + j)*RPC + lane/CPR. Each wave's first row is
@@ -363,7 +390,7 @@ gemm_f16_direct_kernel(GemmParams p)
 #pragma unroll
     for (int j = 0; j < NB_SRC; ++j) {
         const int kr = (wave * COPIES_B + j) * 2 + (lane >> 5);
-        const int col = n0 + ((((lane & 31) >> 1) ^ (2 * (kr & 3))) * 16) + (lane & 1) * 8;
+        const int col = n0 + ((((lane & 31) >> 1) ^ bsw(kr)) * 16) + (lane & 1) * 8;
         b_src[j] = B + (int64_t)kr * p.ldb + col;
         b_col_ok[j] = col < N;
     }
@@ -404,46 +431,51 @@ gemm_f16_direct_kernel(GemmParams p)
         lds_dma_16(src, dst);
     };
 
-    f32x16 acc[FM][FN];
+    using Acc = typename AccBlock<MF>::type;
+    Acc acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < AccBlock<MF>::R; ++r)
                 acc[i][j][r] = 0.0f;
 
-    const int h = lane >> 5, l32 = lane & 31;
+    // Lane l supplies row (or column) l % MF of its block and k-values
+    // 8*(l/MF) .. +7 of the k-step.
+    const int grp = lane / MF, lrow = lane % MF;
     const int g_lo = (lane >> 4) & 1, j16 = lane & 15;
     typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-    // Operands of k-step s (k = 16s + 8h + 0..7) of the stage in buffer buf.
+    // Operands of k-step s (k = KSTEP*s + 8*grp + 0..7) of the stage in buffer buf.
     auto read_step = [&](int buf, int s, f16x8 (&af)[FM], f16x8 (&bf)[FN]) {
         const uint16_t *as = As[buf];
         const uint16_t *bs = Bs[buf];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            const int row = wm * WTM + fm * 32 + l32;
-            const int c = (2 * s + h) ^ swz(row);
+            const int row = wm * WTM + fm * MF + lrow;
+            const int c = (KSTEP / 8 * s + grp) ^ swz(row);
             af[fm] = *reinterpret_cast<const f16x8 *>(&as[row * BK + c * 8]);
         }
         if (BT) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const int row = wn * WTN + fn * 32 + l32;
-                const int c = (2 * s + h) ^ swz(row);
+                const int row = wn * WTN + fn * MF + lrow;
+                const int c = (KSTEP / 8 * s + grp) ^ swz(row);
                 bf[fn] = *reinterpret_cast<const f16x8 *>(&bs[row * BK + c * 8]);
             }
             return;
         }
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
-            const int n = wn * WTN + fn * 32 + g_lo * 16 + 4 * (j16 & 3);
+            // 16 columns per 16-lane group: a 32-wide block splits them over
+            // the two groups of a half-wave, a 16-wide one repeats them
+            const int n = wn * WTN + fn * MF + (MF == 32 ? g_lo * 16 : 0) + 4 * (j16 & 3);
             s16x4 v[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const int k = 16 * s + 8 * h + 4 * e + (j16 >> 2);
-                const int addr = k * BN + (((n >> 4) ^ (2 * (k & 3))) << 4) + (n & 15);
+                const int k = KSTEP * s + 8 * grp + 4 * e + (j16 >> 2);
+                const int addr = k * BN + (((n >> 4) ^ bsw(k)) << 4) + (n & 15);
                 v[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) s16x4 *)(lds_addr(&bs[addr])));
             }
@@ -510,14 +542,20 @@ gemm_f16_direct_kernel(GemmParams p)
         // stage they are stale, in-bounds and unused) so that no control-flow
         // join makes the compiler's LDS wait counts conservative.
         read_step(nbuf, 0, fa[0], fb[0]);
-        constexpr int G = PER_STAGE / FM;   // refill copies after each row of MFMAs
+        // The refill copies follow the first CROWS rows of MFMAs, G after
+        // each. 16x16 blocks (eight rows of four 16-cycle MFMAs): two rows
+        // measured 2-4 % faster than one row per copy pair or than all
+        // copies before the first MFMA.
+        constexpr int CROWS = MF == 16 ? 2 : FM;
+        constexpr int G = PER_STAGE / CROWS;
+        static_assert(PER_STAGE % CROWS == 0 && CROWS <= FM, "refill placement");
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
                 acc[fm][fn] = mma16<BF16>(fa[1][fm], fb[1][fn], acc[fm][fn]);
-            if (refill) {
+            if (refill && fm < CROWS) {
 #pragma unroll
                 for (int g = 0; g < G; ++g)
                     copy(buf, k_next, fm * G + g);
@@ -530,8 +568,13 @@ gemm_f16_direct_kernel(GemmParams p)
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            write_block<EPI>(p, acc[fm][fn], m0 + wm * WTM + fm * 32, n0 + wn * WTN + fn * 32, lane);
+        for (int fn = 0; fn < FN; ++fn) {
+            const int r0 = m0 + wm * WTM + fm * MF, c0 = n0 + wn * WTN + fn * MF;
+            if constexpr (MF == 32)
+                write_block<EPI>(p, acc[fm][fn], r0, c0, lane);
+            else
+                write_block16<EPI>(p, acc[fm][fn], r0, c0, lane);
+        }
 }
 
 // Stage depth and ring length of the direct kernel. At BK = 64 a row panel's
@@ -540,12 +583,14 @@ gemm_f16_direct_kernel(GemmParams p)
 // (BK = 32) for both B layouts on 4096- and 8192-cubed products.
 // Wave grid, per B layout: 2 x 4 (eight waves, two per SIMD, 128x64 each)
 // measured faster than 2 x 2 (one wave per SIMD) and 4 x 2, in one process:
-// 8192^3 fp16 1079 -> 1168 TFLOP/s, bf16 1114 -> 1234, B given N-by-K
-// 1171 -> 1191. A wave that waits to issue a copy no longer idles its SIMD's
-// matrix core, and the 4-wave kernel's 8 spilled registers are gone.
+// with 32x32 blocks 8192^3 fp16 1079 -> 1168 TFLOP/s, bf16 1114 -> 1234,
+// B given N-by-K 1171 -> 1191; with 16x16 blocks (2 x 2 then keeps its
+// accumulators in AGPRs without spills) 1084 -> 1244 for fp16. A wave that
+// waits to issue a copy no longer idles its SIMD's matrix core.
 template <bool BT> struct DirectCfg {
     static constexpr int BK = 64, NBUF = 2;
     static constexpr int WGM = 2, WGN = 4;
+    static constexpr int MF = 16;
 };
 
 using F16_L = F16Tile<256, 256, 64>;
@@ -604,10 +649,10 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
     do { \
         if (in) \
             hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF, Cfg::WGM, \
-                                                       Cfg::WGN, true>), grid, block, 0, s, p); \
+                                                       Cfg::WGN, true, Cfg::MF>), grid, block, 0, s, p); \
         else \
             hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF, Cfg::WGM, \
-                                                       Cfg::WGN, false>), grid, block, 0, s, p); \
+                                                       Cfg::WGN, false, Cfg::MF>), grid, block, 0, s, p); \
     } while (0)
     if (epi == EPI_GEMM_BETA0)
         LL_DIRECT(EPI_GEMM_BETA0);
