@@ -247,7 +247,8 @@ int ll_chosen_tile(int dtype, int M, int N, int K, int batch, int num_cus);
 int ll_chosen_split_k(int dtype, int M, int N, int K, int batch, int num_cus);
 
 /*
- * Stream-K (FP32 products with 128-bit-aligned operands, single products):
+ * Stream-K (single products with 128-bit-aligned operands; FP32 on tiles
+ * without K-slices, 16-bit on the 256x256 tile):
  * when the output tiles do not fill a whole number of rounds of the CUs, the
  * planner may run the full rounds tile by tile and share the leftover tiles'
  * K range out evenly over one round of workgroups, whose partial sums are
@@ -256,8 +257,9 @@ int ll_chosen_split_k(int dtype, int M, int N, int K, int batch, int num_cus);
  * order of those tiles run-dependent (still within the error bound; integer
  * inputs stay exact); it allocates nothing.
  *   ll_set_stream_k: -1 automatic (default), 0 never, 1 whenever the shape
- *   allows it (a forced K-split takes precedence; K-sliced tiles never
- *   share out). Returns LL_OK or LL_ERR_INVALID_VALUE.
+ *   allows it (a forced K-split takes precedence; K-sliced FP32 tiles and
+ *   the 128x128 and 64x64 16-bit tiles never share out). Returns LL_OK or
+ *   LL_ERR_INVALID_VALUE.
  *   ll_chosen_stream_k: the number of tiles the plan shares out (0: none),
  *   assuming 128-bit-aligned operands; dtype and flags as for
  *   ll_chosen_tile; -1 for an unknown dtype or flag, or batch < 1.

@@ -144,10 +144,12 @@ std::atomic<int> g_split_override{-1};
 constexpr int kSplitAlign = 64;     // K per split is a multiple of every kernel's stage depth
 constexpr int kMaxSplits = 16;
 
-// Work units are multiply-adds on one CU at the 256x256 tile's throughput;
-// at the FP32 matrix peak one CU does 157.3e12 / 2 / 256 = 307e3 of them per
-// microsecond.
-constexpr double kUnitsPerUs = 307e3;
+// Work units are multiply-adds on one CU at the 256x256 tile's throughput.
+// FP32: at the matrix peak one CU does 157.3e12 / 2 / 256 = 307e3 of them per
+// microsecond. 16-bit: the 256x256 kernel's measured rate on 8192^3 products,
+// about 1250e12 / 2 / 256 = 2.4e6 (the matrix peak would be 4.9e6). Fixed
+// costs (passes, atomic traffic) are converted to units at the same rate.
+constexpr double kUnitsPerUs[2] = {307e3, 2.4e6};
 // Fixed cost (us) of the extra launches a K-split or stream-K plan makes: the
 // pass that prepares C (or Y) and, for ReLU, the pass after. Through the
 // Python binding a 256^3 product measured 8.6 us per call as one launch and
@@ -179,10 +181,10 @@ struct Plan {
 std::atomic<int> g_sk_override{-1};   // -1 automatic, 0 never, 1 whenever possible
 
 // Whether a plan may share tiles out with stream-K on tile shape `ti`: it
-// needs the direct kernels (128-bit-aligned operands) and no K-slices.
+// needs a direct kernel (128-bit-aligned operands) and no K-slices.
 bool sk_tile_ok(const TileInfo &ti)
 {
-    return ti.k_slices == 1;
+    return ti.stream_k && ti.k_slices == 1;
 }
 
 // Choose the tile shape and the number of K-splits minimising the estimate:
@@ -225,7 +227,7 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
             if (splits > 1) {
                 const double mn = (double)M * N * items;
                 const double bytes = 8.0 * mn * (relu ? 2 : 1) + 4.0 * mn * splits;
-                cost += ((relu ? kPassUs + kReluPassUs : kPassUs) + bytes / 3.0e6) * kUnitsPerUs;
+                cost += ((relu ? kPassUs + kReluPassUs : kPassUs) + bytes / 3.0e6) * kUnitsPerUs[dtype];
             }
             if (!have || cost < best_cost) {
                 best = Plan{t, splits, k_split, 0, 0};
@@ -251,7 +253,7 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
                 // them); passes: the prepare write and, for ReLU, a read and write
                 const double area = 4.0 * ti.bm * ti.bn;
                 const double bytes = area * (double)(grid + rest) + area * rest * (relu ? 3 : 1);
-                cost += ((relu ? kPassUs + kReluPassUs : kPassUs) + bytes / 3.0e6) * kUnitsPerUs;
+                cost += ((relu ? kPassUs + kReluPassUs : kPassUs) + bytes / 3.0e6) * kUnitsPerUs[dtype];
                 if (!have_sk || cost < best_sk_cost) {
                     best_sk = Plan{t, 1, K, (int)(rounds * slots), (int)grid};
                     best_sk_cost = cost;
@@ -445,8 +447,8 @@ static int gemm_16(int M, int N, int K, float alpha, const uint16_t *A, int lda,
                      ldb % 8 == 0 && ldc % 4 == 0 && K % 8 == 0 && (bt || N % 8 == 0) &&
                      batch_aligned(bat, 2);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false, bat.count);
-    return launch_status(run_gemm(p, pl, vec, s, launch, 2, bat));
+    const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false, bat.count, vec);
+    return launch_status(run_gemm(p, pl, vec, s, launch, 2, bat, &kF16Tiles[pl.tile]));
 }
 
 int gemm_f16f32(int M, int N, int K, float alpha, const uint16_t *A, int lda, const uint16_t *B,
@@ -612,7 +614,7 @@ static Plan chosen_plan(int dtype, int M, int N, int K, int batch, int num_cus, 
     const int cus = num_cus > 0 ? num_cus : 256;
     if (base == LL_DTYPE_F32)
         return plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, relu, batch, true);
-    return plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch);
+    return plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch, true);
 }
 
 int ll_chosen_tile(int dtype, int M, int N, int K, int batch, int num_cus)

@@ -327,7 +327,7 @@ gemm_f16_kernel(GemmParams p)
 // IN (interior): launched only when every tile lies inside M and N and every
 // workgroup's K range is a whole number of stages; the copies then need no
 // bounds selects.
-template <int EPI, bool BF16, bool BT, int BK, int NBUF, int WGM, int WGN, bool IN, int MF>
+template <int EPI, bool BF16, bool BT, int BK, int NBUF, int WGM, int WGN, bool IN, int MF, bool SK>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 __attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
 gemm_f16_direct_kernel(GemmParams p)
@@ -355,11 +355,24 @@ gemm_f16_direct_kernel(GemmParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
     select_batch(p);
-    int tm, tn;
-    tile_coords(p, tm, tn);
+    // One tile per workgroup, or (a stream-K launch's sharing workgroups, from
+    // sk_block on) up to two (tile, k-range) segments, each a complete pass of
+    // the pipeline below whose partial sums are added atomically.
+    const bool sharing = SK && (int)blockIdx.x >= p.sk_block;
+    for (int seg = 0;; ++seg) {
+    int tm, tn, K, kb;
+    if (sharing) {
+        if (!sk_segment(p, seg, tm, tn, kb, K))
+            break;
+        if (seg > 0)
+            __syncthreads();   // every wave is done with the previous segment's LDS
+    } else {
+        if (seg > 0)
+            break;
+        tile_coords(p, tm, tn);
+        kb = split_range(p, K);
+    }
     const int m0 = tm * BM, n0 = tn * BN;
-    int K;
-    const int kb = split_range(p, K);
     const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A) + kb;
     const uint16_t *__restrict__ B =
         static_cast<const uint16_t *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
@@ -570,11 +583,19 @@ gemm_f16_direct_kernel(GemmParams p)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int r0 = m0 + wm * WTM + fm * MF, c0 = n0 + wn * WTN + fn * MF;
-            if constexpr (MF == 32)
-                write_block<EPI>(p, acc[fm][fn], r0, c0, lane);
-            else
-                write_block16<EPI>(p, acc[fm][fn], r0, c0, lane);
+            if constexpr (MF == 32) {
+                if (sharing)
+                    write_block<EPI_ATOMIC>(p, acc[fm][fn], r0, c0, lane);
+                else
+                    write_block<EPI>(p, acc[fm][fn], r0, c0, lane);
+            } else {
+                if (sharing)
+                    write_block16<EPI_ATOMIC>(p, acc[fm][fn], r0, c0, lane);
+                else
+                    write_block16<EPI>(p, acc[fm][fn], r0, c0, lane);
+            }
         }
+    }
 }
 
 // Stage depth and ring length of the direct kernel. At BK = 64 a row panel's
@@ -605,7 +626,7 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     p.tiles_n = (p.N + T::BN - 1) / T::BN;
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ || p.grid_x != 0 || p.sk_tiles != 0)
-        return hipErrorInvalidValue;   // the 16-bit kernels run whole grids only
+        return hipErrorInvalidValue;   // the register-staged kernels run whole grids only
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F16_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f16_kernel<T, E, V, WPE, BF16, BT>), grid, block, 0, s, p)
@@ -626,8 +647,9 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // FP32 table); measured on the 8192^3 product.
 const TileInfo kF16Tiles[kF16NumTiles] = {
     {F16_L::BM, F16_L::BN, 1, 1.00f, 1.00f, "f16_256x256_direct"},
-    {F16_S::BM, F16_S::BN, 2, 0.52f, 0.68f, "f16_128x128x64"},
-    {F16_XS::BM, F16_XS::BN, 2, 0.22f, 0.28f, "f16_64x64x64"},
+    // the register-staged tiles take no stream-K share
+    {F16_S::BM, F16_S::BN, 2, 0.52f, 0.68f, "f16_128x128x64", 1, false},
+    {F16_XS::BM, F16_XS::BN, 2, 0.22f, 0.28f, "f16_64x64x64", 1, false},
 };
 
 template <bool BF16, bool BT>
@@ -638,29 +660,44 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
     GemmParams p = p0;
     p.tiles_m = (p.M + 255) / 256;
     p.tiles_n = (p.N + 255) / 256;
-    const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
-    if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ || p.grid_x != 0 || p.sk_tiles != 0)
-        return hipErrorInvalidValue;   // the 16-bit kernels run whole grids only
+    int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
+        return hipErrorInvalidValue;
+    if (p.grid_x > 0)
+        ntiles = p.grid_x;   // a stream-K launch: whole tiles, then the sharing workgroups
+    const bool sk = p.sk_tiles > 0;
+    if (sk && (epi == EPI_ATOMIC || p.batch != 1))
+        return hipErrorInvalidValue;
     using Cfg = DirectCfg<BT>;
+    static_assert(kSkUnit % Cfg::BK == 0, "stream-K segments are whole stages");
     const dim3 grid = gemm_grid(p, ntiles), block(64 * Cfg::WGM * Cfg::WGN);
     // every copy inside the matrices: whole tiles, whole stages in every K range
     const bool in = p.M % 256 == 0 && p.N % 256 == 0 && p.K % Cfg::BK == 0 && p.k_split % Cfg::BK == 0;
-#define LL_DIRECT(E) \
+#define LL_DIRECT_K(E, IN, SK) \
+    hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF, Cfg::WGM, Cfg::WGN, \
+                                               IN, Cfg::MF, SK>), grid, block, 0, s, p)
+#define LL_DIRECT(E, SK) \
     do { \
         if (in) \
-            hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF, Cfg::WGM, \
-                                                       Cfg::WGN, true, Cfg::MF>), grid, block, 0, s, p); \
+            LL_DIRECT_K(E, true, SK); \
         else \
-            hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF, Cfg::WGM, \
-                                                       Cfg::WGN, false, Cfg::MF>), grid, block, 0, s, p); \
+            LL_DIRECT_K(E, false, SK); \
     } while (0)
-    if (epi == EPI_GEMM_BETA0)
-        LL_DIRECT(EPI_GEMM_BETA0);
-    else if (epi == EPI_GEMM_BETA)
-        LL_DIRECT(EPI_GEMM_BETA);
-    else
-        LL_DIRECT(EPI_ATOMIC);
+    if (sk) {
+        // whole tiles with `epi`, shared ones added atomically
+        if (epi == EPI_GEMM_BETA0)
+            LL_DIRECT(EPI_GEMM_BETA0, true);
+        else
+            LL_DIRECT(EPI_GEMM_BETA, true);
+    } else if (epi == EPI_GEMM_BETA0) {
+        LL_DIRECT(EPI_GEMM_BETA0, false);
+    } else if (epi == EPI_GEMM_BETA) {
+        LL_DIRECT(EPI_GEMM_BETA, false);
+    } else {
+        LL_DIRECT(EPI_ATOMIC, false);
+    }
 #undef LL_DIRECT
+#undef LL_DIRECT_K
     return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@ struct TileInfo {
     float eff_paired;  // relative CU throughput with wg_per_cu workgroups on it
     const char *name;
     int k_slices = 1;  // K-slices inside the workgroup (such tiles take no stream-K share)
+    bool stream_k = true;  // the tile's kernel can run a stream-K launch
 };
 
 constexpr int kF32NumTiles = 6;

@@ -183,7 +183,7 @@ def test_tile_choice():
     assert choice(f32, 2047, 11008, 4096) == ("f32_256x256", 1)
     assert ll.chosen_stream_k(f32, 2047, 11008, 4096, 256) == 88
     assert ll.chosen_stream_k(f32, 4096, 4096, 4096, 256) == 0     # one whole round
-    assert ll.chosen_stream_k(f16, 8192, 8192, 8192, 256) == 0     # 16-bit: never
+    assert ll.chosen_stream_k(f16, 8192, 8192, 8192, 256) == 0     # four whole rounds
     ll.set_stream_k(0)
     try:
         assert choice(f32, 2047, 11008, 4096) == ("f32_256x128", 1)
@@ -193,6 +193,24 @@ def test_tile_choice():
     with pytest.raises(ll.LinearLayerError):
         ll.set_stream_k(2)
     assert choice(f16, 8192, 8192, 8192) == ("f16_256x256_direct", 1)
+    # 16-bit: 6144^2 is 576 tiles of 256x256, 2.25 rounds: two run whole, 64
+    # tiles are shared out; 3072^3 (144 tiles, one short round) runs whole,
+    # and a K-split is not worth its passes at the 16-bit rate
+    assert choice(f16, 6144, 6144, 6144) == ("f16_256x256_direct", 1)
+    assert ll.chosen_stream_k(f16, 6144, 6144, 6144, 256) == 64
+    assert choice(f16, 3072, 3072, 3072) == ("f16_256x256_direct", 1)
+    assert ll.chosen_stream_k(f16, 3072, 3072, 3072, 256) == 0
+    # the register-staged 16-bit tiles take no stream-K share, even when forced
+    ll.set_stream_k(1)
+    try:
+        for t in (1, 2):
+            ll.set_tile(f16, t)
+            assert ll.chosen_stream_k(f16, 2047, 11008, 4096, 256) == 0
+        ll.set_tile(f16, 0)
+        assert ll.chosen_stream_k(f16, 300, 264, 200, 256) > 0
+    finally:
+        ll.set_stream_k(-1)
+        ll.set_tile(f16, -1)
     # problems too small to fill 256 CUs use small tiles split along K: in
     # the workgroup (K-slices), across workgroups, or both
     assert choice(f32, 1024, 1024, 1024) == ("f32_64x64_k4", 1)

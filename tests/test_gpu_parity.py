@@ -886,6 +886,76 @@ def test_stream_k_guards_untouched(tile, stream_k):
     assert_close(np32(Cd), R, T, "stream-K strided C")
 
 
+SK16 = {("f16", False): ll.gemm_f16f32, ("f16", True): ll.gemm_f16f32_nt,
+        ("bf16", False): ll.gemm_bf16f32, ("bf16", True): ll.gemm_bf16f32_nt}
+
+
+def run_16(which, trans_b, A, B, alpha=1.0, beta=0.0, C=None):
+    """One of the 16-bit products on device copies; B is N-by-K when trans_b."""
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    N = B.shape[0] if trans_b else B.shape[1]
+    Cd = (C.clone() if C is not None else torch.full((A.shape[0], N), float("nan"))).to(DEV)
+    SK16[(which, trans_b)](Ad, Bd, Cd, alpha, beta)
+    torch.cuda.synchronize()
+    return np32(Cd)
+
+
+@pytest.mark.parametrize("which,trans_b", list(SK16))
+@pytest.mark.parametrize("M,N,K", [(300, 264, 200), (257, 70, 1000), (600, 520, 72), (512, 512, 256)])
+@pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (1.5, 0.5), (-0.5, 1.0)])
+def test_16bit_stream_k(which, trans_b, M, N, K, alpha, beta, tile, stream_k):
+    """The 256x256 16-bit kernel with every tile shared out (fewer tiles than CUs):
+    several atomic segments per tile, ragged and whole (512^3-like) shapes."""
+    tile(F16, 0)
+    stream_k(1)
+    dt = torch.float16 if which == "f16" else torch.bfloat16
+    A = rand((M, K), 161).to(dt)
+    B = rand((N, K) if trans_b else (K, N), 162).to(dt)
+    C = rand((M, N), 163)
+    got = run_16(which, trans_b, A, B, alpha, beta, C if beta else None)
+    R, T = oracle.gemm(bits16(A), bits16(B), alpha, beta, np32(C), bf16=which == "bf16",
+                       b_trans=trans_b)
+    assert_close(got, R, T, f"{which} tb={trans_b} stream-K {M}x{N}x{K} a={alpha} b={beta}")
+
+
+@pytest.mark.parametrize("which,trans_b", [("f16", False), ("bf16", True)])
+def test_16bit_stream_k_hybrid_rounds(which, trans_b, tile, stream_k):
+    """289 tiles of 256x256 on 256 CUs: one data-parallel round, 33 tiles shared
+    out; integer inputs, so every order of the atomic additions gives the
+    oracle's result exactly."""
+    tile(F16, 0)
+    stream_k(1)
+    M = N = 17 * 256
+    K = 192
+    props = torch.cuda.get_device_properties(0)
+    assert ll.chosen_stream_k(F16, M, N, K, props.multi_processor_count) > 0
+    dt = torch.float16 if which == "f16" else torch.bfloat16
+    A = wl.integers((M, K), 164, -2, 2).to(dt)
+    B = wl.integers((N, K) if trans_b else (K, N), 165, -2, 2).to(dt)
+    C = wl.integers((M, N), 166, -4, 4)
+    R, _ = oracle.gemm(bits16(A), bits16(B), 1.5, 0.5, np32(C), bf16=which == "bf16", b_trans=trans_b)
+    assert_exact(run_16(which, trans_b, A, B, 1.5, 0.5, C), R, f"{which} hybrid integer")
+    Af, Bf = rand((M, K), 167).to(dt), rand(tuple(B.shape), 168).to(dt)
+    R, T = oracle.gemm(bits16(Af), bits16(Bf), bf16=which == "bf16", b_trans=trans_b)
+    assert_close(run_16(which, trans_b, Af, Bf), R, T, f"{which} hybrid")
+
+
+def test_16bit_stream_k_guards_untouched(tile, stream_k):
+    """The shared-out tiles' passes and atomics stay inside C."""
+    tile(F16, 0)
+    stream_k(1)
+    M, N, K = 300, 264, 192
+    A, B = rand((M, K), 169).half(), rand((K, N), 170).half()
+    Cw = torch.full((M, N + 8), 7.0, device=DEV)
+    Cd = Cw[:, :N]
+    Cd.copy_(torch.ones((M, N)))
+    ll.gemm_f16f32(A.to(DEV), B.to(DEV), Cd, 1.0, 0.5)
+    torch.cuda.synchronize()
+    assert torch.all(Cw[:, N:] == 7.0)
+    R, T = oracle.gemm(bits16(A), bits16(B), 1.0, 0.5, np.ones((M, N), np.float32))
+    assert_close(np32(Cd), R, T, "16-bit stream-K strided C")
+
+
 # ---- full-size workloads, as the bench launches them ------------------------
 
 def relu_matches(got, got0, tol=1e-5):
