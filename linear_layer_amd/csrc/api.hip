@@ -150,6 +150,12 @@ constexpr int kMaxSplits = 16;
 // about 1250e12 / 2 / 256 = 2.4e6 (the matrix peak would be 4.9e6). Fixed
 // costs (passes, atomic traffic) are converted to units at the same rate.
 constexpr double kUnitsPerUs[2] = {307e3, 2.4e6};
+// Effective rate (bytes per microsecond) of the atomic partial sums and
+// passes of a K-split or stream-K plan. 16-bit: fitted to stream-K on
+// 5120^3 and 6144^3, whose shared phases took 72-87 us beyond their MFMA
+// work for 84-105 MB of atomic traffic; the FP32 kernels' longer tiles hide
+// more of it.
+constexpr double kAtomicBytesPerUs[2] = {3.0e6, 1.2e6};
 // Fixed cost (us) of the extra launches a K-split or stream-K plan makes: the
 // pass that prepares C (or Y) and, for ReLU, the pass after. Through the
 // Python binding a 256^3 product measured 8.6 us per call as one launch and
@@ -227,7 +233,8 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
             if (splits > 1) {
                 const double mn = (double)M * N * items;
                 const double bytes = 8.0 * mn * (relu ? 2 : 1) + 4.0 * mn * splits;
-                cost += ((relu ? kPassUs + kReluPassUs : kPassUs) + bytes / 3.0e6) * kUnitsPerUs[dtype];
+                cost += ((relu ? kPassUs + kReluPassUs : kPassUs) + bytes / kAtomicBytesPerUs[dtype]) *
+                        kUnitsPerUs[dtype];
             }
             if (!have || cost < best_cost) {
                 best = Plan{t, splits, k_split, 0, 0};
@@ -253,7 +260,8 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
                 // them); passes: the prepare write and, for ReLU, a read and write
                 const double area = 4.0 * ti.bm * ti.bn;
                 const double bytes = area * (double)(grid + rest) + area * rest * (relu ? 3 : 1);
-                cost += ((relu ? kPassUs + kReluPassUs : kPassUs) + bytes / 3.0e6) * kUnitsPerUs[dtype];
+                cost += ((relu ? kPassUs + kReluPassUs : kPassUs) + bytes / kAtomicBytesPerUs[dtype]) *
+                        kUnitsPerUs[dtype];
                 if (!have_sk || cost < best_sk_cost) {
                     best_sk = Plan{t, 1, K, (int)(rounds * slots), (int)grid};
                     best_sk_cost = cost;
@@ -639,7 +647,7 @@ int ll_chosen_stream_k(int dtype, int M, int N, int K, int batch, int num_cus)
         return -1;
     if (p.sk_grid == 0)
         return 0;
-    const TileInfo &ti = kF32Tiles[p.tile];
+    const TileInfo &ti = (dtype & 0xFF) == LL_DTYPE_F32 ? kF32Tiles[p.tile] : kF16Tiles[p.tile];
     return (int)((int64_t)((M + ti.bm - 1) / ti.bm) * ((N + ti.bn - 1) / ti.bn) - p.dp_tiles);
 }
 

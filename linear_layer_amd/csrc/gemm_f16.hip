@@ -327,12 +327,13 @@ gemm_f16_kernel(GemmParams p)
 // IN (interior): launched only when every tile lies inside M and N and every
 // workgroup's K range is a whole number of stages; the copies then need no
 // bounds selects.
-template <int EPI, bool BF16, bool BT, int BK, int NBUF, int WGM, int WGN, bool IN, int MF, bool SK>
-__global__ void __launch_bounds__(64 * WGM * WGN)
-__attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
+template <int EPI, bool BF16, bool BT, int BM, int BN, int BK, int NBUF, int WGM, int WGN, int WPE,
+          bool IN, int MF, bool SK>
+__global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f16_direct_kernel(GemmParams p)
 {
-    constexpr int BM = 256, BN = 256, NW = WGM * WGN;
+    constexpr int NW = WGM * WGN;
+    static_assert(BM == BN && (BN == 128 || BN == 256), "square tiles of 128 or 256");
     constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / MF, FN = WTN / MF;
     constexpr int KSTEP = MF == 32 ? 16 : 32;             // k per MFMA
     constexpr int STEPS = BK / KSTEP;                     // MFMA k-steps per stage
@@ -340,11 +341,13 @@ gemm_f16_direct_kernel(GemmParams p)
     constexpr int RPC = 64 / CPR;                         // A rows per copy
     constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;   // halves
     constexpr int COPIES_A = BM / RPC / NW;               // per wave per stage
-    constexpr int COPIES_B = BT ? COPIES_A : BK / 2 / NW;
+    constexpr int LPR = BN / 8;                           // lanes per B k-row (K-by-N)
+    constexpr int RB = 64 / LPR;                          // B k-rows per copy
+    constexpr int COPIES_B = BT ? COPIES_A : BK / RB / NW;
     constexpr int PER_STAGE = COPIES_A + COPIES_B;        // vmcnt entries per stage
     static_assert(STEPS % 2 == 0 && PER_STAGE % FM == 0, "stage layout");
     static_assert(COPIES_A * RPC * NW == BM && (COPIES_A * RPC) % 16 == 0 &&
-                      (BT || COPIES_B * 2 * NW == BK) && WTM % MF == 0 && WTN % MF == 0 &&
+                      (BT || COPIES_B * RB * NW == BK) && WTM % MF == 0 && WTN % MF == 0 &&
                       (MF == 16 || MF == 32),
                   "copies cover the stage; each wave's rows start at a multiple of 16");
     static_assert((NBUF - 1) * PER_STAGE <= 63, "vmcnt range");
@@ -395,15 +398,16 @@ gemm_f16_direct_kernel(GemmParams p)
         a_src[v] = A + (int64_t)(m0 + r_lane) * p.lda + ch[v] * 8;
         bt_src[v] = B + (int64_t)(n0 + r_lane) * p.ldb + ch[v] * 8;
     }
-    // B copy j (given K-by-N): k-row (wave*COPIES_B + j)*2 + lane/32; the
-    // lane's 16 bytes hold logical unit (((lane%32)/2) ^ (k%4)), half lane%2.
+    // B copy j (given K-by-N): k-row (wave*COPIES_B + j)*RB + lane/LPR; the
+    // lane's 16 bytes fill unit slot (lane%LPR)/2, half lane%2, and hold
+    // logical unit slot ^ bsw(k).
     constexpr int NB_SRC = BT ? 1 : COPIES_B;
     const uint16_t *b_src[NB_SRC];
     bool b_col_ok[NB_SRC];
 #pragma unroll
     for (int j = 0; j < NB_SRC; ++j) {
-        const int kr = (wave * COPIES_B + j) * 2 + (lane >> 5);
-        const int col = n0 + ((((lane & 31) >> 1) ^ bsw(kr)) * 16) + (lane & 1) * 8;
+        const int kr = (wave * COPIES_B + j) * RB + lane / LPR;
+        const int col = n0 + ((((lane % LPR) >> 1) ^ bsw(kr)) * 16) + (lane & 1) * 8;
         b_src[j] = B + (int64_t)kr * p.ldb + col;
         b_col_ok[j] = col < N;
     }
@@ -437,7 +441,7 @@ gemm_f16_direct_kernel(GemmParams p)
             if constexpr (IN)
                 src = in;
             else
-                src = k0 + (wave * COPIES_B + j) * 2 + (lane >> 5) < K && b_col_ok[j]
+                src = k0 + (wave * COPIES_B + j) * RB + lane / LPR < K && b_col_ok[j]
                           ? in
                           : zero_chunk<uint16_t>();
         }
@@ -608,9 +612,16 @@ gemm_f16_direct_kernel(GemmParams p)
 // B given N-by-K 1171 -> 1191; with 16x16 blocks (2 x 2 then keeps its
 // accumulators in AGPRs without spills) 1084 -> 1244 for fp16. A wave that
 // waits to issue a copy no longer idles its SIMD's matrix core.
-template <bool BT> struct DirectCfg {
+template <int BM> struct DirectCfg {
     static constexpr int BK = 64, NBUF = 2;
-    static constexpr int WGM = 2, WGN = 4;
+    static constexpr int WGM = 2, WGN = 4, WPE = 2;
+    static constexpr int MF = 16;
+};
+// 128x128: four waves of 64x64 and 64 KiB of LDS, so two workgroups share a
+// CU (two waves per SIMD, as with one 256x256 workgroup).
+template <> struct DirectCfg<128> {
+    static constexpr int BK = 64, NBUF = 2;
+    static constexpr int WGM = 2, WGN = 2, WPE = 2;
     static constexpr int MF = 16;
 };
 
@@ -644,38 +655,48 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 }
 
 // {BM, BN, workgroups per CU, relative throughput alone, paired} (see the
-// FP32 table); measured on the 8192^3 product.
+// FP32 table), against the 256x256 kernel's 4096^3 rate. 128x128 (direct):
+// paired 0.91 on 8192^3 and 0.86 on 4096^3; alone 0.50 on 2048^3 and 0.62
+// with K = 8192, entered as 0.45 so that a last half round of lone 128x128
+// workgroups (6144^3: 4.5 rounds, 1048 TFLOP/s) loses to 256x256 with
+// stream-K (1140). 64x64 (register-staged): about 0.20 paired.
+// Stream-K runs on the 256x256 tile only: on 128x128 tiles (3072^3, 5120^3,
+// 6144^3) it lost to the best other plan by 4-10 %, its many short shared
+// segments paying more per atomic byte.
 const TileInfo kF16Tiles[kF16NumTiles] = {
     {F16_L::BM, F16_L::BN, 1, 1.00f, 1.00f, "f16_256x256_direct"},
-    // the register-staged tiles take no stream-K share
-    {F16_S::BM, F16_S::BN, 2, 0.52f, 0.68f, "f16_128x128x64", 1, false},
-    {F16_XS::BM, F16_XS::BN, 2, 0.22f, 0.28f, "f16_64x64x64", 1, false},
+    {F16_S::BM, F16_S::BN, 2, 0.45f, 0.88f, "f16_128x128x64", 1, false},
+    {F16_XS::BM, F16_XS::BN, 2, 0.15f, 0.20f, "f16_64x64x64", 1, false},
 };
 
-template <bool BF16, bool BT>
+// The direct kernel on BM x BM tiles for 128-bit-aligned operands; the
+// register-staged kernel of the same tile (T) otherwise.
+template <bool BF16, bool BT, int BM, class T, int WPE_T>
 static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
+    static_assert(T::BM == BM && T::BN == BM, "fallback tile");
     if (!vec)
-        return launch_t<F16_L, 1, BF16, BT>(p0, epi, vec, s);
+        return launch_t<T, WPE_T, BF16, BT>(p0, epi, vec, s);
     GemmParams p = p0;
-    p.tiles_m = (p.M + 255) / 256;
-    p.tiles_n = (p.N + 255) / 256;
+    p.tiles_m = (p.M + BM - 1) / BM;
+    p.tiles_n = (p.N + BM - 1) / BM;
     int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
         return hipErrorInvalidValue;
     if (p.grid_x > 0)
         ntiles = p.grid_x;   // a stream-K launch: whole tiles, then the sharing workgroups
     const bool sk = p.sk_tiles > 0;
-    if (sk && (epi == EPI_ATOMIC || p.batch != 1))
-        return hipErrorInvalidValue;
-    using Cfg = DirectCfg<BT>;
+    if (sk && (BM != 256 || epi == EPI_ATOMIC || p.batch != 1))
+        return hipErrorInvalidValue;   // stream-K: the 256x256 tile only
+    using Cfg = DirectCfg<BM>;
     static_assert(kSkUnit % Cfg::BK == 0, "stream-K segments are whole stages");
     const dim3 grid = gemm_grid(p, ntiles), block(64 * Cfg::WGM * Cfg::WGN);
     // every copy inside the matrices: whole tiles, whole stages in every K range
-    const bool in = p.M % 256 == 0 && p.N % 256 == 0 && p.K % Cfg::BK == 0 && p.k_split % Cfg::BK == 0;
+    const bool in = p.M % BM == 0 && p.N % BM == 0 && p.K % Cfg::BK == 0 && p.k_split % Cfg::BK == 0;
 #define LL_DIRECT_K(E, IN, SK) \
-    hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, Cfg::BK, Cfg::NBUF, Cfg::WGM, Cfg::WGN, \
-                                               IN, Cfg::MF, SK>), grid, block, 0, s, p)
+    hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, BM, BM, Cfg::BK, Cfg::NBUF, Cfg::WGM, \
+                                               Cfg::WGN, Cfg::WPE, IN, Cfg::MF, SK>), \
+                       grid, block, 0, s, p)
 #define LL_DIRECT(E, SK) \
     do { \
         if (in) \
@@ -683,13 +704,17 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
         else \
             LL_DIRECT_K(E, false, SK); \
     } while (0)
-    if (sk) {
-        // whole tiles with `epi`, shared ones added atomically
-        if (epi == EPI_GEMM_BETA0)
-            LL_DIRECT(EPI_GEMM_BETA0, true);
-        else
-            LL_DIRECT(EPI_GEMM_BETA, true);
-    } else if (epi == EPI_GEMM_BETA0) {
+    if constexpr (BM == 256) {
+        if (sk) {
+            // whole tiles with `epi`, shared ones added atomically
+            if (epi == EPI_GEMM_BETA0)
+                LL_DIRECT(EPI_GEMM_BETA0, true);
+            else
+                LL_DIRECT(EPI_GEMM_BETA, true);
+            return hipGetLastError();
+        }
+    }
+    if (epi == EPI_GEMM_BETA0) {
         LL_DIRECT(EPI_GEMM_BETA0, false);
     } else if (epi == EPI_GEMM_BETA) {
         LL_DIRECT(EPI_GEMM_BETA, false);
@@ -705,8 +730,8 @@ template <bool BF16, bool BT>
 static hipError_t launch_16(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
 {
     switch (tile) {
-    case 0: return launch_direct<BF16, BT>(p, epi, vec, s);
-    case 1: return launch_t<F16_S, 2, BF16, BT>(p, epi, vec, s);
+    case 0: return launch_direct<BF16, BT, 256, F16_L, 1>(p, epi, vec, s);
+    case 1: return launch_direct<BF16, BT, 128, F16_S, 2>(p, epi, vec, s);
     default: return launch_t<F16_XS, 2, BF16, BT>(p, epi, vec, s);
     }
 }

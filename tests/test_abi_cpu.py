@@ -194,13 +194,18 @@ def test_tile_choice():
         ll.set_stream_k(2)
     assert choice(f16, 8192, 8192, 8192) == ("f16_256x256_direct", 1)
     # 16-bit: 6144^2 is 576 tiles of 256x256, 2.25 rounds: two run whole, 64
-    # tiles are shared out; 3072^3 (144 tiles, one short round) runs whole,
-    # and a K-split is not worth its passes at the 16-bit rate
+    # tiles are shared out; 3072^3 (144 tiles, one short round) and 5120^3
+    # (400 tiles) run whole; a K-split is not worth its passes at the 16-bit
+    # rate; 2048^3 and thin products take the 128x128 direct tile
     assert choice(f16, 6144, 6144, 6144) == ("f16_256x256_direct", 1)
     assert ll.chosen_stream_k(f16, 6144, 6144, 6144, 256) == 64
     assert choice(f16, 3072, 3072, 3072) == ("f16_256x256_direct", 1)
+    assert choice(f16, 5120, 5120, 5120) == ("f16_256x256_direct", 1)
     assert ll.chosen_stream_k(f16, 3072, 3072, 3072, 256) == 0
-    # the register-staged 16-bit tiles take no stream-K share, even when forced
+    assert ll.chosen_stream_k(f16, 5120, 5120, 5120, 256) == 0
+    assert choice(f16, 2048, 2048, 2048) == ("f16_128x128x64", 1)
+    assert choice(f16, 1024, 8192, 8192) == ("f16_128x128x64", 1)
+    # only the 256x256 16-bit tile takes a stream-K share, even when forced
     ll.set_stream_k(1)
     try:
         for t in (1, 2):

@@ -904,9 +904,11 @@ def run_16(which, trans_b, A, B, alpha=1.0, beta=0.0, C=None):
 @pytest.mark.parametrize("M,N,K", [(300, 264, 200), (257, 70, 1000), (600, 520, 72), (512, 512, 256)])
 @pytest.mark.parametrize("alpha,beta", [(1.0, 0.0), (1.5, 0.5), (-0.5, 1.0)])
 def test_16bit_stream_k(which, trans_b, M, N, K, alpha, beta, tile, stream_k):
-    """The 256x256 16-bit kernel with every tile shared out (fewer tiles than CUs):
-    several atomic segments per tile, ragged and whole (512^3-like) shapes."""
-    tile(F16, 0)
+    """The 256x256 16-bit direct kernel with every tile shared out (fewer tiles
+    than CUs): several atomic segments per tile, ragged and whole (512^3-like)
+    shapes."""
+    t = 0
+    tile(F16, t)
     stream_k(1)
     dt = torch.float16 if which == "f16" else torch.bfloat16
     A = rand((M, K), 161).to(dt)
@@ -915,7 +917,7 @@ def test_16bit_stream_k(which, trans_b, M, N, K, alpha, beta, tile, stream_k):
     got = run_16(which, trans_b, A, B, alpha, beta, C if beta else None)
     R, T = oracle.gemm(bits16(A), bits16(B), alpha, beta, np32(C), bf16=which == "bf16",
                        b_trans=trans_b)
-    assert_close(got, R, T, f"{which} tb={trans_b} stream-K {M}x{N}x{K} a={alpha} b={beta}")
+    assert_close(got, R, T, f"{which} tb={trans_b} tile {t} stream-K {M}x{N}x{K} a={alpha} b={beta}")
 
 
 @pytest.mark.parametrize("which,trans_b", [("f16", False), ("bf16", True)])
