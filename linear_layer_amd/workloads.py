@@ -70,6 +70,11 @@ WORKLOADS = {
     # many small products in one batched call: 256 independent 256^3 FP32 GEMMs
     "gemm_f32_batched_256x256x256_b256": Workload(9, "gemm_f32_batched_256x256x256_b256",
                                                   "gemm_f32_batched", 256, 256, 256, batch=256),
+    # one GPU's share when the 4096^3 product is split 8 ways along M, and when
+    # the fully-connected layer is split 8 ways along N (its output features)
+    "gemm_f32_512x4096x4096": Workload(10, "gemm_f32_512x4096x4096", "gemm_f32", 512, 4096, 4096),
+    "linear_relu_2047x1376x4096": Workload(11, "linear_relu_2047x1376x4096", "linear", 2047, 1376, 4096,
+                                           act=1, scale=1.0 / 64.0),
 }
 
 HALF_KINDS = ("gemm_f16f32", "gemm_bf16f32", "gemm_f16f32_nt")

@@ -1006,7 +1006,8 @@ def checksums(gpu, A64, B64, alpha=1.0, beta=0.0, C64=None, bias=None):
     assert np.all(np.abs(g.sum(axis=0) - col) <= slack_c), "column checksums"
 
 
-@pytest.mark.parametrize("name", ["gemm_f32_256", "gemm_f32_1024_ab", "gemm_f32_4096"])
+@pytest.mark.parametrize("name", ["gemm_f32_256", "gemm_f32_1024_ab", "gemm_f32_4096",
+                                  "gemm_f32_512x4096x4096"])
 def test_full_gemm_f32(name):
     w = wl.WORKLOADS[name]
     x = wl.make_inputs(w)
@@ -1022,8 +1023,9 @@ def test_full_gemm_f32(name):
     checksums(got, np32(A).astype(np.float64), np32(B).astype(np.float64), w.alpha, w.beta, C64)
 
 
-def test_full_linear():
-    w = wl.WORKLOADS["linear_relu_2047x4096x11008"]
+@pytest.mark.parametrize("name", ["linear_relu_2047x4096x11008", "linear_relu_2047x1376x4096"])
+def test_full_linear(name):
+    w = wl.WORKLOADS[name]
     x = wl.make_inputs(w)
     X, W, b = x["A"], x["B"], x["bias"]
     got = run_linear(X, W, b, w.act)
