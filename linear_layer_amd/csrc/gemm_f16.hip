@@ -273,30 +273,32 @@ gemm_f16_kernel(GemmParams p)
 
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS FP16 kernel (256x256 block tile, 128-bit-aligned operands).
+// Direct-to-LDS FP16 kernel (BM x BN = 256x256 or 128x128 block tile,
+// 128-bit-aligned operands).
 //
 // Both operands travel global -> LDS with global_load_lds_dwordx4, so no
-// registers hold prefetched tiles and the 128 accumulators per lane leave room
-// for two register sets of MFMA operands.
+// registers hold prefetched tiles and the accumulators (128 per lane for a
+// 128x64 wave block) leave room for two register sets of MFMA operands.
 //
 // The inner product runs on v_mfma_f32_16x16x32 (MF = 16; MF = 32 selects
 // v_mfma_f32_32x32x16, the same 8 k-values per lane over half the k-step).
 // Both reach the same peak rate, but in a register-only loop over changing
 // operands on all CUs the 16x16 form sustained about 1.5x the 32x32 one (the
-// chip holds a higher clock), and in this kernel it measured 3-10 % faster. B keeps its row-major [k][n] layout
-// in LDS; the MFMA's B operand (8 consecutive k of one column per lane) is
-// read with ds_read_b64_tr_b16, gfx950's transposing LDS load: within each
+// chip holds a higher clock), and in this kernel it measured 3-10 % faster.
+//
+// B keeps its row-major [k][n] layout in LDS; the MFMA's B operand (8
+// consecutive k of one column per lane) is read with ds_read_b64_tr_b16, gfx950's transposing LDS load: within each
 // group of 16 lanes, lane i receives element i%4 of the 8-byte rows that lanes
 // i/4, 4+i/4, 8+i/4 and 12+i/4 address. If lane j points at
 // B[kb + j/4][nb + 4*(j%4)], lane i therefore receives B[kb .. kb+3][nb + i].
 //
 // LDS, per stage of BK k-values (CPR = BK/8 16-byte chunks per A row):
-//   A: 256 rows x 2*BK bytes; chunks XOR-swizzled by (row / (16/CPR)) % CPR,
+//   A: BM rows x 2*BK bytes; chunks XOR-swizzled by (row / (16/CPR)) % CPR,
 //      so the 16 lanes one LDS cycle serves (16 consecutive rows, one logical
 //      chunk) hit 16 different 16-byte bank groups (measured conflict-free).
 //      One copy (KiB) = 64/CPR rows; lane l fills row l/CPR, slot l%CPR, and
 //      fetches the logical chunk that the swizzle puts in that slot.
-//   B: BK rows x 512 bytes; 32-byte units XOR-swizzled per k-row. A
+//   B: BK rows x 2*BN bytes; 32-byte units XOR-swizzled per k-row. A
 //      transposing read is served 32 lanes (256 bytes) per LDS cycle: two
 //      16-lane groups, each reading one 32-byte unit of four k-rows.
 //      MF = 32: the groups read units u and u+1 (u even) of the same rows;
@@ -306,7 +308,9 @@ gemm_f16_kernel(GemmParams p)
 //      a two-way conflict, measured).
 //      MF = 16: the groups read the same unit u of rows k..k+3 and k+8..k+11;
 //      XOR by 2*(k%4) + (k/8)%2 sends them to u^{0,2,4,6} and u^{1,3,5,7}.
-//      One copy = 2 rows; lane l fills row l/32, bytes 16*(l%32) .. +15.
+//      (With BN = 128 a k-row is one bank line; with 256 the XOR stays in
+//      its half.) One copy = 1024/(2*BN) rows; lane l fills row l/(BN/8),
+//      bytes 16*(l%(BN/8)) .. +15.
 // NBUF stages form a ring. A stage holds BK/32 k-steps (BK/16 with MF = 32);
 // each step's operands are read while the previous step's MFMAs run. The
 // stage's barrier sits before its last step, whose operands are then in
@@ -317,12 +321,16 @@ gemm_f16_kernel(GemmParams p)
 // during those MFMAs too, so no LDS latency is exposed after a barrier.
 //
 // With BT (B given N-by-K, k contiguous) B is copied and read exactly like A:
-// 256 rows x 2*BK bytes, the same swizzle, 128-bit operand reads, no
+// BN rows x 2*BK bytes, the same swizzle, 128-bit operand reads, no
 // transposing loads.
 //
-// The workgroup is a WGM x WGN grid of waves, each owning a (256/WGM) x
-// (256/WGN) block: 2 x 2 runs one wave per SIMD; with 8 waves, two per SIMD,
-// one wave's MFMAs can run while the other waits to issue its copies.
+// The workgroup is a WGM x WGN grid of waves, each owning a (BM/WGM) x
+// (BN/WGN) block, with WPE waves per SIMD: 256x256 runs 2 x 4 waves, two per
+// SIMD, so one wave's MFMAs can run while the other waits to issue its
+// copies; 128x128 runs 2 x 2 waves and two workgroups per CU.
+//
+// SK: a stream-K launch (whole tiles first, then sharing workgroups that add
+// partial sums of (tile, k-range) segments atomically).
 //
 // IN (interior): launched only when every tile lies inside M and N and every
 // workgroup's K range is a whole number of stages; the copies then need no
