@@ -30,8 +30,11 @@ extern "C" {
 #define LL_OK 0
 #define LL_ERR_INVALID_VALUE 1   /* negative dimension, leading dimension too small,
                                     NULL pointer that would be dereferenced, pointer not
-                                    aligned to its element size, unknown activation, or
-                                    an output range overlapping an input range */
+                                    aligned to its element size, unknown activation,
+                                    an output range overlapping an input range, or an
+                                    output whose tiles exceed one launch's grid (only
+                                    extreme shapes: M or N within about 2^8 of 2^31
+                                    with the other one small) */
 #define LL_ERR_NO_DEVICE 2       /* no HIP device is current / visible */
 #define LL_ERR_UNSUPPORTED_ARCH 3/* the current device is not gfx950 (MI355X class) */
 #define LL_ERR_LAUNCH 4          /* the HIP runtime reported an error at launch */

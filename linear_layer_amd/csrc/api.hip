@@ -215,7 +215,9 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
         if (t_ov >= 0 && t != t_ov)
             continue;
         const TileInfo &ti = tiles[t];
-        const int64_t tiles_mn = (int64_t)((M + ti.bm - 1) / ti.bm) * ((N + ti.bn - 1) / ti.bn);
+        const int64_t tiles_mn = (int64_t)cdiv(M, ti.bm) * cdiv(N, ti.bn);
+        if (tiles_mn > max_grid_x(ti.threads))
+            continue;   // more workgroups than one launch can hold
         for (int s = 1; s <= kMaxSplits; ++s) {
             if (s_ov >= 1 && s != s_ov)
                 continue;
@@ -250,7 +252,7 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
             const int64_t slots = (int64_t)cus * ti.wg_per_cu;
             const int64_t rounds = tiles_mn / slots, rest = tiles_mn - rounds * slots;
             const int64_t units = ((int64_t)K + kSkUnit - 1) / kSkUnit;
-            if (rest > 0 && units >= 2 && tiles_mn <= kMaxTiles) {
+            if (rest > 0 && units >= 2 && tiles_mn + slots <= max_grid_x(ti.threads)) {
                 const int64_t grid = rest * units < slots ? rest * units : slots;
                 const int64_t per_wg = (rest * units + grid - 1) / grid;
                 const double work = (double)ti.bm * ti.bn * K;
@@ -273,6 +275,8 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
     // stream-K forced: its best plan whenever the shape allows one
     if (have_sk && (sk_ov == 1 || !have || best_sk_cost < best_cost))
         best = best_sk;
+    else if (!have)
+        best.tile = -1;   // no tile's grid fits one launch (or the forced one does not)
     if (best.k_split <= 0)
         best.k_split = 1;
     return best;
@@ -324,8 +328,8 @@ hipError_t run_one(GemmParams p, const Plan &pl, bool vec, hipStream_t s, launch
 // Tile grid of a plan's tile shape, for the per-tile passes.
 GemmParams with_tile_grid(GemmParams p, const TileInfo &ti)
 {
-    p.tiles_m = (p.M + ti.bm - 1) / ti.bm;
-    p.tiles_n = (p.N + ti.bn - 1) / ti.bn;
+    p.tiles_m = cdiv(p.M, ti.bm);
+    p.tiles_n = cdiv(p.N, ti.bn);
     return p;
 }
 
@@ -420,6 +424,8 @@ static int gemm_f32_impl(int M, int N, int K, float alpha, const float *A, int l
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     const Plan pl =
         plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false, bat.count, vec);
+    if (pl.tile < 0)
+        return LL_ERR_INVALID_VALUE;
     return launch_status(run_gemm(p, pl, vec, s, bt ? launch_gemm_f32_bt : launch_gemm_f32, 4, bat,
                                   &kF32Tiles[pl.tile]));
 }
@@ -456,6 +462,8 @@ static int gemm_16(int M, int N, int K, float alpha, const uint16_t *A, int lda,
                      batch_aligned(bat, 2);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false, bat.count, vec);
+    if (pl.tile < 0)
+        return LL_ERR_INVALID_VALUE;
     return launch_status(run_gemm(p, pl, vec, s, launch, 2, bat, &kF16Tiles[pl.tile]));
 }
 
@@ -542,6 +550,8 @@ static int linear_impl(int M, int N, int K, const float *X, int ldx, const float
     const launch_fn launch = wt ? launch_gemm_f32_bt : launch_gemm_f32;
     const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU, 1,
                          vec);
+    if (pl.tile < 0)
+        return LL_ERR_INVALID_VALUE;
     if (pl.sk_grid > 0)
         return launch_status(run_stream_k(p, pl, kF32Tiles[pl.tile], EPI_LINEAR, TILE_BIAS,
                                           act == LL_ACT_RELU, vec, s, launch));
@@ -620,9 +630,12 @@ static Plan chosen_plan(int dtype, int M, int N, int K, int batch, int num_cus, 
     if (!*ok)
         return Plan{-1, -1, 0};
     const int cus = num_cus > 0 ? num_cus : 256;
-    if (base == LL_DTYPE_F32)
-        return plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, relu, batch, true);
-    return plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch, true);
+    const Plan pl = base == LL_DTYPE_F32
+                        ? plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, relu, batch, true)
+                        : plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch, true);
+    if (pl.tile < 0)
+        *ok = false;
+    return pl;
 }
 
 int ll_chosen_tile(int dtype, int M, int N, int K, int batch, int num_cus)
@@ -648,7 +661,7 @@ int ll_chosen_stream_k(int dtype, int M, int N, int K, int batch, int num_cus)
     if (p.sk_grid == 0)
         return 0;
     const TileInfo &ti = (dtype & 0xFF) == LL_DTYPE_F32 ? kF32Tiles[p.tile] : kF16Tiles[p.tile];
-    return (int)((int64_t)((M + ti.bm - 1) / ti.bm) * ((N + ti.bn - 1) / ti.bn) - p.dp_tiles);
+    return (int)((int64_t)cdiv(M, ti.bm) * cdiv(N, ti.bn) - p.dp_tiles);
 }
 
 int ll_set_stream_k(int mode)

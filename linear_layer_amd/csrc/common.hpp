@@ -52,6 +52,13 @@ constexpr int kSkUnit = 64;
 // Strided batch: workgroups with blockIdx.z = i compute item i, whose A, B and
 // C start stride_{a,b,c}*i bytes after the first item's (page "GEMM 优化详解",
 // section "矩阵大小选择策略": small products are run as one batched GEMM).
+// ceil(a / b) for a >= 0, b > 0, without the overflow of (a + b - 1) / b
+// when a is close to INT_MAX.
+__host__ __device__ constexpr int cdiv(int a, int b)
+{
+    return a / b + (a % b != 0);
+}
+
 __device__ __forceinline__ void select_batch(GemmParams &p)
 {
     const int64_t z = blockIdx.z;
@@ -119,7 +126,7 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int &tm, int &t
 __device__ __forceinline__ bool sk_segment(const GemmParams &p, int seg, int &tm, int &tn, int &kb,
                                            int &k_len)
 {
-    const int units = (p.K + kSkUnit - 1) / kSkUnit;
+    const int units = cdiv(p.K, kSkUnit);
     const int64_t total = (int64_t)p.sk_tiles * units;
     const int64_t w = (int64_t)blockIdx.x - p.sk_block, nw = (int64_t)gridDim.x - p.sk_block;
     int64_t u0 = total * w / nw;

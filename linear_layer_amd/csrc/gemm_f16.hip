@@ -225,7 +225,7 @@ gemm_f16_kernel(GemmParams p)
                 acc[i][j][r] = 0.0f;
 
     const int h = lane >> 5, l32 = lane & 31;
-    const int nk = (K + BK - 1) / BK;
+    const int nk = cdiv(K, BK);
 
     gload(0);
     lstore(0);
@@ -535,7 +535,7 @@ gemm_f16_direct_kernel(GemmParams p)
     };
     static_assert(NBUF - 1 <= 3, "wait_stages covers at most three stages in flight");
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = cdiv(K, BK);
     for (int st = 0; st < NBUF; ++st)
         if (st < nk) {
 #pragma unroll
@@ -641,8 +641,8 @@ template <class T, int WPE, bool BF16, bool BT>
 static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
     GemmParams p = p0;
-    p.tiles_m = (p.M + T::BM - 1) / T::BM;
-    p.tiles_n = (p.N + T::BN - 1) / T::BN;
+    p.tiles_m = cdiv(p.M, T::BM);
+    p.tiles_n = cdiv(p.N, T::BN);
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ || p.grid_x != 0 || p.sk_tiles != 0)
         return hipErrorInvalidValue;   // the register-staged kernels run whole grids only
@@ -672,7 +672,8 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // 6144^3) it lost to the best other plan by 4-10 %, its many short shared
 // segments paying more per atomic byte.
 const TileInfo kF16Tiles[kF16NumTiles] = {
-    {F16_L::BM, F16_L::BN, 1, 1.00f, 1.00f, "f16_256x256_direct"},
+    {F16_L::BM, F16_L::BN, 1, 1.00f, 1.00f, "f16_256x256_direct", 1, true,
+     64 * DirectCfg<256>::WGM * DirectCfg<256>::WGN},
     {F16_S::BM, F16_S::BN, 2, 0.45f, 0.88f, "f16_128x128x64", 1, false},
     {F16_XS::BM, F16_XS::BN, 2, 0.15f, 0.20f, "f16_64x64x64", 1, false},
 };
@@ -686,8 +687,8 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
     if (!vec)
         return launch_t<T, WPE_T, BF16, BT>(p0, epi, vec, s);
     GemmParams p = p0;
-    p.tiles_m = (p.M + BM - 1) / BM;
-    p.tiles_n = (p.N + BM - 1) / BM;
+    p.tiles_m = cdiv(p.M, BM);
+    p.tiles_n = cdiv(p.N, BM);
     int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
         return hipErrorInvalidValue;
@@ -698,6 +699,8 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
         return hipErrorInvalidValue;   // stream-K: the 256x256 tile only
     using Cfg = DirectCfg<BM>;
     static_assert(kSkUnit % Cfg::BK == 0, "stream-K segments are whole stages");
+    if (ntiles > max_grid_x(64 * Cfg::WGM * Cfg::WGN))
+        return hipErrorInvalidValue;
     const dim3 grid = gemm_grid(p, ntiles), block(64 * Cfg::WGM * Cfg::WGN);
     // every copy inside the matrices: whole tiles, whole stages in every K range
     const bool in = p.M % BM == 0 && p.N % BM == 0 && p.K % Cfg::BK == 0 && p.k_split % Cfg::BK == 0;

@@ -208,7 +208,7 @@ gemm_f32_kernel(GemmParams p)
                 acc[i][j][r] = 0.0f;
 
     const int h = lane >> 5, l32 = lane & 31;
-    const int nk = (K + BK - 1) / BK;
+    const int nk = cdiv(K, BK);
 
     gload(0);
     lstore(0);
@@ -368,7 +368,7 @@ gemm_f32_direct_kernel(GemmParams p)
     // This slice's part of the K range; every slice runs k_steps k-values.
     int k_steps = K;
     if (KS > 1) {
-        k_steps = ((K + KS - 1) / KS + BK - 1) / BK * BK;
+        k_steps = cdiv(cdiv(K, KS), BK) * BK;
         const int lo = slice * k_steps;
         kb += lo < K ? lo : K;
         K = K - lo < k_steps ? (K - lo > 0 ? K - lo : 0) : k_steps;
@@ -513,7 +513,7 @@ gemm_f32_direct_kernel(GemmParams p)
             __builtin_amdgcn_s_waitcnt(LL_VMCNT(0));
     };
 
-    const int nk = (k_steps + BK - 1) / BK;   // the same in every slice
+    const int nk = cdiv(k_steps, BK);   // the same in every slice
     for (int st = 0; st < NBUF; ++st)
         if (st < nk) {
 #pragma unroll
@@ -702,6 +702,8 @@ static int launch_checks(const GemmParams &p, int BM, int BN, int BK, int KS)
 template <int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, bool BT, int KS = 1>
 static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hipStream_t s)
 {
+    if (ntiles > max_grid_x(64 * WGM * WGN * KS))
+        return hipErrorInvalidValue;
     const dim3 grid = gemm_grid(p, ntiles), block(64 * WGM * WGN * KS);
     const int chk = launch_checks(p, BM, BN, BK, KS);
 #define LL_F32_DIRECT_C(E, SK, C) \
@@ -744,8 +746,8 @@ template <class T, int WPE, bool BT, int KS = 1>
 static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
     GemmParams p = p0;
-    p.tiles_m = (p.M + T::BM - 1) / T::BM;
-    p.tiles_n = (p.N + T::BN - 1) / T::BN;
+    p.tiles_m = cdiv(p.M, T::BM);
+    p.tiles_n = cdiv(p.N, T::BN);
     int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ)
         return hipErrorInvalidValue;
@@ -792,14 +794,14 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // second workgroup beside it} -- throughputs measured on MI355X relative to
 // the 256x256 tile.
 const TileInfo kF32Tiles[kF32NumTiles] = {
-    {F32_L::BM, F32_L::BN, 1, 1.00f, 1.00f, "f32_256x256"},
+    {F32_L::BM, F32_L::BN, 1, 1.00f, 1.00f, "f32_256x256", 1, true, 64 * WaveGridL<false>::M * WaveGridL<false>::N},
     {F32_M::BM, F32_M::BN, 2, 0.89f, 0.985f, "f32_256x128"},
     {F32_S::BM, F32_S::BN, 2, 0.80f, 0.94f, "f32_128x128"},
     {F32_XS::BM, F32_XS::BN, 2, 0.52f, 0.72f, "f32_64x64"},
     // K-sliced tiles (direct kernel only; the staged fallback runs the plain
     // tile): four slices of 64x64 (1024^3: 0.57), two of 128x128 (2048^3: 0.90).
-    {F32_XS::BM, F32_XS::BN, 1, 0.57f, 0.57f, "f32_64x64_k4", 4},
-    {F32_S::BM, F32_S::BN, 1, 0.90f, 0.90f, "f32_128x128_k2", 2},
+    {F32_XS::BM, F32_XS::BN, 1, 0.57f, 0.57f, "f32_64x64_k4", 4, true, 1024},
+    {F32_S::BM, F32_S::BN, 1, 0.90f, 0.90f, "f32_128x128_k2", 2, true, 512},
 };
 #endif
 

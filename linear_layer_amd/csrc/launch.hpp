@@ -15,6 +15,7 @@ struct TileInfo {
     const char *name;
     int k_slices = 1;  // K-slices inside the workgroup (such tiles take no stream-K share)
     bool stream_k = true;  // the tile's kernel can run a stream-K launch
+    int threads = 256;     // largest workgroup of the tile's kernels
 };
 
 constexpr int kF32NumTiles = 6;
@@ -35,10 +36,15 @@ hipError_t launch_gemm_bf16(const GemmParams &p, int tile, int epi, bool vec, hi
 hipError_t launch_gemm_f16_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
 hipError_t launch_gemm_bf16_bt(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s);
 
-// Largest grid y / z extent a launch may use, and the most output tiles
-// (grid x) a 256-thread launch may have (its work-item count must fit 32 bits).
+// Largest grid y / z extent a launch may use, and the most workgroups along
+// x a launch of `threads`-thread workgroups may have (its work-item count
+// along x must fit 32 bits).
 constexpr int kMaxGridZ = 65535;
-constexpr int64_t kMaxTiles = (int64_t)(0xffffffffu / 256u);
+constexpr int64_t max_grid_x(int threads)
+{
+    return (int64_t)(0xffffffffu / (unsigned)threads);
+}
+constexpr int64_t kMaxTiles = max_grid_x(256);
 
 // C = beta*C over an M x N matrix (beta == 0 writes zeros without reading C),
 // for each of `batch` matrices stride_c bytes apart.

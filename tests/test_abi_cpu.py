@@ -165,6 +165,23 @@ def test_no_device_is_a_status_not_an_abort():
     assert lib.linear_bias_act(4, 4, 4, PA, 4, PB, 4, None, 1, PC, 4, None) == ll.ERR_NO_DEVICE
 
 
+def test_plans_at_int32_limits():
+    """Tile counts are computed without overflow near 2^31, and a plan never has
+    more workgroups than one launch can hold: an output whose tiles cannot fit
+    gets no plan (-1), and the product call then returns LL_ERR_INVALID_VALUE."""
+    f32, f16 = ll.DTYPE_F32, ll.DTYPE_F16
+    big = 2 ** 31 - 1
+    t = ll.chosen_tile(f32, big, 4, 4, 256)
+    assert ll.tile_name(f32, t) == "f32_256x128"          # 8.4M tiles of 256 threads
+    assert ll.chosen_tile(f16, big - 512, 1, 1, 256) == 1   # 128x128: 16.8M tiles
+    for dt, shape in ((f32, (1, big, 1)), (f16, (big, 64, 64)), (f16, (1, big, 1))):
+        assert ll.chosen_tile(dt, *shape, 256) == -1
+        assert ll.chosen_split_k(dt, *shape, 256) == -1
+        assert ll.chosen_stream_k(dt, *shape, 256) == -1
+    # a deep K splits or streams without overflow
+    assert ll.chosen_tile(f32, 1, 1, big, 256) >= 0 and ll.chosen_tile(f16, 1, 1, big, 256) >= 0
+
+
 def test_tile_choice():
     f32, f16 = ll.DTYPE_F32, ll.DTYPE_F16
     names32 = [ll.tile_name(f32, t) for t in range(ll.num_tiles(f32))]

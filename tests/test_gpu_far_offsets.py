@@ -213,3 +213,35 @@ def test_batched_far_items(bufs, which):
     flat = bufs["C"].view(torch.float32)
     g = flat.as_strided((nb, 64), (stride, 1), m * n).cpu().view(torch.int32)
     assert torch.all(g == (NAN16 << 16 | NAN16)), "a write outside C"
+
+
+def test_rows_near_int_max():
+    """M = 2^31 - 1 (FP32, N = K = 4, 32 GB per operand): the last tile's row
+    indices, the tile count and the launch grid sit at the 32-bit limits. A
+    repeats a seeded 5-row integer pattern down its rows, so every output row
+    equals the pattern row m % 5: the oracle computes those five rows (and a
+    sample of rows at the end is compared with them), and the whole of C is
+    checked for that period."""
+    M, N, K = 2 ** 31 - 1, 4, 4
+    assert ll.chosen_tile(F32, M, N, K, torch.cuda.get_device_properties(0).multi_processor_count) >= 0
+    pat = wl.integers((5, K), 351, -2, 2)
+    Bh = wl.integers((K, N), 352, -2, 2)
+    q = -(-M // 5)
+    Ad = pat.to(DEV).repeat(q, 1)[:M]          # row m is pat[m % 5]
+    Cd = torch.full((M, N), float("nan"), device=DEV)
+    ll.gemm_f32(Ad, Bh.to(DEV), Cd)
+    torch.cuda.synchronize()
+    R, _ = oracle.gemm(pat.numpy(), Bh.numpy())
+    want = torch.from_numpy(R.astype(np.float32)).to(DEV)
+    rows = np.concatenate([np.arange(5), np.arange(M - 300, M), np.random.default_rng(353).integers(0, M, 300)])
+    got = Cd[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    assert np.array_equal(got, R.astype(np.float32)[rows % 5]), "sampled rows"
+    chunk = 5 * (1 << 24)
+    for s0 in range(0, M, chunk):
+        c = Cd[s0:s0 + chunk]
+        full = (c.shape[0] // 5) * 5
+        assert torch.equal(c[:full].view(-1, 5, N), want.expand(full // 5, 5, N)), f"rows from {s0}"
+        if full < c.shape[0]:
+            assert torch.equal(c[full:], want[:c.shape[0] - full]), "tail rows"
+    del Ad, Cd
+    torch.cuda.empty_cache()
