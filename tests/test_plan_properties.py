@@ -1,0 +1,92 @@
+"""Properties every plan of the tile / K-split / stream-K planner must have,
+over random shapes (host logic only: the plan queries run without a GPU).
+
+For any product the planner either returns a usable plan or none (-1, for
+shapes whose tiles cannot fit one launch's grid); a usable plan names a tile
+of the data type's table whose grid fits, splits K into at most 16 parts of
+at least one 64-deep stage (unless forced), shares out stream-K tiles only
+for single products without a K-split, never shares out more tiles than the
+product has, and honours forced settings.
+"""
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import linear_layer_amd as ll
+
+F32, F16 = ll.DTYPE_F32, ll.DTYPE_F16
+TILE_SHAPES = {
+    F32: [(256, 256), (256, 128), (128, 128), (64, 64), (64, 64), (128, 128)],
+    F16: [(256, 256), (128, 128), (64, 64)],
+}
+dims = st.one_of(st.integers(1, 300), st.integers(1, 20000), st.sampled_from([255, 256, 257, 2047, 4096, 11008]))
+
+
+def tiles_of(dt, t, M, N):
+    bm, bn = TILE_SHAPES[dt][t]
+    return -(-M // bm) * -(-N // bn)
+
+
+@pytest.fixture(autouse=True)
+def _automatic():
+    yield
+    for dt in (F32, F16):
+        ll.set_tile(dt, -1)
+    ll.set_split_k(-1)
+    ll.set_stream_k(-1)
+
+
+def test_table_shapes_match_names():
+    for dt, shapes in TILE_SHAPES.items():
+        assert ll.num_tiles(dt) == len(shapes)
+        for t, (bm, bn) in enumerate(shapes):
+            assert f"{bm}x{bn}" in ll.tile_name(dt, t)
+
+
+@settings(max_examples=400, deadline=None)
+@given(dt=st.sampled_from([F32, F16]), M=dims, N=dims, K=dims, batch=st.sampled_from([1, 1, 2, 7]),
+       cus=st.sampled_from([0, 256, 304, 64]), relu=st.booleans(), nk=st.booleans())
+def test_automatic_plans_are_well_formed(dt, M, N, K, batch, cus, relu, nk):
+    q = dt | (ll.PLAN_RELU if relu and dt == F32 else 0) | (ll.PLAN_B_NK if nk else 0)
+    t = ll.chosen_tile(q, M, N, K, cus, batch)
+    s = ll.chosen_split_k(q, M, N, K, cus, batch)
+    sk = ll.chosen_stream_k(q, M, N, K, cus, batch)
+    assert 0 <= t < ll.num_tiles(dt)                 # these shapes always fit
+    assert 1 <= s <= 16
+    if s > 1:
+        assert K >= 64 * (s - 1), "a split is at least one stage deep"
+    assert sk >= 0
+    if sk > 0:
+        assert batch == 1 and s == 1
+        assert sk <= tiles_of(dt, t, M, N)
+
+
+@settings(max_examples=200, deadline=None)
+@given(dt=st.sampled_from([F32, F16]), M=dims, N=dims, K=dims, data=st.data())
+def test_forced_settings_are_honoured(dt, M, N, K, data):
+    t = data.draw(st.integers(0, ll.num_tiles(dt) - 1))
+    ll.set_tile(dt, t)
+    assert ll.chosen_tile(dt, M, N, K, 256) == t
+    s = data.draw(st.integers(1, 16))
+    ll.set_split_k(s)
+    got = ll.chosen_split_k(dt, M, N, K, 256)
+    # the split length is ceil(K / s) rounded up to whole 64-deep stages, so
+    # the count may come out smaller
+    k_split = -(-(-(-K // s)) // 64) * 64
+    assert got == -(-K // k_split) and 1 <= got <= s
+    assert ll.chosen_stream_k(dt, M, N, K, 256) == 0   # a forced split excludes stream-K
+    ll.set_split_k(-1)
+    ll.set_stream_k(0)
+    assert ll.chosen_stream_k(dt, M, N, K, 256) == 0
+
+
+@settings(max_examples=100, deadline=None)
+@given(dt=st.sampled_from([F32, F16]), M=dims, N=dims, K=st.integers(128, 20000))
+def test_forced_stream_k_shares_only_leftover_tiles(dt, M, N, K):
+    ll.set_stream_k(1)
+    t = ll.chosen_tile(dt, M, N, K, 256)
+    sk = ll.chosen_stream_k(dt, M, N, K, 256)
+    assert ll.chosen_split_k(dt, M, N, K, 256) == 1 or sk == 0
+    if sk > 0:
+        tiles = tiles_of(dt, t, M, N)
+        slots = 256 * (1 if TILE_SHAPES[dt][t] == (256, 256) or (dt == F32 and t in (4, 5)) else 2)
+        assert sk == tiles % slots if tiles >= slots else sk == tiles
