@@ -502,6 +502,73 @@ def test_non_default_stream():
     assert_close(np32(C), R, T, "stream")
 
 
+def test_concurrent_streams_and_threads():
+    """Products of every kind running at the same time on two streams, issued
+    from two host threads: the library keeps no state between calls (beyond
+    the device-property cache), so each result matches the oracle."""
+    import threading
+    cases = []
+    shapes = [(600, 520, 200), (257, 300, 1000), (1024, 768, 512), (300, 264, 72)]
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = rand((M, K), 171 + 2 * i), rand((K, N), 172 + 2 * i)
+        cases.append(("f32", A, B, oracle.gemm(np32(A), np32(B))))
+        Ah, Bh = A.half(), B.half()
+        cases.append(("f16", Ah, Bh, oracle.gemm(bits16(Ah), bits16(Bh))))
+        Ab, Bb = A.bfloat16(), B.t().contiguous().bfloat16()
+        cases.append(("bf16_nt", Ab, Bb, oracle.gemm(bits16(Ab), bits16(Bb), bf16=True, b_trans=True)))
+        b = wl.bias_uniform(N, 180 + i)
+        cases.append(("linear", A, (B, b), oracle.linear(np32(A), np32(B), np32(b), 1)))
+    dev_in = [(kind, a.to(DEV), tuple(x.to(DEV) for x in bb) if isinstance(bb, tuple) else bb.to(DEV))
+              for kind, a, bb, _ in cases]
+    outs = [torch.full((a.shape[0], (bb[0] if isinstance(bb, tuple) else bb).shape[0 if kind.endswith("_nt") else 1]),
+                       float("nan"), device=DEV) for kind, a, bb in dev_in]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    errors = []
+
+    def worker(w):
+        try:
+            with torch.cuda.stream(streams[w]):
+                for rep in range(3):
+                    for i in range(w, len(dev_in), 2):
+                        kind, a, bb = dev_in[i]
+                        if kind == "f32":
+                            ll.gemm_f32(a, bb, outs[i])
+                        elif kind == "f16":
+                            ll.gemm_f16f32(a, bb, outs[i])
+                        elif kind == "bf16_nt":
+                            ll.gemm_bf16f32_nt(a, bb, outs[i])
+                        else:
+                            ll.linear_bias_act(a, bb[0], bb[1], 1, outs[i])
+            streams[w].synchronize()
+        except Exception as e:   # reported below, in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(w,)) for w in (0, 1)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for (kind, _, _, (R, T)), out in zip(cases, outs):
+        assert_close(np32(out), R, T, f"concurrent {kind} {tuple(out.shape)}")
+
+
+def test_16bit_non_default_stream():
+    M, N, K = 512, 384, 256
+    A, B = rand((M, K), 38).half(), rand((K, N), 39).half()
+    s = torch.cuda.Stream()
+    C = torch.empty((M, N), device=DEV)
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        ll.gemm_f16f32(Ad, Bd, C)
+    s.synchronize()
+    R, T = oracle.gemm(bits16(A), bits16(B))
+    assert_close(np32(C), R, T, "16-bit stream")
+
+
 def test_errors_raise():
     A = torch.zeros((4, 4), device=DEV)
     with pytest.raises(ll.LinearLayerError):
