@@ -218,6 +218,8 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
         const int64_t tiles_mn = (int64_t)cdiv(M, ti.bm) * cdiv(N, ti.bn);
         if (tiles_mn > max_grid_x(ti.threads))
             continue;   // more workgroups than one launch can hold
+        if (K < ti.min_k && t_ov != t)
+            continue;   // K too short for the tile's K-slices (unless forced)
         for (int s = 1; s <= kMaxSplits; ++s) {
             if (s_ov >= 1 && s != s_ov)
                 continue;

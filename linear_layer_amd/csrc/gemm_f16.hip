@@ -336,11 +336,11 @@ gemm_f16_kernel(GemmParams p)
 // workgroup's K range is a whole number of stages; the copies then need no
 // bounds selects.
 template <int EPI, bool BF16, bool BT, int BM, int BN, int BK, int NBUF, int WGM, int WGN, int WPE,
-          bool IN, int MF, bool SK>
-__global__ void __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+          bool IN, int MF, bool SK, int KS>
+__global__ void __launch_bounds__(64 * WGM * WGN * KS) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f16_direct_kernel(GemmParams p)
 {
-    constexpr int NW = WGM * WGN;
+    constexpr int NW = WGM * WGN;   // waves of one K-slice
     static_assert(BM == BN && (BN == 128 || BN == 256), "square tiles of 128 or 256");
     constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / MF, FN = WTN / MF;
     constexpr int KSTEP = MF == 32 ? 16 : 32;             // k per MFMA
@@ -359,11 +359,15 @@ gemm_f16_direct_kernel(GemmParams p)
                       (MF == 16 || MF == 32),
                   "copies cover the stage; each wave's rows start at a multiple of 16");
     static_assert((NBUF - 1) * PER_STAGE <= 63, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) uint16_t As[NBUF][A_STAGE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Bs[NBUF][B_STAGE];
+    static_assert(KS >= 1 && (KS == 1 || !SK), "K-slices take no stream-K share");
+    static_assert((KS - 1) * NW * FM * FN * AccBlock<MF>::R * 64 * 4 <= KS * NBUF * A_STAGE * 2,
+                  "slice partials fit in the A rings");
+    __shared__ __attribute__((aligned(1024))) uint16_t As[KS][NBUF][A_STAGE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Bs[KS][NBUF][B_STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slice = wave_wg / NW, wave = wave_wg % NW;   // wave within the slice
     const int wm = wave / WGN, wn = wave % WGN;
     select_batch(p);
     // One tile per workgroup, or (a stream-K launch's sharing workgroups, from
@@ -382,6 +386,14 @@ gemm_f16_direct_kernel(GemmParams p)
             break;
         tile_coords(p, tm, tn);
         kb = split_range(p, K);
+    }
+    // This slice's part of the K range; every slice runs k_steps k-values.
+    int k_steps = K;
+    if (KS > 1) {
+        k_steps = cdiv(cdiv(K, KS), BK) * BK;
+        const int lo = slice * k_steps;
+        kb += lo < K ? lo : K;
+        K = K - lo < k_steps ? (K - lo > 0 ? K - lo : 0) : k_steps;
     }
     const int m0 = tm * BM, n0 = tn * BN;
     const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A) + kb;
@@ -419,7 +431,7 @@ gemm_f16_direct_kernel(GemmParams p)
         b_src[j] = B + (int64_t)kr * p.ldb + col;
         b_col_ok[j] = col < N;
     }
-    const uint32_t as_base = lds_addr(&As[0][0]), bs_base = lds_addr(&Bs[0][0]);
+    const uint32_t as_base = lds_addr(&As[slice][0][0]), bs_base = lds_addr(&Bs[slice][0][0]);
 
     // Copy c (A: 0 .. COPIES_A-1, then B) of the stage at k0 into buffer buf.
     // Every copy is one global_load_lds on every lane: lanes whose 16 bytes
@@ -474,8 +486,8 @@ gemm_f16_direct_kernel(GemmParams p)
 
     // Operands of k-step s (k = KSTEP*s + 8*grp + 0..7) of the stage in buffer buf.
     auto read_step = [&](int buf, int s, f16x8 (&af)[FM], f16x8 (&bf)[FN]) {
-        const uint16_t *as = As[buf];
-        const uint16_t *bs = Bs[buf];
+        const uint16_t *as = As[slice][buf];
+        const uint16_t *bs = Bs[slice][buf];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
             const int row = wm * WTM + fm * MF + lrow;
@@ -535,7 +547,7 @@ gemm_f16_direct_kernel(GemmParams p)
     };
     static_assert(NBUF - 1 <= 3, "wait_stages covers at most three stages in flight");
 
-    const int nk = cdiv(K, BK);
+    const int nk = cdiv(k_steps, BK);   // the same in every slice
     for (int st = 0; st < NBUF; ++st)
         if (st < nk) {
 #pragma unroll
@@ -588,6 +600,36 @@ gemm_f16_direct_kernel(GemmParams p)
         }
         __builtin_amdgcn_s_setprio(0);
         buf = nbuf;
+    }
+
+    if constexpr (KS > 1) {
+        // Slices 1.. park their partial tiles in the (now idle) A rings, one
+        // float per lane per slot, then slice 0 adds them in slice order.
+        float *part = reinterpret_cast<float *>(&As[0][0][0]);
+        constexpr int R = AccBlock<MF>::R, SLOTS = FM * FN * R;
+        __syncthreads();   // every slice is done reading its ring
+        if (slice > 0) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        part[((((slice - 1) * NW + wave) * SLOTS) + (fm * FN + fn) * R + r) * 64 + lane] =
+                            acc[fm][fn][r];
+        }
+        __syncthreads();
+        if (slice > 0)
+            return;   // no barrier follows
+        for (int sl = 1; sl < KS; ++sl)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[fm][fn][r] +=
+                            part[((((sl - 1) * NW + wave) * SLOTS) + (fm * FN + fn) * R + r) * 64 + lane];
     }
 
 #pragma unroll
@@ -667,7 +709,9 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // paired 0.91 on 8192^3 and 0.86 on 4096^3; alone 0.50 on 2048^3 and 0.62
 // with K = 8192, entered as 0.45 so that a last half round of lone 128x128
 // workgroups (6144^3: 4.5 rounds, 1048 TFLOP/s) loses to 256x256 with
-// stream-K (1140). 64x64 (register-staged): about 0.20 paired.
+// stream-K (1140). 64x64 (register-staged): about 0.20 paired, 0.10 alone
+// (1024^3). 128x128 in two K-slices (one workgroup per CU): 0.56 on 2048^3,
+// 0.76 with K = 8192, 0.62-0.73 on 4096^3-8192^3.
 // Stream-K runs on the 256x256 tile only: on 128x128 tiles (3072^3, 5120^3,
 // 6144^3) it lost to the best other plan by 4-10 %, its many short shared
 // segments paying more per atomic byte.
@@ -675,12 +719,17 @@ const TileInfo kF16Tiles[kF16NumTiles] = {
     {F16_L::BM, F16_L::BN, 1, 1.00f, 1.00f, "f16_256x256_direct", 1, true,
      64 * DirectCfg<256>::WGM * DirectCfg<256>::WGN},
     {F16_S::BM, F16_S::BN, 2, 0.45f, 0.88f, "f16_128x128x64", 1, false},
-    {F16_XS::BM, F16_XS::BN, 2, 0.15f, 0.20f, "f16_64x64x64", 1, false},
+    {F16_XS::BM, F16_XS::BN, 2, 0.10f, 0.20f, "f16_64x64x64", 1, false},
+    // 128x128 in two K-slices (direct kernel only; the staged fallback runs
+    // the plain tile): eight waves, one workgroup per CU; only with at least
+    // 8 stages of 64 per slice (below, 0.5-1 us slower than plain 128x128)
+    {F16_S::BM, F16_S::BN, 1, 0.60f, 0.60f, "f16_128x128_k2", 2, false, 512, 2 * 8 * 64},
 };
 
-// The direct kernel on BM x BM tiles for 128-bit-aligned operands; the
-// register-staged kernel of the same tile (T) otherwise.
-template <bool BF16, bool BT, int BM, class T, int WPE_T>
+// The direct kernel on BM x BM tiles (KS K-slices) for 128-bit-aligned
+// operands; the register-staged kernel of the same tile (T, without slices)
+// otherwise.
+template <bool BF16, bool BT, int BM, class T, int WPE_T, int KS = 1>
 static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
     static_assert(T::BM == BM && T::BN == BM, "fallback tile");
@@ -695,18 +744,19 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
     if (p.grid_x > 0)
         ntiles = p.grid_x;   // a stream-K launch: whole tiles, then the sharing workgroups
     const bool sk = p.sk_tiles > 0;
-    if (sk && (BM != 256 || epi == EPI_ATOMIC || p.batch != 1))
+    if (sk && (BM != 256 || KS != 1 || epi == EPI_ATOMIC || p.batch != 1))
         return hipErrorInvalidValue;   // stream-K: the 256x256 tile only
     using Cfg = DirectCfg<BM>;
     static_assert(kSkUnit % Cfg::BK == 0, "stream-K segments are whole stages");
-    if (ntiles > max_grid_x(64 * Cfg::WGM * Cfg::WGN))
+    if (ntiles > max_grid_x(64 * Cfg::WGM * Cfg::WGN * KS))
         return hipErrorInvalidValue;
-    const dim3 grid = gemm_grid(p, ntiles), block(64 * Cfg::WGM * Cfg::WGN);
+    const dim3 grid = gemm_grid(p, ntiles), block(64 * Cfg::WGM * Cfg::WGN * KS);
     // every copy inside the matrices: whole tiles, whole stages in every K range
-    const bool in = p.M % BM == 0 && p.N % BM == 0 && p.K % Cfg::BK == 0 && p.k_split % Cfg::BK == 0;
+    const int kq = KS * Cfg::BK;   // every slice's K range a whole number of stages
+    const bool in = p.M % BM == 0 && p.N % BM == 0 && p.K % kq == 0 && p.k_split % kq == 0;
 #define LL_DIRECT_K(E, IN, SK) \
     hipLaunchKernelGGL((gemm_f16_direct_kernel<E, BF16, BT, BM, BM, Cfg::BK, Cfg::NBUF, Cfg::WGM, \
-                                               Cfg::WGN, Cfg::WPE, IN, Cfg::MF, SK>), \
+                                               Cfg::WGN, Cfg::WPE, IN, Cfg::MF, SK, KS>), \
                        grid, block, 0, s, p)
 #define LL_DIRECT(E, SK) \
     do { \
@@ -715,7 +765,7 @@ static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStre
         else \
             LL_DIRECT_K(E, false, SK); \
     } while (0)
-    if constexpr (BM == 256) {
+    if constexpr (BM == 256 && KS == 1) {
         if (sk) {
             // whole tiles with `epi`, shared ones added atomically
             if (epi == EPI_GEMM_BETA0)
@@ -743,6 +793,7 @@ static hipError_t launch_16(const GemmParams &p, int tile, int epi, bool vec, hi
     switch (tile) {
     case 0: return launch_direct<BF16, BT, 256, F16_L, 1>(p, epi, vec, s);
     case 1: return launch_direct<BF16, BT, 128, F16_S, 2>(p, epi, vec, s);
+    case 3: return launch_direct<BF16, BT, 128, F16_S, 2, 2>(p, epi, vec, s);
     default: return launch_t<F16_XS, 2, BF16, BT>(p, epi, vec, s);
     }
 }

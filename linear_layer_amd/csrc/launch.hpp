@@ -16,10 +16,11 @@ struct TileInfo {
     int k_slices = 1;  // K-slices inside the workgroup (such tiles take no stream-K share)
     bool stream_k = true;  // the tile's kernel can run a stream-K launch
     int threads = 256;     // largest workgroup of the tile's kernels
+    int min_k = 0;         // K-sliced tiles: the K below which slices get too few stages
 };
 
 constexpr int kF32NumTiles = 6;
-constexpr int kF16NumTiles = 3;
+constexpr int kF16NumTiles = 4;
 extern const TileInfo kF32Tiles[kF32NumTiles];
 extern const TileInfo kF16Tiles[kF16NumTiles];
 

@@ -213,19 +213,23 @@ def test_tile_choice():
     # 16-bit: 6144^2 is 576 tiles of 256x256, 2.25 rounds: two run whole, 64
     # tiles are shared out; 3072^3 (144 tiles, one short round) and 5120^3
     # (400 tiles) run whole; a K-split is not worth its passes at the 16-bit
-    # rate; 2048^3 and thin products take the 128x128 direct tile
+    # rate; 2048^3 and the thin 512x4096x4096 take 128x128 in two K-slices
+    # (one lone workgroup per CU otherwise), 1024x8192x8192 plain 128x128
+    # (two per CU), tiny products plain 128x128 (too few stages per slice)
     assert choice(f16, 6144, 6144, 6144) == ("f16_256x256_direct", 1)
     assert ll.chosen_stream_k(f16, 6144, 6144, 6144, 256) == 64
     assert choice(f16, 3072, 3072, 3072) == ("f16_256x256_direct", 1)
     assert choice(f16, 5120, 5120, 5120) == ("f16_256x256_direct", 1)
     assert ll.chosen_stream_k(f16, 3072, 3072, 3072, 256) == 0
     assert ll.chosen_stream_k(f16, 5120, 5120, 5120, 256) == 0
-    assert choice(f16, 2048, 2048, 2048) == ("f16_128x128x64", 1)
+    assert choice(f16, 2048, 2048, 2048) == ("f16_128x128_k2", 1)
+    assert choice(f16, 512, 4096, 4096) == ("f16_128x128_k2", 1)
     assert choice(f16, 1024, 8192, 8192) == ("f16_128x128x64", 1)
+    assert choice(f16, 512, 512, 512) == ("f16_128x128x64", 1)
     # only the 256x256 16-bit tile takes a stream-K share, even when forced
     ll.set_stream_k(1)
     try:
-        for t in (1, 2):
+        for t in (1, 2, 3):
             ll.set_tile(f16, t)
             assert ll.chosen_stream_k(f16, 2047, 11008, 4096, 256) == 0
         ll.set_tile(f16, 0)
@@ -237,8 +241,9 @@ def test_tile_choice():
     # the workgroup (K-slices), across workgroups, or both
     assert choice(f32, 1024, 1024, 1024) == ("f32_64x64_k4", 1)
     assert choice(f32, 2048, 2048, 2048) == ("f32_128x128_k2", 1)
-    assert choice(f32, 256, 256, 256) == ("f32_64x64_k4", 1)   # one launch: launch-bound size
-    assert choice(f32, 512, 512, 512) == ("f32_64x64_k4", 4)
+    # below 8 stages per slice the slices cost more than they save
+    assert choice(f32, 256, 256, 256) == ("f32_64x64", 1)   # one launch: launch-bound size
+    assert choice(f32, 512, 512, 512) == ("f32_64x64", 4)
     # K-sliced tiles take no stream-K share
     ll.set_tile(f32, 4)
     ll.set_stream_k(1)
@@ -265,10 +270,10 @@ def test_tile_choice():
         ll.set_split_k(-1)
     assert ll.chosen_tile(f32, 4096, 4096, 4096, 256) == 0
     # a batch counts all its items' tiles: 256 items of 256^3 fill the CUs
-    # with 256x256 tiles, one item alone takes small K-sliced tiles
+    # with 256x256 tiles, one item alone takes small tiles
     assert ll.chosen_tile(f32, 256, 256, 256, 256, batch=256) == 0
     assert ll.chosen_split_k(f32, 256, 256, 256, 256, batch=256) == 1
-    assert ll.tile_name(f32, ll.chosen_tile(f32, 256, 256, 256, 256, batch=1)) == "f32_64x64_k4"
+    assert ll.tile_name(f32, ll.chosen_tile(f32, 256, 256, 256, 256, batch=1)) == "f32_64x64"
     assert ll.chosen_tile(f32, 256, 256, 256, 256, batch=0) == -1
     with pytest.raises(ll.LinearLayerError):
         ll.set_tile(f32, 17)

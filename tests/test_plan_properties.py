@@ -16,7 +16,7 @@ import linear_layer_amd as ll
 F32, F16 = ll.DTYPE_F32, ll.DTYPE_F16
 TILE_SHAPES = {
     F32: [(256, 256), (256, 128), (128, 128), (64, 64), (64, 64), (128, 128)],
-    F16: [(256, 256), (128, 128), (64, 64)],
+    F16: [(256, 256), (128, 128), (64, 64), (128, 128)],
 }
 dims = st.one_of(st.integers(1, 300), st.integers(1, 20000), st.sampled_from([255, 256, 257, 2047, 4096, 11008]))
 
@@ -88,5 +88,6 @@ def test_forced_stream_k_shares_only_leftover_tiles(dt, M, N, K):
     assert ll.chosen_split_k(dt, M, N, K, 256) == 1 or sk == 0
     if sk > 0:
         tiles = tiles_of(dt, t, M, N)
-        slots = 256 * (1 if TILE_SHAPES[dt][t] == (256, 256) or (dt == F32 and t in (4, 5)) else 2)
+        slots = 256 * (1 if TILE_SHAPES[dt][t] == (256, 256) or (dt == F32 and t in (4, 5)) or
+                       (dt == F16 and t == 3) else 2)
         assert sk == tiles % slots if tiles >= slots else sk == tiles
