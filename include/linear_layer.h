@@ -210,11 +210,13 @@ const char *ll_status_string(int status);
  * then applies the ReLU in a pass afterwards). The result is the same sum in
  * a different, run-dependent order; it still allocates nothing.
  *
- * Two FP32 shapes split K inside the workgroup instead ("K-sliced" tiles,
- * named *_k4 and *_k2): the workgroup's slices sum disjoint stage-aligned
- * K ranges and add their partial tiles through on-chip memory in a fixed
- * order, so the result does not depend on the run; no atomics, no extra
- * pass. They serve problems too small to fill the device (e.g. 1024^3).
+ * Some shapes split K inside the workgroup instead ("K-sliced" tiles, named
+ * *_k4 and *_k2: f32_64x64_k4, f32_128x128_k2, f16_128x128_k2): the
+ * workgroup's slices sum disjoint stage-aligned K ranges and add their
+ * partial tiles through on-chip memory in a fixed order, so the result does
+ * not depend on the run; no atomics, no extra pass. They serve problems too
+ * small to fill the device (e.g. 1024^3), and the automatic choice takes them
+ * only when each slice gets at least 8 stages (a forced tile is always used).
  *
  * These calls let a benchmark or a caller pin the choice. They touch only
  * host memory and never the GPU.
@@ -260,8 +262,8 @@ int ll_chosen_split_k(int dtype, int M, int N, int K, int batch, int num_cus);
  * order of those tiles run-dependent (still within the error bound; integer
  * inputs stay exact); it allocates nothing.
  *   ll_set_stream_k: -1 automatic (default), 0 never, 1 whenever the shape
- *   allows it (a forced K-split takes precedence; K-sliced FP32 tiles and
- *   the 128x128 and 64x64 16-bit tiles never share out). Returns LL_OK or
+ *   allows it (a forced K-split takes precedence; K-sliced tiles and the
+ *   128x128 and 64x64 16-bit tiles never share out). Returns LL_OK or
  *   LL_ERR_INVALID_VALUE.
  *   ll_chosen_stream_k: the number of tiles the plan shares out (0: none),
  *   assuming 128-bit-aligned operands; dtype and flags as for
