@@ -332,9 +332,15 @@ gemm_f16_kernel(GemmParams p)
 // SK: a stream-K launch (whole tiles first, then sharing workgroups that add
 // partial sums of (tile, k-range) segments atomically).
 //
+// KS: K-slices. The workgroup holds KS wave grids; slice s runs the pipeline
+// on its own LDS ring over the s-th of KS stage-aligned parts of the tile's
+// K range (all slices run the same number of stages and share every
+// barrier); at the end the other slices park their partial tiles in the A
+// rings and slice 0 adds them in slice order and writes the tile.
+//
 // IN (interior): launched only when every tile lies inside M and N and every
-// workgroup's K range is a whole number of stages; the copies then need no
-// bounds selects.
+// workgroup's (and slice's) K range is a whole number of stages; the copies
+// then need no bounds selects.
 template <int EPI, bool BF16, bool BT, int BM, int BN, int BK, int NBUF, int WGM, int WGN, int WPE,
           bool IN, int MF, bool SK, int KS>
 __global__ void __launch_bounds__(64 * WGM * WGN * KS) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
