@@ -309,6 +309,7 @@ def main():
             "traffic": measured_traffic(w.name, w.kind),
             "kernel_avg_ms": round(avg_launch_ms, 5),
             "kernel_min_ms": round(min(launch_ms), 5),
+            "kernel_median_ms": round(sorted(launch_ms)[len(launch_ms) // 2], 5),
             "flops_per_launch": flops,
         },
         "cpu_baseline": cpu,
