@@ -1,0 +1,57 @@
+"""The bench's command-line contract: one JSON line with the fields a driver
+reads, the roofline and CPU-baseline objects, and a refusal of more than one
+GPU. bench.py runs as a child process, as a driver would start it."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_bench(*args, timeout=300):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
+                          capture_output=True, text=True, timeout=timeout)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = run_bench("--gpus", "2", timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr and not r.stdout.strip()
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not _has_gpu(), reason="needs a GPU")
+@pytest.mark.parametrize("workload", ["gemm_f32_256", "linear_relu_2047x1376x4096"])
+def test_one_json_line_with_every_field(workload):
+    r = run_bench("--workload", workload, "--steps", "3", "--warmup", "1", "--cpu-seconds", "0.5")
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["value"] > 0 and d["ms_per_step"] > 0
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["higher_is_better"] is True and d["vs_baseline"] is None
+    assert d["config"]["workload"] == workload
+    rl = d["roofline"]
+    assert rl["bound"] == "mfma" and rl["unit"] == "TFLOP/s" and rl["peak"] == 157.3
+    assert 0 < rl["frac"] <= 1 and abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-3
+    assert rl["traffic"] is None or rl["traffic"] > 0
+    assert rl["kernel_min_ms"] <= rl["kernel_median_ms"] and rl["kernel_min_ms"] <= rl["kernel_avg_ms"]
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert cb["unit"] == d["unit"]
