@@ -273,8 +273,8 @@ gemm_f16_kernel(GemmParams p)
 
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS FP16 kernel (BM x BN = 256x256 or 128x128 block tile,
-// 128-bit-aligned operands).
+// Direct-to-LDS FP16 kernel (BM x BN = 256x256, 192x192 or 128x128 block
+// tile, 128-bit-aligned operands).
 //
 // Both operands travel global -> LDS with global_load_lds_dwordx4, so no
 // registers hold prefetched tiles and the accumulators (128 per lane for a
@@ -309,8 +309,11 @@ gemm_f16_kernel(GemmParams p)
 //      MF = 16: the groups read the same unit u of rows k..k+3 and k+8..k+11;
 //      XOR by 2*(k%4) + (k/8)%2 sends them to u^{0,2,4,6} and u^{1,3,5,7}.
 //      (With BN = 128 a k-row is one bank line; with 256 the XOR stays in
-//      its half.) One copy = 1024/(2*BN) rows; lane l fills row l/(BN/8),
-//      bytes 16*(l%(BN/8)) .. +15.
+//      its half; with 192 it stays in the first eight units or, within the
+//      last four, uses the low two bits.) The stage is filled as one byte
+//      array, 1 KiB per copy: lane l of copy c fills bytes 1024*c + 16*l,
+//      which is k-row (1024*c + 16*l) / (2*BN). With BN = 192 a copy ends
+//      inside a k-row; each wave's three copies cover eight whole k-rows.
 // NBUF stages form a ring. A stage holds BK/32 k-steps (BK/16 with MF = 32);
 // each step's operands are read while the previous step's MFMAs run. The
 // stage's barrier sits before its last step, whose operands are then in
@@ -327,7 +330,8 @@ gemm_f16_kernel(GemmParams p)
 // The workgroup is a WGM x WGN grid of waves, each owning a (BM/WGM) x
 // (BN/WGN) block, with WPE waves per SIMD: 256x256 runs 2 x 4 waves, two per
 // SIMD, so one wave's MFMAs can run while the other waits to issue its
-// copies; 128x128 runs 2 x 2 waves and two workgroups per CU.
+// copies; 192x192 runs the same 2 x 4 grid (96x48 per wave); 128x128 runs
+// 2 x 2 waves and two workgroups per CU.
 //
 // SK: a stream-K launch (whole tiles first, then sharing workgroups that add
 // partial sums of (tile, k-range) segments atomically).
@@ -347,7 +351,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN * KS) __attribute__((amdgpu_wav
 gemm_f16_direct_kernel(GemmParams p)
 {
     constexpr int NW = WGM * WGN;   // waves of one K-slice
-    static_assert(BM == BN && (BN == 128 || BN == 256), "square tiles of 128 or 256");
+    static_assert(BM == BN && (BN == 128 || BN == 192 || BN == 256), "square tiles of 128, 192 or 256");
     constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / MF, FN = WTN / MF;
     constexpr int KSTEP = MF == 32 ? 16 : 32;             // k per MFMA
     constexpr int STEPS = BK / KSTEP;                     // MFMA k-steps per stage
@@ -355,15 +359,13 @@ gemm_f16_direct_kernel(GemmParams p)
     constexpr int RPC = 64 / CPR;                         // A rows per copy
     constexpr int A_STAGE = BM * BK, B_STAGE = BK * BN;   // halves
     constexpr int COPIES_A = BM / RPC / NW;               // per wave per stage
-    constexpr int LPR = BN / 8;                           // lanes per B k-row (K-by-N)
-    constexpr int RB = 64 / LPR;                          // B k-rows per copy
-    constexpr int COPIES_B = BT ? COPIES_A : BK / RB / NW;
+    constexpr int COPIES_B = BT ? COPIES_A : B_STAGE * 2 / 1024 / NW;
     constexpr int PER_STAGE = COPIES_A + COPIES_B;        // vmcnt entries per stage
     static_assert(STEPS % 2 == 0 && PER_STAGE % FM == 0, "stage layout");
-    static_assert(COPIES_A * RPC * NW == BM && (COPIES_A * RPC) % 16 == 0 &&
-                      (BT || COPIES_B * RB * NW == BK) && WTM % MF == 0 && WTN % MF == 0 &&
-                      (MF == 16 || MF == 32),
-                  "copies cover the stage; each wave's rows start at a multiple of 16");
+    static_assert(COPIES_A * RPC * NW == BM && RPC % 8 == 0 &&
+                      (BT || COPIES_B * 1024 * NW == B_STAGE * 2) && WTM % MF == 0 &&
+                      WTN % MF == 0 && (MF == 16 || MF == 32),
+                  "copies cover the stage; a copy's rows start at a multiple of 8");
     static_assert((NBUF - 1) * PER_STAGE <= 63, "vmcnt range");
     static_assert(KS >= 1 && (KS == 1 || !SK), "K-slices take no stream-K share");
     static_assert((KS - 1) * NW * FM * FN * AccBlock<MF>::R * 64 * 4 <= KS * NBUF * A_STAGE * 2,
@@ -409,11 +411,23 @@ gemm_f16_direct_kernel(GemmParams p)
     auto swz = [](int row) { return (row / (16 / CPR)) & (CPR - 1); };
     // B (K-by-N) unit swizzle of k-row k (see the layout notes above).
     auto bsw = [](int k) { return MF == 32 ? 2 * (k & 3) : 2 * (k & 3) + ((k >> 3) & 1); };
+    // Unit u of k-row k is stored in slot bunit(u, k): the XOR acts within
+    // groups of eight units (a 256-byte bank line), and within the last group
+    // of four when BN = 192.
+    auto bunit = [&](int u, int k) {
+        if constexpr (BN % 128 == 0) {
+            return u ^ bsw(k);
+        } else {
+            constexpr int NU = BN / 16;
+            const int g = u & ~7, span = NU - g < 8 ? NU - g : 8;
+            return g + ((u & 7) ^ (bsw(k) & (span - 1)));
+        }
+    };
 
     // Copy sources. Row-panel copy j of this wave (A, or B given N-by-K)
-    // covers rows (wave*COPIES_A + j)*RPC + lane/CPR. Each wave's first row is
-    // a multiple of 16, so the swizzled chunk a lane fetches depends only on
-    // (j*RPC) % 16: one variant when RPC = 16, two (j even, j odd) when RPC = 8.
+    // covers rows (wave*COPIES_A + j)*RPC + lane/CPR. A copy's first row is a
+    // multiple of 8, so the swizzled chunk a lane fetches depends only on
+    // whether that row is a multiple of 16: two variants.
     const int r_lane = wave * COPIES_A * RPC + lane / CPR;   // row of copy 0
     const int slot = lane % CPR;
     int ch[2];
@@ -424,16 +438,18 @@ gemm_f16_direct_kernel(GemmParams p)
         a_src[v] = A + (int64_t)(m0 + r_lane) * p.lda + ch[v] * 8;
         bt_src[v] = B + (int64_t)(n0 + r_lane) * p.ldb + ch[v] * 8;
     }
-    // B copy j (given K-by-N): k-row (wave*COPIES_B + j)*RB + lane/LPR; the
-    // lane's 16 bytes fill unit slot (lane%LPR)/2, half lane%2, and hold
-    // logical unit slot ^ bsw(k).
+    // B copy j (given K-by-N) fills stage bytes (wave*COPIES_B + j)*1024 +
+    // 16*lane: k-row b_row(j), unit slot s = (offset within the row)/32, half
+    // (offset/16)%2, holding logical unit bunit(s, k) (an involution).
+    auto b_off = [&](int j) { return (wave * COPIES_B + j) * 1024 + 16 * lane; };
+    auto b_row = [&](int j) { return b_off(j) / (2 * BN); };
     constexpr int NB_SRC = BT ? 1 : COPIES_B;
     const uint16_t *b_src[NB_SRC];
     bool b_col_ok[NB_SRC];
 #pragma unroll
     for (int j = 0; j < NB_SRC; ++j) {
-        const int kr = (wave * COPIES_B + j) * RB + lane / LPR;
-        const int col = n0 + ((((lane % LPR) >> 1) ^ bsw(kr)) * 16) + (lane & 1) * 8;
+        const int kr = b_row(j), u2 = (b_off(j) % (2 * BN)) / 16;
+        const int col = n0 + bunit(u2 >> 1, kr) * 16 + (u2 & 1) * 8;
         b_src[j] = B + (int64_t)kr * p.ldb + col;
         b_col_ok[j] = col < N;
     }
@@ -449,7 +465,8 @@ gemm_f16_direct_kernel(GemmParams p)
         if (c < COPIES_A || BT) {
             const bool is_a = c < COPIES_A;
             const int j = is_a ? c : c - COPIES_A;
-            const int v = ((j * RPC) & 15) != 0;
+            // (each wave's first row is a multiple of 16 unless BM = 192)
+            const int v = (((COPIES_A * RPC) % 16 == 0 ? j : wave * COPIES_A + j) * RPC & 15) != 0;
             dst = (is_a ? as_base + buf * (A_STAGE * 2) : bs_base + buf * (B_STAGE * 2)) +
                   (wave * COPIES_A + j) * 1024;
             const int64_t step = (int64_t)(j * RPC) * (is_a ? p.lda : p.ldb) + k0;
@@ -467,7 +484,7 @@ gemm_f16_direct_kernel(GemmParams p)
             if constexpr (IN)
                 src = in;
             else
-                src = k0 + (wave * COPIES_B + j) * RB + lane / LPR < K && b_col_ok[j]
+                src = k0 + b_row(j) < K && b_col_ok[j]
                           ? in
                           : zero_chunk<uint16_t>();
         }
@@ -518,7 +535,7 @@ gemm_f16_direct_kernel(GemmParams p)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int k = KSTEP * s + 8 * grp + 4 * e + (j16 >> 2);
-                const int addr = k * BN + (((n >> 4) ^ bsw(k)) << 4) + (n & 15);
+                const int addr = k * BN + (bunit(n >> 4, k) << 4) + (n & 15);
                 v[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) s16x4 *)(lds_addr(&bs[addr])));
             }
@@ -731,15 +748,21 @@ const TileInfo kF16Tiles[kF16NumTiles] = {
     // the plain tile): eight waves, one workgroup per CU; only with at least
     // 8 stages of 64 per slice (below, 0.5-1 us slower than plain 128x128)
     {F16_S::BM, F16_S::BN, 1, 0.60f, 0.60f, "f16_128x128_k2", 2, false, 512, 2 * 8 * 64},
+    // 192x192 (direct kernel; unaligned operands run the staged 128x128):
+    // eight waves, one workgroup per CU; 0.74 on 3072^3, 0.79 on 8192^3,
+    // 0.85 on 4096^3. It wins where 256x256 leaves CUs idle and 192x192 does
+    // not (3072^2: 256 tiles against 144).
+    {192, 192, 1, 0.75f, 0.75f, "f16_192x192_direct", 1, false,
+     64 * DirectCfg<192>::WGM * DirectCfg<192>::WGN},
 };
 
 // The direct kernel on BM x BM tiles (KS K-slices) for 128-bit-aligned
-// operands; the register-staged kernel of the same tile (T, without slices)
-// otherwise.
+// operands; otherwise the register-staged kernel of tile T, without slices
+// (the same tile, except 128x128 for 192x192).
 template <bool BF16, bool BT, int BM, class T, int WPE_T, int KS = 1>
 static hipError_t launch_direct(const GemmParams &p0, int epi, bool vec, hipStream_t s)
 {
-    static_assert(T::BM == BM && T::BN == BM, "fallback tile");
+    static_assert(T::BM == T::BN && (T::BM == BM || (BM == 192 && T::BM == 128)), "fallback tile");
     if (!vec)
         return launch_t<T, WPE_T, BF16, BT>(p0, epi, vec, s);
     GemmParams p = p0;
@@ -801,6 +824,7 @@ static hipError_t launch_16(const GemmParams &p, int tile, int epi, bool vec, hi
     case 0: return launch_direct<BF16, BT, 256, F16_L, 1>(p, epi, vec, s);
     case 1: return launch_direct<BF16, BT, 128, F16_S, 2>(p, epi, vec, s);
     case 3: return launch_direct<BF16, BT, 128, F16_S, 2, 2>(p, epi, vec, s);
+    case 4: return launch_direct<BF16, BT, 192, F16_S, 2>(p, epi, vec, s);
     default: return launch_t<F16_XS, 2, BF16, BT>(p, epi, vec, s);
     }
 }

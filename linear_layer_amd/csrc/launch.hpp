@@ -20,7 +20,7 @@ struct TileInfo {
 };
 
 constexpr int kF32NumTiles = 6;
-constexpr int kF16NumTiles = 4;
+constexpr int kF16NumTiles = 5;
 extern const TileInfo kF32Tiles[kF32NumTiles];
 extern const TileInfo kF16Tiles[kF16NumTiles];
 

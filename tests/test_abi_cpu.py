@@ -211,16 +211,20 @@ def test_tile_choice():
         ll.set_stream_k(2)
     assert choice(f16, 8192, 8192, 8192) == ("f16_256x256_direct", 1)
     # 16-bit: 6144^2 is 576 tiles of 256x256, 2.25 rounds: two run whole, 64
-    # tiles are shared out; 3072^3 (144 tiles, one short round) and 5120^3
-    # (400 tiles) run whole; a K-split is not worth its passes at the 16-bit
-    # rate; 2048^3 and the thin 512x4096x4096 take 128x128 in two K-slices
-    # (one lone workgroup per CU otherwise), 1024x8192x8192 plain 128x128
-    # (two per CU), tiny products plain 128x128 (too few stages per slice)
+    # tiles are shared out; 3072^2 is 256 tiles of 192x192, one full round
+    # (144 of 256x256 would leave 112 CUs idle), at any K; 5120^3 (400 tiles)
+    # runs whole on 256x256 (729 tiles of 192x192 are three rounds); a K-split
+    # is not worth its passes at the 16-bit rate; 2048^3 and the thin
+    # 512x4096x4096 take 128x128 in two K-slices (one lone workgroup per CU
+    # otherwise), 1024x8192x8192 plain 128x128 (two per CU), tiny products
+    # plain 128x128 (too few stages per slice)
     assert choice(f16, 6144, 6144, 6144) == ("f16_256x256_direct", 1)
     assert ll.chosen_stream_k(f16, 6144, 6144, 6144, 256) == 64
-    assert choice(f16, 3072, 3072, 3072) == ("f16_256x256_direct", 1)
+    for K in (1024, 3072, 8192):
+        assert choice(f16, 3072, 3072, K) == ("f16_192x192_direct", 1)
+        assert ll.chosen_stream_k(f16, 3072, 3072, K, 256) == 0
     assert choice(f16, 5120, 5120, 5120) == ("f16_256x256_direct", 1)
-    assert ll.chosen_stream_k(f16, 3072, 3072, 3072, 256) == 0
+    assert choice(f16, 4096, 4096, 4096) == ("f16_256x256_direct", 1)
     assert ll.chosen_stream_k(f16, 5120, 5120, 5120, 256) == 0
     assert choice(f16, 2048, 2048, 2048) == ("f16_128x128_k2", 1)
     assert choice(f16, 512, 4096, 4096) == ("f16_128x128_k2", 1)

@@ -16,7 +16,7 @@ import linear_layer_amd as ll
 F32, F16 = ll.DTYPE_F32, ll.DTYPE_F16
 TILE_SHAPES = {
     F32: [(256, 256), (256, 128), (128, 128), (64, 64), (64, 64), (128, 128)],
-    F16: [(256, 256), (128, 128), (64, 64), (128, 128)],
+    F16: [(256, 256), (128, 128), (64, 64), (128, 128), (192, 192)],
 }
 dims = st.one_of(st.integers(1, 300), st.integers(1, 20000), st.sampled_from([255, 256, 257, 2047, 4096, 11008]))
 
