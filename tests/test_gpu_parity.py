@@ -414,6 +414,27 @@ def test_16bit_interior_and_edge_tiles_exact(N):
         assert_exact(run_nt(fn_nt, A8.to(dt), B8.t().contiguous().to(dt)), R, f"16-bit nt bf16={bf} N={N}")
 
 
+@pytest.mark.parametrize("M,N", [(384, 384), (385, 392), (3072, 3072)])
+def test_16bit_192_tile_exact(M, N, tile):
+    """The 192x192 tile: whole tiles (the interior path, no bounds selects;
+    3072^2 is one tile per CU), or a ragged last row and column; both B
+    layouts, fp16 and bf16; integer inputs, exact."""
+    tile(F16, ll.num_tiles(F16) - 1)
+    assert ll.tile_name(F16, ll.num_tiles(F16) - 1) == "f16_192x192_direct"
+    K = 256
+    A8, B8 = wl.integers((M, K), 176, -8, 8), wl.integers((K, N), 177, -8, 8)
+    R, _ = oracle.gemm(np32(A8), np32(B8))
+    for bf in (False, True):
+        dt = torch.bfloat16 if bf else torch.float16
+        fn, fn_nt = (ll.gemm_bf16f32, ll.gemm_bf16f32_nt) if bf else (ll.gemm_f16f32, ll.gemm_f16f32_nt)
+        Cd = torch.full((M, N), float("nan"), device=DEV)
+        fn(A8.to(dt).to(DEV), B8.to(dt).to(DEV), Cd)
+        torch.cuda.synchronize()
+        assert_exact(np32(Cd), R, f"192 tile bf16={bf} {M}x{N}")
+        assert_exact(run_nt(fn_nt, A8.to(dt), B8.t().contiguous().to(dt)), R,
+                     f"192 tile nt bf16={bf} {M}x{N}")
+
+
 @pytest.mark.parametrize("t", [4, 5])
 @pytest.mark.parametrize("K", [1, 40, 96, 97, 1000])
 @pytest.mark.parametrize("S", [1, 3])
