@@ -75,6 +75,9 @@ WORKLOADS = {
     "gemm_f32_512x4096x4096": Workload(10, "gemm_f32_512x4096x4096", "gemm_f32", 512, 4096, 4096),
     "linear_relu_2047x1376x4096": Workload(11, "linear_relu_2047x1376x4096", "linear", 2047, 1376, 4096,
                                            act=1, scale=1.0 / 64.0),
+    # a 16-bit product whose 256x256 tiles (144) would leave CUs idle; it runs
+    # on 192x192 tiles, one per CU
+    "gemm_f16f32_3072": Workload(12, "gemm_f16f32_3072", "gemm_f16f32", 3072, 3072, 3072),
 }
 
 HALF_KINDS = ("gemm_f16f32", "gemm_bf16f32", "gemm_f16f32_nt")

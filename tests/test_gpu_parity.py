@@ -1128,7 +1128,7 @@ def test_full_linear(name):
     relu_matches(got, got0)
 
 
-@pytest.mark.parametrize("name", ["gemm_f16f32_8192", "gemm_bf16f32_8192"])
+@pytest.mark.parametrize("name", ["gemm_f16f32_8192", "gemm_bf16f32_8192", "gemm_f16f32_3072"])
 def test_full_gemm_16bit(name):
     w = wl.WORKLOADS[name]
     x = wl.make_inputs(w)
