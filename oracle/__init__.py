@@ -36,7 +36,7 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
            "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
            _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)

@@ -37,9 +37,11 @@
  * Besides the value r, every routine returns t = sum over k of |A(m,k)*B(k,n)|,
  * which is the basis of the parity tolerance |C_gpu - r| <= 1e-4 * t.
  *
- * Blocking: the full-matrix routines split the output over row blocks and
- * column blocks for cache reuse and threads, but each element's k order is
- * that of the plain triple loop, so the result is bitwise that loop's.
+ * Blocking: the full-matrix routines first decode A and B to double (exact for
+ * every input format; B into K-by-N order), then split the output over row
+ * blocks and column blocks for cache reuse and threads and walk k in chunks
+ * within a block, but each element still receives its products in increasing
+ * k, so the result is bitwise that of the plain triple loop.
  */
 #include <math.h>
 #include <stddef.h>
@@ -147,6 +149,36 @@ static inline int needs_sum(const epilogue_t *e)
 
 #define NB 64 /* output columns per block */
 #define MB 16 /* output rows per block */
+#define KB 256 /* k values per chunk of a block */
+
+/* A (M-by-K) decoded to double, row-major with leading dimension K. Every
+ * input format converts to double exactly, so the decoded operands are the
+ * values of the definition themselves. */
+static double *decode_a(int64_t M, int64_t K, const void *A, int64_t lda, loader_fn la)
+{
+    double *Ad = malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(double));
+    if (!Ad)
+        abort();
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            Ad[m * K + k] = la(A, m * lda + k);
+    return Ad;
+}
+
+/* B decoded to double in K-by-N order (leading dimension N), whether it is
+ * stored K-by-N or, with b_trans, N-by-K. */
+static double *decode_b(int64_t K, int64_t N, const void *B, int64_t ldb, loader_fn lb, int b_trans)
+{
+    double *Bd = malloc((size_t)(K * N > 0 ? K * N : 1) * sizeof(double));
+    if (!Bd)
+        abort();
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t col = 0; col < N; ++col)
+            Bd[k * N + col] = lb(B, b_trans ? col * ldb + k : k * ldb + col);
+    return Bd;
+}
 
 /* Full M-by-N result into R (row-major, ld N) and T (same layout). */
 static void full_product(int64_t M, int64_t N, int64_t K,
@@ -157,36 +189,46 @@ static void full_product(int64_t M, int64_t N, int64_t K,
     if (M <= 0 || N <= 0)
         return;
     set_threads(nthreads);
+    const int sum = needs_sum(e) && K > 0;
+    double *Ad = sum ? decode_a(M, K, A, lda, la) : NULL;
+    double *Bd = sum ? decode_b(K, N, B, ldb, lb, b_trans) : NULL;
     const int64_t nmb = (M + MB - 1) / MB, nnb = (N + NB - 1) / NB;
-    const int sum = needs_sum(e);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t task = 0; task < nmb * nnb; ++task) {
         const int64_t n0 = (task % nnb) * NB, m0 = (task / nnb) * MB;
         const int64_t nb = (N - n0 < NB) ? N - n0 : NB;
         const int64_t mb = (M - m0 < MB) ? M - m0 : MB;
-        for (int64_t m = m0; m < m0 + mb; ++m) {
-            double s[NB], t[NB];
+        double s[MB][NB], t[MB][NB];
+        for (int64_t i = 0; i < mb; ++i)
             for (int64_t j = 0; j < nb; ++j) {
-                s[j] = 0.0;
-                t[j] = 0.0;
+                s[i][j] = 0.0;
+                t[i][j] = 0.0;
             }
-            if (sum) {
-                for (int64_t k = 0; k < K; ++k) {
-                    const double a = la(A, m * lda + k);
+        /* k in chunks of KB, each chunk over every row of the block: every
+         * element still receives its products in increasing k */
+        for (int64_t k0 = 0; sum && k0 < K; k0 += KB) {
+            const int64_t k1 = (K - k0 < KB) ? K : k0 + KB;
+            for (int64_t i = 0; i < mb; ++i) {
+                const int64_t m = m0 + i;
+                for (int64_t k = k0; k < k1; ++k) {
+                    const double a = Ad[m * K + k];
+                    const double *brow = Bd + k * N + n0;
                     for (int64_t j = 0; j < nb; ++j) {
-                        const int64_t bi = b_trans ? (n0 + j) * ldb + k : k * ldb + n0 + j;
-                        const double p = a * lb(B, bi);
-                        s[j] += p;
-                        t[j] += fabs(p);
+                        const double p = a * brow[j];
+                        s[i][j] += p;
+                        t[i][j] += fabs(p);
                     }
                 }
             }
-            for (int64_t j = 0; j < nb; ++j) {
-                R[m * N + n0 + j] = finish(e, m, n0 + j, s[j]);
-                T[m * N + n0 + j] = t[j];
-            }
         }
+        for (int64_t i = 0; i < mb; ++i)
+            for (int64_t j = 0; j < nb; ++j) {
+                R[(m0 + i) * N + n0 + j] = finish(e, m0 + i, n0 + j, s[i][j]);
+                T[(m0 + i) * N + n0 + j] = t[i][j];
+            }
     }
+    free(Ad);
+    free(Bd);
 }
 
 /* Selected elements (rows[p], cols[p]): each is one plain dot product over k. */

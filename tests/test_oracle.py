@@ -279,9 +279,12 @@ def test_ragged_rows_are_a_prefix():
     assert np.array_equal(L127, L128[:127])
 
 
+@pytest.mark.parametrize("K", [77, 600])
 @pytest.mark.parametrize("kind", ["f32", "f16", "bf16", "linear"])
-def test_blocked_equals_per_element_loop(kind):
-    M, N, K = 40, 150, 77  # several row and column blocks, ragged both ways
+def test_blocked_equals_per_element_loop(kind, K):
+    # several row and column blocks, ragged both ways; K = 600 spans three k
+    # chunks of the blocked loop, the last one partial
+    M, N = 40, 150
     rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
     rows, cols = rows.ravel(), cols.ravel()
     if kind == "linear":

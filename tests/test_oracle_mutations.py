@@ -19,17 +19,23 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # (name, file under oracle/, text in it, replacement)
 MUTANTS = [
     ("last k dropped in the blocked loop", "oracle.c",
-     "for (int64_t k = 0; k < K; ++k) {\n                    const double a",
-     "for (int64_t k = 0; k < K - (K > 3); ++k) {\n                    const double a"),
+     "const int64_t k1 = (K - k0 < KB) ? K : k0 + KB;",
+     "const int64_t k1 = (K - k0 < KB) ? K - (K > 3) : k0 + KB;"),
+    ("a k chunk summed twice in the blocked loop", "oracle.c",
+     "k0 < K; k0 += KB)", "k0 < K; k0 += KB / 2)"),
     ("last k dropped in the per-element loop", "oracle.c",
      "for (int64_t k = 0; k < K; ++k) {\n                const double prod",
      "for (int64_t k = 0; k < K - (K > 3); ++k) {\n                const double prod"),
     ("A read at a shifted k", "oracle.c",
      "la(A, m * lda + k);", "la(A, m * lda + (k + 1) % K);"),
-    ("B read from the neighbouring column", "oracle.c",
-     ": k * ldb + n0 + j;", ": k * ldb + n0 + (j + 1) % nb;"),
-    ("transposed B read with k reversed", "oracle.c",
-     "b_trans ? (n0 + j) * ldb + k :", "b_trans ? (n0 + j) * ldb + (K - 1 - k) :"),
+    ("B decoded from the neighbouring column", "oracle.c",
+     ": k * ldb + col);", ": k * ldb + (col + 1) % N);"),
+    ("B read from the neighbouring column in the blocked loop", "oracle.c",
+     "const double p = a * brow[j];", "const double p = a * brow[(j + 1) % nb];"),
+    ("A row taken from the neighbouring row in the blocked loop", "oracle.c",
+     "const double a = Ad[m * K + k];", "const double a = Ad[((m + 1) % M) * K + k];"),
+    ("transposed B decoded with k reversed", "oracle.c",
+     "b_trans ? col * ldb + k :", "b_trans ? col * ldb + (K - 1 - k) :"),
     ("per-element loop reads B transposed the wrong way", "oracle.c",
      "b_trans ? n * ldb + k : k * ldb + n", "b_trans ? k * ldb + n : n * ldb + k"),
     ("sample column taken from the wrong position", "oracle.c",
@@ -54,7 +60,7 @@ MUTANTS = [
     ("ReLU gives negative zero", "oracle.c",
      "y = (y > 0.0) ? y : 0.0;", "y = (y > 0.0) ? y : -0.0;"),
     ("magnitude sum without the absolute value", "oracle.c",
-     "t[j] += fabs(p);", "t[j] += p;"),
+     "t[i][j] += fabs(p);", "t[i][j] += p;"),
     ("per-element magnitude sum without the absolute value", "oracle.c",
      "t += fabs(prod);", "t += prod;"),
     ("binary16 exponent bias off by one", "oracle.c",
