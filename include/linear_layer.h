@@ -218,8 +218,9 @@ const char *ll_status_string(int status);
  * small to fill the device (e.g. 1024^3), and the automatic choice takes them
  * only when each slice gets at least 8 stages (a forced tile is always used).
  *
- * These calls let a benchmark or a caller pin the choice. They touch only
- * host memory and never the GPU.
+ * The calls below report the choice; they touch only host memory and never
+ * the GPU. (linear_layer_tuning.h declares process-wide overrides of the
+ * choice for benchmarks and tests.)
  */
 #define LL_DTYPE_F32 0 /* gemm_f32, linear_bias_act and their _nt forms */
 #define LL_DTYPE_F16 1 /* gemm_f16f32, gemm_bf16f32 and their _nt forms */
@@ -227,22 +228,20 @@ const char *ll_status_string(int status);
  * LL_PLAN_RELU: linear_bias_act with the ReLU, whose K-split and stream-K
  * plans pay for one more pass over Y (LL_DTYPE_F32 only);
  * LL_PLAN_B_NK: the _nt form (B given N-by-K; accepted for callers that
- * describe the call fully, the plans do not currently depend on it). */
+ * describe the call fully, the plans do not currently depend on it);
+ * LL_PLAN_UNALIGNED: operands that do not allow the 128-bit-load kernels
+ * (a base not 16-byte aligned, or a leading dimension, K or N not a multiple
+ * of 4 (fp32) or 8 (16-bit)): no stream-K, and the tiles that exist only as
+ * 128-bit-load kernels (the K-sliced ones and f16_192x192_direct) are not
+ * chosen automatically. */
 #define LL_PLAN_RELU 0x100
 #define LL_PLAN_B_NK 0x200
+#define LL_PLAN_UNALIGNED 0x400
 
 /* Number of tile shapes for a data type (0 for an unknown dtype). */
 int ll_num_tiles(int dtype);
 /* Name of a tile shape, e.g. "f32_256x256" ("" if out of range). Static string. */
 const char *ll_tile_name(int dtype, int tile);
-/* Force tile `tile` for every later call of that dtype in this process;
- * -1 restores the automatic choice. Process-wide, thread-safe.
- * Returns LL_OK or LL_ERR_INVALID_VALUE. */
-int ll_set_tile(int dtype, int tile);
-/* Force `splits` K-splits (1 .. 16; the split length is rounded up to a
- * multiple of 64, so small K may use fewer) for every later call of any dtype;
- * -1 restores the automatic choice. Returns LL_OK or LL_ERR_INVALID_VALUE. */
-int ll_set_split_k(int splits);
 /* The tile / the number of K-splits the library would use for `batch`
  * M-by-N outputs (batch 1: a single product) with inner dimension K on a
  * device with num_cus compute units (num_cus <= 0: 256), honouring the
@@ -261,15 +260,10 @@ int ll_chosen_split_k(int dtype, int M, int N, int K, int batch, int num_cus);
  * the ReLU applied afterwards). Like a K-split, this makes the summation
  * order of those tiles run-dependent (still within the error bound; integer
  * inputs stay exact); it allocates nothing.
- *   ll_set_stream_k: -1 automatic (default), 0 never, 1 whenever the shape
- *   allows it (a forced K-split takes precedence; K-sliced tiles and the
- *   128x128 and 64x64 16-bit tiles never share out). Returns LL_OK or
- *   LL_ERR_INVALID_VALUE.
- *   ll_chosen_stream_k: the number of tiles the plan shares out (0: none),
- *   assuming 128-bit-aligned operands; dtype and flags as for
- *   ll_chosen_tile; -1 for an unknown dtype or flag, or batch < 1.
+ *   ll_chosen_stream_k: the number of tiles the plan shares out (0: none);
+ *   dtype and flags as for ll_chosen_tile; -1 for an unknown dtype or flag,
+ *   or batch < 1.
  */
-int ll_set_stream_k(int mode);
 int ll_chosen_stream_k(int dtype, int M, int N, int K, int batch, int num_cus);
 
 #ifdef __cplusplus

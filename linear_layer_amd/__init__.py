@@ -34,14 +34,14 @@ __all__ = [
     "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
     "library_path", "load", "set_tile", "num_tiles", "tile_name", "chosen_tile",
     "set_split_k", "chosen_split_k", "set_stream_k", "chosen_stream_k",
-    "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16", "PLAN_RELU", "PLAN_B_NK",
+    "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16", "PLAN_RELU", "PLAN_B_NK", "PLAN_UNALIGNED",
     "OK", "ERR_INVALID_VALUE", "ERR_NO_DEVICE", "ERR_UNSUPPORTED_ARCH", "ERR_LAUNCH",
 ]
 
 OK, ERR_INVALID_VALUE, ERR_NO_DEVICE, ERR_UNSUPPORTED_ARCH, ERR_LAUNCH = 0, 1, 2, 3, 4
 ACT_NONE, ACT_RELU = 0, 1
 DTYPE_F32, DTYPE_F16 = 0, 1
-PLAN_RELU, PLAN_B_NK = 0x100, 0x200   # flags OR-ed into dtype for the chosen_* queries
+PLAN_RELU, PLAN_B_NK, PLAN_UNALIGNED = 0x100, 0x200, 0x400   # flags OR-ed into dtype for chosen_*
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liblinear_layer.so")
@@ -121,6 +121,11 @@ def _check(status: int, where: str):
 
 
 def set_tile(dtype: int, tile: int) -> None:
+    """Force a tile shape for later calls of that dtype; -1 = automatic.
+
+    Like set_split_k and set_stream_k, a process-wide override for benchmarks
+    and tests (include/linear_layer_tuning.h): it steers every later call from
+    every thread and on every stream until reset."""
     _check(load().ll_set_tile(int(dtype), int(tile)), "ll_set_tile")
 
 
@@ -137,7 +142,8 @@ def chosen_tile(dtype: int, M: int, N: int, K: int, num_cus: int = 0, batch: int
 
 
 def set_split_k(splits: int) -> None:
-    """Force the number of K-splits (1..16) for later calls; -1 = automatic."""
+    """Force the number of K-splits (1..16) for later calls; -1 = automatic.
+    Process-wide, like set_tile."""
     _check(load().ll_set_split_k(int(splits)), "ll_set_split_k")
 
 
@@ -146,7 +152,8 @@ def chosen_split_k(dtype: int, M: int, N: int, K: int, num_cus: int = 0, batch: 
 
 
 def set_stream_k(mode: int) -> None:
-    """Stream-K for leftover tiles: -1 automatic, 0 never, 1 whenever possible."""
+    """Stream-K for leftover tiles: -1 automatic, 0 never, 1 whenever possible.
+    Process-wide, like set_tile."""
     _check(load().ll_set_stream_k(int(mode)), "ll_set_stream_k")
 
 

@@ -1,7 +1,7 @@
 // The C ABI: argument checks, quick returns, tile choice and one launch on the
 // caller's stream. Nothing here allocates, synchronises or keeps per-call
 // state; the only global data are a per-device property cache and the
-// optional tile overrides.
+// plan overrides of linear_layer_tuning.h.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include "linear_layer.h"
+#include "linear_layer_tuning.h"
 #include "launch.hpp"
 
 using namespace ll;
@@ -138,8 +139,33 @@ int current_device(DevInfo *out)
 
 // ---- tile and K-split choice ----
 
-std::atomic<int> g_tile_override[2] = {{-1}, {-1}};  // [0] fp32, [1] fp16
-std::atomic<int> g_split_override{-1};
+// Plan overrides for sweeps and tests (declared in linear_layer_tuning.h).
+// They are process-wide: every later call on any thread or stream plans with
+// them. The four values live in one atomic word, so a call reads one
+// consistent set even while another thread changes them.
+struct Overrides {
+    int tile[2];   // forced tile, [0] fp32, [1] 16-bit (both formats); -1 automatic
+    int splits;    // forced K-split count; -1 automatic
+    int sk;        // stream-K: -1 automatic, 0 never, 1 whenever possible
+};
+// 8 bits per value, each stored as value + 1 (so -1 .. 254)
+std::atomic<uint32_t> g_overrides{0u};
+
+Overrides load_overrides()
+{
+    const uint32_t w = g_overrides.load(std::memory_order_relaxed);
+    return Overrides{{(int)(w & 0xff) - 1, (int)((w >> 8) & 0xff) - 1}, (int)((w >> 16) & 0xff) - 1,
+                     (int)((w >> 24) & 0xff) - 1};
+}
+
+// Set field `shift` (0 fp32 tile, 8 16-bit tile, 16 splits, 24 stream-K) to v.
+void store_override(int shift, int v)
+{
+    uint32_t w = g_overrides.load(std::memory_order_relaxed), nw;
+    do {
+        nw = (w & ~(0xffu << shift)) | ((uint32_t)(v + 1) << shift);
+    } while (!g_overrides.compare_exchange_weak(w, nw, std::memory_order_relaxed));
+}
 
 constexpr int kSplitAlign = 64;     // K per split is a multiple of every kernel's stage depth
 constexpr int kMaxSplits = 16;
@@ -184,8 +210,6 @@ struct Plan {
     int sk_grid;    // workgroups of the stream-K share; 0 when the plan has none
 };
 
-std::atomic<int> g_sk_override{-1};   // -1 automatic, 0 never, 1 whenever possible
-
 // Whether a plan may share tiles out with stream-K on tile shape `ti`: it
 // needs a direct kernel (128-bit-aligned operands) and no K-slices.
 bool sk_tile_ok(const TileInfo &ti)
@@ -199,15 +223,17 @@ bool sk_tile_ok(const TileInfo &ti)
 // CUs idle (wave quantisation). This is the size-dependent choice of page
 // "GEMM 优化详解", section "矩阵大小选择策略", re-derived for 256 CUs.
 // A split costs a pre-pass over C (beta*C, or the bias), the atomic traffic of
-// every split's partial tile and, for ReLU, a pass afterwards.
+// every split's partial tile and, for ReLU, a pass afterwards. `vec`: the
+// operands allow the 128-bit-load kernels; without it the tiles that exist
+// only as direct kernels (whose calls would run a staged kernel of another
+// shape) and stream-K are not considered, unless a tile is forced.
 Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int cus, bool relu,
-          int batch = 1, bool allow_sk = false)
+          int batch, bool vec)
 {
     const int items = batch < kMaxGridZ ? batch : kMaxGridZ;   // items per launch
-    const int t_ov = g_tile_override[dtype].load(std::memory_order_relaxed);
-    const int s_ov = g_split_override.load(std::memory_order_relaxed);
-    const int sk_ov = g_sk_override.load(std::memory_order_relaxed);
-    allow_sk = allow_sk && batch == 1 && s_ov < 1 && sk_ov != 0 && K > 0;
+    const Overrides ov = load_overrides();
+    const int t_ov = ov.tile[dtype], s_ov = ov.splits, sk_ov = ov.sk;
+    const bool allow_sk = vec && batch == 1 && s_ov < 1 && sk_ov != 0 && K > 0;
     Plan best{0, 1, K, 0, 0}, best_sk{0, 1, K, 0, 0};
     double best_cost = 0.0, best_sk_cost = 0.0;
     bool have = false, have_sk = false;
@@ -220,6 +246,8 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
             continue;   // more workgroups than one launch can hold
         if (K < ti.min_k && t_ov != t)
             continue;   // K too short for the tile's K-slices (unless forced)
+        if (!vec && ti.direct_only && t_ov != t)
+            continue;   // unaligned operands would run another tile's staged kernel
         for (int s = 1; s <= kMaxSplits; ++s) {
             if (s_ov >= 1 && s != s_ov)
                 continue;
@@ -550,8 +578,7 @@ static int linear_impl(int M, int N, int K, const float *X, int ldx, const float
     p.bias = bias;
     p.act = act;
     const launch_fn launch = wt ? launch_gemm_f32_bt : launch_gemm_f32;
-    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU, 1,
-                         vec);
+    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU, 1, vec);
     if (pl.tile < 0)
         return LL_ERR_INVALID_VALUE;
     if (pl.sk_grid > 0)
@@ -601,7 +628,7 @@ int ll_set_tile(int dtype, int tile)
     const int n = dtype == LL_DTYPE_F32 ? kF32NumTiles : kF16NumTiles;
     if (tile < -1 || tile >= n)
         return LL_ERR_INVALID_VALUE;
-    g_tile_override[dtype].store(tile, std::memory_order_relaxed);
+    store_override(dtype == LL_DTYPE_F32 ? 0 : 8, tile);
     return LL_OK;
 }
 
@@ -627,14 +654,15 @@ static Plan chosen_plan(int dtype, int M, int N, int K, int batch, int num_cus, 
 {
     const int base = dtype & 0xff, flags = dtype & ~0xff;
     const bool relu = flags & LL_PLAN_RELU;   // LL_PLAN_B_NK: accepted, plans alike
+    const bool vec = !(flags & LL_PLAN_UNALIGNED);
     *ok = (base == LL_DTYPE_F32 || (base == LL_DTYPE_F16 && !relu)) &&
-          (flags & ~(LL_PLAN_RELU | LL_PLAN_B_NK)) == 0 && batch >= 1;
+          (flags & ~(LL_PLAN_RELU | LL_PLAN_B_NK | LL_PLAN_UNALIGNED)) == 0 && batch >= 1;
     if (!*ok)
         return Plan{-1, -1, 0};
     const int cus = num_cus > 0 ? num_cus : 256;
     const Plan pl = base == LL_DTYPE_F32
-                        ? plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, relu, batch, true)
-                        : plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch, true);
+                        ? plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, relu, batch, vec)
+                        : plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch, vec);
     if (pl.tile < 0)
         *ok = false;
     return pl;
@@ -670,7 +698,7 @@ int ll_set_stream_k(int mode)
 {
     if (mode < -1 || mode > 1)
         return LL_ERR_INVALID_VALUE;
-    g_sk_override.store(mode, std::memory_order_relaxed);
+    store_override(24, mode);
     return LL_OK;
 }
 
@@ -678,7 +706,7 @@ int ll_set_split_k(int splits)
 {
     if (splits != -1 && (splits < 1 || splits > kMaxSplits))
         return LL_ERR_INVALID_VALUE;
-    g_split_override.store(splits, std::memory_order_relaxed);
+    store_override(16, splits);
     return LL_OK;
 }
 

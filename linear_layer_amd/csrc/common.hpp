@@ -70,7 +70,7 @@ __device__ __forceinline__ void select_batch(GemmParams &p)
 // Launch grid of a product: x = output tiles, y = K-splits, z = batch items.
 inline dim3 gemm_grid(const GemmParams &p, int64_t ntiles)
 {
-    return dim3((unsigned)ntiles, (unsigned)((p.K + p.k_split - 1) / p.k_split), (unsigned)p.batch);
+    return dim3((unsigned)ntiles, (unsigned)cdiv(p.K, p.k_split), (unsigned)p.batch);
 }
 
 // The K range of this workgroup: split blockIdx.y covers

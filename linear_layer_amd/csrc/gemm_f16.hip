@@ -747,13 +747,13 @@ const TileInfo kF16Tiles[kF16NumTiles] = {
     // 128x128 in two K-slices (direct kernel only; the staged fallback runs
     // the plain tile): eight waves, one workgroup per CU; only with at least
     // 8 stages of 64 per slice (below, 0.5-1 us slower than plain 128x128)
-    {F16_S::BM, F16_S::BN, 1, 0.60f, 0.60f, "f16_128x128_k2", 2, false, 512, 2 * 8 * 64},
+    {F16_S::BM, F16_S::BN, 1, 0.60f, 0.60f, "f16_128x128_k2", 2, false, 512, 2 * 8 * 64, true},
     // 192x192 (direct kernel; unaligned operands run the staged 128x128):
     // eight waves, one workgroup per CU; 0.74 on 3072^3, 0.79 on 8192^3,
     // 0.85 on 4096^3. It wins where 256x256 leaves CUs idle and 192x192 does
     // not (3072^2: 256 tiles against 144).
     {192, 192, 1, 0.75f, 0.75f, "f16_192x192_direct", 1, false,
-     64 * DirectCfg<192>::WGM * DirectCfg<192>::WGN},
+     64 * DirectCfg<192>::WGM * DirectCfg<192>::WGN, 0, true},
 };
 
 // The direct kernel on BM x BM tiles (KS K-slices) for 128-bit-aligned

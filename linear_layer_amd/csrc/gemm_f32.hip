@@ -803,8 +803,8 @@ const TileInfo kF32Tiles[kF32NumTiles] = {
     // each only when every slice gets at least 8 stages of 32 (smaller K: the
     // partial-sum exchange costs more than the slices save; 256^3 8.9 us with
     // slices against 8.3 plain, 512^3 11.1 against 10.3 split across workgroups).
-    {F32_XS::BM, F32_XS::BN, 1, 0.57f, 0.57f, "f32_64x64_k4", 4, true, 1024, 4 * 8 * 32},
-    {F32_S::BM, F32_S::BN, 1, 0.90f, 0.90f, "f32_128x128_k2", 2, true, 512, 2 * 8 * 32},
+    {F32_XS::BM, F32_XS::BN, 1, 0.57f, 0.57f, "f32_64x64_k4", 4, true, 1024, 4 * 8 * 32, true},
+    {F32_S::BM, F32_S::BN, 1, 0.90f, 0.90f, "f32_128x128_k2", 2, true, 512, 2 * 8 * 32, true},
 };
 #endif
 

@@ -17,6 +17,7 @@ struct TileInfo {
     bool stream_k = true;  // the tile's kernel can run a stream-K launch
     int threads = 256;     // largest workgroup of the tile's kernels
     int min_k = 0;         // K-sliced tiles: the K below which slices get too few stages
+    bool direct_only = false;  // only the 128-bit-load kernels have this shape
 };
 
 constexpr int kF32NumTiles = 6;

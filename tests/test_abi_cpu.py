@@ -10,7 +10,7 @@ import pytest
 import linear_layer_amd as ll
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "linear_layer.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("linear_layer.h", "linear_layer_tuning.h")]
 
 # Fake, well-aligned, non-overlapping "device" addresses: these calls must
 # fail validation (or find no device) before anything is dereferenced.
@@ -18,9 +18,11 @@ PA, PB, PC = 0x10000000, 0x20000000, 0x30000000
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", text))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", text))
+    return names
 
 
 def test_library_exports_every_declared_symbol():
@@ -314,8 +316,10 @@ def test_plan_query_flags():
     # 16-bit: the layout flag is accepted, the ReLU flag (no 16-bit layer) is not
     assert ll.chosen_tile(f16 | nk, 8192, 8192, 8192, 256) == 0
     assert ll.chosen_tile(f16 | relu, 8192, 8192, 8192, 256) == -1
-    assert ll.chosen_tile(f32 | 0x400, 8192, 8192, 8192, 256) == -1
-    assert ll.chosen_split_k(f32 | 0x400, 64, 64, 64, 256) == -1
+    # an unknown flag is rejected (0x400 is LL_PLAN_UNALIGNED)
+    assert ll.chosen_tile(f32 | 0x800, 8192, 8192, 8192, 256) == -1
+    assert ll.chosen_split_k(f32 | 0x800, 64, 64, 64, 256) == -1
+    assert ll.chosen_tile(f32 | ll.PLAN_UNALIGNED, 8192, 8192, 8192, 256) == 0
 
 
 def test_binding_rejects_host_tensors():

@@ -91,3 +91,32 @@ def test_forced_stream_k_shares_only_leftover_tiles(dt, M, N, K):
         slots = 256 * (1 if TILE_SHAPES[dt][t] == (256, 256) or (dt == F32 and t in (4, 5)) or
                        (dt == F16 and t == 3) else 2)
         assert sk == tiles % slots if tiles >= slots else sk == tiles
+
+
+@settings(max_examples=300, deadline=None)
+@given(dt=st.sampled_from([F32, F16]), M=dims, N=dims, K=dims, batch=st.sampled_from([1, 1, 3]),
+       relu=st.booleans())
+def test_unaligned_plans_cost_what_runs(dt, M, N, K, batch, relu):
+    """Operands that rule out the 128-bit-load kernels: the planner picks
+    neither stream-K nor a tile that exists only as a direct kernel (whose
+    call would then run another shape's staged kernel)."""
+    q = dt | ll.PLAN_UNALIGNED | (ll.PLAN_RELU if relu and dt == F32 else 0)
+    t = ll.chosen_tile(q, M, N, K, 256, batch)
+    assert 0 <= t < ll.num_tiles(dt)
+    name = ll.tile_name(dt, t)
+    assert not name.endswith(("_k2", "_k4")) and "192x192" not in name, name
+    assert ll.chosen_stream_k(q, M, N, K, 256, batch) == 0
+
+
+def test_unaligned_flag_changes_only_direct_only_choices():
+    # 3072^2 16-bit takes the 192x192 direct tile when aligned, a staged one when not
+    assert ll.tile_name(F16, ll.chosen_tile(F16, 3072, 3072, 3072, 256)) == "f16_192x192_direct"
+    assert ll.tile_name(F16, ll.chosen_tile(F16 | ll.PLAN_UNALIGNED, 3072, 3072, 3072, 256)) != \
+        "f16_192x192_direct"
+    # 1024^3 FP32 takes four K-slices when aligned
+    assert ll.tile_name(F32, ll.chosen_tile(F32, 1024, 1024, 1024, 256)) == "f32_64x64_k4"
+    assert not ll.tile_name(F32, ll.chosen_tile(F32 | ll.PLAN_UNALIGNED, 1024, 1024, 1024,
+                                                 256)).endswith("_k4")
+    # 4096^3 is unaffected
+    assert ll.chosen_tile(F32 | ll.PLAN_UNALIGNED, 4096, 4096, 4096, 256) == \
+        ll.chosen_tile(F32, 4096, 4096, 4096, 256)
