@@ -13,6 +13,13 @@ its own pair of HIP events on the launch stream; peak = MI355X's published
 dense matrix peak for the dtype) and a ``cpu_baseline``
 object: the float64 CPU oracle timed on a bounded sample of the same workload
 (a block of whole output rows, or of whole batch items) on this host's cores.
+
+The default run (the 4096^3 headline) then measures the other configurations
+of the same family the same way -- 256^3, 1024^3 with alpha 1.5 and beta 0.5,
+the fused layer ReLU(X*W + b) at 2047x4096x11008 and the FP16-input 8192^3
+product -- and reports each under ``configs``: time per step, TFLOP/s and
+fraction of its dtype's matrix peak (back to back and per launch), its plan
+and an oracle sample.
 """
 from __future__ import annotations
 
@@ -55,6 +62,11 @@ def parse():
                     help="stream-K for leftover tiles: -1 automatic, 0 never, 1 whenever possible")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other configurations (256^3, 1024^3 alpha/beta, the fused layer, "
+                         "FP16 8192^3) that the default run measures after the headline one")
+    ap.add_argument("--config-cpu-seconds", type=float, default=4.0,
+                    help="target CPU time of each other configuration's oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the GEMM, run a plain device-to-device copy of 256 MiB "
                          "--steps times (the reference kernel for scaling HBM byte counters)")
@@ -172,6 +184,114 @@ def cpu_baseline(w, x, target_s: float):
     }
 
 
+def prepare(w, args, dev):
+    """Device inputs of workload w, the step callable and the plan it runs."""
+    import torch
+    import linear_layer_amd as ll
+    from linear_layer_amd import workloads as wl
+
+    x = wl.make_inputs(w)
+    A = x["A"].to(dev)
+    B = x["B"].to(dev)
+    batched = w.kind in wl.BATCHED_KINDS
+    C = torch.empty(((w.batch,) if batched else ()) + (w.M, w.N), device=dev, dtype=torch.float32)
+    if "C" in x:
+        C.copy_(x["C"].to(dev))
+    bias = x["bias"].to(dev) if "bias" in x else None
+    dtype_id = ll.DTYPE_F16 if w.kind in wl.HALF_KINDS else ll.DTYPE_F32
+    props = torch.cuda.get_device_properties(dev)
+    # the plan the step runs: the fused layer with ReLU pays for its extra
+    # pass; B given N-by-K is planned on its own
+    plan_id = dtype_id
+    if w.kind.startswith("linear") and w.act == 1:
+        plan_id |= ll.PLAN_RELU
+    if w.kind in wl.B_TRANSPOSED_KINDS:
+        plan_id |= ll.PLAN_B_NK
+    cus = props.multi_processor_count
+    plan = {
+        "tile": ll.tile_name(dtype_id, ll.chosen_tile(plan_id, w.M, w.N, w.K, cus, w.batch)),
+        "split_k": ll.chosen_split_k(plan_id, w.M, w.N, w.K, cus, w.batch),
+        "stream_k_tiles": ll.chosen_stream_k(plan_id, w.M, w.N, w.K, cus, w.batch),
+    }
+
+    def step():
+        if w.kind == "gemm_f32":
+            ll.gemm_f32(A, B, C, w.alpha, w.beta)
+        elif w.kind == "gemm_f16f32":
+            ll.gemm_f16f32(A, B, C, w.alpha, w.beta)
+        elif w.kind == "gemm_bf16f32":
+            ll.gemm_bf16f32(A, B, C, w.alpha, w.beta)
+        elif w.kind == "gemm_f16f32_nt":
+            ll.gemm_f16f32_nt(A, B, C, w.alpha, w.beta)
+        elif w.kind == "linear_nt":
+            ll.linear_bias_act_nt(A, B, bias, w.act, C)
+        elif w.kind == "gemm_f32_batched":
+            ll.gemm_f32_batched(A, B, C, w.alpha, w.beta)
+        else:
+            ll.linear_bias_act(A, B, bias, w.act, C)
+
+    return x, step, plan
+
+
+def time_steps(step, steps: int, warmup: int, dev):
+    """W untimed steps, then K steps back to back between two events on the
+    launch stream (device synchronisation on both sides); then a second pass
+    of K steps, each between its own pair of events, for per-launch times."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)  # the stream the library launches on
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return ms_per_step, launch_ms
+
+
+# The other configurations of the headline metric's workload family (the
+# 256^3 and 1024^3 alpha/beta products, the fused layer and the FP16-input
+# product), measured after the headline one in the default run.
+OTHER_CONFIGS = ["gemm_f32_256", "gemm_f32_1024_ab", "linear_relu_2047x4096x11008", "gemm_f16f32_8192"]
+
+
+def config_record(w, step, plan, args, dev, x, cpu_seconds):
+    """One configuration's figures: time per step, TFLOP/s and fraction of the
+    dtype's matrix peak (from the back-to-back pass and from the per-launch
+    pass), the plan, and the oracle timed on a bounded sample."""
+    ms_per_step, launch_ms = time_steps(step, args.steps, args.warmup, dev)
+    flops = float(w.flops)
+    peak = PEAK_TFLOPS[w.kind]
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    avg = sum(launch_ms) / len(launch_ms)
+    rec = {
+        "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta, **plan,
+        "ms_per_step": round(ms_per_step, 5),
+        "tflops": round(tflops, 3),
+        "frac_of_peak": round(tflops / peak, 4),
+        "kernel_avg_ms": round(avg, 5),
+        "kernel_median_ms": round(sorted(launch_ms)[len(launch_ms) // 2], 5),
+        "kernel_frac_of_peak": round(flops / (avg * 1e-3) / 1e12 / peak, 4),
+        "peak_tflops": peak,
+    }
+    if cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(w, x, cpu_seconds)
+    return rec
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -193,14 +313,6 @@ def main():
     w = wl.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x = wl.make_inputs(w)
-    A = x["A"].to(dev)
-    B = x["B"].to(dev)
-    batched = w.kind in wl.BATCHED_KINDS
-    C = torch.empty(((w.batch,) if batched else ()) + (w.M, w.N), device=dev, dtype=torch.float32)
-    if "C" in x:
-        C.copy_(x["C"].to(dev))
-    bias = x["bias"].to(dev) if "bias" in x else None
     dtype_id = ll.DTYPE_F16 if w.kind in wl.HALF_KINDS else ll.DTYPE_F32
     if args.tile >= 0:
         ll.set_tile(dtype_id, args.tile)
@@ -209,60 +321,8 @@ def main():
     if args.stream_k != -1:
         ll.set_stream_k(args.stream_k)
     props = torch.cuda.get_device_properties(dev)
-    # the plan the step runs: the fused layer with ReLU pays for its extra
-    # pass; B given N-by-K is planned on its own
-    plan_id = dtype_id
-    if w.kind.startswith("linear") and w.act == 1:
-        plan_id |= ll.PLAN_RELU
-    if w.kind in wl.B_TRANSPOSED_KINDS:
-        plan_id |= ll.PLAN_B_NK
-    tile = ll.chosen_tile(plan_id, w.M, w.N, w.K, props.multi_processor_count, w.batch)
-    splits = ll.chosen_split_k(plan_id, w.M, w.N, w.K, props.multi_processor_count, w.batch)
-    sk_tiles = ll.chosen_stream_k(plan_id, w.M, w.N, w.K, props.multi_processor_count, w.batch)
-
-    def step():
-        if w.kind == "gemm_f32":
-            ll.gemm_f32(A, B, C, w.alpha, w.beta)
-        elif w.kind == "gemm_f16f32":
-            ll.gemm_f16f32(A, B, C, w.alpha, w.beta)
-        elif w.kind == "gemm_bf16f32":
-            ll.gemm_bf16f32(A, B, C, w.alpha, w.beta)
-        elif w.kind == "gemm_f16f32_nt":
-            ll.gemm_f16f32_nt(A, B, C, w.alpha, w.beta)
-        elif w.kind == "linear_nt":
-            ll.linear_bias_act_nt(A, B, bias, w.act, C)
-        elif w.kind == "gemm_f32_batched":
-            ll.gemm_f32_batched(A, B, C, w.alpha, w.beta)
-        else:
-            ll.linear_bias_act(A, B, bias, w.act, C)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)  # the stream the library launches on
-    # Timed region: K steps back to back, bracketed by events on the launch
-    # stream and a device synchronisation on both sides.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    # Per-launch durations for the roofline: a second pass of K steps, each
-    # bracketed by its own pair of events on the same stream.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    x, step, plan = prepare(w, args, dev)
+    ms_per_step, launch_ms = time_steps(step, args.steps, args.warmup, dev)
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
     flops = float(w.flops)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -272,7 +332,22 @@ def main():
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, x, args.cpu_seconds)
+    del x, step
+    torch.cuda.empty_cache()
 
+    # the other configurations (default run only, with the automatic plan)
+    configs = None
+    if (args.workload == "gemm_f32_4096" and not args.no_configs and args.tile < 0
+            and args.split_k < 1 and args.stream_k == -1):
+        configs = {}
+        for name in OTHER_CONFIGS:
+            wo = wl.WORKLOADS[name]
+            xo, so, po = prepare(wo, args, dev)
+            configs[name] = config_record(wo, so, po, args, dev, xo, args.config_cpu_seconds)
+            del xo, so
+            torch.cuda.empty_cache()
+
+    batched = w.kind in wl.BATCHED_KINDS
     dtype = {"gemm_f32": "f32", "linear": "f32", "linear_nt": "f32", "gemm_f32_batched": "f32",
              "gemm_f16f32": "f16 in, f32 accumulate", "gemm_f16f32_nt": "f16 in, f32 accumulate",
              "gemm_bf16f32": "bf16 in, f32 accumulate"}[w.kind]
@@ -296,7 +371,7 @@ def main():
                if w.kind in ("linear", "linear_nt") else {}),
             **({"b_layout": "N-by-K"} if w.kind in wl.B_TRANSPOSED_KINDS else {}),
             **({"batch": w.batch} if batched else {}),
-            "tile": ll.tile_name(dtype_id, tile), "split_k": splits, "stream_k_tiles": sk_tiles,
+            **plan,
             "device": props.name, "cus": props.multi_processor_count, "hip": torch.version.hip,
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
@@ -314,6 +389,8 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if configs is not None:
+        out["configs"] = configs
     print(json.dumps(out), flush=True)
 
 

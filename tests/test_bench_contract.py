@@ -55,3 +55,27 @@ def test_one_json_line_with_every_field(workload):
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
     assert cb["unit"] == d["unit"]
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not _has_gpu(), reason="needs a GPU")
+def test_default_run_reports_every_configuration():
+    """The default run (the 4096^3 headline) also reports the 256^3, 1024^3
+    alpha/beta, fused-layer and FP16 8192^3 configurations, each with its time
+    per step, TFLOP/s, fraction of its dtype's peak and an oracle sample."""
+    r = run_bench("--steps", "3", "--warmup", "1", "--cpu-seconds", "0.5",
+                  "--config-cpu-seconds", "0.3", timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    assert d["config"]["workload"] == "gemm_f32_4096" and d["roofline"]["peak"] == 157.3
+    cf = d["configs"]
+    assert set(cf) == {"gemm_f32_256", "gemm_f32_1024_ab", "linear_relu_2047x4096x11008",
+                       "gemm_f16f32_8192"}
+    for name, c in cf.items():
+        assert c["ms_per_step"] > 0 and c["tflops"] > 0, name
+        assert 0 < c["frac_of_peak"] <= 1 and 0 < c["kernel_frac_of_peak"] <= 1, name
+        assert abs(c["tflops"] / c["peak_tflops"] - c["frac_of_peak"]) < 1e-3, name
+        assert c["cpu_baseline"]["kind"] == "oracle" and c["cpu_baseline"]["cores"] >= 1, name
+    assert cf["gemm_f16f32_8192"]["peak_tflops"] == 2516.6
