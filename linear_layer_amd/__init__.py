@@ -44,7 +44,10 @@ DTYPE_F32, DTYPE_F16 = 0, 1
 PLAN_RELU, PLAN_B_NK, PLAN_UNALIGNED = 0x100, 0x200, 0x400   # flags OR-ed into dtype for chosen_*
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liblinear_layer.so")
+# The in-package library, or another build of it named by LINEAR_LAYER_LIBRARY
+# (the CPU sanitizer test loads an AddressSanitizer build of the host code
+# that way). Either way the file must exist: there is no fallback.
+_LIB_PATH = os.environ.get("LINEAR_LAYER_LIBRARY") or os.path.join(_HERE, "liblinear_layer.so")
 _lib = None
 
 # Every symbol the C header declares.

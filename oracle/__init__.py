@@ -31,13 +31,16 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so (gcc, OpenMP, strict IEEE double)."""
+def build(force: bool = True, extra_flags=()) -> str:
+    """Compile oracle.c into liboracle.so (gcc, OpenMP, strict IEEE double).
+
+    ``extra_flags`` go to gcc as well (the sanitizer test builds a copy with
+    AddressSanitizer and UndefinedBehaviorSanitizer this way)."""
     if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra", *extra_flags,
            _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)

@@ -329,3 +329,26 @@ def test_binding_rejects_host_tensors():
         ll.gemm_f32(A, A, A)
     with pytest.raises(TypeError):
         ll.gemm_f32(A.double(), A, A)
+
+
+def test_extreme_sizes_stay_in_range():
+    """Sizes at the 32-bit limits go through the argument checks and the plan
+    queries without overflow (the sanitizer build runs this under UBSan)."""
+    big = 2**31 - 1
+    lib = ll.load()
+    for f16 in (False, True):
+        fn = lib.gemm_f16f32 if f16 else lib.gemm_f32
+        elem = 2 if f16 else 4
+        # K at the limit, one output element
+        st = fn(1, 1, big, 1.0, PA, big, PA + big * elem + 64, 1, 0.0, PC + 2 * big * elem, 1, None)
+        assert st in (ll.OK, ll.ERR_NO_DEVICE, ll.ERR_UNSUPPORTED_ARCH, ll.ERR_INVALID_VALUE)
+        # leading dimensions at the limit
+        st = fn(2, 2, 2, 1.0, PA, big, PB, big, 0.0, PC, big, None)
+        assert st in (ll.ERR_NO_DEVICE, ll.ERR_UNSUPPORTED_ARCH, ll.ERR_INVALID_VALUE)
+    for dt in (ll.DTYPE_F32, ll.DTYPE_F16):
+        for M, N, K in [(1, 1, big), (big, 1, 1), (1, big, 1), (big, big, big), (big, 256, big)]:
+            for flags in (0, ll.PLAN_UNALIGNED):
+                t = ll.chosen_tile(dt | flags, M, N, K, 256)
+                s = ll.chosen_split_k(dt | flags, M, N, K, 256)
+                sk = ll.chosen_stream_k(dt | flags, M, N, K, 256)
+                assert t == -1 or (0 <= t < ll.num_tiles(dt) and 1 <= s <= 16 and sk >= 0)
