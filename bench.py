@@ -14,12 +14,12 @@ dense matrix peak for the dtype) and a ``cpu_baseline``
 object: the float64 CPU oracle timed on a bounded sample of the same workload
 (a block of whole output rows, or of whole batch items) on this host's cores.
 
-The default run (the 4096^3 headline) then measures the other configurations
-of the same family the same way -- 256^3, 1024^3 with alpha 1.5 and beta 0.5,
-the fused layer ReLU(X*W + b) at 2047x4096x11008 and the FP16-input 8192^3
-product -- and reports each under ``configs``: time per step, TFLOP/s and
-fraction of its dtype's matrix peak (back to back and per launch), its plan
-and an oracle sample.
+The default run also measures the other configurations of the same family --
+256^3, 1024^3 with alpha 1.5 and beta 0.5, the fused layer ReLU(X*W + b) at
+2047x4096x11008 and the FP16-input 8192^3 product -- before the headline, and
+reports each under ``configs``: time per step, TFLOP/s and fraction of its
+dtype's matrix peak (back to back and per launch), its plan and an oracle
+sample. All oracle samples run after all GPU timing.
 """
 from __future__ import annotations
 
@@ -233,14 +233,24 @@ def prepare(w, args, dev):
     return x, step, plan
 
 
-def time_steps(step, steps: int, warmup: int, dev):
-    """W untimed steps, then K steps back to back between two events on the
-    launch stream (device synchronisation on both sides); then a second pass
-    of K steps, each between its own pair of events, for per-launch times."""
+def time_steps(step, steps: int, warmup: int, dev, min_warm_ms: float = 0.0):
+    """W untimed steps (continued, when min_warm_ms > 0, until that much GPU
+    time has passed, so that short kernels run at a settled clock), then K
+    steps back to back between two events on the launch stream (device
+    synchronisation on both sides); then a second pass of K steps, each
+    between its own pair of events, for per-launch times. Returns
+    (ms per step, per-launch ms, warm-up steps run)."""
     import torch
+    t_warm = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    done = warmup
+    while min_warm_ms > 0 and (time.perf_counter() - t_warm) * 1e3 < min_warm_ms:
+        for _ in range(max(warmup, 8)):
+            step()
+        done += max(warmup, 8)
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)  # the stream the library launches on
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -259,7 +269,7 @@ def time_steps(step, steps: int, warmup: int, dev):
         e1.record(stream)
     torch.cuda.synchronize()
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-    return ms_per_step, launch_ms
+    return ms_per_step, launch_ms, done
 
 
 # The other configurations of the headline metric's workload family (the
@@ -268,17 +278,24 @@ def time_steps(step, steps: int, warmup: int, dev):
 OTHER_CONFIGS = ["gemm_f32_256", "gemm_f32_1024_ab", "linear_relu_2047x4096x11008", "gemm_f16f32_8192"]
 
 
-def config_record(w, step, plan, args, dev, x, cpu_seconds):
-    """One configuration's figures: time per step, TFLOP/s and fraction of the
-    dtype's matrix peak (from the back-to-back pass and from the per-launch
-    pass), the plan, and the oracle timed on a bounded sample."""
-    ms_per_step, launch_ms = time_steps(step, args.steps, args.warmup, dev)
+# Warm-up of each other configuration: the driver's W steps, continued until
+# this much GPU time has passed (a few steps of a 20-us kernel would be timed
+# while the clock still ramps up).
+CONFIG_WARM_MS = 50.0
+
+
+def config_record(w, step, plan, args, dev):
+    """One configuration's GPU figures: time per step, TFLOP/s and fraction of
+    the dtype's matrix peak (from the back-to-back pass and from the per-launch
+    pass) and the plan; the oracle sample is added later."""
+    ms_per_step, launch_ms, warm = time_steps(step, args.steps, args.warmup, dev, CONFIG_WARM_MS)
     flops = float(w.flops)
     peak = PEAK_TFLOPS[w.kind]
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     avg = sum(launch_ms) / len(launch_ms)
     rec = {
         "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha, "beta": w.beta, **plan,
+        "steps": args.steps, "warmup_steps": warm,
         "ms_per_step": round(ms_per_step, 5),
         "tflops": round(tflops, 3),
         "frac_of_peak": round(tflops / peak, 4),
@@ -287,8 +304,6 @@ def config_record(w, step, plan, args, dev, x, cpu_seconds):
         "kernel_frac_of_peak": round(flops / (avg * 1e-3) / 1e12 / peak, 4),
         "peak_tflops": peak,
     }
-    if cpu_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline(w, x, cpu_seconds)
     return rec
 
 
@@ -321,31 +336,41 @@ def main():
     if args.stream_k != -1:
         ll.set_stream_k(args.stream_k)
     props = torch.cuda.get_device_properties(dev)
+    # the headline's inputs, made and uploaded before any timing
     x, step, plan = prepare(w, args, dev)
-    ms_per_step, launch_ms = time_steps(step, args.steps, args.warmup, dev)
-    avg_launch_ms = sum(launch_ms) / len(launch_ms)
-    flops = float(w.flops)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.kind]
 
-    cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, x, args.cpu_seconds)
-    del x, step
-    torch.cuda.empty_cache()
-
-    # the other configurations (default run only, with the automatic plan)
-    configs = None
+    # The other configurations (default run only, with the automatic plan)
+    # are timed first and the headline right after them, and every oracle
+    # sample runs after all GPU timing: while the host works the GPU idles
+    # and its clock drops.
+    configs, config_inputs = None, {}
     if (args.workload == "gemm_f32_4096" and not args.no_configs and args.tile < 0
             and args.split_k < 1 and args.stream_k == -1):
         configs = {}
         for name in OTHER_CONFIGS:
             wo = wl.WORKLOADS[name]
             xo, so, po = prepare(wo, args, dev)
-            configs[name] = config_record(wo, so, po, args, dev, xo, args.config_cpu_seconds)
-            del xo, so
+            configs[name] = config_record(wo, so, po, args, dev)
+            config_inputs[name] = (wo, xo)
+            del so
             torch.cuda.empty_cache()
+
+    # the headline: exactly W warm-up steps, then K timed steps
+    ms_per_step, launch_ms, _ = time_steps(step, args.steps, args.warmup, dev)
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.kind]
+    del step
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, x, args.cpu_seconds)
+    if configs is not None and args.config_cpu_seconds > 0:
+        for name, (wo, xo) in config_inputs.items():
+            configs[name]["cpu_baseline"] = cpu_baseline(wo, xo, args.config_cpu_seconds)
 
     batched = w.kind in wl.BATCHED_KINDS
     dtype = {"gemm_f32": "f32", "linear": "f32", "linear_nt": "f32", "gemm_f32_batched": "f32",

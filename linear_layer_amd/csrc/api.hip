@@ -244,6 +244,9 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
         const int64_t tiles_mn = (int64_t)cdiv(M, ti.bm) * cdiv(N, ti.bn);
         if (tiles_mn > max_grid_x(ti.threads))
             continue;   // more workgroups than one launch can hold
+        if ((int64_t)cdiv(M, ti.bm) * ti.bm > (int64_t)1 << 31 ||
+            (int64_t)cdiv(N, ti.bn) * ti.bn > (int64_t)1 << 31)
+            continue;   // a row or column index inside the last tile would pass 2^31 - 1
         if (K < ti.min_k && t_ov != t)
             continue;   // K too short for the tile's K-slices (unless forced)
         if (!vec && ti.direct_only && t_ov != t)

@@ -200,70 +200,95 @@ __device__ __forceinline__ const T *zero_chunk()
 // this wave are outstanding (expcnt and lgkmcnt left at their maxima).
 #define LL_VMCNT(n) ((((n) & 0xF) | (0x7 << 4) | (0xF << 8) | ((((n) >> 4) & 3) << 14)))
 
-// The fused epilogue of one output element: acc is the accumulated product,
-// bv the bias of its column (EPI_LINEAR).
-template <int EPI>
-__device__ __forceinline__ void store_one(const GemmParams &p, float *dst, float v, float bv)
+// The fused write-back of one MFMA accumulator block (page "GEMM 优化详解",
+// "Level 6: Kernel Fusion": alpha/beta, or bias by output column then ReLU,
+// applied to the accumulators before the single store).
+//
+// Accumulator layouts (wave64): v_mfma_f32_32x32x* (MF = 32, 16 registers):
+// lane l holds column l % 32, register r row 8*(r/4) + 4*(l/32) + r%4;
+// v_mfma_f32_16x16x* (MF = 16, 4 registers): lane l holds column l % 16,
+// register r row 4*(l/16) + r.
+//
+// The values are computed first, with the loads they need (beta*C, the
+// bias) issued together from in-bounds addresses (row and column clamped to
+// the matrix), and stored afterwards. A masked store is a branch, and a load
+// whose result is first used inside one would make every later store wait
+// for all earlier memory operations (loads and stores share one counter), so
+// no store may depend on a load that was not consumed before the first store.
+// Rows of a block that lies inside the matrix (a uniform test) need no mask.
+template <int EPI, int MF, class Acc>
+__device__ __forceinline__ void write_acc(const GemmParams &p, const Acc &acc, int row0, int col0,
+                                          int lane)
 {
+    constexpr int R = MF == 32 ? 16 : 4;
+    const int col = col0 + (lane % MF);
+    const int rbase = row0 + (lane / MF) * 4;
+    auto row = [&](int r) { return MF == 32 ? rbase + ((r >> 2) << 3) + (r & 3) : rbase + r; };
+    const bool full = row0 <= p.M - MF;
+    const bool col_ok = col < p.N;
+    float *dst = p.C + col;
+    auto put = [&](int r, float v) {
+        if (col_ok && (full || row(r) < p.M))
+            dst[(int64_t)row(r) * p.ldc] = v;
+    };
     if (EPI == EPI_ATOMIC) {
-        // split-K: every split adds its share; C was pre-scaled by beta
-        __hip_atomic_fetch_add(dst, p.alpha * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return;
-    }
-    if (EPI == EPI_GEMM_BETA0) {
-        v = p.alpha * v;
+        // split-K / stream-K share: every contributor adds alpha times its
+        // partial sum; C was prepared (beta*C, or the bias) beforehand
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (col_ok && row(r) < p.M)
+                __hip_atomic_fetch_add(dst + (int64_t)row(r) * p.ldc, p.alpha * acc[r],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else if (EPI == EPI_GEMM_BETA) {
-        v = __builtin_fmaf(p.alpha, v, p.beta * *dst);
+        // beta*C in groups of G rows (loads, then stores): at most G values of
+        // C are held at once
+        constexpr int G = R < 4 ? R : 4;
+        const int64_t cc = col_ok ? col : p.N - 1;
+#pragma unroll
+        for (int g = 0; g < R; g += G) {
+            float c[G];
+#pragma unroll
+            for (int r = 0; r < G; ++r) {
+                const int rr = row(g + r);
+                c[r] = p.C[(int64_t)(rr < p.M ? rr : p.M - 1) * p.ldc + cc];
+            }
+#pragma unroll
+            for (int r = 0; r < G; ++r)
+                c[r] = __builtin_fmaf(p.alpha, acc[g + r], p.beta * c[r]);
+#pragma unroll
+            for (int r = 0; r < G; ++r)
+                put(g + r, c[r]);
+        }
+    } else if (EPI == EPI_LINEAR) {
+        const float bv = p.bias != nullptr ? p.bias[col_ok ? col : p.N - 1] : 0.0f;
+        float v[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float y = acc[r] + bv;
+            v[r] = (p.act == 1 && !(y > 0.0f)) ? 0.0f : y;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            put(r, v[r]);
     } else {
-        v = v + bv;
-        if (p.act == 1)
-            v = v > 0.0f ? v : 0.0f;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            put(r, p.alpha * acc[r]);
     }
-    *dst = v;
 }
 
-// The fused write-back of one 32x32 MFMA accumulator block.
-//
-// Accumulator layout of v_mfma_f32_32x32x* (wave64): lane l holds column
-// l % 32; register r holds row 8*(r/4) + 4*(l/32) + r%4.
 template <int EPI>
 __device__ __forceinline__ void write_block(const GemmParams &p, const f32x16 &acc,
                                             int row0, int col0, int lane)
 {
-    const int col = col0 + (lane & 31);
-    if (col >= p.N)
-        return;
-    const int rbase = row0 + ((lane >> 5) << 2);
-    float bv = 0.0f;
-    if (EPI == EPI_LINEAR && p.bias != nullptr)
-        bv = p.bias[col];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = rbase + ((r >> 2) << 3) + (r & 3);
-        if (row < p.M)
-            store_one<EPI>(p, p.C + (int64_t)row * p.ldc + col, acc[r], bv);
-    }
+    write_acc<EPI, 32>(p, acc, row0, col0, lane);
 }
 
-// The same for one 16x16 block of v_mfma_f32_16x16x*: lane l holds column
-// l % 16; register r holds row 4*(l/16) + r.
 template <int EPI>
 __device__ __forceinline__ void write_block16(const GemmParams &p, const f32x4 &acc,
                                               int row0, int col0, int lane)
 {
-    const int col = col0 + (lane & 15);
-    if (col >= p.N)
-        return;
-    const int rbase = row0 + ((lane >> 4) << 2);
-    float bv = 0.0f;
-    if (EPI == EPI_LINEAR && p.bias != nullptr)
-        bv = p.bias[col];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = rbase + r;
-        if (row < p.M)
-            store_one<EPI>(p, p.C + (int64_t)row * p.ldc + col, acc[r], bv);
-    }
+    write_acc<EPI, 16>(p, acc, row0, col0, lane);
 }
 
 }  // namespace ll
