@@ -284,6 +284,97 @@ __device__ __forceinline__ void write_block(const GemmParams &p, const f32x16 &a
     write_acc<EPI, 32>(p, acc, row0, col0, lane);
 }
 
+// LDS floats one wave needs for write_block_x4.
+constexpr int kStageFloats = 608;
+
+// The fused write-back of one 32x32 block with 128-bit stores (C 16-byte
+// aligned, ldc a multiple of 4). A lane holds one column of the block, so
+// each half of 16 rows goes through `stage` (kStageFloats floats of LDS
+// owned by this wave) to give every lane four consecutive columns of two
+// rows: local row lr sits at float (lr + lr/4)*32, so the two half-waves of
+// a 32-bit write (rows lr and lr+4) hit opposite halves of the 64 banks and
+// the 16 lanes of a 128-bit read (rows 2i, 2i+1) eight 16-byte groups each.
+// The epilogue is the one of write_acc; four columns that cross N are
+// stored one by one.
+template <int EPI>
+__device__ __forceinline__ void write_block_x4(const GemmParams &p, const f32x16 &acc, int row0,
+                                               int col0, int lane, float *stage)
+{
+    const int c = lane & 31, rb = (lane >> 5) << 2;
+    const int cq = (lane & 7) << 2, rq = lane >> 3;
+    const int col = col0 + cq;
+    const bool vec = col + 3 < p.N;
+    f32x4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (EPI == EPI_LINEAR && p.bias != nullptr) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            bv[e] = p.bias[col + e < p.N ? col + e : p.N - 1];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int lr = ((r >> 2) << 3) + rb + (r & 3);
+            stage[(lr + (lr >> 2)) * 32 + c] = acc[8 * h + r];
+        }
+        f32x4 v[2];
+        int row[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int lr = rq + 8 * j;
+            v[j] = *reinterpret_cast<const f32x4 *>(&stage[(lr + (lr >> 2)) * 32 + cq]);
+            row[j] = row0 + 16 * h + lr;
+        }
+        if (EPI == EPI_GEMM_BETA) {
+            f32x4 cv[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t rr = row[j] < p.M ? row[j] : p.M - 1;
+                if (vec) {
+                    cv[j] = *reinterpret_cast<const f32x4 *>(&p.C[rr * p.ldc + col]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        cv[j][e] = p.C[rr * p.ldc + (col + e < p.N ? col + e : p.N - 1)];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[j][e] = __builtin_fmaf(p.alpha, v[j][e], p.beta * cv[j][e]);
+        } else if (EPI == EPI_LINEAR) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float y = v[j][e] + bv[e];
+                    v[j][e] = (p.act == 1 && !(y > 0.0f)) ? 0.0f : y;
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[j][e] = p.alpha * v[j][e];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (row[j] >= p.M)
+                continue;
+            float *dst = p.C + (int64_t)row[j] * p.ldc + col;
+            if (vec) {
+                *reinterpret_cast<f32x4 *>(dst) = v[j];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < p.N)
+                        dst[e] = v[j][e];
+            }
+        }
+    }
+}
+
 template <int EPI>
 __device__ __forceinline__ void write_block16(const GemmParams &p, const f32x4 &acc,
                                               int row0, int col0, int lane)
