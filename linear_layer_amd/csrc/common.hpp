@@ -296,14 +296,49 @@ constexpr int kStageFloats = 608;
 // the 16 lanes of a 128-bit read (rows 2i, 2i+1) eight 16-byte groups each.
 // The epilogue is the one of write_acc; four columns that cross N are
 // stored one by one.
-template <int EPI>
+// The values of C (beta*C) that write_block_x4 combines into this lane's
+// stores, index 2*h + j: rows row0 + 16h + 8j + lane/8, columns col0 +
+// 4*(lane%8) .. +3 (rows and columns clamped to the matrix). A kernel may
+// load them early, so their latency hides behind the product.
+__device__ __forceinline__ void load_c_x4(const GemmParams &p, int row0, int col0, int lane,
+                                          f32x4 (&cv)[4])
+{
+    const int col = col0 + ((lane & 7) << 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = row0 + 16 * (i >> 1) + 8 * (i & 1) + (lane >> 3);
+        const int64_t rr = row < p.M ? row : p.M - 1;
+        if (col + 3 < p.N) {
+            cv[i] = *reinterpret_cast<const f32x4 *>(&p.C[rr * p.ldc + col]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                cv[i][e] = p.C[rr * p.ldc + (col + e < p.N ? col + e : p.N - 1)];
+        }
+    }
+}
+
+template <int EPI, bool PRE = false>
 __device__ __forceinline__ void write_block_x4(const GemmParams &p, const f32x16 &acc, int row0,
-                                               int col0, int lane, float *stage)
+                                               int col0, int lane, float *stage,
+                                               const f32x4 *cpre = nullptr)
 {
     const int c = lane & 31, rb = (lane >> 5) << 2;
     const int cq = (lane & 7) << 2, rq = lane >> 3;
     const int col = col0 + cq;
     const bool vec = col + 3 < p.N;
+    // beta*C of both halves, loaded before the first LDS round trip (or
+    // earlier, by the caller: PRE)
+    f32x4 cv[4];
+    if (EPI == EPI_GEMM_BETA) {
+        if constexpr (PRE) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                cv[i] = cpre[i];
+        } else {
+            load_c_x4(p, row0, col0, lane, cv);
+        }
+    }
     f32x4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
     if (EPI == EPI_LINEAR && p.bias != nullptr) {
 #pragma unroll
@@ -326,23 +361,11 @@ __device__ __forceinline__ void write_block_x4(const GemmParams &p, const f32x16
             row[j] = row0 + 16 * h + lr;
         }
         if (EPI == EPI_GEMM_BETA) {
-            f32x4 cv[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int64_t rr = row[j] < p.M ? row[j] : p.M - 1;
-                if (vec) {
-                    cv[j] = *reinterpret_cast<const f32x4 *>(&p.C[rr * p.ldc + col]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        cv[j][e] = p.C[rr * p.ldc + (col + e < p.N ? col + e : p.N - 1)];
-                }
-            }
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    v[j][e] = __builtin_fmaf(p.alpha, v[j][e], p.beta * cv[j][e]);
+                    v[j][e] = __builtin_fmaf(p.alpha, v[j][e], p.beta * cv[2 * h + j][e]);
         } else if (EPI == EPI_LINEAR) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)

@@ -378,6 +378,15 @@ gemm_f32_direct_kernel(GemmParams p)
     const float *__restrict__ B =
         static_cast<const float *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
     const int M = p.M, N = p.N;
+    // beta*C with K-slices and one block per wave (the small tiles of small
+    // problems): slice 0 loads its C values now, so that their latency hides
+    // behind the product instead of following it
+    constexpr bool PRE_C = EPI == EPI_GEMM_BETA && KS > 1 && FM * FN == 1;
+    f32x4 cpre[PRE_C ? 4 : 1];
+    if constexpr (PRE_C) {
+        if (slice == 0)
+            load_c_x4(p, m0 + wm * WTM, n0 + wn * WTN, lane, cpre);
+    }
 
     // Copy sources. Row-panel copy j (A, or B given N-by-K) covers rows
     // (wave*COPIES + j)*RPC + lane/CPR. Each wave's rows start at a multiple
@@ -667,8 +676,8 @@ gemm_f32_direct_kernel(GemmParams p)
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
-                write_block_x4<EPI>(p, acc[fm][fn], m0 + wm * WTM + fm * 32, n0 + wn * WTN + fn * 32,
-                                    lane, stage);
+                write_block_x4<EPI, PRE_C>(p, acc[fm][fn], m0 + wm * WTM + fm * 32,
+                                           n0 + wn * WTN + fn * 32, lane, stage, cpre);
     }
     }
 }
