@@ -296,6 +296,64 @@ constexpr int kStageFloats = 608;
 // the 16 lanes of a 128-bit read (rows 2i, 2i+1) eight 16-byte groups each.
 // The epilogue is the one of write_acc; four columns that cross N are
 // stored one by one.
+// The fused epilogue of four consecutive outputs C(row, col .. col+3), whose
+// accumulated sums are v (cv: their beta*C inputs, for EPI_GEMM_BETA), stored
+// with one 128-bit access when all four lie inside N, else one by one; rows
+// outside M store nothing. EPI_ATOMIC adds alpha*v atomically.
+template <int EPI>
+__device__ __forceinline__ void finish4(const GemmParams &p, f32x4 v, int row, int col,
+                                        const f32x4 &cv)
+{
+    if (row >= p.M)
+        return;
+    const bool vec = col + 3 < p.N;
+    float *dst = p.C + (int64_t)row * p.ldc + col;
+    if (EPI == EPI_ATOMIC) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (col + e < p.N)
+                __hip_atomic_fetch_add(dst + e, p.alpha * v[e], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (EPI == EPI_GEMM_BETA) {
+            v[e] = __builtin_fmaf(p.alpha, v[e], p.beta * cv[e]);
+        } else if (EPI == EPI_LINEAR) {
+            const float bv = p.bias != nullptr ? p.bias[col + e < p.N ? col + e : p.N - 1] : 0.0f;
+            const float y = v[e] + bv;
+            v[e] = (p.act == 1 && !(y > 0.0f)) ? 0.0f : y;
+        } else {
+            v[e] = p.alpha * v[e];
+        }
+    }
+    if (vec) {
+        *reinterpret_cast<f32x4 *>(dst) = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (col + e < p.N)
+                dst[e] = v[e];
+    }
+}
+
+// The four values of C at (row, col .. col+3), the row and columns clamped to
+// the matrix (beta*C inputs of finish4).
+__device__ __forceinline__ f32x4 load_c4(const GemmParams &p, int row, int col)
+{
+    const int64_t rr = row < p.M ? row : p.M - 1;
+    f32x4 c;
+    if (col + 3 < p.N) {
+        c = *reinterpret_cast<const f32x4 *>(&p.C[rr * p.ldc + col]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            c[e] = p.C[rr * p.ldc + (col + e < p.N ? col + e : p.N - 1)];
+    }
+    return c;
+}
+
 // The values of C (beta*C) that write_block_x4 combines into this lane's
 // stores, index 2*h + j: rows row0 + 16h + 8j + lane/8, columns col0 +
 // 4*(lane%8) .. +3 (rows and columns clamped to the matrix). A kernel may

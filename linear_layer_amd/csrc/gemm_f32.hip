@@ -381,9 +381,22 @@ gemm_f32_direct_kernel(GemmParams p)
     // beta*C with K-slices and one block per wave (the small tiles of small
     // problems): slice 0 loads its C values now, so that their latency hides
     // behind the product instead of following it
-    constexpr bool PRE_C = EPI == EPI_GEMM_BETA && KS > 1 && FM * FN == 1;
+    // With K-slices whose partial tiles fit the A rings whole (SUM_ALL: the
+    // 64x64 tile in four slices), every lane finishes one 128-bit group of the
+    // tile, and preloads its beta*C too.
+    constexpr bool SUM_ALL = KS > 1 && BN <= NBUF * BK && BN >= 64 && BN % 64 == 0;
+    constexpr int SUM_GROUPS = SUM_ALL ? BM * BN / 4 / (KS * NW * 64) : 1;   // per lane
+    static_assert(!SUM_ALL || SUM_GROUPS * KS * NW * 64 * 4 == BM * BN, "groups per lane");
+    constexpr bool PRE_C = EPI == EPI_GEMM_BETA && KS > 1 && (SUM_ALL || FM * FN == 1);
     f32x4 cpre[PRE_C ? 4 : 1];
-    if constexpr (PRE_C) {
+    if constexpr (PRE_C && SUM_ALL) {
+        static_assert(SUM_GROUPS <= 4, "preloaded groups");
+#pragma unroll
+        for (int i = 0; i < SUM_GROUPS; ++i) {
+            const int q = tid + i * (KS * NW * 64);
+            cpre[i] = load_c4(p, m0 + q / (BN / 4), n0 + (q % (BN / 4)) * 4);
+        }
+    } else if constexpr (PRE_C) {
         if (slice == 0)
             load_c_x4(p, m0 + wm * WTM, n0 + wn * WTN, lane, cpre);
     }
@@ -616,7 +629,43 @@ gemm_f32_direct_kernel(GemmParams p)
         buf = nbuf;
     }
 
-    if constexpr (KS > 1) {
+    if constexpr (SUM_ALL) {
+        // Every slice writes its partial tile into its own (now idle) A ring
+        // as a BM x BN row-major array, columns XOR 32 on rows with bit 2 set
+        // (the two half-waves of a write, rows r and r+4, then fill opposite
+        // halves of the 64 banks); then every lane of the workgroup adds the
+        // slices of its groups of four columns in slice order (the order of
+        // the path below) and finishes them with 128-bit accesses.
+        __syncthreads();   // every slice is done reading its ring
+        float *part = &As[slice][0][0];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wm * WTM + fm * 32 + ((r >> 2) << 3) + ((lane >> 5) << 2) + (r & 3);
+                    const int col = wn * WTN + fn * 32 + (lane & 31);
+                    part[row * BN + (col ^ (((row >> 2) & 1) << 5))] = acc[fm][fn][r];
+                }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < SUM_GROUPS; ++i) {
+            const int q = tid + i * (KS * NW * 64);
+            const int row = q / (BN / 4), col = (q % (BN / 4)) * 4;
+            const int pc = col ^ (((row >> 2) & 1) << 5);
+            f32x4 v = *reinterpret_cast<const f32x4 *>(&As[0][0][row * BN + pc]);
+#pragma unroll
+            for (int sl = 1; sl < KS; ++sl) {
+                const f32x4 w = *reinterpret_cast<const f32x4 *>(&As[sl][0][row * BN + pc]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[e] += w[e];
+            }
+            finish4<EPI>(p, v, m0 + row, n0 + col, PRE_C ? cpre[PRE_C ? i : 0] : v);
+        }
+        continue;   // (a K-sliced tile has one segment)
+    } else if constexpr (KS > 1) {
         // Slices 1.. park their partial tiles in the (now idle) A rings, one
         // float per lane per slot, then slice 0 adds them in slice order.
         float *part = &As[0][0][0];
