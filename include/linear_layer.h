@@ -159,6 +159,48 @@ int linear_bias_act_nt(int M, int N, int K,
                        float *Y, int ldy, void *stream);
 
 /*
+ * linear_bias_act_ws — the fused layer of linear_bias_act (w_layout
+ * LL_W_K_BY_N) or linear_bias_act_nt (LL_W_N_BY_K) with a caller-provided
+ * workspace, so that the bias and ReLU stay fused into the write-back of
+ * every output tile (page "GEMM 优化详解", "Level 6: Kernel Fusion").
+ *
+ * Without a workspace, a plan that shares the K range of leftover tiles out
+ * over several workgroups (stream-K; e.g. 2047 x 11008 x 4096, 88 of 344
+ * tiles) adds their partial sums atomically into Y, which a pass fills with
+ * the bias first and another pass finishes with the ReLU: three launches.
+ * With a workspace of at least ll_linear_workspace_size bytes, the partial
+ * sums go to a workspace tile and the last workgroup to contribute to a tile
+ * applies bias and ReLU and writes it: one launch, no pass over Y.
+ *
+ *   workspace        device memory owned by the caller, 256-byte aligned, not
+ *                    overlapping X, W, bias or Y; it must hold zeros before
+ *                    its first use (e.g. hipMemset to 0), and every call that
+ *                    completes leaves it holding zeros again. NULL (with
+ *                    workspace_bytes 0) or a workspace smaller than the plan
+ *                    needs: the three-launch plan runs, with the same result
+ *                    up to the order of the atomic additions.
+ *   workspace_bytes  its size in bytes.
+ * Calls that use one workspace must not overlap in time (on one stream they
+ * never do); calls with different workspaces are independent. Everything
+ * else as linear_bias_act / linear_bias_act_nt; LL_ERR_INVALID_VALUE also for
+ * an unknown w_layout or a misaligned or overlapping workspace.
+ */
+#define LL_W_K_BY_N 0
+#define LL_W_N_BY_K 1
+int linear_bias_act_ws(int M, int N, int K,
+                       const float *X, int ldx, const float *W, int ldw, int w_layout,
+                       const float *bias, int act,
+                       float *Y, int ldy, void *workspace, int64_t workspace_bytes,
+                       void *stream);
+/* Bytes of workspace linear_bias_act_ws uses for this shape on a device with
+ * num_cus compute units (num_cus <= 0: 256), assuming 128-bit-aligned
+ * operands (other calls use less or none); 0 if its plan needs none; -1 for
+ * a negative size or an unknown w_layout or act. Honours the overrides of
+ * linear_layer_tuning.h. For 2047 x 11008 x 4096 on 256 CUs: 88 tiles of
+ * 256 KiB plus counters, about 22 MiB. */
+int64_t ll_linear_workspace_size(int M, int N, int K, int w_layout, int act, int num_cus);
+
+/*
  * Strided-batched products (page "GEMM 优化详解", section "矩阵大小选择策略":
  * small matrices are best run as one batched GEMM). For i in [0, batch):
  *

@@ -32,6 +32,7 @@ __all__ = [
     "LinearLayerError", "gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "status_string",
     "gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt", "linear_bias_act_nt",
     "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
+    "linear_bias_act_ws", "linear_workspace_size",
     "library_path", "load", "set_tile", "num_tiles", "tile_name", "chosen_tile",
     "set_split_k", "chosen_split_k", "set_stream_k", "chosen_stream_k",
     "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16", "PLAN_RELU", "PLAN_B_NK", "PLAN_UNALIGNED",
@@ -55,7 +56,8 @@ EXPORTED = ("gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "ll_st
             "gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt", "linear_bias_act_nt",
             "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
             "ll_num_tiles", "ll_tile_name", "ll_set_tile", "ll_chosen_tile",
-            "ll_set_split_k", "ll_chosen_split_k", "ll_set_stream_k", "ll_chosen_stream_k")
+            "ll_set_split_k", "ll_chosen_split_k", "ll_set_stream_k", "ll_chosen_stream_k",
+            "linear_bias_act_ws", "ll_linear_workspace_size")
 
 
 class LinearLayerError(RuntimeError):
@@ -81,6 +83,11 @@ def load():
     lib.gemm_f16f32.argtypes = lib.gemm_f32.argtypes
     lib.gemm_bf16f32.argtypes = lib.gemm_f32.argtypes
     lib.linear_bias_act.argtypes = [i32, i32, i32, vp, i32, vp, i32, vp, i32, vp, i32, vp]
+    lib.linear_bias_act_ws.argtypes = [i32, i32, i32, vp, i32, vp, i32, i32, vp, i32, vp, i32, vp,
+                                       ctypes.c_int64, vp]
+    lib.linear_bias_act_ws.restype = i32
+    lib.ll_linear_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.ll_linear_workspace_size.restype = ctypes.c_int64
     for nt in ("gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt"):
         getattr(lib, nt).argtypes = lib.gemm_f32.argtypes
     lib.linear_bias_act_nt.argtypes = lib.linear_bias_act.argtypes
@@ -337,7 +344,30 @@ def linear_bias_act(X, W, bias, act: int, Y, stream=None):
     return _linear("linear_bias_act", X, W, bias, act, Y, stream)
 
 
-def _linear(fn_name, X, W, bias, act, Y, stream, wt=False):
+def linear_workspace_size(M: int, N: int, K: int, w_trans: bool = False, act: int = ACT_RELU,
+                          num_cus: int = 0) -> int:
+    """Bytes of workspace linear_bias_act_ws uses for this shape (0: none)."""
+    n = load().ll_linear_workspace_size(int(M), int(N), int(K), int(bool(w_trans)), int(act),
+                                        int(num_cus))
+    if n < 0:
+        raise ValueError("invalid shape, layout or activation")
+    return n
+
+
+def linear_bias_act_ws(X, W, bias, act: int, Y, workspace, w_trans: bool = False, stream=None):
+    """Y = act(X*W + bias) (or X*W^T with w_trans) with a workspace tensor (zero-filled
+    before its first use; the call leaves it zero-filled), so the epilogue stays
+    fused into every tile of a stream-K plan. ``workspace`` may be None."""
+    torch = _torch()
+    pws, nws = None, 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        pws, nws = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return _linear("linear_bias_act_ws", X, W, bias, act, Y, stream, wt=w_trans, ws=(pws, nws))
+
+
+def _linear(fn_name, X, W, bias, act, Y, stream, wt=False, ws=None):
     torch = _torch()
     px, M, K, ldx = _mat(X, torch.float32, "X")
     if wt:
@@ -354,7 +384,11 @@ def _linear(fn_name, X, W, bias, act, Y, stream, wt=False):
         if N > 1 and bias.stride(0) != 1:
             raise ValueError("bias must be contiguous")
         pbias = bias.data_ptr()
-    st = getattr(load(), fn_name)(M, N, K, px, ldx, pw, ldw, pbias, int(act), py, ldy,
-                                  _stream(stream, X, W, Y, bias))
+    if ws is not None:
+        st = getattr(load(), fn_name)(M, N, K, px, ldx, pw, ldw, int(bool(wt)), pbias, int(act), py,
+                                      ldy, ws[0], ws[1], _stream(stream, X, W, Y, bias))
+    else:
+        st = getattr(load(), fn_name)(M, N, K, px, ldx, pw, ldw, pbias, int(act), py, ldy,
+                                      _stream(stream, X, W, Y, bias))
     _check(st, fn_name)
     return Y

@@ -317,6 +317,14 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
 
 int launch_status(hipError_t e) { return e == hipSuccess ? LL_OK : LL_ERR_LAUNCH; }
 
+// Stream-K workspace of a plan sharing out `rest` tiles of ti: one int counter
+// per shared tile (the block rounded up to 256 bytes), then one FP32 tile each.
+int64_t sk_counter_bytes(int64_t rest) { return (4 * rest + 255) / 256 * 256; }
+int64_t sk_workspace_bytes(int64_t rest, const TileInfo &ti)
+{
+    return rest > 0 ? sk_counter_bytes(rest) + rest * ti.bm * ti.bn * 4 : 0;
+}
+
 GemmParams make_params(int M, int N, int K, float alpha, const void *A, int lda, const void *B,
                        int ldb, float beta, float *C, int ldc)
 {
@@ -371,21 +379,28 @@ GemmParams with_tile_grid(GemmParams p, const TileInfo &ti)
 // sk_grid others share out the rest (they start as whole tiles finish), then
 // (ReLU) finish the shared-out tiles.
 hipError_t run_stream_k(GemmParams p, const Plan &pl, const TileInfo &ti, int epi, int pre_pass,
-                        bool relu_after, bool vec, hipStream_t s, launch_fn launch)
+                        bool relu_after, bool vec, hipStream_t s, launch_fn launch,
+                        void *ws = nullptr)
 {
     const GemmParams g = with_tile_grid(p, ti);
     const int64_t tiles_mn = (int64_t)g.tiles_m * g.tiles_n;
     const int rest = (int)(tiles_mn - pl.dp_tiles);
+    GemmParams q = p;
+    q.grid_x = pl.dp_tiles + pl.sk_grid;
+    q.sk_block = pl.dp_tiles;
+    q.sk_tiles = rest;
+    if (ws != nullptr) {
+        // one launch: the sharing workgroups add into the workspace tiles and
+        // the last contributor of each tile writes it, epilogue fused
+        q.ws_cnt = static_cast<int *>(ws);
+        q.ws = reinterpret_cast<float *>(static_cast<char *>(ws) + sk_counter_bytes(rest));
+        return launch(q, pl.tile, epi, vec, s);
+    }
     hipError_t e = hipSuccess;
     if (pre_pass >= 0)
         e = launch_tile_pass(g, ti.bm, ti.bn, pl.dp_tiles, rest, pre_pass, s);
-    if (e == hipSuccess) {
-        GemmParams q = p;
-        q.grid_x = pl.dp_tiles + pl.sk_grid;
-        q.sk_block = pl.dp_tiles;
-        q.sk_tiles = rest;
+    if (e == hipSuccess)
         e = launch(q, pl.tile, epi, vec, s);
-    }
     if (e == hipSuccess && relu_after)
         e = launch_tile_pass(g, ti.bm, ti.bn, pl.dp_tiles, rest, TILE_RELU, s);
     return e;
@@ -556,8 +571,19 @@ int gemm_bf16f32_batched(int trans_b, int M, int N, int K, float alpha, const ui
                    Batch{batch, stride_a, stride_b, stride_c});
 }
 
+// The workspace a fused-layer call would use (0: its plan needs none).
+static int64_t linear_ws_need(const Plan &pl, int M, int N)
+{
+    if (pl.tile < 0 || pl.sk_grid <= 0)
+        return 0;
+    const TileInfo &ti = kF32Tiles[pl.tile];
+    const int64_t rest = (int64_t)cdiv(M, ti.bm) * cdiv(N, ti.bn) - pl.dp_tiles;
+    return sk_workspace_bytes(rest, ti);
+}
+
 static int linear_impl(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
-                       const float *bias, int act, float *Y, int ldy, void *stream, bool wt)
+                       const float *bias, int act, float *Y, int ldy, void *stream, bool wt,
+                       void *ws = nullptr, int64_t ws_bytes = 0)
 {
     if (act != LL_ACT_NONE && act != LL_ACT_RELU)
         return LL_ERR_INVALID_VALUE;
@@ -584,9 +610,14 @@ static int linear_impl(int M, int N, int K, const float *X, int ldx, const float
     const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU, 1, vec);
     if (pl.tile < 0)
         return LL_ERR_INVALID_VALUE;
-    if (pl.sk_grid > 0)
+    if (pl.sk_grid > 0) {
+        // with a large enough workspace, one launch with the epilogue fused
+        // into every tile; without, the bias pass, the launch and a ReLU pass
+        const int64_t need = linear_ws_need(pl, M, N);
+        void *use = ws != nullptr && ws_bytes >= need ? ws : nullptr;
         return launch_status(run_stream_k(p, pl, kF32Tiles[pl.tile], EPI_LINEAR, TILE_BIAS,
-                                          act == LL_ACT_RELU, vec, s, launch));
+                                          act == LL_ACT_RELU, vec, s, launch, use));
+    }
     if (pl.splits == 1)
         return launch_status(launch(p, pl.tile, EPI_LINEAR, vec, s));
     // split-K: Y = bias, then every split adds its partial product, then ReLU
@@ -610,6 +641,39 @@ int linear_bias_act_nt(int M, int N, int K, const float *X, int ldx, const float
                        const float *bias, int act, float *Y, int ldy, void *stream)
 {
     return linear_impl(M, N, K, X, ldx, W, ldw, bias, act, Y, ldy, stream, true);
+}
+
+int linear_bias_act_ws(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
+                       int w_layout, const float *bias, int act, float *Y, int ldy, void *workspace,
+                       int64_t workspace_bytes, void *stream)
+{
+    if ((w_layout != LL_W_K_BY_N && w_layout != LL_W_N_BY_K) || workspace_bytes < 0 ||
+        (workspace == nullptr && workspace_bytes != 0) || !aligned(workspace, 256))
+        return LL_ERR_INVALID_VALUE;
+    const bool wt = w_layout == LL_W_N_BY_K;
+    if (workspace != nullptr && workspace_bytes > 0 && M > 0 && N > 0) {
+        // the workspace may not overlap the operands or the output
+        const int64_t xb = span_bytes(M, K, ldx, 4);
+        const int64_t wb = wt ? span_bytes(N, K, ldw, 4) : span_bytes(K, N, ldw, 4);
+        if (overlap(workspace, workspace_bytes, X, xb) || overlap(workspace, workspace_bytes, W, wb) ||
+            overlap(workspace, workspace_bytes, Y, span_bytes(M, N, ldy, 4)) ||
+            (bias != nullptr && overlap(workspace, workspace_bytes, bias, (int64_t)N * 4)))
+            return LL_ERR_INVALID_VALUE;
+    }
+    return linear_impl(M, N, K, X, ldx, W, ldw, bias, act, Y, ldy, stream, wt, workspace,
+                       workspace_bytes);
+}
+
+int64_t ll_linear_workspace_size(int M, int N, int K, int w_layout, int act, int num_cus)
+{
+    if ((w_layout != LL_W_K_BY_N && w_layout != LL_W_N_BY_K) || M < 0 || N < 0 || K < 0 ||
+        (act != LL_ACT_NONE && act != LL_ACT_RELU))
+        return -1;
+    if (M == 0 || N == 0 || K == 0)
+        return 0;
+    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, num_cus > 0 ? num_cus : 256,
+                         act == LL_ACT_RELU, 1, true);
+    return linear_ws_need(pl, M, N);
 }
 
 const char *ll_status_string(int status)

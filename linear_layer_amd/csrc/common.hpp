@@ -41,6 +41,12 @@ struct GemmParams {
     int grid_x;           // workgroups along x; 0: one per tile of the whole grid
     int sk_tiles;         // stream-K: the number of tiles shared out; 0: none
     int sk_block;         // stream-K: workgroups below this run whole tiles, the rest share
+    // stream-K with a workspace (nullptr: none): a zero-filled FP32 tile per
+    // shared tile, into which the sharing workgroups add their partial sums,
+    // and an arrival counter per shared tile; the last contributor applies
+    // the epilogue and clears both
+    float *ws;
+    int *ws_cnt;
 };
 
 // Bounds a direct kernel's copies check (a template mask; see the launchers).
@@ -124,7 +130,7 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int &tm, int &t
 // two segments. Segment `seg` of this workgroup: returns false if there is
 // none, else its tile and k-range [kb, kb + k_len).
 __device__ __forceinline__ bool sk_segment(const GemmParams &p, int seg, int &tm, int &tn, int &kb,
-                                           int &k_len)
+                                           int &k_len, int *shared_tile = nullptr)
 {
     const int units = cdiv(p.K, kSkUnit);
     const int64_t total = (int64_t)p.sk_tiles * units;
@@ -141,7 +147,22 @@ __device__ __forceinline__ bool sk_segment(const GemmParams &p, int seg, int &tm
     tile_of(p, p.tile_base + p.sk_block + t, tm, tn);
     kb = lo * kSkUnit;
     k_len = min(p.K, hi * kSkUnit) - kb;
+    if (shared_tile != nullptr)
+        *shared_tile = t;
     return true;
+}
+
+// The number of sharing workgroups whose runs meet shared tile t. Workgroup w
+// covers units [total*w/nw, total*(w+1)/nw), every run at least one unit
+// long (the planner shares out at least as many units as it has sharing
+// workgroups), so the workgroup holding unit u is floor(((u+1)*nw - 1)/total).
+__device__ __forceinline__ int sk_contributors(const GemmParams &p, int t)
+{
+    const int64_t units = cdiv(p.K, kSkUnit);
+    const int64_t total = (int64_t)p.sk_tiles * units;
+    const int64_t nw = (int64_t)gridDim.x - p.sk_block;
+    auto owner = [&](int64_t u) { return ((u + 1) * nw - 1) / total; };
+    return (int)(owner((int64_t)(t + 1) * units - 1) - owner((int64_t)t * units) + 1);
 }
 
 // XOR swizzle of 16-byte chunks inside an LDS row of ROW_BYTES bytes. The

@@ -314,10 +314,11 @@ gemm_f32_kernel(GemmParams p)
 // copy needs no select: interior launches save about a quarter of the
 // per-stage VALU work.
 template <int EPI, int BM, int BN, int BK, int NBUF, int WPE, int WGM, int WGN, int KS, bool BT,
-          bool SK, int CHK>
+          bool SK, int CHK, bool WS = false>
 __global__ void __launch_bounds__(64 * WGM * WGN * KS) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f32_direct_kernel(GemmParams p)
 {
+    static_assert(!WS || SK, "the workspace serves stream-K launches");
     constexpr int NW = WGM * WGN;                             // waves per slice
     constexpr int HALVES = BK / 16, STEPS = BK / 2;           // half-stages, MFMA k-steps
     constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
@@ -352,10 +353,11 @@ gemm_f32_direct_kernel(GemmParams p)
     // sk_block on) up to two (tile, k-range) segments, each a complete pass of
     // the pipeline below whose partial sums are added atomically.
     const bool sharing = SK && (int)blockIdx.x >= p.sk_block;
+    __shared__ int sk_last;   // stream-K with a workspace: this workgroup finishes the tile
     for (int seg = 0;; ++seg) {
-    int tm, tn, K, kb;
+    int tm, tn, K, kb, st = 0;
     if (sharing) {
-        if (!sk_segment(p, seg, tm, tn, kb, K))
+        if (!sk_segment(p, seg, tm, tn, kb, K, &st))
             break;
         if (seg > 0)
             __syncthreads();   // every wave is done with the previous segment's LDS
@@ -695,7 +697,62 @@ gemm_f32_direct_kernel(GemmParams p)
                             part[((((sl - 1) * NW + wave) * SLOTS) + (fm * FN + fn) * 16 + r) * 64 + lane];
     }
 
-    if (sharing || EPI == EPI_ATOMIC || EPI == EPI_GEMM_BETA0) {
+    // Stream-K with a workspace (WS): add this segment's partial sums into
+    // the shared tile's workspace tile, then count the arrival. The last of
+    // the tile's contributors applies the epilogue to the sums, writes the
+    // tile and clears the workspace tile and counter for the next call.
+    // Nobody waits for anybody: each contributor only adds and counts, and the
+    // count tells the last one that all sums are in. The workspace tile is
+    // kept in accumulator order (wave, block, register, lane): a lane's adds
+    // are one base address plus constants, 256 bytes per wave instruction,
+    // and four consecutive floats are four consecutive columns of one row.
+    if (WS && sharing) {
+        constexpr int NB = FM * FN;            // accumulator blocks per wave
+        constexpr int NT = 64 * NW * KS;
+        float *wt = p.ws + (int64_t)st * (BM * BN);
+        float *mine = wt + wave * (NB * 16 * 64) + lane;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    __hip_atomic_fetch_add(mine + ((fm * FN + fn) * 16 + r) * 64, acc[fm][fn][r],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // The barrier orders every wave's adds before thread 0's count (and
+        // waits for them); the count's release and acquire, one per
+        // workgroup, make them visible device-wide and the other
+        // contributors' adds visible here.
+        __syncthreads();
+        if (tid == 0) {
+            const int before = __hip_atomic_fetch_add(p.ws_cnt + st, 1, __ATOMIC_ACQ_REL,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+            sk_last = before == sk_contributors(p, st) - 1;
+        }
+        __syncthreads();
+        if (sk_last) {
+            // eight groups in flight per lane: the loop is latency-bound
+#pragma unroll 8
+            for (int q = tid; q < BM * BN / 4; q += NT) {
+                const int e = 4 * q, l = e & 63, r = (e >> 6) & 15, blk = (e >> 10) % NB;
+                const int w = (e >> 10) / NB;
+                const int row = (w / WGN) * WTM + (blk / FN) * 32 + ((r >> 2) << 3) + ((l >> 5) << 2) +
+                                (r & 3);
+                const int col = (w % WGN) * WTN + (blk % FN) * 32 + (l & 31);
+                f32x4 *src = reinterpret_cast<f32x4 *>(wt + e);
+                const f32x4 v = *src;
+                *src = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                const f32x4 cv = EPI == EPI_GEMM_BETA ? load_c4(p, m0 + row, n0 + col) : v;
+                finish4<EPI>(p, v, m0 + row, n0 + col, cv);
+            }
+            if (tid == 0)
+                __hip_atomic_store(p.ws_cnt + st, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    if (WS && sharing) {
+        // the workspace path above wrote (or left to a later contributor) the tile
+    } else if (sharing || EPI == EPI_ATOMIC || EPI == EPI_GEMM_BETA0) {
         // atomic partial sums, or alpha*acc: 32-bit stores, one column per lane
         // (alpha*acc measured no faster with 128-bit stores: 4096^3 +0.4 %,
         // 256^3 +5 % in time)
@@ -790,6 +847,10 @@ static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hi
 #define LL_F32_DIRECT_C(E, SK, C) \
     hipLaunchKernelGGL((gemm_f32_direct_kernel<E, BM, BN, BK, NBUF, WPE, WGM, WGN, KS, BT, SK, C>), \
                        grid, block, 0, s, p)
+#define LL_F32_DIRECT_WS(C) \
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<EPI_LINEAR, BM, BN, BK, NBUF, WPE, WGM, WGN, KS, BT, \
+                                               true, C, true>), \
+                       grid, block, 0, s, p)
 #define LL_F32_DIRECT(E, SK) \
     do { \
         if (chk == 0) \
@@ -806,6 +867,14 @@ static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hi
         else if (epi == EPI_GEMM_BETA) LL_F32_DIRECT(EPI_GEMM_BETA, false);
         else if (epi == EPI_LINEAR) LL_F32_DIRECT(EPI_LINEAR, false);
         else LL_F32_DIRECT(EPI_ATOMIC, false);
+    } else if (p.sk_tiles > 0 && p.ws != nullptr) {
+        // the fused layer's stream-K with a workspace: every tile finished in
+        // this launch, epilogue fused
+        if (epi != EPI_LINEAR)
+            return hipErrorInvalidValue;
+        if (chk == 0) LL_F32_DIRECT_WS(0);
+        else if (chk == CHK_M) LL_F32_DIRECT_WS(CHK_M);
+        else LL_F32_DIRECT_WS(CHK_M | CHK_N | CHK_K);
     } else if (p.sk_tiles > 0) {
         // whole tiles with `epi`, shared ones added atomically
         if (epi == EPI_GEMM_BETA0) LL_F32_DIRECT(EPI_GEMM_BETA0, true);
@@ -820,6 +889,7 @@ static hipError_t launch_direct(const GemmParams &p, int64_t ntiles, int epi, hi
     }
 #undef LL_F32_DIRECT
 #undef LL_F32_DIRECT_C
+#undef LL_F32_DIRECT_WS
     return hipGetLastError();
 }
 

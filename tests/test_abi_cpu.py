@@ -352,3 +352,31 @@ def test_extreme_sizes_stay_in_range():
                 s = ll.chosen_split_k(dt | flags, M, N, K, 256)
                 sk = ll.chosen_stream_k(dt | flags, M, N, K, 256)
                 assert t == -1 or (0 <= t < ll.num_tiles(dt) and 1 <= s <= 16 and sk >= 0)
+
+
+def test_linear_workspace_query():
+    """Workspace of the fused layer's stream-K plan: 88 shared 256x256 tiles at
+    2047 x 11008 x 4096 (one int counter each, rounded up to 256 bytes, then one
+    FP32 tile each); none for plans without stream-K; -1 for bad arguments."""
+    need = ll.linear_workspace_size(2047, 11008, 4096, False, 1, 256)
+    assert need == 512 + 88 * 256 * 256 * 4
+    assert ll.linear_workspace_size(2047, 11008, 4096, True, 1, 256) == need
+    assert ll.linear_workspace_size(4096, 4096, 4096, False, 1, 256) == 0
+    assert ll.linear_workspace_size(0, 11008, 4096) == 0
+    lib = ll.load()
+    assert lib.ll_linear_workspace_size(-1, 8, 8, 0, 1, 256) == -1
+    assert lib.ll_linear_workspace_size(8, 8, 8, 2, 1, 256) == -1
+    assert lib.ll_linear_workspace_size(8, 8, 8, 0, 5, 256) == -1
+
+
+def test_linear_ws_argument_checks():
+    lib = ll.load()
+    E = ll.ERR_INVALID_VALUE
+    args = (8, 8, 8, PA, 8, PB, 8)
+    assert lib.linear_bias_act_ws(*args, 2, None, 1, PC, 8, 0x40000000, 4096, None) == E   # layout
+    assert lib.linear_bias_act_ws(*args, 0, None, 1, PC, 8, 0x40000010, 4096, None) == E   # alignment
+    assert lib.linear_bias_act_ws(*args, 0, None, 1, PC, 8, None, 64, None) == E           # NULL, bytes
+    assert lib.linear_bias_act_ws(*args, 0, None, 1, PC, 8, PC, 4096, None) == E           # overlaps Y
+    assert lib.linear_bias_act_ws(*args, 0, None, 1, PC, 8, PA, 4096, None) == E           # overlaps X
+    st = lib.linear_bias_act_ws(*args, 0, None, 1, PC, 8, 0x40000000, 4096, None)
+    assert st in (ll.ERR_NO_DEVICE, ll.ERR_UNSUPPORTED_ARCH, ll.OK)

@@ -72,10 +72,12 @@ def test_default_run_reports_every_configuration():
     assert d["config"]["workload"] == "gemm_f32_4096" and d["roofline"]["peak"] == 157.3
     cf = d["configs"]
     assert set(cf) == {"gemm_f32_256", "gemm_f32_1024_ab", "linear_relu_2047x4096x11008",
-                       "gemm_f16f32_8192"}
+                       "gemm_f16f32_8192", "linear_relu_2047x4096x11008_workspace"}
     for name, c in cf.items():
         assert c["ms_per_step"] > 0 and c["tflops"] > 0, name
         assert 0 < c["frac_of_peak"] <= 1 and 0 < c["kernel_frac_of_peak"] <= 1, name
         assert abs(c["tflops"] / c["peak_tflops"] - c["frac_of_peak"]) < 1e-3, name
-        assert c["cpu_baseline"]["kind"] == "oracle" and c["cpu_baseline"]["cores"] >= 1, name
+        if not name.endswith("_workspace"):
+            assert c["cpu_baseline"]["kind"] == "oracle" and c["cpu_baseline"]["cores"] >= 1, name
+    assert cf["linear_relu_2047x4096x11008_workspace"]["workspace_bytes"] > 0
     assert cf["gemm_f16f32_8192"]["peak_tflops"] == 2516.6
