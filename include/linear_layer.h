@@ -201,6 +201,26 @@ int linear_bias_act_ws(int M, int N, int K,
 int64_t ll_linear_workspace_size(int M, int N, int K, int w_layout, int act, int num_cus);
 
 /*
+ * linear_bias_act_noalloc — linear_bias_act_ws for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the workspace is the library's own
+ * static device array of LL_NOALLOC_SCRATCH_BYTES (one per GPU, held until
+ * the process ends), so the call allocates nothing and takes no workspace
+ * argument. A shape whose plan needs more workspace than that (see
+ * ll_linear_workspace_size) returns LL_ERR_INVALID_VALUE and runs nothing.
+ * Every call on one GPU uses that GPU's single array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and give wrong
+ * results; calls on one stream never overlap. Each call leaves the array
+ * zero-filled, as the next one needs it. Arguments and results otherwise as
+ * linear_bias_act_ws.
+ */
+#define LL_NOALLOC_SCRATCH_BYTES (32ll << 20)
+int linear_bias_act_noalloc(int M, int N, int K,
+                            const float *X, int ldx, const float *W, int ldw, int w_layout,
+                            const float *bias, int act,
+                            float *Y, int ldy, void *stream);
+
+/*
  * Strided-batched products (page "GEMM 优化详解", section "矩阵大小选择策略":
  * small matrices are best run as one batched GEMM). For i in [0, batch):
  *

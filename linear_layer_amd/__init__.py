@@ -32,7 +32,7 @@ __all__ = [
     "LinearLayerError", "gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "status_string",
     "gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt", "linear_bias_act_nt",
     "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
-    "linear_bias_act_ws", "linear_workspace_size",
+    "linear_bias_act_ws", "linear_workspace_size", "linear_bias_act_noalloc", "NOALLOC_SCRATCH_BYTES",
     "library_path", "load", "set_tile", "num_tiles", "tile_name", "chosen_tile",
     "set_split_k", "chosen_split_k", "set_stream_k", "chosen_stream_k",
     "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16", "PLAN_RELU", "PLAN_B_NK", "PLAN_UNALIGNED",
@@ -43,6 +43,7 @@ OK, ERR_INVALID_VALUE, ERR_NO_DEVICE, ERR_UNSUPPORTED_ARCH, ERR_LAUNCH = 0, 1, 2
 ACT_NONE, ACT_RELU = 0, 1
 DTYPE_F32, DTYPE_F16 = 0, 1
 PLAN_RELU, PLAN_B_NK, PLAN_UNALIGNED = 0x100, 0x200, 0x400   # flags OR-ed into dtype for chosen_*
+NOALLOC_SCRATCH_BYTES = 32 << 20   # the static workspace of linear_bias_act_noalloc
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # The in-package library, or another build of it named by LINEAR_LAYER_LIBRARY
@@ -57,7 +58,7 @@ EXPORTED = ("gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "ll_st
             "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
             "ll_num_tiles", "ll_tile_name", "ll_set_tile", "ll_chosen_tile",
             "ll_set_split_k", "ll_chosen_split_k", "ll_set_stream_k", "ll_chosen_stream_k",
-            "linear_bias_act_ws", "ll_linear_workspace_size")
+            "linear_bias_act_ws", "ll_linear_workspace_size", "linear_bias_act_noalloc")
 
 
 class LinearLayerError(RuntimeError):
@@ -86,6 +87,8 @@ def load():
     lib.linear_bias_act_ws.argtypes = [i32, i32, i32, vp, i32, vp, i32, i32, vp, i32, vp, i32, vp,
                                        ctypes.c_int64, vp]
     lib.linear_bias_act_ws.restype = i32
+    lib.linear_bias_act_noalloc.argtypes = [i32, i32, i32, vp, i32, vp, i32, i32, vp, i32, vp, i32, vp]
+    lib.linear_bias_act_noalloc.restype = i32
     lib.ll_linear_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.ll_linear_workspace_size.restype = ctypes.c_int64
     for nt in ("gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt"):
@@ -367,6 +370,12 @@ def linear_bias_act_ws(X, W, bias, act: int, Y, workspace, w_trans: bool = False
     return _linear("linear_bias_act_ws", X, W, bias, act, Y, stream, wt=w_trans, ws=(pws, nws))
 
 
+def linear_bias_act_noalloc(X, W, bias, act: int, Y, w_trans: bool = False, stream=None):
+    """linear_bias_act_ws on the library's own static workspace (nothing is
+    allocated); calls that overlap in time on one GPU race."""
+    return _linear("linear_bias_act_noalloc", X, W, bias, act, Y, stream, wt=w_trans, ws="static")
+
+
 def _linear(fn_name, X, W, bias, act, Y, stream, wt=False, ws=None):
     torch = _torch()
     px, M, K, ldx = _mat(X, torch.float32, "X")
@@ -384,7 +393,10 @@ def _linear(fn_name, X, W, bias, act, Y, stream, wt=False, ws=None):
         if N > 1 and bias.stride(0) != 1:
             raise ValueError("bias must be contiguous")
         pbias = bias.data_ptr()
-    if ws is not None:
+    if ws == "static":
+        st = getattr(load(), fn_name)(M, N, K, px, ldx, pw, ldw, int(bool(wt)), pbias, int(act), py,
+                                      ldy, _stream(stream, X, W, Y, bias))
+    elif ws is not None:
         st = getattr(load(), fn_name)(M, N, K, px, ldx, pw, ldw, int(bool(wt)), pbias, int(act), py,
                                       ldy, ws[0], ws[1], _stream(stream, X, W, Y, bias))
     else:

@@ -581,9 +581,11 @@ static int64_t linear_ws_need(const Plan &pl, int M, int N)
     return sk_workspace_bytes(rest, ti);
 }
 
+// ws_strict: a plan needing more workspace than ws_bytes is an error (the
+// no-allocation entry point), not a reason to run the plan without one.
 static int linear_impl(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
                        const float *bias, int act, float *Y, int ldy, void *stream, bool wt,
-                       void *ws = nullptr, int64_t ws_bytes = 0)
+                       void *ws = nullptr, int64_t ws_bytes = 0, bool ws_strict = false)
 {
     if (act != LL_ACT_NONE && act != LL_ACT_RELU)
         return LL_ERR_INVALID_VALUE;
@@ -614,6 +616,8 @@ static int linear_impl(int M, int N, int K, const float *X, int ldx, const float
         // with a large enough workspace, one launch with the epilogue fused
         // into every tile; without, the bias pass, the launch and a ReLU pass
         const int64_t need = linear_ws_need(pl, M, N);
+        if (ws_strict && need > ws_bytes)
+            return LL_ERR_INVALID_VALUE;
         void *use = ws != nullptr && ws_bytes >= need ? ws : nullptr;
         return launch_status(run_stream_k(p, pl, kF32Tiles[pl.tile], EPI_LINEAR, TILE_BIAS,
                                           act == LL_ACT_RELU, vec, s, launch, use));
@@ -662,6 +666,55 @@ int linear_bias_act_ws(int M, int N, int K, const float *X, int ldx, const float
     }
     return linear_impl(M, N, K, X, ldx, W, ldw, bias, act, Y, ldy, stream, wt, workspace,
                        workspace_bytes);
+}
+
+// ---- the no-allocation entry point ----
+//
+// linear_bias_act_noalloc runs linear_bias_act_ws on a workspace the library
+// owns: `scratch`, a static device array (one copy per GPU, held until the
+// process ends), zero-filled when the code object loads and left zero-filled
+// by every call. Host code reaches it only through the device address
+// hipGetSymbolAddress returns for the current device, looked up once per
+// device; the array's own name is a host-side stand-in, never an address.
+static __device__ __align__(256) unsigned char scratch[LL_NOALLOC_SCRATCH_BYTES];
+
+static std::once_flag g_scratch_once[kMaxDevices];
+static void *g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, or nullptr.
+static void *scratch_address()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            ptr = nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
+int linear_bias_act_noalloc(int M, int N, int K, const float *X, int ldx, const float *W, int ldw,
+                            int w_layout, const float *bias, int act, float *Y, int ldy,
+                            void *stream)
+{
+    if (w_layout != LL_W_K_BY_N && w_layout != LL_W_N_BY_K)
+        return LL_ERR_INVALID_VALUE;
+    DevInfo dev;
+    int st = current_device(&dev);
+    if (st != LL_OK)
+        return st;
+    void *ws = scratch_address();
+    if (ws == nullptr)
+        return LL_ERR_LAUNCH;
+    return linear_impl(M, N, K, X, ldx, W, ldw, bias, act, Y, ldy, stream, w_layout == LL_W_N_BY_K,
+                       ws, LL_NOALLOC_SCRATCH_BYTES, true);
 }
 
 int64_t ll_linear_workspace_size(int M, int N, int K, int w_layout, int act, int num_cus)

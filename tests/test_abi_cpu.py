@@ -21,6 +21,7 @@ def header_functions():
     names = set()
     for h in HEADERS:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        text = re.sub(r"^\s*#.*$", "", text, flags=re.M)   # preprocessor lines
         names |= set(re.findall(r"\b([A-Za-z_]\w*)\s*\([^;{]*\)\s*;", text))
     return names
 
@@ -379,4 +380,12 @@ def test_linear_ws_argument_checks():
     assert lib.linear_bias_act_ws(*args, 0, None, 1, PC, 8, PC, 4096, None) == E           # overlaps Y
     assert lib.linear_bias_act_ws(*args, 0, None, 1, PC, 8, PA, 4096, None) == E           # overlaps X
     st = lib.linear_bias_act_ws(*args, 0, None, 1, PC, 8, 0x40000000, 4096, None)
+    assert st in (ll.ERR_NO_DEVICE, ll.ERR_UNSUPPORTED_ARCH, ll.OK)
+
+
+def test_linear_noalloc_argument_checks():
+    lib = ll.load()
+    args = (8, 8, 8, PA, 8, PB, 8)
+    assert lib.linear_bias_act_noalloc(*args, 2, None, 1, PC, 8, None) == ll.ERR_INVALID_VALUE
+    st = lib.linear_bias_act_noalloc(*args, 0, None, 1, PC, 8, None)
     assert st in (ll.ERR_NO_DEVICE, ll.ERR_UNSUPPORTED_ARCH, ll.OK)

@@ -1,0 +1,163 @@
+"""The no-allocation fused layer (linear_bias_act_noalloc), called through the
+C ABI: its output against linear_bias_act_ws on the same inputs and against
+the float64 oracle, on two calls in a row (the second smaller) that share the
+library's static workspace; shapes whose plan needs more workspace than the
+static array are refused and leave Y untouched."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import linear_layer_amd as ll
+import oracle
+from linear_layer_amd import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+F32 = ll.DTYPE_F32
+
+
+@pytest.fixture(autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+@pytest.fixture
+def auto_plan():
+    """Every test here starts and ends with the automatic plan."""
+    ll.set_tile(F32, -1)
+    ll.set_stream_k(-1)
+    ll.set_split_k(-1)
+    yield
+    ll.set_tile(F32, -1)
+    ll.set_stream_k(-1)
+
+
+def cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def np32(t):
+    return t.detach().cpu().numpy()
+
+
+def bound(R, T):
+    return 1e-4 * T + np.spacing(np.abs(R).astype(np.float32)).astype(np.float64) / 2
+
+
+def call(lib_fn, X, W, b, act, Y, w_trans, *ws):
+    """One call of a fused-layer entry point through the C ABI on torch's
+    current stream; returns the status."""
+    s = torch.cuda.current_stream().cuda_stream
+    ldw = W.stride(0)
+    return lib_fn(X.shape[0], Y.shape[1], X.shape[1], X.data_ptr(), X.stride(0), W.data_ptr(), ldw,
+                  int(w_trans), None if b is None else b.data_ptr(), act, Y.data_ptr(), Y.stride(0),
+                  *ws, s)
+
+
+def both(X, W, b, act, w_trans):
+    """(Y from linear_bias_act_noalloc, Y from linear_bias_act_ws) on device
+    copies of the host inputs (W given K-by-N, handed over N-by-K when
+    w_trans), each Y NaN-filled first."""
+    lib = ll.load()
+    M, K = X.shape
+    N = W.shape[1]
+    Xd, Wd = X.to(DEV), (W.t().contiguous() if w_trans else W).to(DEV)
+    bd = None if b is None else b.to(DEV)
+    need = ll.linear_workspace_size(M, N, K, w_trans, act, cus())
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=DEV)
+    Yn = torch.full((M, N), float("nan"), device=DEV)
+    Yw = torch.full((M, N), float("nan"), device=DEV)
+    assert call(lib.linear_bias_act_noalloc, Xd, Wd, bd, act, Yn, w_trans) == ll.OK
+    assert call(lib.linear_bias_act_ws, Xd, Wd, bd, act, Yw, w_trans, ws.data_ptr(),
+                ctypes.c_int64(ws.numel())) == ll.OK
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(ws)) == 0
+    return np32(Yn), np32(Yw), need
+
+
+def check(case, X, W, b, act, w_trans, integer):
+    got, ref, need = both(X, W, b, act, w_trans)
+    R, T = oracle.linear(np32(X), np32(W), None if b is None else np32(b), act)
+    if integer:
+        assert np.array_equal(got, ref), f"{case}: noalloc and ws differ"
+        assert np.array_equal(got, R.astype(np.float32)), f"{case}: noalloc differs from the oracle"
+    else:
+        B = bound(R, T)
+        bad = ~(np.abs(got.astype(np.float64) - R) <= B)
+        assert not bad.any(), f"{case}: {bad.sum()} of {bad.size} outside the oracle bound"
+        bad = ~(np.abs(got.astype(np.float64) - ref.astype(np.float64)) <= 2 * B)
+        assert not bad.any(), f"{case}: {bad.sum()} of {bad.size} away from linear_bias_act_ws"
+    if act:
+        assert not np.any(np.signbit(got))
+    return need
+
+
+@pytest.mark.parametrize("integer", [True, False])
+@pytest.mark.parametrize("w_trans", [False, True])
+def test_two_calls_second_smaller(integer, w_trans, auto_plan):
+    """The fused-layer workload 2047x4096x11008 (a stream-K hybrid using the
+    static workspace), then a smaller stream-K layer on the same workspace:
+    the second call reads only counters and partials the first left zeroed."""
+    w = wl.WORKLOADS["linear_relu_2047x4096x11008"]
+    x = wl.make_inputs(w, integer=integer)
+    need1 = check("first call", x["A"], x["B"], x["bias"], 1, w_trans, integer)
+    assert 0 < need1 <= ll.NOALLOC_SCRATCH_BYTES
+    M, N, K = 1536, 1536, 256
+    ll.set_tile(F32, 3)
+    ll.set_stream_k(1)
+    flags = F32 | ll.PLAN_RELU | (ll.PLAN_B_NK if w_trans else 0)
+    assert ll.chosen_stream_k(flags, M, N, K, cus()) > 0
+    if integer:
+        X, W, b = (wl.integers((M, K), 301, -2, 2), wl.integers((K, N), 302, -2, 2),
+                   wl.integers((N,), 303, -4, 4))
+    else:
+        X, W, b = wl.uniform((M, K), 301, 0.125), wl.uniform((K, N), 302, 0.125), wl.bias_uniform(N, 303)
+    need2 = check("second call", X, W, b, 1, w_trans, integer)
+    assert 0 < need2 < need1
+
+
+@pytest.mark.parametrize("shape,act,with_bias", [((330, 270, 520), 0, False),
+                                                 ((257, 300, 200), 1, True),
+                                                 ((4096, 4096, 512), 1, True)])
+def test_small_and_whole_tile_plans(shape, act, with_bias, auto_plan):
+    """Plans with and without shared tiles, with and without bias and ReLU."""
+    M, N, K = shape
+    X, W = wl.uniform((M, K), 311, 0.125), wl.uniform((K, N), 312, 0.125)
+    b = wl.bias_uniform(N, 313) if with_bias else None
+    check(f"{M}x{N}x{K}", X, W, b, act, False, False)
+
+
+def test_too_large_is_refused(auto_plan):
+    """A shape whose plan needs more than the static workspace is refused with
+    LL_ERR_INVALID_VALUE before anything runs: Y keeps its NaNs."""
+    M, N, K = 3000, 5000, 11008
+    need = ll.linear_workspace_size(M, N, K, False, 1, cus())
+    assert need > ll.NOALLOC_SCRATCH_BYTES
+    lib = ll.load()
+    X = torch.zeros((M, K), device=DEV)
+    W = torch.zeros((K, N), device=DEV)
+    Y = torch.full((M, N), float("nan"), device=DEV)
+    assert call(lib.linear_bias_act_noalloc, X, W, None, 1, Y, False) == ll.ERR_INVALID_VALUE
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(Y).all())
+    with pytest.raises(ll.LinearLayerError):
+        ll.linear_bias_act_noalloc(X, W, None, 1, Y)
+
+
+def test_argument_errors(auto_plan):
+    lib = ll.load()
+    X = torch.zeros((8, 8), device=DEV)
+    W = torch.zeros((8, 8), device=DEV)
+    Y = torch.zeros((8, 8), device=DEV)
+    s = torch.cuda.current_stream().cuda_stream
+    args = (8, 8, 8, X.data_ptr(), 8, W.data_ptr(), 8)
+    E = ll.ERR_INVALID_VALUE
+    assert lib.linear_bias_act_noalloc(*args, 2, None, 1, Y.data_ptr(), 8, s) == E
+    assert lib.linear_bias_act_noalloc(*args, 0, None, 5, Y.data_ptr(), 8, s) == E
+    assert lib.linear_bias_act_noalloc(*args, 0, None, 1, Y.data_ptr(), 4, s) == E
+    assert lib.linear_bias_act_noalloc(*args, 0, None, 1, Y.data_ptr(), 8, s) == ll.OK
+    torch.cuda.synchronize()
