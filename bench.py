@@ -67,6 +67,9 @@ def parse():
                          "FP16 8192^3) that the default run measures after the headline one")
     ap.add_argument("--config-cpu-seconds", type=float, default=4.0,
                     help="target CPU time of each other configuration's oracle sample")
+    ap.add_argument("--workspace", action="store_true",
+                    help="fused-layer workloads: run linear_bias_act_ws with a workspace "
+                         "(stream-K in one launch) instead of linear_bias_act")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="instead of the GEMM, run a plain device-to-device copy of 256 MiB "
                          "--steps times (the reference kernel for scaling HBM byte counters)")
@@ -340,6 +343,9 @@ def main():
         sys.exit(1)
     ll.load()  # fails loudly if the HIP library is missing
     w = wl.WORKLOADS[args.workload]
+    if args.workspace and w.kind not in ("linear", "linear_nt"):
+        print("--workspace applies to the fused-layer workloads only", file=sys.stderr)
+        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dtype_id = ll.DTYPE_F16 if w.kind in wl.HALF_KINDS else ll.DTYPE_F32
@@ -351,14 +357,14 @@ def main():
         ll.set_stream_k(args.stream_k)
     props = torch.cuda.get_device_properties(dev)
     # the headline's inputs, made and uploaded before any timing
-    x, step, plan = prepare(w, args, dev)
+    x, step, plan = prepare(w, args, dev, workspace=args.workspace)
 
     # The other configurations (default run only, with the automatic plan)
     # are timed first and the headline right after them, and every oracle
     # sample runs after all GPU timing: while the host works the GPU idles
     # and its clock drops.
     configs, config_inputs = None, {}
-    if (args.workload == "gemm_f32_4096" and not args.no_configs and args.tile < 0
+    if (args.workload == "gemm_f32_4096" and not args.no_configs and args.tile < 0 and not args.workspace
             and args.split_k < 1 and args.stream_k == -1):
         configs = {}
         for name in OTHER_CONFIGS + [WS_CONFIG + "_workspace"]:
@@ -394,7 +400,8 @@ def main():
              "gemm_bf16f32": "bf16 in, f32 accumulate"}[w.kind]
     out = {
         "metric": "TFLOPS (2MNK/t) for 4096^3 FP32 GEMM on 1 MI355X; % of matrix peak"
-        if w.name == "gemm_f32_4096" else f"TFLOPS (2MNK/t), {w.name}",
+        if w.name == "gemm_f32_4096" else f"TFLOPS (2MNK/t), {w.name}"
+        + (" through linear_bias_act_ws" if args.workspace else ""),
         "value": round(value, 3),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -422,7 +429,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(w.name, w.kind),
+            "traffic": measured_traffic(w.name + ("_workspace" if args.workspace else ""), w.kind),
             "kernel_avg_ms": round(avg_launch_ms, 5),
             "kernel_min_ms": round(min(launch_ms), 5),
             "kernel_median_ms": round(sorted(launch_ms)[len(launch_ms) // 2], 5),
