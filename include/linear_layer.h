@@ -211,7 +211,9 @@ int64_t ll_linear_workspace_size(int M, int N, int K, int w_layout, int act, int
  * Every call on one GPU uses that GPU's single array: calls that overlap in
  * time on one GPU (other streams, other threads) race and give wrong
  * results; calls on one stream never overlap. Each call leaves the array
- * zero-filled, as the next one needs it. Arguments and results otherwise as
+ * zero-filled, as the next one needs it. The array used is the current
+ * device's, so `stream` must belong to the current device (else
+ * LL_ERR_INVALID_VALUE). Arguments and results otherwise as
  * linear_bias_act_ws.
  */
 #define LL_NOALLOC_SCRATCH_BYTES (32ll << 20)

@@ -710,6 +710,17 @@ int linear_bias_act_noalloc(int M, int N, int K, const float *X, int ldx, const 
     int st = current_device(&dev);
     if (st != LL_OK)
         return st;
+    if (stream != nullptr) {
+        // the array used is the current device's: the kernels must run there
+        int sdev = -1, cur = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess ||
+            hipGetDevice(&cur) != hipSuccess) {
+            (void)hipGetLastError();
+            return LL_ERR_INVALID_VALUE;
+        }
+        if (sdev != cur)
+            return LL_ERR_INVALID_VALUE;
+    }
     void *ws = scratch_address();
     if (ws == nullptr)
         return LL_ERR_LAUNCH;

@@ -161,3 +161,22 @@ def test_argument_errors(auto_plan):
     assert lib.linear_bias_act_noalloc(*args, 0, None, 1, Y.data_ptr(), 4, s) == E
     assert lib.linear_bias_act_noalloc(*args, 0, None, 1, Y.data_ptr(), 8, s) == ll.OK
     torch.cuda.synchronize()
+
+
+def test_non_default_stream(auto_plan):
+    """On a stream of its own (same device): the same result as
+    linear_bias_act_ws on the default stream, and the stream check passes."""
+    M, N, K = 330, 270, 520
+    X, W = wl.uniform((M, K), 321, 0.125), wl.uniform((K, N), 322, 0.125)
+    b = wl.bias_uniform(N, 323)
+    Xd, Wd, bd = X.to(DEV), W.to(DEV), b.to(DEV)
+    side = torch.cuda.Stream()
+    Yn = torch.full((M, N), float("nan"), device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ll.linear_bias_act_noalloc(Xd, Wd, bd, 1, Yn)
+    side.synchronize()
+    torch.cuda.current_stream().wait_stream(side)
+    R, T = oracle.linear(np32(X), np32(W), np32(b), 1)
+    bad = ~(np.abs(np32(Yn).astype(np.float64) - R) <= bound(R, T))
+    assert not bad.any(), f"{bad.sum()} of {bad.size} outside the oracle bound"
