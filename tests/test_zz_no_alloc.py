@@ -2,7 +2,8 @@
 C ABI: its output against linear_bias_act_ws on the same inputs and against
 the float64 oracle, on two calls in a row (the second smaller) that share the
 library's static workspace; shapes whose plan needs more workspace than the
-static array are refused and leave Y untouched."""
+static array are refused and leave Y untouched; a call on a stream of its own;
+and the call captured in a HIP graph, replayed with new inputs."""
 import ctypes
 
 import numpy as np
@@ -180,3 +181,49 @@ def test_non_default_stream(auto_plan):
     R, T = oracle.linear(np32(X), np32(W), np32(b), 1)
     bad = ~(np.abs(np32(Yn).astype(np.float64) - R) <= bound(R, T))
     assert not bad.any(), f"{bad.sum()} of {bad.size} outside the oracle bound"
+
+
+def test_graph_capture_replays(auto_plan):
+    """The use the entry point exists for: captured once in a HIP graph (no
+    allocation, no memset inside), then replayed three times with new inputs
+    written eagerly between the replays; every replay against the oracle and
+    against an eager linear_bias_act_ws call on the same inputs."""
+    w = wl.WORKLOADS["linear_relu_2047x4096x11008"]
+    M, N, K = w.M, w.N, w.K
+    need = ll.linear_workspace_size(M, N, K, False, 1, cus())
+    assert 0 < need <= ll.NOALLOC_SCRATCH_BYTES   # a stream-K plan that uses the static array
+    Xd = torch.empty((M, K), device=DEV)
+    Wd = torch.empty((K, N), device=DEV)
+    bd = torch.empty((N,), device=DEV)
+    Y = torch.empty((M, N), device=DEV)
+    x = wl.make_inputs(w, integer=True)
+    Xd.copy_(x["A"]); Wd.copy_(x["B"]); bd.copy_(x["bias"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # first call outside the capture: device set-up
+        ll.linear_bias_act_noalloc(Xd, Wd, bd, 1, Y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ll.linear_bias_act_noalloc(Xd, Wd, bd, 1, Y)
+    torch.cuda.synchronize()
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for rep in range(3):
+        X = wl.integers((M, K), 330 + rep, -2, 2)
+        Wh = wl.integers((K, N), 340 + rep, -2, 2)
+        b = wl.integers((N,), 350 + rep, -4, 4)
+        Xd.copy_(X); Wd.copy_(Wh); bd.copy_(b)
+        Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = np32(Y)
+        Ye = torch.full((M, N), float("nan"), device=DEV)
+        ll.linear_bias_act_ws(Xd, Wd, bd, 1, Ye, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, np32(Ye)), f"replay {rep}: graph and eager call differ"
+        R, _ = oracle.linear(np32(X), np32(Wh), np32(b), 1)
+        assert np.array_equal(got, R.astype(np.float32)), f"replay {rep}: differs from the oracle"
+        assert int(torch.count_nonzero(ws)) == 0
+    del g
