@@ -389,3 +389,12 @@ def test_linear_noalloc_argument_checks():
     assert lib.linear_bias_act_noalloc(*args, 2, None, 1, PC, 8, None) == ll.ERR_INVALID_VALUE
     st = lib.linear_bias_act_noalloc(*args, 0, None, 1, PC, 8, None)
     assert st in (ll.ERR_NO_DEVICE, ll.ERR_UNSUPPORTED_ARCH, ll.OK)
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADERS[0]).read()
+    m = re.search(r"#define\s+LL_NOALLOC_SCRATCH_BYTES\s+\((\d+)ll\s*<<\s*(\d+)\)", text)
+    assert m, "LL_NOALLOC_SCRATCH_BYTES not found"
+    assert ll.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    # the fused-layer workload's stream-K plan fits the static workspace
+    assert 0 < ll.linear_workspace_size(2047, 11008, 4096, False, 1, 256) <= ll.NOALLOC_SCRATCH_BYTES
