@@ -1,7 +1,8 @@
 // The C ABI: argument checks, quick returns, tile choice and one launch on the
 // caller's stream. Nothing here allocates, synchronises or keeps per-call
-// state; the only global data are a per-device property cache and the
-// plan overrides of linear_layer_tuning.h.
+// state; the only global data are a per-device property cache, the plan
+// overrides of linear_layer_tuning.h, and the no-allocation entry point's
+// static device workspace with its per-device address cache.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
