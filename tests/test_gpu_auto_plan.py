@@ -120,3 +120,52 @@ def test_random_shape_automatic_plan(case):
     bound = 1e-4 * T + np.spacing(np.abs(R).astype(np.float32)).astype(np.float64) / 2
     bad = ~(np.abs(got.astype(np.float64) - R) <= bound)
     assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} outside the bound"
+
+
+def draw_batched(n=24, seed=20261203, max_macs=2.0e9):
+    """(dtype, trans_b, batch, M, N, K, alpha, beta) for the strided-batch
+    entry points: batch in [1, 48], log-uniform sizes in [1, 700]."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        dt = ["f32", "f16", "bf16"][len(out) % 3]
+        nb = int(rng.integers(1, 49))
+        M, N, K = (int(round(np.exp(rng.uniform(0.0, np.log(700.0))))) for _ in range(3))
+        if float(nb) * M * N * K > max_macs:
+            continue
+        alpha, beta = AB[int(rng.integers(len(AB)))]
+        out.append((dt, bool(rng.integers(2)), nb, M, N, K, alpha, beta))
+    return out
+
+
+BATCHED = draw_batched()
+
+
+@pytest.mark.parametrize("case", BATCHED,
+                         ids=[f"{c[0]}-{'nt' if c[1] else 'nn'}-b{c[2]}-{c[3]}x{c[4]}x{c[5]}" for c in BATCHED])
+def test_random_batched_automatic_plan(case):
+    dt, tb, nb, M, N, K, alpha, beta = case
+    seed = 9000 + BATCHED.index(case) * 4
+    A = wl.uniform((nb, M, K), seed)
+    Bkn = wl.uniform((nb, K, N), seed + 1)
+    C0 = wl.uniform((nb, M, N), seed + 2)
+    Bg = Bkn.transpose(1, 2).contiguous() if tb else Bkn
+    if dt == "f32":
+        R, T = oracle.gemm_batched(np32(A), np32(Bkn), alpha, beta, np32(C0))
+        Ad, Bd = A.to(DEV), Bg.to(DEV)
+        fn = ll.gemm_f32_batched
+    else:
+        conv = wl.to_bf16 if dt == "bf16" else wl.to_half
+        Ah, Bh = conv(A), conv(Bkn)
+        R, T = oracle.gemm_batched(wl.half_bits(Ah), wl.half_bits(Bh), alpha, beta, np32(C0),
+                                   bf16=dt == "bf16")
+        Ad = Ah.to(DEV)
+        Bd = (Bh.transpose(1, 2).contiguous() if tb else Bh).to(DEV)
+        fn = ll.gemm_bf16f32_batched if dt == "bf16" else ll.gemm_f16f32_batched
+    Cd = C0.to(DEV)
+    fn(Ad, Bd, Cd, alpha, beta, trans_b=tb)
+    torch.cuda.synchronize()
+    got = np32(Cd).astype(np.float64)
+    bound = 1e-4 * T + np.spacing(np.abs(R).astype(np.float32)).astype(np.float64) / 2
+    bad = ~(np.abs(got - R) <= bound)
+    assert not bad.any(), f"{case}: {bad.sum()} of {bad.size} outside the bound"
