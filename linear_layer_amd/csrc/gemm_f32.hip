@@ -731,7 +731,7 @@ gemm_f32_direct_kernel(GemmParams p)
         }
         __syncthreads();
         if (sk_last) {
-            // eight groups in flight per lane (unrolled by 8: 3 us faster per
+            // eight groups in flight per lane (unrolled by 8: 2 us faster per
             // fused-layer call than no unrolling; 16 or 32 measured no faster,
             // and 32 spills registers)
 #pragma unroll 8
