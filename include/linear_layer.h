@@ -206,8 +206,11 @@ int64_t ll_linear_workspace_size(int M, int N, int K, int w_layout, int act, int
  * harnesses that forbid allocation): the workspace is the library's own
  * static device array of LL_NOALLOC_SCRATCH_BYTES (one per GPU, held until
  * the process ends), so the call allocates nothing and takes no workspace
- * argument. A shape whose plan needs more workspace than that (see
- * ll_linear_workspace_size) returns LL_ERR_INVALID_VALUE and runs nothing.
+ * argument. The array covers every plan on a device of up to 256 compute
+ * units (a stream-K plan shares out less than one round of tiles: at most
+ * 64 MiB of partial tiles plus their counters). A shape whose plan needs more
+ * workspace than that (see ll_linear_workspace_size) returns
+ * LL_ERR_INVALID_VALUE and runs nothing.
  * Every call on one GPU uses that GPU's single array: calls that overlap in
  * time on one GPU (other streams, other threads) race and give wrong
  * results; calls on one stream never overlap. Each call leaves the array
@@ -216,7 +219,7 @@ int64_t ll_linear_workspace_size(int M, int N, int K, int w_layout, int act, int
  * LL_ERR_INVALID_VALUE). Arguments and results otherwise as
  * linear_bias_act_ws.
  */
-#define LL_NOALLOC_SCRATCH_BYTES (32ll << 20)
+#define LL_NOALLOC_SCRATCH_BYTES (65ll << 20)
 int linear_bias_act_noalloc(int M, int N, int K,
                             const float *X, int ldx, const float *W, int ldw, int w_layout,
                             const float *bias, int act,

@@ -40,6 +40,12 @@ int ll_set_split_k(int splits);
  * the 128x128 and 64x64 16-bit tiles never share out). */
 int ll_set_stream_k(int mode);
 
+/* Lower the workspace linear_bias_act_noalloc may use to `bytes` (0 ..
+ * LL_NOALLOC_SCRATCH_BYTES) for every later call, so that its refusal of
+ * larger needs can be exercised on a device where no plan reaches the full
+ * array; -1 restores the full array. */
+int ll_set_noalloc_limit(int64_t bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,11 @@ Entry points (same names as the C ABI in ``include/linear_layer.h``):
 * ``gemm_f32_nt``, ``gemm_f16f32_nt``, ``gemm_bf16f32_nt``, ``linear_bias_act_nt``
   — the same with B (W) given N-by-K: C = alpha*A*B^T + beta*C, Y = act(X*W^T + b)
   (W in the [out_features, in_features] layout of ``torch.nn.Linear.weight``).
+* ``linear_bias_act_ws(X, W, bias, act, Y, workspace, w_trans=False)`` — the fused
+  layer with a caller workspace (``linear_workspace_size``): stream-K shapes in one
+  launch with bias and ReLU in every tile's write-back.
+* ``linear_bias_act_noalloc(X, W, bias, act, Y, w_trans=False)`` — the same on the
+  library's static per-GPU workspace, for callers that cannot allocate.
 * ``gemm_f32_batched``, ``gemm_f16f32_batched``, ``gemm_bf16f32_batched``
   ``(A, B, C, alpha=1.0, beta=0.0, trans_b=False)`` — C[i] = alpha*A[i]*op(B[i])
   + beta*C[i] over 3-D tensors whose first axis is the batch; its stride is the
@@ -33,6 +38,7 @@ __all__ = [
     "gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt", "linear_bias_act_nt",
     "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
     "linear_bias_act_ws", "linear_workspace_size", "linear_bias_act_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "set_noalloc_limit",
     "library_path", "load", "set_tile", "num_tiles", "tile_name", "chosen_tile",
     "set_split_k", "chosen_split_k", "set_stream_k", "chosen_stream_k",
     "ACT_NONE", "ACT_RELU", "DTYPE_F32", "DTYPE_F16", "PLAN_RELU", "PLAN_B_NK", "PLAN_UNALIGNED",
@@ -43,7 +49,7 @@ OK, ERR_INVALID_VALUE, ERR_NO_DEVICE, ERR_UNSUPPORTED_ARCH, ERR_LAUNCH = 0, 1, 2
 ACT_NONE, ACT_RELU = 0, 1
 DTYPE_F32, DTYPE_F16 = 0, 1
 PLAN_RELU, PLAN_B_NK, PLAN_UNALIGNED = 0x100, 0x200, 0x400   # flags OR-ed into dtype for chosen_*
-NOALLOC_SCRATCH_BYTES = 32 << 20   # the static workspace of linear_bias_act_noalloc
+NOALLOC_SCRATCH_BYTES = 65 << 20   # the static workspace of linear_bias_act_noalloc
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # The in-package library, or another build of it named by LINEAR_LAYER_LIBRARY
@@ -58,7 +64,8 @@ EXPORTED = ("gemm_f32", "gemm_f16f32", "gemm_bf16f32", "linear_bias_act", "ll_st
             "gemm_f32_batched", "gemm_f16f32_batched", "gemm_bf16f32_batched",
             "ll_num_tiles", "ll_tile_name", "ll_set_tile", "ll_chosen_tile",
             "ll_set_split_k", "ll_chosen_split_k", "ll_set_stream_k", "ll_chosen_stream_k",
-            "linear_bias_act_ws", "ll_linear_workspace_size", "linear_bias_act_noalloc")
+            "linear_bias_act_ws", "ll_linear_workspace_size", "linear_bias_act_noalloc",
+            "ll_set_noalloc_limit")
 
 
 class LinearLayerError(RuntimeError):
@@ -89,6 +96,8 @@ def load():
     lib.linear_bias_act_ws.restype = i32
     lib.linear_bias_act_noalloc.argtypes = [i32, i32, i32, vp, i32, vp, i32, i32, vp, i32, vp, i32, vp]
     lib.linear_bias_act_noalloc.restype = i32
+    lib.ll_set_noalloc_limit.argtypes = [ctypes.c_int64]
+    lib.ll_set_noalloc_limit.restype = i32
     lib.ll_linear_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.ll_linear_workspace_size.restype = ctypes.c_int64
     for nt in ("gemm_f32_nt", "gemm_f16f32_nt", "gemm_bf16f32_nt"):
@@ -368,6 +377,12 @@ def linear_bias_act_ws(X, W, bias, act: int, Y, workspace, w_trans: bool = False
             raise ValueError("workspace must be a contiguous device tensor")
         pws, nws = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     return _linear("linear_bias_act_ws", X, W, bias, act, Y, stream, wt=w_trans, ws=(pws, nws))
+
+
+def set_noalloc_limit(nbytes: int) -> None:
+    """Lower the workspace linear_bias_act_noalloc may use (process-wide;
+    -1 restores the full static array). For tests of its refusal."""
+    _check(load().ll_set_noalloc_limit(int(nbytes)), "ll_set_noalloc_limit")
 
 
 def linear_bias_act_noalloc(X, W, bias, act: int, Y, w_trans: bool = False, stream=None):

@@ -681,6 +681,8 @@ static __device__ __align__(256) unsigned char scratch[LL_NOALLOC_SCRATCH_BYTES]
 
 static std::once_flag g_scratch_once[kMaxDevices];
 static void *g_scratch_ptr[kMaxDevices];
+// the part of `scratch` calls may use (ll_set_noalloc_limit; process-wide)
+static std::atomic<int64_t> g_noalloc_limit{LL_NOALLOC_SCRATCH_BYTES};
 
 // The current device's copy of `scratch`, or nullptr.
 static void *scratch_address()
@@ -726,7 +728,15 @@ int linear_bias_act_noalloc(int M, int N, int K, const float *X, int ldx, const 
     if (ws == nullptr)
         return LL_ERR_LAUNCH;
     return linear_impl(M, N, K, X, ldx, W, ldw, bias, act, Y, ldy, stream, w_layout == LL_W_N_BY_K,
-                       ws, LL_NOALLOC_SCRATCH_BYTES, true);
+                       ws, g_noalloc_limit.load(std::memory_order_relaxed), true);
+}
+
+int ll_set_noalloc_limit(int64_t bytes)
+{
+    if (bytes != -1 && (bytes < 0 || bytes > LL_NOALLOC_SCRATCH_BYTES))
+        return LL_ERR_INVALID_VALUE;
+    g_noalloc_limit.store(bytes == -1 ? LL_NOALLOC_SCRATCH_BYTES : bytes, std::memory_order_relaxed);
+    return LL_OK;
 }
 
 int64_t ll_linear_workspace_size(int M, int N, int K, int w_layout, int act, int num_cus)

@@ -396,5 +396,34 @@ def test_noalloc_limit_matches_header():
     m = re.search(r"#define\s+LL_NOALLOC_SCRATCH_BYTES\s+\((\d+)ll\s*<<\s*(\d+)\)", text)
     assert m, "LL_NOALLOC_SCRATCH_BYTES not found"
     assert ll.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
-    # the fused-layer workload's stream-K plan fits the static workspace
-    assert 0 < ll.linear_workspace_size(2047, 11008, 4096, False, 1, 256) <= ll.NOALLOC_SCRATCH_BYTES
+    # every fused-layer plan on 256 CUs fits the static workspace: a stream-K
+    # plan shares out less than a round of tiles (at most 64 MiB of them)
+    for M, N, K in ((2047, 11008, 4096), (4096, 11008, 4096), (4096, 14336, 4096),
+                    (3000, 5000, 11008), (11008, 6000, 4096)):
+        for wt in (False, True):
+            assert ll.linear_workspace_size(M, N, K, wt, 1, 256) <= ll.NOALLOC_SCRATCH_BYTES
+    lib = ll.load()
+    E = ll.ERR_INVALID_VALUE
+    assert lib.ll_set_noalloc_limit(-2) == E
+    assert lib.ll_set_noalloc_limit(ll.NOALLOC_SCRATCH_BYTES + 1) == E
+    assert lib.ll_set_noalloc_limit(0) == ll.OK
+    assert lib.ll_set_noalloc_limit(-1) == ll.OK
+
+
+def test_every_forced_stream_k_plan_fits_the_static_workspace():
+    """Even with a tile and stream-K forced, no fused-layer plan on 256 CUs
+    needs more than the no-allocation entry point's static array."""
+    sizes = [64, 300, 1024, 2047, 3000, 4096, 5000, 8192, 11008, 16384]
+    worst = 0
+    try:
+        for t in range(ll.num_tiles(ll.DTYPE_F32)):
+            ll.set_tile(ll.DTYPE_F32, t)
+            ll.set_stream_k(1)
+            for M in sizes:
+                for N in sizes:
+                    for K in (512, 4096):
+                        worst = max(worst, ll.linear_workspace_size(M, N, K, False, 1, 256))
+    finally:
+        ll.set_tile(ll.DTYPE_F32, -1)
+        ll.set_stream_k(-1)
+    assert 40 << 20 < worst <= ll.NOALLOC_SCRATCH_BYTES

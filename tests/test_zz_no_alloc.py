@@ -32,9 +32,11 @@ def auto_plan():
     ll.set_tile(F32, -1)
     ll.set_stream_k(-1)
     ll.set_split_k(-1)
+    ll.set_noalloc_limit(-1)
     yield
     ll.set_tile(F32, -1)
     ll.set_stream_k(-1)
+    ll.set_noalloc_limit(-1)
 
 
 def cus():
@@ -133,11 +135,14 @@ def test_small_and_whole_tile_plans(shape, act, with_bias, auto_plan):
 
 
 def test_too_large_is_refused(auto_plan):
-    """A shape whose plan needs more than the static workspace is refused with
-    LL_ERR_INVALID_VALUE before anything runs: Y keeps its NaNs."""
-    M, N, K = 3000, 5000, 11008
+    """A shape whose plan needs more than the usable static workspace is
+    refused with LL_ERR_INVALID_VALUE before anything runs: Y keeps its NaNs.
+    (No plan on 256 CUs needs the whole array, so the usable part is lowered
+    to 16 MiB for the fused-layer workload's 22 MiB.)"""
+    M, N, K = 2047, 11008, 4096
     need = ll.linear_workspace_size(M, N, K, False, 1, cus())
-    assert need > ll.NOALLOC_SCRATCH_BYTES
+    assert 16 << 20 < need <= ll.NOALLOC_SCRATCH_BYTES
+    ll.set_noalloc_limit(16 << 20)
     lib = ll.load()
     X = torch.zeros((M, K), device=DEV)
     W = torch.zeros((K, N), device=DEV)
@@ -147,6 +152,24 @@ def test_too_large_is_refused(auto_plan):
     assert bool(torch.isnan(Y).all())
     with pytest.raises(ll.LinearLayerError):
         ll.linear_bias_act_noalloc(X, W, None, 1, Y)
+    ll.set_noalloc_limit(need)   # exactly enough: runs
+    assert call(lib.linear_bias_act_noalloc, X, W, None, 1, Y, False) == ll.OK
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(Y)) == 0
+
+
+def test_largest_plans_fit(auto_plan):
+    """Plans that share out most of a round of tiles fit the static array:
+    4096 x 11008 x 4096 (44 MiB of workspace) and 3000 x 5000 x 11008 (60 MiB),
+    integer inputs, bit for bit against linear_bias_act_ws."""
+    for (M, N, K), seed in (((4096, 11008, 4096), 361), ((3000, 5000, 11008), 365)):
+        need = ll.linear_workspace_size(M, N, K, False, 1, cus())
+        assert 40 << 20 < need <= ll.NOALLOC_SCRATCH_BYTES
+        X, W = wl.integers((M, K), seed, -2, 2), wl.integers((K, N), seed + 1, -1, 1)
+        b = wl.integers((N,), seed + 2, -4, 4)
+        got, ref, _ = both(X, W, b, 1, False)
+        assert np.array_equal(got, ref), f"{M}x{N}x{K}: noalloc and ws differ"
+        assert not np.isnan(got).any()
 
 
 def test_argument_errors(auto_plan):
