@@ -47,7 +47,23 @@ struct GemmParams {
     // the epilogue and clears both
     float *ws;
     int *ws_cnt;
+    // 1: 16-byte chunk loads of A and B never cross the end of a row's valid
+    // elements (K, and N for B given K-by-N, are multiples of a chunk), so the
+    // register-staged kernels may load whole chunks whatever the alignment
+    int chunks;
 };
+
+// A 16-byte load from an address of any alignment. The target allows
+// unaligned global accesses (the compiler itself emits one dwordx4 load for
+// this copy even at 2-byte alignment).
+template <class V>
+__device__ __forceinline__ V load16(const void *src)
+{
+    static_assert(sizeof(V) == 16, "16-byte vector");
+    V v;
+    __builtin_memcpy(&v, src, 16);
+    return v;
+}
 
 // Bounds a direct kernel's copies check (a template mask; see the launchers).
 enum : int { CHK_M = 1, CHK_N = 2, CHK_K = 4 };

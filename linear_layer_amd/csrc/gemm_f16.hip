@@ -120,7 +120,7 @@ gemm_f16_kernel(GemmParams p)
             if (VEC) {
                 u32x4 v = {0u, 0u, 0u, 0u};
                 if (rok && kk < K)
-                    v = *reinterpret_cast<const u32x4 *>(src);
+                    v = load16<u32x4>(src);
                 dst[i] = v;
             } else {
 #pragma unroll
@@ -158,7 +158,7 @@ gemm_f16_kernel(GemmParams p)
                 if (VEC) {
                     u32x4 v = {0u, 0u, 0u, 0u};
                     if (active && kk < K && nn < N)
-                        v = *reinterpret_cast<const u32x4 *>(src);
+                        v = load16<u32x4>(src);
                     rb[i][j] = v;
                 } else {
 #pragma unroll
@@ -715,7 +715,9 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F16_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f16_kernel<T, E, V, WPE, BF16, BT>), grid, block, 0, s, p)
-    if (vec) {
+    // whole 16-byte chunks: aligned operands, or unaligned ones whose rows
+    // hold whole chunks
+    if (vec || p.chunks) {
         if (epi == EPI_GEMM_BETA0) LL_F16_LAUNCH(EPI_GEMM_BETA0, true);
         else if (epi == EPI_GEMM_BETA) LL_F16_LAUNCH(EPI_GEMM_BETA, true);
         else LL_F16_LAUNCH(EPI_ATOMIC, true);

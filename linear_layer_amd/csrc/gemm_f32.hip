@@ -90,7 +90,7 @@ struct RowPanel {
             if (VEC) {
                 f32x4 v = {0.f, 0.f, 0.f, 0.f};
                 if (rok && kk < K)
-                    v = *reinterpret_cast<const f32x4 *>(src);
+                    v = load16<f32x4>(src);
                 reg[i] = v;
             } else {
 #pragma unroll
@@ -175,7 +175,7 @@ gemm_f32_kernel(GemmParams p)
             if (VEC) {
                 f32x4 v = {0.f, 0.f, 0.f, 0.f};
                 if (kk < K && nn < N)
-                    v = *reinterpret_cast<const f32x4 *>(src);
+                    v = load16<f32x4>(src);
                 rb[i] = v;
             } else {
 #pragma unroll
@@ -924,7 +924,9 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
 #define LL_F32_LAUNCH(E, V) \
     hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE, BT>), grid, block, 0, s, p)
-    if (vec) {
+    // whole 16-byte chunks: aligned operands, or unaligned ones whose rows
+    // hold whole chunks
+    if (vec || p.chunks) {
         if (epi == EPI_GEMM_BETA0) LL_F32_LAUNCH(EPI_GEMM_BETA0, true);
         else if (epi == EPI_GEMM_BETA) LL_F32_LAUNCH(EPI_GEMM_BETA, true);
         else if (epi == EPI_LINEAR) LL_F32_LAUNCH(EPI_LINEAR, true);
