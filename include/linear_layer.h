@@ -63,9 +63,9 @@ extern "C" {
  * Products are accumulated in FP32 on the matrix cores (MFMA), in an order of
  * the kernel's choosing. C must not overlap A or B. Pointers need only be
  * 4-byte aligned; 16-byte aligned pointers with lda, ldb, ldc, K and N all
- * multiples of 4 take the direct-to-LDS kernels; otherwise, with K (and N,
- * for B given K-by-N) multiples of 4, register-staged kernels with 128-bit
- * loads at any alignment; anything else their per-element-load variants.
+ * multiples of 4 take the direct-to-LDS kernels; anything else the
+ * register-staged kernels, which load 128-bit chunks at any alignment and
+ * the chunk that crosses K or N element by element.
  */
 int gemm_f32(int M, int N, int K, float alpha,
              const float *A, int lda, const float *B, int ldb,
@@ -85,9 +85,8 @@ int gemm_f32(int M, int N, int K, float alpha,
  *   C  M-by-N fp32, ldc >= max(1, N).
  * Every other argument, rule and error as gemm_f32. Pointers to A and B need
  * only be 2-byte aligned; the direct-to-LDS kernels need 16-byte aligned
- * pointers and lda, ldb, K, N multiples of 8 (ldc a multiple of 4), the
- * register-staged 128-bit-load kernels only K (and N for B given K-by-N)
- * multiples of 8.
+ * pointers and lda, ldb, K, N multiples of 8 (ldc a multiple of 4), other
+ * operands run the register-staged kernels.
  */
 int gemm_f16f32(int M, int N, int K, float alpha,
                 const uint16_t *A, int lda, const uint16_t *B, int ldb,

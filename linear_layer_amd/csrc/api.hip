@@ -471,7 +471,6 @@ static int gemm_f32_impl(int M, int N, int K, float alpha, const float *A, int l
                      ldb % 4 == 0 && ldc % 4 == 0 && K % 4 == 0 && (bt || N % 4 == 0) &&
                      batch_aligned(bat, 4);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    p.chunks = K % 4 == 0 && (bt || N % 4 == 0);
     const Plan pl =
         plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false, bat.count, vec);
     if (pl.tile < 0)
@@ -511,7 +510,6 @@ static int gemm_16(int M, int N, int K, float alpha, const uint16_t *A, int lda,
                      ldb % 8 == 0 && ldc % 4 == 0 && K % 8 == 0 && (bt || N % 8 == 0) &&
                      batch_aligned(bat, 2);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    p.chunks = K % 8 == 0 && (bt || N % 8 == 0);
     const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false, bat.count, vec);
     if (pl.tile < 0)
         return LL_ERR_INVALID_VALUE;
@@ -611,7 +609,6 @@ static int linear_impl(int M, int N, int K, const float *X, int ldx, const float
     GemmParams p = make_params(M, N, K, 1.0f, X, ldx, W, ldw, 0.0f, Y, ldy);
     p.bias = bias;
     p.act = act;
-    p.chunks = K % 4 == 0 && (wt || N % 4 == 0);
     const launch_fn launch = wt ? launch_gemm_f32_bt : launch_gemm_f32;
     const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU, 1, vec);
     if (pl.tile < 0)

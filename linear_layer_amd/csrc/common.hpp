@@ -47,10 +47,6 @@ struct GemmParams {
     // the epilogue and clears both
     float *ws;
     int *ws_cnt;
-    // 1: 16-byte chunk loads of A and B never cross the end of a row's valid
-    // elements (K, and N for B given K-by-N, are multiples of a chunk), so the
-    // register-staged kernels may load whole chunks whatever the alignment
-    int chunks;
 };
 
 // A 16-byte load from an address of any alignment. The target allows

@@ -77,7 +77,7 @@ template <> struct AccBlock<16> { using type = f32x4; static constexpr int R = 4
 
 // BT: B is given N-by-K (k contiguous); it is then loaded and stored exactly
 // like A and needs no transposition.
-template <class T, int EPI, bool VEC, int WPE, bool BF16, bool BT>
+template <class T, int EPI, int WPE, bool BF16, bool BT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f16_kernel(GemmParams p)
 {
@@ -117,19 +117,20 @@ gemm_f16_kernel(GemmParams p)
             const bool rok = first + a_r0 + i * A_RSTEP < nrows;
             const int kk = k0 + a_c * 8;
             const uint16_t *src = ptr + i * istep + k0;
-            if (VEC) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (rok && kk < K)
-                    v = load16<u32x4>(src);
-                dst[i] = v;
-            } else {
+            // whole chunks at any alignment; the chunk that crosses K
+            // element by element
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (rok && kk + 8 <= K) {
+                v = load16<u32x4>(src);
+            } else if (rok && kk < K) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const uint32_t lo = (rok && kk + 2 * j < K) ? ld_u16(src + 2 * j) : 0u;
-                    const uint32_t hi = (rok && kk + 2 * j + 1 < K) ? ld_u16(src + 2 * j + 1) : 0u;
-                    dst[i][j] = lo | (hi << 16);
+                    const uint32_t lo = kk + 2 * j < K ? ld_u16(src + 2 * j) : 0u;
+                    const uint32_t hi = kk + 2 * j + 1 < K ? ld_u16(src + 2 * j + 1) : 0u;
+                    v[j] = lo | (hi << 16);
                 }
             }
+            dst[i] = v;
         }
     };
 
@@ -155,20 +156,18 @@ gemm_f16_kernel(GemmParams p)
             for (int j = 0; j < 8; ++j) {
                 const int kk = k0 + kb * 8 + j;
                 const uint16_t *src = B + (int64_t)kk * p.ldb + nn;
-                if (VEC) {
-                    u32x4 v = {0u, 0u, 0u, 0u};
-                    if (active && kk < K && nn < N)
-                        v = load16<u32x4>(src);
-                    rb[i][j] = v;
-                } else {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (active && kk < K && nn + 8 <= N) {
+                    v = load16<u32x4>(src);
+                } else if (active && kk < K && nn < N) {
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
-                        const bool ok = active && kk < K;
-                        const uint32_t lo = (ok && nn + 2 * d < N) ? ld_u16(src + 2 * d) : 0u;
-                        const uint32_t hi = (ok && nn + 2 * d + 1 < N) ? ld_u16(src + 2 * d + 1) : 0u;
-                        rb[i][j][d] = lo | (hi << 16);
+                        const uint32_t lo = nn + 2 * d < N ? ld_u16(src + 2 * d) : 0u;
+                        const uint32_t hi = nn + 2 * d + 1 < N ? ld_u16(src + 2 * d + 1) : 0u;
+                        v[d] = lo | (hi << 16);
                     }
                 }
+                rb[i][j] = v;
             }
         }
     };
@@ -713,19 +712,13 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     if (ntiles > kMaxTiles || p.batch < 1 || p.batch > kMaxGridZ || p.grid_x != 0 || p.sk_tiles != 0)
         return hipErrorInvalidValue;   // the register-staged kernels run whole grids only
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
-#define LL_F16_LAUNCH(E, V) \
-    hipLaunchKernelGGL((gemm_f16_kernel<T, E, V, WPE, BF16, BT>), grid, block, 0, s, p)
-    // whole 16-byte chunks: aligned operands, or unaligned ones whose rows
-    // hold whole chunks
-    if (vec || p.chunks) {
-        if (epi == EPI_GEMM_BETA0) LL_F16_LAUNCH(EPI_GEMM_BETA0, true);
-        else if (epi == EPI_GEMM_BETA) LL_F16_LAUNCH(EPI_GEMM_BETA, true);
-        else LL_F16_LAUNCH(EPI_ATOMIC, true);
-    } else {
-        if (epi == EPI_GEMM_BETA0) LL_F16_LAUNCH(EPI_GEMM_BETA0, false);
-        else if (epi == EPI_GEMM_BETA) LL_F16_LAUNCH(EPI_GEMM_BETA, false);
-        else LL_F16_LAUNCH(EPI_ATOMIC, false);
-    }
+#define LL_F16_LAUNCH(E) \
+    hipLaunchKernelGGL((gemm_f16_kernel<T, E, WPE, BF16, BT>), grid, block, 0, s, p)
+    // 16-byte chunk loads at any alignment, the chunk that crosses K or N
+    // element by element
+    if (epi == EPI_GEMM_BETA0) LL_F16_LAUNCH(EPI_GEMM_BETA0);
+    else if (epi == EPI_GEMM_BETA) LL_F16_LAUNCH(EPI_GEMM_BETA);
+    else LL_F16_LAUNCH(EPI_ATOMIC);
 #undef LL_F16_LAUNCH
     return hipGetLastError();
 }

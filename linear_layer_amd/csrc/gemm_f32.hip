@@ -61,7 +61,7 @@ struct F32Tile {
 // matrix (A, or B given N-by-K), staged through registers into a swizzled
 // [row][k] LDS tile. Thread t owns chunks (t + i*NT): row (t + i*NT)/CPR,
 // 16-byte chunk t%CPR.
-template <class T, int ROWS, bool VEC>
+template <class T, int ROWS>
 struct RowPanel {
     static constexpr int CPR = T::CPR, BK = T::BK;
     static constexpr int PT = ROWS * CPR / T::NT;
@@ -87,16 +87,17 @@ struct RowPanel {
             const bool rok = row_base + r0 + i * RSTEP < rows;
             const float *src = ptr + i * istep + k0;
             const int kk = k0 + c * 4;
-            if (VEC) {
-                f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (rok && kk < K)
-                    v = load16<f32x4>(src);
-                reg[i] = v;
-            } else {
+            // whole chunks at any alignment; the chunk that crosses K
+            // element by element
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (rok && kk + 4 <= K) {
+                v = load16<f32x4>(src);
+            } else if (rok && kk < K) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    reg[i][j] = (rok && kk + j < K) ? src[j] : 0.0f;
+                    v[j] = kk + j < K ? src[j] : 0.0f;
             }
+            reg[i] = v;
         }
     }
     __device__ void store(float *lds) const
@@ -126,7 +127,7 @@ __device__ __forceinline__ void read_rows(const float *lds, int row, int h, f32x
 // BT = true: B is given N-by-K (k contiguous, e.g. a fully-connected weight
 // stored [out][in]); it is staged exactly like A, as swizzled [n][k] rows, and
 // read with 128-bit LDS loads like A.
-template <class T, int EPI, bool VEC, int WPE, bool BT>
+template <class T, int EPI, int WPE, bool BT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 gemm_f32_kernel(GemmParams p)
 {
@@ -148,9 +149,9 @@ gemm_f32_kernel(GemmParams p)
         static_cast<const float *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
     const int M = p.M, N = p.N;
 
-    RowPanel<T, BM, VEC> pa;
+    RowPanel<T, BM> pa;
     pa.init(A, p.lda, m0, M, tid);
-    RowPanel<T, BN, VEC> pbt;   // B given N-by-K
+    RowPanel<T, BN> pbt;   // B given N-by-K
     // B given K-by-N: chunk i is k-row b_k0 + i*B_KSTEP, columns n0 + 4*b_c ..
     const int b_c = tid % T::BCPR;
     const int b_k0 = tid / T::BCPR;
@@ -172,16 +173,15 @@ gemm_f32_kernel(GemmParams p)
             const int kk = k0 + b_k0 + i * B_KSTEP;
             const int nn = n0 + b_c * 4;
             const float *src = b_ptr + i * b_istep + (int64_t)k0 * p.ldb;
-            if (VEC) {
-                f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (kk < K && nn < N)
-                    v = load16<f32x4>(src);
-                rb[i] = v;
-            } else {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (kk < K && nn + 4 <= N) {
+                v = load16<f32x4>(src);
+            } else if (kk < K && nn < N) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    rb[i][j] = (kk < K && nn + j < N) ? src[j] : 0.0f;
+                    v[j] = nn + j < N ? src[j] : 0.0f;
             }
+            rb[i] = v;
         }
     };
 
@@ -922,21 +922,14 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
             return launch_direct<64, 64, 32, 2, (KS > 1 ? KS : 4), 2, 2, BT, KS>(p, ntiles, epi, s);
     }
     const dim3 grid = gemm_grid(p, ntiles), block(T::NT);
-#define LL_F32_LAUNCH(E, V) \
-    hipLaunchKernelGGL((gemm_f32_kernel<T, E, V, WPE, BT>), grid, block, 0, s, p)
-    // whole 16-byte chunks: aligned operands, or unaligned ones whose rows
-    // hold whole chunks
-    if (vec || p.chunks) {
-        if (epi == EPI_GEMM_BETA0) LL_F32_LAUNCH(EPI_GEMM_BETA0, true);
-        else if (epi == EPI_GEMM_BETA) LL_F32_LAUNCH(EPI_GEMM_BETA, true);
-        else if (epi == EPI_LINEAR) LL_F32_LAUNCH(EPI_LINEAR, true);
-        else LL_F32_LAUNCH(EPI_ATOMIC, true);
-    } else {
-        if (epi == EPI_GEMM_BETA0) LL_F32_LAUNCH(EPI_GEMM_BETA0, false);
-        else if (epi == EPI_GEMM_BETA) LL_F32_LAUNCH(EPI_GEMM_BETA, false);
-        else if (epi == EPI_LINEAR) LL_F32_LAUNCH(EPI_LINEAR, false);
-        else LL_F32_LAUNCH(EPI_ATOMIC, false);
-    }
+#define LL_F32_LAUNCH(E) \
+    hipLaunchKernelGGL((gemm_f32_kernel<T, E, WPE, BT>), grid, block, 0, s, p)
+    // register-staged: 16-byte chunk loads at any alignment, the chunk that
+    // crosses K or N element by element
+    if (epi == EPI_GEMM_BETA0) LL_F32_LAUNCH(EPI_GEMM_BETA0);
+    else if (epi == EPI_GEMM_BETA) LL_F32_LAUNCH(EPI_GEMM_BETA);
+    else if (epi == EPI_LINEAR) LL_F32_LAUNCH(EPI_LINEAR);
+    else LL_F32_LAUNCH(EPI_ATOMIC);
 #undef LL_F32_LAUNCH
     return hipGetLastError();
 }

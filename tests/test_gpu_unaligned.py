@@ -1,8 +1,9 @@
-"""GPU parity with unaligned operands: leading dimensions one, two or three
-elements longer than a 16-byte multiple and base pointers offset by one
-element, with K and N multiples of a 16-byte chunk, so the register-staged
-kernels load whole chunks at 4- or 2-byte alignment; against the float64
-oracle element by element, guard columns untouched."""
+"""GPU parity with unaligned operands, which run the register-staged kernels:
+16-byte chunk loads at 4- or 2-byte alignment, and the chunk that crosses K
+or N element by element. Leading dimensions 1-9 elements past a multiple,
+base pointers shifted by 1-3 elements, K and N that are and are not chunk
+multiples; against the float64 oracle element by element, guard columns
+untouched."""
 import numpy as np
 import pytest
 
@@ -119,3 +120,36 @@ def test_batched_unaligned_items():
     torch.cuda.synchronize()
     R, T = oracle.gemm_batched(np32(A), np32(Bkn), 1.5, 0.5, np32(C0))
     check(np32(Cd), R, T, "batched unaligned items")
+
+
+@pytest.mark.parametrize("M,N,K", [(301, 517, 203), (257, 263, 1001), (1000, 999, 997)])
+@pytest.mark.parametrize("which", ["f32", "f16", "bf16", "linear"])
+def test_ragged_k_and_n(M, N, K, which):
+    """K and N that are not chunk multiples: whole chunks, then the crossing
+    chunk element by element."""
+    A, Bkn, C0 = wl.uniform((M, K), 541), wl.uniform((K, N), 542), wl.uniform((M, N), 543)
+    if which == "linear":
+        b = wl.bias_uniform(N, 544)
+        _, Xd = view(A, 1, 0)
+        _, Wd = view(Bkn, 1, 0)
+        ybuf, Yd = view(torch.full((M, N), float("nan")), 1, 0, fill=7.0)
+        ll.linear_bias_act(Xd, Wd, b.to(DEV), 1, Yd)
+        torch.cuda.synchronize()
+        R, T = oracle.linear(np32(A), np32(Bkn), np32(b), 1)
+        check(np32(Yd), R, T, f"linear {M}x{N}x{K}")
+        assert guards_ok(ybuf, 0, N, 7.0)
+        return
+    if which == "f32":
+        Ad, Bd = A.to(DEV), Bkn.to(DEV)
+        R, T = oracle.gemm(np32(A), np32(Bkn), 1.5, 0.5, np32(C0))
+        fn = ll.gemm_f32
+    else:
+        conv = wl.to_bf16 if which == "bf16" else wl.to_half
+        Ah, Bh = conv(A), conv(Bkn)
+        Ad, Bd = Ah.to(DEV), Bh.to(DEV)
+        R, T = oracle.gemm(wl.half_bits(Ah), wl.half_bits(Bh), 1.5, 0.5, np32(C0), bf16=which == "bf16")
+        fn = ll.gemm_bf16f32 if which == "bf16" else ll.gemm_f16f32
+    cbuf, Cd = view(C0, 0, 0)
+    fn(Ad, Bd, Cd, 1.5, 0.5)
+    torch.cuda.synchronize()
+    check(np32(Cd), R, T, f"{which} {M}x{N}x{K}")
