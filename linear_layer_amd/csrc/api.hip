@@ -228,18 +228,53 @@ bool sk_tile_ok(const TileInfo &ti)
 // operands allow the 128-bit-load kernels; without it the tiles that exist
 // only as direct kernels (whose calls would run a staged kernel of another
 // shape) and stream-K are not considered, unless a tile is forced.
+// The skinny FP32 kernel (a few rows of A, memory-bound): one workgroup per
+// 256 columns and K-split. The K-splits give about two workgroups per CU (B
+// given K-by-N) or three (N-by-K, whose waves stream fewer bytes at a time),
+// as measured fastest on MI355X, and keep each split within the A block the
+// kernel stages whole (skinny_kmax); at most kMaxSkinnySplits (the atomic
+// partial sums of a few rows cost little), each at least kSplitAlign long.
+constexpr int kMaxSkinnySplits = 64;
+Plan skinny_plan(int M, int N, int K, int cus, int s_ov, bool bt)
+{
+    const int64_t nblk = cdiv(N, kSkinnyCols);
+    if (nblk > max_grid_x(256) || nblk * kSkinnyCols > ((int64_t)1 << 31))
+        return Plan{-1, 1, K, 0, 0};   // more workgroups than one launch holds
+    int64_t s = s_ov;
+    if (s_ov < 1) {
+        const int64_t fill = ((bt ? 3 : 2) * (int64_t)(cus > 0 ? cus : 1) + nblk - 1) / nblk;
+        const int64_t fit = ((int64_t)K + skinny_kmax(M) - 1) / skinny_kmax(M);
+        const int64_t smax = ((int64_t)K + kSplitAlign - 1) / kSplitAlign;
+        s = fill > fit ? fill : fit;
+        s = s > kMaxSkinnySplits ? kMaxSkinnySplits : s;
+        s = s > smax ? smax : s;
+    }
+    if (s <= 1 || K <= 0)
+        return Plan{kSkinnyTile, 1, K, 0, 0};
+    const int k_split =
+        (int)((((int64_t)K + s - 1) / s + kSplitAlign - 1) / kSplitAlign * kSplitAlign);
+    return Plan{kSkinnyTile, (int)(((int64_t)K + k_split - 1) / k_split), k_split, 0, 0};
+}
+
 Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int cus, bool relu,
-          int batch, bool vec)
+          int batch, bool vec, bool bt)
 {
     const int items = batch < kMaxGridZ ? batch : kMaxGridZ;   // items per launch
     const Overrides ov = load_overrides();
     const int t_ov = ov.tile[dtype], s_ov = ov.splits, sk_ov = ov.sk;
+    // FP32 products of at most kSkinnyMaxM rows of A (single, not batched)
+    // run the skinny kernel; it runs others only when forced
+    if (dtype == LL_DTYPE_F32 && (t_ov == kSkinnyTile || (t_ov < 0 && M <= kSkinnyMaxM && batch == 1))) {
+        const Plan sp = skinny_plan(M, N, K, cus, s_ov, bt);
+        if (sp.tile >= 0 || t_ov == kSkinnyTile)
+            return sp;
+    }
     const bool allow_sk = vec && batch == 1 && s_ov < 1 && sk_ov != 0 && K > 0;
     Plan best{0, 1, K, 0, 0}, best_sk{0, 1, K, 0, 0};
     double best_cost = 0.0, best_sk_cost = 0.0;
     bool have = false, have_sk = false;
     for (int t = 0; t < ntiles; ++t) {
-        if (t_ov >= 0 && t != t_ov)
+        if ((t_ov >= 0 && t != t_ov) || (dtype == LL_DTYPE_F32 && t == kSkinnyTile))
             continue;
         const TileInfo &ti = tiles[t];
         const int64_t tiles_mn = (int64_t)cdiv(M, ti.bm) * cdiv(N, ti.bn);
@@ -472,7 +507,7 @@ static int gemm_f32_impl(int M, int N, int K, float alpha, const float *A, int l
                      batch_aligned(bat, 4);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     const Plan pl =
-        plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false, bat.count, vec);
+        plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, false, bat.count, vec, bt);
     if (pl.tile < 0)
         return LL_ERR_INVALID_VALUE;
     return launch_status(run_gemm(p, pl, vec, s, bt ? launch_gemm_f32_bt : launch_gemm_f32, 4, bat,
@@ -510,7 +545,7 @@ static int gemm_16(int M, int N, int K, float alpha, const uint16_t *A, int lda,
                      ldb % 8 == 0 && ldc % 4 == 0 && K % 8 == 0 && (bt || N % 8 == 0) &&
                      batch_aligned(bat, 2);
     GemmParams p = make_params(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-    const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false, bat.count, vec);
+    const Plan pl = plan(1, kF16Tiles, kF16NumTiles, M, N, K, dev.cus, false, bat.count, vec, bt);
     if (pl.tile < 0)
         return LL_ERR_INVALID_VALUE;
     return launch_status(run_gemm(p, pl, vec, s, launch, 2, bat, &kF16Tiles[pl.tile]));
@@ -610,7 +645,7 @@ static int linear_impl(int M, int N, int K, const float *X, int ldx, const float
     p.bias = bias;
     p.act = act;
     const launch_fn launch = wt ? launch_gemm_f32_bt : launch_gemm_f32;
-    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU, 1, vec);
+    const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, dev.cus, act == LL_ACT_RELU, 1, vec, wt);
     if (pl.tile < 0)
         return LL_ERR_INVALID_VALUE;
     if (pl.sk_grid > 0) {
@@ -747,7 +782,7 @@ int64_t ll_linear_workspace_size(int M, int N, int K, int w_layout, int act, int
     if (M == 0 || N == 0 || K == 0)
         return 0;
     const Plan pl = plan(0, kF32Tiles, kF32NumTiles, M, N, K, num_cus > 0 ? num_cus : 256,
-                         act == LL_ACT_RELU, 1, true);
+                         act == LL_ACT_RELU, 1, true, w_layout == LL_W_N_BY_K);
     return linear_ws_need(pl, M, N);
 }
 
@@ -795,7 +830,7 @@ const char *ll_tile_name(int dtype, int tile)
 static Plan chosen_plan(int dtype, int M, int N, int K, int batch, int num_cus, bool *ok)
 {
     const int base = dtype & 0xff, flags = dtype & ~0xff;
-    const bool relu = flags & LL_PLAN_RELU;   // LL_PLAN_B_NK: accepted, plans alike
+    const bool relu = flags & LL_PLAN_RELU, bt = flags & LL_PLAN_B_NK;
     const bool vec = !(flags & LL_PLAN_UNALIGNED);
     *ok = (base == LL_DTYPE_F32 || (base == LL_DTYPE_F16 && !relu)) &&
           (flags & ~(LL_PLAN_RELU | LL_PLAN_B_NK | LL_PLAN_UNALIGNED)) == 0 && batch >= 1;
@@ -803,8 +838,8 @@ static Plan chosen_plan(int dtype, int M, int N, int K, int batch, int num_cus, 
         return Plan{-1, -1, 0};
     const int cus = num_cus > 0 ? num_cus : 256;
     const Plan pl = base == LL_DTYPE_F32
-                        ? plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, relu, batch, vec)
-                        : plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch, vec);
+                        ? plan(0, kF32Tiles, kF32NumTiles, M, N, K, cus, relu, batch, vec, bt)
+                        : plan(1, kF16Tiles, kF16NumTiles, M, N, K, cus, false, batch, vec, bt);
     if (pl.tile < 0)
         *ok = false;
     return pl;

@@ -9,44 +9,51 @@
 
 namespace ll {
 
-// One workgroup per row-stripe, threads striding along the row; grid z walks
-// the items of a strided batch (stride_c bytes apart).
+// A workgroup sweeps 1024 columns of a row (four values per thread, 256
+// apart, all four loads issued before the stores), grid y walks the rows and
+// grid z the items of a strided batch (stride_c bytes apart); a row of a
+// thousand or so values is one wave of loads, not a loop of dependent ones.
+constexpr int kSweepCols = 1024;
+
+template <class F>
+__device__ __forceinline__ void sweep_rows(float *base, int64_t ld, int M, int N, bool reads, F f)
+{
+    const int64_t n0 = (int64_t)blockIdx.x * kSweepCols + threadIdx.x;
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        float *row = base + m * ld;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = reads && n0 + 256 * j < N ? row[n0 + 256 * j] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (n0 + 256 * j < N)
+                row[n0 + 256 * j] = f(v[j], n0 + 256 * j);
+    }
+}
+
 __global__ void __launch_bounds__(256) scale_kernel(float *C, int64_t ldc, int M, int N, float beta,
                                                     int64_t stride_c)
 {
     C = reinterpret_cast<float *>(reinterpret_cast<char *>(C) + (int64_t)blockIdx.z * stride_c);
-    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
-        float *row = C + m * ldc;
-        for (int n = threadIdx.x; n < N; n += blockDim.x)
-            row[n] = (beta == 0.0f) ? 0.0f : beta * row[n];
-    }
+    sweep_rows(C, ldc, M, N, beta != 0.0f,
+               [beta](float v, int64_t) { return beta == 0.0f ? 0.0f : beta * v; });
 }
 
 __global__ void __launch_bounds__(256) bias_fill_kernel(float *Y, int64_t ldy, int M, int N,
                                                         const float *bias, int act)
 {
-    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
-        float *row = Y + m * ldy;
-        for (int n = threadIdx.x; n < N; n += blockDim.x) {
-            float v = bias ? bias[n] : 0.0f;
-            if (act == 1)
-                v = v > 0.0f ? v : 0.0f;
-            row[n] = v;
-        }
-    }
+    sweep_rows(Y, ldy, M, N, false, [bias, act](float, int64_t n) {
+        const float v = bias ? bias[n] : 0.0f;
+        return act == 1 ? (v > 0.0f ? v : 0.0f) : v;
+    });
 }
 
 // In-place ReLU (y <= 0 and NaN -> +0), the last step of a split-K
 // fully-connected layer whose partial sums were accumulated atomically.
 __global__ void __launch_bounds__(256) relu_kernel(float *Y, int64_t ldy, int M, int N)
 {
-    for (int64_t m = blockIdx.x; m < M; m += gridDim.x) {
-        float *row = Y + m * ldy;
-        for (int n = threadIdx.x; n < N; n += blockDim.x) {
-            const float v = row[n];
-            row[n] = v > 0.0f ? v : 0.0f;
-        }
-    }
+    sweep_rows(Y, ldy, M, N, true, [](float v, int64_t) { return v > 0.0f ? v : 0.0f; });
 }
 
 // The same three operations on whole output tiles: tiles tile_base ..
@@ -112,30 +119,36 @@ hipError_t launch_tile_pass(const GemmParams &p0, int bm, int bn, int first_tile
     return hipGetLastError();
 }
 
-static unsigned rows_grid(int M)
+static dim3 sweep_grid(int M, int N, int batch = 1)
 {
-    return (unsigned)(M < 65536 ? M : 65536);
+    return dim3((unsigned)((N + kSweepCols - 1) / kSweepCols), (unsigned)(M < 65535 ? M : 65535),
+                (unsigned)batch);
 }
 
 hipError_t launch_scale(float *C, int64_t ldc, int M, int N, float beta, hipStream_t s, int batch,
                         int64_t stride_c)
 {
-    hipLaunchKernelGGL(scale_kernel, dim3(rows_grid(M), 1, (unsigned)batch), dim3(256), 0, s, C, ldc,
-                       M, N, beta, stride_c);
+    if (M <= 0 || N <= 0 || batch <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(scale_kernel, sweep_grid(M, N, batch), dim3(256), 0, s, C, ldc, M, N, beta,
+                       stride_c);
     return hipGetLastError();
 }
 
 hipError_t launch_relu(float *Y, int64_t ldy, int M, int N, hipStream_t s)
 {
-    hipLaunchKernelGGL(relu_kernel, dim3(rows_grid(M)), dim3(256), 0, s, Y, ldy, M, N);
+    if (M <= 0 || N <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(relu_kernel, sweep_grid(M, N), dim3(256), 0, s, Y, ldy, M, N);
     return hipGetLastError();
 }
 
 hipError_t launch_bias_fill(float *Y, int64_t ldy, int M, int N, const float *bias, int act,
                             hipStream_t s)
 {
-    hipLaunchKernelGGL(bias_fill_kernel, dim3(rows_grid(M)), dim3(256), 0, s, Y, ldy, M, N, bias,
-                       act);
+    if (M <= 0 || N <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(bias_fill_kernel, sweep_grid(M, N), dim3(256), 0, s, Y, ldy, M, N, bias, act);
     return hipGetLastError();
 }
 

@@ -798,6 +798,257 @@ gemm_f32_direct_kernel(GemmParams p)
 // 4096^3 product (about 89 % of the FP32 matrix peak); 256x128 at two
 // workgroups per CU is the plain choice for the 2047 x 11008 fully-connected
 // layer, whose leftover tiles stream-K otherwise shares out.
+// Skinny products (a few rows of A): memory-bound, so vector FMAs instead of
+// MFMAs, which would compute a whole 32-row block for every row. A
+// workgroup of four waves covers 256 columns of C over its K range (a
+// K-split), A's rows MR at a time (MR = 1, 4 or 16, the fewest that cover
+// M). The A block of the K range is staged in LDS once (SK_XS floats: the
+// planner keeps the range within SK_XS / MR k-values; a longer one, from a
+// forced plan, is walked in chunks of that size). B streams from HBM with
+// the next loads issued before the current ones are used.
+//   B given K-by-N: lane l covers columns 4l .. 4l+3 (one 16-byte load per
+//     k-row); wave w takes the runs of U k-rows numbered w mod 4; A's values
+//     are LDS broadcasts; the four waves' sums meet in LDS at the end.
+//   B given N-by-K: wave w covers columns 64w .. 64w+63 in 16 groups of four;
+//     in a group, lane l reads column 4g + l/16's row of B at k-values
+//     4(l%16) + 64j, so a load covers 64 consecutive k of four rows; the 16
+//     lanes of a row add their sums by DPP and the result goes to an LDS row
+//     of C, stored once at the end.
+// B's loads take whole 16-byte chunks at any alignment, the chunk that
+// crosses N or K element by element. The epilogue: alpha*acc (+ beta*C),
+// bias and ReLU, or atomic partial sums for a K-split.
+constexpr int SK_COLS = 256;     // columns of C per workgroup
+constexpr int SK_XS = 8192;      // LDS floats for the staged A block (32 KiB)
+
+__device__ __forceinline__ float dpp_row_sum16(float v)
+{
+    // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror:
+    // after the four steps every lane of a 16-lane row holds the row's sum
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false));
+    return v;
+}
+
+template <int EPI>
+__device__ __forceinline__ void skinny_store(const GemmParams &p, int row, int col, float a)
+{
+    float *dst = p.C + (int64_t)row * p.ldc + col;
+    if constexpr (EPI == EPI_ATOMIC) {
+        __hip_atomic_fetch_add(dst, p.alpha * a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (EPI == EPI_GEMM_BETA) {
+        *dst = __builtin_fmaf(p.alpha, a, p.beta * *dst);
+    } else if constexpr (EPI == EPI_LINEAR) {
+        const float y = a + (p.bias != nullptr ? p.bias[col] : 0.0f);
+        *dst = (p.act == 1 && !(y > 0.0f)) ? 0.0f : y;
+    } else {
+        *dst = p.alpha * a;
+    }
+}
+
+// A's rows mc .. mc+MR-1 (zero past M), k-values kc .. kc+kn-1 of the K
+// range, into xs[m][0 .. kpad) (zero past kn; kpad = kn rounded up to 64).
+template <int MR>
+__device__ __forceinline__ void skinny_stage(float *xs, const float *A, int64_t lda, int64_t mc, int M,
+                                             int64_t kc, int kn)
+{
+    constexpr int KC = SK_XS / MR;
+    const int kq = ((kn + 63) & ~63) / 4;   // 16-byte chunks per row
+    for (int i = threadIdx.x; i < MR * kq; i += 256) {
+        const int m = i / kq, k = (i % kq) * 4;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (mc + m < M) {
+            const float *src = A + (mc + m) * lda + kc + k;
+            if (k + 4 <= kn) {
+                v = load16<f32x4>(src);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    v[j] = k + j < kn ? src[j] : 0.0f;
+            }
+        }
+        *reinterpret_cast<f32x4 *>(xs + m * KC + k) = v;
+    }
+}
+
+template <int EPI, bool BT, int MR>
+__global__ void __launch_bounds__(256) gemm_f32_skinny_kernel(GemmParams p)
+{
+    constexpr int KC = SK_XS / MR;                        // k-values staged at once
+    constexpr int RED = BT ? MR * SK_COLS : 3 * MR * SK_COLS;   // N-by-K: C row block; K-by-N: 3 waves' sums
+    __shared__ __attribute__((aligned(16))) float lds[BT ? SK_XS + RED : (SK_XS > RED ? SK_XS : RED)];
+    float *xs = lds;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    select_batch(p);
+    int K;
+    const int kb = split_range(p, K);
+    const float *__restrict__ A = static_cast<const float *>(p.A) + kb;
+    const float *__restrict__ B =
+        static_cast<const float *>(p.B) + (BT ? (int64_t)kb : (int64_t)kb * p.ldb);
+    const int M = p.M, N = p.N;
+    const int nblk = blockIdx.x * SK_COLS;
+
+    // 64-bit chunk counters: M or K may lie within one chunk of 2^31
+    for (int64_t mc = 0; mc < M; mc += MR) {
+        if constexpr (!BT) {
+            constexpr int U = MR == 16 ? 4 : 8;   // k-rows per run (loads in flight per lane, twice)
+            const int ncol = nblk + 4 * lane;
+            const bool full = ncol <= N - 4, part = ncol < N;
+            f32x4 acc[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int64_t kc = 0; kc < K; kc += KC) {
+                const int kn = K - kc < KC ? (int)(K - kc) : KC;
+                __syncthreads();   // the previous chunk's (or row block's) A values are read
+                skinny_stage<MR>(xs, A, p.lda, mc, M, kc, kn);
+                __syncthreads();
+                const float *Bc = B + kc * p.ldb + ncol;
+                auto fetch = [&](f32x4 (&w)[U], int run) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int k = (4 * run + wave) * U + u;
+                        const float *src = Bc + (int64_t)k * p.ldb;
+                        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                        if (k < kn && full) {
+                            v = load16<f32x4>(src);
+                        } else if (k < kn && part) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                v[j] = ncol + j < N ? src[j] : 0.0f;
+                        }
+                        w[u] = v;
+                    }
+                };
+                const int runs = (kn + 4 * U - 1) / (4 * U);   // runs of all four waves
+                f32x4 wc[U], wn[U];
+                fetch(wc, 0);
+                for (int r = 0; r < runs; ++r) {
+                    if (r + 1 < runs)
+                        fetch(wn, r + 1);
+                    const int k0 = (4 * r + wave) * U;   // within KC: KC is a multiple of 4U
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+#pragma unroll
+                        for (int q = 0; q < U / 4; ++q) {
+                            const f32x4 x = *reinterpret_cast<const f32x4 *>(xs + m * KC + k0 + 4 * q);
+                            acc[m] += x[0] * wc[4 * q] + x[1] * wc[4 * q + 1] + x[2] * wc[4 * q + 2] +
+                                      x[3] * wc[4 * q + 3];
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        wc[u] = wn[u];
+                }
+            }
+            // the four waves' sums of the same columns, through LDS
+            __syncthreads();   // xs is read; red aliases it
+            f32x4 *red = reinterpret_cast<f32x4 *>(lds);
+            if (wave > 0) {
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    red[((wave - 1) * MR + m) * 64 + lane] = acc[m];
+            }
+            __syncthreads();
+            if (wave == 0) {
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    const f32x4 a = acc[m] + red[m * 64 + lane] + red[(MR + m) * 64 + lane] +
+                                    red[(2 * MR + m) * 64 + lane];
+                    const int row = (int)mc + m;
+                    if (row < M) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (ncol + j < N)
+                                skinny_store<EPI>(p, row, ncol + j, a[j]);
+                    }
+                }
+            }
+        } else {
+            float *ys = lds + SK_XS;   // [MR][SK_COLS]: this row block of C
+            for (int i = tid; i < MR * SK_COLS; i += 256)
+                ys[i] = 0.0f;
+            constexpr int D = MR == 16 ? 2 : 8;   // loads in flight per lane
+            const int c4 = 4 * (lane & 15), rg = lane >> 4;
+            for (int64_t kc = 0; kc < K; kc += KC) {
+                const int kn = K - kc < KC ? (int)(K - kc) : KC;
+                __syncthreads();   // the previous chunk's (or row block's) A values are read
+                skinny_stage<MR>(xs, A, p.lda, mc, M, kc, kn);
+                __syncthreads();
+                const int steps = (kn + 63) / 64;      // 64 k-values of a row per load
+                const int total = 16 * steps;          // (group, step) pairs of this wave
+                auto fetch = [&](int t) -> f32x4 {
+                    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                    if (t >= total)
+                        return v;
+                    const int g = t / steps, k = (t - g * steps) * 64 + c4;
+                    const int col = nblk + 64 * wave + 4 * g + rg;
+                    if (col >= N)
+                        return v;
+                    const float *src = B + (int64_t)col * p.ldb + kc + k;
+                    if (k + 4 <= kn) {
+                        v = load16<f32x4>(src);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            v[j] = k + j < kn ? src[j] : 0.0f;
+                    }
+                    return v;
+                };
+                f32x4 w[D];
+#pragma unroll
+                for (int d = 0; d < D; ++d)
+                    w[d] = fetch(d);
+                float acc[MR];
+#pragma unroll
+                for (int m = 0; m < MR; ++m)
+                    acc[m] = 0.0f;
+                int g = 0, st = 0;
+                for (int tb = 0; tb < total; tb += D) {
+#pragma unroll
+                    for (int d = 0; d < D; ++d) {
+                        if (tb + d < total) {
+                            const int k0 = st * 64 + c4;   // within KC: KC is a multiple of 64
+#pragma unroll
+                            for (int m = 0; m < MR; ++m) {
+                                const f32x4 x = *reinterpret_cast<const f32x4 *>(xs + m * KC + k0);
+                                acc[m] += x[0] * w[d][0] + x[1] * w[d][1] + x[2] * w[d][2] + x[3] * w[d][3];
+                            }
+                            w[d] = fetch(tb + d + D);
+                            if (++st == steps) {
+                                // group g done: the 16 lanes of each row add up, lane 0 of the
+                                // row adds the sums into the C row block
+#pragma unroll
+                                for (int m = 0; m < MR; ++m) {
+                                    const float v = dpp_row_sum16(acc[m]);
+                                    if ((lane & 15) == 0)
+                                        ys[m * SK_COLS + 64 * wave + 4 * g + rg] += v;
+                                    acc[m] = 0.0f;
+                                }
+                                st = 0;
+                                ++g;
+                            }
+                        }
+                    }
+                }
+            }
+            __syncthreads();   // every wave's groups are in ys
+            const int col = nblk + tid;
+            if (col < N) {
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    const int row = (int)mc + m;
+                    if (row < M)
+                        skinny_store<EPI>(p, row, col, ys[m * SK_COLS + tid]);
+                }
+            }
+            __syncthreads();   // ys is read before the next row block clears it
+        }
+    }
+}
+
 using F32_L = F32Tile<256, 256, 16>;   // 128x128 per wave
 using F32_M = F32Tile<256, 128, 16>;   // 128x64 per wave
 using F32_S = F32Tile<128, 128, 16>;   // 64x64 per wave
@@ -953,8 +1204,37 @@ const TileInfo kF32Tiles[kF32NumTiles] = {
     // slices against 8.3 plain, 512^3 11.1 against 10.3 split across workgroups).
     {F32_XS::BM, F32_XS::BN, 1, 0.57f, 0.57f, "f32_64x64_k4", 4, true, 1024, 4 * 8 * 32, true},
     {F32_S::BM, F32_S::BN, 1, 0.90f, 0.90f, "f32_128x128_k2", 2, true, 512, 2 * 8 * 32, true},
+    // the skinny kernel: 16 rows of A at a time, 256 columns per workgroup
+    {16, SK_COLS, 2, 1.0f, 1.0f, "f32_16x256_skinny", 1, false},
 };
 #endif
+
+template <bool BT>
+static hipError_t launch_skinny(const GemmParams &p0, int epi, hipStream_t s)
+{
+    static_assert(SK_COLS == kSkinnyCols && SK_XS == kSkinnyStage, "skinny kernel shape");
+    GemmParams p = p0;
+    p.tiles_m = 1;
+    p.tiles_n = cdiv(p.N, SK_COLS);
+    if (p.batch < 1 || p.batch > kMaxGridZ || p.grid_x != 0 || p.sk_tiles != 0)
+        return hipErrorInvalidValue;   // whole grids only, no stream-K
+    const dim3 grid = gemm_grid(p, p.tiles_n), block(256);
+    const int mr = skinny_rows(p.M);
+#define LL_SKINNY_MR(E, MR) hipLaunchKernelGGL((gemm_f32_skinny_kernel<E, BT, MR>), grid, block, 0, s, p)
+#define LL_SKINNY(E) \
+    do { \
+        if (mr == 1) LL_SKINNY_MR(E, 1); \
+        else if (mr == 4) LL_SKINNY_MR(E, 4); \
+        else LL_SKINNY_MR(E, 16); \
+    } while (0)
+    if (epi == EPI_GEMM_BETA0) LL_SKINNY(EPI_GEMM_BETA0);
+    else if (epi == EPI_GEMM_BETA) LL_SKINNY(EPI_GEMM_BETA);
+    else if (epi == EPI_LINEAR) LL_SKINNY(EPI_LINEAR);
+    else LL_SKINNY(EPI_ATOMIC);
+#undef LL_SKINNY
+#undef LL_SKINNY_MR
+    return hipGetLastError();
+}
 
 template <bool BT>
 static hipError_t launch_f32(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
@@ -965,7 +1245,8 @@ static hipError_t launch_f32(const GemmParams &p, int tile, int epi, bool vec, h
     case 2: return launch_t<F32_S, 2, BT>(p, epi, vec, s);
     case 3: return launch_t<F32_XS, 2, BT>(p, epi, vec, s);
     case 4: return launch_t<F32_XS, 2, BT, 4>(p, epi, vec, s);
-    default: return launch_t<F32_S, 2, BT, 2>(p, epi, vec, s);
+    case 5: return launch_t<F32_S, 2, BT, 2>(p, epi, vec, s);
+    default: return launch_skinny<BT>(p, epi, s);
     }
 }
 

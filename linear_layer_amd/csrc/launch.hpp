@@ -20,7 +20,19 @@ struct TileInfo {
     bool direct_only = false;  // only the 128-bit-load kernels have this shape
 };
 
-constexpr int kF32NumTiles = 6;
+constexpr int kF32NumTiles = 7;
+// The FP32 tile that is the skinny kernel (vector FMAs for a few rows of A;
+// planned by rule, not by the MFMA tiles' cost model), its column width, and
+// the most rows of A it is chosen for automatically (measured on MI355X: 1.6
+// to 1.8 times the 64x64 MFMA tile's rate up to 4 rows; from 5 rows on, its
+// 16-row pass does more vector FMAs than it saves and the MFMA tiles win).
+constexpr int kSkinnyTile = 6, kSkinnyCols = 256, kSkinnyMaxM = 4;
+// Floats of A the skinny kernel stages in LDS at once, its rows per pass
+// for a product of M rows (the fewest of 1, 4, 16 that cover M), and so the
+// longest K range it stages whole.
+constexpr int kSkinnyStage = 8192;
+constexpr int skinny_rows(int M) { return M <= 1 ? 1 : M <= 4 ? 4 : 16; }
+constexpr int skinny_kmax(int M) { return kSkinnyStage / skinny_rows(M); }
 constexpr int kF16NumTiles = 5;
 extern const TileInfo kF32Tiles[kF32NumTiles];
 extern const TileInfo kF16Tiles[kF16NumTiles];

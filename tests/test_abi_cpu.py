@@ -177,7 +177,10 @@ def test_plans_at_int32_limits():
     t = ll.chosen_tile(f32, big, 4, 4, 256)
     assert ll.tile_name(f32, t) == "f32_256x128"          # 8.4M tiles of 256 threads
     assert ll.chosen_tile(f16, big - 512, 1, 1, 256) == 1   # 128x128: 16.8M tiles
-    for dt, shape in ((f32, (1, big, 1)), (f16, (big, 64, 64)), (f16, (1, big, 1))):
+    # a single row of 2^31 - 1 columns: 8.4M skinny workgroups fit one launch;
+    # 17 rows are past the skinny kernel, and no MFMA tile's grid fits
+    assert ll.tile_name(f32, ll.chosen_tile(f32, 1, big, 1, 256)) == "f32_16x256_skinny"
+    for dt, shape in ((f32, (17, big, 1)), (f16, (big, 64, 64)), (f16, (1, big, 1))):
         assert ll.chosen_tile(dt, *shape, 256) == -1
         assert ll.chosen_split_k(dt, *shape, 256) == -1
         assert ll.chosen_stream_k(dt, *shape, 256) == -1
@@ -352,7 +355,8 @@ def test_extreme_sizes_stay_in_range():
                 t = ll.chosen_tile(dt | flags, M, N, K, 256)
                 s = ll.chosen_split_k(dt | flags, M, N, K, 256)
                 sk = ll.chosen_stream_k(dt | flags, M, N, K, 256)
-                assert t == -1 or (0 <= t < ll.num_tiles(dt) and 1 <= s <= 16 and sk >= 0)
+                smax = 64 if t >= 0 and ll.tile_name(dt, t).endswith("_skinny") else 16
+                assert t == -1 or (0 <= t < ll.num_tiles(dt) and 1 <= s <= smax and sk >= 0)
 
 
 def test_linear_workspace_query():

@@ -633,11 +633,13 @@ def test_f32_nt_strided_b(t, tile):
         assert_close(np32(Cd), R, T, f"f32_nt tile {t} ldb={K + pad}")
 
 
-@pytest.mark.parametrize("t", T32)
+@pytest.mark.parametrize("t", [t for t in T32 if not ll.tile_name(F32, t).endswith("_skinny")])
 def test_f32_nt_matches_explicit_transpose(t, tile, split):
     """A*B^T through the _nt entry point equals gemm_f32 on B^T made contiguous, bit for bit:
     both feed the matrix units the same operands in the same k order. (One K-split:
-    split-K adds its partial sums atomically, in no fixed order.)"""
+    split-K adds its partial sums atomically, in no fixed order. The skinny
+    kernel is left out: its two layouts add a column's k-values in different
+    orders, by design, and its own tests compare each with the oracle.)"""
     tile(F32, t)
     split(1)
     M, N, K = 520, 392, 200

@@ -3,8 +3,8 @@ over random shapes (host logic only: the plan queries run without a GPU).
 
 For any product the planner either returns a usable plan or none (-1, for
 shapes whose tiles cannot fit one launch's grid); a usable plan names a tile
-of the data type's table whose grid fits, splits K into at most 16 parts of
-at least one 64-deep stage (unless forced), shares out stream-K tiles only
+of the data type's table whose grid fits, splits K into at most 16 parts (64
+for the skinny kernel) of at least one 64-deep stage (unless forced), shares out stream-K tiles only
 for single products without a K-split, never shares out more tiles than the
 product has, and honours forced settings.
 """
@@ -15,7 +15,7 @@ import linear_layer_amd as ll
 
 F32, F16 = ll.DTYPE_F32, ll.DTYPE_F16
 TILE_SHAPES = {
-    F32: [(256, 256), (256, 128), (128, 128), (64, 64), (64, 64), (128, 128)],
+    F32: [(256, 256), (256, 128), (128, 128), (64, 64), (64, 64), (128, 128), (16, 256)],
     F16: [(256, 256), (128, 128), (64, 64), (128, 128), (192, 192)],
 }
 dims = st.one_of(st.integers(1, 300), st.integers(1, 20000), st.sampled_from([255, 256, 257, 2047, 4096, 11008]))
@@ -51,7 +51,8 @@ def test_automatic_plans_are_well_formed(dt, M, N, K, batch, cus, relu, nk):
     s = ll.chosen_split_k(q, M, N, K, cus, batch)
     sk = ll.chosen_stream_k(q, M, N, K, cus, batch)
     assert 0 <= t < ll.num_tiles(dt)                 # these shapes always fit
-    assert 1 <= s <= 16
+    # the skinny kernel (a few rows of A) splits K up to 64 ways, the others 16
+    assert 1 <= s <= (64 if ll.tile_name(dt, t).endswith("_skinny") else 16)
     if s > 1:
         assert K >= 64 * (s - 1), "a split is at least one stage deep"
     assert sk >= 0
@@ -120,3 +121,31 @@ def test_unaligned_flag_changes_only_direct_only_choices():
     # 4096^3 is unaffected
     assert ll.chosen_tile(F32 | ll.PLAN_UNALIGNED, 4096, 4096, 4096, 256) == \
         ll.chosen_tile(F32, 4096, 4096, 4096, 256)
+
+
+def test_skinny_kernel_choice():
+    """FP32 products of at most 4 rows of A (single, not batched) take the
+    skinny kernel; its K-splits give about two workgroups per CU with B given
+    K-by-N, three with B given N-by-K, keep each split within the A block the
+    kernel stages whole (8192 / rows-per-pass k-values), and stay at most 64."""
+    name = lambda q, M, N, K, batch=1: ll.tile_name(F32, ll.chosen_tile(q, M, N, K, 256, batch))
+    split = lambda q, M, N, K: ll.chosen_split_k(q, M, N, K, 256)
+    for M in (1, 2, 3, 4):
+        for q in (F32, F32 | ll.PLAN_B_NK, F32 | ll.PLAN_RELU, F32 | ll.PLAN_UNALIGNED):
+            assert name(q, M, 11008, 4096).endswith("_skinny")
+    assert not name(F32, 5, 11008, 4096).endswith("_skinny")
+    assert not name(F32, 4, 11008, 4096, batch=2).endswith("_skinny")
+    assert not ll.tile_name(F16, ll.chosen_tile(F16, 1, 11008, 4096, 256)).endswith("_skinny")
+    # 43 column blocks of 256: ceil(512 / 43) = 12 splits of 384 -> 11 splits;
+    # N-by-K: ceil(768 / 43) = 18 splits of 256 -> 16 splits
+    assert split(F32, 1, 11008, 4096) == 11
+    assert split(F32 | ll.PLAN_B_NK, 1, 11008, 4096) == 16
+    # 4 rows stage 2048 k-values: K = 20000 needs at least 10 splits even with
+    # many column blocks
+    assert split(F32, 4, 65536, 20000) >= 10
+    # the split count never passes 64; a K no split can keep within the
+    # staged block still gets 64 splits (the kernel then walks its range in
+    # chunks)
+    assert split(F32, 4, 256, 2 ** 20) == 64
+    # short K: no split shorter than 64
+    assert split(F32, 1, 256, 100) == 2 and split(F32, 1, 256, 64) == 1
