@@ -262,9 +262,10 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
     const int items = batch < kMaxGridZ ? batch : kMaxGridZ;   // items per launch
     const Overrides ov = load_overrides();
     const int t_ov = ov.tile[dtype], s_ov = ov.splits, sk_ov = ov.sk;
-    // FP32 products of at most kSkinnyMaxM rows of A (single, not batched)
-    // run the skinny kernel; it runs others only when forced
-    if (dtype == LL_DTYPE_F32 && (t_ov == kSkinnyTile || (t_ov < 0 && M <= kSkinnyMaxM && batch == 1))) {
+    // single FP32 products of a few rows of A run the skinny kernel; it runs
+    // others only when forced
+    const bool skinny = M <= kSkinnyMaxM || (M <= kSkinnyMaxMLarge && (int64_t)K * N >= kSkinnyLargeKN);
+    if (dtype == LL_DTYPE_F32 && (t_ov == kSkinnyTile || (t_ov < 0 && skinny && batch == 1))) {
         const Plan sp = skinny_plan(M, N, K, cus, s_ov, bt);
         if (sp.tile >= 0 || t_ov == kSkinnyTile)
             return sp;

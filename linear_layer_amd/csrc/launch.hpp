@@ -22,16 +22,20 @@ struct TileInfo {
 
 constexpr int kF32NumTiles = 7;
 // The FP32 tile that is the skinny kernel (vector FMAs for a few rows of A;
-// planned by rule, not by the MFMA tiles' cost model), its column width, and
-// the most rows of A it is chosen for automatically (measured on MI355X: 1.6
-// to 1.8 times the 64x64 MFMA tile's rate up to 4 rows; from 5 rows on, its
-// 16-row pass does more vector FMAs than it saves and the MFMA tiles win).
-constexpr int kSkinnyTile = 6, kSkinnyCols = 256, kSkinnyMaxM = 4;
+// planned by rule, not by the MFMA tiles' cost model) and its column width.
+// It is chosen automatically for at most kSkinnyMaxM rows of A, and for up
+// to kSkinnyMaxMLarge rows when B holds at least kSkinnyLargeKN values.
+// Measured on MI355X against the 64x64 MFMA plan: 1.6 to 1.8 times its rate
+// up to 4 rows; 1.1 to 1.5 times for 5 to 8 rows with a 4096 x 11008 B, but
+// slower with a 4096 x 4096 one (its K-splits' atomic sums and short ranges
+// cost more there than the vector FMAs save); past 8 rows the MFMA tiles win.
+constexpr int kSkinnyTile = 6, kSkinnyCols = 256, kSkinnyMaxM = 4, kSkinnyMaxMLarge = 8;
+constexpr int64_t kSkinnyLargeKN = (int64_t)1 << 25;
 // Floats of A the skinny kernel stages in LDS at once, its rows per pass
-// for a product of M rows (the fewest of 1, 4, 16 that cover M), and so the
+// for a product of M rows (the fewest of 1, 4, 8, 16 that cover M), and so the
 // longest K range it stages whole.
 constexpr int kSkinnyStage = 8192;
-constexpr int skinny_rows(int M) { return M <= 1 ? 1 : M <= 4 ? 4 : 16; }
+constexpr int skinny_rows(int M) { return M <= 1 ? 1 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 constexpr int skinny_kmax(int M) { return kSkinnyStage / skinny_rows(M); }
 constexpr int kF16NumTiles = 5;
 extern const TileInfo kF32Tiles[kF32NumTiles];

@@ -1,11 +1,11 @@
 """GPU parity of the skinny FP32 kernel (vector FMAs for a few rows of A,
-memory-bound; chosen by itself for up to 4 rows, forced here for more):
-every row count from 1 to 16 and a few past it, all three row-pass widths
-(1, 4, 16), both B layouts, every epilogue (beta = 0, general beta, K-split
-atomics, the fused layer with and without bias and ReLU), K ranges longer
-than the staged A block, ragged and unaligned N and K, and the layer's
-decode-sized shapes at full size; against the float64 oracle element by
-element, and bit-exact on integer inputs."""
+memory-bound; chosen by itself for up to 4 rows, or 8 with a large B, and
+forced here for more): every row count from 1 to 16 and a few past it, all
+four row-pass widths (1, 4, 8, 16), both B layouts, every epilogue (beta = 0,
+general beta, K-split atomics, the fused layer with and without bias and
+ReLU), K ranges longer than the staged A block, ragged and unaligned N and
+K, and the layer's decode-sized shapes at full size; against the float64
+oracle element by element, and bit-exact on integer inputs."""
 import numpy as np
 import pytest
 
@@ -72,8 +72,8 @@ def force_skinny():
 @pytest.mark.parametrize("M", list(range(1, 17)))
 @pytest.mark.parametrize("nt", [False, True])
 def test_every_row_count(M, nt):
-    """M = 1 .. 4 take the skinny kernel by themselves, 5 .. 16 when forced;
-    N and K ragged."""
+    """M = 1 .. 4 take the skinny kernel by themselves here (5 .. 8 do only
+    with a larger B), 5 .. 16 when forced; N and K ragged."""
     N, K = 1000, 777
     flags = F32 | (ll.PLAN_B_NK if nt else 0)
     if M <= 4:
@@ -187,7 +187,7 @@ def test_batched_forced():
         assert_close(np32(Cd), R, T, f"batched tb={tb}")
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 16])
+@pytest.mark.parametrize("M", [1, 3, 4, 8, 16])
 @pytest.mark.parametrize("nt", [False, True])
 def test_decode_sized_layer_full_size(M, nt):
     """The layer's weight at full size (K 4096, N 11008) with a handful of
@@ -195,7 +195,7 @@ def test_decode_sized_layer_full_size(M, nt):
     checked on every element against the oracle."""
     N, K = 11008, 4096
     flags = F32 | ll.PLAN_RELU | (ll.PLAN_B_NK if nt else 0)
-    if M > 4:
+    if M > 8:
         force_skinny()
     name, s = plan(flags, M, N, K)
     assert name == SKINNY and s > 1

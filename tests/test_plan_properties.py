@@ -124,8 +124,8 @@ def test_unaligned_flag_changes_only_direct_only_choices():
 
 
 def test_skinny_kernel_choice():
-    """FP32 products of at most 4 rows of A (single, not batched) take the
-    skinny kernel; its K-splits give about two workgroups per CU with B given
+    """Single FP32 products of at most 4 rows of A, or at most 8 with a large
+    B, take the skinny kernel; its K-splits give about two workgroups per CU with B given
     K-by-N, three with B given N-by-K, keep each split within the A block the
     kernel stages whole (8192 / rows-per-pass k-values), and stay at most 64."""
     name = lambda q, M, N, K, batch=1: ll.tile_name(F32, ll.chosen_tile(q, M, N, K, 256, batch))
@@ -133,7 +133,12 @@ def test_skinny_kernel_choice():
     for M in (1, 2, 3, 4):
         for q in (F32, F32 | ll.PLAN_B_NK, F32 | ll.PLAN_RELU, F32 | ll.PLAN_UNALIGNED):
             assert name(q, M, 11008, 4096).endswith("_skinny")
-    assert not name(F32, 5, 11008, 4096).endswith("_skinny")
+    # 5 to 8 rows only with a B of at least 2^25 values
+    for M in (5, 8):
+        assert name(F32, M, 11008, 4096).endswith("_skinny")
+        assert name(F32 | ll.PLAN_B_NK, M, 4096, 8192).endswith("_skinny")
+        assert not name(F32, M, 4096, 4096).endswith("_skinny")
+    assert not name(F32, 9, 11008, 4096).endswith("_skinny")
     assert not name(F32, 4, 11008, 4096, batch=2).endswith("_skinny")
     assert not ll.tile_name(F16, ll.chosen_tile(F16, 1, 11008, 4096, 256)).endswith("_skinny")
     # 43 column blocks of 256: ceil(512 / 43) = 12 splits of 384 -> 11 splits;
