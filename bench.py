@@ -10,7 +10,9 @@ Prints ONE JSON line with the metric (TFLOPS = 2*M*N*K*batch / time per step),
 a ``roofline`` object for the GEMM kernel (achieved = algorithmic FLOPs per
 launch / average launch duration, from a second pass of K steps each between
 its own pair of HIP events on the launch stream; peak = MI355X's published
-dense matrix peak for the dtype) and a ``cpu_baseline``
+dense matrix peak for the dtype; for the workloads with a few rows of A,
+which HBM bounds, compulsory bytes per launch over the same duration against
+the 8 TB/s HBM peak) and a ``cpu_baseline``
 object: the float64 CPU oracle timed on a bounded sample of the same workload
 (a block of whole output rows, or of whole batch items) on this host's cores.
 
@@ -36,6 +38,8 @@ sys.path.insert(0, ROOT)
 
 COPY_BYTES = 256 << 20
 
+# Published MI355X HBM bandwidth (GB/s), the peak of the memory-bound workloads.
+PEAK_HBM_GBS = 8000.0
 # Published MI355X dense matrix peaks (TFLOP/s).
 PEAK_TFLOPS = {"gemm_f32": 157.3, "linear": 157.3, "linear_nt": 157.3, "gemm_f32_batched": 157.3,
                "gemm_f16f32": 2516.6, "gemm_bf16f32": 2516.6, "gemm_f16f32_nt": 2516.6}
@@ -324,6 +328,23 @@ def config_record(w, step, plan, args, dev):
     return rec
 
 
+def roofline(w, achieved_tflops, avg_ms, launch_ms, peak_tflops, args):
+    """The roofline object: against the dtype's matrix peak in TFLOP/s, or,
+    for the workloads HBM bounds (a few rows of A), algorithmic bytes per call
+    over the average call against the HBM peak in GB/s."""
+    traffic = measured_traffic(w.name + ("_workspace" if args.workspace else ""), w.kind)
+    times = {"kernel_avg_ms": round(avg_ms, 5), "kernel_min_ms": round(min(launch_ms), 5),
+             "kernel_median_ms": round(sorted(launch_ms)[len(launch_ms) // 2], 5)}
+    if w.bound == "hbm":
+        gbs = w.hbm_bytes / (avg_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic, **times,
+                "bytes_per_launch": w.hbm_bytes}
+    return {"bound": "mfma", "achieved": round(achieved_tflops, 3), "peak": peak_tflops,
+            "unit": "TFLOP/s", "frac": round(achieved_tflops / peak_tflops, 4), "traffic": traffic,
+            **times, "flops_per_launch": float(w.flops)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -423,18 +444,7 @@ def main():
             "device": props.name, "cus": props.multi_processor_count, "hip": torch.version.hip,
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 3),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(w.name + ("_workspace" if args.workspace else ""), w.kind),
-            "kernel_avg_ms": round(avg_launch_ms, 5),
-            "kernel_min_ms": round(min(launch_ms), 5),
-            "kernel_median_ms": round(sorted(launch_ms)[len(launch_ms) // 2], 5),
-            "flops_per_launch": flops,
-        },
+        "roofline": roofline(w, achieved, avg_launch_ms, launch_ms, peak, args),
         "cpu_baseline": cpu,
     }
     if configs is not None:

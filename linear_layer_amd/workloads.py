@@ -23,7 +23,13 @@ matrix units take FP16 or BF16); the seventh and eighth give B (W) N-by-K, the
 "为什么 GEMM 重要"). B (W) of the transposed forms is drawn in its N-by-K shape.
 The ninth runs C1's 256-cubed product 256 times as one strided batch (page
 "GEMM 优化详解", section "矩阵大小选择策略": small matrices are batched); its
-operands are drawn as (batch, rows, cols) tensors.
+operands are drawn as (batch, rows, cols) tensors. The tenth and eleventh are
+one GPU's share of the 4096-cubed product and of the fully-connected layer
+split eight ways; the twelfth a 16-bit product of 144 256-square tiles. The
+thirteenth and fourteenth are the fully-connected layer with one and four
+rows of X: by the intensity formula of page "GEMM 优化详解" (table
+"计算复杂度分析"), 2MNK / (MK + KN + MN) / 4, they do about M/2 FLOP per byte,
+far below the ridge, so HBM bounds them and the bench rates them in GB/s.
 """
 from __future__ import annotations
 
@@ -46,11 +52,21 @@ class Workload:
     act: int = 1        # linear only: 0 none, 1 ReLU
     scale: float = 1.0  # operand scale (linear: 1/64)
     batch: int = 1      # strided batch of independent products (batched kinds)
+    bound: str = "mfma"  # the roofline that bounds it: "mfma", or "hbm" for a few rows of A
     extra: dict = field(default_factory=dict)
 
     @property
     def flops(self) -> int:
         return 2 * self.M * self.N * self.K * self.batch
+
+    @property
+    def hbm_bytes(self) -> int:
+        """Compulsory HBM bytes of one call: A, B and the bias read once, C
+        read (beta != 0) and written once."""
+        esize = 2 if self.kind in HALF_KINDS else 4
+        rw_c = 2 if self.beta != 0.0 else 1
+        bias = 4 * self.N if self.kind in ("linear", "linear_nt") else 0
+        return self.batch * (esize * (self.M * self.K + self.K * self.N) + 4 * rw_c * self.M * self.N) + bias
 
 
 WORKLOADS = {
@@ -78,6 +94,13 @@ WORKLOADS = {
     # a 16-bit product whose 256x256 tiles (144) would leave CUs idle; it runs
     # on 192x192 tiles, one per CU
     "gemm_f16f32_3072": Workload(12, "gemm_f16f32_3072", "gemm_f16f32", 3072, 3072, 3072),
+    # the fully-connected layer's weight with a handful of input rows (one
+    # token's decode through the [out][in] weight, four rows through the
+    # [in][out] one): bound by reading the weight from HBM, not by the MFMAs
+    "linear_relu_nt_1x4096x11008": Workload(13, "linear_relu_nt_1x4096x11008", "linear_nt", 1, 11008, 4096,
+                                            act=1, scale=1.0 / 64.0, bound="hbm"),
+    "linear_relu_4x4096x11008": Workload(14, "linear_relu_4x4096x11008", "linear", 4, 11008, 4096,
+                                         act=1, scale=1.0 / 64.0, bound="hbm"),
 }
 
 HALF_KINDS = ("gemm_f16f32", "gemm_bf16f32", "gemm_f16f32_nt")

@@ -59,6 +59,24 @@ def test_one_json_line_with_every_field(workload):
 
 @pytest.mark.gpu
 @pytest.mark.skipif(not _has_gpu(), reason="needs a GPU")
+def test_memory_bound_workload_rates_hbm_bytes():
+    """A decode-sized layer (one row of X) is rated against the HBM peak: its
+    compulsory bytes per call over the average call time, in GB/s."""
+    workload = "linear_relu_nt_1x4096x11008"
+    r = run_bench("--workload", workload, "--steps", "5", "--warmup", "2", "--cpu-seconds", "0.2")
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads([l for l in r.stdout.splitlines() if l.strip()][0])
+    rl = d["roofline"]
+    assert rl["bound"] == "hbm" and rl["unit"] == "GB/s" and rl["peak"] == 8000.0
+    # X 4096, W 4096 x 11008 and the bias read, Y written, 4 bytes each
+    assert rl["bytes_per_launch"] == 4 * (4096 + 4096 * 11008 + 11008 + 11008)
+    assert abs(rl["achieved"] - rl["bytes_per_launch"] / (rl["kernel_avg_ms"] * 1e-3) / 1e9) < 1.0
+    assert 0 < rl["frac"] <= 1
+    assert d["config"]["tile"].endswith("_skinny")
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not _has_gpu(), reason="needs a GPU")
 def test_default_run_reports_every_configuration():
     """The default run (the 4096^3 headline) also reports the 256^3, 1024^3
     alpha/beta, fused-layer and FP16 8192^3 configurations, each with its time
