@@ -807,8 +807,9 @@ gemm_f32_direct_kernel(GemmParams p)
 // forced plan, is walked in chunks of that size). B streams from HBM with
 // the next loads issued before the current ones are used.
 //   B given K-by-N: lane l covers columns 4l .. 4l+3 (one 16-byte load per
-//     k-row); wave w takes the runs of U k-rows numbered w mod 4; A's values
-//     are LDS broadcasts; the four waves' sums meet in LDS at the end.
+//     k-row); wave w takes the runs of U k-rows numbered w mod 4, split y
+//     starting at run y mod runs and wrapping around; A's values are LDS
+//     broadcasts; the four waves' sums meet in LDS at the end.
 //   B given N-by-K: wave w covers columns 64w .. 64w+63 in 16 groups of four;
 //     in a group, lane l reads column 4g + l/16's row of B at k-values
 //     4(l%16) + 64j, so a load covers 64 consecutive k of four rows; the 16
@@ -906,7 +907,14 @@ __global__ void __launch_bounds__(256) gemm_f32_skinny_kernel(GemmParams p)
                 skinny_stage<MR>(xs, A, p.lda, mc, M, kc, kn);
                 __syncthreads();
                 const float *Bc = B + kc * p.ldb + ncol;
+                const int runs = (kn + 4 * U - 1) / (4 * U);   // runs of all four waves
+                // the K-splits walk their runs from different starting points, so
+                // that the splits in flight do not read rows a multiple of the
+                // split length apart (a power-of-two stride in common shapes)
+                const int rot = (int)(blockIdx.y % (unsigned)runs);
                 auto fetch = [&](f32x4 (&w)[U], int run) {
+                    run += rot;
+                    run = run >= runs ? run - runs : run;
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int k = (4 * run + wave) * U + u;
@@ -922,13 +930,13 @@ __global__ void __launch_bounds__(256) gemm_f32_skinny_kernel(GemmParams p)
                         w[u] = v;
                     }
                 };
-                const int runs = (kn + 4 * U - 1) / (4 * U);   // runs of all four waves
                 f32x4 wc[U], wn[U];
                 fetch(wc, 0);
                 for (int r = 0; r < runs; ++r) {
                     if (r + 1 < runs)
                         fetch(wn, r + 1);
-                    const int k0 = (4 * r + wave) * U;   // within KC: KC is a multiple of 4U
+                    const int rr = r + rot < runs ? r + rot : r + rot - runs;
+                    const int k0 = (4 * rr + wave) * U;   // within KC: KC is a multiple of 4U
 #pragma unroll
                     for (int m = 0; m < MR; ++m) {
 #pragma unroll
