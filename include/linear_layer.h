@@ -287,6 +287,14 @@ const char *ll_status_string(int status);
  * small to fill the device (e.g. 1024^3), and the automatic choice takes them
  * only when each slice gets at least 8 stages (a forced tile is always used).
  *
+ * Single FP32 products with a few rows of A (at most 4, or at most 8 when B
+ * holds at least 2^25 values) are bound by reading B from HBM, not by the
+ * matrix units (page "GEMM 优化详解", table "计算复杂度分析": the intensity
+ * 2MNK / (MK + KN + MN) / 4 is about M/2 FLOP per byte). They take the tile
+ * f32_16x256_skinny: vector FMAs over 256 columns of C per workgroup with
+ * A's rows staged in LDS, and up to 64 K-splits (added atomically, framed by
+ * the same passes as above). Forced on more rows it walks them 16 at a time.
+ *
  * The calls below report the choice; they touch only host memory and never
  * the GPU. (linear_layer_tuning.h declares process-wide overrides of the
  * choice for benchmarks and tests.)
@@ -296,8 +304,8 @@ const char *ll_status_string(int status);
 /* Flags the ll_chosen_* queries accept OR-ed into `dtype`:
  * LL_PLAN_RELU: linear_bias_act with the ReLU, whose K-split and stream-K
  * plans pay for one more pass over Y (LL_DTYPE_F32 only);
- * LL_PLAN_B_NK: the _nt form (B given N-by-K; accepted for callers that
- * describe the call fully, the plans do not currently depend on it);
+ * LL_PLAN_B_NK: the _nt form (B given N-by-K; only the skinny kernel's
+ * K-split count depends on it);
  * LL_PLAN_UNALIGNED: operands that do not allow the 128-bit-load kernels
  * (a base not 16-byte aligned, or a leading dimension, K or N not a multiple
  * of 4 (fp32) or 8 (16-bit)): no stream-K, and the tiles that exist only as
