@@ -203,6 +203,26 @@ double wg_cost(const TileInfo &t, int64_t wgs, double work, int cus)
     return pairs * 2.0 * work / t.eff_paired + single * work / t.eff_alone;
 }
 
+// A K-sliced tile's cost factor at a K range of k values per workgroup,
+// relative to its measured rate (eff_alone at k_ref): each of its KS slices
+// walks k/KS values and its pipeline fill and drain cost about kFillK of
+// them, so the rate scales as x / (x + kFillK) with x = k/KS, up to the
+// tile's eff_max. Fitted to FP32 products of 128 to 512 rows on MI355X (e.g.
+// 512 x 2048 x 2048: 37.8 us on 64x64 in four slices against 52.8 on 128x128
+// in two slices split four ways, which K-independent rates ranked the other
+// way round).
+constexpr double kFillK = 128.0;
+double k_factor(const TileInfo &t, double k)
+{
+    if (t.k_ref <= 0 || k <= 0.0)
+        return 1.0;
+    const double x = k / t.k_slices, r = (double)t.k_ref / t.k_slices;
+    const double cap = t.eff_max > 0.0f ? t.eff_max : t.eff_alone;
+    double rate = t.eff_alone * (x / (x + kFillK)) / (r / (r + kFillK));
+    rate = rate < cap ? rate : cap;
+    return t.eff_alone / rate;
+}
+
 struct Plan {
     int tile;
     int splits;
@@ -301,7 +321,8 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
                 if (splits != s && s_ov < 1)
                     continue;   // the same partition is reached with fewer splits
             }
-            double cost = wg_cost(ti, tiles_mn * splits * items, (double)ti.bm * ti.bn * k_split, cus);
+            double cost = wg_cost(ti, tiles_mn * splits * items,
+                                  (double)ti.bm * ti.bn * k_split * k_factor(ti, k_split), cus);
             if (splits > 1) {
                 const double mn = (double)M * N * items;
                 const double bytes = 8.0 * mn * (relu ? 2 : 1) + 4.0 * mn * splits;
@@ -326,8 +347,9 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
                 const int64_t grid = rest * units < slots ? rest * units : slots;
                 const int64_t per_wg = (rest * units + grid - 1) / grid;
                 const double work = (double)ti.bm * ti.bn * K;
-                double cost = rounds > 0 ? wg_cost(ti, rounds * slots, work, cus) : 0.0;
-                cost += wg_cost(ti, grid, work * (double)per_wg / (double)units, cus);
+                double cost = rounds > 0 ? wg_cost(ti, rounds * slots, work * k_factor(ti, K), cus) : 0.0;
+                cost += wg_cost(ti, grid, work * (double)per_wg / (double)units *
+                                              k_factor(ti, (double)per_wg * kSkUnit), cus);
                 // atomics: one partial tile per segment (at most grid + rest of
                 // them); passes: the prepare write and, for ReLU, a read and write
                 const double area = 4.0 * ti.bm * ti.bn;

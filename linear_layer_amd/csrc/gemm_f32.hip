@@ -1200,6 +1200,12 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // {BM, BN, workgroups per CU, relative throughput alone on a CU, with a
 // second workgroup beside it} -- throughputs measured on MI355X relative to
 // the 256x256 tile.
+// For the K-sliced tiles, the last two fields are the K per workgroup of
+// those measurements and the rate they reach at long K ranges: each slice
+// walks K/KS values with its own pipeline fill and drain, so their rates
+// depend on K (64x64 in four slices: 0.57 at K = 1024, 0.72 at 2048, 0.78
+// at 4096; 128x128 in two: 0.69 at 512, 0.75 at 1024, 0.90 at 2048, no
+// higher at 4096). The other tiles' rates stand at any K.
 const TileInfo kF32Tiles[kF32NumTiles] = {
     {F32_L::BM, F32_L::BN, 1, 1.00f, 1.00f, "f32_256x256", 1, true, 64 * WaveGridL<false>::M * WaveGridL<false>::N},
     {F32_M::BM, F32_M::BN, 2, 0.89f, 0.985f, "f32_256x128"},
@@ -1210,8 +1216,8 @@ const TileInfo kF32Tiles[kF32NumTiles] = {
     // each only when every slice gets at least 8 stages of 32 (smaller K: the
     // partial-sum exchange costs more than the slices save; 256^3 8.9 us with
     // slices against 8.3 plain, 512^3 11.1 against 10.3 split across workgroups).
-    {F32_XS::BM, F32_XS::BN, 1, 0.57f, 0.57f, "f32_64x64_k4", 4, true, 1024, 4 * 8 * 32, true},
-    {F32_S::BM, F32_S::BN, 1, 0.90f, 0.90f, "f32_128x128_k2", 2, true, 512, 2 * 8 * 32, true},
+    {F32_XS::BM, F32_XS::BN, 1, 0.57f, 0.57f, "f32_64x64_k4", 4, true, 1024, 4 * 8 * 32, true, 1024, 0.80f},
+    {F32_S::BM, F32_S::BN, 1, 0.90f, 0.90f, "f32_128x128_k2", 2, true, 512, 2 * 8 * 32, true, 2048},
     // the skinny kernel: 16 rows of A at a time, 256 columns per workgroup
     {16, SK_COLS, 2, 1.0f, 1.0f, "f32_16x256_skinny", 1, false},
 };

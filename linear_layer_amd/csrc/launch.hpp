@@ -18,6 +18,8 @@ struct TileInfo {
     int threads = 256;     // largest workgroup of the tile's kernels
     int min_k = 0;         // K-sliced tiles: the K below which slices get too few stages
     bool direct_only = false;  // only the 128-bit-load kernels have this shape
+    int k_ref = 0;         // K per workgroup at which eff_* were measured (0: rates independent of K)
+    float eff_max = 0.0f;  // the highest rate at longer K ranges (0: eff_alone)
 };
 
 constexpr int kF32NumTiles = 7;

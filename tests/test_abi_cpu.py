@@ -215,6 +215,16 @@ def test_tile_choice():
         ll.set_stream_k(-1)
     with pytest.raises(ll.LinearLayerError):
         ll.set_stream_k(2)
+    # the K-sliced tiles' rates depend on the K each slice walks: 64x64 in
+    # four slices over the whole of K = 2048 or 4096 (its slices long enough),
+    # but not split 16 ways over K = 1024 or 2048 (64 or 32 k-values per
+    # slice), where the plain 64x64 tile runs the splits
+    assert choice(f32, 512, 2048, 2048) == ("f32_64x64_k4", 1)
+    assert choice(f32, 256, 4096, 4096) == ("f32_64x64_k4", 1)
+    assert choice(f32, 1024, 64, 1024) == ("f32_64x64", 16)
+    assert choice(f32, 512, 128, 2048) == ("f32_64x64", 16)
+    assert choice(f32, 2048, 2048, 2048) == ("f32_128x128_k2", 1)
+    assert choice(f32, 1024, 1024, 1024) == ("f32_64x64_k4", 1)
     assert choice(f16, 8192, 8192, 8192) == ("f16_256x256_direct", 1)
     # 16-bit: 6144^2 is 576 tiles of 256x256, 2.25 rounds: two run whole, 64
     # tiles are shared out; 3072^2 is 256 tiles of 192x192, one full round
