@@ -545,14 +545,21 @@ gemm_f16_direct_kernel(GemmParams p)
     };
     // The MFMA groups raise the wave's issue priority (s_setprio), so a wave
     // with MFMAs ready wins the arbitration over its SIMD's other wave while
-    // that one issues reads and copies (measured about +1 %).
+    // that one issues reads and copies (measured about +1 %). They walk the
+    // blocks row by row in alternating column order, so that consecutive
+    // MFMAs always share an operand: fewer operand bits change from one to
+    // the next, and the chip, power-limited at this precision, keeps a higher
+    // clock (8192^3: +1.3 to 1.6 % fp16, +0.8 to 1.2 % bf16, bit-identical
+    // results; columns outermost instead measured no gain).
     auto mfma_step = [&](const f16x8 (&af)[FM], const f16x8 (&bf)[FN]) {
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int j = 0; j < FN; ++j) {
+                const int fn = (fm & 1) ? FN - 1 - j : j;
                 acc[fm][fn] = mma16<BF16>(af[fm], bf[fn], acc[fm][fn]);
+            }
         __builtin_amdgcn_s_setprio(0);
     };
 
@@ -613,8 +620,10 @@ gemm_f16_direct_kernel(GemmParams p)
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int j = 0; j < FN; ++j) {   // the same alternating order
+                const int fn = (fm & 1) ? FN - 1 - j : j;
                 acc[fm][fn] = mma16<BF16>(fa[1][fm], fb[1][fn], acc[fm][fn]);
+            }
             if (refill && fm < CROWS) {
 #pragma unroll
                 for (int g = 0; g < G; ++g)
