@@ -287,6 +287,10 @@ const char *ll_status_string(int status);
  * small to fill the device (e.g. 1024^3), and the automatic choice takes them
  * only when each slice gets at least 8 stages (a forced tile is always used).
  *
+ * FP32 products of at most 32 rows of A may take f32_32x128: two-wave
+ * workgroups of 32x128, up to four per CU, for the rows that the 64-row
+ * tiles would mostly pad.
+ *
  * Single FP32 products with a few rows of A (at most 4, or at most 8 when B
  * holds at least 2^25 values) are bound by reading B from HBM, not by the
  * matrix units (page "GEMM 优化详解", table "计算复杂度分析": the intensity
@@ -309,8 +313,8 @@ const char *ll_status_string(int status);
  * LL_PLAN_UNALIGNED: operands that do not allow the 128-bit-load kernels
  * (a base not 16-byte aligned, or a leading dimension, K or N not a multiple
  * of 4 (fp32) or 8 (16-bit)): no stream-K, and the tiles that exist only as
- * 128-bit-load kernels (the K-sliced ones and f16_192x192_direct) are not
- * chosen automatically. */
+ * 128-bit-load kernels (the K-sliced ones, f32_32x128 and f16_192x192_direct)
+ * are not chosen automatically. */
 #define LL_PLAN_RELU 0x100
 #define LL_PLAN_B_NK 0x200
 #define LL_PLAN_UNALIGNED 0x400

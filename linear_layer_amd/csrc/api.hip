@@ -194,16 +194,28 @@ constexpr double kPassUs = 5.0, kReluPassUs = 3.0;
 // ceil(wgs/CUs). With one workgroup per CU they run one after another at
 // eff_alone; with two they run in pairs at eff_paired (a pair takes twice a
 // workgroup's work), and an odd last one runs alone.
+// A tile of more than two workgroups per CU (the two-wave 32x128 tile) runs
+// up to wg_per_cu of them side by side in rounds; a round of r takes as long
+// as one workgroup alone (eff_alone: each is bound by its own latency) or as
+// r at the CU's full rate (eff_paired), whichever is longer.
 double wg_cost(const TileInfo &t, int64_t wgs, double work, int cus)
 {
     const int64_t per_cu = (wgs + cus - 1) / cus;
+    if (t.wg_per_cu > 2) {
+        const int64_t full = per_cu / t.wg_per_cu, last = per_cu % t.wg_per_cu;
+        const auto round = [&](int64_t r) {
+            const double alone = work / t.eff_alone, shared = (double)r * work / t.eff_paired;
+            return alone > shared ? alone : shared;
+        };
+        return (double)full * round(t.wg_per_cu) + (last > 0 ? round(last) : 0.0);
+    }
     if (t.wg_per_cu <= 1 || per_cu == 1)
         return per_cu * work / t.eff_alone;
     const int64_t pairs = per_cu / 2, single = per_cu % 2;
     return pairs * 2.0 * work / t.eff_paired + single * work / t.eff_alone;
 }
 
-// A K-sliced tile's cost factor at a K range of k values per workgroup,
+// A K-sliced tile's (or the 32x128 tile's) cost factor at a K range of k values per workgroup,
 // relative to its measured rate (eff_alone at k_ref): each of its KS slices
 // walks k/KS values and its pipeline fill and drain cost about kFillK of
 // them, so the rate scales as x / (x + kFillK) with x = k/KS, up to the
@@ -297,6 +309,8 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
     for (int t = 0; t < ntiles; ++t) {
         if ((t_ov >= 0 && t != t_ov) || (dtype == LL_DTYPE_F32 && t == kSkinnyTile))
             continue;
+        if (dtype == LL_DTYPE_F32 && t == kThinTile && M > tiles[t].bm && t_ov != t)
+            continue;   // a second row of 32x128 tiles reads B again
         const TileInfo &ti = tiles[t];
         const int64_t tiles_mn = (int64_t)cdiv(M, ti.bm) * cdiv(N, ti.bn);
         if (tiles_mn > max_grid_x(ti.threads))
@@ -320,6 +334,8 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
                 splits = (int)(((int64_t)K + k_split - 1) / k_split);
                 if (splits != s && s_ov < 1)
                     continue;   // the same partition is reached with fewer splits
+                if (dtype == LL_DTYPE_F32 && t == kThinTile && k_split < kThinMinSplit && s_ov < 1)
+                    break;      // 32x128 splits shorter than this measured slower than 64x64
             }
             double cost = wg_cost(ti, tiles_mn * splits * items,
                                   (double)ti.bm * ti.bn * k_split * k_factor(ti, k_split), cus);

@@ -1200,10 +1200,10 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // {BM, BN, workgroups per CU, relative throughput alone on a CU, with a
 // second workgroup beside it} -- throughputs measured on MI355X relative to
 // the 256x256 tile.
-// For the K-sliced tiles, the last two fields are the K per workgroup of
-// those measurements and the rate they reach at long K ranges: each slice
-// walks K/KS values with its own pipeline fill and drain, so their rates
-// depend on K (64x64 in four slices: 0.57 at K = 1024, 0.72 at 2048, 0.78
+// For the K-sliced tiles (and the 32x128 one), the last two fields are the K
+// per workgroup of those measurements and the rate they reach at long K
+// ranges: each slice walks K/KS values with its own pipeline fill and drain,
+// so their rates depend on K (64x64 in four slices: 0.57 at K = 1024, 0.72 at 2048, 0.78
 // at 4096; 128x128 in two: 0.69 at 512, 0.75 at 1024, 0.90 at 2048, no
 // higher at 4096). The other tiles' rates stand at any K.
 const TileInfo kF32Tiles[kF32NumTiles] = {
@@ -1220,6 +1220,15 @@ const TileInfo kF32Tiles[kF32NumTiles] = {
     {F32_S::BM, F32_S::BN, 1, 0.90f, 0.90f, "f32_128x128_k2", 2, true, 512, 2 * 8 * 32, true, 2048},
     // the skinny kernel: 16 rows of A at a time, 256 columns per workgroup
     {16, SK_COLS, 2, 1.0f, 1.0f, "f32_16x256_skinny", 1, false},
+    // 32x128 for a few tens of rows of A (direct kernel only): two waves per
+    // workgroup, up to four workgroups per CU. A few per CU each run at about
+    // the same speed (16x4096x4096 in 16 K-splits: 2 per CU, 16.8 us of
+    // kernel); four fill the CU at about 0.70 (16x11008x4096 in 11 splits,
+    // 27.7 us; 2048x2048x1024, 80 us). Its rate was measured at K = 256 per
+    // workgroup and falls with shorter ranges as the K-sliced tiles' do
+    // (32x8192x1024 in 16 splits, 64 k-values each: 21 us against 16 on
+    // 64x64 in 4).
+    {32, 128, 4, 0.185f, 0.70f, "f32_32x128", 1, false, 128, 0, true, 256, 0.21f},
 };
 #endif
 
@@ -1251,6 +1260,39 @@ static hipError_t launch_skinny(const GemmParams &p0, int epi, hipStream_t s)
     return hipGetLastError();
 }
 
+// The 32-row tile (a few tens of rows of A): 32x128, two waves of 32x64, no
+// stream-K. Direct kernel only; unaligned operands run the staged 64x64
+// kernel instead.
+template <bool BT>
+static hipError_t launch_thin(const GemmParams &p0, int epi, bool vec, hipStream_t s)
+{
+    if (!vec)
+        return launch_t<F32_XS, 2, BT>(p0, epi, vec, s);
+    GemmParams p = p0;
+    p.tiles_m = cdiv(p.M, 32);
+    p.tiles_n = cdiv(p.N, 128);
+    const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (ntiles > max_grid_x(128) || p.batch < 1 || p.batch > kMaxGridZ || p.sk_tiles != 0 || p.grid_x != 0)
+        return hipErrorInvalidValue;
+    const dim3 grid = gemm_grid(p, ntiles), block(128);
+    const int chk = launch_checks(p, 32, 128, 32, 1);
+#define LL_THIN_C(E, C) \
+    hipLaunchKernelGGL((gemm_f32_direct_kernel<E, 32, 128, 32, 2, 2, 1, 2, 1, BT, false, C>), grid, block, 0, s, p)
+#define LL_THIN(E) \
+    do { \
+        if (chk == 0) LL_THIN_C(E, 0); \
+        else if (chk == CHK_M) LL_THIN_C(E, CHK_M); \
+        else LL_THIN_C(E, CHK_M | CHK_N | CHK_K); \
+    } while (0)
+    if (epi == EPI_GEMM_BETA0) LL_THIN(EPI_GEMM_BETA0);
+    else if (epi == EPI_GEMM_BETA) LL_THIN(EPI_GEMM_BETA);
+    else if (epi == EPI_LINEAR) LL_THIN(EPI_LINEAR);
+    else LL_THIN(EPI_ATOMIC);
+#undef LL_THIN
+#undef LL_THIN_C
+    return hipGetLastError();
+}
+
 template <bool BT>
 static hipError_t launch_f32(const GemmParams &p, int tile, int epi, bool vec, hipStream_t s)
 {
@@ -1261,6 +1303,7 @@ static hipError_t launch_f32(const GemmParams &p, int tile, int epi, bool vec, h
     case 3: return launch_t<F32_XS, 2, BT>(p, epi, vec, s);
     case 4: return launch_t<F32_XS, 2, BT, 4>(p, epi, vec, s);
     case 5: return launch_t<F32_S, 2, BT, 2>(p, epi, vec, s);
+    case 7: return launch_thin<BT>(p, epi, vec, s);
     default: return launch_skinny<BT>(p, epi, s);
     }
 }

@@ -22,7 +22,7 @@ struct TileInfo {
     float eff_max = 0.0f;  // the highest rate at longer K ranges (0: eff_alone)
 };
 
-constexpr int kF32NumTiles = 7;
+constexpr int kF32NumTiles = 8;
 // The FP32 tile that is the skinny kernel (vector FMAs for a few rows of A;
 // planned by rule, not by the MFMA tiles' cost model) and its column width.
 // It is chosen automatically for at most kSkinnyMaxM rows of A, and for up
@@ -32,6 +32,13 @@ constexpr int kF32NumTiles = 7;
 // slower with a 4096 x 4096 one (its K-splits' atomic sums and short ranges
 // cost more there than the vector FMAs save); past 8 rows the MFMA tiles win.
 constexpr int kSkinnyTile = 6, kSkinnyCols = 256, kSkinnyMaxM = 4, kSkinnyMaxMLarge = 8;
+// The 32x128 tile: chosen automatically only when one row of its tiles covers
+// M (more rows read B once per row of tiles; from 40 rows on, 64x64 measured
+// faster) ...
+constexpr int kThinTile = 7;
+// ... and split only into K ranges of at least this many values
+// (32x8192x2048 in 16 splits of 128: 30 us against 25 on 64x64 in 4).
+constexpr int kThinMinSplit = 256;
 constexpr int64_t kSkinnyLargeKN = (int64_t)1 << 25;
 // Floats of A the skinny kernel stages in LDS at once, its rows per pass
 // for a product of M rows (the fewest of 1, 4, 8, 16 that cover M), and so the

@@ -178,9 +178,11 @@ def test_plans_at_int32_limits():
     assert ll.tile_name(f32, t) == "f32_256x128"          # 8.4M tiles of 256 threads
     assert ll.chosen_tile(f16, big - 512, 1, 1, 256) == 1   # 128x128: 16.8M tiles
     # a single row of 2^31 - 1 columns: 8.4M skinny workgroups fit one launch;
-    # 17 rows are past the skinny kernel, and no MFMA tile's grid fits
+    # 17 rows: 16.8M workgroups of the two-wave 32x128 tile; 33 rows are past
+    # both, and no 64-row tile's grid fits
     assert ll.tile_name(f32, ll.chosen_tile(f32, 1, big, 1, 256)) == "f32_16x256_skinny"
-    for dt, shape in ((f32, (17, big, 1)), (f16, (big, 64, 64)), (f16, (1, big, 1))):
+    assert ll.tile_name(f32, ll.chosen_tile(f32, 17, big, 1, 256)) == "f32_32x128"
+    for dt, shape in ((f32, (33, big, 1)), (f16, (big, 64, 64)), (f16, (1, big, 1))):
         assert ll.chosen_tile(dt, *shape, 256) == -1
         assert ll.chosen_split_k(dt, *shape, 256) == -1
         assert ll.chosen_stream_k(dt, *shape, 256) == -1
