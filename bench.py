@@ -100,11 +100,37 @@ def copy_calibration(steps: int):
                       "GB_per_s": round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def code_text(src: str) -> str:
+    """C++ source without its comments and blank lines or trailing spaces, so
+    that the hash below follows the code, not its commentary. String and
+    character literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            while i < n and src[i] != "\n":
+                i += 1
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(l.rstrip() for l in "".join(out).splitlines() if l.strip())
+
+
 def kernel_hash(kind: str) -> str:
+    """Hash of the code (comments aside) of the kernels and planner of a kind."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "linear_layer_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "linear_layer_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

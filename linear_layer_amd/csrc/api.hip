@@ -215,11 +215,11 @@ double wg_cost(const TileInfo &t, int64_t wgs, double work, int cus)
     return pairs * 2.0 * work / t.eff_paired + single * work / t.eff_alone;
 }
 
-// A K-sliced tile's (or the 32x128 tile's) cost factor at a K range of k values per workgroup,
-// relative to its measured rate (eff_alone at k_ref): each of its KS slices
-// walks k/KS values and its pipeline fill and drain cost about kFillK of
-// them, so the rate scales as x / (x + kFillK) with x = k/KS, up to the
-// tile's eff_max. Fitted to FP32 products of 128 to 512 rows on MI355X (e.g.
+// The cost factor of a K-sliced tile (or of the 32x128 tile) at a K range of
+// k values per workgroup, relative to its measured rate (eff_alone at
+// k_ref): each of its KS slices walks k/KS values and its pipeline fill and
+// drain cost about kFillK of them, so the rate scales as x / (x + kFillK)
+// with x = k/KS, up to the tile's eff_max. Fitted to FP32 products of 128 to 512 rows on MI355X (e.g.
 // 512 x 2048 x 2048: 37.8 us on 64x64 in four slices against 52.8 on 128x128
 // in two slices split four ways, which K-independent rates ranked the other
 // way round).
@@ -250,16 +250,6 @@ bool sk_tile_ok(const TileInfo &ti)
     return ti.stream_k && ti.k_slices == 1;
 }
 
-// Choose the tile shape and the number of K-splits minimising the estimate:
-// big tiles for big problems; smaller ones, or several workgroups along K
-// whose partial sums are added atomically into C, when big tiles would leave
-// CUs idle (wave quantisation). This is the size-dependent choice of page
-// "GEMM 优化详解", section "矩阵大小选择策略", re-derived for 256 CUs.
-// A split costs a pre-pass over C (beta*C, or the bias), the atomic traffic of
-// every split's partial tile and, for ReLU, a pass afterwards. `vec`: the
-// operands allow the 128-bit-load kernels; without it the tiles that exist
-// only as direct kernels (whose calls would run a staged kernel of another
-// shape) and stream-K are not considered, unless a tile is forced.
 // The skinny FP32 kernel (a few rows of A, memory-bound): one workgroup per
 // 256 columns and K-split. The K-splits give about two workgroups per CU (B
 // given K-by-N) or three (N-by-K, whose waves stream fewer bytes at a time),
@@ -288,6 +278,16 @@ Plan skinny_plan(int M, int N, int K, int cus, int s_ov, bool bt)
     return Plan{kSkinnyTile, (int)(((int64_t)K + k_split - 1) / k_split), k_split, 0, 0};
 }
 
+// Choose the tile shape and the number of K-splits minimising the estimate:
+// big tiles for big problems; smaller ones, or several workgroups along K
+// whose partial sums are added atomically into C, when big tiles would leave
+// CUs idle (wave quantisation). This is the size-dependent choice of page
+// "GEMM 优化详解", section "矩阵大小选择策略", re-derived for 256 CUs.
+// A split costs a pre-pass over C (beta*C, or the bias), the atomic traffic of
+// every split's partial tile and, for ReLU, a pass afterwards. `vec`: the
+// operands allow the 128-bit-load kernels; without it the tiles that exist
+// only as direct kernels (whose calls would run a staged kernel of another
+// shape) and stream-K are not considered, unless a tile is forced.
 Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int cus, bool relu,
           int batch, bool vec, bool bt)
 {

@@ -16,6 +16,21 @@ def run_bench(*args, timeout=300):
                           capture_output=True, text=True, timeout=timeout)
 
 
+def test_kernel_hash_follows_code_not_comments():
+    """The source hash that ties the committed traffic counters to the kernels
+    ignores comments, blank lines and trailing spaces, keeps string literals
+    (comment markers inside them included), and changes with the code."""
+    sys.path.insert(0, ROOT)
+    import bench
+    a = 'int f() { return 1; } // one\n/* block\n comment */\nconst char *s = "a // b /* c */";\n'
+    b = '// other words\nint f() { return 1; }\n\nconst char *s = "a // b /* c */";   \n'
+    assert bench.code_text(a) == bench.code_text(b)
+    assert '"a // b /* c */"' in bench.code_text(a)
+    assert bench.code_text("int x = 1;") != bench.code_text("int x = 2;")
+    assert bench.code_text("char c = '/'; // x") == "char c = '/';"
+    assert len(bench.kernel_hash("gemm_f32")) == 16
+
+
 def test_more_than_one_gpu_is_refused():
     r = run_bench("--gpus", "2", timeout=120)
     assert r.returncode != 0
