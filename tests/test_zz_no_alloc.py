@@ -2,8 +2,9 @@
 C ABI: its output against linear_bias_act_ws on the same inputs and against
 the float64 oracle, on two calls in a row (the second smaller) that share the
 library's static workspace; shapes whose plan needs more workspace than the
-static array are refused and leave Y untouched; a call on a stream of its own;
-and the call captured in a HIP graph, replayed with new inputs."""
+static array are refused and leave Y untouched; decode-sized plans (a few rows,
+K split, no workspace); a call on a stream of its own; and the call captured
+in a HIP graph, a stream-K plan and a K-split one, replayed with new inputs."""
 import ctypes
 
 import numpy as np
@@ -134,6 +135,21 @@ def test_small_and_whole_tile_plans(shape, act, with_bias, auto_plan):
     check(f"{M}x{N}x{K}", X, W, b, act, False, False)
 
 
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("w_trans", [False, True])
+def test_decode_sized_plans(M, w_trans, auto_plan):
+    """A few rows against the 4096 x 11008 weight: the skinny kernel (1 and 4
+    rows) or the 32x128 tile (16 rows) with K split over the CUs, so bias
+    fill, atomic partial sums and ReLU pass, and no workspace."""
+    N, K = 11008, 4096
+    flags = F32 | ll.PLAN_RELU | (ll.PLAN_B_NK if w_trans else 0)
+    assert ll.tile_name(F32, ll.chosen_tile(flags, M, N, K, cus())) == (
+        "f32_16x256_skinny" if M <= 4 else "f32_32x128")
+    assert ll.chosen_split_k(flags, M, N, K, cus()) > 1
+    X, W, b = wl.uniform((M, K), 321, 0.125), wl.uniform((K, N), 322, 0.125), wl.bias_uniform(N, 323)
+    assert check(f"decode {M} rows w_trans={w_trans}", X, W, b, 1, w_trans, False) == 0
+
+
 def test_too_large_is_refused(auto_plan):
     """A shape whose plan needs more than the usable static workspace is
     refused with LL_ERR_INVALID_VALUE before anything runs: Y keeps its NaNs.
@@ -249,4 +265,41 @@ def test_graph_capture_replays(auto_plan):
         R, _ = oracle.linear(np32(X), np32(Wh), np32(b), 1)
         assert np.array_equal(got, R.astype(np.float32)), f"replay {rep}: differs from the oracle"
         assert int(torch.count_nonzero(ws)) == 0
+    del g
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_graph_capture_replays_split_plan(M, auto_plan):
+    """A decode-sized call (a few rows against the 4096 x 11008 weight: bias
+    fill, K-split atomics and ReLU pass, three launches) captured in a graph
+    and replayed three times with new integer inputs; every replay bit-exact
+    against the oracle."""
+    N, K = 11008, 4096
+    assert ll.chosen_split_k(F32 | ll.PLAN_RELU, M, N, K, cus()) > 1
+    Xd = torch.empty((M, K), device=DEV)
+    Wd = torch.empty((K, N), device=DEV)
+    bd = torch.empty((N,), device=DEV)
+    Y = torch.empty((M, N), device=DEV)
+    Xd.zero_(); Wd.zero_(); bd.zero_()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # first call outside the capture: device set-up
+        ll.linear_bias_act_noalloc(Xd, Wd, bd, 1, Y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ll.linear_bias_act_noalloc(Xd, Wd, bd, 1, Y)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        X = wl.integers((M, K), 360 + rep, -2, 2)
+        Wh = wl.integers((K, N), 370 + rep, -2, 2)
+        b = wl.integers((N,), 380 + rep, -4, 4)
+        Xd.copy_(X); Wd.copy_(Wh); bd.copy_(b)
+        Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        R, _ = oracle.linear(np32(X), np32(Wh), np32(b), 1)
+        assert np.array_equal(np32(Y), R.astype(np.float32)), f"replay {rep}: differs from the oracle"
     del g
