@@ -891,7 +891,7 @@ __global__ void __launch_bounds__(256) gemm_f32_skinny_kernel(GemmParams p)
     const int M = p.M, N = p.N;
     const int nblk = blockIdx.x * SK_COLS;
 
-    // 64-bit chunk counters: M or K may lie within one chunk of 2^31
+    // 64-bit chunk counters and row checks: M or K may lie within one chunk of 2^31
     for (int64_t mc = 0; mc < M; mc += MR) {
         if constexpr (!BT) {
             constexpr int U = MR == 16 ? 4 : 8;   // k-rows per run (loads in flight per lane, twice)
@@ -965,12 +965,11 @@ __global__ void __launch_bounds__(256) gemm_f32_skinny_kernel(GemmParams p)
                 for (int m = 0; m < MR; ++m) {
                     const f32x4 a = acc[m] + red[m * 64 + lane] + red[(MR + m) * 64 + lane] +
                                     red[(2 * MR + m) * 64 + lane];
-                    const int row = (int)mc + m;
-                    if (row < M) {
+                    if (mc + m < M) {
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
                             if (ncol + j < N)
-                                skinny_store<EPI>(p, row, ncol + j, a[j]);
+                                skinny_store<EPI>(p, (int)mc + m, ncol + j, a[j]);
                     }
                 }
             }
@@ -1047,9 +1046,8 @@ __global__ void __launch_bounds__(256) gemm_f32_skinny_kernel(GemmParams p)
             if (col < N) {
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
-                    const int row = (int)mc + m;
-                    if (row < M)
-                        skinny_store<EPI>(p, row, col, ys[m * SK_COLS + tid]);
+                    if (mc + m < M)
+                        skinny_store<EPI>(p, (int)mc + m, col, ys[m * SK_COLS + tid]);
                 }
             }
             __syncthreads();   // ys is read before the next row block clears it
