@@ -298,6 +298,11 @@ const char *ll_status_string(int status);
  * f32_16x256_skinny: vector FMAs over 256 columns of C per workgroup with
  * A's rows staged in LDS, and up to 64 K-splits (added atomically, framed by
  * the same passes as above). Forced on more rows it walks them 16 at a time.
+ * Single 16-bit products of one row of A with B given N-by-K and holding at
+ * least 2^25 values likewise take f16_16x256_skinny_nt: dot2 instructions
+ * (two 16-bit products added into an FP32 sum) over 256 columns of C per
+ * workgroup, the same K-splits; forced with B given K-by-N, the 128x128 tile
+ * runs in its place.
  *
  * The calls below report the choice; they touch only host memory and never
  * the GPU. (linear_layer_tuning.h declares process-wide overrides of the
@@ -308,8 +313,8 @@ const char *ll_status_string(int status);
 /* Flags the ll_chosen_* queries accept OR-ed into `dtype`:
  * LL_PLAN_RELU: linear_bias_act with the ReLU, whose K-split and stream-K
  * plans pay for one more pass over Y (LL_DTYPE_F32 only);
- * LL_PLAN_B_NK: the _nt form (B given N-by-K; only the skinny kernel's
- * K-split count depends on it);
+ * LL_PLAN_B_NK: the _nt form (B given N-by-K; the FP32 skinny kernel's
+ * K-split count and the 16-bit skinny kernel's choice depend on it);
  * LL_PLAN_UNALIGNED: operands that do not allow the 128-bit-load kernels
  * (a base not 16-byte aligned, or a leading dimension, K or N not a multiple
  * of 4 (fp32) or 8 (16-bit)): no stream-K, and the tiles that exist only as

@@ -250,14 +250,15 @@ bool sk_tile_ok(const TileInfo &ti)
     return ti.stream_k && ti.k_slices == 1;
 }
 
-// The skinny FP32 kernel (a few rows of A, memory-bound): one workgroup per
-// 256 columns and K-split. The K-splits give about two workgroups per CU (B
-// given K-by-N) or three (N-by-K, whose waves stream fewer bytes at a time),
-// as measured fastest on MI355X, and keep each split within the A block the
-// kernel stages whole (skinny_kmax); at most kMaxSkinnySplits (the atomic
-// partial sums of a few rows cost little), each at least kSplitAlign long.
+// The skinny kernels (a few rows of A, memory-bound; `tile` is the FP32 or
+// the 16-bit one): one workgroup per 256 columns and K-split. The K-splits
+// give about two workgroups per CU (B given K-by-N) or three (N-by-K, whose
+// waves stream fewer bytes at a time), as measured fastest on MI355X, and
+// keep each split within the A block the kernel stages whole (kmax); at most
+// kMaxSkinnySplits (the atomic partial sums of a few rows cost little), each
+// at least kSplitAlign long.
 constexpr int kMaxSkinnySplits = 64;
-Plan skinny_plan(int M, int N, int K, int cus, int s_ov, bool bt)
+Plan skinny_plan(int tile, int kmax, int M, int N, int K, int cus, int s_ov, bool bt)
 {
     const int64_t nblk = cdiv(N, kSkinnyCols);
     if (nblk > max_grid_x(256) || nblk * kSkinnyCols > ((int64_t)1 << 31))
@@ -265,17 +266,17 @@ Plan skinny_plan(int M, int N, int K, int cus, int s_ov, bool bt)
     int64_t s = s_ov;
     if (s_ov < 1) {
         const int64_t fill = ((bt ? 3 : 2) * (int64_t)(cus > 0 ? cus : 1) + nblk - 1) / nblk;
-        const int64_t fit = ((int64_t)K + skinny_kmax(M) - 1) / skinny_kmax(M);
+        const int64_t fit = ((int64_t)K + kmax - 1) / kmax;
         const int64_t smax = ((int64_t)K + kSplitAlign - 1) / kSplitAlign;
         s = fill > fit ? fill : fit;
         s = s > kMaxSkinnySplits ? kMaxSkinnySplits : s;
         s = s > smax ? smax : s;
     }
     if (s <= 1 || K <= 0)
-        return Plan{kSkinnyTile, 1, K, 0, 0};
+        return Plan{tile, 1, K, 0, 0};
     const int k_split =
         (int)((((int64_t)K + s - 1) / s + kSplitAlign - 1) / kSplitAlign * kSplitAlign);
-    return Plan{kSkinnyTile, (int)(((int64_t)K + k_split - 1) / k_split), k_split, 0, 0};
+    return Plan{tile, (int)(((int64_t)K + k_split - 1) / k_split), k_split, 0, 0};
 }
 
 // Choose the tile shape and the number of K-splits minimising the estimate:
@@ -294,12 +295,18 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
     const int items = batch < kMaxGridZ ? batch : kMaxGridZ;   // items per launch
     const Overrides ov = load_overrides();
     const int t_ov = ov.tile[dtype], s_ov = ov.splits, sk_ov = ov.sk;
-    // single FP32 products of a few rows of A run the skinny kernel; it runs
-    // others only when forced
+    // single products of a few rows of A run a skinny kernel (FP32, or 16-bit
+    // with B given N-by-K); it runs others only when forced
     const bool skinny = M <= kSkinnyMaxM || (M <= kSkinnyMaxMLarge && (int64_t)K * N >= kSkinnyLargeKN);
     if (dtype == LL_DTYPE_F32 && (t_ov == kSkinnyTile || (t_ov < 0 && skinny && batch == 1))) {
-        const Plan sp = skinny_plan(M, N, K, cus, s_ov, bt);
+        const Plan sp = skinny_plan(kSkinnyTile, skinny_kmax(M), M, N, K, cus, s_ov, bt);
         if (sp.tile >= 0 || t_ov == kSkinnyTile)
+            return sp;
+    }
+    const bool skinny16 = M <= kSkinny16MaxM && (int64_t)K * N >= kSkinnyLargeKN && bt;
+    if (dtype != LL_DTYPE_F32 && (t_ov == kSkinny16Tile || (t_ov < 0 && skinny16 && batch == 1))) {
+        const Plan sp = skinny_plan(kSkinny16Tile, skinny16_kmax(M), M, N, K, cus, s_ov, bt);
+        if (sp.tile >= 0 || t_ov == kSkinny16Tile)
             return sp;
     }
     const bool allow_sk = vec && batch == 1 && s_ov < 1 && sk_ov != 0 && K > 0;
@@ -307,7 +314,7 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
     double best_cost = 0.0, best_sk_cost = 0.0;
     bool have = false, have_sk = false;
     for (int t = 0; t < ntiles; ++t) {
-        if ((t_ov >= 0 && t != t_ov) || (dtype == LL_DTYPE_F32 && t == kSkinnyTile))
+        if ((t_ov >= 0 && t != t_ov) || (dtype == LL_DTYPE_F32 ? t == kSkinnyTile : t == kSkinny16Tile))
             continue;
         if (dtype == LL_DTYPE_F32 && t == kThinTile && M > tiles[t].bm && t_ov != t)
             continue;   // a second row of 32x128 tiles reads B again

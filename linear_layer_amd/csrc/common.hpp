@@ -496,4 +496,34 @@ __device__ __forceinline__ void write_block16(const GemmParams &p, const f32x4 &
     write_acc<EPI, 16>(p, acc, row0, col0, lane);
 }
 
+// The skinny kernels' helpers. dpp_row_sum16: the sum of v over each row of
+// 16 lanes, in every lane of the row (quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror, row_mirror). skinny_store: one output value
+// through the epilogue (alpha*a, + beta*C, bias and ReLU, or an atomic
+// partial sum of a K-split).
+__device__ __forceinline__ float dpp_row_sum16(float v)
+{
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false));
+    return v;
+}
+
+template <int EPI>
+__device__ __forceinline__ void skinny_store(const GemmParams &p, int row, int col, float a)
+{
+    float *dst = p.C + (int64_t)row * p.ldc + col;
+    if constexpr (EPI == EPI_ATOMIC) {
+        __hip_atomic_fetch_add(dst, p.alpha * a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if constexpr (EPI == EPI_GEMM_BETA) {
+        *dst = __builtin_fmaf(p.alpha, a, p.beta * *dst);
+    } else if constexpr (EPI == EPI_LINEAR) {
+        const float y = a + (p.bias != nullptr ? p.bias[col] : 0.0f);
+        *dst = (p.act == 1 && !(y > 0.0f)) ? 0.0f : y;
+    } else {
+        *dst = p.alpha * a;
+    }
+}
+
 }  // namespace ll

@@ -732,6 +732,175 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
     return hipGetLastError();
 }
 
+// Skinny 16-bit products with B given N-by-K (a few rows of A: memory-bound,
+// so no MFMAs, which would compute a whole block of rows for every row). The
+// inner product runs on dot2 instructions: two 16-bit products added into an
+// FP32 sum per lane and instruction, the precision of the MFMA path. A
+// workgroup of four waves covers 256 columns of C over its K range (a
+// K-split), A's rows MR at a time (MR = 1, 4, 8 or 16). The A block of the K
+// range is staged raw in LDS (H16_XS values; the planner keeps the range
+// within H16_XS / MR k-values, and a longer one, from a forced plan, is
+// walked in chunks of that size). Wave w covers columns 64w .. 64w+63 in 16
+// groups of four; in a group, lane l reads column 4g + l/16's row of B at
+// k-values 8(l%16) + 128j, so one 16-byte load per lane covers 128
+// consecutive k of four rows; the 16 lanes of a row add their sums by DPP and
+// the result goes to an LDS row block of C, stored once at the end. Loads of
+// B take whole 16-byte chunks at any alignment, the chunk that crosses K
+// element by element.
+constexpr int H16_COLS = 256;     // columns of C per workgroup
+constexpr int H16_XS = 16384;     // LDS values for the staged A block (32 KiB)
+
+template <bool BF16>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    if constexpr (BF16)
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
+    else
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
+}
+
+// 16-bit values k .. k+7 of a row (zero from kn on) as one 16-byte chunk.
+__device__ __forceinline__ u32x4 h16_chunk(const uint16_t *src, int k, int kn)
+{
+    if (k + 8 <= kn)
+        return load16<u32x4>(src);
+    uint16_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        h[j] = k + j < kn ? src[j] : (uint16_t)0;
+    return __builtin_bit_cast(u32x4, h);
+}
+
+template <int EPI, bool BF16, int MR>
+__global__ void __launch_bounds__(256) gemm_h16_skinny_nt_kernel(GemmParams p)
+{
+    constexpr int KC = H16_XS / MR;   // k-values staged at once (a multiple of 128)
+    constexpr int D = MR == 16 ? 2 : 8;   // loads in flight per lane
+    __shared__ __attribute__((aligned(16))) uint16_t xs[H16_XS];
+    __shared__ float ys[MR * H16_COLS];   // this row block of C
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    select_batch(p);
+    int K;
+    const int kb = split_range(p, K);
+    const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A) + kb;
+    const uint16_t *__restrict__ B = static_cast<const uint16_t *>(p.B) + kb;
+    const int M = p.M, N = p.N;
+    const int nblk = blockIdx.x * H16_COLS;
+    const int c8 = 8 * (lane & 15), rg = lane >> 4;
+
+    // 64-bit chunk counters and row checks: M or K may lie within one chunk of 2^31
+    for (int64_t mc = 0; mc < M; mc += MR) {
+        for (int i = tid; i < MR * H16_COLS; i += 256)
+            ys[i] = 0.0f;
+        for (int64_t kc = 0; kc < K; kc += KC) {
+            const int kn = K - kc < KC ? (int)(K - kc) : KC;
+            __syncthreads();   // the previous chunk's (or row block's) A values are read
+            // rows mc .. mc+MR-1 (zero past M), k-values kc .. kc+kn-1 (zero up
+            // to kn rounded up to 128)
+            const int kq = ((kn + 127) & ~127) / 8;   // 16-byte chunks per row
+            for (int i = tid; i < MR * kq; i += 256) {
+                const int m = i / kq, k = (i % kq) * 8;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (mc + m < M)
+                    v = h16_chunk(A + (mc + m) * p.lda + kc + k, k, kn);
+                *reinterpret_cast<u32x4 *>(xs + m * KC + k) = v;
+            }
+            __syncthreads();
+            const int steps = (kn + 127) / 128;   // 128 k-values of a row per load
+            const int total = 16 * steps;         // (group, step) pairs of this wave
+            auto fetch = [&](int t) -> u32x4 {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (t >= total)
+                    return v;
+                const int g = t / steps, k = (t - g * steps) * 128 + c8;
+                const int col = nblk + 64 * wave + 4 * g + rg;
+                if (col >= N)
+                    return v;
+                return h16_chunk(B + (int64_t)col * p.ldb + kc + k, k, kn);
+            };
+            u32x4 w[D];
+#pragma unroll
+            for (int d = 0; d < D; ++d)
+                w[d] = fetch(d);
+            float acc[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                acc[m] = 0.0f;
+            int g = 0, st = 0;
+            for (int tb = 0; tb < total; tb += D) {
+#pragma unroll
+                for (int d = 0; d < D; ++d) {
+                    if (tb + d < total) {
+                        const int k0 = st * 128 + c8;   // within KC: KC is a multiple of 128
+#pragma unroll
+                        for (int m = 0; m < MR; ++m) {
+                            const u32x4 x = *reinterpret_cast<const u32x4 *>(xs + m * KC + k0);
+                            float a = acc[m];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                a = dot2<BF16>(x[j], w[d][j], a);
+                            acc[m] = a;
+                        }
+                        w[d] = fetch(tb + d + D);
+                        if (++st == steps) {
+                            // group g done: the 16 lanes of each row add up, lane 0 of the
+                            // row adds the sums into the C row block
+#pragma unroll
+                            for (int m = 0; m < MR; ++m) {
+                                const float v = dpp_row_sum16(acc[m]);
+                                if ((lane & 15) == 0)
+                                    ys[m * H16_COLS + 64 * wave + 4 * g + rg] += v;
+                                acc[m] = 0.0f;
+                            }
+                            st = 0;
+                            ++g;
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();   // every wave's groups are in ys
+        const int col = nblk + tid;
+        if (col < N) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m)
+                if (mc + m < M)
+                    skinny_store<EPI>(p, (int)mc + m, col, ys[m * H16_COLS + tid]);
+        }
+        __syncthreads();   // ys is read before the next row block clears it
+    }
+}
+
+template <bool BF16>
+static hipError_t launch_skinny16(const GemmParams &p0, int epi, hipStream_t s)
+{
+    static_assert(H16_COLS == kSkinnyCols && H16_XS == kSkinny16Stage, "skinny kernel shape");
+    GemmParams p = p0;
+    p.tiles_m = 1;
+    p.tiles_n = cdiv(p.N, H16_COLS);
+    if (p.batch < 1 || p.batch > kMaxGridZ || p.grid_x != 0 || p.sk_tiles != 0)
+        return hipErrorInvalidValue;   // whole grids only, no stream-K
+    const dim3 grid = gemm_grid(p, p.tiles_n), block(256);
+    const int mr = skinny_rows(p.M);
+#define LL_SKINNY_MR(E, MR) hipLaunchKernelGGL((gemm_h16_skinny_nt_kernel<E, BF16, MR>), grid, block, 0, s, p)
+#define LL_SKINNY(E) \
+    do { \
+        if (mr == 1) LL_SKINNY_MR(E, 1); \
+        else if (mr == 4) LL_SKINNY_MR(E, 4); \
+        else if (mr == 8) LL_SKINNY_MR(E, 8); \
+        else LL_SKINNY_MR(E, 16); \
+    } while (0)
+    if (epi == EPI_GEMM_BETA0) LL_SKINNY(EPI_GEMM_BETA0);
+    else if (epi == EPI_GEMM_BETA) LL_SKINNY(EPI_GEMM_BETA);
+    else LL_SKINNY(EPI_ATOMIC);
+#undef LL_SKINNY
+#undef LL_SKINNY_MR
+    return hipGetLastError();
+}
+
 // {BM, BN, workgroups per CU, relative throughput alone, paired} (see the
 // FP32 table), against the 256x256 kernel's 4096^3 rate. 128x128 (direct):
 // paired 0.91 on 8192^3 and 0.86 on 4096^3; alone 0.50 on 2048^3 and 0.62
@@ -758,6 +927,9 @@ const TileInfo kF16Tiles[kF16NumTiles] = {
     // not (3072^2: 256 tiles against 144).
     {192, 192, 1, 0.75f, 0.75f, "f16_192x192_direct", 1, false,
      64 * DirectCfg<192>::WGM * DirectCfg<192>::WGN, 0, true},
+    // the skinny kernel (B given N-by-K; forced with B given K-by-N, the
+    // 128x128 tile runs in its place): 16 rows of A at a time, 256 columns
+    {16, H16_COLS, 2, 1.0f, 1.0f, "f16_16x256_skinny_nt", 1, false},
 };
 
 // The direct kernel on BM x BM tiles (KS K-slices) for 128-bit-aligned
@@ -829,6 +1001,11 @@ static hipError_t launch_16(const GemmParams &p, int tile, int epi, bool vec, hi
     case 1: return launch_direct<BF16, BT, 128, F16_S, 2>(p, epi, vec, s);
     case 3: return launch_direct<BF16, BT, 128, F16_S, 2, 2>(p, epi, vec, s);
     case 4: return launch_direct<BF16, BT, 192, F16_S, 2>(p, epi, vec, s);
+    case 5:
+        if constexpr (BT)
+            return launch_skinny16<BF16>(p, epi, s);
+        else
+            return launch_direct<BF16, BT, 128, F16_S, 2>(p, epi, vec, s);
     default: return launch_t<F16_XS, 2, BF16, BT>(p, epi, vec, s);
     }
 }

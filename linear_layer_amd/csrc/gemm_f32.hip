@@ -821,33 +821,6 @@ gemm_f32_direct_kernel(GemmParams p)
 constexpr int SK_COLS = 256;     // columns of C per workgroup
 constexpr int SK_XS = 8192;      // LDS floats for the staged A block (32 KiB)
 
-__device__ __forceinline__ float dpp_row_sum16(float v)
-{
-    // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror:
-    // after the four steps every lane of a 16-lane row holds the row's sum
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false));
-    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false));
-    return v;
-}
-
-template <int EPI>
-__device__ __forceinline__ void skinny_store(const GemmParams &p, int row, int col, float a)
-{
-    float *dst = p.C + (int64_t)row * p.ldc + col;
-    if constexpr (EPI == EPI_ATOMIC) {
-        __hip_atomic_fetch_add(dst, p.alpha * a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if constexpr (EPI == EPI_GEMM_BETA) {
-        *dst = __builtin_fmaf(p.alpha, a, p.beta * *dst);
-    } else if constexpr (EPI == EPI_LINEAR) {
-        const float y = a + (p.bias != nullptr ? p.bias[col] : 0.0f);
-        *dst = (p.act == 1 && !(y > 0.0f)) ? 0.0f : y;
-    } else {
-        *dst = p.alpha * a;
-    }
-}
-
 // A's rows mc .. mc+MR-1 (zero past M), k-values kc .. kc+kn-1 of the K
 // range, into xs[m][0 .. kpad) (zero past kn; kpad = kn rounded up to 64).
 template <int MR>

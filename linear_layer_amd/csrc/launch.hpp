@@ -46,7 +46,18 @@ constexpr int64_t kSkinnyLargeKN = (int64_t)1 << 25;
 constexpr int kSkinnyStage = 8192;
 constexpr int skinny_rows(int M) { return M <= 1 ? 1 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 constexpr int skinny_kmax(int M) { return kSkinnyStage / skinny_rows(M); }
-constexpr int kF16NumTiles = 5;
+constexpr int kF16NumTiles = 6;
+// The 16-bit tile that is the skinny kernel (dot2 instructions for a few rows
+// of A, B given N-by-K) and the 16-bit values of A it stages at once. It is
+// chosen automatically for one row of A with B of at least kSkinnyLargeKN
+// values. Measured on MI355X against the 128x128 MFMA plan, per call: one
+// row 0.87 times its time with an 11008 x 4096 B, 0.89 with 4096 x 11008,
+// the same with 14336 x 4096, but 1.03 with 4096 x 4096; two to eight rows
+// 1.06 to 1.9 times (each lane reads A's values from LDS again for every
+// group of four columns).
+constexpr int kSkinny16Tile = 5, kSkinny16MaxM = 1;
+constexpr int kSkinny16Stage = 16384;
+constexpr int skinny16_kmax(int M) { return kSkinny16Stage / skinny_rows(M); }
 extern const TileInfo kF32Tiles[kF32NumTiles];
 extern const TileInfo kF16Tiles[kF16NumTiles];
 

@@ -30,6 +30,8 @@ thirteenth and fourteenth are the fully-connected layer with one and four
 rows of X: by the intensity formula of page "GEMM 优化详解" (table
 "计算复杂度分析"), 2MNK / (MK + KN + MN) / 4, they do about M/2 FLOP per byte,
 far below the ridge, so HBM bounds them and the bench rates them in GB/s.
+The fifteenth is the one-row decode step with 16-bit operands and B given
+N-by-K, HBM-bound too.
 """
 from __future__ import annotations
 
@@ -101,6 +103,10 @@ WORKLOADS = {
                                             act=1, scale=1.0 / 64.0, bound="hbm"),
     "linear_relu_4x4096x11008": Workload(14, "linear_relu_4x4096x11008", "linear", 4, 11008, 4096,
                                          act=1, scale=1.0 / 64.0, bound="hbm"),
+    # the same decode step with 16-bit inputs: one row of A (K = 4096) against
+    # B given 11008 x 4096 [out][in]
+    "gemm_f16f32_nt_1x4096x11008": Workload(15, "gemm_f16f32_nt_1x4096x11008", "gemm_f16f32_nt", 1, 11008, 4096,
+                                            bound="hbm"),
 }
 
 HALF_KINDS = ("gemm_f16f32", "gemm_bf16f32", "gemm_f16f32_nt")

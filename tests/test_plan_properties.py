@@ -4,7 +4,7 @@ over random shapes (host logic only: the plan queries run without a GPU).
 For any product the planner either returns a usable plan or none (-1, for
 shapes whose tiles cannot fit one launch's grid); a usable plan names a tile
 of the data type's table whose grid fits, splits K into at most 16 parts (64
-for the skinny kernel) of at least one 64-deep stage (unless forced), shares out stream-K tiles only
+for the skinny kernels) of at least one 64-deep stage (unless forced), shares out stream-K tiles only
 for single products without a K-split, never shares out more tiles than the
 product has, and honours forced settings.
 """
@@ -16,7 +16,7 @@ import linear_layer_amd as ll
 F32, F16 = ll.DTYPE_F32, ll.DTYPE_F16
 TILE_SHAPES = {
     F32: [(256, 256), (256, 128), (128, 128), (64, 64), (64, 64), (128, 128), (16, 256), (32, 128)],
-    F16: [(256, 256), (128, 128), (64, 64), (128, 128), (192, 192)],
+    F16: [(256, 256), (128, 128), (64, 64), (128, 128), (192, 192), (16, 256)],
 }
 dims = st.one_of(st.integers(1, 300), st.integers(1, 20000), st.sampled_from([255, 256, 257, 2047, 4096, 11008]))
 
@@ -51,8 +51,8 @@ def test_automatic_plans_are_well_formed(dt, M, N, K, batch, cus, relu, nk):
     s = ll.chosen_split_k(q, M, N, K, cus, batch)
     sk = ll.chosen_stream_k(q, M, N, K, cus, batch)
     assert 0 <= t < ll.num_tiles(dt)                 # these shapes always fit
-    # the skinny kernel (a few rows of A) splits K up to 64 ways, the others 16
-    assert 1 <= s <= (64 if ll.tile_name(dt, t).endswith("_skinny") else 16)
+    # the skinny kernels (a few rows of A) split K up to 64 ways, the others 16
+    assert 1 <= s <= (64 if "_skinny" in ll.tile_name(dt, t) else 16)
     if s > 1:
         assert K >= 64 * (s - 1), "a split is at least one stage deep"
     assert sk >= 0
@@ -144,7 +144,7 @@ def test_skinny_kernel_choice():
         assert not name(F32, M, 4096, 4096).endswith("_skinny")
     assert not name(F32, 9, 11008, 4096).endswith("_skinny")
     assert not name(F32, 4, 11008, 4096, batch=2).endswith("_skinny")
-    assert not ll.tile_name(F16, ll.chosen_tile(F16, 1, 11008, 4096, 256)).endswith("_skinny")
+    assert "_skinny" not in ll.tile_name(F16, ll.chosen_tile(F16, 1, 11008, 4096, 256))
     # 43 column blocks of 256: ceil(512 / 43) = 12 splits of 384 -> 11 splits;
     # N-by-K: ceil(768 / 43) = 18 splits of 256 -> 16 splits
     assert split(F32, 1, 11008, 4096) == 11
@@ -158,3 +158,20 @@ def test_skinny_kernel_choice():
     assert split(F32, 4, 256, 2 ** 20) == 64
     # short K: no split shorter than 64
     assert split(F32, 1, 256, 100) == 2 and split(F32, 1, 256, 64) == 1
+
+
+def test_skinny16_kernel_choice():
+    """Single 16-bit products of one row of A with B given N-by-K and at least
+    2^25 values take the 16-bit skinny kernel, split K in ranges the kernel
+    stages whole; B given K-by-N, more rows, smaller B or a batch do not."""
+    nt = F16 | ll.PLAN_B_NK
+    name = lambda q, M, N, K, batch=1: ll.tile_name(F16, ll.chosen_tile(q, M, N, K, 256, batch))
+    for N, K in ((11008, 4096), (4096, 11008), (14336, 4096)):
+        assert name(nt, 1, N, K) == "f16_16x256_skinny_nt"
+        assert "_skinny" not in name(F16, 1, N, K)
+        assert "_skinny" not in name(nt, 2, N, K)
+        assert "_skinny" not in name(nt, 1, N, K, batch=2)
+    assert "_skinny" not in name(nt, 1, 4096, 4096)
+    # 43 column blocks of 256: ceil(768 / 43) = 18 splits of 228 -> 256 -> 16 splits
+    assert ll.chosen_split_k(nt, 1, 11008, 4096, 256) == 16
+    assert ll.chosen_stream_k(nt, 1, 11008, 4096, 256) == 0
