@@ -31,9 +31,10 @@ extern "C" {
 int ll_set_tile(int dtype, int tile);
 
 /* Force `splits` K-splits (1 .. 16; the split length is rounded up to a
- * multiple of 64, so small K may use fewer) for every later call of any
- * dtype; -1 restores the automatic choice (which for the skinny tiles may
- * use up to 64). */
+ * multiple of 64, or of 128 on the 16-bit skinny tile, and to whole stages
+ * of every slice on the K-sliced tiles, so small K may use fewer) for every
+ * later call of any dtype; -1 restores the automatic choice (which for the
+ * skinny tiles may use up to 64). */
 int ll_set_split_k(int splits);
 
 /* Stream-K for leftover tiles: -1 automatic (default), 0 never, 1 whenever

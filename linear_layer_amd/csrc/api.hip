@@ -256,9 +256,10 @@ bool sk_tile_ok(const TileInfo &ti)
 // waves stream fewer bytes at a time), as measured fastest on MI355X, and
 // keep each split within the A block the kernel stages whole (kmax); at most
 // kMaxSkinnySplits (the atomic partial sums of a few rows cost little), each
-// at least kSplitAlign long.
+// a multiple of `align` long: kSplitAlign, or the k-values one load of the
+// 16-bit kernel covers (128), so that no load of a split is partial.
 constexpr int kMaxSkinnySplits = 64;
-Plan skinny_plan(int tile, int kmax, int M, int N, int K, int cus, int s_ov, bool bt)
+Plan skinny_plan(int tile, int kmax, int align, int M, int N, int K, int cus, int s_ov, bool bt)
 {
     const int64_t nblk = cdiv(N, kSkinnyCols);
     if (nblk > max_grid_x(256) || nblk * kSkinnyCols > ((int64_t)1 << 31))
@@ -267,15 +268,14 @@ Plan skinny_plan(int tile, int kmax, int M, int N, int K, int cus, int s_ov, boo
     if (s_ov < 1) {
         const int64_t fill = ((bt ? 3 : 2) * (int64_t)(cus > 0 ? cus : 1) + nblk - 1) / nblk;
         const int64_t fit = ((int64_t)K + kmax - 1) / kmax;
-        const int64_t smax = ((int64_t)K + kSplitAlign - 1) / kSplitAlign;
+        const int64_t smax = ((int64_t)K + align - 1) / align;
         s = fill > fit ? fill : fit;
         s = s > kMaxSkinnySplits ? kMaxSkinnySplits : s;
         s = s > smax ? smax : s;
     }
     if (s <= 1 || K <= 0)
         return Plan{tile, 1, K, 0, 0};
-    const int k_split =
-        (int)((((int64_t)K + s - 1) / s + kSplitAlign - 1) / kSplitAlign * kSplitAlign);
+    const int k_split = (int)((((int64_t)K + s - 1) / s + align - 1) / align * align);
     return Plan{tile, (int)(((int64_t)K + k_split - 1) / k_split), k_split, 0, 0};
 }
 
@@ -299,13 +299,13 @@ Plan plan(int dtype, const TileInfo *tiles, int ntiles, int M, int N, int K, int
     // with B given N-by-K); it runs others only when forced
     const bool skinny = M <= kSkinnyMaxM || (M <= kSkinnyMaxMLarge && (int64_t)K * N >= kSkinnyLargeKN);
     if (dtype == LL_DTYPE_F32 && (t_ov == kSkinnyTile || (t_ov < 0 && skinny && batch == 1))) {
-        const Plan sp = skinny_plan(kSkinnyTile, skinny_kmax(M), M, N, K, cus, s_ov, bt);
+        const Plan sp = skinny_plan(kSkinnyTile, skinny_kmax(M), kSplitAlign, M, N, K, cus, s_ov, bt);
         if (sp.tile >= 0 || t_ov == kSkinnyTile)
             return sp;
     }
     const bool skinny16 = M <= kSkinny16MaxM && (int64_t)K * N >= kSkinnyLargeKN && bt;
     if (dtype != LL_DTYPE_F32 && (t_ov == kSkinny16Tile || (t_ov < 0 && skinny16 && batch == 1))) {
-        const Plan sp = skinny_plan(kSkinny16Tile, skinny16_kmax(M), M, N, K, cus, s_ov, bt);
+        const Plan sp = skinny_plan(kSkinny16Tile, skinny16_kmax(M), kSkinny16Align, M, N, K, cus, s_ov, bt);
         if (sp.tile >= 0 || t_ov == kSkinny16Tile)
             return sp;
     }

@@ -737,7 +737,7 @@ static hipError_t launch_t(const GemmParams &p0, int epi, bool vec, hipStream_t 
 // inner product runs on dot2 instructions: two 16-bit products added into an
 // FP32 sum per lane and instruction, the precision of the MFMA path. A
 // workgroup of four waves covers 256 columns of C over its K range (a
-// K-split), A's rows MR at a time (MR = 1, 4, 8 or 16). The A block of the K
+// K-split), A's rows MR at a time (MR = 1, 2, 4, 8 or 16). The A block of the K
 // range is staged raw in LDS (H16_XS values; the planner keeps the range
 // within H16_XS / MR k-values, and a longer one, from a forced plan, is
 // walked in chunks of that size). Wave w covers columns 64w .. 64w+63 in 16
@@ -889,6 +889,7 @@ static hipError_t launch_skinny16(const GemmParams &p0, int epi, hipStream_t s)
 #define LL_SKINNY(E) \
     do { \
         if (mr == 1) LL_SKINNY_MR(E, 1); \
+        else if (mr == 2) LL_SKINNY_MR(E, 2); \
         else if (mr == 4) LL_SKINNY_MR(E, 4); \
         else if (mr == 8) LL_SKINNY_MR(E, 8); \
         else LL_SKINNY_MR(E, 16); \

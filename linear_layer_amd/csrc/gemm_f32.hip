@@ -801,7 +801,7 @@ gemm_f32_direct_kernel(GemmParams p)
 // Skinny products (a few rows of A): memory-bound, so vector FMAs instead of
 // MFMAs, which would compute a whole 32-row block for every row. A
 // workgroup of four waves covers 256 columns of C over its K range (a
-// K-split), A's rows MR at a time (MR = 1, 4, 8 or 16, the fewest that
+// K-split), A's rows MR at a time (MR = 1, 2, 4, 8 or 16, the fewest that
 // cover M). The A block of the K range is staged in LDS once (SK_XS floats: the
 // planner keeps the range within SK_XS / MR k-values; a longer one, from a
 // forced plan, is walked in chunks of that size). B streams from HBM with
@@ -1218,6 +1218,7 @@ static hipError_t launch_skinny(const GemmParams &p0, int epi, hipStream_t s)
 #define LL_SKINNY(E) \
     do { \
         if (mr == 1) LL_SKINNY_MR(E, 1); \
+        else if (mr == 2) LL_SKINNY_MR(E, 2); \
         else if (mr == 4) LL_SKINNY_MR(E, 4); \
         else if (mr == 8) LL_SKINNY_MR(E, 8); \
         else LL_SKINNY_MR(E, 16); \

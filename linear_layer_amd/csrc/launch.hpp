@@ -41,22 +41,23 @@ constexpr int kThinTile = 7;
 constexpr int kThinMinSplit = 256;
 constexpr int64_t kSkinnyLargeKN = (int64_t)1 << 25;
 // Floats of A the skinny kernel stages in LDS at once, its rows per pass
-// for a product of M rows (the fewest of 1, 4, 8, 16 that cover M), and so the
-// longest K range it stages whole.
+// for a product of M rows (the fewest of 1, 2, 4, 8, 16 that cover M), and so
+// the longest K range it stages whole.
 constexpr int kSkinnyStage = 8192;
-constexpr int skinny_rows(int M) { return M <= 1 ? 1 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+constexpr int skinny_rows(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
 constexpr int skinny_kmax(int M) { return kSkinnyStage / skinny_rows(M); }
 constexpr int kF16NumTiles = 6;
 // The 16-bit tile that is the skinny kernel (dot2 instructions for a few rows
 // of A, B given N-by-K) and the 16-bit values of A it stages at once. It is
 // chosen automatically for one row of A with B of at least kSkinnyLargeKN
-// values. Measured on MI355X against the 128x128 MFMA plan, per call: one
-// row 0.87 times its time with an 11008 x 4096 B, 0.89 with 4096 x 11008,
-// the same with 14336 x 4096, but 1.03 with 4096 x 4096; two to eight rows
-// 1.06 to 1.9 times (each lane reads A's values from LDS again for every
-// group of four columns).
+// values. Measured on MI355X against the MFMA plan, per call: one row 0.79
+// to 1.01 times its time with such a B (11008 x 4096 0.85, 28672 x 8192
+// 0.79, 4096 x 8192 1.01), 1.00 to 1.03 with smaller ones (4096 x 4096,
+// 5120 x 5120); two rows 0.76 to 1.06 times, four and eight 1.05 to 1.9
+// (each lane reads A's values from LDS again for every group of four
+// columns, and the work per byte of B grows with the rows).
 constexpr int kSkinny16Tile = 5, kSkinny16MaxM = 1;
-constexpr int kSkinny16Stage = 16384;
+constexpr int kSkinny16Stage = 16384, kSkinny16Align = 128;
 constexpr int skinny16_kmax(int M) { return kSkinny16Stage / skinny_rows(M); }
 extern const TileInfo kF32Tiles[kF32NumTiles];
 extern const TileInfo kF16Tiles[kF16NumTiles];

@@ -1,7 +1,7 @@
 """GPU parity of the skinny FP32 kernel (vector FMAs for a few rows of A,
 memory-bound; chosen by itself for up to 4 rows, or 8 with a large B, and
 forced here for more): every row count from 1 to 16 and a few past it, all
-four row-pass widths (1, 4, 8, 16), both B layouts, every epilogue (beta = 0,
+five row-pass widths (1, 2, 4, 8, 16), both B layouts, every epilogue (beta = 0,
 general beta, K-split atomics, the fused layer with and without bias and
 ReLU), K ranges longer than the staged A block, ragged and unaligned N and
 K, and the layer's decode-sized shapes at full size; against the float64
@@ -187,7 +187,7 @@ def test_batched_forced():
         assert_close(np32(Cd), R, T, f"batched tb={tb}")
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 8, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16])
 @pytest.mark.parametrize("nt", [False, True])
 def test_decode_sized_layer_full_size(M, nt):
     """The layer's weight at full size (K 4096, N 11008) with a handful of

@@ -1,7 +1,7 @@
 """GPU parity of the skinny 16-bit kernel (dot2 instructions for a few rows of
 A with B given N-by-K, memory-bound; chosen by itself for one row of A with a
 large B, and forced here for the rest): binary16 and bfloat16, every row
-count from 1 to 16 and a few past it, all four row-pass widths (1, 4, 8, 16),
+count from 1 to 16 and a few past it, all five row-pass widths (1, 2, 4, 8, 16),
 both epilogues and the K-split atomics, K ranges longer than the staged A
 block, ragged and unaligned N and K, a strided batch, the forced tile with B
 given K-by-N (the 128x128 tile runs in its place), and the decode-sized
@@ -174,7 +174,7 @@ def test_batched_forced(which):
     assert_close(np32(Cd), R, T, f"{which} batched")
 
 
-@pytest.mark.parametrize("M", [1, 3, 4, 8, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 16])
 @pytest.mark.parametrize("which", ["f16", "bf16"])
 def test_decode_sized_full_size(M, which):
     """A 11008 x 4096 weight given [out][in] with a handful of rows: the

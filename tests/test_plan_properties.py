@@ -72,10 +72,13 @@ def test_forced_settings_are_honoured(dt, M, N, K, data):
     got = ll.chosen_split_k(dt, M, N, K, 256)
     # the split length is ceil(K / s) rounded up to whole 64-deep stages, or
     # for a K-sliced tile to whole stages of every slice (KS x 32 FP32 or
-    # KS x 64 16-bit values, if more), so the count may come out smaller
+    # KS x 64 16-bit values, if more), or for the 16-bit skinny tile to whole
+    # 128-value loads, so the count may come out smaller
     name = ll.tile_name(dt, t)
     ks = 4 if name.endswith("_k4") else 2 if name.endswith("_k2") else 1
     align = max(64, ks * (64 if dt == F16 else 32))
+    if dt == F16 and "_skinny" in name:
+        align = 128
     k_split = -(-(-(-K // s)) // align) * align
     assert got == -(-K // k_split) and 1 <= got <= s
     assert ll.chosen_stream_k(dt, M, N, K, 256) == 0   # a forced split excludes stream-K
