@@ -525,10 +525,13 @@ def test_non_default_stream():
 def test_concurrent_streams_and_threads():
     """Products of every kind running at the same time on two streams, issued
     from two host threads: the library keeps no state between calls (beyond
-    the device-property cache), so each result matches the oracle."""
+    the device-property cache), so each result matches the oracle. The shapes
+    include one row against a 4096 x 11008 B (the skinny kernels, K split
+    over the CUs) and 16 rows against an 8192 x 4096 one (the 32x128 tile)."""
     import threading
     cases = []
-    shapes = [(600, 520, 200), (257, 300, 1000), (1024, 768, 512), (300, 264, 72)]
+    shapes = [(600, 520, 200), (257, 300, 1000), (1024, 768, 512), (300, 264, 72), (1, 11008, 4096),
+              (16, 4096, 8192)]
     for i, (M, N, K) in enumerate(shapes):
         A, B = rand((M, K), 171 + 2 * i), rand((K, N), 172 + 2 * i)
         cases.append(("f32", A, B, oracle.gemm(np32(A), np32(B))))
